@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the compressed linear forward on one MI355X.
+
+Default workload: the LLaMA-7B decode layer set at batch 1 -- fused qkv
+4096->12288, o 4096->4096, gate and up 4096->11008, down 11008->4096 -- with
+4-bit per-row LUT codes and 0.45% fp16 CSR outliers, seeded synthetic
+weights and activations.  One step is one forward of every layer of the set
+(five launches of the decode kernel).  Packed weights rotate over enough
+copies (>= 1 GiB) that no step finds its weights in the 256 MB last-level cache.
+
+Prints one JSON line on stdout:
+  value       effective HBM GB/s on algorithmic bytes (packed weights + x + y)
+  roofline    the decode kernel against the 8 TB/s HBM peak
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same layers
+
+Other workloads (`--config 1..5`, `--M`) are for measurement sweeps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "batch-1 µs/layer & effective HBM GB/s (% of peak) for compressed GEMV"
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_lut4_llama7b_b1_traffic.txt")
+KERNEL_SOURCES = ["compressed_linear_amd/csrc/decode_impl.h", "compressed_linear_amd/csrc/unpack.h",
+                  "compressed_linear_amd/csrc/decode.hip", "compressed_linear_amd/csrc/layout.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(bytes_per_launch_alg: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
+
+    The summary holds FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the decode
+    kernel, the same counters for a copy kernel of known size (calibration), and
+    the hash of the kernel sources it was taken with; a different hash means the
+    kernel changed since, and the figure no longer applies.
+    """
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"^\s*([a-z_]+)\s*[:=]\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def layer_bytes(acct: dict, K: int, N: int, M: int) -> int:
+    return int(acct["total"]) + 2 * M * K + 4 * M * N
+
+
+def cpu_baseline(layers, xs, budget_s: float = 12.0):
+    """Time the fp64 oracle on a row sample of each layer; scale to GB/s and us/layer."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1)
+    except Exception:  # noqa: BLE001 -- optional
+        limit = None
+    frac = 1.0 / 16
+    t_total, bytes_total, rows_total, rows_all = 0.0, 0.0, 0, 0
+    per_layer_us = []
+    for (layer, acct), x in zip(layers, xs):
+        n_rows = max(64, int(layer.N * frac))
+        rows = np.arange(n_rows)
+        t0 = time.perf_counter()
+        oracle.forward(layer, x, rows)
+        dt = time.perf_counter() - t0
+        scale = layer.N / n_rows
+        t_total += dt * scale
+        bytes_total += layer_bytes(acct, layer.K, layer.N, x.shape[0])
+        per_layer_us.append(dt * scale * 1e6)
+        rows_total += n_rows
+        rows_all += layer.N
+        if t_total > budget_s * 16:
+            break
+    if limit is not None:
+        limit.unregister() if hasattr(limit, "unregister") else None
+    return {
+        "value": round(bytes_total / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "us_per_layer": round(float(np.mean(per_layer_us)), 1),
+        "sample": f"fp64 reconstruct + x W^T of the first 1/16 of the rows of each layer "
+                  f"({rows_total} of {rows_all} rows), single thread, scaled to whole layers",
+    }
+
+
+def to_dev_x(x, x_dtype, dev):
+    import torch
+    if x_dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(x.astype(np.float16))).to(dev)
+
+
+def build_layers(cfg: int, M: int):
+    from synth.layers import CONFIGS, make_layer, make_x
+    import compressed_linear_amd as cla
+    out, xs = [], []
+    for li, (name, K, N) in enumerate(CONFIGS[cfg]["layers"]):
+        layer = make_layer(cfg, li, M_for_clamp=M)
+        blob, acct = cla.pack(layer)
+        out.append((layer, acct, blob))
+        xs.append(make_x(cfg, li, M))
+    return out, xs
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--M", type=int, default=1)
+    ap.add_argument("--path", default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-layer", action="store_true", help="also time each layer alone")
+    a = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU; multi-GPU runs (--gpus > 1) are not part of it.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import compressed_linear_amd as cla
+    from synth.layers import CONFIGS
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg, M = a.config, a.M
+
+    log(f"building config {cfg} M={M}")
+    built, xs_np = build_layers(cfg, M)
+    set_bytes = sum(layer_bytes(acct, l.K, l.N, M) for l, acct, _ in built)
+    weight_bytes = sum(int(acct["total"]) for _, acct, _ in built)
+    R = max(2, -(-ROTATE_BYTES // weight_bytes))
+    log(f"layer set: {len(built)} layers, {set_bytes / 1e6:.2f} MB algorithmic per step, {R} rotating copies")
+
+    mods = [[cla.CompressedLinear(blob, max_M=max(M, 1), device=dev) for (_, _, blob) in built] for _ in range(R)]
+    xs = [[to_dev_x(x, l.x_dtype, dev) for (l, _, _), x in zip(built, xs_np)] for _ in range(R)]
+    ys = [[torch.empty((M, l.N), dtype=torch.float32, device=dev) for (l, _, _) in built] for _ in range(R)]
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    ptrs = [[(m._h, x.data_ptr(), y.data_ptr()) for m, x, y in zip(mods[r], xs[r], ys[r])] for r in range(R)]
+    path = cla.PATH[a.path]
+    fwd = cla.lib().cl_forward_path
+
+    def step(i):
+        for h, xp, yp in ptrs[i % R]:
+            st = fwd(h, M, xp, yp, sp, path)
+            if st != 0:
+                raise cla.ClError(st, "cl_forward", cla.lib().cl_last_error().decode())
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(a.steps):
+        step(a.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / a.steps
+    n_launch = len(built)
+    gbs = set_bytes / (ms_per_step * 1e-3) / 1e9
+    us_per_layer = ms_per_step * 1e3 / n_launch
+    log(f"{ms_per_step * 1e3:.2f} us/step, {us_per_layer:.2f} us/layer, {gbs:.1f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
+
+    per_layer = []
+    if a.per_layer or cfg == 2:
+        for li, (l, acct, _) in enumerate(built):
+            reps = max(20, a.steps)
+            for i in range(5):
+                h, xp, yp = ptrs[i % R][li]
+                fwd(h, M, xp, yp, sp, path)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(reps):
+                h, xp, yp = ptrs[i % R][li]
+                fwd(h, M, xp, yp, sp, path)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            b = layer_bytes(acct, l.K, l.N, M)
+            per_layer.append({"layer": CONFIGS[cfg]["layers"][li][0], "K": l.K, "N": l.N, "us": round(us, 3),
+                              "GBps": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                              "bytes": b})
+            log(f"  {per_layer[-1]}")
+
+    # roofline of the decode kernel: algorithmic bytes per launch over the mean launch duration
+    bytes_per_launch = set_bytes / n_launch
+    us_per_launch = ms_per_step * 1e3 / n_launch
+    achieved = bytes_per_launch / us_per_launch / 1e3
+    traffic = read_traffic(bytes_per_launch)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "decode_kernel (LUT4, batch 1)", "bytes_per_launch": int(bytes_per_launch),
+            "us_per_launch": round(us_per_launch, 3)}
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        cpu = cpu_baseline([(l, acct) for l, acct, _ in built], xs_np)
+        log(f"  {cpu}")
+
+    dtype = "bf16 x, fp16 weights, f32 acc" if built[0][0].x_dtype == "bf16" else "f16"
+    layers_desc = ", ".join(f"{n} {K}->{N}" for n, K, N in CONFIGS[cfg]["layers"])
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_layer": round(us_per_layer, 3),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded; LLaMA layer shapes, random codes/LUTs/outliers)",
+        "config": {"workload": f"{CONFIGS[cfg]['desc']}: {layers_desc}", "batch": M,
+                   "layers_per_step": n_launch, "rotating_copies": R,
+                   "algorithmic_bytes_per_step": int(set_bytes)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_layer": per_layer,
+    }
+    for r in mods:
+        for m in r:
+            m.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

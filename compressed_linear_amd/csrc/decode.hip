@@ -1,0 +1,55 @@
+// decode.hip -- dispatch of the batch 1..32 forward to the per-kind kernels.
+#include "decode_impl.h"
+
+namespace cl {
+
+extern template hipError_t launch_decode_kind<K_LUT3>(const DecodeArgs&, bool, hipStream_t);
+extern template hipError_t launch_decode_kind<K_LUT4>(const DecodeArgs&, bool, hipStream_t);
+extern template hipError_t launch_decode_kind<K_INT4>(const DecodeArgs&, bool, hipStream_t);
+extern template hipError_t launch_decode_kind<K_INT4_24>(const DecodeArgs&, bool, hipStream_t);
+extern template hipError_t launch_decode_kind<K_INT8>(const DecodeArgs&, bool, hipStream_t);
+extern template hipError_t launch_decode_kind<K_INT8_BM>(const DecodeArgs&, bool, hipStream_t);
+
+hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream) {
+
+  const cl_blob_header& h = L.h;
+  DecodeArgs a = {};
+  a.dense = reinterpret_cast<const uint4*>(L.dense);
+  a.meta = L.meta;
+  a.nzstart = L.nzstart;
+  a.table = reinterpret_cast<const uint16_t*>(L.table);
+  a.rowptr = h.nnz > 0 ? L.rowptr : nullptr;
+  a.col = L.col;
+  a.val = L.val;
+  a.R = L.R;
+  a.Rscale = L.Rscale;
+  a.t = L.t;
+  a.x = x;
+  a.y = y;
+  a.part = L.part;
+  a.counters = L.counters;
+  a.K = h.K;
+  a.N = h.N;
+  a.M = M;
+  a.ldx = (x == L.xprep) ? L.Kx : h.K;
+  a.chunks = h.chunks;
+  a.span = h.span;
+  a.split = L.split;
+  a.G = h.n_tiles * L.split;
+  a.Gpad = (a.G + 7) & ~7;
+  a.rank = h.rank;
+  a.group = h.group > 0 ? h.group : 1;
+  a.lr_kind = h.lr;
+  a.Npad = L.Npad;
+  const bool bf16 = h.x_dtype == CL_ACT_BF16;
+  switch (h.dense) {
+    case CL_DENSE_LUT3: return launch_decode_kind<K_LUT3>(a, bf16, stream);
+    case CL_DENSE_LUT4: return launch_decode_kind<K_LUT4>(a, bf16, stream);
+    case CL_DENSE_INT4:
+      return h.mask == CL_MASK_2_4 ? launch_decode_kind<K_INT4_24>(a, bf16, stream) : launch_decode_kind<K_INT4>(a, bf16, stream);
+    default:
+      return h.mask == CL_MASK_BITMAP ? launch_decode_kind<K_INT8_BM>(a, bf16, stream) : launch_decode_kind<K_INT8>(a, bf16, stream);
+  }
+}
+
+}  // namespace cl

@@ -1,0 +1,6 @@
+// decode_lut4.hip -- decode kernels for the LUT4 dense format.
+#include "decode_impl.h"
+
+namespace cl {
+template hipError_t launch_decode_kind<K_LUT4>(const DecodeArgs&, bool, hipStream_t);
+}  // namespace cl

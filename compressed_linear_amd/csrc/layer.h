@@ -1,0 +1,57 @@
+// layer.h -- the host-side handle of an uploaded layer and the launch entry points.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "compressed_linear.h"
+#include "layout.h"
+
+namespace cl {
+
+constexpr int kMaxDecodeM = 32;
+
+struct Layer {
+  cl_blob_header h;          // copy of the blob header
+  uint8_t* dev = nullptr;    // dev_buf (caller owned)
+  size_t dev_bytes = 0;
+  int32_t max_M = 0;
+  int Npad = 0;
+  int split = 1;             // split-K workgroups per tile (decode)
+  int num_cus = 256;
+
+  // packed sections on the device (NULL when absent)
+  const uint8_t* dense = nullptr;
+  const uint8_t* table = nullptr;
+  const uint8_t* meta = nullptr;
+  const int32_t* nzoff = nullptr;
+  int32_t* nzstart = nullptr;    // bitmap: [Npad][4*split] (workspace, filled at create)
+  const int32_t* rowptr = nullptr;
+  const int32_t* col = nullptr;
+  const uint16_t* val = nullptr;
+  const uint8_t* L = nullptr;
+  const uint8_t* R = nullptr;
+  const uint16_t* Lscale = nullptr;
+  const uint16_t* Rscale = nullptr;
+
+  // workspace (inside dev_buf, after the packed sections)
+  uint32_t* counters = nullptr;  // [n_tiles + 1], zero between forwards
+  float* part = nullptr;         // [n_tiles][split][kMaxDecodeM][64]
+  float* tpart = nullptr;        // [prologue blocks][max_M][rank]
+  float* t = nullptr;            // [max_M][rank]
+  uint16_t* xprep = nullptr;     // [max_M][Kx]  clamped / padded activations
+  int Kx = 0;                    // row stride of xprep (even)
+  int lr_blocks = 0;             // prologue workgroups
+  size_t ws_bytes = 0;
+};
+
+// Workspace layout and size for a blob header (used by cl_device_bytes and cl_create).
+size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L /* may be NULL */, size_t base);
+
+// Kernel launchers (kernels.hip).  All asynchronous on `stream`.
+hipError_t launch_prep_x(const Layer& L, int M, const void* x, hipStream_t stream);
+hipError_t launch_lowrank_prologue(const Layer& L, int M, const void* x, hipStream_t stream);
+hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream);
+hipError_t launch_prefill(const Layer& L, int M, const void* x, float* y, hipStream_t stream);
+hipError_t launch_debug(const Layer& L, uint16_t* D16, uint16_t* S16, float* L32, float* R32, hipStream_t stream);
+
+}  // namespace cl

@@ -1,0 +1,67 @@
+// layout.h -- device layout of a packed compressed linear layer.
+//
+// Shared by the host packer and the HIP runtime.  Plain C++, no HIP types.
+//
+// Rows (output channels) are grouped in tiles of 64; one wavefront lane owns
+// one row of a tile.  Every dense stream is stored tile-interleaved,
+//
+//     stream[tile][chunk][lane][bytes_per_chunk],
+//
+// so that the 64 lanes of a wavefront reading chunk c of their rows touch one
+// contiguous, aligned block (1 KiB for 16-byte chunks): fully coalesced
+// 128-bit loads.  A chunk covers `span` consecutive k of the row.  Rows are
+// padded to whole chunks and N to whole tiles; padding bytes are zero.
+//
+// Per dense kind (bit positions count from the least significant bit):
+//
+//   LUT3  span 40: the chunk is 4 words; word i holds the ten 3-bit codes of
+//         k = 40c + 10i + t, t = 0..9 (the same ten codes as the i-th canonical
+//         10-per-word word of the row), rearranged so that the code pair
+//         p_j = code[2j] | code[2j+1] << 3 (j = 0..4) sits in
+//           p_0..p_3 : bits 0..5 of byte j;
+//           p_4      : bits 6..7 of bytes 0, 1, 2 (two bits each, low bits first);
+//         bits 6..7 of byte 3 are zero.
+//   LUT4  span 32: word i holds codes k = 32c + 8i + t at bits 4t..4t+3
+//         (canonical order, least significant nibble first).
+//   INT4  span 32 (no mask): word i holds u = q + 8 of k = 32c + 8i + t; the
+//         pair (2j, 2j+1) sits at bits 4j..4j+3 and 16+4j..16+4j+3.
+//   INT4 + 2:4, span 64: 16 groups of four k per chunk.  DENSE word i holds
+//         the two kept values (u = q + 8) of groups 4i..4i+3, group g' of the
+//         word at bits 4g'..4g'+3 (first kept) and 16+4g'.. (second kept).
+//         META (8 bytes per chunk) word i holds groups 8i..8i+7, a nibble
+//         i0 | i1 << 2 per group (positions 0..3 of the two kept weights,
+//         i0 < i1) at bits 4t..4t+3.
+//   INT8  span 16 (no mask): byte t holds u = q + 128 of k = 16c + t.
+//   INT8 + BITMAP, span 128: META (16 bytes per chunk) holds the keep bits,
+//         bit t of word i <-> k = 128c + 32i + t.  The kept values (signed
+//         int8, ascending k) of each row are contiguous in DENSE starting at
+//         NZOFF[n] (a multiple of 16), not tile-interleaved.
+#pragma once
+#include <stdint.h>
+
+namespace cl {
+
+constexpr int kTileRows = 64;
+constexpr int kChunkBytes = 16;
+
+struct KindInfo {
+  int span;               // logical k per chunk of the dense stream (bitmap: per meta chunk)
+  int meta_chunk_bytes;   // bytes of META per row per chunk
+  int table_entries;      // LUT entries per row (0 for integer formats)
+};
+
+inline KindInfo kind_info(int dense, int mask) {
+  // dense: 0 LUT3, 1 LUT4, 2 INT4, 3 INT8; mask: 0 none, 1 2:4, 2 bitmap
+  if (dense == 0) return {40, 0, 8};
+  if (dense == 1) return {32, 0, 16};
+  if (dense == 2 && mask == 0) return {32, 0, 0};
+  if (dense == 2 && mask == 1) return {64, 8, 0};
+  if (dense == 3 && mask == 0) return {16, 0, 0};
+  if (dense == 3 && mask == 2) return {128, 16, 0};
+  return {0, 0, 0};
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+}  // namespace cl

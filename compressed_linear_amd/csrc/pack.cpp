@@ -1,0 +1,452 @@
+// pack.cpp -- host packer: validates a logical layer and lays it out for the GPU.
+//
+// Host only (no HIP calls), so the whole packer is testable on a CPU.
+// Format sources:
+//   "SqueezeLLM: Dense-and-Sparse Quantization", Approach: per-weight LUT
+//     codes and a full-precision CSR matrix of outliers;
+//   "SLiM: One-shot Quantization and Sparsity with Low-rank Approximation for
+//     LLM Weight Compression", review highlights and rebuttal: symmetric
+//     integer weights, 2:4 or unstructured masks, low-rank adapters with
+//     AbsMax int4 groups of 128;
+//   "Compressing Large Language Models by Joint Sparsification and
+//     Quantization", Approach: unstructured sparsity with quantization and a
+//     per-layer activation clamp.
+// The device layout of each section is described in layout.h.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "internal.h"
+#include "layout.h"
+
+namespace cl {
+
+static thread_local std::string g_err;
+
+cl_status fail(cl_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+void clear_error() { g_err.clear(); }
+
+cl_status check_blob(const void* blob, const cl_blob_header** out) {
+  if (!blob) return fail(CL_EINVAL, "blob is NULL");
+  if (reinterpret_cast<uintptr_t>(blob) % 8) return fail(CL_EINVAL, "blob is not 8-byte aligned");
+  const cl_blob_header* h = static_cast<const cl_blob_header*>(blob);
+  if (h->magic != CL_BLOB_MAGIC || h->version != CL_BLOB_VERSION)
+    return fail(CL_EINVAL, "not a compressed-linear blob (magic/version)");
+  if (h->K < 1 || h->N < 1 || h->n_tiles != (int32_t)ceil_div(h->N, kTileRows))
+    return fail(CL_EINVAL, "blob header has inconsistent dimensions");
+  KindInfo ki = kind_info(h->dense, h->mask);
+  if (ki.span == 0 || ki.span != h->span) return fail(CL_EINVAL, "blob header has an unknown format");
+  for (int s = 0; s < CL_SEC_COUNT; ++s) {
+    if (h->len[s] && (h->off[s] % 256 || h->off[s] + h->len[s] > h->total_bytes))
+      return fail(CL_EINVAL, "blob section %d lies outside the blob", s);
+  }
+  if (out) *out = h;
+  return CL_OK;
+}
+
+namespace {
+
+inline bool f16_is_finite_nonneg(uint16_t b) { return !(b & 0x8000u) && ((b >> 10) & 0x1F) != 0x1F; }
+
+struct Plan {
+  int64_t K, N, n_tiles, Npad, chunks, span, meta_cb, tab_entries;
+  int64_t nnz, rank, group, lr_half_r;
+  uint64_t off[CL_SEC_COUNT] = {}, len[CL_SEC_COUNT] = {};
+  uint64_t total = 0;
+  std::vector<int64_t> nz_count;  // BITMAP: kept per row
+  std::vector<int64_t> nz_off;    // BITMAP: device start of each row (16-aligned)
+  cl_bytes acct = {};
+};
+
+cl_status validate(const cl_layer_desc* d) {
+  if (!d) return fail(CL_EINVAL, "desc is NULL");
+  if (d->K < 1 || d->N < 1) return fail(CL_EINVAL, "K and N must be >= 1 (K=%d N=%d)", d->K, d->N);
+  if (d->K > (1 << 24) || d->N > (1 << 24)) return fail(CL_ESIZE, "K and N must be <= 2^24");
+  if (d->dense < 0 || d->dense > 3) return fail(CL_EINVAL, "unknown dense kind %d", d->dense);
+  if (d->mask < 0 || d->mask > 2) return fail(CL_EINVAL, "unknown mask kind %d", d->mask);
+  if (d->lr < 0 || d->lr > 3) return fail(CL_EINVAL, "unknown low-rank kind %d", d->lr);
+  if (d->x_dtype != CL_ACT_F16 && d->x_dtype != CL_ACT_BF16) return fail(CL_EINVAL, "unknown x dtype %d", d->x_dtype);
+  const bool lut = d->dense <= CL_DENSE_LUT4;
+  if (lut && d->mask != CL_MASK_NONE) return fail(CL_EUNSUPPORTED, "masks are built for the integer formats only");
+  if (d->dense == CL_DENSE_INT4 && d->mask == CL_MASK_BITMAP)
+    return fail(CL_EUNSUPPORTED, "the bitmap mask is built for INT8 values");
+  if (d->dense == CL_DENSE_INT8 && d->mask == CL_MASK_2_4)
+    return fail(CL_EUNSUPPORTED, "the 2:4 mask is built for INT4 values");
+  if (d->mask == CL_MASK_2_4 && d->K % 4) return fail(CL_EUNSUPPORTED, "2:4 needs K %% 4 == 0 (K=%d)", d->K);
+  const int64_t K = d->K, N = d->N;
+  if (lut) {
+    if (!d->codes || !d->lut) return fail(CL_EINVAL, "LUT formats need codes and lut");
+    const int nb = d->dense == CL_DENSE_LUT3 ? 8 : 16;
+    for (int64_t i = 0; i < N * K; ++i)
+      if (d->codes[i] >= nb) return fail(CL_EINVAL, "code %d out of range at %lld", d->codes[i], (long long)i);
+  } else {
+    if (!d->qvals || !d->row_scale) return fail(CL_EINVAL, "integer formats need qvals and row_scale");
+    const int lo = d->dense == CL_DENSE_INT4 ? -8 : -127, hi = d->dense == CL_DENSE_INT4 ? 7 : 127;
+    if (d->mask != CL_MASK_NONE && !d->keep) return fail(CL_EINVAL, "a mask needs keep");
+    for (int64_t i = 0; i < N * K; ++i) {
+      const bool kept = d->mask == CL_MASK_NONE || d->keep[i];
+      if (d->mask != CL_MASK_NONE && d->keep[i] > 1) return fail(CL_EINVAL, "keep must be 0 or 1 (at %lld)", (long long)i);
+      if (kept && (d->qvals[i] < lo || d->qvals[i] > hi))
+        return fail(CL_EINVAL, "value %d out of range [%d,%d] at %lld", d->qvals[i], lo, hi, (long long)i);
+    }
+    if (d->mask == CL_MASK_2_4) {
+      for (int64_t n = 0; n < N; ++n)
+        for (int64_t g = 0; g < K / 4; ++g) {
+          const uint8_t* kp = d->keep + n * K + 4 * g;
+          if (kp[0] + kp[1] + kp[2] + kp[3] != 2)
+            return fail(CL_EINVAL, "2:4 group (row %lld, k %lld) does not keep exactly two", (long long)n, (long long)(4 * g));
+        }
+    }
+  }
+  if (d->nnz < 0 || d->nnz > 0x7FFFFFFFLL) return fail(CL_ESIZE, "nnz out of range");
+  if (d->nnz > 0) {
+    if (!d->csr_row_ptr || !d->csr_col || !d->csr_val) return fail(CL_EINVAL, "CSR arrays are NULL");
+    if (d->csr_row_ptr[0] != 0 || d->csr_row_ptr[N] != d->nnz)
+      return fail(CL_EINVAL, "CSR row_ptr must start at 0 and end at nnz");
+    for (int64_t n = 0; n < N; ++n) {
+      const int64_t a = d->csr_row_ptr[n], b = d->csr_row_ptr[n + 1];
+      if (b < a) return fail(CL_EINVAL, "CSR row_ptr decreases at row %lld", (long long)n);
+      for (int64_t p = a; p < b; ++p) {
+        const int32_t c = d->csr_col[p];
+        if (c < 0 || c >= K) return fail(CL_EINVAL, "CSR column %d out of range in row %lld", c, (long long)n);
+        if (p > a && c <= d->csr_col[p - 1])
+          return fail(CL_EINVAL, "CSR columns of row %lld are not strictly increasing", (long long)n);
+      }
+    }
+  }
+  if (d->lr != CL_LR_NONE && d->rank > 0) {
+    if (d->rank > 4096) return fail(CL_ESIZE, "rank above 4096");
+    if (!d->L || !d->R) return fail(CL_EINVAL, "low-rank factors are NULL");
+    if (d->lr == CL_LR_INT4) {
+      if (d->group < 1) return fail(CL_EINVAL, "int4 low-rank needs group >= 1");
+      if (!d->L_scale || !d->R_scale) return fail(CL_EINVAL, "int4 low-rank needs scales");
+      const int8_t* L = static_cast<const int8_t*>(d->L);
+      const int8_t* R = static_cast<const int8_t*>(d->R);
+      for (int64_t i = 0; i < K * d->rank; ++i)
+        if (L[i] < -8 || L[i] > 7) return fail(CL_EINVAL, "L code out of range");
+      for (int64_t i = 0; i < (int64_t)d->rank * N; ++i)
+        if (R[i] < -8 || R[i] > 7) return fail(CL_EINVAL, "R code out of range");
+    }
+  } else if (d->rank < 0) {
+    return fail(CL_EINVAL, "rank must be >= 0");
+  }
+  if (d->has_clamp && !f16_is_finite_nonneg(d->act_clamp))
+    return fail(CL_EINVAL, "the clamp must be a finite, non-negative fp16 value");
+  return CL_OK;
+}
+
+void make_plan(const cl_layer_desc* d, Plan& p) {
+  const KindInfo ki = kind_info(d->dense, d->mask);
+  p.K = d->K;
+  p.N = d->N;
+  p.n_tiles = ceil_div(p.N, kTileRows);
+  p.Npad = p.n_tiles * kTileRows;
+  p.span = ki.span;
+  p.chunks = ceil_div(p.K, ki.span);
+  p.meta_cb = ki.meta_chunk_bytes;
+  p.tab_entries = ki.table_entries;
+  p.nnz = d->nnz;
+  const bool has_lr = d->lr != CL_LR_NONE && d->rank > 0;
+  p.rank = has_lr ? d->rank : 0;
+  p.group = d->lr == CL_LR_INT4 ? d->group : 0;
+
+  uint64_t len[CL_SEC_COUNT] = {};
+  const bool bitmap = d->mask == CL_MASK_BITMAP;
+  if (bitmap) {
+    p.nz_count.assign(p.N, 0);
+    p.nz_off.assign(p.N + 1, 0);
+    int64_t off = 0, kept = 0;
+    for (int64_t n = 0; n < p.N; ++n) {
+      int64_t c = 0;
+      for (int64_t k = 0; k < p.K; ++k) c += d->keep[n * p.K + k] != 0;
+      p.nz_count[n] = c;
+      kept += c;
+      p.nz_off[n] = off;
+      off += round_up(c, 16);
+    }
+    p.nz_off[p.N] = off;
+    len[CL_SEC_DENSE] = off + 64;  // slack: a lane's 16-byte loads may run past its row
+    len[CL_SEC_META] = p.n_tiles * p.chunks * kTileRows * p.meta_cb;
+    len[CL_SEC_NZOFF] = (p.N + 1) * 4;
+    p.acct.codes = kept;
+    p.acct.mask_meta = p.N * ceil_div(p.K, 32) * 4 + (p.N + 1) * 4;
+  } else {
+    len[CL_SEC_DENSE] = p.n_tiles * p.chunks * kTileRows * kChunkBytes;
+    if (p.meta_cb) len[CL_SEC_META] = p.n_tiles * p.chunks * kTileRows * p.meta_cb;
+    switch (d->dense) {
+      case CL_DENSE_LUT3: p.acct.codes = p.N * ceil_div(p.K, 10) * 4; break;
+      case CL_DENSE_LUT4: p.acct.codes = p.N * ceil_div(p.K, 8) * 4; break;
+      case CL_DENSE_INT4:
+        if (d->mask == CL_MASK_2_4) {
+          p.acct.codes = p.N * (p.K / 2) / 2;     // kept values, 4 bits each
+          p.acct.mask_meta = p.N * (p.K / 2) / 4; // 2 bits per kept value
+        } else {
+          p.acct.codes = p.N * ceil_div(p.K, 8) * 4;
+        }
+        break;
+      case CL_DENSE_INT8: p.acct.codes = p.N * p.K; break;
+    }
+  }
+  len[CL_SEC_TABLE] = p.tab_entries ? p.Npad * p.tab_entries * 2 : p.Npad * 2;
+  p.acct.lut_or_scale = p.tab_entries ? p.N * p.tab_entries * 2 : p.N * 2;
+  if (p.nnz > 0) {
+    len[CL_SEC_ROWPTR] = (p.N + 1) * 4;
+    len[CL_SEC_COL] = p.nnz * 4;
+    len[CL_SEC_VAL] = p.nnz * 2;
+    p.acct.csr = 6 * p.nnz + 4 * (p.N + 1);
+  }
+  if (p.rank) {
+    const int64_t r = p.rank;
+    if (d->lr == CL_LR_INT4) {
+      p.lr_half_r = ceil_div(r, 2);
+      len[CL_SEC_L] = p.K * p.lr_half_r;
+      len[CL_SEC_R] = r * (p.Npad / 2);
+      len[CL_SEC_LSCALE] = ceil_div(p.K, p.group) * r * 2;
+      len[CL_SEC_RSCALE] = ceil_div(r, p.group) * p.Npad * 2;
+      p.acct.lowrank = ceil_div(p.K * r, 2) + 2 * ceil_div(p.K, p.group) * r + ceil_div(r * p.N, 2) +
+                       2 * ceil_div(r, p.group) * p.N;
+    } else {
+      len[CL_SEC_L] = p.K * r * 2;
+      len[CL_SEC_R] = r * p.Npad * 2;
+      p.acct.lowrank = 2 * (p.K * r + r * p.N);
+    }
+  }
+  uint64_t off = round_up(sizeof(cl_blob_header), 256);
+  uint64_t dev_total = 0;
+  for (int s = 0; s < CL_SEC_COUNT; ++s) {
+    if (!len[s]) continue;
+    p.off[s] = off;
+    p.len[s] = len[s];
+    off = round_up(off + len[s], 256);
+    dev_total += len[s];
+  }
+  p.total = off;
+  p.acct.total = p.acct.codes + p.acct.lut_or_scale + p.acct.mask_meta + p.acct.csr + p.acct.lowrank;
+  // every device byte of the packed sections that the canonical count does not include
+  const uint64_t canon_dev = p.acct.total - (bitmap ? 0 : 0);
+  p.acct.device_padding = dev_total > canon_dev ? dev_total - canon_dev : 0;
+}
+
+template <class F>
+void parallel_for(int64_t n, F f) {
+  unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  if (n < 4 * (int64_t)nt || nt == 1) {
+    for (int64_t i = 0; i < n; ++i) f(i);
+    return;
+  }
+  std::vector<std::thread> th;
+  for (unsigned t = 0; t < nt; ++t)
+    th.emplace_back([&, t] {
+      for (int64_t i = t; i < n; i += nt) f(i);
+    });
+  for (auto& x : th) x.join();
+}
+
+void pack_dense(const cl_layer_desc* d, const Plan& p, uint8_t* blob) {
+  const int64_t K = p.K, N = p.N, C = p.chunks;
+  uint8_t* dense = blob + p.off[CL_SEC_DENSE];
+  uint8_t* meta = p.len[CL_SEC_META] ? blob + p.off[CL_SEC_META] : nullptr;
+  auto chunk_ptr = [&](uint8_t* base, int64_t tile, int64_t c, int64_t lane, int64_t cb) {
+    return base + ((tile * C + c) * kTileRows + lane) * cb;
+  };
+  parallel_for(N, [&](int64_t n) {
+    const int64_t tile = n / kTileRows, lane = n % kTileRows;
+    if (d->dense == CL_DENSE_LUT3) {
+      const uint8_t* row = d->codes + n * K;
+      auto code = [&](int64_t k) -> uint32_t { return k < K ? row[k] : 0u; };
+      for (int64_t c = 0; c < C; ++c) {
+        uint32_t* w = reinterpret_cast<uint32_t*>(chunk_ptr(dense, tile, c, lane, 16));
+        for (int i = 0; i < 4; ++i) {
+          const int64_t k0 = 40 * c + 10 * i;
+          uint32_t pr[5];
+          for (int j = 0; j < 5; ++j) pr[j] = code(k0 + 2 * j) | (code(k0 + 2 * j + 1) << 3);
+          w[i] = pr[0] | (pr[1] << 8) | (pr[2] << 16) | (pr[3] << 24) | ((pr[4] & 3u) << 6) |
+                 (((pr[4] >> 2) & 3u) << 14) | (((pr[4] >> 4) & 3u) << 22);
+        }
+      }
+    } else if (d->dense == CL_DENSE_LUT4) {
+      const uint8_t* row = d->codes + n * K;
+      for (int64_t c = 0; c < C; ++c) {
+        uint32_t* w = reinterpret_cast<uint32_t*>(chunk_ptr(dense, tile, c, lane, 16));
+        for (int i = 0; i < 4; ++i) {
+          uint32_t v = 0;
+          for (int t = 0; t < 8; ++t) {
+            const int64_t k = 32 * c + 8 * i + t;
+            v |= (k < K ? (uint32_t)row[k] : 0u) << (4 * t);
+          }
+          w[i] = v;
+        }
+      }
+    } else if (d->dense == CL_DENSE_INT4 && d->mask == CL_MASK_NONE) {
+      const int8_t* row = d->qvals + n * K;
+      for (int64_t c = 0; c < C; ++c) {
+        uint32_t* w = reinterpret_cast<uint32_t*>(chunk_ptr(dense, tile, c, lane, 16));
+        for (int i = 0; i < 4; ++i) {
+          uint32_t v = 0;
+          for (int t = 0; t < 8; ++t) {
+            const int64_t k = 32 * c + 8 * i + t;
+            const uint32_t u = k < K ? (uint32_t)(row[k] + 8) : 8u;
+            v |= u << ((t & 1) ? 16 + 4 * (t >> 1) : 4 * (t >> 1));
+          }
+          w[i] = v;
+        }
+      }
+    } else if (d->dense == CL_DENSE_INT4 && d->mask == CL_MASK_2_4) {
+      const int8_t* row = d->qvals + n * K;
+      const uint8_t* kp = d->keep + n * K;
+      for (int64_t c = 0; c < C; ++c) {
+        uint32_t* w = reinterpret_cast<uint32_t*>(chunk_ptr(dense, tile, c, lane, 16));
+        uint32_t* m = reinterpret_cast<uint32_t*>(chunk_ptr(meta, tile, c, lane, 8));
+        for (int g = 0; g < 16; ++g) {
+          const int64_t k0 = 64 * c + 4 * g;
+          uint32_t i0 = 0, i1 = 1, u0 = 8, u1 = 8;
+          if (k0 < K) {
+            int found = 0;
+            for (int t = 0; t < 4; ++t)
+              if (kp[k0 + t]) (found++ == 0 ? i0 : i1) = t;
+            u0 = (uint32_t)(row[k0 + i0] + 8);
+            u1 = (uint32_t)(row[k0 + i1] + 8);
+          }
+          w[g / 4] |= (u0 << (4 * (g % 4))) | (u1 << (16 + 4 * (g % 4)));
+          m[g / 8] |= (i0 | (i1 << 2)) << (4 * (g % 8));
+        }
+      }
+    } else if (d->dense == CL_DENSE_INT8 && d->mask == CL_MASK_NONE) {
+      const int8_t* row = d->qvals + n * K;
+      for (int64_t c = 0; c < C; ++c) {
+        uint8_t* b = chunk_ptr(dense, tile, c, lane, 16);
+        for (int t = 0; t < 16; ++t) {
+          const int64_t k = 16 * c + t;
+          b[t] = k < K ? (uint8_t)(row[k] + 128) : 128u;
+        }
+      }
+    } else {  // INT8 + bitmap
+      const int8_t* row = d->qvals + n * K;
+      const uint8_t* kp = d->keep + n * K;
+      int8_t* nz = reinterpret_cast<int8_t*>(dense) + p.nz_off[n];
+      int64_t j = 0;
+      for (int64_t c = 0; c < C; ++c) {
+        uint32_t* m = reinterpret_cast<uint32_t*>(chunk_ptr(meta, tile, c, lane, 16));
+        for (int t = 0; t < 128; ++t) {
+          const int64_t k = 128 * c + t;
+          if (k < K && kp[k]) {
+            m[t / 32] |= 1u << (t % 32);
+            nz[j++] = row[k];
+          }
+        }
+      }
+    }
+  });
+  if (d->mask == CL_MASK_BITMAP) {
+    int32_t* off = reinterpret_cast<int32_t*>(blob + p.off[CL_SEC_NZOFF]);
+    for (int64_t n = 0; n <= N; ++n) off[n] = (int32_t)p.nz_off[n];
+  }
+}
+
+void pack_rest(const cl_layer_desc* d, const Plan& p, uint8_t* blob) {
+  const int64_t K = p.K, N = p.N;
+  uint16_t* tab = reinterpret_cast<uint16_t*>(blob + p.off[CL_SEC_TABLE]);
+  if (p.tab_entries)
+    memcpy(tab, d->lut, N * p.tab_entries * 2);
+  else
+    memcpy(tab, d->row_scale, N * 2);
+  if (p.nnz > 0) {
+    memcpy(blob + p.off[CL_SEC_ROWPTR], d->csr_row_ptr, (N + 1) * 4);
+    memcpy(blob + p.off[CL_SEC_COL], d->csr_col, p.nnz * 4);
+    memcpy(blob + p.off[CL_SEC_VAL], d->csr_val, p.nnz * 2);
+  }
+  if (p.rank) {
+    const int64_t r = p.rank;
+    if (d->lr == CL_LR_INT4) {
+      const int8_t* L = static_cast<const int8_t*>(d->L);
+      const int8_t* R = static_cast<const int8_t*>(d->R);
+      uint8_t* Lp = blob + p.off[CL_SEC_L];
+      uint8_t* Rp = blob + p.off[CL_SEC_R];
+      for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < r; ++j)
+          Lp[k * p.lr_half_r + j / 2] |= (uint8_t)((L[k * r + j] + 8) << (4 * (j & 1)));
+      for (int64_t j = 0; j < r; ++j)
+        for (int64_t n = 0; n < p.Npad; ++n) {
+          const uint32_t u = n < N ? (uint32_t)(R[j * N + n] + 8) : 8u;
+          Rp[j * (p.Npad / 2) + n / 2] |= (uint8_t)(u << (4 * (n & 1)));
+        }
+      memcpy(blob + p.off[CL_SEC_LSCALE], d->L_scale, ceil_div(K, p.group) * r * 2);
+      uint16_t* Rs = reinterpret_cast<uint16_t*>(blob + p.off[CL_SEC_RSCALE]);
+      for (int64_t g = 0; g < ceil_div(r, p.group); ++g) memcpy(Rs + g * p.Npad, d->R_scale + g * N, N * 2);
+    } else {
+      memcpy(blob + p.off[CL_SEC_L], d->L, K * r * 2);
+      uint16_t* Rp = reinterpret_cast<uint16_t*>(blob + p.off[CL_SEC_R]);
+      const uint16_t* R = static_cast<const uint16_t*>(d->R);
+      for (int64_t j = 0; j < r; ++j) memcpy(Rp + j * p.Npad, R + j * N, N * 2);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace cl
+
+using namespace cl;
+
+extern "C" cl_status cl_pack(const cl_layer_desc* d, void* blob, size_t* blob_bytes, cl_bytes* acct) {
+  clear_error();
+  if (!blob_bytes) return fail(CL_EINVAL, "blob_bytes is NULL");
+  cl_status st = validate(d);
+  if (st != CL_OK) return st;
+  Plan p;
+  make_plan(d, p);
+  if (acct) *acct = p.acct;
+  if (!blob) {
+    *blob_bytes = p.total;
+    return CL_OK;
+  }
+  if (reinterpret_cast<uintptr_t>(blob) % 16) return fail(CL_EINVAL, "blob must be 16-byte aligned");
+  if (*blob_bytes < p.total) {
+    const size_t cap = *blob_bytes;
+    *blob_bytes = p.total;
+    return fail(CL_ENOMEM, "blob needs %zu bytes, got %zu", (size_t)p.total, cap);
+  }
+  uint8_t* b = static_cast<uint8_t*>(blob);
+  memset(b, 0, p.total);
+  cl_blob_header* h = reinterpret_cast<cl_blob_header*>(b);
+  h->magic = CL_BLOB_MAGIC;
+  h->version = CL_BLOB_VERSION;
+  h->K = d->K;
+  h->N = d->N;
+  h->dense = d->dense;
+  h->mask = d->mask;
+  h->lr = p.rank ? d->lr : CL_LR_NONE;
+  h->rank = (int32_t)p.rank;
+  h->group = (int32_t)p.group;
+  h->x_dtype = d->x_dtype;
+  h->has_clamp = d->has_clamp ? 1 : 0;
+  h->act_clamp = d->has_clamp ? d->act_clamp : 0;
+  h->n_tiles = (int32_t)p.n_tiles;
+  h->chunks = (int32_t)p.chunks;
+  h->span = (int32_t)p.span;
+  h->meta_chunk_bytes = (int32_t)p.meta_cb;
+  h->nnz = p.nnz;
+  h->total_bytes = p.total;
+  for (int s = 0; s < CL_SEC_COUNT; ++s) {
+    h->off[s] = p.off[s];
+    h->len[s] = p.len[s];
+  }
+  h->acct = p.acct;
+  pack_dense(d, p, b);
+  pack_rest(d, p, b);
+  *blob_bytes = p.total;
+  return CL_OK;
+}
+
+extern "C" const char* cl_last_error(void) { return g_err.c_str(); }

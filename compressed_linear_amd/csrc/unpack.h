@@ -1,0 +1,249 @@
+// unpack.h -- device functions that turn packed chunks into fp16 weight pairs.
+//
+// One lane owns one row of a 64-row tile.  Every function here returns the
+// dequantised weights of one chunk of that row as `uint32_t` words, each the
+// bit pattern of two fp16 values (low half = even k, high half = odd k), so
+// that the forward can multiply them with pairs of activations and the debug
+// kernel can store them.  The forward, the debug kernel and the prefill
+// dequantiser all call these same functions.
+//
+// LUT lookups go through tables in LDS laid out "lane-interleaved": entry e of
+// lane l is the dword at byte address e*256 + l*4.  The 64 lanes of a
+// wavefront then always hit 64 distinct banks (dword l of each 256-byte row),
+// whatever codes they look up, and the address is built with one v_perm_b32:
+// the code (or code pair) byte goes into address byte 1, the lane offset
+// l*4 stays in byte 0.  This needs the table to start at LDS address 0, so
+// every kernel that uses these tables declares exactly one __shared__ array.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cl {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+}
+
+__device__ __forceinline__ uint32_t lds_u32(uint32_t byte_addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
+      static_cast<uintptr_t>(byte_addr));
+}
+__device__ __forceinline__ uint32_t lds_u16(uint32_t byte_addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(
+      static_cast<uintptr_t>(byte_addr));
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 lds_u64(uint32_t byte_addr) {
+  const u32x2 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+      static_cast<uintptr_t>(byte_addr));
+  return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// address byte 1 <- byte `i` of `src`; bytes 0, 2, 3 from `lanebase`
+template <int I>
+__device__ __forceinline__ uint32_t addr_from_byte(uint32_t src, uint32_t lanebase) {
+  return perm(src, lanebase, 0x03020000u | ((4u + I) << 8));
+}
+
+// ---------------------------------------------------------------------------
+// 3-bit LUT: pair table.  Entry (a | b << 3) holds fp16 lut[a] (low) and
+// lut[b] (high): one lookup dequantises two consecutive weights.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lut3_word(uint32_t w, uint32_t lanebase, uint32_t out[5]) {
+  const uint32_t m = w & 0x3F3F3F3Fu;
+  // p4 is split over bits 6-7 of bytes 0..2; one 24-bit multiply gathers the
+  // three 2-bit pieces into bits 24..29 (the partial products do not overlap).
+  const uint32_t p4 = __umul24(w & 0x00C0C0C0u, 0x41040u);
+  out[0] = lds_u32(addr_from_byte<0>(m, lanebase));
+  out[1] = lds_u32(addr_from_byte<1>(m, lanebase));
+  out[2] = lds_u32(addr_from_byte<2>(m, lanebase));
+  out[3] = lds_u32(addr_from_byte<3>(m, lanebase));
+  out[4] = lds_u32(addr_from_byte<3>(p4, lanebase));
+}
+
+// ---------------------------------------------------------------------------
+// 4-bit LUT: single-code table, entry c = fp16 lut[c] in the low half.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lut4_word(uint32_t w, uint32_t lanebase, uint32_t out[4]) {
+  const uint32_t ev = w & 0x0F0F0F0Fu;         // codes of even k, one per byte
+  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // codes of odd k
+  uint32_t lo[4], hi[4];
+  lo[0] = lds_u16(addr_from_byte<0>(ev, lanebase));
+  hi[0] = lds_u16(addr_from_byte<0>(od, lanebase));
+  lo[1] = lds_u16(addr_from_byte<1>(ev, lanebase));
+  hi[1] = lds_u16(addr_from_byte<1>(od, lanebase));
+  lo[2] = lds_u16(addr_from_byte<2>(ev, lanebase));
+  hi[2] = lds_u16(addr_from_byte<2>(od, lanebase));
+  lo[3] = lds_u16(addr_from_byte<3>(ev, lanebase));
+  hi[3] = lds_u16(addr_from_byte<3>(od, lanebase));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[j] = perm(hi[j], lo[j], 0x05040100u);
+}
+
+// ---------------------------------------------------------------------------
+// Integers to fp16 without a convert: 0x6400 | u is the fp16 value 1024 + u
+// for 0 <= u < 1024, so subtracting the bias (1024 + offset) gives q exactly.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t int4_pair(uint32_t w, int shift) {
+  const uint32_t b = ((w >> shift) & 0x000F000Fu) | 0x64006400u;  // 1024 + u, u = q + 8
+  const half2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  return as_u32(as_h2(b) - bias);
+}
+
+__device__ __forceinline__ void int4_word(uint32_t w, uint32_t out[4]) {
+  out[0] = int4_pair(w, 0);
+  out[1] = int4_pair(w, 4);
+  out[2] = int4_pair(w, 8);
+  out[3] = int4_pair(w, 12);
+}
+
+__device__ __forceinline__ void int8_word(uint32_t w, uint32_t out[2]) {
+  const half2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};      // 1024 + 128
+  out[0] = as_u32(as_h2(perm(0x64646464u, w, 0x04010400u)) - bias);  // bytes 0, 1
+  out[1] = as_u32(as_h2(perm(0x64646464u, w, 0x04030402u)) - bias);  // bytes 2, 3
+}
+
+// 2:4 group: kept pair Q = (v0, v1) and the selector entry for its meta nibble
+// expand into the four weights of the group (two fp16 pairs); positions not
+// kept read selector value 12, which v_perm turns into a zero byte.
+__device__ __forceinline__ void int4_24_group(uint32_t vw, int g4, uint32_t meta_word, int g8,
+                                              uint32_t seltab_base, uint32_t out[2]) {
+  const uint32_t q = int4_pair(vw, 4 * g4);
+  const uint32_t nib = (meta_word >> (4 * g8)) & 0xFu;
+  const uint2 sel = lds_u64(seltab_base + nib * 8u);
+  out[0] = perm(q, q, sel.x);
+  out[1] = perm(q, q, sel.y);
+}
+
+// Selector table of the 2:4 expansion (16 entries x 2 dwords); nibble = i0 | i1 << 2.
+__device__ __forceinline__ uint2 seltab_2_4_entry(uint32_t nib) {
+  const uint32_t i0 = nib & 3u, i1 = nib >> 2;
+  uint32_t bytes[4];
+#pragma unroll
+  for (uint32_t p = 0; p < 4; ++p) {
+    // selector bytes of fp16 position p: Q bytes (0,1) for the first kept,
+    // (2,3) for the second, (12,12) -> zero when p is dropped
+    bytes[p] = (p == i0) ? 0x0100u : (p == i1 && i1 != i0) ? 0x0302u : 0x0C0Cu;
+  }
+  return make_uint2(bytes[0] | (bytes[1] << 16), bytes[2] | (bytes[3] << 16));
+}
+
+// Nibble selector of the bitmap expansion: byte p of the entry is the rank of
+// weight p among the kept weights of the nibble, or 12 (zero) if p is dropped.
+__device__ __forceinline__ uint32_t bitmap_sel_entry(uint32_t nib) {
+  uint32_t r = 0, sel = 0;
+#pragma unroll
+  for (uint32_t p = 0; p < 4; ++p) {
+    const bool kept = (nib >> p) & 1u;
+    sel |= (kept ? r : 12u) << (8 * p);
+    r += kept;
+  }
+  return sel;
+}
+
+// Four signed int8 weights (dropped ones already zero) to two fp16 pairs.
+__device__ __forceinline__ void int8x4_signed(uint32_t d4, uint32_t out[2]) {
+  int8_word(d4 ^ 0x80808080u, out);
+}
+
+
+// ---------------------------------------------------------------------------
+// Per-kind chunk dequantisation (shared by the forward, the debug kernel and
+// the prefill tile loader).
+// ---------------------------------------------------------------------------
+enum Kind { K_LUT3 = 0, K_LUT4, K_INT4, K_INT4_24, K_INT8, K_INT8_BM };
+
+// Bitmap expansion: 16 nibble selectors, then one staging slot per dense lane
+// of 35 dwords (odd stride: the 64 lanes fall in distinct banks); a slot holds
+// the <= 128 kept bytes of one chunk plus alignment slack.
+constexpr int kBmSlot = 35;
+constexpr int kBmSelDwords = 16;
+
+template <int KIND>
+struct KindTraits;
+template <> struct KindTraits<K_LUT3> { static constexpr int span = 40, pairs = 20, tab_dwords = 64 * 64; };
+template <> struct KindTraits<K_LUT4> { static constexpr int span = 32, pairs = 16, tab_dwords = 16 * 64; };
+template <> struct KindTraits<K_INT4> { static constexpr int span = 32, pairs = 16, tab_dwords = 0; };
+template <> struct KindTraits<K_INT4_24> { static constexpr int span = 64, pairs = 32, tab_dwords = 32; };
+template <> struct KindTraits<K_INT8> { static constexpr int span = 16, pairs = 8, tab_dwords = 0; };
+template <> struct KindTraits<K_INT8_BM> { static constexpr int span = 128, pairs = 64, tab_dwords = kBmSelDwords + 4 * 64 * kBmSlot; };
+
+// Dequantise one chunk of this lane's row into fp16 pairs wp[j] = (k = 2j, 2j+1).
+//   w          the 16-byte chunk of the dense stream (bitmap: the keep bits)
+//   mw         2:4 metadata (x, y) of the chunk
+//   lanebase   lane * 4 (LUT tables), slot_base: byte address of the lane's
+//              staged kept values (bitmap), already offset to the first one
+template <int KIND>
+__device__ __forceinline__ void chunk_pairs(uint4 w, uint4 mw, uint32_t lanebase, uint32_t slot_base,
+                                            uint32_t (&wp)[KindTraits<KIND>::pairs]) {
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  if constexpr (KIND == K_LUT3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lut3_word(ww[i], lanebase, &wp[5 * i]);
+  } else if constexpr (KIND == K_LUT4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lut4_word(ww[i], lanebase, &wp[4 * i]);
+  } else if constexpr (KIND == K_INT4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) int4_word(ww[i], &wp[4 * i]);
+  } else if constexpr (KIND == K_INT4_24) {
+    const uint32_t mm[2] = {mw.x, mw.y};
+#pragma unroll
+    for (int g = 0; g < 16; ++g) int4_24_group(ww[g / 4], g % 4, mm[g / 8], g % 8, 0u, &wp[2 * g]);
+  } else if constexpr (KIND == K_INT8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) int8_word(ww[i], &wp[2 * i]);
+  } else {
+    uint32_t off = slot_base;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t nib = (ww[i] >> (4 * t)) & 0xFu;
+        const uint32_t lo = lds_u32(off & ~3u), hi = lds_u32((off & ~3u) + 4u);
+        const uint32_t win = __builtin_amdgcn_alignbyte(hi, lo, off & 3u);
+        const uint32_t d4 = perm(0u, win, lds_u32(nib * 4u));
+        int8x4_signed(d4, &wp[16 * i + 2 * t]);
+        off += __builtin_popcount(nib);
+      }
+    }
+  }
+}
+
+// LDS tables of a 64-row tile, built by `nthreads` threads (>= 64, a multiple of 64):
+// LUT pair / single tables at address 0, or the selector tables.
+template <int KIND>
+__device__ __forceinline__ void build_tables(uint32_t* smem, const uint16_t* table, int tile, int tid, int nthreads) {
+  const int lane = tid & 63, grp = tid >> 6, ngrp = nthreads >> 6;
+  const int n = tile * 64 + lane;
+  if constexpr (KIND == K_LUT3) {
+    const uint4 lv = reinterpret_cast<const uint4*>(table)[n];
+    const uint32_t lw[4] = {lv.x, lv.y, lv.z, lv.w};
+    for (int i = grp; i < 64; i += ngrp) {
+      const int ca = i & 7, cb = i >> 3;
+      const uint32_t va = (lw[ca >> 1] >> (16 * (ca & 1))) & 0xFFFFu;
+      const uint32_t vb = (lw[cb >> 1] >> (16 * (cb & 1))) & 0xFFFFu;
+      smem[i * 64 + lane] = va | (vb << 16);
+    }
+  } else if constexpr (KIND == K_LUT4) {
+    const uint4 l0 = reinterpret_cast<const uint4*>(table)[2 * n];
+    const uint4 l1 = reinterpret_cast<const uint4*>(table)[2 * n + 1];
+    const uint32_t lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+    for (int c = grp; c < 16; c += ngrp) smem[c * 64 + lane] = (lw[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
+  } else if constexpr (KIND == K_INT4_24) {
+    if (tid < 16) {
+      const uint2 e = seltab_2_4_entry((uint32_t)tid);
+      smem[2 * tid] = e.x;
+      smem[2 * tid + 1] = e.y;
+    }
+  } else if constexpr (KIND == K_INT8_BM) {
+    if (tid < 16) smem[tid] = bitmap_sel_entry((uint32_t)tid);
+  }
+}
+
+}  // namespace cl

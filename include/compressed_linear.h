@@ -1,0 +1,256 @@
+/*
+ * compressed_linear.h -- C ABI of the MI355X (gfx950) compressed linear layer.
+ *
+ * The operation is the forward of one linear layer whose weight is stored
+ * compressed:
+ *
+ *     y[m, n] = sum_k x'[m, k] * W_hat[n, k]        W_hat = D + S + (L_hat R_hat)^T
+ *
+ *   D      dense low-bit part, one row per output channel n:
+ *            - 3- or 4-bit codes into a per-row table of fp16 centroids
+ *              ("SqueezeLLM: Dense-and-Sparse Quantization", Approach: non-uniform
+ *              LUT quantization with k-means centroids);
+ *            - or symmetric int4 / int8 values times a per-row fp16 scale
+ *              ("SLiM: One-shot Quantization and Sparsity with Low-rank
+ *              Approximation for LLM Weight Compression", review highlights,
+ *              SLiM-Quant: symmetric quantization, round to nearest);
+ *            optionally under a 2:4 semi-structured or an unstructured mask
+ *            (SLiM page, rebuttal "Unstructured vs. 2:4 Sparsity";
+ *            "Compressing Large Language Models by Joint Sparsification and
+ *            Quantization", Approach).
+ *   S      outliers in CSR with fp16 values (SqueezeLLM page, Approach: the
+ *          top-sensitivity and outlier weights, 0.45% in total, in a
+ *          full-precision sparse matrix).
+ *   L, R   low-rank correction (SLiM page, review highlights, SLiM-LoRA), fp16,
+ *          bf16, or int4 with AbsMax group quantization, group 128 (SLiM page,
+ *          review highlights, "Low-rank adapter quantization").
+ *   x'     activations, clamped to [-c, c] when the layer carries a clamp c
+ *          (JSQ page, Approach: activation editor with a per-layer strength).
+ *
+ * Conventions for every entry point:
+ *   - Status codes are returned; nothing throws across the ABI.  The message of
+ *     the last failure on the calling thread is returned by cl_last_error().
+ *   - "host" pointers are CPU memory the caller owns; "device" pointers are GPU
+ *     memory the caller owns (PyTorch allocates it in the Python binding).
+ *     The library never frees caller memory and keeps no pointer to host
+ *     arrays after a call returns.
+ *   - Streams are hipStream_t values passed as void*; NULL means the default
+ *     stream.  GPU work is asynchronous on that stream.
+ *   - Every array is row-major and contiguous.  fp16 and bf16 values are
+ *     passed as their uint16 bit patterns.
+ */
+#ifndef COMPRESSED_LINEAR_H
+#define COMPRESSED_LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CL_OK = 0,
+  CL_EINVAL = -1,        /* malformed argument or layer description */
+  CL_EUNSUPPORTED = -2,  /* valid, but a combination this library does not build */
+  CL_ENOMEM = -3,        /* a caller buffer is too small */
+  CL_EHIP = -4,          /* a HIP runtime call or kernel launch failed */
+  CL_ESIZE = -5          /* a size exceeds the supported limits */
+} cl_status;
+
+typedef enum { CL_DENSE_LUT3 = 0, CL_DENSE_LUT4 = 1, CL_DENSE_INT4 = 2, CL_DENSE_INT8 = 3 } cl_dense_kind;
+typedef enum { CL_MASK_NONE = 0, CL_MASK_2_4 = 1, CL_MASK_BITMAP = 2 } cl_mask_kind;
+typedef enum { CL_LR_NONE = 0, CL_LR_FP16 = 1, CL_LR_BF16 = 2, CL_LR_INT4 = 3 } cl_lr_kind;
+typedef enum { CL_ACT_F16 = 0, CL_ACT_BF16 = 1 } cl_act_dtype;
+typedef enum { CL_PATH_AUTO = 0, CL_PATH_DECODE = 1, CL_PATH_PREFILL = 2 } cl_path;
+
+/*
+ * Logical (unpacked) description of one layer.  All pointers are host
+ * pointers to arrays the caller owns; they are read only during cl_pack.
+ * W_hat is [N, K]: N = out_features (rows), K = in_features.
+ *
+ *   dense = LUT3 / LUT4 : codes [N*K] uint8 in 0..2^b-1; lut [N * 2^b] fp16 bits,
+ *                         the table of row n at lut[n * 2^b].
+ *   dense = INT4 / INT8 : qvals [N*K] int8 (INT4: -8..7, INT8: -127..127);
+ *                         row_scale [N] fp16 bits; D[n,k] = qvals[n,k] * row_scale[n].
+ *   mask  = 2_4         : keep [N*K] 0/1, exactly two kept in each group of four
+ *                         consecutive k (K % 4 == 0).  INT4 and INT8 only.
+ *   mask  = BITMAP      : keep [N*K] 0/1, any pattern.  INT4 and INT8 only.
+ *                         qvals at dropped positions are ignored.
+ *   CSR                 : csr_row_ptr [N+1] int32 (row_ptr[0] = 0, nondecreasing,
+ *                         row_ptr[N] = nnz), csr_col [nnz] int32 strictly
+ *                         increasing within a row and < K, csr_val [nnz] fp16 bits.
+ *                         nnz may be 0 (then the three pointers may be NULL).
+ *   lr    = FP16 / BF16 : L [K*rank], R [rank*N] uint16 bit patterns.
+ *   lr    = INT4        : L, R int8 codes in -8..7; L_scale [ceil(K/group) * rank]
+ *                         (groups of `group` consecutive k per rank column),
+ *                         R_scale [ceil(rank/group) * N] (groups along the rank
+ *                         axis per output column), fp16 bits.
+ *   has_clamp, act_clamp: x' = min(max(x, -c), c) with c = act_clamp (fp16 bits, c >= 0).
+ *   x_dtype             : element type of x in cl_forward (fp16 or bf16).
+ */
+typedef struct {
+  int32_t K, N;
+  int32_t dense;            /* cl_dense_kind */
+  int32_t mask;             /* cl_mask_kind */
+  const uint8_t* codes;
+  const uint16_t* lut;
+  const int8_t* qvals;
+  const uint16_t* row_scale;
+  const uint8_t* keep;
+  int64_t nnz;
+  const int32_t* csr_row_ptr;
+  const int32_t* csr_col;
+  const uint16_t* csr_val;
+  int32_t lr;               /* cl_lr_kind */
+  int32_t rank;
+  int32_t group;
+  const void* L;
+  const void* R;
+  const uint16_t* L_scale;
+  const uint16_t* R_scale;
+  int32_t has_clamp;
+  uint16_t act_clamp;
+  uint16_t reserved0;
+  int32_t x_dtype;          /* cl_act_dtype */
+} cl_layer_desc;
+
+/*
+ * Canonical byte accounting of a packed layer: what the method must move per
+ * forward, independent of device padding.
+ *   codes        LUT3: N*ceil(K/10)*4 (ten 3-bit codes per 32-bit word, each row
+ *                starting a new word); LUT4 / INT4: N*ceil(K/8)*4; INT8: N*K;
+ *                masked INT: the kept values only (2:4: N*K/2 values).
+ *   lut_or_scale N * 2^b * 2 (LUT) or N * 2 (per-row scales)
+ *   mask_meta    2:4: 2 bits per kept value (N*K/8 bytes); BITMAP: N*ceil(K/32)*4
+ *                bitmap words plus (N+1)*4 bytes of nonzero offsets.
+ *   csr          6*nnz + 4*(N+1)
+ *   lowrank      factor bytes (2 per value; int4: 1/2 per value) plus scales
+ *   total        the sum of the above
+ *   device_padding  extra bytes of the device layout (row and tile padding),
+ *                   not part of `total`.
+ */
+typedef struct {
+  uint64_t codes, lut_or_scale, mask_meta, csr, lowrank, total;
+  uint64_t device_padding;
+} cl_bytes;
+
+/*
+ * cl_pack -- validate a layer description and lay it out for the device.
+ *   desc        host, read only.
+ *   blob        host output buffer of *blob_bytes bytes, 16-byte aligned; NULL
+ *               asks for the size only.
+ *   blob_bytes  in: capacity of blob; out: bytes needed / written.
+ *   acct        host, optional (NULL): canonical byte accounting.
+ * Host only; never touches a GPU.  Errors: CL_EINVAL for malformed input
+ * (shapes, code or value ranges, a 2:4 group without exactly two kept, CSR
+ * pointers not nondecreasing, columns out of range, unsorted or repeated),
+ * CL_EUNSUPPORTED for combinations not built (a mask on a LUT format, a
+ * 2:4 mask with K % 4 != 0), CL_ESIZE for dimensions above 2^24 or
+ * nnz above 2^31 - 1, CL_ENOMEM if *blob_bytes is too small.
+ * The blob is self-describing (it starts with a cl_blob_header) and may be
+ * saved and reloaded byte for byte.
+ */
+cl_status cl_pack(const cl_layer_desc* desc, void* blob, size_t* blob_bytes, cl_bytes* acct);
+
+/*
+ * cl_device_bytes -- device memory (bytes) that cl_create needs for `blob`
+ * with forwards of up to max_M activation rows: the packed layer plus the
+ * workspace (split-K partial sums, counters, the low-rank intermediate
+ * x' L_hat).  Returns 0 if the blob is malformed or max_M < 1.
+ */
+size_t cl_device_bytes(const void* blob, int32_t max_M);
+
+/*
+ * cl_create -- upload a packed layer to the current HIP device.
+ *   blob      host, read during the call (the copy is synchronised before
+ *             return, so the caller may free it afterwards).
+ *   dev_buf   device, at least cl_device_bytes(blob, max_M) bytes, 256-byte
+ *             aligned, owned by the caller, must outlive the handle.
+ *   max_M     largest M a later cl_forward will pass.
+ *   stream    hipStream_t for the upload and the workspace clear.
+ *   handle    out: opaque handle (host memory owned by the library).
+ * Errors: CL_EINVAL (malformed blob, NULL or misaligned pointers),
+ * CL_ENOMEM (dev_bytes too small), CL_EHIP (copy failed).
+ */
+cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes, int32_t max_M,
+                    void* stream, void** handle);
+
+/*
+ * cl_forward -- y = x' W_hat^T for M rows of activations.
+ *   x_dev  device, [M, K] fp16 or bf16 (the layer's x_dtype), 16-byte aligned.
+ *   y_dev  device, [M, N] fp32, overwritten, 16-byte aligned.
+ *   1 <= M <= max_M.  M <= 32 runs the decode kernels (VALU, bandwidth
+ *   bound at small M); larger M runs the prefill kernels (bf16 MFMA).
+ * One forward at a time per handle (the workspace inside dev_buf is shared).
+ * Deterministic: the same inputs give bitwise identical y.
+ * Errors: CL_EINVAL (M out of range, NULL or misaligned pointers),
+ * CL_EHIP (launch failure).
+ */
+cl_status cl_forward(void* handle, int32_t M, const void* x_dev, float* y_dev, void* stream);
+
+/* cl_forward with an explicit path (cl_path); CL_PATH_AUTO behaves as cl_forward.
+ * CL_PATH_DECODE requires M <= 32. */
+cl_status cl_forward_path(void* handle, int32_t M, const void* x_dev, float* y_dev,
+                          void* stream, int32_t path);
+
+/*
+ * cl_debug_dequant -- write the dequantised parts of W_hat with the same
+ * unpacking device code the forward uses (a parity aid; not timed).
+ *   D16  device, [N, K] fp16: D, zero where masked (integer formats: q*s
+ *        rounded once to fp16, nearest-even).
+ *   S16  device, [N, K] fp16: the CSR outliers at their positions, else 0.
+ *   L32  device, [K, rank] fp32 and R32 device, [rank, N] fp32 (exact); may
+ *        be NULL, and are ignored for a layer without a low-rank part.
+ * Errors: CL_EINVAL (NULL D16 / S16), CL_EHIP.
+ */
+cl_status cl_debug_dequant(void* handle, uint16_t* D16, uint16_t* S16, float* L32, float* R32,
+                           void* stream);
+
+/* cl_destroy -- free the host handle.  The caller frees dev_buf afterwards. */
+cl_status cl_destroy(void* handle);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* cl_last_error(void);
+
+/*
+ * Header at the start of every packed blob (little endian).  Exposed so that
+ * tools can inspect a blob; the section layouts are documented with the
+ * packer.
+ */
+#define CL_BLOB_MAGIC 0x31424C43u /* "CLB1" */
+#define CL_BLOB_VERSION 1u
+enum {
+  CL_SEC_DENSE = 0,   /* tile-interleaved dense stream */
+  CL_SEC_TABLE,       /* LUT [Npad * 2^b] fp16 or row scales [Npad] fp16 */
+  CL_SEC_META,        /* 2:4 metadata or bitmap words, tile-interleaved */
+  CL_SEC_NZOFF,       /* BITMAP: int32 [N+1] start of each row's kept values */
+  CL_SEC_ROWPTR,      /* CSR row_ptr int32 [N+1] */
+  CL_SEC_COL,         /* CSR col int32 [nnz] */
+  CL_SEC_VAL,         /* CSR val fp16 [nnz] */
+  CL_SEC_L,           /* low-rank L */
+  CL_SEC_R,           /* low-rank R */
+  CL_SEC_LSCALE,      /* int4 L scales */
+  CL_SEC_RSCALE,      /* int4 R scales */
+  CL_SEC_COUNT = 16
+};
+typedef struct {
+  uint32_t magic, version;
+  int32_t K, N, dense, mask, lr, rank, group, x_dtype, has_clamp;
+  uint16_t act_clamp, reserved0;
+  int32_t n_tiles;       /* ceil(N / 64) */
+  int32_t chunks;        /* 16-byte chunks per row in the dense stream */
+  int32_t span;          /* logical k covered by one chunk */
+  int32_t meta_chunk_bytes; /* bytes of META per row per chunk (0 if none) */
+  int64_t nnz;
+  uint64_t total_bytes;  /* size of the whole blob */
+  uint64_t off[CL_SEC_COUNT];
+  uint64_t len[CL_SEC_COUNT];
+  cl_bytes acct;
+  uint8_t reserved[64];
+} cl_blob_header;
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* COMPRESSED_LINEAR_H */
