@@ -144,6 +144,8 @@ def main():
     ap.add_argument("--path", default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-layer", action="store_true", help="also time each layer alone")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (reference for the byte counters)")
     a = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -159,6 +161,15 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}), flush=True)
+        return
     cfg, M = a.config, a.M
 
     log(f"building config {cfg} M={M}")

@@ -23,7 +23,9 @@ ARCH = os.environ.get("CL_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["pack.cpp", "runtime.hip", "decode.hip", "aux.hip", "prefill.hip",
            "decode_lut3.hip", "decode_lut4.hip", "decode_int4.hip", "decode_int4_24.hip",
-           "decode_int8.hip", "decode_int8_bm.hip"]
+           "decode_int8.hip", "decode_int8_bm.hip",
+           "decode_rows_lut3.hip", "decode_rows_lut4.hip", "decode_rows_int4.hip", "decode_rows_int4_24.hip",
+           "decode_rows_int8.hip"]
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

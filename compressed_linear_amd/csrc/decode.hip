@@ -1,5 +1,7 @@
-// decode.hip -- dispatch of the batch 1..32 forward to the per-kind kernels.
+// decode.hip -- dispatch of the batch 1..32 forward: the row-wise kernel for
+// M <= 4, the tile kernel for larger batches and for the bitmap format.
 #include "decode_impl.h"
+#include "decode_rows.h"
 
 namespace cl {
 
@@ -9,6 +11,12 @@ extern template hipError_t launch_decode_kind<K_INT4>(const DecodeArgs&, bool, h
 extern template hipError_t launch_decode_kind<K_INT4_24>(const DecodeArgs&, bool, hipStream_t);
 extern template hipError_t launch_decode_kind<K_INT8>(const DecodeArgs&, bool, hipStream_t);
 extern template hipError_t launch_decode_kind<K_INT8_BM>(const DecodeArgs&, bool, hipStream_t);
+
+extern template hipError_t launch_rows_kind<K_LUT3>(const RowArgs&, int, bool, hipStream_t);
+extern template hipError_t launch_rows_kind<K_LUT4>(const RowArgs&, int, bool, hipStream_t);
+extern template hipError_t launch_rows_kind<K_INT4>(const RowArgs&, int, bool, hipStream_t);
+extern template hipError_t launch_rows_kind<K_INT4_24>(const RowArgs&, int, bool, hipStream_t);
+extern template hipError_t launch_rows_kind<K_INT8>(const RowArgs&, int, bool, hipStream_t);
 
 hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream) {
 
@@ -42,6 +50,38 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
   a.lr_kind = h.lr;
   a.Npad = L.Npad;
   const bool bf16 = h.x_dtype == CL_ACT_BF16;
+  // M <= 4: row-wise kernel (bandwidth bound); the bitmap format always uses
+  // the tile kernel (its kept values are consumed per row at a varying rate)
+  if (M <= 4 && h.mask != CL_MASK_BITMAP) {
+    RowArgs r = {};
+    r.dense = a.dense;
+    r.meta = a.meta;
+    r.table = a.table;
+    r.rowptr = a.rowptr;
+    r.col = a.col;
+    r.val = a.val;
+    r.R = a.R;
+    r.Rscale = a.Rscale;
+    r.t = a.t;
+    r.x = x;
+    r.y = y;
+    r.K = a.K;
+    r.N = a.N;
+    r.M = M;
+    r.ldx = a.ldx;
+    r.chunks = a.chunks;
+    r.rank = a.rank;
+    r.group = a.group;
+    r.lr_kind = a.lr_kind;
+    switch (h.dense) {
+      case CL_DENSE_LUT3: return launch_rows_kind<K_LUT3>(r, L.Npad, bf16, stream);
+      case CL_DENSE_LUT4: return launch_rows_kind<K_LUT4>(r, L.Npad, bf16, stream);
+      case CL_DENSE_INT4:
+        return h.mask == CL_MASK_2_4 ? launch_rows_kind<K_INT4_24>(r, L.Npad, bf16, stream)
+                                     : launch_rows_kind<K_INT4>(r, L.Npad, bf16, stream);
+      default: return launch_rows_kind<K_INT8>(r, L.Npad, bf16, stream);
+    }
+  }
   switch (h.dense) {
     case CL_DENSE_LUT3: return launch_decode_kind<K_LUT3>(a, bf16, stream);
     case CL_DENSE_LUT4: return launch_decode_kind<K_LUT4>(a, bf16, stream);

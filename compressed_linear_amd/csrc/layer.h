@@ -36,11 +36,9 @@ struct Layer {
   // workspace (inside dev_buf, after the packed sections)
   uint32_t* counters = nullptr;  // [n_tiles + 1], zero between forwards
   float* part = nullptr;         // [n_tiles][split][kMaxDecodeM][64]
-  float* tpart = nullptr;        // [prologue blocks][max_M][rank]
   float* t = nullptr;            // [max_M][rank]
   uint16_t* xprep = nullptr;     // [max_M][Kx]  clamped / padded activations
   int Kx = 0;                    // row stride of xprep (even)
-  int lr_blocks = 0;             // prologue workgroups
   size_t ws_bytes = 0;
 };
 

@@ -2,15 +2,15 @@
 //
 // Shared by the host packer and the HIP runtime.  Plain C++, no HIP types.
 //
-// Rows (output channels) are grouped in tiles of 64; one wavefront lane owns
-// one row of a tile.  Every dense stream is stored tile-interleaved,
+// Every dense stream is row-major in 16-byte chunks,
 //
-//     stream[tile][chunk][lane][bytes_per_chunk],
+//     stream[row][chunk][bytes_per_chunk],
 //
-// so that the 64 lanes of a wavefront reading chunk c of their rows touch one
-// contiguous, aligned block (1 KiB for 16-byte chunks): fully coalesced
-// 128-bit loads.  A chunk covers `span` consecutive k of the row.  Rows are
-// padded to whole chunks and N to whole tiles; padding bytes are zero.
+// a chunk covering `span` consecutive k of the row.  Rows are padded to whole
+// chunks and N to whole 64-row tiles; padding bytes are zero.  A wavefront
+// whose lanes take consecutive chunks of one row issues fully coalesced
+// 128-bit loads (1 KiB per wavefront); a wavefront whose lanes take one row
+// each reads one 128-byte line per lane every eight chunks.
 //
 // Per dense kind (bit positions count from the least significant bit):
 //
@@ -18,9 +18,9 @@
 //         k = 40c + 10i + t, t = 0..9 (the same ten codes as the i-th canonical
 //         10-per-word word of the row), rearranged so that the code pair
 //         p_j = code[2j] | code[2j+1] << 3 (j = 0..4) sits in
-//           p_0..p_3 : bits 0..5 of byte j;
-//           p_4      : bits 6..7 of bytes 0, 1, 2 (two bits each, low bits first);
-//         bits 6..7 of byte 3 are zero.
+//           p_0..p_3 : bits 2..7 of byte j (so the byte reads 4 * p_j);
+//           p_4      : bits 0..1 of bytes 0, 1, 2 (two bits each, low bits first);
+//         bits 0..1 of byte 3 are zero.
 //   LUT4  span 32: word i holds codes k = 32c + 8i + t at bits 4t..4t+3
 //         (canonical order, least significant nibble first).
 //   INT4  span 32 (no mask): word i holds u = q + 8 of k = 32c + 8i + t; the
@@ -35,7 +35,7 @@
 //   INT8 + BITMAP, span 128: META (16 bytes per chunk) holds the keep bits,
 //         bit t of word i <-> k = 128c + 32i + t.  The kept values (signed
 //         int8, ascending k) of each row are contiguous in DENSE starting at
-//         NZOFF[n] (a multiple of 16), not tile-interleaved.
+//         NZOFF[n] (a multiple of 16).
 #pragma once
 #include <stdint.h>
 

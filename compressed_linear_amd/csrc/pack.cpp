@@ -144,6 +144,12 @@ cl_status validate(const cl_layer_desc* d) {
   }
   if (d->has_clamp && !f16_is_finite_nonneg(d->act_clamp))
     return fail(CL_EINVAL, "the clamp must be a finite, non-negative fp16 value");
+  if (d->has_clamp && d->x_dtype == CL_ACT_BF16) {
+    // the clamped activation -c / c must be exact in bf16 (8-bit significand)
+    const uint32_t e = (d->act_clamp >> 10) & 0x1F, m = d->act_clamp & 0x3FF;
+    if (e != 0 && (m & 7u)) return fail(CL_EUNSUPPORTED, "the clamp value is not representable in bf16");
+    if (e == 0 && m && (m >> __builtin_ctz(m)) > 0xFF) return fail(CL_EUNSUPPORTED, "the clamp value is not representable in bf16");
+  }
   return CL_OK;
 }
 
@@ -211,8 +217,8 @@ void make_plan(const cl_layer_desc* d, Plan& p) {
     const int64_t r = p.rank;
     if (d->lr == CL_LR_INT4) {
       p.lr_half_r = ceil_div(r, 2);
-      len[CL_SEC_L] = p.K * p.lr_half_r;
-      len[CL_SEC_R] = r * (p.Npad / 2);
+      len[CL_SEC_L] = r * ceil_div(p.K, 2);
+      len[CL_SEC_R] = p.Npad * p.lr_half_r;
       len[CL_SEC_LSCALE] = ceil_div(p.K, p.group) * r * 2;
       len[CL_SEC_RSCALE] = ceil_div(r, p.group) * p.Npad * 2;
       p.acct.lowrank = ceil_div(p.K * r, 2) + 2 * ceil_div(p.K, p.group) * r + ceil_div(r * p.N, 2) +
@@ -258,8 +264,9 @@ void pack_dense(const cl_layer_desc* d, const Plan& p, uint8_t* blob) {
   const int64_t K = p.K, N = p.N, C = p.chunks;
   uint8_t* dense = blob + p.off[CL_SEC_DENSE];
   uint8_t* meta = p.len[CL_SEC_META] ? blob + p.off[CL_SEC_META] : nullptr;
+  // row-major streams: chunk c of row n at (n * C + c) * chunk_bytes
   auto chunk_ptr = [&](uint8_t* base, int64_t tile, int64_t c, int64_t lane, int64_t cb) {
-    return base + ((tile * C + c) * kTileRows + lane) * cb;
+    return base + ((tile * kTileRows + lane) * C + c) * cb;
   };
   parallel_for(N, [&](int64_t n) {
     const int64_t tile = n / kTileRows, lane = n % kTileRows;
@@ -272,8 +279,8 @@ void pack_dense(const cl_layer_desc* d, const Plan& p, uint8_t* blob) {
           const int64_t k0 = 40 * c + 10 * i;
           uint32_t pr[5];
           for (int j = 0; j < 5; ++j) pr[j] = code(k0 + 2 * j) | (code(k0 + 2 * j + 1) << 3);
-          w[i] = pr[0] | (pr[1] << 8) | (pr[2] << 16) | (pr[3] << 24) | ((pr[4] & 3u) << 6) |
-                 (((pr[4] >> 2) & 3u) << 14) | (((pr[4] >> 4) & 3u) << 22);
+          w[i] = (pr[0] << 2) | (pr[1] << 10) | (pr[2] << 18) | (pr[3] << 26) | (pr[4] & 3u) |
+                 (((pr[4] >> 2) & 3u) << 8) | (((pr[4] >> 4) & 3u) << 16);
         }
       }
     } else if (d->dense == CL_DENSE_LUT4) {
@@ -368,28 +375,36 @@ void pack_rest(const cl_layer_desc* d, const Plan& p, uint8_t* blob) {
     memcpy(blob + p.off[CL_SEC_VAL], d->csr_val, p.nnz * 2);
   }
   if (p.rank) {
+    // transposed factors: L^T [r][K] and R^T [Npad][r] (see layout.h)
     const int64_t r = p.rank;
     if (d->lr == CL_LR_INT4) {
       const int8_t* L = static_cast<const int8_t*>(d->L);
       const int8_t* R = static_cast<const int8_t*>(d->R);
+      const int64_t hk = ceil_div(K, 2), gk = ceil_div(K, p.group), gr = ceil_div(r, p.group);
       uint8_t* Lp = blob + p.off[CL_SEC_L];
       uint8_t* Rp = blob + p.off[CL_SEC_R];
-      for (int64_t k = 0; k < K; ++k)
-        for (int64_t j = 0; j < r; ++j)
-          Lp[k * p.lr_half_r + j / 2] |= (uint8_t)((L[k * r + j] + 8) << (4 * (j & 1)));
       for (int64_t j = 0; j < r; ++j)
-        for (int64_t n = 0; n < p.Npad; ++n) {
+        for (int64_t k = 0; k < K; ++k) Lp[j * hk + k / 2] |= (uint8_t)((L[k * r + j] + 8) << (4 * (k & 1)));
+      for (int64_t n = 0; n < p.Npad; ++n)
+        for (int64_t j = 0; j < r; ++j) {
           const uint32_t u = n < N ? (uint32_t)(R[j * N + n] + 8) : 8u;
-          Rp[j * (p.Npad / 2) + n / 2] |= (uint8_t)(u << (4 * (n & 1)));
+          Rp[n * p.lr_half_r + j / 2] |= (uint8_t)(u << (4 * (j & 1)));
         }
-      memcpy(blob + p.off[CL_SEC_LSCALE], d->L_scale, ceil_div(K, p.group) * r * 2);
+      uint16_t* Ls = reinterpret_cast<uint16_t*>(blob + p.off[CL_SEC_LSCALE]);
+      for (int64_t g = 0; g < gk; ++g)
+        for (int64_t j = 0; j < r; ++j) Ls[j * gk + g] = d->L_scale[g * r + j];
       uint16_t* Rs = reinterpret_cast<uint16_t*>(blob + p.off[CL_SEC_RSCALE]);
-      for (int64_t g = 0; g < ceil_div(r, p.group); ++g) memcpy(Rs + g * p.Npad, d->R_scale + g * N, N * 2);
+      for (int64_t g = 0; g < gr; ++g)
+        for (int64_t n = 0; n < N; ++n) Rs[n * gr + g] = d->R_scale[g * N + n];
     } else {
-      memcpy(blob + p.off[CL_SEC_L], d->L, K * r * 2);
-      uint16_t* Rp = reinterpret_cast<uint16_t*>(blob + p.off[CL_SEC_R]);
+      const uint16_t* L = static_cast<const uint16_t*>(d->L);
       const uint16_t* R = static_cast<const uint16_t*>(d->R);
-      for (int64_t j = 0; j < r; ++j) memcpy(Rp + j * p.Npad, R + j * N, N * 2);
+      uint16_t* Lp = reinterpret_cast<uint16_t*>(blob + p.off[CL_SEC_L]);
+      uint16_t* Rp = reinterpret_cast<uint16_t*>(blob + p.off[CL_SEC_R]);
+      for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < r; ++j) Lp[j * K + k] = L[k * r + j];
+      for (int64_t j = 0; j < r; ++j)
+        for (int64_t n = 0; n < N; ++n) Rp[n * r + j] = R[j * N + n];
     }
   }
 }

@@ -48,27 +48,21 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
   const int mblocks = (int)ceil_div(max_M, 32);
   const size_t o_cnt = take((size_t)(h.n_tiles + mblocks + 8) * 4);
   const size_t o_part = take((size_t)h.n_tiles * split * kMaxDecodeM * 64 * 4);
-  size_t o_nzs = 0, o_tpart = 0, o_t = 0, o_xp = 0;
+  size_t o_nzs = 0, o_t = 0, o_xp = 0;
   if (h.mask == CL_MASK_BITMAP) o_nzs = take((size_t)Npad * 4 * split * 4);
-  int lr_blocks = 0;
-  if (h.lr != CL_LR_NONE && h.rank > 0) {
-    lr_blocks = (int)ceil_div(h.K, 256);
-    if (lr_blocks > 64) lr_blocks = 64;
-    o_tpart = take((size_t)lr_blocks * max_M * h.rank * 4);
-    o_t = take((size_t)max_M * h.rank * 4);
-  }
-  const int Kx = (int)round_up(h.K, 2);
-  if (h.has_clamp || (h.K & 1)) o_xp = take((size_t)max_M * Kx * 2);
+  if (h.lr != CL_LR_NONE && h.rank > 0) o_t = take((size_t)max_M * h.rank * 4);
+  // activations are restaged (clamped, row stride a multiple of 8 for aligned
+  // 128-bit loads) when the layer clamps them or K is not a multiple of 8
+  const int Kx = (int)round_up(h.K, 8);
+  if (h.has_clamp || (h.K & 7)) o_xp = take((size_t)max_M * Kx * 2);
   if (L) {
     uint8_t* d = L->dev;
     L->counters = reinterpret_cast<uint32_t*>(d + o_cnt);
     L->part = reinterpret_cast<float*>(d + o_part);
     L->nzstart = o_nzs ? reinterpret_cast<int32_t*>(d + o_nzs) : nullptr;
-    L->tpart = o_tpart ? reinterpret_cast<float*>(d + o_tpart) : nullptr;
     L->t = o_t ? reinterpret_cast<float*>(d + o_t) : nullptr;
     L->xprep = o_xp ? reinterpret_cast<uint16_t*>(d + o_xp) : nullptr;
     L->Kx = Kx;
-    L->lr_blocks = lr_blocks;
     L->ws_bytes = off - align256(base);
   }
   return off;
@@ -141,13 +135,12 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
     const int32_t* off = reinterpret_cast<const int32_t*>(b + h->off[CL_SEC_NZOFF]);
     const uint32_t* meta = reinterpret_cast<const uint32_t*>(b + h->off[CL_SEC_META]);
     for (int n = 0; n < h->N; ++n) {
-      const int tile = n / 64, lane = n % 64;
       long long cnt = 0;
       int c = 0;
       for (int q = 0; q < nsl; ++q) {
         const int cb = (int)((long long)h->chunks * q / nsl);
         for (; c < cb; ++c) {
-          const uint32_t* w = meta + (((size_t)tile * h->chunks + c) * 64 + lane) * 4;
+          const uint32_t* w = meta + ((size_t)n * h->chunks + c) * 4;
           cnt += __builtin_popcount(w[0]) + __builtin_popcount(w[1]) + __builtin_popcount(w[2]) + __builtin_popcount(w[3]);
         }
         nzs[(size_t)n * nsl + q] = (int32_t)(off[n] + cnt);

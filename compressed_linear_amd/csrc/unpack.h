@@ -26,19 +26,32 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint3
   return __builtin_amdgcn_perm(hi_src, lo_src, sel);
 }
 
-__device__ __forceinline__ uint32_t lds_u32(uint32_t byte_addr) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
-      static_cast<uintptr_t>(byte_addr));
+// LDS reads at a byte address inside the kernel's LDS array `lds`.  The array
+// is the kernel's only LDS object, so it starts at address 0 and byte_addr is
+// also its absolute LDS address (the v_perm address tricks rely on that).
+// Indexing through `lds` keeps the table stores visibly live to the compiler.
+__device__ __forceinline__ uint32_t lds_u32(const uint32_t* lds, uint32_t byte_addr) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(lds) + byte_addr);
 }
-__device__ __forceinline__ uint32_t lds_u16(uint32_t byte_addr) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(
-      static_cast<uintptr_t>(byte_addr));
+__device__ __forceinline__ uint32_t lds_u16(const uint32_t* lds, uint32_t byte_addr) {
+  return *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(lds) + byte_addr);
 }
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint2 lds_u64(uint32_t byte_addr) {
-  const u32x2 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
-      static_cast<uintptr_t>(byte_addr));
-  return make_uint2(v.x, v.y);
+__device__ __forceinline__ uint2 lds_u64(const uint32_t* lds, uint32_t byte_addr) {
+  return *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(lds) + byte_addr);
+}
+
+// Device-scope (all XCDs) relaxed atomic store / load of one float, and a wait
+// until this wave's stores have completed (written through to the coherent level).
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), expcnt(7), lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
@@ -52,35 +65,71 @@ __device__ __forceinline__ uint32_t addr_from_byte(uint32_t src, uint32_t laneba
 
 // ---------------------------------------------------------------------------
 // 3-bit LUT: pair table.  Entry (a | b << 3) holds fp16 lut[a] (low) and
-// lut[b] (high): one lookup dequantises two consecutive weights.
+// lut[b] (high): one lookup dequantises two consecutive weights.  The packed
+// byte j reads 4 * p_j for the first four pairs; the fifth pair's three 2-bit
+// pieces (bits 0-1 of bytes 0..2) are gathered by one 24-bit multiply into
+// byte 2 as 4 * p_4 (the partial products do not overlap).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void lut3_word(uint32_t w, uint32_t lanebase, uint32_t out[5]) {
-  const uint32_t m = w & 0x3F3F3F3Fu;
-  // p4 is split over bits 6-7 of bytes 0..2; one 24-bit multiply gathers the
-  // three 2-bit pieces into bits 24..29 (the partial products do not overlap).
-  const uint32_t p4 = __umul24(w & 0x00C0C0C0u, 0x41040u);
-  out[0] = lds_u32(addr_from_byte<0>(m, lanebase));
-  out[1] = lds_u32(addr_from_byte<1>(m, lanebase));
-  out[2] = lds_u32(addr_from_byte<2>(m, lanebase));
-  out[3] = lds_u32(addr_from_byte<3>(m, lanebase));
-  out[4] = lds_u32(addr_from_byte<3>(p4, lanebase));
+__device__ __forceinline__ uint32_t lut3_p4x4(uint32_t w) {  // byte 2 = 4 * p_4
+  return __umul24(w & 0x00030303u, 0x41040u);
+}
+
+// Lane-interleaved table (entry e of lane l at e*256 + 4*l): entry index in
+// address byte 1.
+__device__ __forceinline__ void lut3_word(const uint32_t* lds, uint32_t w, uint32_t lanebase, uint32_t out[5]) {
+  const uint32_t m = (w >> 2) & 0x3F3F3F3Fu;
+  const uint32_t p4 = lut3_p4x4(w) >> 2;  // byte 2 = p_4
+  out[0] = lds_u32(lds, addr_from_byte<0>(m, lanebase));
+  out[1] = lds_u32(lds, addr_from_byte<1>(m, lanebase));
+  out[2] = lds_u32(lds, addr_from_byte<2>(m, lanebase));
+  out[3] = lds_u32(lds, addr_from_byte<3>(m, lanebase));
+  out[4] = lds_u32(lds, addr_from_byte<2>(p4, lanebase));
+}
+
+// Row table (entry e of the row at rowbase + 4*e, rowbase a multiple of 256):
+// the byte 4 * p goes straight into address byte 0.
+__device__ __forceinline__ void lut3_word_row(const uint32_t* lds, uint32_t w, uint32_t rowbase, uint32_t out[5]) {
+  const uint32_t m = w & 0xFCFCFCFCu;
+  const uint32_t p4 = lut3_p4x4(w);
+  out[0] = lds_u32(lds, perm(m, rowbase, 0x03020104u));
+  out[1] = lds_u32(lds, perm(m, rowbase, 0x03020105u));
+  out[2] = lds_u32(lds, perm(m, rowbase, 0x03020106u));
+  out[3] = lds_u32(lds, perm(m, rowbase, 0x03020107u));
+  out[4] = lds_u32(lds, perm(p4, rowbase, 0x03020106u));
+}
+
+// 4-bit LUT, row table of 16 entries: the codes times 4 go into address byte 0.
+__device__ __forceinline__ void lut4_word_row(const uint32_t* lds, uint32_t w, uint32_t rowbase, uint32_t out[4]) {
+  const uint32_t ev = (w << 2) & 0x3C3C3C3Cu;  // 4 * code of even k, one per byte
+  const uint32_t od = (w >> 2) & 0x3C3C3C3Cu;  // 4 * code of odd k
+  uint32_t lo[4], hi[4];
+  lo[0] = lds_u16(lds, perm(ev, rowbase, 0x03020104u));
+  hi[0] = lds_u16(lds, perm(od, rowbase, 0x03020104u));
+  lo[1] = lds_u16(lds, perm(ev, rowbase, 0x03020105u));
+  hi[1] = lds_u16(lds, perm(od, rowbase, 0x03020105u));
+  lo[2] = lds_u16(lds, perm(ev, rowbase, 0x03020106u));
+  hi[2] = lds_u16(lds, perm(od, rowbase, 0x03020106u));
+  lo[3] = lds_u16(lds, perm(ev, rowbase, 0x03020107u));
+  hi[3] = lds_u16(lds, perm(od, rowbase, 0x03020107u));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[j] = perm(hi[j], lo[j], 0x05040100u);
 }
 
 // ---------------------------------------------------------------------------
 // 4-bit LUT: single-code table, entry c = fp16 lut[c] in the low half.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void lut4_word(uint32_t w, uint32_t lanebase, uint32_t out[4]) {
+__device__ __forceinline__ void lut4_word(const uint32_t* lds, uint32_t w, uint32_t lanebase, uint32_t out[4]) {
   const uint32_t ev = w & 0x0F0F0F0Fu;         // codes of even k, one per byte
   const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // codes of odd k
   uint32_t lo[4], hi[4];
-  lo[0] = lds_u16(addr_from_byte<0>(ev, lanebase));
-  hi[0] = lds_u16(addr_from_byte<0>(od, lanebase));
-  lo[1] = lds_u16(addr_from_byte<1>(ev, lanebase));
-  hi[1] = lds_u16(addr_from_byte<1>(od, lanebase));
-  lo[2] = lds_u16(addr_from_byte<2>(ev, lanebase));
-  hi[2] = lds_u16(addr_from_byte<2>(od, lanebase));
-  lo[3] = lds_u16(addr_from_byte<3>(ev, lanebase));
-  hi[3] = lds_u16(addr_from_byte<3>(od, lanebase));
+  lo[0] = lds_u16(lds, addr_from_byte<0>(ev, lanebase));
+  hi[0] = lds_u16(lds, addr_from_byte<0>(od, lanebase));
+  lo[1] = lds_u16(lds, addr_from_byte<1>(ev, lanebase));
+  hi[1] = lds_u16(lds, addr_from_byte<1>(od, lanebase));
+  lo[2] = lds_u16(lds, addr_from_byte<2>(ev, lanebase));
+  hi[2] = lds_u16(lds, addr_from_byte<2>(od, lanebase));
+  lo[3] = lds_u16(lds, addr_from_byte<3>(ev, lanebase));
+  hi[3] = lds_u16(lds, addr_from_byte<3>(od, lanebase));
 #pragma unroll
   for (int j = 0; j < 4; ++j) out[j] = perm(hi[j], lo[j], 0x05040100u);
 }
@@ -111,11 +160,11 @@ __device__ __forceinline__ void int8_word(uint32_t w, uint32_t out[2]) {
 // 2:4 group: kept pair Q = (v0, v1) and the selector entry for its meta nibble
 // expand into the four weights of the group (two fp16 pairs); positions not
 // kept read selector value 12, which v_perm turns into a zero byte.
-__device__ __forceinline__ void int4_24_group(uint32_t vw, int g4, uint32_t meta_word, int g8,
+__device__ __forceinline__ void int4_24_group(const uint32_t* lds, uint32_t vw, int g4, uint32_t meta_word, int g8,
                                               uint32_t seltab_base, uint32_t out[2]) {
   const uint32_t q = int4_pair(vw, 4 * g4);
   const uint32_t nib = (meta_word >> (4 * g8)) & 0xFu;
-  const uint2 sel = lds_u64(seltab_base + nib * 8u);
+  const uint2 sel = lds_u64(lds, seltab_base + nib * 8u);
   out[0] = perm(q, q, sel.x);
   out[1] = perm(q, q, sel.y);
 }
@@ -158,6 +207,9 @@ __device__ __forceinline__ void int8x4_signed(uint32_t d4, uint32_t out[2]) {
 // ---------------------------------------------------------------------------
 enum Kind { K_LUT3 = 0, K_LUT4, K_INT4, K_INT4_24, K_INT8, K_INT8_BM };
 
+template <int KIND>
+constexpr bool is_int_kind() { return KIND == K_INT4 || KIND == K_INT4_24 || KIND == K_INT8 || KIND == K_INT8_BM; }
+
 // Bitmap expansion: 16 nibble selectors, then one staging slot per dense lane
 // of 35 dwords (odd stride: the 64 lanes fall in distinct banks); a slot holds
 // the <= 128 kept bytes of one chunk plus alignment slack.
@@ -178,23 +230,31 @@ template <> struct KindTraits<K_INT8_BM> { static constexpr int span = 128, pair
 //   mw         2:4 metadata (x, y) of the chunk
 //   lanebase   lane * 4 (LUT tables), slot_base: byte address of the lane's
 //              staged kept values (bitmap), already offset to the first one
-template <int KIND>
-__device__ __forceinline__ void chunk_pairs(uint4 w, uint4 mw, uint32_t lanebase, uint32_t slot_base,
+//   ROWTAB     LUT tables are per-row tables at `lanebase` (rowbase) instead of
+//              lane-interleaved tables
+template <int KIND, bool ROWTAB = false>
+__device__ __forceinline__ void chunk_pairs(const uint32_t* lds, uint4 w, uint4 mw, uint32_t lanebase, uint32_t slot_base,
                                             uint32_t (&wp)[KindTraits<KIND>::pairs]) {
   const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-  if constexpr (KIND == K_LUT3) {
+  if constexpr (KIND == K_LUT3 && ROWTAB) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lut3_word(ww[i], lanebase, &wp[5 * i]);
+    for (int i = 0; i < 4; ++i) lut3_word_row(lds, ww[i], lanebase, &wp[5 * i]);
+  } else if constexpr (KIND == K_LUT4 && ROWTAB) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lut4_word_row(lds, ww[i], lanebase, &wp[4 * i]);
+  } else if constexpr (KIND == K_LUT3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lut3_word(lds, ww[i], lanebase, &wp[5 * i]);
   } else if constexpr (KIND == K_LUT4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lut4_word(ww[i], lanebase, &wp[4 * i]);
+    for (int i = 0; i < 4; ++i) lut4_word(lds, ww[i], lanebase, &wp[4 * i]);
   } else if constexpr (KIND == K_INT4) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) int4_word(ww[i], &wp[4 * i]);
   } else if constexpr (KIND == K_INT4_24) {
     const uint32_t mm[2] = {mw.x, mw.y};
 #pragma unroll
-    for (int g = 0; g < 16; ++g) int4_24_group(ww[g / 4], g % 4, mm[g / 8], g % 8, 0u, &wp[2 * g]);
+    for (int g = 0; g < 16; ++g) int4_24_group(lds, ww[g / 4], g % 4, mm[g / 8], g % 8, 0u, &wp[2 * g]);
   } else if constexpr (KIND == K_INT8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) int8_word(ww[i], &wp[2 * i]);
@@ -205,9 +265,9 @@ __device__ __forceinline__ void chunk_pairs(uint4 w, uint4 mw, uint32_t lanebase
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const uint32_t nib = (ww[i] >> (4 * t)) & 0xFu;
-        const uint32_t lo = lds_u32(off & ~3u), hi = lds_u32((off & ~3u) + 4u);
+        const uint32_t lo = lds_u32(lds, off & ~3u), hi = lds_u32(lds, (off & ~3u) + 4u);
         const uint32_t win = __builtin_amdgcn_alignbyte(hi, lo, off & 3u);
-        const uint32_t d4 = perm(0u, win, lds_u32(nib * 4u));
+        const uint32_t d4 = perm(0u, win, lds_u32(lds, nib * 4u));
         int8x4_signed(d4, &wp[16 * i + 2 * t]);
         off += __builtin_popcount(nib);
       }
@@ -243,6 +303,28 @@ __device__ __forceinline__ void build_tables(uint32_t* smem, const uint16_t* tab
     }
   } else if constexpr (KIND == K_INT8_BM) {
     if (tid < 16) smem[tid] = bitmap_sel_entry((uint32_t)tid);
+  }
+}
+
+// Per-row LUT tables of `nrows` consecutive rows starting at row0 (row q at
+// dword q*64; LUT3: 64 pair entries, LUT4: 16 single entries); the 2:4 and
+// bitmap selector tables at address 0 as for the tile tables.
+template <int KIND>
+__device__ __forceinline__ void build_row_tables(uint32_t* smem, const uint16_t* table, int row0, int nrows, int tid,
+                                                 int nthreads) {
+  if constexpr (KIND == K_LUT3) {
+    for (int i = tid; i < nrows * 64; i += nthreads) {
+      const int q = i >> 6, e = i & 63, ca = e & 7, cb = e >> 3;
+      const uint16_t* lt = table + (size_t)(row0 + q) * 8;
+      smem[q * 64 + e] = (uint32_t)lt[ca] | ((uint32_t)lt[cb] << 16);
+    }
+  } else if constexpr (KIND == K_LUT4) {
+    for (int i = tid; i < nrows * 16; i += nthreads) {
+      const int q = i >> 4, c = i & 15;
+      smem[q * 64 + c] = table[(size_t)(row0 + q) * 16 + c];
+    }
+  } else {
+    build_tables<KIND>(smem, table, 0, tid, nthreads < 64 ? 64 : nthreads);
   }
 }
 

@@ -221,17 +221,17 @@ const char* cl_last_error(void);
 #define CL_BLOB_MAGIC 0x31424C43u /* "CLB1" */
 #define CL_BLOB_VERSION 1u
 enum {
-  CL_SEC_DENSE = 0,   /* tile-interleaved dense stream */
+  CL_SEC_DENSE = 0,   /* dense stream, row-major 16-byte chunks (bitmap: kept values) */
   CL_SEC_TABLE,       /* LUT [Npad * 2^b] fp16 or row scales [Npad] fp16 */
-  CL_SEC_META,        /* 2:4 metadata or bitmap words, tile-interleaved */
+  CL_SEC_META,        /* 2:4 metadata or bitmap words, row-major chunks */
   CL_SEC_NZOFF,       /* BITMAP: int32 [N+1] start of each row's kept values */
   CL_SEC_ROWPTR,      /* CSR row_ptr int32 [N+1] */
   CL_SEC_COL,         /* CSR col int32 [nnz] */
   CL_SEC_VAL,         /* CSR val fp16 [nnz] */
-  CL_SEC_L,           /* low-rank L */
-  CL_SEC_R,           /* low-rank R */
-  CL_SEC_LSCALE,      /* int4 L scales */
-  CL_SEC_RSCALE,      /* int4 R scales */
+  CL_SEC_L,           /* low-rank L, transposed: [rank][K] */
+  CL_SEC_R,           /* low-rank R, transposed: [Npad][rank] */
+  CL_SEC_LSCALE,      /* int4 L scales, [rank][ceil(K/group)] */
+  CL_SEC_RSCALE,      /* int4 R scales, [Npad][ceil(rank/group)] */
   CL_SEC_COUNT = 16
 };
 typedef struct {

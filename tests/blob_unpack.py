@@ -22,17 +22,17 @@ def unpack(blob):
     out = {"K": K, "N": N, "dense": dense_kind, "mask": mask}
 
     def tiled(name, cb):
-        a = _sec(blob, h, name)[: T * C * 64 * cb].reshape(T, C, 64, cb)
-        return a.transpose(0, 2, 1, 3).reshape(Npad, C * cb)  # row-major chunk bytes per row
+        """Row-major chunk stream -> [Npad, C * cb] bytes."""
+        return _sec(blob, h, name)[: Npad * C * cb].reshape(Npad, C * cb)
 
     if dense_kind in ("lut3", "lut4"):
         rows = tiled("dense", 16).view(np.uint32)  # [Npad, C*4]
         if dense_kind == "lut3":
             w = rows.astype(np.uint64)
             b = [(w >> (8 * i)) & 0xFF for i in range(4)]
-            pairs = [bi & 0x3F for bi in b]
-            pairs.append((b[0] >> 6) | ((b[1] >> 6) << 2) | ((b[2] >> 6) << 4))
-            assert ((b[3] >> 6) == 0).all()
+            pairs = [bi >> 2 for bi in b]
+            pairs.append((b[0] & 3) | ((b[1] & 3) << 2) | ((b[2] & 3) << 4))
+            assert ((b[3] & 3) == 0).all()
             codes = np.zeros((Npad, C * 40), np.uint8)
             for j, p in enumerate(pairs):
                 for half in range(2):
@@ -94,16 +94,18 @@ def unpack(blob):
         out["csr_val"] = _sec(blob, h, "val", np.uint16).view(np.float16)
     if h["lr"]:
         r, g = h["rank"], max(h["group"], 1)
+        # factors are stored transposed: L^T [r][K], R^T [Npad][r]
         if h["lr"] == 3:
-            hr = (r + 1) // 2
-            Lb = _sec(blob, h, "L").reshape(K, hr)
-            Lq = np.stack([(Lb & 0xF), (Lb >> 4)], axis=2).reshape(K, 2 * hr)[:, :r].astype(np.int16) - 8
-            Rb = _sec(blob, h, "R").reshape(r, Npad // 2)
-            Rq = np.stack([(Rb & 0xF), (Rb >> 4)], axis=2).reshape(r, Npad)[:, :N].astype(np.int16) - 8
-            out["L"], out["R"] = Lq.astype(np.int8), Rq.astype(np.int8)
-            out["L_scale"] = _sec(blob, h, "Lscale", np.uint16).reshape(-1, r).view(np.float16)
-            out["R_scale"] = _sec(blob, h, "Rscale", np.uint16).reshape(-1, Npad)[:, :N].view(np.float16)
+            hk, hr = (K + 1) // 2, (r + 1) // 2
+            Lb = _sec(blob, h, "L").reshape(r, hk)
+            LqT = np.stack([(Lb & 0xF), (Lb >> 4)], axis=2).reshape(r, 2 * hk)[:, :K].astype(np.int16) - 8
+            Rb = _sec(blob, h, "R").reshape(Npad, hr)
+            RqT = np.stack([(Rb & 0xF), (Rb >> 4)], axis=2).reshape(Npad, 2 * hr)[:N, :r].astype(np.int16) - 8
+            out["L"], out["R"] = LqT.T.astype(np.int8), RqT.T.astype(np.int8)
+            gk, gr = -(-K // g), -(-r // g)
+            out["L_scale"] = _sec(blob, h, "Lscale", np.uint16).reshape(r, gk).T.view(np.float16)
+            out["R_scale"] = _sec(blob, h, "Rscale", np.uint16).reshape(Npad, gr)[:N].T.view(np.float16)
         else:
-            out["L"] = _sec(blob, h, "L", np.uint16).reshape(K, r)
-            out["R"] = _sec(blob, h, "R", np.uint16).reshape(r, Npad)[:, :N]
+            out["L"] = _sec(blob, h, "L", np.uint16).reshape(r, K).T
+            out["R"] = _sec(blob, h, "R", np.uint16).reshape(Npad, r)[:N].T
     return h, out
