@@ -50,8 +50,9 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
   a.lr_kind = h.lr;
   a.Npad = L.Npad;
   const bool bf16 = h.x_dtype == CL_ACT_BF16;
-  // M <= 4: row-wise kernel (bandwidth bound); the bitmap format always uses
-  // the tile kernel (its kept values are consumed per row at a varying rate)
+  // M <= 4: row-wise kernel (bandwidth bound) when its staged activations fit
+  // in LDS; the bitmap format always uses the tile kernel (its kept values are
+  // consumed per row at a varying rate)
   if (M <= 4 && h.mask != CL_MASK_BITMAP) {
     RowArgs r = {};
     r.dense = a.dense;
@@ -74,12 +75,22 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
     r.group = a.group;
     r.lr_kind = a.lr_kind;
     switch (h.dense) {
-      case CL_DENSE_LUT3: return launch_rows_kind<K_LUT3>(r, L.Npad, bf16, stream);
-      case CL_DENSE_LUT4: return launch_rows_kind<K_LUT4>(r, L.Npad, bf16, stream);
+      case CL_DENSE_LUT3:
+        if (rows_fit<K_LUT3>(r)) return launch_rows_kind<K_LUT3>(r, L.Npad, bf16, stream);
+        break;
+      case CL_DENSE_LUT4:
+        if (rows_fit<K_LUT4>(r)) return launch_rows_kind<K_LUT4>(r, L.Npad, bf16, stream);
+        break;
       case CL_DENSE_INT4:
-        return h.mask == CL_MASK_2_4 ? launch_rows_kind<K_INT4_24>(r, L.Npad, bf16, stream)
-                                     : launch_rows_kind<K_INT4>(r, L.Npad, bf16, stream);
-      default: return launch_rows_kind<K_INT8>(r, L.Npad, bf16, stream);
+        if (h.mask == CL_MASK_2_4) {
+          if (rows_fit<K_INT4_24>(r)) return launch_rows_kind<K_INT4_24>(r, L.Npad, bf16, stream);
+        } else if (rows_fit<K_INT4>(r)) {
+          return launch_rows_kind<K_INT4>(r, L.Npad, bf16, stream);
+        }
+        break;
+      default:
+        if (rows_fit<K_INT8>(r)) return launch_rows_kind<K_INT8>(r, L.Npad, bf16, stream);
+        break;
     }
   }
   switch (h.dense) {
