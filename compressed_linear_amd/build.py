@@ -25,7 +25,8 @@ SOURCES = ["pack.cpp", "runtime.hip", "decode.hip", "aux.hip", "prefill.hip",
            "decode_lut3.hip", "decode_lut4.hip", "decode_int4.hip", "decode_int4_24.hip",
            "decode_int8.hip", "decode_int8_bm.hip",
            "decode_rows_lut3.hip", "decode_rows_lut4.hip", "decode_rows_int4.hip", "decode_rows_int4_24.hip",
-           "decode_rows_int8.hip"]
+           "decode_rows_int8.hip",
+           "prefill_lut3.hip", "prefill_lut4.hip", "prefill_int.hip", "prefill_lr.hip"]
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

@@ -50,7 +50,7 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
   const size_t o_part = take((size_t)h.n_tiles * split * kMaxDecodeM * 64 * 4);
   size_t o_nzs = 0, o_t = 0, o_xp = 0;
   if (h.mask == CL_MASK_BITMAP) o_nzs = take((size_t)Npad * 4 * split * 4);
-  if (h.lr != CL_LR_NONE && h.rank > 0) o_t = take((size_t)max_M * h.rank * 4);
+  if (h.lr != CL_LR_NONE && h.rank > 0) o_t = take((size_t)max_M * round_up(h.rank, 8) * 4);  // row stride <= rank rounded to 8
   // activations are restaged (clamped, row stride a multiple of 8 for aligned
   // 128-bit loads) when the layer clamps them or K is not a multiple of 8
   const int Kx = (int)round_up(h.K, 8);

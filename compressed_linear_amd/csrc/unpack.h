@@ -75,10 +75,12 @@ __device__ __forceinline__ uint32_t lut3_p4x4(uint32_t w) {  // byte 2 = 4 * p_4
 }
 
 // Lane-interleaved table (entry e of lane l at e*256 + 4*l): entry index in
-// address byte 1.
-__device__ __forceinline__ void lut3_word(const uint32_t* lds, uint32_t w, uint32_t lanebase, uint32_t out[5]) {
-  const uint32_t m = (w >> 2) & 0x3F3F3F3Fu;
-  const uint32_t p4 = lut3_p4x4(w) >> 2;  // byte 2 = p_4
+// address byte 1.  `ebias` is ORed into every entry byte (selects one of
+// several stacked tables: 64 * g for table g).
+__device__ __forceinline__ void lut3_word(const uint32_t* lds, uint32_t w, uint32_t lanebase, uint32_t out[5],
+                                         uint32_t ebias = 0) {
+  const uint32_t m = ((w >> 2) & 0x3F3F3F3Fu) | (ebias * 0x01010101u);
+  const uint32_t p4 = (lut3_p4x4(w) >> 2) | (ebias << 16);  // byte 2 = p_4
   out[0] = lds_u32(lds, addr_from_byte<0>(m, lanebase));
   out[1] = lds_u32(lds, addr_from_byte<1>(m, lanebase));
   out[2] = lds_u32(lds, addr_from_byte<2>(m, lanebase));
@@ -118,9 +120,10 @@ __device__ __forceinline__ void lut4_word_row(const uint32_t* lds, uint32_t w, u
 // ---------------------------------------------------------------------------
 // 4-bit LUT: single-code table, entry c = fp16 lut[c] in the low half.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void lut4_word(const uint32_t* lds, uint32_t w, uint32_t lanebase, uint32_t out[4]) {
-  const uint32_t ev = w & 0x0F0F0F0Fu;         // codes of even k, one per byte
-  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // codes of odd k
+__device__ __forceinline__ void lut4_word(const uint32_t* lds, uint32_t w, uint32_t lanebase, uint32_t out[4],
+                                         uint32_t ebias = 0) {
+  const uint32_t ev = (w & 0x0F0F0F0Fu) | (ebias * 0x01010101u);         // codes of even k, one per byte
+  const uint32_t od = ((w >> 4) & 0x0F0F0F0Fu) | (ebias * 0x01010101u);  // codes of odd k
   uint32_t lo[4], hi[4];
   lo[0] = lds_u16(lds, addr_from_byte<0>(ev, lanebase));
   hi[0] = lds_u16(lds, addr_from_byte<0>(od, lanebase));
@@ -232,9 +235,10 @@ template <> struct KindTraits<K_INT8_BM> { static constexpr int span = 128, pair
 //              staged kept values (bitmap), already offset to the first one
 //   ROWTAB     LUT tables are per-row tables at `lanebase` (rowbase) instead of
 //              lane-interleaved tables
+//   ebias      lane-interleaved tables only: ORed into the entry index (stacked tables)
 template <int KIND, bool ROWTAB = false>
 __device__ __forceinline__ void chunk_pairs(const uint32_t* lds, uint4 w, uint4 mw, uint32_t lanebase, uint32_t slot_base,
-                                            uint32_t (&wp)[KindTraits<KIND>::pairs]) {
+                                            uint32_t (&wp)[KindTraits<KIND>::pairs], uint32_t ebias = 0) {
   const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
   if constexpr (KIND == K_LUT3 && ROWTAB) {
 #pragma unroll
@@ -244,10 +248,10 @@ __device__ __forceinline__ void chunk_pairs(const uint32_t* lds, uint4 w, uint4 
     for (int i = 0; i < 4; ++i) lut4_word_row(lds, ww[i], lanebase, &wp[4 * i]);
   } else if constexpr (KIND == K_LUT3) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lut3_word(lds, ww[i], lanebase, &wp[5 * i]);
+    for (int i = 0; i < 4; ++i) lut3_word(lds, ww[i], lanebase, &wp[5 * i], ebias);
   } else if constexpr (KIND == K_LUT4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lut4_word(lds, ww[i], lanebase, &wp[4 * i]);
+    for (int i = 0; i < 4; ++i) lut4_word(lds, ww[i], lanebase, &wp[4 * i], ebias);
   } else if constexpr (KIND == K_INT4) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) int4_word(ww[i], &wp[4 * i]);

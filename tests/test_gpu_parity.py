@@ -74,6 +74,18 @@ def test_prefill_small_lut3_lr():
         check_bound(y, layer, x, what=f"prefill M={M}")
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_prefill_small_all_formats(cfg):
+    # the matrix-core path at ragged M, N and K (several tiles and a partial one each way)
+    K, N = SMALL[cfg]
+    for M in (40, 129):
+        layer = make_layer(cfg, 1 if cfg in (3, 4) else 0, K=K, N=N, M_for_clamp=M)
+        x = make_x(cfg, 1 if cfg in (3, 4) else 0, M, K=K)
+        say("prefill all", layer.name, "M", M)
+        y = gpu_forward(layer, x, path="prefill")
+        check_bound(y, layer, x, what=f"prefill {layer.name} M={M}")
+
+
 def test_deterministic():
     torch = torch_cuda()
     layer = make_layer(5, 0, K=1450, N=190)
