@@ -39,6 +39,15 @@ struct Layer {
   float* t = nullptr;            // [max_M][rank]
   uint16_t* xprep = nullptr;     // [max_M][Kx]  clamped / padded activations
   int Kx = 0;                    // row stride of xprep (even)
+
+  // matrix-core prefill (built at create)
+  int pf_nd = 0;                 // K steps over the packed weights
+  int32_t* pf_cptr = nullptr;    // outliers per (128-row tile, step): offsets [n_tiles128][pf_nd + 1]
+  uint32_t* pf_cent = nullptr;   // entries: row in tile | k in step << 7 | fp16 value << 16
+  uint16_t* pf_r16 = nullptr;    // [Npad][2 rp]: R^T twice, in the MFMA input type
+  uint16_t* pf_l16 = nullptr;    // [rank][Kl]: L^T, rows padded to Kl = K rounded up to 8, MFMA input type
+  uint16_t* pf_t16 = nullptr;    // [max_M][2 rp]: t_hi | t_lo of t = x' L (workspace)
+  int pf_rp = 0, pf_Kl = 0;
   size_t ws_bytes = 0;
 };
 

@@ -62,6 +62,15 @@ inline KindInfo kind_info(int dense, int mask) {
 }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Matrix-core prefill: output tiles of kPfTileN weight rows; K advances in steps
+// of pf_step_k() (a whole number of chunks, a multiple of 16).
+constexpr int kPfTileN = 128;
+inline int pf_step_k(int dense, int mask) {
+  if (dense == 0) return 80;               // LUT3: two chunks of 40
+  if (dense == 2 && mask == 1) return 128;  // INT4 2:4: two chunks of 64
+  return 64;
+}
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 }  // namespace cl

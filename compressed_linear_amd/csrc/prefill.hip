@@ -14,9 +14,23 @@ extern template hipError_t launch_prefill_kind<K_INT4>(const PfArgs&, bool, hipS
 extern template hipError_t launch_prefill_kind<K_INT4_24>(const PfArgs&, bool, hipStream_t);
 extern template hipError_t launch_prefill_kind<K_INT8>(const PfArgs&, bool, hipStream_t);
 extern template hipError_t launch_prefill_kind<K_DENSE16>(const PfArgs&, bool, hipStream_t);
-extern template hipError_t launch_prefill_kind<K_DENSE_INT4>(const PfArgs&, bool, hipStream_t);
 
-// The bitmap format has no matrix-core loader yet: row blocks of 32 through the decode kernels.
+// t_hi | t_lo of t = the sum of the prologue's K-split partials, added in a
+// fixed order: [M][2 rp], t_hi = t rounded to the MFMA type, t_lo = the rest.
+template <bool BF16>
+__global__ void __launch_bounds__(256) pf_tsplit_kernel(const float* t, size_t tstride, int split, int M, int rp,
+                                                        uint16_t* t16) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * 2 * rp) return;
+  const int m = i / (2 * rp), v = i - m * 2 * rp, j = v < rp ? v : v - rp;
+  float s = 0.f;
+  for (int z = 0; z < split; ++z) s += t[(size_t)z * tstride + (size_t)m * rp + j];
+  const uint32_t hi = to16<BF16>(s);
+  const float hif = BF16 ? __uint_as_float(hi << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)hi);
+  t16[i] = (uint16_t)(v < rp ? hi : to16<BF16>(s - hif));
+}
+
+// The bitmap format has no matrix-core loader: row blocks of 32 through the decode kernels.
 static hipError_t prefill_by_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream) {
   const int ldx = (x == L.xprep) ? L.Kx : L.h.K;
   for (int m0 = 0; m0 < M; m0 += kMaxDecodeM) {
@@ -32,11 +46,6 @@ static hipError_t prefill_by_decode(const Layer& L, int M, const void* x, float*
   return hipSuccess;
 }
 
-template <int KIND>
-static int dense_steps(const cl_blob_header& h) {
-  return (int)ceil_div(h.chunks, PfCfg<KIND>::bk / PfCfg<KIND>::span);
-}
-
 hipError_t launch_prefill(const Layer& L, int M, const void* x, float* y, hipStream_t stream) {
   const cl_blob_header& h = L.h;
   if (h.mask == CL_MASK_BITMAP) return prefill_by_decode(L, M, x, y, stream);
@@ -47,28 +56,43 @@ hipError_t launch_prefill(const Layer& L, int M, const void* x, float* y, hipStr
   a.M = M;
   a.K = h.K;
   const bool has_lr = h.lr != CL_LR_NONE && h.rank > 0;
-  const int rp = (int)round_up(h.rank, 8);
+  const int rp = L.pf_rp;
   hipError_t e = hipSuccess;
   if (has_lr) {
-    // t = x' L on the matrix cores: L^T rows are the weight tile; t is [M][rp], zero past the rank
+    // t = x' L on the matrix cores (L^T rows as the weight tile), split along K
+    // so that the few output tiles of t still fill the chip
     PfArgs p = a;
     p.N = h.rank;
     p.Npad = h.rank;
-    p.group = h.group > 0 ? h.group : 1;
-    p.b_bf16 = h.lr == CL_LR_BF16;
+    p.b16 = L.pf_l16;
+    p.ldb16 = L.pf_Kl;
+    p.nb16 = h.rank;
     p.y = L.t;
     p.ldy = rp;
     p.ncols = rp;
-    p.nsteps = p.nsteps_dense = (int)ceil_div(h.K, PfCfg<K_DENSE16>::bk);
-    if (h.lr == CL_LR_INT4) {
-      p.b4 = L.L;
-      p.b4s = L.Lscale;
-      e = launch_prefill_kind<K_DENSE_INT4>(p, bf16, stream);
-    } else {
-      p.b16 = reinterpret_cast<const uint16_t*>(L.L);
-      e = launch_prefill_kind<K_DENSE16>(p, bf16, stream);
-    }
+    p.nsteps = p.nsteps_dense = (int)ceil_div(L.pf_Kl, PfCfg<K_DENSE16>::bk);
+    const int tiles = (int)(ceil_div(rp, kPfBN) * ceil_div(M, kPfBM));
+    int split = (int)ceil_div(256, tiles);
+    if (split > kPfMaxSplit) split = kPfMaxSplit;
+    if (split > p.nsteps) split = p.nsteps;
+    p.steps_per_split = (int)ceil_div(p.nsteps, split);
+    split = (int)ceil_div(p.nsteps, p.steps_per_split);
+    p.ystride = (size_t)M * rp;
+    e = launch_prefill_kind<K_DENSE16>(p, bf16, stream);
     if (e != hipSuccess) return e;
+    const int total = M * 2 * rp;
+    if (bf16)
+      hipLaunchKernelGGL(pf_tsplit_kernel<true>, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, stream, L.t,
+                         p.ystride, split, M, rp, L.pf_t16);
+    else
+      hipLaunchKernelGGL(pf_tsplit_kernel<false>, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, stream, L.t,
+                         p.ystride, split, M, rp, L.pf_t16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.a2 = L.pf_t16;
+    a.lda2 = 2 * rp;
+    a.r16 = L.pf_r16;
+    a.ldr16 = 2 * rp;
   }
   a.N = h.N;
   a.Npad = L.Npad;
@@ -76,37 +100,25 @@ hipError_t launch_prefill(const Layer& L, int M, const void* x, float* y, hipStr
   a.meta = L.meta;
   a.table = reinterpret_cast<const uint16_t*>(L.table);
   a.chunks = h.chunks;
-  if (h.nnz > 0) {
-    a.rowptr = L.rowptr;
-    a.col = L.col;
-    a.val = L.val;
-  }
-  if (has_lr) {
-    a.t = L.t;
-    a.ldt = rp;
-    a.rank = h.rank;
-    a.rp = rp;
-    a.lr_kind = h.lr;
-    a.R = L.R;
-    a.Rscale = L.Rscale;
-    a.rgroup = h.group > 0 ? h.group : 1;
-  }
+  a.cptr = L.pf_cptr;
+  a.cent = L.pf_cent;
   a.y = y;
   a.ldy = h.N;
   a.ncols = h.N;
-  auto run = [&](auto kind_tag, int bk) {
+  a.ystride = 0;
+  a.nsteps_dense = L.pf_nd;
+  auto run = [&](auto kind_tag) {
     constexpr int KIND = decltype(kind_tag)::value;
-    a.nsteps_dense = dense_steps<KIND>(h);
-    a.nsteps = a.nsteps_dense + (has_lr ? (int)ceil_div(2 * rp, bk) : 0);
+    a.nsteps = a.nsteps_dense + (has_lr ? (int)ceil_div(2 * rp, PfCfg<KIND>::bk) : 0);
+    a.steps_per_split = a.nsteps;
     return launch_prefill_kind<KIND>(a, bf16, stream);
   };
   switch (h.dense) {
-    case CL_DENSE_LUT3: return run(std::integral_constant<int, K_LUT3>{}, PfCfg<K_LUT3>::bk);
-    case CL_DENSE_LUT4: return run(std::integral_constant<int, K_LUT4>{}, PfCfg<K_LUT4>::bk);
+    case CL_DENSE_LUT3: return run(std::integral_constant<int, K_LUT3>{});
+    case CL_DENSE_LUT4: return run(std::integral_constant<int, K_LUT4>{});
     case CL_DENSE_INT4:
-      return h.mask == CL_MASK_2_4 ? run(std::integral_constant<int, K_INT4_24>{}, PfCfg<K_INT4_24>::bk)
-                                   : run(std::integral_constant<int, K_INT4>{}, PfCfg<K_INT4>::bk);
-    default: return run(std::integral_constant<int, K_INT8>{}, PfCfg<K_INT8>::bk);
+      return h.mask == CL_MASK_2_4 ? run(std::integral_constant<int, K_INT4_24>{}) : run(std::integral_constant<int, K_INT4>{});
+    default: return run(std::integral_constant<int, K_INT8>{});
   }
 }
 

@@ -2,26 +2,31 @@
 //
 // y[M, N] = x'[M, K] . W^T on bf16 (bf16 activations) or fp16 (fp16
 // activations) MFMA with fp32 accumulation, v_mfma_f32_32x32x16.  A workgroup
-// of four wavefronts owns a 128 x 128 output tile (128 activation rows m,
-// 128 weight rows n); each wavefront a 64 x 64 quarter, 2 x 2 MFMA blocks.
-// Per K step the workgroup
-//   - stages the activation tile x'[m0.., k0..k0+BK) in LDS,
-//   - dequantises the weight tile W[n0.., k0..) into LDS through the same
-//     unpack functions as the decode path (two threads per weight row, one
-//     chunk each), adding the row's outliers that fall in the step
-//     ("SqueezeLLM: Dense-and-Sparse Quantization", Approach: W = D + S),
-//   - and runs BK/16 MFMA steps over the two tiles,
-// with the next step's activations and codes already loaded into registers.
+// owns a 128 x 128 output tile (128 activation rows m, 128 weight rows n) and
+// has two roles of four wavefronts each:
+//   - MFMA waves: each owns a 64 x 64 quarter (2 x 2 MFMA blocks) and only
+//     reads operands from LDS and issues MFMAs;
+//   - staging waves: load the activations and packed codes three K steps
+//     ahead into a ring of register stages, dequantise the weight tile into
+//     LDS through the same unpack functions as the decode path (two threads
+//     per weight row), and add the step's outliers.
+// Two LDS tile buffers: while the MFMA waves consume step s from one, the
+// staging waves fill the other with step s + 1; two barriers per step (the
+// outliers are added after the dequantised tile has landed).
+//
+// Outliers ("SqueezeLLM: Dense-and-Sparse Quantization", Approach: W = D + S)
+// come as per-(tile, step) lists built when the layer is created: one entry
+// per thread per step, added to the tile with LDS packed atomic adds.
 //
 // The rank-r correction ("SLiM" page, review highlights: y += (x' L) R) runs
-// as extra K steps of the same loop: the activation side is t = x' L split
-// into t_hi + t_lo (two 16-bit numbers whose sum carries t to about 16
-// significant bits), the weight side is R^T twice, so the MFMA adds
-// t_hi R + t_lo R.  t itself is computed beforehand by this same kernel with
-// L^T as the weight tile (the "dense" weight kinds below).
+// as extra K steps: the activation side is t = x' L split into t_hi + t_lo
+// (two 16-bit numbers carrying t to about 16 significant bits), the weight side
+// is R^T twice, so the MFMA adds t_hi R + t_lo R.  t is computed beforehand by
+// this same kernel with L^T as the weight tile, split along K into partial
+// sums that a small kernel adds in a fixed order.
 //
 // Weights enter the matrix cores as 16-bit values of the activation type: fp16
-// LUT values exactly for fp16 activations; rounded to nearest-even bf16 for
+// LUT values exactly for fp16 activations, rounded to nearest-even bf16 for
 // bf16 activations; integer codes times the row scale rounded to the type.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -31,14 +36,19 @@
 
 namespace cl {
 
-// Weight sources of the prologue t = x' L: L^T rows, 16-bit, or int4 with group scales.
-enum { K_DENSE16 = 16, K_DENSE_INT4 = 17 };
+// Weight source of the prologue t = x' L: 16-bit L^T rows prepared at create.
+enum { K_DENSE16 = 16 };
 
 typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 pf_f16x8 __attribute__((ext_vector_type(8)));
 typedef float pf_f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 pf_bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 pf_f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kPfBM = 128, kPfBN = 128, kPfThreads = 256;
+constexpr int kPfBM = 128, kPfBN = kPfTileN, kPfThreads = 256;  // threads of one role
+constexpr int kPfMaxSplit = 8;      // K splits of the prologue (the workspace holds this many partials)
+constexpr int kPfMaxSteps = 1536;   // K steps whose outlier offsets fit the LDS cache
+constexpr uint32_t kPfNoEntry = 0xFFFFFFFFu;
 
 // Per weight kind: span of a chunk, K per step (a whole number of chunks and
 // of 16), chunks each thread dequantises per step (two threads per row).
@@ -46,54 +56,50 @@ template <int KIND>
 struct PfCfg {
   static constexpr int span = KIND == K_LUT3 ? 40 : KIND == K_INT4_24 ? 64 : KIND == K_INT8 ? 16 : 32;
   static constexpr int bk = KIND == K_LUT3 ? 80 : KIND == K_INT4_24 ? 128 : 64;
-  static constexpr int cpt = bk / span / 2;                 // chunks per thread per step
-  static constexpr int vpt = bk / 2;                        // weight values per thread per step
-  static constexpr int ts = bk * 2 + 16;                    // LDS bytes per tile row (padded)
+  static constexpr int cpt = bk / span / 2;  // chunks per thread per step
+  static constexpr int vpt = bk / 2;         // weight values per thread per step
+  static constexpr int ts = bk * 2 + 16;     // LDS bytes per tile row (padded: conflict-free 128-bit reads)
   static constexpr int tab = KIND == K_LUT3 ? 2 * 64 * 256 : KIND == K_LUT4 ? 2 * 16 * 256 : KIND == K_INT4_24 ? 256 : 0;
-  static constexpr int lds = tab + 2 * 128 * ts;
+  static constexpr int buf = 2 * 128 * ts;   // one (A, B) tile pair
+  static constexpr int cptr = tab + 2 * buf; // LDS cache of the workgroup's outlier offsets
+  static constexpr int lds = cptr + (kPfMaxSteps + 1) * 4;
 };
+static_assert(PfCfg<K_LUT3>::bk == 80 && PfCfg<K_INT4_24>::bk == 128 && PfCfg<K_LUT4>::bk == 64,
+              "step sizes must match pf_step_k()");
 
 struct PfArgs {
   const uint16_t* x;   // activations [M][ldx], zero past K up to ldx
   int ldx, M, K;
-  int N;               // weight rows that exist (outputs: N, or rank for the prologue)
-  int Npad;            // rows with storage (codes, tables): a multiple of 64
+  int N;               // weight rows that exist
+  int Npad;            // rows with storage (codes, tables)
   // packed weights
   const uint4* dense;
   const uint8_t* meta;
   const uint16_t* table;
   int chunks;
-  // prologue weights: L^T [rank][K] 16-bit, or int4 codes [rank][ceil(K/2)] + scales [rank][ceil(K/g)]
+  // 16-bit weight rows of the prologue (L^T, [nb16][ldb16], MFMA type)
   const uint16_t* b16;
-  const uint8_t* b4;
-  const uint16_t* b4s;
-  int group;
-  int b_bf16;          // b16 holds bf16 (else fp16)
-  // outliers
-  const int32_t* rowptr;
-  const int32_t* col;
-  const uint16_t* val;
-  // rank-r extension
-  const float* t;      // [M][ldt]
-  int ldt, rank, rp, lr_kind;
-  const uint8_t* R;    // R^T [Npad][rank] 16-bit, or int4 [Npad][ceil(rank/2)]
-  const uint16_t* Rscale;
-  int rgroup;
-  // output
+  int ldb16, nb16;
+  // outliers per (tile, step): offsets [tiles][nsteps_dense + 1], entries
+  const int32_t* cptr;
+  const uint32_t* cent;
+  // rank steps: activations t_hi | t_lo [M][lda2], weights R^T | R^T [Npad][ldr16]
+  const uint16_t* a2;
+  int lda2;
+  const uint16_t* r16;
+  int ldr16;
+  // output (the prologue's split z writes its partial at y + z * ystride)
   float* y;
   int ldy, ncols;      // store columns n < ncols
+  size_t ystride;
   int nsteps, nsteps_dense;
+  int steps_per_split;
 };
 
 template <bool BF16>
 __device__ __forceinline__ uint32_t to16(float f) {
   if constexpr (BF16) return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
-}
-template <bool BF16>
-__device__ __forceinline__ float from16(uint32_t u) {
-  if constexpr (BF16) return __uint_as_float(u << 16);
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)u);
 }
 // fp16 pair -> pair of the MFMA type
 template <bool BF16>
@@ -119,216 +125,258 @@ __device__ __forceinline__ pf_f32x16 pf_mfma(uint4 a, uint4 b, pf_f32x16 c) {
                                                 0);
 }
 
+// Adds one outlier entry to the weight tile at byte offset `btile` (row in tile,
+// k in step, fp16 value) with a packed atomic add on the dword holding it.
+template <bool BF16, int TS>
+__device__ __forceinline__ void pf_add_outlier(uint32_t* smem, uint32_t btile, uint32_t e) {
+  const uint32_t row = e & 127u, kl = (e >> 7) & 127u;
+  const uint32_t addr = btile + row * TS + (kl & ~1u) * 2u;
+  const uint32_t v16 = to16<BF16>((float)__builtin_bit_cast(_Float16, (uint16_t)(e >> 16)));
+  const uint32_t pk = (kl & 1u) ? (v16 << 16) : v16;
+  void* p = reinterpret_cast<uint8_t*>(smem) + addr;
+  if constexpr (BF16)
+    __builtin_amdgcn_ds_atomic_fadd_v2bf16((__attribute__((address_space(3))) pf_bf16x2*)p,
+                                           __builtin_bit_cast(pf_bf16x2, pk));
+  else
+    __builtin_amdgcn_ds_atomic_fadd_v2f16((__attribute__((address_space(3))) pf_f16x2*)p,
+                                          __builtin_bit_cast(pf_f16x2, pk));
+}
+
 template <int KIND, bool BF16>
-__global__ void __launch_bounds__(kPfThreads) prefill_kernel(PfArgs a) {
+__global__ void __launch_bounds__(2 * kPfThreads, 1) prefill_kernel(PfArgs a) {
   using C = PfCfg<KIND>;
-  constexpr int BK = C::bk, TS = C::ts, SPAN = C::span;
-  constexpr bool CODES = KIND != K_DENSE16 && KIND != K_DENSE_INT4;
-  constexpr int A_OFF = C::tab, B_OFF = C::tab + 128 * TS;
-  constexpr int AU = 128 * (BK / 8) / kPfThreads;  // 16-byte activation units per thread per step
+  constexpr int BK = C::bk, TS = C::ts, SPAN = C::span, BUF = C::buf;
+  constexpr bool CODES = KIND != K_DENSE16;
+  constexpr bool LUT = KIND == K_LUT3 || KIND == K_LUT4;
+  constexpr int A_OFF = C::tab, B_OFF = C::tab + 128 * TS;  // tile buffer b at + b * BUF
+  constexpr int AU = 128 * (BK / 8) / kPfThreads;           // 16-byte activation units per thread per step
+  constexpr int BU = CODES ? C::cpt : C::vpt / 8;           // 16-byte weight loads per thread per step
   __shared__ __attribute__((aligned(16))) uint32_t smem[C::lds / 4];  // the only LDS object: tables at address 0
 
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // Waves 0..3 read the tiles and run the MFMAs; waves 4..7 load, dequantise
+  // and stage the next step into the other tile buffer.
+  const int gwave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const bool stager = gwave >= 4;
+  const int tid = (int)threadIdx.x & (kPfThreads - 1), wave = gwave & 3, lane = tid & 63;
   const int n0 = blockIdx.x * kPfBN, m0 = blockIdx.y * kPfBM;
-  // the weight row this thread dequantises and its half of each step
-  const int nl = (wave & 1) * 64 + lane, half = wave >> 1, n = n0 + nl;
-  const uint32_t lanebase = (uint32_t)lane * 4u, ebias = (uint32_t)(wave & 1) * (KIND == K_LUT3 ? 64u : 16u);
+  const int s0 = blockIdx.z * a.steps_per_split;
+  const int s1 = min(s0 + a.steps_per_split, a.nsteps);
+  const bool has_csr = CODES && a.cptr != nullptr;
+  int32_t* s_cptr = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(smem) + C::cptr);
 
-  // ---- LUT tables of the 128 rows (two stacked lane-interleaved tables) ----
+  // ---- per-workgroup tables: LUTs of the 128 rows (two stacked lane-interleaved
+  // tables in the MFMA type, so a lookup yields the operand pair), the 2:4
+  // selectors, and the outlier offsets of this row tile ----
+  auto lut16 = [&](uint32_t h) -> uint32_t {
+    return BF16 ? to16<true>((float)__builtin_bit_cast(_Float16, (uint16_t)h)) : h;
+  };
   if constexpr (KIND == K_LUT3) {
-    for (int i = tid; i < 2 * 64 * 64; i += kPfThreads) {
-      const int g = i >> 12, e = (i >> 6) & 63, l = i & 63, row = n0 + g * 64 + l;
-      uint32_t v = 0;
-      if (row < a.Npad) {
-        const uint16_t* lt = a.table + (size_t)row * 8;
-        v = (uint32_t)lt[e & 7] | ((uint32_t)lt[e >> 3] << 16);
-      }
-      smem[(g * 64 + e) * 64 + l] = v;
+    const int r = (int)threadIdx.x & 127, e0 = 16 * ((int)threadIdx.x >> 7), row = n0 + r;
+    const uint4 lv = row < a.Npad ? reinterpret_cast<const uint4*>(a.table)[row] : make_uint4(0, 0, 0, 0);
+    const uint32_t lw[4] = {lv.x, lv.y, lv.z, lv.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = e0 + i, ca = e & 7, cb = e >> 3;
+      const uint32_t va = lut16((lw[ca >> 1] >> (16 * (ca & 1))) & 0xFFFFu);
+      const uint32_t vb = lut16((lw[cb >> 1] >> (16 * (cb & 1))) & 0xFFFFu);
+      smem[((r >> 6) * 64 + e) * 64 + (r & 63)] = va | (vb << 16);
     }
   } else if constexpr (KIND == K_LUT4) {
-    for (int i = tid; i < 2 * 16 * 64; i += kPfThreads) {
-      const int g = i >> 10, c = (i >> 6) & 15, l = i & 63, row = n0 + g * 64 + l;
-      smem[(g * 16 + c) * 64 + l] = row < a.Npad ? a.table[(size_t)row * 16 + c] : 0u;
-    }
-  } else if constexpr (KIND == K_INT4_24) {
-    if (tid < 16) {
-      const uint2 e = seltab_2_4_entry((uint32_t)tid);
-      smem[2 * tid] = e.x;
-      smem[2 * tid + 1] = e.y;
-    }
-  }
-  // integer formats: the row scale multiplies every dequantised weight of the row
-  half2_t rscale = {(_Float16)1.0f, (_Float16)1.0f};
-  if constexpr (is_int_kind<KIND>()) {
-    const _Float16 s = n < a.Npad ? __builtin_bit_cast(_Float16, a.table[n]) : (_Float16)0.0f;
-    rscale = half2_t{s, s};
-  }
-
-  // ---- outlier cursor of row n: the next four entries in column order ----
-  const bool has_csr = CODES && a.rowptr != nullptr;
-  int cp = 0, ce = 0, bcol[4];
-  float bval[4];
-  if (has_csr) {
-    cp = n < a.N ? a.rowptr[n] : 0;
-    ce = n < a.N ? a.rowptr[n + 1] : 0;
-  }
+    const int r = (int)threadIdx.x & 127, c0 = 4 * ((int)threadIdx.x >> 7), row = n0 + r;
+    const uint2 lv = row < a.Npad ? reinterpret_cast<const uint2*>(a.table)[(size_t)row * 4 + (c0 >> 2)] : make_uint2(0, 0);
+    const uint32_t lw[2] = {lv.x, lv.y};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool ok = cp + i < ce;
-    bcol[i] = ok ? a.col[cp + i] : 0x7FFFFFFF;
-    bval[i] = ok ? (float)__builtin_bit_cast(_Float16, a.val[cp + i]) : 0.f;
+    for (int i = 0; i < 4; ++i)
+      smem[((r >> 6) * 16 + c0 + i) * 64 + (r & 63)] = lut16((lw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+  } else if constexpr (KIND == K_INT4_24) {
+    if (threadIdx.x < 16) {
+      const uint2 e = seltab_2_4_entry((uint32_t)threadIdx.x);
+      smem[2 * threadIdx.x] = e.x;
+      smem[2 * threadIdx.x + 1] = e.y;
+    }
   }
+  if (has_csr) {
+    const int32_t* cp = a.cptr + (size_t)blockIdx.x * (a.nsteps_dense + 1);
+    for (int i = (int)threadIdx.x; i <= a.nsteps_dense; i += 2 * kPfThreads) s_cptr[i] = cp[i];
+  }
+  __syncthreads();
 
-  // ---- register stages of one step ----
-  uint4 xa[AU];        // activation units
-  uint4 wc[C::cpt];    // code chunks
-  uint2 wm[C::cpt];    // 2:4 metadata
-  auto load_step = [&](int s) {
-    // activations (dense steps only; the rank steps build theirs directly)
+  if (stager) {
+    // ---- staging waves ----
+    // the weight row this thread dequantises and its half of each step
+    const int nl = (wave & 1) * 64 + lane, half = wave >> 1, n = n0 + nl;
+    const uint32_t lanebase = (uint32_t)lane * 4u, ebias = (uint32_t)(wave & 1) * (KIND == K_LUT3 ? 64u : 16u);
+    // integer formats: the row scale multiplies every dequantised weight of the row
+    half2_t rscale = {(_Float16)1.0f, (_Float16)1.0f};
+    if constexpr (is_int_kind<KIND>()) {
+      const _Float16 sc = n < a.Npad ? __builtin_bit_cast(_Float16, a.table[n]) : (_Float16)0.0f;
+      rscale = half2_t{sc, sc};
+    }
+    // buffer resources: activation rows past M and weight rows past the
+    // stored ones fall outside and read as zero
+    const brsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.ldx * 2u);
+    const brsrc_t rd = make_rsrc(CODES ? (const void*)a.dense : (const void*)a.b16,
+                                 CODES ? (uint32_t)a.Npad * (uint32_t)a.chunks * 16u : (uint32_t)a.nb16 * (uint32_t)a.ldb16 * 2u);
+    const brsrc_t rm = make_rsrc(a.meta, KIND == K_INT4_24 ? (uint32_t)a.Npad * (uint32_t)a.chunks * 8u : 0u);
+    const brsrc_t rc = make_rsrc(a.cent, has_csr ? (uint32_t)s_cptr[a.nsteps_dense] * 4u : 0u);
+    uint32_t xoff[AU];
 #pragma unroll
     for (int i = 0; i < AU; ++i) {
       const int u = tid + i * kPfThreads, m = u / (BK / 8), kk = u - m * (BK / 8);
-      const int k = s * BK + 8 * kk;
-      const bool ok = s < a.nsteps_dense && m0 + m < a.M && k < a.ldx;
-      xa[i] = ok ? *reinterpret_cast<const uint4*>(a.x + (size_t)(m0 + m) * a.ldx + k) : make_uint4(0, 0, 0, 0);
+      xoff[i] = ((uint32_t)(m0 + m) * (uint32_t)a.ldx + 8u * kk) * 2u;
     }
-    if constexpr (CODES) {
-#pragma unroll
-      for (int q = 0; q < C::cpt; ++q) {
-        const int c = s * (BK / SPAN) + half * C::cpt + q;
-        const bool ok = s < a.nsteps_dense && c < a.chunks && n < a.Npad;
-        const size_t idx = (size_t)n * a.chunks + c;
-        wc[q] = ok ? a.dense[idx] : make_uint4(0, 0, 0, 0);
-        if constexpr (KIND == K_INT4_24)
-          wm[q] = ok ? reinterpret_cast<const uint2*>(a.meta)[idx] : make_uint2(0, 0);
-        else
-          wm[q] = make_uint2(0, 0);
-      }
-    }
-  };
+    const uint32_t woff = CODES ? ((uint32_t)n * (uint32_t)a.chunks + (uint32_t)(half * C::cpt)) * 16u
+                                : ((uint32_t)n * (uint32_t)a.ldb16 + (uint32_t)(half * C::vpt)) * 2u;
 
-  // 16-bit weight of the prologue source at (row n, k), as float
-  auto dense_w = [&](int k) -> float {
-    if (n >= a.N || k >= a.K) return 0.f;
-    if constexpr (KIND == K_DENSE16) {
-      const uint32_t u = a.b16[(size_t)n * a.K + k];
-      return a.b_bf16 ? __uint_as_float(u << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)u);
-    } else {
-      const uint32_t byte = a.b4[(size_t)n * ((a.K + 1) >> 1) + (k >> 1)];
-      const int q = (int)((byte >> (4 * (k & 1))) & 0xFu) - 8;
-      const int ng = (a.K + a.group - 1) / a.group;
-      return (float)q * (float)__builtin_bit_cast(_Float16, a.b4s[(size_t)n * ng + k / a.group]);
-    }
-  };
-  // rank-r factor R^T at (row n, j), as float
-  auto r_w = [&](int j) -> float {
-    if (n >= a.N || j >= a.rank) return 0.f;
-    if (a.lr_kind == CL_LR_INT4) {
-      const uint32_t byte = a.R[(size_t)n * ((a.rank + 1) >> 1) + (j >> 1)];
-      const int q = (int)((byte >> (4 * (j & 1))) & 0xFu) - 8;
-      const int ng = (a.rank + a.rgroup - 1) / a.rgroup;
-      return (float)q * (float)__builtin_bit_cast(_Float16, a.Rscale[(size_t)n * ng + j / a.rgroup]);
-    }
-    const uint32_t u = reinterpret_cast<const uint16_t*>(a.R)[(size_t)n * a.rank + j];
-    return a.lr_kind == CL_LR_BF16 ? __uint_as_float(u << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)u);
-  };
-
-  // ---- write step s into the LDS tiles ----
-  auto stage_step = [&](int s) {
-    if (s < a.nsteps_dense) {
+    // register stage of one step
+    struct Stage {
+      uint4 xa[AU];      // activation units
+      uint4 wb[BU];      // code chunks, or 16-bit weights
+      uint2 wm[C::cpt];  // 2:4 metadata
+      uint32_t ce;       // this thread's outlier entry of the step
+    };
+    auto load_step = [&](Stage& st, int s) {
+      // activations: only the last dense step can reach past the row (k >= ldx);
+      // everything below ldx is x' or the zero padding past K
+      if (s < a.nsteps_dense - 1) {
 #pragma unroll
-      for (int i = 0; i < AU; ++i) {
-        const int u = tid + i * kPfThreads, m = u / (BK / 8), kk = u - m * (BK / 8);
-        pf_st128(smem, (uint32_t)(A_OFF + m * TS + kk * 16), xa[i]);
-      }
-    } else {
-      // rank steps: virtual index v < rp -> t_hi[m][v], rp <= v < 2 rp -> t_lo[m][v - rp]
+        for (int i = 0; i < AU; ++i) st.xa[i] = bload128(rx, xoff[i], (uint32_t)(s * BK * 2));
+      } else {
 #pragma unroll
-      for (int i = 0; i < AU; ++i) {
-        const int u = tid + i * kPfThreads, m = u / (BK / 8), kk = u - m * (BK / 8);
-        const int v0 = (s - a.nsteps_dense) * BK + 8 * kk;
-        const bool lo = v0 >= a.rp;
-        const int j0 = lo ? v0 - a.rp : v0;
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = j0 + e;
-          const float tv = (m0 + m < a.M && v0 < 2 * a.rp && j < a.rank) ? a.t[(size_t)(m0 + m) * a.ldt + j] : 0.f;
-          const uint32_t hi = to16<BF16>(tv);
-          h[e] = lo ? to16<BF16>(tv - from16<BF16>(hi)) : hi;
+        for (int i = 0; i < AU; ++i) {
+          const int kk8 = 8 * ((tid + i * kPfThreads) % (BK / 8));
+          st.xa[i] = s * BK + kk8 < a.ldx ? bload128(rx, xoff[i], (uint32_t)(s * BK * 2)) : make_uint4(0, 0, 0, 0);
         }
-        pf_st128(smem, (uint32_t)(A_OFF + m * TS + kk * 16),
-                 make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16));
       }
-    }
-    const uint32_t brow = (uint32_t)(B_OFF + nl * TS + half * C::vpt * 2);
-    const int klo = s * BK + half * C::vpt;  // first k of this thread's part of the step
-    if (s < a.nsteps_dense) {
+      if constexpr (CODES) {
+        // chunks past a row's end only meet zero activations
+        const uint32_t so = (uint32_t)(s * (BK / SPAN)) * 16u;
+#pragma unroll
+        for (int q = 0; q < C::cpt; ++q) {
+          st.wb[q] = bload128(rd, woff + 16u * q, so);
+          if constexpr (KIND == K_INT4_24)
+            st.wm[q] = bload64(rm, (woff + 16u * q) >> 1, so >> 1);
+          else
+            st.wm[q] = make_uint2(0, 0);
+        }
+        st.ce = kPfNoEntry;
+        if (has_csr) {
+          const int e0 = s_cptr[s], cnt = s_cptr[s + 1] - e0;
+          if (tid < cnt) st.ce = bload32(rc, (uint32_t)(e0 + tid) * 4u, 0);
+        }
+      } else {
+        const int klo = s * BK + half * C::vpt;
+#pragma unroll
+        for (int j = 0; j < BU; ++j)
+          st.wb[j] = klo + 8 * j < a.ldb16 ? bload128(rd, woff + 16u * j, (uint32_t)(s * BK * 2)) : make_uint4(0, 0, 0, 0);
+      }
+    };
+    // dense step s from stage st into tile buffer buf
+    auto stage_dense = [&](const Stage& st, int s, int buf) {
+      const uint32_t bo = (uint32_t)(buf * BUF);
+#pragma unroll
+      for (int i = 0; i < AU; ++i) {
+        const int u = tid + i * kPfThreads, m = u / (BK / 8), kk = u - m * (BK / 8);
+        pf_st128(smem, bo + (uint32_t)(A_OFF + m * TS + kk * 16), st.xa[i]);
+      }
+      const uint32_t brow = bo + (uint32_t)(B_OFF + nl * TS + half * C::vpt * 2);
       if constexpr (CODES) {
 #pragma unroll
         for (int q = 0; q < C::cpt; ++q) {
           uint32_t wp[KindTraits<KIND>::pairs];
-          chunk_pairs<KIND, false>(smem, wc[q], make_uint4(wm[q].x, wm[q].y, 0, 0), lanebase, 0u, wp, ebias);
+          chunk_pairs<KIND, false>(smem, st.wb[q], make_uint4(st.wm[q].x, st.wm[q].y, 0, 0), lanebase, 0u, wp, ebias);
+          if constexpr (!LUT) {  // LUT tables already hold the MFMA type
 #pragma unroll
-          for (int j = 0; j < KindTraits<KIND>::pairs; ++j) {
-            if constexpr (is_int_kind<KIND>()) wp[j] = as_u32(as_h2(wp[j]) * rscale);
-            wp[j] = pair_to16<BF16>(wp[j]);
+            for (int j = 0; j < KindTraits<KIND>::pairs; ++j) wp[j] = pair_to16<BF16>(as_u32(as_h2(wp[j]) * rscale));
           }
 #pragma unroll
           for (int j = 0; j < KindTraits<KIND>::pairs / 4; ++j)
             pf_st128(smem, brow + (uint32_t)(q * SPAN * 2 + j * 16),
                      make_uint4(wp[4 * j], wp[4 * j + 1], wp[4 * j + 2], wp[4 * j + 3]));
         }
-        // outliers of row n inside [klo, klo + vpt): added to the tile entries
-        if (has_csr) {
-          const int khi = klo + C::vpt;
-          while (bcol[0] < khi) {
-            if (bcol[0] >= klo) {
-              const uint32_t ad = brow + (uint32_t)(bcol[0] - klo) * 2u;
-              const float w = from16<BF16>(lds_u16(smem, ad)) + bval[0];
-              *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(smem) + ad) = (uint16_t)to16<BF16>(w);
-            }
-            ++cp;
-            bcol[0] = bcol[1];
-            bcol[1] = bcol[2];
-            bcol[2] = bcol[3];
-            bval[0] = bval[1];
-            bval[1] = bval[2];
-            bval[2] = bval[3];
-            const bool ok = cp + 3 < ce;
-            bcol[3] = ok ? a.col[cp + 3] : 0x7FFFFFFF;
-            bval[3] = ok ? (float)__builtin_bit_cast(_Float16, a.val[cp + 3]) : 0.f;
-          }
-        }
       } else {
 #pragma unroll
-        for (int j = 0; j < C::vpt / 8; ++j) {
-          uint32_t h[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) h[e] = to16<BF16>(dense_w(klo + 8 * j + e));
-          pf_st128(smem, brow + (uint32_t)(j * 16),
-                   make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16));
-        }
+        for (int j = 0; j < BU; ++j) pf_st128(smem, brow + (uint32_t)(j * 16), st.wb[j]);
       }
-    } else {
-      // rank steps: R^T row n at virtual index v -> j = v mod rp
-      const int v0 = (s - a.nsteps_dense) * BK + half * C::vpt;
+    };
+    // outliers of dense step s, after the dequantised tile has landed
+    auto add_outliers = [&](const Stage& st, int s, int buf) {
+      if (!has_csr) return;
+      const uint32_t btile = (uint32_t)(buf * BUF + B_OFF);
+      if (st.ce != kPfNoEntry) pf_add_outlier<BF16, TS>(smem, btile, st.ce);
+      const int e0 = s_cptr[s], cnt = s_cptr[s + 1] - e0;
+      for (int i = kPfThreads + tid; i < cnt; i += kPfThreads) pf_add_outlier<BF16, TS>(smem, btile, a.cent[e0 + i]);
+    };
+    // rank step s: activations t_hi | t_lo and weights R^T | R^T, loaded directly
+    auto stage_rank = [&](int s, int buf) {
+      const uint32_t bo = (uint32_t)(buf * BUF);
+      const int k0 = (s - a.nsteps_dense) * BK;
+      const brsrc_t ra = make_rsrc(a.a2, (uint32_t)a.M * (uint32_t)a.lda2 * 2u);
+      const brsrc_t rr = make_rsrc(a.r16, (uint32_t)a.Npad * (uint32_t)a.ldr16 * 2u);
+      uint4 va[AU], vb[C::vpt / 8];
 #pragma unroll
-      for (int j = 0; j < C::vpt / 8; ++j) {
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int v = v0 + 8 * j + e;
-          const int jj = v < a.rp ? v : v - a.rp;
-          h[e] = v < 2 * a.rp ? to16<BF16>(r_w(jj)) : 0u;
-        }
-        pf_st128(smem, brow + (uint32_t)(j * 16),
-                 make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16));
+      for (int i = 0; i < AU; ++i) {
+        const int u = tid + i * kPfThreads, m = u / (BK / 8), kk = u - m * (BK / 8);
+        va[i] = k0 + 8 * kk < a.lda2 ? bload128(ra, ((uint32_t)(m0 + m) * (uint32_t)a.lda2 + (uint32_t)(k0 + 8 * kk)) * 2u, 0)
+                                     : make_uint4(0, 0, 0, 0);
       }
-    }
-  };
+      const int klo = k0 + half * C::vpt;
+#pragma unroll
+      for (int j = 0; j < C::vpt / 8; ++j)
+        vb[j] = klo + 8 * j < a.ldr16 ? bload128(rr, ((uint32_t)n * (uint32_t)a.ldr16 + (uint32_t)(klo + 8 * j)) * 2u, 0)
+                                      : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < AU; ++i) {
+        const int u = tid + i * kPfThreads, m = u / (BK / 8), kk = u - m * (BK / 8);
+        pf_st128(smem, bo + (uint32_t)(A_OFF + m * TS + kk * 16), va[i]);
+      }
+      const uint32_t brow = bo + (uint32_t)(B_OFF + nl * TS + half * C::vpt * 2);
+#pragma unroll
+      for (int j = 0; j < C::vpt / 8; ++j) pf_st128(smem, brow + (uint32_t)(j * 16), vb[j]);
+    };
 
-  // ---- main loop ----
+    // Three register stages in a ring, each loaded three steps before it is
+    // staged.  Step t goes into tile buffer (t - s0) mod 2.
+    const int sd = min(s1, a.nsteps_dense);
+    Stage S0, S1, S2;
+    if (s0 < sd) load_step(S0, s0);
+    if (s0 + 1 < sd) load_step(S1, s0 + 1);
+    if (s0 + 2 < sd) load_step(S2, s0 + 2);
+    if (s0 < sd) {
+      stage_dense(S0, s0, 0);
+      __syncthreads();
+      add_outliers(S0, s0, 0);
+      if (s0 + 3 < sd) load_step(S0, s0 + 3);
+    } else {
+      stage_rank(s0, 0);
+      __syncthreads();
+    }
+    __syncthreads();
+    // one step: stage step S + 1 from register stage NXT, refill NXT with step S + 4
+#define CL_PF_ITER(NXT, S)                          \
+  {                                                 \
+    const int t_ = (S) + 1, buf_ = ((t_ - s0) & 1); \
+    if (t_ < sd) {                                  \
+      stage_dense(NXT, t_, buf_);                   \
+      __syncthreads();                              \
+      add_outliers(NXT, t_, buf_);                  \
+      if (t_ + 3 < sd) load_step(NXT, t_ + 3);      \
+    } else {                                        \
+      if (t_ < s1) stage_rank(t_, buf_);            \
+      __syncthreads();                              \
+    }                                               \
+    __syncthreads();                                \
+  }
+    for (int s = s0; s < s1; s += 3) {
+      CL_PF_ITER(S1, s);
+      if (s + 1 < s1) CL_PF_ITER(S2, s + 1);
+      if (s + 2 < s1) CL_PF_ITER(S0, s + 2);
+    }
+#undef CL_PF_ITER
+    return;
+  }
+
+  // ---- MFMA waves: two barriers per step, matching the staging waves ----
   const int wm_ = wave & 1, wn_ = wave >> 1;
   pf_f32x16 acc[2][2];
 #pragma unroll
@@ -337,27 +385,32 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PfArgs a) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  __syncthreads();  // tables
-  load_step(0);
   const uint32_t arow = (uint32_t)(A_OFF + (wm_ * 64 + (lane & 31)) * TS + (lane >> 5) * 16);
-  const uint32_t bcol0 = (uint32_t)(B_OFF + (wn_ * 64 + (lane & 31)) * TS + (lane >> 5) * 16);
-  for (int s = 0; s < a.nsteps; ++s) {
-    stage_step(s);
-    __syncthreads();
-    if (s + 1 < a.nsteps) load_step(s + 1);
+  const uint32_t brow0 = (uint32_t)(B_OFF + (wn_ * 64 + (lane & 31)) * TS + (lane >> 5) * 16);
+  auto mma = [&](int buf, int ks0, int ks1) {
+    const uint32_t bo = (uint32_t)(buf * BUF);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const uint4 a0 = pf_lds128(smem, arow + ks * 32), a1 = pf_lds128(smem, arow + 32 * TS + ks * 32);
-      const uint4 b0 = pf_lds128(smem, bcol0 + ks * 32), b1 = pf_lds128(smem, bcol0 + 32 * TS + ks * 32);
+    for (int ks = ks0; ks < ks1; ++ks) {
+      const uint4 a0 = pf_lds128(smem, bo + arow + ks * 32), a1 = pf_lds128(smem, bo + arow + 32 * TS + ks * 32);
+      const uint4 b0 = pf_lds128(smem, bo + brow0 + ks * 32), b1 = pf_lds128(smem, bo + brow0 + 32 * TS + ks * 32);
       acc[0][0] = pf_mfma<BF16>(a0, b0, acc[0][0]);
       acc[0][1] = pf_mfma<BF16>(a0, b1, acc[0][1]);
       acc[1][0] = pf_mfma<BF16>(a1, b0, acc[1][0]);
       acc[1][1] = pf_mfma<BF16>(a1, b1, acc[1][1]);
     }
+  };
+  __syncthreads();  // first staged step: tile landed
+  __syncthreads();  // its outliers added
+  for (int s = s0; s < s1; ++s) {
+    const int buf = (s - s0) & 1;
+    mma(buf, 0, (BK / 16) / 2);
+    __syncthreads();
+    mma(buf, (BK / 16) / 2, BK / 16);
     __syncthreads();
   }
 
   // ---- store: lane l of block (i, j) holds column n = l mod 32, rows 8 (v/4) + 4 (l/32) + v mod 4 ----
+  float* yz = a.y + (size_t)blockIdx.z * a.ystride;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -366,15 +419,17 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(PfArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = m0 + wm_ * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (m < a.M && nn < a.ncols) a.y[(size_t)m * a.ldy + nn] = acc[i][j][v];
+        if (m < a.M && nn < a.ncols) yz[(size_t)m * a.ldy + nn] = acc[i][j][v];
       }
     }
 }
 
 template <int KIND, bool BF16>
 hipError_t launch_prefill_t(const PfArgs& a, hipStream_t st) {
-  dim3 grid((unsigned)ceil_div(a.ncols, kPfBN), (unsigned)ceil_div(a.M, kPfBM));
-  hipLaunchKernelGGL((prefill_kernel<KIND, BF16>), grid, dim3(kPfThreads), 0, st, a);
+  if (a.cptr && a.nsteps_dense > kPfMaxSteps) return hipErrorInvalidValue;
+  const int z = (int)ceil_div(a.nsteps, a.steps_per_split);
+  dim3 grid((unsigned)ceil_div(a.ncols, kPfBN), (unsigned)ceil_div(a.M, kPfBM), (unsigned)z);
+  hipLaunchKernelGGL((prefill_kernel<KIND, BF16>), grid, dim3(2 * kPfThreads), 0, st, a);
   return hipGetLastError();
 }
 

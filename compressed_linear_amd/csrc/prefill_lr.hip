@@ -3,5 +3,4 @@
 
 namespace cl {
 template hipError_t launch_prefill_kind<K_DENSE16>(const PfArgs&, bool, hipStream_t);
-template hipError_t launch_prefill_kind<K_DENSE_INT4>(const PfArgs&, bool, hipStream_t);
 }  // namespace cl

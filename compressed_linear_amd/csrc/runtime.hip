@@ -50,11 +50,31 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
   const size_t o_part = take((size_t)h.n_tiles * split * kMaxDecodeM * 64 * 4);
   size_t o_nzs = 0, o_t = 0, o_xp = 0;
   if (h.mask == CL_MASK_BITMAP) o_nzs = take((size_t)Npad * 4 * split * 4);
-  if (h.lr != CL_LR_NONE && h.rank > 0) o_t = take((size_t)max_M * round_up(h.rank, 8) * 4);  // row stride <= rank rounded to 8
+  // t = x' L: [max_M][rank] for decode; prefill keeps up to 8 K-split partials [8][max_M][rank rounded to 8]
+  if (h.lr != CL_LR_NONE && h.rank > 0) o_t = take((size_t)8 * max_M * round_up(h.rank, 8) * 4);
   // activations are restaged (clamped, row stride a multiple of 8 for aligned
   // 128-bit loads) when the layer clamps them or K is not a multiple of 8
   const int Kx = (int)round_up(h.K, 8);
   if (h.has_clamp || (h.K & 7)) o_xp = take((size_t)max_M * Kx * 2);
+  // matrix-core prefill (all formats but the bitmap): outlier lists per
+  // (128-row tile, K step), R^T twice and L^T in the MFMA input type, t_hi | t_lo
+  size_t o_pfp = 0, o_pfe = 0, o_pfr = 0, o_pfl = 0, o_pft = 0;
+  int pf_nd = 0;
+  const int rp = (int)round_up(h.rank, 8);
+  const bool has_lr = h.lr != CL_LR_NONE && h.rank > 0;
+  if (h.mask != CL_MASK_BITMAP) {
+    const int cps = pf_step_k(h.dense, h.mask) / kind_info(h.dense, h.mask).span;
+    pf_nd = (int)ceil_div(h.chunks, cps);
+    if (h.nnz > 0) {
+      o_pfp = take((size_t)ceil_div(Npad, kPfTileN) * (pf_nd + 1) * 4);
+      o_pfe = take((size_t)h.nnz * 4);
+    }
+    if (has_lr) {
+      o_pfr = take((size_t)Npad * 2 * rp * 2);
+      o_pfl = take((size_t)h.rank * Kx * 2);
+      o_pft = take((size_t)max_M * 2 * rp * 2);
+    }
+  }
   if (L) {
     uint8_t* d = L->dev;
     L->counters = reinterpret_cast<uint32_t*>(d + o_cnt);
@@ -63,9 +83,96 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
     L->t = o_t ? reinterpret_cast<float*>(d + o_t) : nullptr;
     L->xprep = o_xp ? reinterpret_cast<uint16_t*>(d + o_xp) : nullptr;
     L->Kx = Kx;
+    L->pf_nd = pf_nd;
+    L->pf_cptr = o_pfp ? reinterpret_cast<int32_t*>(d + o_pfp) : nullptr;
+    L->pf_cent = o_pfe ? reinterpret_cast<uint32_t*>(d + o_pfe) : nullptr;
+    L->pf_r16 = o_pfr ? reinterpret_cast<uint16_t*>(d + o_pfr) : nullptr;
+    L->pf_l16 = o_pfl ? reinterpret_cast<uint16_t*>(d + o_pfl) : nullptr;
+    L->pf_t16 = o_pft ? reinterpret_cast<uint16_t*>(d + o_pft) : nullptr;
+    L->pf_rp = rp;
+    L->pf_Kl = Kx;
     L->ws_bytes = off - align256(base);
   }
   return off;
+}
+
+// Host fp16 / bf16 helpers for the prefill's converted copies (round to nearest even).
+static float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+static float bf2f(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+static uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+static uint16_t f2bf(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Host-built inputs of the matrix-core prefill, from the blob: the outlier
+// lists per (128-row tile, K step) -- entry = row in tile | k in step << 7 |
+// fp16 value << 16, tiles in order, steps in order, rows then columns inside --
+// and the rank factors in the MFMA input type (bf16 for bf16 activations, else
+// fp16): R^T twice per row [Npad][2 rp], L^T rows padded to Kl = K rounded to 8.
+struct PrefillHost {
+  std::vector<int32_t> cptr;
+  std::vector<uint32_t> cent;
+  std::vector<uint16_t> r16, l16;
+};
+static void build_prefill_host(const cl_blob_header& h, const uint8_t* b, int Npad, int nd, int rp, int Kl,
+                               PrefillHost& out) {
+  const bool bf = h.x_dtype == CL_ACT_BF16;
+  auto to16 = [&](float f) { return bf ? f2bf(f) : f2h(f); };
+  if (h.nnz > 0) {
+    const int bk = pf_step_k(h.dense, h.mask), nt = (int)ceil_div(Npad, kPfTileN);
+    const int32_t* rp_ = reinterpret_cast<const int32_t*>(b + h.off[CL_SEC_ROWPTR]);
+    const int32_t* col = reinterpret_cast<const int32_t*>(b + h.off[CL_SEC_COL]);
+    const uint16_t* val = reinterpret_cast<const uint16_t*>(b + h.off[CL_SEC_VAL]);
+    out.cptr.assign((size_t)nt * (nd + 1), 0);
+    std::vector<int32_t> cnt((size_t)nt * nd, 0);
+    for (int n = 0; n < h.N; ++n)
+      for (int p = rp_[n]; p < rp_[n + 1]; ++p) ++cnt[(size_t)(n / kPfTileN) * nd + col[p] / bk];
+    int32_t acc = 0;
+    for (int t = 0; t < nt; ++t) {
+      for (int s = 0; s < nd; ++s) {
+        out.cptr[(size_t)t * (nd + 1) + s] = acc;
+        acc += cnt[(size_t)t * nd + s];
+      }
+      out.cptr[(size_t)t * (nd + 1) + nd] = acc;
+    }
+    out.cent.assign((size_t)h.nnz, 0);
+    std::vector<int32_t> fill((size_t)nt * nd);
+    for (int t = 0; t < nt; ++t)
+      for (int s = 0; s < nd; ++s) fill[(size_t)t * nd + s] = out.cptr[(size_t)t * (nd + 1) + s];
+    for (int n = 0; n < h.N; ++n)
+      for (int p = rp_[n]; p < rp_[n + 1]; ++p) {
+        const int s = col[p] / bk;
+        out.cent[fill[(size_t)(n / kPfTileN) * nd + s]++] =
+            (uint32_t)(n % kPfTileN) | ((uint32_t)(col[p] - s * bk) << 7) | ((uint32_t)val[p] << 16);
+      }
+  }
+  if (h.lr != CL_LR_NONE && h.rank > 0) {
+    const int r = h.rank, g = h.group > 0 ? h.group : 1;
+    const uint8_t* R = b + h.off[CL_SEC_R];
+    const uint8_t* Lf = b + h.off[CL_SEC_L];
+    const uint16_t* Rs = reinterpret_cast<const uint16_t*>(b + h.off[CL_SEC_RSCALE]);
+    const uint16_t* Ls = reinterpret_cast<const uint16_t*>(b + h.off[CL_SEC_LSCALE]);
+    auto factor = [&](const uint8_t* F, const uint16_t* S, int row, int j, int len) -> float {
+      if (h.lr == CL_LR_INT4) {
+        const int q = (int)((F[(size_t)row * ((len + 1) / 2) + j / 2] >> (4 * (j & 1))) & 0xF) - 8;
+        return (float)q * h2f(S[(size_t)row * ceil_div(len, g) + j / g]);
+      }
+      const uint16_t u = reinterpret_cast<const uint16_t*>(F)[(size_t)row * len + j];
+      return h.lr == CL_LR_BF16 ? bf2f(u) : h2f(u);
+    };
+    out.r16.assign((size_t)Npad * 2 * rp, 0);
+    for (int n = 0; n < Npad; ++n)
+      for (int j = 0; j < r; ++j) {
+        const uint16_t v = to16(factor(R, Rs, n, j, r));
+        out.r16[(size_t)n * 2 * rp + j] = v;
+        out.r16[(size_t)n * 2 * rp + rp + j] = v;
+      }
+    out.l16.assign((size_t)r * Kl, 0);
+    for (int j = 0; j < r; ++j)
+      for (int k = 0; k < h.K; ++k) out.l16[(size_t)j * Kl + k] = to16(factor(Lf, Ls, j, k, h.K));
+  }
 }
 
 template <class T>
@@ -147,10 +254,21 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
       }
     }
   }
+  PrefillHost pf;
+  if (h->mask != CL_MASK_BITMAP)
+    build_prefill_host(*h, static_cast<const uint8_t*>(blob), L->Npad, L->pf_nd, L->pf_rp, L->pf_Kl, pf);
   hipError_t e = hipMemcpyAsync(d, blob, h->total_bytes, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemsetAsync(L->counters, 0, (size_t)(h->n_tiles + ceil_div(max_M, 32) + 8) * 4, s);
   if (e == hipSuccess && !nzs.empty())
     e = hipMemcpyAsync(L->nzstart, nzs.data(), nzs.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !pf.cptr.empty())
+    e = hipMemcpyAsync(L->pf_cptr, pf.cptr.data(), pf.cptr.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !pf.cent.empty())
+    e = hipMemcpyAsync(L->pf_cent, pf.cent.data(), pf.cent.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !pf.r16.empty())
+    e = hipMemcpyAsync(L->pf_r16, pf.r16.data(), pf.r16.size() * 2, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !pf.l16.empty())
+    e = hipMemcpyAsync(L->pf_l16, pf.l16.data(), pf.l16.size() * 2, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     delete L;

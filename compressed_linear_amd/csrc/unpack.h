@@ -54,6 +54,29 @@ __device__ __forceinline__ void wait_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Raw buffer loads: a 32-bit per-lane byte offset plus a uniform one, and a
+// hardware range check against the buffer size (loads past it return zero).
+typedef __amdgpu_buffer_rsrc_t brsrc_t;
+typedef uint32_t bu32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ brsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload128(brsrc_t r, uint32_t voff, uint32_t soff) {
+  const bu32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 bload64(brsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef uint32_t bu32x2 __attribute__((ext_vector_type(2)));
+  const bu32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t bload32(brsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t bload16(brsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
 __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 __device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 
