@@ -34,7 +34,7 @@ METRIC = "batch-1 µs/layer & effective HBM GB/s (% of peak) for compressed GEMV
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_lut4_llama7b_b1_traffic.txt")
-KERNEL_SOURCES = ["compressed_linear_amd/csrc/decode_impl.h", "compressed_linear_amd/csrc/unpack.h",
+KERNEL_SOURCES = ["compressed_linear_amd/csrc/decode_rows.h", "compressed_linear_amd/csrc/unpack.h",
                   "compressed_linear_amd/csrc/decode.hip", "compressed_linear_amd/csrc/layout.h"]
 
 
@@ -238,7 +238,7 @@ def main():
     traffic = read_traffic(bytes_per_launch)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "decode_kernel (LUT4, batch 1)", "bytes_per_launch": int(bytes_per_launch),
+            "kernel": "decode_rows_kernel (LUT4 + CSR, batch 1)", "bytes_per_launch": int(bytes_per_launch),
             "us_per_launch": round(us_per_launch, 3)}
 
     cpu = None
