@@ -241,8 +241,7 @@ void make_plan(const cl_layer_desc* d, Plan& p) {
   p.total = off;
   p.acct.total = p.acct.codes + p.acct.lut_or_scale + p.acct.mask_meta + p.acct.csr + p.acct.lowrank;
   // every device byte of the packed sections that the canonical count does not include
-  const uint64_t canon_dev = p.acct.total - (bitmap ? 0 : 0);
-  p.acct.device_padding = dev_total > canon_dev ? dev_total - canon_dev : 0;
+  p.acct.device_padding = dev_total > p.acct.total ? dev_total - p.acct.total : 0;
 }
 
 template <class F>

@@ -74,8 +74,8 @@ typedef enum { CL_PATH_AUTO = 0, CL_PATH_DECODE = 1, CL_PATH_PREFILL = 2 } cl_pa
  *   dense = INT4 / INT8 : qvals [N*K] int8 (INT4: -8..7, INT8: -127..127);
  *                         row_scale [N] fp16 bits; D[n,k] = qvals[n,k] * row_scale[n].
  *   mask  = 2_4         : keep [N*K] 0/1, exactly two kept in each group of four
- *                         consecutive k (K % 4 == 0).  INT4 and INT8 only.
- *   mask  = BITMAP      : keep [N*K] 0/1, any pattern.  INT4 and INT8 only.
+ *                         consecutive k (K % 4 == 0).  INT4 only (CL_EUNSUPPORTED otherwise).
+ *   mask  = BITMAP      : keep [N*K] 0/1, any pattern.  INT8 only (CL_EUNSUPPORTED otherwise).
  *                         qvals at dropped positions are ignored.
  *   CSR                 : csr_row_ptr [N+1] int32 (row_ptr[0] = 0, nondecreasing,
  *                         row_ptr[N] = nnz), csr_col [nnz] int32 strictly
@@ -157,7 +157,10 @@ cl_status cl_pack(const cl_layer_desc* desc, void* blob, size_t* blob_bytes, cl_
  * cl_device_bytes -- device memory (bytes) that cl_create needs for `blob`
  * with forwards of up to max_M activation rows: the packed layer plus the
  * workspace (split-K partial sums, counters, the low-rank intermediate
- * x' L_hat).  Returns 0 if the blob is malformed or max_M < 1.
+ * x' L_hat, restaged activations) and the data the matrix-core path derives
+ * at create (outlier lists per 128-row tile and K step, the low-rank factors
+ * in the 16-bit MFMA input type).  Returns 0 if the blob is malformed or
+ * max_M < 1.
  */
 size_t cl_device_bytes(const void* blob, int32_t max_M);
 
@@ -168,7 +171,8 @@ size_t cl_device_bytes(const void* blob, int32_t max_M);
  *   dev_buf   device, at least cl_device_bytes(blob, max_M) bytes, 256-byte
  *             aligned, owned by the caller, must outlive the handle.
  *   max_M     largest M a later cl_forward will pass.
- *   stream    hipStream_t for the upload and the workspace clear.
+ *   stream    hipStream_t for the upload, the workspace clear and the
+ *             derived tables (built on the host from the blob, then copied).
  *   handle    out: opaque handle (host memory owned by the library).
  * Errors: CL_EINVAL (malformed blob, NULL or misaligned pointers),
  * CL_ENOMEM (dev_bytes too small), CL_EHIP (copy failed).
