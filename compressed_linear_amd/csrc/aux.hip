@@ -151,7 +151,7 @@ hipError_t launch_lowrank_prologue(const Layer& L, int M, const void* x, hipStre
 template <int KIND>
 __global__ void __launch_bounds__(256) debug_rows_kernel(const Layer L, uint16_t* __restrict__ D16) {
   constexpr int SPAN = KindTraits<KIND>::span, P = KindTraits<KIND>::pairs;
-  __shared__ uint32_t smem[(KIND == K_LUT3 || KIND == K_LUT4) ? 4 * 64 : 32];
+  __shared__ uint32_t smem[(KIND == K_LUT3 || KIND == K_LUT4) ? 4 * row_table_bytes<KIND>() / 4 : 32];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row0 = blockIdx.x * 4, n = row0 + wave;
   const int K = L.h.K, C = L.h.chunks;
@@ -168,7 +168,7 @@ __global__ void __launch_bounds__(256) debug_rows_kernel(const Layer L, uint16_t
       mw = make_uint4(mv.x, mv.y, 0, 0);
     }
     uint32_t wp[P];
-    chunk_pairs<KIND, true>(smem, w, mw, (uint32_t)(wave * 256), 0u, wp);
+    chunk_pairs<KIND, true>(smem, w, mw, (uint32_t)(wave * row_table_bytes<KIND>()), 0u, wp);
 #pragma unroll
     for (int j = 0; j < P; ++j) {
       const int k = c * SPAN + 2 * j;

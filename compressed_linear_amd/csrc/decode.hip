@@ -71,9 +71,11 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
     r.M = M;
     r.ldx = a.ldx;
     r.chunks = a.chunks;
-    r.rank = a.rank;
+    r.rank = h.lr != CL_LR_NONE ? a.rank : 0;
     r.group = a.group;
     r.lr_kind = a.lr_kind;
+    r.Npad = L.Npad;
+    r.nnz = (int)h.nnz;
     switch (h.dense) {
       case CL_DENSE_LUT3:
         if (rows_fit<K_LUT3>(r)) return launch_rows_kind<K_LUT3>(r, L.Npad, bf16, stream);

@@ -9,13 +9,20 @@
 // no cross-workgroup reduction.
 //
 // Each wavefront moves only a few KiB, so the kernel is shaped around latency:
-// every load a wavefront needs is issued before it waits for any of them
-// (row pointers and LUT values first, then the code stream in blocks of NB
-// passes, two blocks in flight), and nothing that depends on a load sits in
-// front of the code stream.  The activations are staged once per workgroup in
-// LDS (chunk c of row m at c * XS bytes, XS the chunk's activation bytes padded
-// so that eight lanes' 16-byte reads fall in distinct banks), which keeps them
-// out of the registers and lets the outlier gather read LDS instead of memory.
+// every load a wavefront needs is issued before it waits for any of them --
+// LUT values, the activation staging, the first two blocks of NB passes of
+// the code stream, the outlier heads and rank factors -- as a fixed sequence of
+// buffer loads without branches (an element that does not exist gets an
+// offset past the buffer, which reads zero).  The compiler can then count the
+// loads exactly and wait for each block just before it is used, so the
+// dequantisation of the first rows overlaps the arrival of the rest.
+//
+// The activations are staged once per workgroup in LDS (chunk c of row m at
+// c * XS bytes, XS the chunk's activation bytes padded so that eight lanes'
+// 16-byte reads fall in distinct banks), which keeps them out of the registers
+// and lets the outlier gather read LDS instead of memory.  The row tables are
+// the kernel's only static LDS array, at address 0, so the table addresses
+// built from the packed bytes are absolute.
 //
 // The outliers of a row ("SqueezeLLM: Dense-and-Sparse Quantization",
 // Approach: a full-precision CSR matrix) are spread over the 64 lanes, entry
@@ -46,15 +53,17 @@ struct RowArgs {
   const void* x;
   float* y;
   int K, N, M, ldx, chunks, rank, group, lr_kind;
+  int Npad;   // rows with storage (a multiple of 64)
+  int nnz;    // outliers in the layer
   int npass;  // ceil(chunks / 64)
   int xrow;   // LDS bytes per staged activation row (npass * 64 chunks)
-  int lds_t;  // byte offset of the low-rank intermediate in LDS
-  int lds_x;  // byte offset of the staged activations in LDS
+  int lds_t;  // byte offset of the low-rank intermediate in the dynamic LDS
+  int lds_x;  // byte offset of the staged activations in the dynamic LDS
 };
 
-// LDS bytes per chunk of staged activations: 2 * span rounded up to 16 * (odd
-// multiple of 1 in dwords mod 8), so lanes 0..7 of a 128-bit read hit 8
-// distinct groups of four banks.
+// LDS bytes per chunk of staged activations: the chunk's 2 * span bytes padded
+// so that the stride in dwords is 4 * (odd number) and lanes 0..7 of a 128-bit
+// read hit 8 distinct groups of four banks.
 template <int KIND>
 struct RowX {
   static constexpr int span = KindTraits<KIND>::span;
@@ -62,12 +71,17 @@ struct RowX {
   static constexpr int slots = stride / 16;  // 16-byte slots per chunk
 };
 
-// LDS bytes of the row tables in front of t: per wavefront R regions of 256 bytes
-// (LUT formats), the shared 2:4 selector table, or nothing.
+// Static LDS of the row tables: per wavefront R row tables (LUT3: 64 pair
+// entries, 256 bytes; LUT4: 256 pair entries, 1 KiB), the shared 2:4 selector
+// table, or a token array.
 template <int KIND, int R>
 constexpr int row_tab_bytes() {
-  return (KIND == K_LUT3 || KIND == K_LUT4) ? 4 * R * 256 : KIND == K_INT4_24 ? 256 : 0;
+  return (KIND == K_LUT3 || KIND == K_LUT4) ? 4 * R * row_table_bytes<KIND>() : KIND == K_INT4_24 ? 256 : 16;
 }
+
+// 16-byte activation slots each thread stages (the workgroup's activations must fit).
+template <int MB>
+constexpr int row_x_rounds() { return MB <= 2 ? 8 : 12; }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -96,17 +110,23 @@ __device__ __forceinline__ uint4 lds_u128(const uint32_t* lds, uint32_t byte_add
   return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(lds) + byte_addr);
 }
 
-// R = rows per wavefront, MB = activation rows (M <= MB), NB = passes per block.
-template <int KIND, int MB, bool BF16, int R, int NB>
+// R = rows per wavefront, MB = activation rows (M <= MB), NB = passes per block,
+// XR = activation slots staged per thread, LR = the layer has a low-rank part
+// (a template parameter so that layers without one carry no conditional loads,
+// which would make the compiler's load counting conservative).
+template <int KIND, int MB, bool BF16, int R, int NB, int XR, bool LR>
 __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   constexpr int SPAN = KindTraits<KIND>::span, P = KindTraits<KIND>::pairs, XD = SPAN / 8;  // 16-byte x slots per chunk
   constexpr int XS = RowX<KIND>::stride, XSL = RowX<KIND>::slots;
   constexpr bool LUT = KIND == K_LUT3 || KIND == K_LUT4;
-  extern __shared__ uint32_t smem[];  // the only LDS object: starts at address 0
+  constexpr uint32_t RTB = (uint32_t)row_table_bytes<KIND>();  // bytes of one row table
+  __shared__ __attribute__((aligned(16))) uint32_t stab[row_tab_bytes<KIND, R>() / 4];  // at LDS address 0
+  extern __shared__ __attribute__((aligned(16))) uint32_t sdyn[];                      // t, then the activations
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int row0 = (blockIdx.x * 4 + wave) * R;  // < Npad (the grid covers Npad exactly)
-  const uint32_t tabbase = (uint32_t)(wave * R * 256);
-  const bool has_csr = a.rowptr != nullptr, has_lr = a.lr_kind != CL_LR_NONE;
+  const int row0 = (blockIdx.x * 4 + wave) * R;  // rows row0 + r >= Npad read zeros and are not stored
+  const uint32_t tabbase = (uint32_t)wave * R * RTB;
+  const bool has_csr = a.rowptr != nullptr;
+  constexpr bool has_lr = LR;
 
   // ---- scalar loads: row pointers (uniform) ----
   int e0[R], e1[R];
@@ -119,55 +139,68 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
       e1[r] = has_csr ? rp[min(row0 + r + 1, a.N)] : 0;
     }
   }
-  // ---- LUT values (or the integer row scales) ----
-  uint32_t tv[R];
+
+  // ---- LUT values or integer row scales ----
+  // LUT4: lane l builds pair entries 4l..4l+3 = lut[4 (l & 3) + j] | lut[l >> 2] << 16.
+  // LUT3: lane l builds pair entry l = lut[l & 7] | lut[l >> 3] << 16.
+  constexpr uint32_t TB = KIND == K_LUT4 ? 32u : KIND == K_LUT3 ? 16u : 2u;  // table bytes per row
+  const brsrc_t rtab = make_rsrc(a.table, (uint32_t)a.Npad * TB);
+  uint32_t tva[R], tvb[R];
+  uint2 tv4[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
+    const uint32_t rb = (uint32_t)(row0 + r) * TB;
     if constexpr (KIND == K_LUT4) {
-      tv[r] = a.table[(size_t)(row0 + r) * 16 + (lane & 15)];
+      tv4[r] = bload64(rtab, rb + 8u * (lane & 3), 0);
+      tva[r] = bload16(rtab, rb + 2u * (lane >> 2), 0);
+      tvb[r] = 0;
     } else if constexpr (KIND == K_LUT3) {
-      const uint16_t* lt = a.table + (size_t)(row0 + r) * 8;
-      tv[r] = (uint32_t)lt[lane & 7] | ((uint32_t)lt[lane >> 3] << 16);  // pair entry (a, b) = lane
+      tva[r] = bload16(rtab, rb + 2u * (lane & 7), 0);
+      tvb[r] = bload16(rtab, rb + 2u * (lane >> 3), 0);
+      tv4[r] = make_uint2(0, 0);
     } else {
-      tv[r] = a.table[row0 + r];  // fp16 row scale
+      tva[r] = bload16(rtab, rb, 0);
+      tvb[r] = 0;
+      tv4[r] = make_uint2(0, 0);
     }
   }
 
-  // ---- activations, first round: issued before the code stream so that
-  // waiting for them does not wait for the codes ----
-  constexpr int XR0 = 8;  // 16-byte slots per thread in the first round
+  // ---- activations (and t): the workgroup stages them in LDS, zero past K and past M ----
   const int xch = a.npass * 64;  // staged chunks per row
   const int xslots = MB * xch * XSL;
-  const uint16_t* xg = static_cast<const uint16_t*>(a.x);
-  auto x_slot = [&](int s) -> uint4 {
+  const brsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.ldx * 2u);
+  uint4 xs[XR];
+#pragma unroll
+  for (int i = 0; i < XR; ++i) {
+    const int s = i * 256 + tid;
     const int m = s / (xch * XSL), rem = s - m * (xch * XSL), c = rem / XSL, d = rem - c * XSL;
     const int k = c * SPAN + 8 * d;
     const bool ok = s < xslots && d < XD && m < a.M && k < a.ldx;  // ldx: a multiple of 8, zero past K
-    return ok ? *reinterpret_cast<const uint4*>(xg + (size_t)m * a.ldx + k) : make_uint4(0, 0, 0, 0);
-  };
-  auto x_store = [&](int s, uint4 v) {
-    if (s < xslots) {
-      const int m = s / (xch * XSL), rem = s - m * (xch * XSL);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(smem) + a.lds_x + m * a.xrow + rem * 16) = v;
-    }
-  };
-  uint4 xs0[XR0];
+    xs[i] = bload128(rx, ok ? ((uint32_t)m * (uint32_t)a.ldx + (uint32_t)k) * 2u : kNoLoad, 0);
+  }
+  uint32_t ts[MB];
+  if constexpr (LR) {
+    const brsrc_t rt = make_rsrc(a.t, (uint32_t)a.M * (uint32_t)a.rank * 4u);
 #pragma unroll
-  for (int i = 0; i < XR0; ++i) xs0[i] = x_slot(i * 256 + tid);
+    for (int m = 0; m < MB; ++m)
+      ts[m] = bload32(rt, (tid < a.rank && m < a.M) ? ((uint32_t)m * (uint32_t)a.rank + (uint32_t)tid) * 4u : kNoLoad, 0);
+  }
 
-  // ---- the code stream: two blocks of NB passes in flight ----
+  // ---- the code stream: blocks of NB passes, two in flight ----
   const int nblk = (a.npass + NB - 1) / NB;
+  const brsrc_t rd = make_rsrc(a.dense, (uint32_t)a.Npad * (uint32_t)a.chunks * 16u);
+  const brsrc_t rm = make_rsrc(a.meta, KIND == K_INT4_24 ? (uint32_t)a.Npad * (uint32_t)a.chunks * 8u : 0u);
   auto load_blk = [&](uint4 (&w)[NB][R], uint2 (&mw)[NB][R], int b) {
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
       const int c = (b * NB + q) * 64 + lane;
-      const bool ok = b < nblk && c < a.chunks;
+      const bool okc = b < nblk && c < a.chunks;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const size_t idx = (size_t)(row0 + r) * a.chunks + c;
-        w[q][r] = ok ? a.dense[idx] : make_uint4(0, 0, 0, 0);
+        const uint32_t idx = (uint32_t)(row0 + r) * (uint32_t)a.chunks + (uint32_t)c;  // rows past Npad: out of range
+        w[q][r] = bload128(rd, okc ? idx * 16u : kNoLoad, 0);
         if constexpr (KIND == K_INT4_24)
-          mw[q][r] = ok ? reinterpret_cast<const uint2*>(a.meta)[idx] : make_uint2(0, 0);
+          mw[q][r] = bload64(rm, okc ? idx * 8u : kNoLoad, 0);
         else
           mw[q][r] = make_uint2(0, 0);
       }
@@ -179,68 +212,69 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   load_blk(WB, MB_, 1);
 
   // ---- outlier heads and rank factors (consumed at the end) ----
+  const brsrc_t rcol = make_rsrc(a.col, (uint32_t)a.nnz * 4u), rval = make_rsrc(a.val, (uint32_t)a.nnz * 2u);
   int ccol[R];
   float cval[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int e = e0[r] + lane;
     const bool ok = e < e1[r];
-    ccol[r] = ok ? a.col[e] : 0;
-    cval[r] = ok ? (float)__builtin_bit_cast(_Float16, a.val[e]) : 0.f;
+    ccol[r] = (int)bload32(rcol, ok ? (uint32_t)e * 4u : kNoLoad, 0);
+    cval[r] = (float)__builtin_bit_cast(_Float16, (uint16_t)bload16(rval, ok ? (uint32_t)e * 2u : kNoLoad, 0));
   }
   float rv[R][4];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = lane + 64 * i, n = row0 + r;
-      float v = 0.f;
-      if (has_lr && j < a.rank) {
-        if (a.lr_kind == CL_LR_INT4) {  // R^T codes [Npad][ceil(r/2)], scales [Npad][ceil(r/g)]
-          const int gr = (a.rank + a.group - 1) / a.group;
-          const uint32_t byte = a.R[(size_t)n * ((a.rank + 1) >> 1) + (j >> 1)];
-          const int qv = (int)((byte >> (4 * (j & 1))) & 0xFu) - 8;
-          v = (float)qv * (float)__builtin_bit_cast(_Float16, a.Rscale[(size_t)n * gr + j / a.group]);
-        } else {  // R^T [Npad][r]
-          const uint16_t u = reinterpret_cast<const uint16_t*>(a.R)[(size_t)n * a.rank + j];
-          v = a.lr_kind == CL_LR_BF16 ? __uint_as_float((uint32_t)u << 16) : (float)__builtin_bit_cast(_Float16, u);
-        }
-      }
-      rv[r][i] = v;
-    }
-
-  // ---- stage the activations (and t) in LDS, zero past K and past M ----
-  {
-#pragma unroll
-    for (int i = 0; i < XR0; ++i) x_store(i * 256 + tid, xs0[i]);
-    for (int s0 = XR0 * 256; s0 < xslots; s0 += 4 * 256) {
-      uint4 v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = x_slot(s0 + i * 256 + tid);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x_store(s0 + i * 256 + tid, v[i]);
-    }
-    if (has_lr) {
-      float* s_t = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem) + a.lds_t);
-      for (int i = tid; i < MB * 256; i += 256) {
-        const int m = i >> 8, j = i & 255;
-        s_t[i] = (j < a.rank && m < a.M) ? a.t[m * a.rank + j] : 0.f;
-      }
-    }
-  }
-  // ---- tables: per-wavefront row tables, or the shared selector table ----
-  if constexpr (KIND == K_LUT4) {
+  if constexpr (LR) {
+    const bool lr4 = a.lr_kind == CL_LR_INT4;
+    const int gr = lr4 ? (a.rank + a.group - 1) / a.group : 1;
+    const brsrc_t rR = make_rsrc(a.R, (uint32_t)a.Npad * (uint32_t)(lr4 ? (a.rank + 1) / 2 : a.rank * 2));
+    const brsrc_t rRs = make_rsrc(a.Rscale, lr4 ? (uint32_t)a.Npad * (uint32_t)gr * 2u : 0u);
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (lane < 16) smem[(tabbase >> 2) + r * 64 + lane] = tv[r];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        const uint32_t n = (uint32_t)(row0 + r);
+        const bool ok = j < a.rank;  // rows past Npad are out of range
+        // int4: R^T codes [Npad][ceil(r/2)], scales [Npad][ceil(r/g)]; else R^T [Npad][r] 16-bit
+        const uint32_t byte = bload8(rR, ok && lr4 ? n * (uint32_t)((a.rank + 1) >> 1) + (uint32_t)(j >> 1) : kNoLoad, 0);
+        const uint32_t sc = bload16(rRs, ok && lr4 ? (n * (uint32_t)gr + (uint32_t)(j / a.group)) * 2u : kNoLoad, 0);
+        const uint32_t u = bload16(rR, ok && !lr4 ? (n * (uint32_t)a.rank + (uint32_t)j) * 2u : kNoLoad, 0);
+        const int qv = (int)((byte >> (4 * (j & 1))) & 0xFu) - 8;
+        const float v4 = ok ? (float)qv * (float)__builtin_bit_cast(_Float16, (uint16_t)sc) : 0.f;
+        const float v16 = a.lr_kind == CL_LR_BF16 ? __uint_as_float(u << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)u);
+        rv[r][i] = lr4 ? v4 : v16;
+      }
+  }
+
+  // ---- LDS: activations, t, tables ----
+#pragma unroll
+  for (int i = 0; i < XR; ++i) {
+    const int s = i * 256 + tid;
+    if (s < xslots) {
+      const int m = s / (xch * XSL), rem = s - m * (xch * XSL);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(sdyn) + a.lds_x + m * a.xrow + rem * 16) = xs[i];
+    }
+  }
+  if constexpr (LR) {
+    float* s_t = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(sdyn) + a.lds_t);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) s_t[m * 256 + tid] = __uint_as_float(ts[m]);
+  }
+  if constexpr (KIND == K_LUT4) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t hi = tva[r] << 16;
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(stab) + tabbase + r * RTB + 16 * lane) =
+          make_uint4((tv4[r].x & 0xFFFFu) | hi, (tv4[r].x >> 16) | hi, (tv4[r].y & 0xFFFFu) | hi, (tv4[r].y >> 16) | hi);
+    }
   } else if constexpr (KIND == K_LUT3) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) smem[(tabbase >> 2) + r * 64 + lane] = tv[r];
+    for (int r = 0; r < R; ++r) stab[(tabbase >> 2) + r * 64 + lane] = tva[r] | (tvb[r] << 16);
   } else if constexpr (KIND == K_INT4_24) {
     if (tid < 16) {
       const uint2 e = seltab_2_4_entry((uint32_t)tid);
-      smem[2 * tid] = e.x;
-      smem[2 * tid + 1] = e.y;
+      stab[2 * tid] = e.x;
+      stab[2 * tid + 1] = e.y;
     }
   }
   __syncthreads();
@@ -262,7 +296,7 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
         for (int m = 0; m < MB; ++m)
 #pragma unroll
           for (int d = 0; d < XD; ++d) {
-            const uint4 v = lds_u128(smem, (uint32_t)(a.lds_x + m * a.xrow + c * XS + 16 * d));
+            const uint4 v = lds_u128(sdyn, (uint32_t)(a.lds_x + m * a.xrow + c * XS + 16 * d));
             xv[m][4 * d] = v.x;
             xv[m][4 * d + 1] = v.y;
             xv[m][4 * d + 2] = v.z;
@@ -271,7 +305,7 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           uint32_t wp[P];
-          chunk_pairs<KIND, true>(smem, w[q][r], make_uint4(mw[q][r].x, mw[q][r].y, 0, 0), tabbase + (uint32_t)(r * 256),
+          chunk_pairs<KIND, true>(stab, w[q][r], make_uint4(mw[q][r].x, mw[q][r].y, 0, 0), tabbase + (uint32_t)r * RTB,
                                   0u, wp);
 #pragma unroll
           for (int m = 0; m < MB; ++m)
@@ -281,20 +315,23 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
       }
     }
   };
-  for (int b = 0; b < nblk; b += 2) {
+  // the first two blocks outside the loop, so that their waits are exact
+  comp_blk(WA, MA, 0);
+  load_blk(WA, MA, 2);
+  comp_blk(WB, MB_, 1);
+  load_blk(WB, MB_, 3);
+  for (int b = 2; b < nblk; b += 2) {
     comp_blk(WA, MA, b);
-    if (b + 2 < nblk) load_blk(WA, MA, b + 2);
-    if (b + 1 < nblk) {
-      comp_blk(WB, MB_, b + 1);
-      if (b + 3 < nblk) load_blk(WB, MB_, b + 3);
-    }
+    load_blk(WA, MA, b + 2);
+    comp_blk(WB, MB_, b + 1);
+    load_blk(WB, MB_, b + 3);
   }
 
   // ---- integer formats: the row scale multiplies the dense part only ----
   if constexpr (!LUT) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)tv[r]);
+      const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)tva[r]);
 #pragma unroll
       for (int m = 0; m < MB; ++m) acc[r][m] *= sc;
     }
@@ -302,7 +339,7 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   // ---- outliers: activations gathered from LDS ----
   auto x_lds = [&](int m, int k) -> float {
     const int c = k / SPAN, o = k - c * SPAN;
-    return act_f32<BF16>(lds_u16(smem, (uint32_t)(a.lds_x + m * a.xrow + c * XS + 2 * o)));
+    return act_f32<BF16>(lds_u16(sdyn, (uint32_t)(a.lds_x + m * a.xrow + c * XS + 2 * o)));
   };
   if (has_csr) {
 #pragma unroll
@@ -318,8 +355,8 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
     }
   }
   // ---- rank terms: t (LDS) times R^T ----
-  if (has_lr) {
-    const float* s_t = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(smem) + a.lds_t);
+  if constexpr (LR) {
+    const float* s_t = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(sdyn) + a.lds_t);
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -338,34 +375,39 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
     }
 }
 
-// Largest LDS a row-wise workgroup may take; larger activation blocks go to the tile kernel.
+// Largest dynamic LDS a row-wise workgroup may take; larger activation blocks go to the tile kernel.
 constexpr int kRowsMaxLds = 64 * 1024;
 
-template <int KIND, int MB, int R>
+template <int KIND, int MB>
 inline int rows_lds_layout(RowArgs& a) {
   a.npass = (a.chunks + 63) / 64;
   a.xrow = a.npass * 64 * RowX<KIND>::stride;
-  a.lds_t = row_tab_bytes<KIND, R>();
-  a.lds_x = a.lds_t + (a.lr_kind != CL_LR_NONE ? MB * 256 * 4 : 0);
+  a.lds_t = 0;
+  a.lds_x = a.lr_kind != CL_LR_NONE ? MB * 256 * 4 : 0;
   return a.lds_x + MB * a.xrow;
 }
 
 template <int KIND, int MB, bool BF16, int R>
 static hipError_t launch_rows_t(RowArgs a, int Npad, hipStream_t st) {
-  const int lds = rows_lds_layout<KIND, MB, R>(a);
-  if (lds > kRowsMaxLds) return hipErrorInvalidConfiguration;
-  const int grid = Npad / (4 * R);  // Npad is a multiple of 64, so of 4 * R
-  hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2>), dim3(grid), dim3(256), lds, st, a);
+  const int lds = rows_lds_layout<KIND, MB>(a);
+  if (lds > kRowsMaxLds || MB * a.npass * 64 * RowX<KIND>::slots > row_x_rounds<MB>() * 256 || a.rank > 256)
+    return hipErrorInvalidConfiguration;
+  const int grid = (Npad + 4 * R - 1) / (4 * R);
+  if (a.lr_kind != CL_LR_NONE)
+    hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, row_x_rounds<MB>(), true>), dim3(grid), dim3(256), lds, st, a);
+  else
+    hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, row_x_rounds<MB>(), false>), dim3(grid), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
-// Whether the row-wise kernel takes this shape (its staged activations fit in LDS).
+// Whether the row-wise kernel takes this shape (its staged activations fit in LDS
+// and in the threads' staging registers).
 template <int KIND>
 bool rows_fit(RowArgs a) {
   const int mb = a.M <= 1 ? 1 : a.M <= 2 ? 2 : 4;
-  const int lds = mb == 1 ? rows_lds_layout<KIND, 1, 2>(a) : mb == 2 ? rows_lds_layout<KIND, 2, 1>(a)
-                                                                     : rows_lds_layout<KIND, 4, 1>(a);
-  return lds <= kRowsMaxLds;
+  const int lds = mb == 1 ? rows_lds_layout<KIND, 1>(a) : mb == 2 ? rows_lds_layout<KIND, 2>(a) : rows_lds_layout<KIND, 4>(a);
+  const int rounds = mb <= 2 ? row_x_rounds<1>() : row_x_rounds<4>();
+  return lds <= kRowsMaxLds && mb * a.npass * 64 * RowX<KIND>::slots <= rounds * 256;
 }
 
 // Rows per wavefront: two for one activation row on layers of at least 8192

@@ -21,8 +21,10 @@
 //           p_0..p_3 : bits 2..7 of byte j (so the byte reads 4 * p_j);
 //           p_4      : bits 0..1 of bytes 0, 1, 2 (two bits each, low bits first);
 //         bits 0..1 of byte 3 are zero.
-//   LUT4  span 32: word i holds codes k = 32c + 8i + t at bits 4t..4t+3
-//         (canonical order, least significant nibble first).
+//   LUT4  span 32: word i holds codes k = 32c + 8i + t, t = 0..7; byte b of the
+//         word holds the pair p_b = code[2b] | code[2b+1] << 4 rotated left by
+//         two bits, so that bits 2..7 of the byte read 4 * (p_b mod 64) and bits
+//         0..1 read p_b / 64 (a 1 KiB pair table is addressed with one v_perm).
 //   INT4  span 32 (no mask): word i holds u = q + 8 of k = 32c + 8i + t; the
 //         pair (2j, 2j+1) sits at bits 4j..4j+3 and 16+4j..16+4j+3.
 //   INT4 + 2:4, span 64: 16 groups of four k per chunk.  DENSE word i holds

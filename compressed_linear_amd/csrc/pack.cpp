@@ -288,9 +288,10 @@ void pack_dense(const cl_layer_desc* d, const Plan& p, uint8_t* blob) {
         uint32_t* w = reinterpret_cast<uint32_t*>(chunk_ptr(dense, tile, c, lane, 16));
         for (int i = 0; i < 4; ++i) {
           uint32_t v = 0;
-          for (int t = 0; t < 8; ++t) {
-            const int64_t k = 32 * c + 8 * i + t;
-            v |= (k < K ? (uint32_t)row[k] : 0u) << (4 * t);
+          for (int b = 0; b < 4; ++b) {  // byte b: pair p = code(2b) | code(2b+1) << 4, rotated left by 2
+            const int64_t k = 32 * c + 8 * i + 2 * b;
+            const uint32_t pr = (k < K ? (uint32_t)row[k] : 0u) | ((k + 1 < K ? (uint32_t)row[k + 1] : 0u) << 4);
+            v |= (((pr << 2) | (pr >> 6)) & 0xFFu) << (8 * b);
           }
           w[i] = v;
         }

@@ -76,6 +76,12 @@ __device__ __forceinline__ uint32_t bload32(brsrc_t r, uint32_t voff, uint32_t s
 __device__ __forceinline__ uint32_t bload16(brsrc_t r, uint32_t voff, uint32_t soff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
+__device__ __forceinline__ uint32_t bload8(brsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+// A buffer offset past any buffer this library makes (all are below 2 GiB):
+// the load returns zero.
+constexpr uint32_t kNoLoad = 0x80000000u;
 
 __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 __device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
@@ -123,21 +129,22 @@ __device__ __forceinline__ void lut3_word_row(const uint32_t* lds, uint32_t w, u
   out[4] = lds_u32(lds, perm(p4, rowbase, 0x03020106u));
 }
 
-// 4-bit LUT, row table of 16 entries: the codes times 4 go into address byte 0.
-__device__ __forceinline__ void lut4_word_row(const uint32_t* lds, uint32_t w, uint32_t rowbase, uint32_t out[4]) {
-  const uint32_t ev = (w << 2) & 0x3C3C3C3Cu;  // 4 * code of even k, one per byte
-  const uint32_t od = (w >> 2) & 0x3C3C3C3Cu;  // 4 * code of odd k
-  uint32_t lo[4], hi[4];
-  lo[0] = lds_u16(lds, perm(ev, rowbase, 0x03020104u));
-  hi[0] = lds_u16(lds, perm(od, rowbase, 0x03020104u));
-  lo[1] = lds_u16(lds, perm(ev, rowbase, 0x03020105u));
-  hi[1] = lds_u16(lds, perm(od, rowbase, 0x03020105u));
-  lo[2] = lds_u16(lds, perm(ev, rowbase, 0x03020106u));
-  hi[2] = lds_u16(lds, perm(od, rowbase, 0x03020106u));
-  lo[3] = lds_u16(lds, perm(ev, rowbase, 0x03020107u));
-  hi[3] = lds_u16(lds, perm(od, rowbase, 0x03020107u));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) out[j] = perm(hi[j], lo[j], 0x05040100u);
+// 4-bit LUT, row pair table of 256 entries (entry p = lut[p & 15] | lut[p >> 4]
+// << 16) at rowbase, a multiple of 1024 below 64 KiB.  The packed byte holds
+// the pair rotated left by 2: its bits 2..7 are address byte 0 (4 * (p mod 64)),
+// its bits 0..1 with the row base form address byte 1.
+__device__ __forceinline__ void lut4_pair_row(const uint32_t* lds, uint32_t w, uint32_t rowbase, uint32_t out[4]) {
+  const uint32_t lo = w & 0xFCFCFCFCu;
+  const uint32_t hi = (w & 0x03030303u) | ((rowbase >> 8) * 0x01010101u);
+  out[0] = lds_u32(lds, perm(hi, lo, 0x0C0C0400u));
+  out[1] = lds_u32(lds, perm(hi, lo, 0x0C0C0501u));
+  out[2] = lds_u32(lds, perm(hi, lo, 0x0C0C0602u));
+  out[3] = lds_u32(lds, perm(hi, lo, 0x0C0C0703u));
+}
+
+// The canonical nibble order of a packed LUT4 word (each byte rotated back right by 2).
+__device__ __forceinline__ uint32_t lut4_canon(uint32_t w) {
+  return ((w >> 2) & 0x3F3F3F3Fu) | ((w << 6) & 0xC0C0C0C0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -145,6 +152,7 @@ __device__ __forceinline__ void lut4_word_row(const uint32_t* lds, uint32_t w, u
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void lut4_word(const uint32_t* lds, uint32_t w, uint32_t lanebase, uint32_t out[4],
                                          uint32_t ebias = 0) {
+  w = lut4_canon(w);
   const uint32_t ev = (w & 0x0F0F0F0Fu) | (ebias * 0x01010101u);         // codes of even k, one per byte
   const uint32_t od = ((w >> 4) & 0x0F0F0F0Fu) | (ebias * 0x01010101u);  // codes of odd k
   uint32_t lo[4], hi[4];
@@ -268,7 +276,7 @@ __device__ __forceinline__ void chunk_pairs(const uint32_t* lds, uint4 w, uint4 
     for (int i = 0; i < 4; ++i) lut3_word_row(lds, ww[i], lanebase, &wp[5 * i]);
   } else if constexpr (KIND == K_LUT4 && ROWTAB) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lut4_word_row(lds, ww[i], lanebase, &wp[4 * i]);
+    for (int i = 0; i < 4; ++i) lut4_pair_row(lds, ww[i], lanebase, &wp[4 * i]);
   } else if constexpr (KIND == K_LUT3) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) lut3_word(lds, ww[i], lanebase, &wp[5 * i], ebias);
@@ -333,9 +341,11 @@ __device__ __forceinline__ void build_tables(uint32_t* smem, const uint16_t* tab
   }
 }
 
-// Per-row LUT tables of `nrows` consecutive rows starting at row0 (row q at
-// dword q*64; LUT3: 64 pair entries, LUT4: 16 single entries); the 2:4 and
-// bitmap selector tables at address 0 as for the tile tables.
+// Per-row LUT tables of `nrows` consecutive rows starting at row0 (LUT3: 64
+// pair entries, row q at byte q*256; LUT4: 256 pair entries, row q at byte
+// q*1024); the 2:4 and bitmap selector tables at address 0 as for the tile tables.
+template <int KIND>
+constexpr int row_table_bytes() { return KIND == K_LUT4 ? 1024 : 256; }
 template <int KIND>
 __device__ __forceinline__ void build_row_tables(uint32_t* smem, const uint16_t* table, int row0, int nrows, int tid,
                                                  int nthreads) {
@@ -346,9 +356,10 @@ __device__ __forceinline__ void build_row_tables(uint32_t* smem, const uint16_t*
       smem[q * 64 + e] = (uint32_t)lt[ca] | ((uint32_t)lt[cb] << 16);
     }
   } else if constexpr (KIND == K_LUT4) {
-    for (int i = tid; i < nrows * 16; i += nthreads) {
-      const int q = i >> 4, c = i & 15;
-      smem[q * 64 + c] = table[(size_t)(row0 + q) * 16 + c];
+    for (int i = tid; i < nrows * 256; i += nthreads) {
+      const int q = i >> 8, e = i & 255;
+      const uint16_t* lt = table + (size_t)(row0 + q) * 16;
+      smem[q * 256 + e] = (uint32_t)lt[e & 15] | ((uint32_t)lt[e >> 4] << 16);
     }
   } else {
     build_tables<KIND>(smem, table, 0, tid, nthreads < 64 ? 64 : nthreads);

@@ -39,9 +39,13 @@ def unpack(blob):
                     kk = np.arange(C * 4)[:, None] * 10 + 2 * j + half
                     codes[:, kk[:, 0]] = ((p >> (3 * half)) & 7).astype(np.uint8)
         else:
+            # byte b of a word: pair p = code(2b) | code(2b+1) << 4, rotated left by 2
             codes = np.zeros((Npad, C * 32), np.uint8)
-            for t in range(8):
-                codes[:, t::8] = ((rows >> (4 * t)) & 0xF).astype(np.uint8)
+            for b in range(4):
+                byte = (rows >> (8 * b)) & 0xFF
+                pr = ((byte >> 2) | (byte << 6)) & 0xFF
+                codes[:, 2 * b::8] = (pr & 0xF).astype(np.uint8)
+                codes[:, 2 * b + 1::8] = (pr >> 4).astype(np.uint8)
         out["codes"] = codes[:N, :K]
         nb = 8 if dense_kind == "lut3" else 16
         out["lut"] = _sec(blob, h, "table", np.uint16).reshape(Npad, nb)[:N].view(np.float16)
