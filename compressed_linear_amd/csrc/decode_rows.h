@@ -79,7 +79,8 @@ constexpr int row_tab_bytes() {
   return (KIND == K_LUT3 || KIND == K_LUT4) ? 4 * R * row_table_bytes<KIND>() : KIND == K_INT4_24 ? 256 : 16;
 }
 
-// 16-byte activation slots each thread stages (the workgroup's activations must fit).
+// 16-byte activation slots each thread stages per round (the first round is
+// issued before the code stream, further rounds after it).
 template <int MB>
 constexpr int row_x_rounds() { return MB <= 2 ? 8 : 12; }
 
@@ -255,6 +256,26 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
       *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(sdyn) + a.lds_x + m * a.xrow + rem * 16) = xs[i];
     }
   }
+  // activation blocks larger than one round of XR slots per thread: further
+  // rounds, loaded after the code stream is in flight (their wait covers it)
+  for (int base = XR * 256; base < xslots; base += XR * 256) {
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const int s = base + i * 256 + tid;
+      const int m = s / (xch * XSL), rem = s - m * (xch * XSL), c = rem / XSL, d = rem - c * XSL;
+      const int k = c * SPAN + 8 * d;
+      const bool ok = s < xslots && d < XD && m < a.M && k < a.ldx;
+      xs[i] = bload128(rx, ok ? ((uint32_t)m * (uint32_t)a.ldx + (uint32_t)k) * 2u : kNoLoad, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const int s = base + i * 256 + tid;
+      if (s < xslots) {
+        const int m = s / (xch * XSL), rem = s - m * (xch * XSL);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(sdyn) + a.lds_x + m * a.xrow + rem * 16) = xs[i];
+      }
+    }
+  }
   if constexpr (LR) {
     float* s_t = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(sdyn) + a.lds_t);
 #pragma unroll
@@ -387,27 +408,42 @@ inline int rows_lds_layout(RowArgs& a) {
   return a.lds_x + MB * a.xrow;
 }
 
+template <int KIND, int MB, bool BF16, int R, int XR>
+static void launch_rows_xr(const RowArgs& a, int grid, int lds, hipStream_t st) {
+  if (a.lr_kind != CL_LR_NONE)
+    hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, XR, true>), dim3(grid), dim3(256), lds, st, a);
+  else
+    hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, XR, false>), dim3(grid), dim3(256), lds, st, a);
+}
+
+// One activation row: the first staging round is sized to the activation block
+// (2, 4 or 8 slots per thread), so that short rows hold no idle staging registers.
 template <int KIND, int MB, bool BF16, int R>
 static hipError_t launch_rows_t(RowArgs a, int Npad, hipStream_t st) {
   const int lds = rows_lds_layout<KIND, MB>(a);
-  if (lds > kRowsMaxLds || MB * a.npass * 64 * RowX<KIND>::slots > row_x_rounds<MB>() * 256 || a.rank > 256)
+  if (lds > kRowsMaxLds || a.rank > 256)
     return hipErrorInvalidConfiguration;
   const int grid = (Npad + 4 * R - 1) / (4 * R);
-  if (a.lr_kind != CL_LR_NONE)
-    hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, row_x_rounds<MB>(), true>), dim3(grid), dim3(256), lds, st, a);
-  else
-    hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, row_x_rounds<MB>(), false>), dim3(grid), dim3(256), lds, st, a);
+  const int per_thread = (MB * a.npass * 64 * RowX<KIND>::slots + 255) / 256;
+  if constexpr (MB == 1) {
+    if (per_thread <= 2)
+      launch_rows_xr<KIND, MB, BF16, R, 2>(a, grid, lds, st);
+    else if (per_thread <= 4)
+      launch_rows_xr<KIND, MB, BF16, R, 4>(a, grid, lds, st);
+    else
+      launch_rows_xr<KIND, MB, BF16, R, row_x_rounds<MB>()>(a, grid, lds, st);
+  } else {
+    launch_rows_xr<KIND, MB, BF16, R, row_x_rounds<MB>()>(a, grid, lds, st);
+  }
   return hipGetLastError();
 }
 
-// Whether the row-wise kernel takes this shape (its staged activations fit in LDS
-// and in the threads' staging registers).
+// Whether the row-wise kernel takes this shape (its staged activations fit in LDS).
 template <int KIND>
 bool rows_fit(RowArgs a) {
   const int mb = a.M <= 1 ? 1 : a.M <= 2 ? 2 : 4;
   const int lds = mb == 1 ? rows_lds_layout<KIND, 1>(a) : mb == 2 ? rows_lds_layout<KIND, 2>(a) : rows_lds_layout<KIND, 4>(a);
-  const int rounds = mb <= 2 ? row_x_rounds<1>() : row_x_rounds<4>();
-  return lds <= kRowsMaxLds && mb * a.npass * 64 * RowX<KIND>::slots <= rounds * 256;
+  return lds <= kRowsMaxLds && a.rank <= 256;
 }
 
 // Rows per wavefront: two for one activation row on layers of at least 8192
