@@ -9,6 +9,7 @@
 namespace cl {
 
 constexpr int kMaxDecodeM = 32;
+constexpr int kLrSlice = 512;  // K rows per workgroup of the decode low-rank prologue
 
 struct Layer {
   cl_blob_header h;          // copy of the blob header
@@ -48,6 +49,17 @@ struct Layer {
   uint16_t* pf_l16 = nullptr;    // [rank][Kl]: L^T, rows padded to Kl = K rounded up to 8, MFMA input type
   uint16_t* pf_t16 = nullptr;    // [max_M][2 rp]: t_hi | t_lo of t = x' L (workspace)
   int pf_rp = 0, pf_Kl = 0;
+
+  // decode low-rank prologue t = x' L, split over K (built at create); lr_mode
+  // -1: the per-column kernel (L type differs from x, or int4 groups below 16),
+  // 0: 16-bit L of the activation type, 1: int4 L
+  int lr_mode = -1;
+  int lr_rpad = 0;               // rank rounded up to 64
+  int lr_S = 0;                  // K slices of kLrSlice rows
+  uint8_t* lr_lk = nullptr;      // L, k-major in k pairs: 16-bit [Kl/2][rpad][2]; int4 bytes [Kl/2][rpad] (k even low nibble)
+  uint16_t* lr_ls = nullptr;     // int4: scales k-major [ceil(Kl/group)][rpad]
+  float* lr_part = nullptr;      // partial sums [tiles][S][256]
+  uint32_t* lr_cnt = nullptr;    // [64] arrivals per output tile, zero between forwards
   size_t ws_bytes = 0;
 };
 

@@ -36,6 +36,16 @@ static int choose_split(const cl_blob_header& h, int num_cus) {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Which decode low-rank prologue a layer takes: 0 for 16-bit L of the
+// activation type (pairwise dot products), 1 for int4 L with groups of at
+// least 16 along K (at most 33 scale rows per K slice), else -1 (per-column kernel).
+static int lowrank_mode(const cl_blob_header& h) {
+  if (h.lr == CL_LR_NONE || h.rank <= 0) return -1;
+  if (h.lr == CL_LR_INT4) return h.group >= 16 ? 1 : -1;
+  const bool lbf = h.lr == CL_LR_BF16, xbf = h.x_dtype == CL_ACT_BF16;
+  return lbf == xbf ? 0 : -1;
+}
+
 size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t base) {
   const int split = L ? L->split : 64;  // size query: the largest split
   const int Npad = h.n_tiles * 64;
@@ -75,8 +85,27 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
       o_pft = take((size_t)max_M * 2 * rp * 2);
     }
   }
+  // decode low-rank prologue: k-major copy of L, partial sums, arrival counters
+  size_t o_lk = 0, o_ls = 0, o_lp = 0, o_lc = 0;
+  const int lr_mode = lowrank_mode(h);
+  const int lr_rpad = (int)round_up(h.rank > 0 ? h.rank : 1, 64), lr_S = (int)ceil_div(h.K, kLrSlice);
+  if (has_lr && lr_mode >= 0) {
+    const size_t Kl = (size_t)lr_S * kLrSlice;
+    o_lk = take(lr_mode == 0 ? Kl * lr_rpad * 2 : Kl / 2 * lr_rpad);
+    if (lr_mode == 1) o_ls = take((size_t)ceil_div(Kl, h.group) * lr_rpad * 2);
+    const int mt = (int)ceil_div(max_M < kMaxDecodeM ? max_M : kMaxDecodeM, 4);
+    o_lp = take((size_t)(lr_rpad / 64) * mt * lr_S * 256 * 4);
+    o_lc = take(64 * 4);
+  }
   if (L) {
     uint8_t* d = L->dev;
+    L->lr_mode = (has_lr && lr_mode >= 0) ? lr_mode : -1;
+    L->lr_rpad = lr_rpad;
+    L->lr_S = lr_S;
+    L->lr_lk = o_lk ? d + o_lk : nullptr;
+    L->lr_ls = o_ls ? reinterpret_cast<uint16_t*>(d + o_ls) : nullptr;
+    L->lr_part = o_lp ? reinterpret_cast<float*>(d + o_lp) : nullptr;
+    L->lr_cnt = o_lc ? reinterpret_cast<uint32_t*>(d + o_lc) : nullptr;
     L->counters = reinterpret_cast<uint32_t*>(d + o_cnt);
     L->part = reinterpret_cast<float*>(d + o_part);
     L->nzstart = o_nzs ? reinterpret_cast<int32_t*>(d + o_nzs) : nullptr;
@@ -175,6 +204,37 @@ static void build_prefill_host(const cl_blob_header& h, const uint8_t* b, int Np
   }
 }
 
+// The decode prologue's copy of L from the blob's L^T: k-major, two consecutive
+// k per (pair, column) -- 16-bit: [Kl/2][rpad][2] values; int4: [Kl/2][rpad]
+// bytes, k even in the low nibble, codes as stored (zero padding is code 8) --
+// and the int4 scales k-major [ceil(Kl/group)][rpad].  Kl = slices * kLrSlice.
+static void build_lowrank_host(const cl_blob_header& h, const uint8_t* b, int mode, int rpad, int S,
+                               std::vector<uint8_t>& lk, std::vector<uint16_t>& ls) {
+  const int r = h.rank, K = h.K;
+  const size_t Kl = (size_t)S * kLrSlice;
+  const uint8_t* Lf = b + h.off[CL_SEC_L];
+  if (mode == 0) {
+    lk.assign(Kl * rpad * 2, 0);
+    uint16_t* o = reinterpret_cast<uint16_t*>(lk.data());
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(Lf);
+    for (int j = 0; j < r; ++j)
+      for (int k = 0; k < K; ++k) o[((size_t)(k >> 1) * rpad + j) * 2 + (k & 1)] = src[(size_t)j * K + k];
+    return;
+  }
+  const int g = h.group, hk = (K + 1) / 2, gk = (int)ceil_div(K, g);
+  lk.assign(Kl / 2 * rpad, 0x88);
+  for (int j = 0; j < r; ++j)
+    for (int k = 0; k < K; ++k) {
+      const uint8_t c = (Lf[(size_t)j * hk + k / 2] >> (4 * (k & 1))) & 0xF;
+      uint8_t& d = lk[(size_t)(k >> 1) * rpad + j];
+      d = (uint8_t)((d & (0xF0 >> (4 * (k & 1)))) | (c << (4 * (k & 1))));
+    }
+  const uint16_t* Ls = reinterpret_cast<const uint16_t*>(b + h.off[CL_SEC_LSCALE]);
+  ls.assign((size_t)ceil_div(Kl, g) * rpad, 0);
+  for (int j = 0; j < r; ++j)
+    for (int q = 0; q < gk; ++q) ls[(size_t)q * rpad + j] = Ls[(size_t)j * gk + q];
+}
+
 template <class T>
 static T* sec(uint8_t* dev, const cl_blob_header& h, int s) {
   return h.len[s] ? reinterpret_cast<T*>(dev + h.off[s]) : nullptr;
@@ -257,7 +317,14 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
   PrefillHost pf;
   if (h->mask != CL_MASK_BITMAP)
     build_prefill_host(*h, static_cast<const uint8_t*>(blob), L->Npad, L->pf_nd, L->pf_rp, L->pf_Kl, pf);
+  std::vector<uint8_t> lrk;
+  std::vector<uint16_t> lrs;
+  if (L->lr_mode >= 0)
+    build_lowrank_host(*h, static_cast<const uint8_t*>(blob), L->lr_mode, L->lr_rpad, L->lr_S, lrk, lrs);
   hipError_t e = hipMemcpyAsync(d, blob, h->total_bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !lrk.empty()) e = hipMemcpyAsync(L->lr_lk, lrk.data(), lrk.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !lrs.empty()) e = hipMemcpyAsync(L->lr_ls, lrs.data(), lrs.size() * 2, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && L->lr_cnt) e = hipMemsetAsync(L->lr_cnt, 0, 64 * 4, s);
   if (e == hipSuccess) e = hipMemsetAsync(L->counters, 0, (size_t)(h->n_tiles + ceil_div(max_M, 32) + 8) * 4, s);
   if (e == hipSuccess && !nzs.empty())
     e = hipMemcpyAsync(L->nzstart, nzs.data(), nzs.size() * 4, hipMemcpyHostToDevice, s);

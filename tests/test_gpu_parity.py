@@ -13,8 +13,8 @@ import compressed_linear_amd as cla
 import oracle
 from golden_cases import golden_names, load_golden
 from gpu_util import check_bound, gpu_forward, gpu_layer, to_device_x, torch_cuda
-from synth.layers import (LogicalLayer, draw_csr, draw_csr_skewed, draw_mask_2_4, draw_mask_half, make_layer,
-                          make_x, bf16_bits_from_f32)
+from synth.layers import (LogicalLayer, absmax_int4_groups, draw_csr, draw_csr_skewed, draw_mask_2_4,
+                          draw_mask_half, make_layer, make_x, bf16_bits_from_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +84,47 @@ def test_prefill_small_all_formats(cfg):
         say("prefill all", layer.name, "M", M)
         y = gpu_forward(layer, x, path="prefill")
         check_bound(y, layer, x, what=f"prefill {layer.name} M={M}")
+
+
+def _with_lowrank(base, kind, rank, group=128, seed=0):
+    r = np.random.default_rng(seed)
+    Lf = r.normal(0, 0.01, (base.K, rank))
+    Rf = r.normal(0, 0.01, (rank, base.N))
+    if kind == "fp16":
+        return base.with_(lr="fp16", rank=rank, L=Lf.astype(np.float16), R=Rf.astype(np.float16))
+    if kind == "bf16":
+        return base.with_(lr="bf16", rank=rank, L=bf16_bits_from_f32(Lf), R=bf16_bits_from_f32(Rf))
+    Lq, Ls = absmax_int4_groups(Lf, group)
+    Rq, Rs = absmax_int4_groups(Rf, group)
+    return base.with_(lr="int4", rank=rank, group=group, L=Lq, R=Rq, L_scale=Ls, R_scale=Rs)
+
+
+# decode low-rank prologue t = x' L: every factor type against both activation
+# types, ranks off the 64-column tile, one K slice and many, odd int4 groups,
+# small groups, and activation blocks that leave a partial row tile
+LOWRANK_CASES = [
+    # (factor, x dtype, rank, group, K, N, Ms)
+    ("fp16", "f16", 70, 128, 1300, 90, (1, 2, 3, 5)),
+    ("bf16", "bf16", 256, 128, 400, 70, (32, 1)),
+    ("fp16", "f16", 64, 128, 9000, 40, (1, 16)),
+    ("int4", "f16", 64, 33, 1100, 80, (2, 7)),
+    ("int4", "bf16", 128, 128, 1500, 60, (4, 1)),
+    ("int4", "f16", 16, 4, 600, 50, (1, 3)),
+    ("fp16", "bf16", 32, 128, 700, 50, (3,)),
+]
+
+
+@pytest.mark.parametrize("case", LOWRANK_CASES, ids=lambda c: f"{c[0]}-{c[1]}-r{c[2]}-g{c[3]}-K{c[4]}")
+def test_decode_lowrank_prologue(case):
+    kind, xdt, rank, group, K, N, Ms = case
+    base = make_layer(2, 0, K=K, N=N).with_(x_dtype=xdt)
+    lay = _with_lowrank(base, kind, rank, group, seed=rank + K)
+    r = np.random.default_rng(K)
+    for M in Ms:
+        xf = r.normal(0, 1, (M, K))
+        x = bf16_bits_from_f32(xf) if xdt == "bf16" else xf.astype(np.float16)
+        say("lowrank", case, "M", M)
+        check_bound(gpu_forward(lay, x, path="decode"), lay, x, what=f"lowrank {case} M={M}")
 
 
 def test_deterministic():
