@@ -167,18 +167,22 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   }
 
   // ---- activations (and t): the workgroup stages them in LDS, zero past K and past M ----
-  const int xch = a.npass * 64;  // staged chunks per row
-  const int xslots = MB * xch * XSL;
+  // Slot s of the staged activations is LDS byte lds_x + 16 s (rows of
+  // npass * 64 chunks of XSL slots each, back to back); its activation row m
+  // takes at most three compares and its chunk a division by a constant.
+  const int SM = a.npass * 64 * XSL;  // slots per activation row
+  const int xslots = MB * SM;
   const brsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.ldx * 2u);
+  auto x_src = [&](int s) -> uint32_t {
+    int m = 0;
+    if constexpr (MB > 1) m = (s >= SM) + (MB > 2 ? (s >= 2 * SM) + (s >= 3 * SM) : 0);
+    const int rem = s - m * SM, c = rem / XSL, d = rem - c * XSL, k = c * SPAN + 8 * d;
+    const bool ok = s < xslots && d < XD && m < a.M && k < a.ldx;  // ldx: a multiple of 8, zero past K
+    return ok ? ((uint32_t)m * (uint32_t)a.ldx + (uint32_t)k) * 2u : kNoLoad;
+  };
   uint4 xs[XR];
 #pragma unroll
-  for (int i = 0; i < XR; ++i) {
-    const int s = i * 256 + tid;
-    const int m = s / (xch * XSL), rem = s - m * (xch * XSL), c = rem / XSL, d = rem - c * XSL;
-    const int k = c * SPAN + 8 * d;
-    const bool ok = s < xslots && d < XD && m < a.M && k < a.ldx;  // ldx: a multiple of 8, zero past K
-    xs[i] = bload128(rx, ok ? ((uint32_t)m * (uint32_t)a.ldx + (uint32_t)k) * 2u : kNoLoad, 0);
-  }
+  for (int i = 0; i < XR; ++i) xs[i] = bload128(rx, x_src(i * 256 + tid), 0);
   uint32_t ts[MB];
   if constexpr (LR) {
     const brsrc_t rt = make_rsrc(a.t, (uint32_t)a.M * (uint32_t)a.rank * 4u);
@@ -251,29 +255,17 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
 #pragma unroll
   for (int i = 0; i < XR; ++i) {
     const int s = i * 256 + tid;
-    if (s < xslots) {
-      const int m = s / (xch * XSL), rem = s - m * (xch * XSL);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(sdyn) + a.lds_x + m * a.xrow + rem * 16) = xs[i];
-    }
+    if (s < xslots) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(sdyn) + a.lds_x + s * 16) = xs[i];
   }
   // activation blocks larger than one round of XR slots per thread: further
   // rounds, loaded after the code stream is in flight (their wait covers it)
   for (int base = XR * 256; base < xslots; base += XR * 256) {
 #pragma unroll
-    for (int i = 0; i < XR; ++i) {
-      const int s = base + i * 256 + tid;
-      const int m = s / (xch * XSL), rem = s - m * (xch * XSL), c = rem / XSL, d = rem - c * XSL;
-      const int k = c * SPAN + 8 * d;
-      const bool ok = s < xslots && d < XD && m < a.M && k < a.ldx;
-      xs[i] = bload128(rx, ok ? ((uint32_t)m * (uint32_t)a.ldx + (uint32_t)k) * 2u : kNoLoad, 0);
-    }
+    for (int i = 0; i < XR; ++i) xs[i] = bload128(rx, x_src(base + i * 256 + tid), 0);
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
       const int s = base + i * 256 + tid;
-      if (s < xslots) {
-        const int m = s / (xch * XSL), rem = s - m * (xch * XSL);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(sdyn) + a.lds_x + m * a.xrow + rem * 16) = xs[i];
-      }
+      if (s < xslots) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(sdyn) + a.lds_x + s * 16) = xs[i];
     }
   }
   if constexpr (LR) {
@@ -408,12 +400,18 @@ inline int rows_lds_layout(RowArgs& a) {
   return a.lds_x + MB * a.xrow;
 }
 
+// Passes per block: one when a row takes at most two passes (both blocks then
+// hold real chunks), else two.
 template <int KIND, int MB, bool BF16, int R, int XR>
 static void launch_rows_xr(const RowArgs& a, int grid, int lds, hipStream_t st) {
-  if (a.lr_kind != CL_LR_NONE)
-    hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, XR, true>), dim3(grid), dim3(256), lds, st, a);
-  else
-    hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, XR, false>), dim3(grid), dim3(256), lds, st, a);
+  const bool lr = a.lr_kind != CL_LR_NONE;
+  if (a.npass <= 2) {
+    if (lr) hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 1, XR, true>), dim3(grid), dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 1, XR, false>), dim3(grid), dim3(256), lds, st, a);
+  } else {
+    if (lr) hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, XR, true>), dim3(grid), dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, XR, false>), dim3(grid), dim3(256), lds, st, a);
+  }
 }
 
 // One activation row: the first staging round is sized to the activation block
