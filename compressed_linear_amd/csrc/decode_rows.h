@@ -129,15 +129,16 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   const bool has_csr = a.rowptr != nullptr;
   constexpr bool has_lr = LR;
 
-  // ---- scalar loads: row pointers (uniform) ----
+  // ---- row pointers: vector loads of uniform addresses, issued first so that
+  // the outlier heads wait for them alone (scalar loads would hold back every
+  // load behind one all-or-nothing wait); no outliers: zeros ----
   int e0[R], e1[R];
   {
-    typedef const __attribute__((address_space(4))) int32_t* sp;
-    const sp rp = (sp)a.rowptr;
+    const brsrc_t rrp = make_rsrc(a.rowptr, has_csr ? (uint32_t)(a.N + 1) * 4u : 0u);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      e0[r] = has_csr ? rp[min(row0 + r, a.N)] : 0;
-      e1[r] = has_csr ? rp[min(row0 + r + 1, a.N)] : 0;
+      e0[r] = (int)bload32(rrp, (uint32_t)min(row0 + r, a.N) * 4u, 0);
+      e1[r] = (int)bload32(rrp, (uint32_t)min(row0 + r + 1, a.N) * 4u, 0);
     }
   }
 
