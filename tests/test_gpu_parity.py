@@ -127,6 +127,21 @@ def test_decode_lowrank_prologue(case):
         check_bound(gpu_forward(lay, x, path="decode"), lay, x, what=f"lowrank {case} M={M}")
 
 
+# batches 2..4 with long K: activation blocks too large for the row-wise kernel's LDS
+# (the tile kernel takes them) next to ones that still fit
+BIG_LDS_CASES = [(5, 9000, 70, (4, 3)), (3, 11008, 60, (4,)), (2, 16000, 50, (2,))]
+
+
+@pytest.mark.parametrize("case", BIG_LDS_CASES, ids=lambda c: f"cfg{c[0]}-K{c[1]}")
+def test_rows_large_activation_block(case):
+    cfg, K, N, Ms = case
+    for M in Ms:
+        layer = make_layer(cfg, 0, K=K, N=N, M_for_clamp=M)
+        x = make_x(cfg, 0, M, K=K)
+        say("big lds", layer.name, "M", M)
+        check_bound(gpu_forward(layer, x, path="decode"), layer, x, what=f"big lds {layer.name} M={M}")
+
+
 def test_deterministic():
     torch = torch_cuda()
     layer = make_layer(5, 0, K=1450, N=190)
