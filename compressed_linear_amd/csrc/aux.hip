@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include "layer.h"
+#include "lowrank.h"
 #include "unpack.h"
 
 namespace cl {
@@ -117,183 +118,10 @@ __global__ void __launch_bounds__(256) lr_prologue_kernel(LrArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// The same t = x' L_hat split over K: workgroup (s, tj, tm) takes K rows
-// [512 s, 512 s + 512), rank columns [64 tj, 64 tj + 64) and activation rows
-// [MT tm, MT tm + MT), reading the k-major copy of L with 16-byte loads (all
-// issued before any arithmetic).  Its partial sums go to memory; the last
-// workgroup of each (tj, tm) tile to arrive adds the slices in slice order and
-// stores t, so the result does not depend on arrival order.
-//   MODE 0: 16-bit L of the activation type; a 16-byte load holds (k, k+1)
-//           for 4 columns, consumed by pairwise dot products with (x_k, x_k+1).
-//   MODE 1: int4 L; a 16-byte load holds (k, k+1) for 16 columns; each value
-//           is q * s in fp32 (exact), s from the slice's scale rows in LDS.
-// ---------------------------------------------------------------------------
-struct LrSplitArgs {
-  const uint16_t* x;
-  int ldx, M, rank, rpad, S, group, Kl;
-  const uint8_t* lk;
-  const uint16_t* ls;
-  float* part;
-  uint32_t* cnt;
-  float* t;
-};
-
-template <bool BF16>
-__device__ __forceinline__ float dot2_act(uint32_t a, uint32_t b, float c) {
-  if constexpr (BF16) {
-    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, a), __builtin_bit_cast(bf2, b), c, false);
-  } else {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
-  }
-}
-
 template <int MODE, int MT, bool BF16>
 __global__ void __launch_bounds__(256) lr_split_kernel(LrSplitArgs a) {
-  constexpr int NL = MODE == 0 ? 16 : 4;        // 16-byte loads per thread
-  constexpr int JL = MODE == 0 ? 4 : 16;        // columns per thread
-  constexpr int LG = 64 / JL;                   // threads per K pair row of the tile
-  constexpr int PR = 256 / LG;                  // K pair rows in flight per workgroup
-  constexpr int NG = MODE == 0 ? 4 : 16;        // reduction groups left after the shuffles
-  constexpr int NSC = kLrSlice / 16 + 1;        // int4 scale rows a slice can touch (group >= 16)
-  __shared__ __attribute__((aligned(16))) uint16_t xs[MT][kLrSlice];
-  __shared__ __attribute__((aligned(16))) float sc[MODE == 1 ? NSC * 64 : 4];
-  __shared__ float red[NG][MT * 64];
-  __shared__ int s_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = blockIdx.x, tj = blockIdx.y, tm = blockIdx.z;
-  const int k0 = s * kLrSlice, j0 = tj * 64, m0 = tm * MT;
-  const int jg = tid % LG, pr = tid / LG;
-
-  // activations of the slice (zero past K and past M)
-  const brsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.ldx * 2u);
-  uint4 xv = make_uint4(0, 0, 0, 0);
-  if (tid < MT * 64) {
-    const int m = tid >> 6, k = k0 + 8 * (tid & 63);
-    const bool ok = m0 + m < a.M && k < a.ldx;
-    xv = bload128(rx, ok ? ((uint32_t)(m0 + m) * (uint32_t)a.ldx + (uint32_t)k) * 2u : kNoLoad, 0);
-  }
-  // the slice of L
-  const brsrc_t rl = make_rsrc(a.lk, MODE == 0 ? (uint32_t)a.Kl * (uint32_t)a.rpad * 2u : (uint32_t)a.Kl / 2u * (uint32_t)a.rpad);
-  uint4 w[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const uint32_t p = (uint32_t)(k0 / 2 + pr + PR * i);
-    w[i] = bload128(rl, MODE == 0 ? (p * (uint32_t)a.rpad + (uint32_t)(j0 + JL * jg)) * 4u
-                                  : p * (uint32_t)a.rpad + (uint32_t)(j0 + JL * jg), 0);
-  }
-  // int4 scale rows of the slice, as fp32
-  const int g0 = MODE == 1 ? k0 / a.group : 0;
-  if constexpr (MODE == 1) {
-    const int ng = (k0 + kLrSlice - 1) / a.group - g0 + 1;
-    const brsrc_t rs = make_rsrc(a.ls, (uint32_t)((a.Kl + a.group - 1) / a.group) * (uint32_t)a.rpad * 2u);
-    for (int i = tid; i < ng * 8; i += 256) {
-      const int row = i >> 3, part = i & 7;
-      const uint4 v = bload128(rs, ((uint32_t)(g0 + row) * (uint32_t)a.rpad + (uint32_t)(j0 + 8 * part)) * 2u, 0);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sc[row * 64 + 8 * part + 2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[e] & 0xFFFFu));
-        sc[row * 64 + 8 * part + 2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[e] >> 16));
-      }
-    }
-  }
-  if (tid < MT * 64) *reinterpret_cast<uint4*>(&xs[tid >> 6][8 * (tid & 63)]) = xv;
-  __syncthreads();
-
-  float acc[MT][JL];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < JL; ++j) acc[m][j] = 0.f;
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int pl = pr + PR * i;  // pair row within the slice
-    if constexpr (MODE == 0) {
-      const uint32_t wv[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const uint32_t xp = *reinterpret_cast<const uint32_t*>(&xs[m][2 * pl]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[m][j] = dot2_act<BF16>(wv[j], xp, acc[m][j]);
-      }
-    } else {
-      const int k = k0 + 2 * pl;
-      const float* s0 = &sc[(k / a.group - g0) * 64 + JL * jg];
-      const float* s1 = &sc[((k + 1) / a.group - g0) * 64 + JL * jg];
-      float x0[MT], x1[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const uint32_t xp = *reinterpret_cast<const uint32_t*>(&xs[m][2 * pl]);
-        x0[m] = BF16 ? __uint_as_float(xp << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)(xp & 0xFFFFu));
-        x1[m] = BF16 ? __uint_as_float(xp & 0xFFFF0000u) : (float)__builtin_bit_cast(_Float16, (uint16_t)(xp >> 16));
-      }
-      const uint32_t wv[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t byte = (wv[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-        const float v0 = (float)((int)(byte & 0xFu) - 8) * s0[j];
-        const float v1 = (float)((int)(byte >> 4) - 8) * s1[j];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m][j] = __builtin_fmaf(v1, x1[m], __builtin_fmaf(v0, x0[m], acc[m][j]));
-      }
-    }
-  }
-  // lanes 16 and 32 apart hold other pair rows of the same columns
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < JL; ++j) {
-      float v = acc[m][j];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      acc[m][j] = v;
-    }
-  if (lane < 16) {
-    const int grp = MODE == 0 ? wave : wave * 4 + (lane >> 2);
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int j = 0; j < JL; ++j) red[grp][m * 64 + JL * jg + j] = acc[m][j];
-  }
-  __syncthreads();
-  float v = 0.f;
-  const int o = tid;  // output m * 64 + column, for tid < MT * 64
-  if (o < MT * 64) {
-#pragma unroll
-    for (int g = 0; g < NG; ++g) v += red[g][o];
-  }
-  const int m = o >> 6, j = j0 + (o & 63);
-  const bool store = o < MT * 64 && m0 + m < a.M && j < a.rank;
-  if (a.S == 1) {
-    if (store) a.t[(size_t)(m0 + m) * a.rank + j] = v;
-    return;
-  }
-  const int tile = tm * gridDim.y + tj;
-  float* base = a.part + (size_t)tile * a.S * 256;
-  if (o < MT * 64) store_dev(base + (size_t)s * 256 + o, v);
-  wait_stores();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&a.cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = old == (uint32_t)(a.S - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  // last arrival: slices in order, eight loads in flight at a time
-  if (o < MT * 64) {
-    float sum = 0.f;
-    for (int q0 = 0; q0 < a.S; q0 += 8) {
-      float pv[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) pv[q] = q0 + q < a.S ? load_dev(base + (size_t)(q0 + q) * 256 + o) : 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) sum += pv[q];
-    }
-    if (store) a.t[(size_t)(m0 + m) * a.rank + j] = sum;
-  }
-  if (tid == 0) __hip_atomic_store(&a.cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next forward
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LrScratch<MODE, MT>::bytes];
+  lr_split_block<MODE, MT, BF16>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.y, smem);
 }
 
 template <int MODE, int MT>
@@ -302,23 +130,30 @@ static void launch_lr_split(const LrSplitArgs& a, bool bf, dim3 grid, hipStream_
   else hipLaunchKernelGGL((lr_split_kernel<MODE, MT, false>), grid, dim3(256), 0, st, a);
 }
 
+LrSplitArgs lowrank_split_args(const Layer& L, int M, const void* x) {
+  LrSplitArgs s = {};  // flag = NULL: a kernel of its own
+  s.x = static_cast<const uint16_t*>(x);
+  s.ldx = (x == L.xprep) ? L.Kx : L.h.K;
+  s.M = M;
+  s.rank = L.h.rank;
+  s.rpad = L.lr_rpad;
+  s.S = L.lr_S;
+  s.group = L.h.group > 0 ? L.h.group : 1;
+  s.Kl = L.lr_S * kLrSlice;
+  s.lk = L.lr_lk;
+  s.ls = L.lr_ls;
+  s.part = L.lr_part;
+  s.cnt = L.lr_cnt;
+  s.t = L.t;
+  s.done = L.lr_cnt + 64;
+  s.ntiles = (L.lr_rpad / 64) * (int)ceil_div(M, lowrank_tile_m(M));
+  return s;
+}
+
 hipError_t launch_lowrank_prologue(const Layer& L, int M, const void* x, hipStream_t stream) {
   if (L.lr_mode >= 0 && M <= kMaxDecodeM) {
-    LrSplitArgs s;
-    s.x = static_cast<const uint16_t*>(x);
-    s.ldx = (x == L.xprep) ? L.Kx : L.h.K;
-    s.M = M;
-    s.rank = L.h.rank;
-    s.rpad = L.lr_rpad;
-    s.S = L.lr_S;
-    s.group = L.h.group > 0 ? L.h.group : 1;
-    s.Kl = L.lr_S * kLrSlice;
-    s.lk = L.lr_lk;
-    s.ls = L.lr_ls;
-    s.part = L.lr_part;
-    s.cnt = L.lr_cnt;
-    s.t = L.t;
-    const int MT = M == 1 ? 1 : M == 2 ? 2 : 4;
+    const LrSplitArgs s = lowrank_split_args(L, M, x);
+    const int MT = lowrank_tile_m(M);
     const dim3 grid((unsigned)L.lr_S, (unsigned)(L.lr_rpad / 64), (unsigned)ceil_div(M, MT));
     const bool bf = L.h.x_dtype == CL_ACT_BF16;
 #define LRS(mode, mt) \

@@ -18,7 +18,7 @@ extern template hipError_t launch_rows_kind<K_INT4>(const RowArgs&, int, bool, h
 extern template hipError_t launch_rows_kind<K_INT4_24>(const RowArgs&, int, bool, hipStream_t);
 extern template hipError_t launch_rows_kind<K_INT8>(const RowArgs&, int, bool, hipStream_t);
 
-hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream) {
+hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, uint32_t epoch) {
 
   const cl_blob_header& h = L.h;
   DecodeArgs a = {};
@@ -76,7 +76,30 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
     r.lr_kind = a.lr_kind;
     r.Npad = L.Npad;
     r.nnz = (int)h.nnz;
+    bool fits = false;
     switch (h.dense) {
+      case CL_DENSE_LUT3: fits = rows_fit<K_LUT3>(r); break;
+      case CL_DENSE_LUT4: fits = rows_fit<K_LUT4>(r); break;
+      case CL_DENSE_INT4: fits = h.mask == CL_MASK_2_4 ? rows_fit<K_INT4_24>(r) : rows_fit<K_INT4>(r); break;
+      default: fits = rows_fit<K_INT8>(r); break;
+    }
+    if (fits && h.lr != CL_LR_NONE) {
+      if (L.lr_mode >= 0) {
+        // the prologue runs as this launch's first workgroups
+        r.lrp = lowrank_split_args(L, M, x);
+        r.lrp.flag = L.lr_cnt + 65;
+        r.lrp.epoch = epoch;
+        r.lr_ntj = L.lr_rpad / 64;
+        r.lr_wgs = L.lr_S * r.lr_ntj * (int)ceil_div(M, lowrank_tile_m(M));
+        r.lr_mode = L.lr_mode;
+        r.lr_flag = r.lrp.flag;
+        r.lr_epoch = epoch;
+      } else {
+        const hipError_t e = launch_lowrank_prologue(L, M, x, stream);
+        if (e != hipSuccess) return e;
+      }
+    }
+    if (fits) switch (h.dense) {
       case CL_DENSE_LUT3:
         if (rows_fit<K_LUT3>(r)) return launch_rows_kind<K_LUT3>(r, L.Npad, bf16, stream);
         break;
@@ -94,6 +117,10 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
         if (rows_fit<K_INT8>(r)) return launch_rows_kind<K_INT8>(r, L.Npad, bf16, stream);
         break;
     }
+  }
+  if (h.lr != CL_LR_NONE) {
+    const hipError_t e = launch_lowrank_prologue(L, M, x, stream);
+    if (e != hipSuccess) return e;
   }
   switch (h.dense) {
     case CL_DENSE_LUT3: return launch_decode_kind<K_LUT3>(a, bf16, stream);

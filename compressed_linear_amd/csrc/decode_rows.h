@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 
 #include "layer.h"
+#include "lowrank.h"
 #include "unpack.h"
 
 namespace cl {
@@ -57,9 +58,28 @@ struct RowArgs {
   int nnz;    // outliers in the layer
   int npass;  // ceil(chunks / 64)
   int xrow;   // LDS bytes per staged activation row (npass * 64 chunks)
-  int lds_t;  // byte offset of the low-rank intermediate in the dynamic LDS
   int lds_x;  // byte offset of the staged activations in the dynamic LDS
+  // Low-rank prologue in the same launch: workgroups [0, lr_wgs) compute t
+  // (lr_mode 0 or 1, blocks S x lr_ntj x activation tiles) and publish
+  // lr_epoch in *lr_flag; the row workgroups wait for it before reading t.
+  // lr_wgs = 0: t was computed by an earlier kernel (lr_flag NULL).
+  LrSplitArgs lrp;
+  int lr_wgs, lr_ntj, lr_mode;
+  const uint32_t* lr_flag;
+  uint32_t lr_epoch;
 };
+
+// Bounded wait of a wavefront for the published t (each poll sleeps a few
+// hundred cycles; the bound, far above any producer's run time, only keeps a
+// wavefront from waiting forever should a producer never publish).
+__device__ __forceinline__ void wait_lowrank(const uint32_t* flag, uint32_t epoch, int lane) {
+  if (lane == 0) {
+    uint32_t it = 0;
+    while (__hip_atomic_load(const_cast<uint32_t*>(flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch &&
+           ++it < (1u << 20))
+      __builtin_amdgcn_s_sleep(4);
+  }
+}
 
 // LDS bytes per chunk of staged activations: the chunk's 2 * span bytes padded
 // so that the stride in dwords is 4 * (odd number) and lanes 0..7 of a 128-bit
@@ -124,7 +144,17 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t stab[row_tab_bytes<KIND, R>() / 4];  // at LDS address 0
   extern __shared__ __attribute__((aligned(16))) uint32_t sdyn[];                      // t, then the activations
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int row0 = (blockIdx.x * 4 + wave) * R;  // rows row0 + r >= Npad read zeros and are not stored
+  if constexpr (LR) {
+    if ((int)blockIdx.x < a.lr_wgs) {  // a prologue workgroup; MB is its activation tile
+      const int b = blockIdx.x, S = a.lrp.S, s = b % S, tj = (b / S) % a.lr_ntj, tm = b / (S * a.lr_ntj);
+      uint8_t* smem = reinterpret_cast<uint8_t*>(sdyn);
+      if (a.lr_mode == 0) lr_split_block<0, MB, BF16>(a.lrp, s, tj, tm, a.lr_ntj, smem);
+      else lr_split_block<1, MB, BF16>(a.lrp, s, tj, tm, a.lr_ntj, smem);
+      return;
+    }
+  }
+  const int rb = (int)blockIdx.x - (LR ? a.lr_wgs : 0);
+  const int row0 = (rb * 4 + wave) * R;  // rows row0 + r >= Npad read zeros and are not stored
   const uint32_t tabbase = (uint32_t)wave * R * RTB;
   const bool has_csr = a.rowptr != nullptr;
   constexpr bool has_lr = LR;
@@ -184,13 +214,6 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   uint4 xs[XR];
 #pragma unroll
   for (int i = 0; i < XR; ++i) xs[i] = bload128(rx, x_src(i * 256 + tid), 0);
-  uint32_t ts[MB];
-  if constexpr (LR) {
-    const brsrc_t rt = make_rsrc(a.t, (uint32_t)a.M * (uint32_t)a.rank * 4u);
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-      ts[m] = bload32(rt, (tid < a.rank && m < a.M) ? ((uint32_t)m * (uint32_t)a.rank + (uint32_t)tid) * 4u : kNoLoad, 0);
-  }
 
   // ---- the code stream: blocks of NB passes, two in flight ----
   const int nblk = (a.npass + NB - 1) / NB;
@@ -268,11 +291,6 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
       const int s = base + i * 256 + tid;
       if (s < xslots) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(sdyn) + a.lds_x + s * 16) = xs[i];
     }
-  }
-  if constexpr (LR) {
-    float* s_t = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(sdyn) + a.lds_t);
-#pragma unroll
-    for (int m = 0; m < MB; ++m) s_t[m * 256 + tid] = __uint_as_float(ts[m]);
   }
   if constexpr (KIND == K_LUT4) {
 #pragma unroll
@@ -370,13 +388,23 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   }
   // ---- rank terms: t (LDS) times R^T ----
   if constexpr (LR) {
-    const float* s_t = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(sdyn) + a.lds_t);
+    // t is ready once the prologue (earlier kernel, or this launch's first
+    // workgroups) has published it; read through the coherent path
+    if (a.lr_flag != nullptr) wait_lowrank(a.lr_flag, a.lr_epoch, lane);
+    float tv[MB][4];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        tv[m][i] = (j < a.rank && m < a.M) ? load_dev(a.t + (size_t)m * a.rank + j) : 0.f;
+      }
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int m = 0; m < MB; ++m) acc[r][m] = __builtin_fmaf(s_t[m * 256 + lane + 64 * i], rv[r][i], acc[r][m]);
+        for (int m = 0; m < MB; ++m) acc[r][m] = __builtin_fmaf(tv[m][i], rv[r][i], acc[r][m]);
   }
   // ---- reduce over the lanes and store ----
 #pragma unroll
@@ -396,9 +424,10 @@ template <int KIND, int MB>
 inline int rows_lds_layout(RowArgs& a) {
   a.npass = (a.chunks + 63) / 64;
   a.xrow = a.npass * 64 * RowX<KIND>::stride;
-  a.lds_t = 0;
-  a.lds_x = a.lr_kind != CL_LR_NONE ? MB * 256 * 4 : 0;
-  return a.lds_x + MB * a.xrow;
+  a.lds_x = 0;
+  const int lds = MB * a.xrow;
+  const int lr = a.lr_wgs > 0 ? lr_scratch_bytes(a.lr_mode, MB) : 0;  // prologue workgroups reuse it
+  return lds > lr ? lds : lr;
 }
 
 // Passes per block: one when a row takes at most two passes (both blocks then
@@ -422,7 +451,7 @@ static hipError_t launch_rows_t(RowArgs a, int Npad, hipStream_t st) {
   const int lds = rows_lds_layout<KIND, MB>(a);
   if (lds > kRowsMaxLds || a.rank > 256)
     return hipErrorInvalidConfiguration;
-  const int grid = (Npad + 4 * R - 1) / (4 * R);
+  const int grid = (Npad + 4 * R - 1) / (4 * R) + a.lr_wgs;  // prologue workgroups first
   const int per_thread = (MB * a.npass * 64 * RowX<KIND>::slots + 255) / 256;
   if constexpr (MB == 1) {
     if (per_thread <= 2)

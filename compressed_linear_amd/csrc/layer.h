@@ -59,7 +59,9 @@ struct Layer {
   uint8_t* lr_lk = nullptr;      // L, k-major in k pairs: 16-bit [Kl/2][rpad][2]; int4 bytes [Kl/2][rpad] (k even low nibble)
   uint16_t* lr_ls = nullptr;     // int4: scales k-major [ceil(Kl/group)][rpad]
   float* lr_part = nullptr;      // partial sums [tiles][S][256]
-  uint32_t* lr_cnt = nullptr;    // [64] arrivals per output tile, zero between forwards
+  uint32_t* lr_cnt = nullptr;    // [128]: arrivals per output tile [0, 64), completed tiles [64],
+                                 // published epoch [65]; counters zero between forwards
+  uint32_t lr_epoch = 0;         // forwards issued (the decode kernel's prologue publishes it)
   size_t ws_bytes = 0;
 };
 
@@ -69,7 +71,9 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L /* may 
 // Kernel launchers (kernels.hip).  All asynchronous on `stream`.
 hipError_t launch_prep_x(const Layer& L, int M, const void* x, hipStream_t stream);
 hipError_t launch_lowrank_prologue(const Layer& L, int M, const void* x, hipStream_t stream);
-hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream);
+// decode forward (M <= kMaxDecodeM), including the low-rank prologue: inside the
+// batch-1..4 kernel when it applies (publishing `epoch`), else as its own kernel
+hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, uint32_t epoch);
 hipError_t launch_prefill(const Layer& L, int M, const void* x, float* y, hipStream_t stream);
 hipError_t launch_debug(const Layer& L, uint16_t* D16, uint16_t* S16, float* L32, float* R32, hipStream_t stream);
 

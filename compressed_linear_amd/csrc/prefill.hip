@@ -38,9 +38,9 @@ static hipError_t prefill_by_decode(const Layer& L, int M, const void* x, float*
     const void* xb = static_cast<const uint16_t*>(x) + (size_t)m0 * ldx;
     Layer Lb = L;
     if (x == L.xprep) Lb.xprep = const_cast<uint16_t*>(static_cast<const uint16_t*>(xb));
-    hipError_t e = hipSuccess;
-    if (L.h.lr != CL_LR_NONE) e = launch_lowrank_prologue(Lb, mb, xb, stream);
-    if (e == hipSuccess) e = launch_decode(Lb, mb, xb, y + (size_t)m0 * L.h.N, stream);
+    // the bitmap format always takes the tile kernel, whose prologue is a kernel
+    // of its own (no epoch is published)
+    const hipError_t e = launch_decode(Lb, mb, xb, y + (size_t)m0 * L.h.N, stream, 0u);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
