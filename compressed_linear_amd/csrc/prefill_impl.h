@@ -233,42 +233,43 @@ __global__ void __launch_bounds__(2 * kPfThreads, 1) prefill_kernel(PfArgs a) {
       uint4 xa[AU];      // activation units
       uint4 wb[BU];      // code chunks, or 16-bit weights
       uint2 wm[C::cpt];  // 2:4 metadata
-      uint32_t ce;       // this thread's outlier entry of the step
+      uint32_t ce;       // this thread's outlier entry of the step (used when ce_ok)
+      bool ce_ok;
     };
-    auto load_step = [&](Stage& st, int s) {
-      // activations: only the last dense step can reach past the row (k >= ldx);
-      // everything below ldx is x' or the zero padding past K
-      if (s < a.nsteps_dense - 1) {
+    // Every load of a step is issued whatever the step (a step past the dense
+    // ones, or units past the activation row, read through a poisoned offset
+    // that lands outside the buffer and returns zero): a fixed number of loads
+    // per step lets the compiler wait for exactly the stage it consumes while
+    // the two younger stages stay in flight.
+    auto load_step = [&](Stage& st, int s, bool valid) {
+      // activations: everything below ldx is x' or the zero padding past K
 #pragma unroll
-        for (int i = 0; i < AU; ++i) st.xa[i] = bload128(rx, xoff[i], (uint32_t)(s * BK * 2));
-      } else {
-#pragma unroll
-        for (int i = 0; i < AU; ++i) {
-          const int kk8 = 8 * ((tid + i * kPfThreads) % (BK / 8));
-          st.xa[i] = s * BK + kk8 < a.ldx ? bload128(rx, xoff[i], (uint32_t)(s * BK * 2)) : make_uint4(0, 0, 0, 0);
-        }
+      for (int i = 0; i < AU; ++i) {
+        const int kk8 = 8 * ((tid + i * kPfThreads) % (BK / 8));
+        const bool ok = valid && s * BK + kk8 < a.ldx;
+        st.xa[i] = bload128(rx, ok ? xoff[i] + (uint32_t)(s * BK * 2) : kNoLoad, 0);
       }
       if constexpr (CODES) {
         // chunks past a row's end only meet zero activations
         const uint32_t so = (uint32_t)(s * (BK / SPAN)) * 16u;
 #pragma unroll
         for (int q = 0; q < C::cpt; ++q) {
-          st.wb[q] = bload128(rd, woff + 16u * q, so);
+          st.wb[q] = bload128(rd, valid ? woff + 16u * q + so : kNoLoad, 0);
           if constexpr (KIND == K_INT4_24)
-            st.wm[q] = bload64(rm, (woff + 16u * q) >> 1, so >> 1);
+            st.wm[q] = bload64(rm, valid ? (woff + 16u * q + so) >> 1 : kNoLoad, 0);
           else
             st.wm[q] = make_uint2(0, 0);
         }
-        st.ce = kPfNoEntry;
-        if (has_csr) {
-          const int e0 = s_cptr[s], cnt = s_cptr[s + 1] - e0;
-          if (tid < cnt) st.ce = bload32(rc, (uint32_t)(e0 + tid) * 4u, 0);
-        }
+        const int sc = valid ? s : 0;
+        const int e0 = s_cptr[sc], cnt = s_cptr[sc + 1] - e0;
+        const bool has = has_csr && valid && tid < cnt;
+        st.ce = bload32(rc, has ? (uint32_t)(e0 + tid) * 4u : kNoLoad, 0);  // consumed three steps later
+        st.ce_ok = has;
       } else {
         const int klo = s * BK + half * C::vpt;
 #pragma unroll
         for (int j = 0; j < BU; ++j)
-          st.wb[j] = klo + 8 * j < a.ldb16 ? bload128(rd, woff + 16u * j, (uint32_t)(s * BK * 2)) : make_uint4(0, 0, 0, 0);
+          st.wb[j] = bload128(rd, valid && klo + 8 * j < a.ldb16 ? woff + 16u * j + (uint32_t)(s * BK * 2) : kNoLoad, 0);
       }
     };
     // dense step s from stage st into tile buffer buf
@@ -303,7 +304,7 @@ __global__ void __launch_bounds__(2 * kPfThreads, 1) prefill_kernel(PfArgs a) {
     auto add_outliers = [&](const Stage& st, int s, int buf) {
       if (!has_csr) return;
       const uint32_t btile = (uint32_t)(buf * BUF + B_OFF);
-      if (st.ce != kPfNoEntry) pf_add_outlier<BF16, TS>(smem, btile, st.ce);
+      if (st.ce_ok) pf_add_outlier<BF16, TS>(smem, btile, st.ce);
       const int e0 = s_cptr[s], cnt = s_cptr[s + 1] - e0;
       for (int i = kPfThreads + tid; i < cnt; i += kPfThreads) pf_add_outlier<BF16, TS>(smem, btile, a.cent[e0 + i]);
     };
@@ -336,43 +337,37 @@ __global__ void __launch_bounds__(2 * kPfThreads, 1) prefill_kernel(PfArgs a) {
     };
 
     // Three register stages in a ring, each loaded three steps before it is
-    // staged.  Step t goes into tile buffer (t - s0) mod 2.
-    const int sd = min(s1, a.nsteps_dense);
+    // staged.  Step t goes into tile buffer (t - s0) mod 2.  Per step: stage
+    // the tile, barrier, add the outliers, refill the stage, barrier -- two
+    // barriers per step like the MFMA waves, plus two after the last step.
+    const int sd = max(s0, min(s1, a.nsteps_dense));  // dense steps [s0, sd), rank steps [sd, s1)
     Stage S0, S1, S2;
-    if (s0 < sd) load_step(S0, s0);
-    if (s0 + 1 < sd) load_step(S1, s0 + 1);
-    if (s0 + 2 < sd) load_step(S2, s0 + 2);
-    if (s0 < sd) {
-      stage_dense(S0, s0, 0);
+    load_step(S0, s0, s0 < sd);
+    load_step(S1, s0 + 1, s0 + 1 < sd);
+    load_step(S2, s0 + 2, s0 + 2 < sd);
+    auto dense_step = [&](Stage& st, int t) {
+      const int buf = (t - s0) & 1;
+      stage_dense(st, t, buf);
       __syncthreads();
-      add_outliers(S0, s0, 0);
-      if (s0 + 3 < sd) load_step(S0, s0 + 3);
-    } else {
-      stage_rank(s0, 0);
+      add_outliers(st, t, buf);
+      load_step(st, t + 3, t + 3 < sd);
+      __syncthreads();
+    };
+    int t = s0;
+    for (; t + 3 <= sd; t += 3) {
+      dense_step(S0, t);
+      dense_step(S1, t + 1);
+      dense_step(S2, t + 2);
+    }
+    if (t < sd) dense_step(S0, t++);
+    if (t < sd) dense_step(S1, t++);
+    for (; t < s1; ++t) {
+      stage_rank(t, (t - s0) & 1);
+      __syncthreads();
       __syncthreads();
     }
     __syncthreads();
-    // one step: stage step S + 1 from register stage NXT, refill NXT with step S + 4
-#define CL_PF_ITER(NXT, S)                          \
-  {                                                 \
-    const int t_ = (S) + 1, buf_ = ((t_ - s0) & 1); \
-    if (t_ < sd) {                                  \
-      stage_dense(NXT, t_, buf_);                   \
-      __syncthreads();                              \
-      add_outliers(NXT, t_, buf_);                  \
-      if (t_ + 3 < sd) load_step(NXT, t_ + 3);      \
-    } else {                                        \
-      if (t_ < s1) stage_rank(t_, buf_);            \
-      __syncthreads();                              \
-    }                                               \
-    __syncthreads();                                \
-  }
-    for (int s = s0; s < s1; s += 3) {
-      CL_PF_ITER(S1, s);
-      if (s + 1 < s1) CL_PF_ITER(S2, s + 1);
-      if (s + 2 < s1) CL_PF_ITER(S0, s + 2);
-    }
-#undef CL_PF_ITER
+    __syncthreads();
     return;
   }
 
