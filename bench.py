@@ -179,7 +179,8 @@ def main():
     R = max(2, -(-ROTATE_BYTES // weight_bytes))
     log(f"layer set: {len(built)} layers, {set_bytes / 1e6:.2f} MB algorithmic per step, {R} rotating copies")
 
-    mods = [[cla.CompressedLinear(blob, max_M=max(M, 1), device=dev) for (_, _, blob) in built] for _ in range(R)]
+    max_M = max(M, 2) if a.path == "decode_mfma" else max(M, 1)  # the matrix-core decode needs a batch workspace
+    mods = [[cla.CompressedLinear(blob, max_M=max_M, device=dev) for (_, _, blob) in built] for _ in range(R)]
     xs = [[to_dev_x(x, l.x_dtype, dev) for (l, _, _), x in zip(built, xs_np)] for _ in range(R)]
     ys = [[torch.empty((M, l.N), dtype=torch.float32, device=dev) for (l, _, _) in built] for _ in range(R)]
     stream = torch.cuda.current_stream(dev)

@@ -27,7 +27,7 @@ DENSE = {"lut3": 0, "lut4": 1, "int4": 2, "int8": 3}
 MASK = {"none": 0, "2:4": 1, "bitmap": 2}
 LR = {"none": 0, "fp16": 1, "bf16": 2, "int4": 3}
 ACT = {"f16": 0, "bf16": 1}
-PATH = {"auto": 0, "decode": 1, "prefill": 2}
+PATH = {"auto": 0, "decode": 1, "prefill": 2, "decode_valu": 3, "decode_mfma": 4}
 STATUS = {0: "CL_OK", -1: "CL_EINVAL", -2: "CL_EUNSUPPORTED", -3: "CL_ENOMEM", -4: "CL_EHIP", -5: "CL_ESIZE"}
 SECTIONS = ["dense", "table", "meta", "nzoff", "rowptr", "col", "val", "L", "R", "Lscale", "Rscale"]
 SEC_COUNT = 16
@@ -80,6 +80,12 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m compressed_linear_amd.build`")
+        # torch's HIP runtime has the same soname as the system one the library
+        # links against: load torch first, so that the library binds to the
+        # runtime that owns torch's device memory and streams (loading the
+        # library first makes torch bind to the system runtime instead, and
+        # the two then disagree about the devices)
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         L.cl_pack.argtypes = [ctypes.POINTER(cl_layer_desc), ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
                               ctypes.POINTER(cl_bytes)]

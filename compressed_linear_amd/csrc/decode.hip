@@ -1,6 +1,8 @@
 // decode.hip -- dispatch of the batch 1..32 forward: the row-wise kernel for
-// M <= 4, the tile kernel for larger batches and for the bitmap format.
+// small M, the matrix-core decode kernel for larger batches, the tile kernel
+// for the bitmap format (and wherever the others do not apply).
 #include "decode_impl.h"
+#include "decode_mfma.h"
 #include "decode_rows.h"
 
 namespace cl {
@@ -18,7 +20,59 @@ extern template hipError_t launch_rows_kind<K_INT4>(const RowArgs&, int, bool, h
 extern template hipError_t launch_rows_kind<K_INT4_24>(const RowArgs&, int, bool, hipStream_t);
 extern template hipError_t launch_rows_kind<K_INT8>(const RowArgs&, int, bool, hipStream_t);
 
-hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, uint32_t epoch) {
+extern template hipError_t launch_mfma_kind<K_LUT3>(const MfArgs&, bool, hipStream_t);
+extern template hipError_t launch_mfma_kind<K_LUT4>(const MfArgs&, bool, hipStream_t);
+extern template hipError_t launch_mfma_kind<K_INT4>(const MfArgs&, bool, hipStream_t);
+extern template hipError_t launch_mfma_kind<K_INT4_24>(const MfArgs&, bool, hipStream_t);
+extern template hipError_t launch_mfma_kind<K_INT8>(const MfArgs&, bool, hipStream_t);
+
+// Smallest batch that the automatic choice sends to the matrix-core decode kernel.
+constexpr int kMfMinM = 4;
+
+static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float* y, hipStream_t stream) {
+  const cl_blob_header& h = L.h;
+  if (h.lr != CL_LR_NONE) {
+    const hipError_t e = launch_lowrank_prologue(L, M, x, stream);
+    if (e != hipSuccess) return e;
+  }
+  MfArgs a = {};
+  a.dense = reinterpret_cast<const uint4*>(L.dense);
+  a.meta = L.meta;
+  a.table = reinterpret_cast<const uint16_t*>(L.table);
+  a.x = x;
+  a.ldx = (x == L.xprep) ? L.Kx : h.K;
+  a.M = M;
+  a.K = h.K;
+  a.N = h.N;
+  a.Npad = L.Npad;
+  a.chunks = h.chunks;
+  a.tiles = L.mf_tiles;
+  a.S = L.mf_S;
+  a.Kz = L.mf_Kz;
+  a.npw = L.mf_npw;
+  a.ooff = h.nnz > 0 ? L.mf_ooff : nullptr;
+  a.oent = L.mf_oent;
+  a.nnz = (int)h.nnz;
+  a.r16 = h.lr != CL_LR_NONE ? L.pf_r16 : nullptr;
+  a.t = L.t;
+  a.rank = h.rank;
+  a.rp = L.pf_rp;
+  a.part = L.mf_part;
+  a.counters = L.counters;
+  a.y = y;
+  const bool bf16 = h.x_dtype == CL_ACT_BF16;
+  switch (h.dense) {
+    case CL_DENSE_LUT3: return launch_mfma_kind<K_LUT3>(a, bf16, stream);
+    case CL_DENSE_LUT4: return launch_mfma_kind<K_LUT4>(a, bf16, stream);
+    case CL_DENSE_INT4:
+      return h.mask == CL_MASK_2_4 ? launch_mfma_kind<K_INT4_24>(a, bf16, stream) : launch_mfma_kind<K_INT4>(a, bf16, stream);
+    default: return launch_mfma_kind<K_INT8>(a, bf16, stream);
+  }
+}
+
+hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, uint32_t epoch,
+                         int variant) {
+  if (L.mf_S > 0 && (variant == 2 || (variant == 0 && M >= kMfMinM))) return launch_decode_mfma(L, M, x, y, stream);
 
   const cl_blob_header& h = L.h;
   DecodeArgs a = {};

@@ -1,0 +1,448 @@
+// decode_mfma.h -- batch 2..32 forward on the matrix cores, weights dequantised
+// in registers.
+//
+// With several activation rows every weight is used M times, and the
+// multiply-adds (M per weight) outgrow the vector ALUs long before the HBM
+// stream does: at M = 32 a 3-bit layer needs ~7x more vector-ALU time than
+// its bytes take to stream.  Here the matrix cores take the multiply-adds
+// (v_mfma_f32_32x32x16, 32 weight rows x 32 activation rows x 16 k), and each
+// weight is still dequantised exactly once, in the registers of the lane that
+// loaded it, so the per-weight cost stays that of the batch-1 path.
+//
+// A workgroup of four wavefronts owns a 128-row tile and one K slice of Kz
+// columns (split-K across workgroups).  Wavefront w owns rows 32w..32w+31 of
+// the tile; lane l holds row 32w + (l mod 32) and, in each pass, four
+// consecutive 16-byte chunks of that row (lane half h = l / 32 takes chunks
+// 4h..4h+3 of the pass' eight), so every pass reads one whole 128-byte line per
+// row.  The MFMA's contraction index runs over these chunks in a fixed
+// permuted order: MFMA (q, j) of a pass contracts k = span*(c0 + q) + 8j..+7 on
+// lane half 0 and span*(c0 + 4 + q) + 8j..+7 on half 1; the activation operand
+// is read from LDS at the same k, so the sum is unchanged.
+//
+// The LUT tables are lane-interleaved single-entry tables (entry e of lane l
+// at byte e*256 + 4l), one stacked set per wavefront, holding the values in the
+// MFMA input type: every lookup is conflict-free.  The activation slice
+// x'[0..M)[k0, k0+Kz) is staged once per workgroup in LDS.
+//
+// Outliers ("SqueezeLLM: Dense-and-Sparse Quantization", Approach: W = D + S)
+// of the tile's rows inside the K slice come as per-(tile, slice, row) lists
+// built when the layer is created; the two lanes of a row add them for their
+// activation rows in fp32 from the staged slice.  The rank-r correction ("SLiM"
+// page, review highlights: y += (x' L) R) is added by the slice-0 workgroups as
+// extra MFMA steps over [t_hi | t_lo] x [R^T | R^T], t = x' L computed
+// beforehand in fp32 and split into two 16-bit parts.  The slices' partial sums
+// meet through device-scope stores, and the last workgroup of a tile adds them
+// in slice order (deterministic, no float atomics).
+//
+// Weights enter the matrix cores as 16-bit values of the activation type: fp16
+// LUT values exactly for fp16 activations, rounded to nearest-even bf16 for
+// bf16 activations (as on the prefill path); integer codes exactly.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "layer.h"
+#include "unpack.h"
+
+namespace cl {
+
+typedef __bf16 mf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 mf_f16x8 __attribute__((ext_vector_type(8)));
+typedef float mf_f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kMfOe = 8;  // outlier entries per lane loaded with the code stream
+
+struct MfArgs {
+  const uint4* dense;
+  const uint8_t* meta;
+  const uint16_t* table;
+  const void* x;
+  int ldx, M, K, N, Npad, chunks;
+  int tiles, S, Kz, npw;        // 128-row tiles, K slices, columns per slice, passes per slice
+  const int32_t* ooff;          // outlier offsets per (slice, tile, row): [S * tiles * 128 + 1]
+  const uint32_t* oent;         // entries: k in slice (low 16 bits) | fp16 value << 16
+  int nnz;                      // entries in oent
+  const uint16_t* r16;          // R^T twice [Npad][2 rp] in the MFMA type, NULL without a rank term
+  const float* t;               // t = x' L, fp32 [M][rank]
+  int rank, rp;
+  float* part;                  // slice partials [tiles][S][32][128]
+  uint32_t* counters;           // arrivals per tile, zero between forwards
+  float* y;
+};
+
+template <bool BF16>
+__device__ __forceinline__ mf_f32x16 mf_mfma(uint4 a, uint4 b, mf_f32x16 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(mf_bf16x8, a), __builtin_bit_cast(mf_bf16x8, b), c,
+                                                   0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(mf_f16x8, a), __builtin_bit_cast(mf_f16x8, b), c, 0, 0,
+                                                0);
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t mf_to16(float f) {
+  if constexpr (BF16) return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float mf_act(uint32_t v16) {
+  if constexpr (BF16) return __uint_as_float(v16 << 16);
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)v16);
+}
+
+// A VGPR holding a constant, so that (x & c) | sgpr folds into one v_and_or_b32
+// (a VOP3 instruction takes one scalar or literal operand on this target).
+__device__ __forceinline__ uint32_t vconst(uint32_t c) {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(c));
+  return v;
+}
+
+// Two 16-bit table values into one register: the first into the low half
+// (ds_read_u16_d16), the second into the high half (ds_read_u16_d16_hi).
+__device__ __forceinline__ uint32_t lds_pair16(const uint32_t* lds, uint32_t a_lo, uint32_t a_hi) {
+  half2_t r;
+  r.x = *reinterpret_cast<const _Float16*>(reinterpret_cast<const uint8_t*>(lds) + a_lo);
+  r.y = *reinterpret_cast<const _Float16*>(reinterpret_cast<const uint8_t*>(lds) + a_hi);
+  return as_u32(r);
+}
+
+// 3-bit LUT word through lane-interleaved single-entry tables (entry e of lane
+// l at e*256 + 4l, value in the low half): the ten codes of the word
+// (byte j bits 2..4 = code 2j, bits 5..7 = code 2j+1 for j < 4; the fifth pair
+// gathered by lut3_p4x4 into byte 2) become five pairs.  `b` = entry bias in
+// every byte (the wavefront's table set).
+__device__ __forceinline__ void lut3_word_single(const uint32_t* lds, uint32_t w, uint32_t lanebase, uint32_t out[5],
+                                                 uint32_t b, uint32_t m7, uint32_t m7b2) {
+  const uint32_t ev = ((w >> 2) & m7) | b, od = ((w >> 5) & m7) | b;
+  const uint32_t p4 = lut3_p4x4(w);
+  const uint32_t e4 = ((p4 >> 2) & m7b2) | b, o4 = ((p4 >> 5) & m7b2) | b;
+  out[0] = lds_pair16(lds, addr_from_byte<0>(ev, lanebase), addr_from_byte<0>(od, lanebase));
+  out[1] = lds_pair16(lds, addr_from_byte<1>(ev, lanebase), addr_from_byte<1>(od, lanebase));
+  out[2] = lds_pair16(lds, addr_from_byte<2>(ev, lanebase), addr_from_byte<2>(od, lanebase));
+  out[3] = lds_pair16(lds, addr_from_byte<3>(ev, lanebase), addr_from_byte<3>(od, lanebase));
+  out[4] = lds_pair16(lds, addr_from_byte<2>(e4, lanebase), addr_from_byte<2>(o4, lanebase));
+}
+
+// 4-bit LUT word (device byte order: the pair (c_2b, c_2b+1) rotated left by
+// two bits in byte b) through lane-interleaved single-entry tables: four pairs.
+__device__ __forceinline__ void lut4_word_single(const uint32_t* lds, uint32_t w, uint32_t lanebase, uint32_t out[4],
+                                                 uint32_t b, uint32_t m15, uint32_t m3, uint32_t m12) {
+  const uint32_t ev = ((w >> 2) & m15) | b;                            // bits 2..5: c_2b
+  const uint32_t od = ((w >> 6) & m3) | ((w << 2) & m12) | b;          // bits 6..7, 0..1: c_2b+1
+  out[0] = lds_pair16(lds, addr_from_byte<0>(ev, lanebase), addr_from_byte<0>(od, lanebase));
+  out[1] = lds_pair16(lds, addr_from_byte<1>(ev, lanebase), addr_from_byte<1>(od, lanebase));
+  out[2] = lds_pair16(lds, addr_from_byte<2>(ev, lanebase), addr_from_byte<2>(od, lanebase));
+  out[3] = lds_pair16(lds, addr_from_byte<3>(ev, lanebase), addr_from_byte<3>(od, lanebase));
+}
+
+template <int KIND>
+struct MfCfg {
+  static constexpr int span = KindTraits<KIND>::span, pairs = KindTraits<KIND>::pairs;
+  static constexpr int passk = 2 * kMfCph * span;  // k per pass
+  static constexpr int ents = KIND == K_LUT3 ? 8 : KIND == K_LUT4 ? 16 : 0;  // table entries per row
+  // static LDS at address 0: four stacked lane-interleaved table sets, or the 2:4 selectors
+  static constexpr int tab_bytes = ents ? 4 * ents * 256 : KIND == K_INT4_24 ? 128 : 16;
+};
+
+// LDS bytes per staged activation row: the slice padded so that the row
+// stride is 16 mod 256 bytes (16-byte reads of 16 consecutive rows are
+// conflict-free).
+__host__ __device__ inline int mf_xrow(int Kz) { return ((Kz * 2 + 255) / 256) * 256 + 16; }
+__host__ __device__ inline int mf_trow(int rp) { return ((4 * rp + 255) / 256) * 256 + 16; }
+
+// MT = activation rows staged (M <= MT).
+template <int KIND, bool BF16, int MT>
+__global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
+  using C = MfCfg<KIND>;
+  constexpr int SPAN = C::span, P = C::pairs, PASSK = C::passk, NMF = P / 4;  // MFMAs per chunk
+  constexpr int XR = MT * kMfKzMax / 8 / 256;  // 16-byte activation slots per thread
+  constexpr bool LUT = C::ents > 0;
+  __shared__ __attribute__((aligned(16))) uint32_t stab[C::tab_bytes / 4];  // at LDS address 0
+  extern __shared__ __attribute__((aligned(16))) uint32_t sdyn[];          // activation slice, then t
+
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = (int)blockIdx.x % a.tiles, z = (int)blockIdx.x / a.tiles;
+  const int rt = wave * 32 + (lane & 31);  // row in tile
+  const int n = tile * kMfRows + rt;       // weight row of this lane (>= Npad: reads zeros)
+  const int k0 = z * a.Kz;
+  const int xrow = mf_xrow(a.Kz);
+  uint8_t* sb = reinterpret_cast<uint8_t*>(sdyn);
+
+  // ---- outlier range of this lane's (slice, tile, row) ----
+  const int vr = (z * a.tiles + tile) * kMfRows + rt;
+  const bool has_csr = a.ooff != nullptr;
+  int oe0 = 0, oe1 = 0;
+  if (has_csr) {
+    const brsrc_t ro = make_rsrc(a.ooff, (uint32_t)(a.S * a.tiles * kMfRows + 1) * 4u);
+    oe0 = (int)bload32(ro, (uint32_t)vr * 4u, 0);
+    oe1 = (int)bload32(ro, (uint32_t)(vr + 1) * 4u, 0);
+  }
+
+  // ---- LUT values or row scale of this lane's row ----
+  constexpr uint32_t TBYTES = KIND == K_LUT4 ? 32u : KIND == K_LUT3 ? 16u : 2u;
+  const brsrc_t rtab = make_rsrc(a.table, (uint32_t)a.Npad * TBYTES);
+  uint4 tv0 = make_uint4(0, 0, 0, 0), tv1 = make_uint4(0, 0, 0, 0);
+  uint32_t scale16 = 0;
+  if constexpr (LUT) {
+    tv0 = bload128(rtab, (uint32_t)n * TBYTES, 0);
+    if constexpr (KIND == K_LUT4) tv1 = bload128(rtab, (uint32_t)n * TBYTES + 16u, 0);
+  } else {
+    scale16 = bload16(rtab, (uint32_t)n * 2u, 0);
+  }
+
+  // ---- activation slice (rows >= M and columns >= ldx read zero) ----
+  const int slots_row = a.Kz / 8;
+  const brsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.ldx * 2u);
+  uint4 xs[XR];
+#pragma unroll
+  for (int i = 0; i < XR; ++i) {
+    const int s = i * 256 + tid, m = s / slots_row, c = s - m * slots_row, k = k0 + 8 * c;
+    const bool ok = m < a.M && k < a.ldx;
+    xs[i] = bload128(rx, ok ? ((uint32_t)m * (uint32_t)a.ldx + (uint32_t)k) * 2u : kNoLoad, 0);
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- the code stream: passes of four chunks per lane, three in flight ----
+  const int cbase = k0 / SPAN;  // first chunk of the slice (Kz is a whole number of passes)
+  const brsrc_t rd = make_rsrc(a.dense, (uint32_t)a.Npad * (uint32_t)a.chunks * 16u);
+  const brsrc_t rm = make_rsrc(a.meta, KIND == K_INT4_24 ? (uint32_t)a.Npad * (uint32_t)a.chunks * 8u : 0u);
+  auto load_pass = [&](uint4 (&w)[kMfCph], uint2 (&mw)[kMfCph], int p) {
+#pragma unroll
+    for (int q = 0; q < kMfCph; ++q) {
+      const int c = cbase + p * 2 * kMfCph + half * kMfCph + q;
+      const bool ok = p < a.npw && c < a.chunks;
+      const uint32_t idx = (uint32_t)n * (uint32_t)a.chunks + (uint32_t)c;
+      w[q] = bload128(rd, ok ? idx * 16u : kNoLoad, 0);
+      if constexpr (KIND == K_INT4_24)
+        mw[q] = bload64(rm, ok ? idx * 8u : kNoLoad, 0);
+      else
+        mw[q] = make_uint2(0, 0);
+    }
+  };
+  uint4 WA[kMfCph], WB[kMfCph], WC[kMfCph];
+  uint2 MA[kMfCph], MB[kMfCph], MC[kMfCph];
+  load_pass(WA, MA, 0);
+  load_pass(WB, MB, 1);
+  load_pass(WC, MC, 2);
+  // keep the issue order (the outlier entries below wait for their offsets:
+  // issued before the code stream they would hold it back by one latency)
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- the first kMfOe outlier entries of this lane's list (consumed at the end) ----
+  uint32_t oent[kMfOe];
+  {
+    const brsrc_t re = make_rsrc(a.oent, has_csr ? (uint32_t)a.nnz * 4u : 0u);  // uniform: no waterfall loop
+#pragma unroll
+    for (int i = 0; i < kMfOe; ++i) oent[i] = bload32(re, oe0 + i < oe1 ? (uint32_t)(oe0 + i) * 4u : kNoLoad, 0);
+  }
+
+  // ---- LDS: activation slice, tables ----
+#pragma unroll
+  for (int i = 0; i < XR; ++i) {
+    const int s = i * 256 + tid, m = s / slots_row, c = s - m * slots_row;
+    if (m < MT && s < MT * slots_row)
+      *reinterpret_cast<uint4*>(sb + m * xrow + c * 16) = xs[i];
+  }
+  const uint32_t lanebase = (uint32_t)lane * 4u, ebias = (uint32_t)(wave * C::ents);
+  if constexpr (LUT) {
+    const uint32_t lw[8] = {tv0.x, tv0.y, tv0.z, tv0.w, tv1.x, tv1.y, tv1.z, tv1.w};
+#pragma unroll
+    for (int e = 0; e < C::ents; ++e) {
+      const uint32_t h = (lw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      stab[(ebias + e) * 64 + lane] = BF16 ? mf_to16<true>((float)__builtin_bit_cast(_Float16, (uint16_t)h)) : h;
+    }
+  } else if constexpr (KIND == K_INT4_24) {
+    if (tid < 16) {
+      const uint2 e = seltab_2_4_entry((uint32_t)tid);
+      stab[2 * tid] = e.x;
+      stab[2 * tid + 1] = e.y;
+    }
+  }
+  __syncthreads();
+
+  // ---- dequantise, multiply on the matrix cores ----
+  mf_f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  const int mrow = lane & 31;  // activation row of this lane's A operand
+  // mask constants in VGPRs and the table-set bias in every byte
+  const uint32_t bias4 = ebias * 0x01010101u;
+  const uint32_t mk0 = vconst(KIND == K_LUT3 ? 0x07070707u : 0x0F0F0F0Fu);
+  const uint32_t mk1 = vconst(KIND == K_LUT3 ? 0x00070000u : 0x03030303u);
+  const uint32_t mk2 = vconst(0x0C0C0C0Cu);
+  const bool mok = mrow < a.M;
+  const uint8_t* xr = sb + mrow * xrow + half * kMfCph * SPAN * 2;
+  auto comp_pass = [&](const uint4 (&w)[kMfCph], const uint2 (&mw)[kMfCph], int p) {
+    if (p >= a.npw) return;
+#pragma unroll
+    for (int q = 0; q < kMfCph; ++q) {
+      uint32_t wp[P];
+      const uint32_t ww[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+      if constexpr (KIND == K_LUT3) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lut3_word_single(stab, ww[i], lanebase, &wp[5 * i], bias4, mk0, mk1);
+      } else if constexpr (KIND == K_LUT4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lut4_word_single(stab, ww[i], lanebase, &wp[4 * i], bias4, mk0, mk1, mk2);
+      } else {
+        chunk_pairs<KIND, false>(stab, w[q], make_uint4(mw[q].x, mw[q].y, 0, 0), lanebase, 0u, wp, ebias);
+        if constexpr (!LUT && BF16) {
+#pragma unroll
+          for (int j = 0; j < P; ++j) {
+            const half2_t hv = as_h2(wp[j]);
+            wp[j] = mf_to16<true>((float)hv.x) | (mf_to16<true>((float)hv.y) << 16);
+          }
+        }
+      }
+      const uint8_t* xq = xr + (p * PASSK + q * SPAN) * 2;
+#pragma unroll
+      for (int j = 0; j < NMF; ++j) {
+        const uint4 xa = mok ? *reinterpret_cast<const uint4*>(xq + 16 * j) : make_uint4(0, 0, 0, 0);
+        acc = mf_mfma<BF16>(xa, make_uint4(wp[4 * j], wp[4 * j + 1], wp[4 * j + 2], wp[4 * j + 3]), acc);
+      }
+    }
+  };
+  // three passes in flight; the first three outside the loop, so that their waits are exact
+  comp_pass(WA, MA, 0);
+  load_pass(WA, MA, 3);
+  comp_pass(WB, MB, 1);
+  load_pass(WB, MB, 4);
+  comp_pass(WC, MC, 2);
+  load_pass(WC, MC, 5);
+  for (int p = 3; p < a.npw; p += 3) {
+    comp_pass(WA, MA, p);
+    load_pass(WA, MA, p + 3);
+    comp_pass(WB, MB, p + 1);
+    load_pass(WB, MB, p + 4);
+    comp_pass(WC, MC, p + 2);
+    load_pass(WC, MC, p + 5);
+  }
+
+  // lane l holds row rt for activation rows m(v) = 8 (v / 4) + 4 half + v mod 4
+  // ---- integer formats: the row scale multiplies the dense part only ----
+  if constexpr (!LUT) {
+    const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)scale16);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] *= sc;
+  }
+  // ---- outliers of this row inside the slice, activations from the staged slice ----
+  if (has_csr) {
+    const brsrc_t re = make_rsrc(a.oent, (uint32_t)a.nnz * 4u);
+    for (int e = oe0; e < oe1; ++e) {
+      const int i = e - oe0;
+      uint32_t en = 0;
+#pragma unroll
+      for (int u = 0; u < kMfOe; ++u)
+        if (i == u) en = oent[u];
+      if (i >= kMfOe) en = bload32(re, (uint32_t)e * 4u, 0);  // lists longer than the prefetch
+      const int kk = (int)(en & 0xFFFFu);
+      const float val = (float)__builtin_bit_cast(_Float16, (uint16_t)(en >> 16));
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = 8 * (v >> 2) + 4 * half + (v & 3);
+        if (m < a.M) acc[v] = __builtin_fmaf(val, mf_act<BF16>(lds_u16(sdyn, (uint32_t)(m * xrow + kk * 2))), acc[v]);
+      }
+    }
+  }
+  // ---- rank term (slice 0): [t_hi | t_lo] x [R^T | R^T] on the matrix cores ----
+  if (a.r16 != nullptr && z == 0) {
+    const int rp2 = 2 * a.rp, trow = mf_trow(a.rp);
+    __syncthreads();  // every wave is done with the activation slice
+    for (int i = tid; i < MT * a.rp; i += 256) {
+      const int m = i / a.rp, j = i - m * a.rp;
+      const float tv = (m < a.M && j < a.rank) ? a.t[(size_t)m * a.rank + j] : 0.f;
+      const uint32_t hi = mf_to16<BF16>(tv);
+      const float hf = BF16 ? __uint_as_float(hi << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)hi);
+      const uint32_t lo = mf_to16<BF16>(tv - hf);
+      *reinterpret_cast<uint16_t*>(sb + m * trow + j * 2) = (uint16_t)hi;
+      *reinterpret_cast<uint16_t*>(sb + m * trow + (a.rp + j) * 2) = (uint16_t)lo;
+    }
+    __syncthreads();
+    const brsrc_t rr = make_rsrc(a.r16, (uint32_t)a.Npad * (uint32_t)rp2 * 2u);
+    for (int s = 0; s < rp2 / 16; ++s) {
+      const uint4 wv = bload128(rr, ((uint32_t)n * (uint32_t)rp2 + (uint32_t)(16 * s + 8 * half)) * 2u, 0);
+      const uint4 ta = mok ? *reinterpret_cast<const uint4*>(sb + mrow * trow + (16 * s + 8 * half) * 2)
+                           : make_uint4(0, 0, 0, 0);
+      acc = mf_mfma<BF16>(ta, wv, acc);
+    }
+  }
+
+  // ---- store, or combine the slices' partial sums (last workgroup of the tile) ----
+  if (a.S == 1) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = 8 * (v >> 2) + 4 * half + (v & 3);
+      if (m < a.M && n < a.N) a.y[(size_t)m * a.N + n] = acc[v];
+    }
+    return;
+  }
+  // Partial sums cross workgroups (possibly on different XCDs, whose L2s are
+  // not coherent with each other) through device-scope stores and loads.
+  float* mypart = a.part + ((size_t)tile * a.S + z) * (32 * kMfRows);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int m = 8 * (v >> 2) + 4 * half + (v & 3);
+    if (m < a.M) store_dev(mypart + m * kMfRows + rt, acc[v]);
+  }
+  wait_stores();
+  __syncthreads();  // every wave is past its last read of the staged slice: its first dword holds the flag
+  volatile uint32_t* s_last = sdyn;
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = old == (uint32_t)(a.S - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!*s_last) return;
+  // each thread owns outputs (m, row) tid + 256 o; per round of eight outputs
+  // and group of eight slices all 64 loads are issued before any is added, so
+  // the reduction waits about S / 8 latencies per round, not S
+  const float* tp = a.part + (size_t)tile * a.S * (32 * kMfRows);
+  const int nout = a.M * kMfRows;
+  for (int ob = 0; ob < nout; ob += 8 * 256) {
+    float acc_o[8];
+#pragma unroll
+    for (int o = 0; o < 8; ++o) acc_o[o] = 0.f;
+    for (int s0 = 0; s0 < a.S; s0 += 8) {
+      float v8[8][8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int o = 0; o < 8; ++o) {
+          const int i = ob + tid + 256 * o;
+          v8[u][o] = (s0 + u < a.S && i < nout) ? load_dev(tp + (size_t)(s0 + u) * (32 * kMfRows) + i) : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int o = 0; o < 8; ++o) acc_o[o] += v8[u][o];  // slices in order for every output
+    }
+#pragma unroll
+    for (int o = 0; o < 8; ++o) {
+      const int i = ob + tid + 256 * o, m = i / kMfRows, row = tile * kMfRows + (i - m * kMfRows);
+      if (i < nout && row < a.N) a.y[(size_t)m * a.N + row] = acc_o[o];
+    }
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next forward
+}
+
+template <int KIND, bool BF16, int MT>
+static hipError_t launch_mfma_t(const MfArgs& a, hipStream_t st) {
+  const int lds_x = MT * mf_xrow(a.Kz);
+  const int lds_t = a.r16 ? MT * mf_trow(a.rp) : 0;
+  const int lds = lds_x > lds_t ? lds_x : lds_t;
+  hipLaunchKernelGGL((decode_mfma_kernel<KIND, BF16, MT>), dim3(a.tiles * a.S), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_mfma_kind(const MfArgs& a, bool bf16, hipStream_t st) {
+  if (a.Kz > kMfKzMax || a.Kz % MfCfg<KIND>::passk || a.M > 32 || a.M < 1 || a.Kz >= 65536)
+    return hipErrorInvalidValue;
+  if (a.M <= 8) return bf16 ? launch_mfma_t<KIND, true, 8>(a, st) : launch_mfma_t<KIND, false, 8>(a, st);
+  if (a.M <= 16) return bf16 ? launch_mfma_t<KIND, true, 16>(a, st) : launch_mfma_t<KIND, false, 16>(a, st);
+  return bf16 ? launch_mfma_t<KIND, true, 32>(a, st) : launch_mfma_t<KIND, false, 32>(a, st);
+}
+
+}  // namespace cl

@@ -62,6 +62,12 @@ struct Layer {
   uint32_t* lr_cnt = nullptr;    // [128]: arrivals per output tile [0, 64), completed tiles [64],
                                  // published epoch [65]; counters zero between forwards
   uint32_t lr_epoch = 0;         // forwards issued (the decode kernel's prologue publishes it)
+
+  // matrix-core decode (batch 2..32, all formats but the bitmap; absent when max_M == 1)
+  int mf_npw = 0, mf_Kz = 0, mf_S = 0, mf_tiles = 0;
+  float* mf_part = nullptr;      // slice partial sums [tiles][S][32][128]
+  int32_t* mf_ooff = nullptr;    // outlier offsets per (slice, tile, row in tile): [S * tiles * 128 + 1]
+  uint32_t* mf_oent = nullptr;   // entries: k in slice | fp16 value << 16
   size_t ws_bytes = 0;
 };
 
@@ -73,7 +79,9 @@ hipError_t launch_prep_x(const Layer& L, int M, const void* x, hipStream_t strea
 hipError_t launch_lowrank_prologue(const Layer& L, int M, const void* x, hipStream_t stream);
 // decode forward (M <= kMaxDecodeM), including the low-rank prologue: inside the
 // batch-1..4 kernel when it applies (publishing `epoch`), else as its own kernel
-hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, uint32_t epoch);
+// variant: 0 the faster kernel for M, 1 the vector-ALU kernels, 2 the matrix-core kernel
+hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, uint32_t epoch,
+                         int variant);
 hipError_t launch_prefill(const Layer& L, int M, const void* x, float* y, hipStream_t stream);
 hipError_t launch_debug(const Layer& L, uint16_t* D16, uint16_t* S16, float* L32, float* R32, hipStream_t stream);
 

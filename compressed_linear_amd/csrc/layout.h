@@ -75,4 +75,23 @@ inline int pf_step_k(int dense, int mask) {
 }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
+// Matrix-core decode (batch 2..32): 128-row tiles, split along K into slices
+// of whole passes (a pass is eight chunks of every row of the tile).
+constexpr int kMfRows = 128;    // weight rows per workgroup (four wavefronts of 32)
+constexpr int kMfCph = 4;       // chunks per lane half per pass (two halves read one 128-byte line of a row)
+constexpr int kMfKzMax = 1024;  // largest K slice (bounds the activation staging in LDS)
+inline int mf_pass_k(int dense, int mask) { return 2 * kMfCph * kind_info(dense, mask).span; }
+// Passes per K slice: about 1024 columns (768 for the 4-bit LUT, whose tables
+// take more LDS), fewer when the layer would give under two workgroups per CU
+// of a 256-CU device.  Independent of M, so that the outlier lists built at
+// create serve every batch size.
+inline int mf_passes(int dense, int mask, int K, int N) {
+  const int passk = mf_pass_k(dense, mask);
+  const int target = dense == 1 ? 768 : kMfKzMax;
+  int npw = target / passk > 0 ? target / passk : 1;
+  const int64_t tiles = ceil_div(N, kMfRows);
+  while (npw > 1 && tiles * ceil_div(K, (int64_t)npw * passk) < 2 * 256) npw = npw / 2 > 0 ? npw / 2 : 1;
+  return npw;
+}
+
 }  // namespace cl

@@ -40,7 +40,7 @@ static hipError_t prefill_by_decode(const Layer& L, int M, const void* x, float*
     if (x == L.xprep) Lb.xprep = const_cast<uint16_t*>(static_cast<const uint16_t*>(xb));
     // the bitmap format always takes the tile kernel, whose prologue is a kernel
     // of its own (no epoch is published)
-    const hipError_t e = launch_decode(Lb, mb, xb, y + (size_t)m0 * L.h.N, stream, 0u);
+    const hipError_t e = launch_decode(Lb, mb, xb, y + (size_t)m0 * L.h.N, stream, 0u, 1);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -85,6 +85,20 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
       o_pft = take((size_t)max_M * 2 * rp * 2);
     }
   }
+  // matrix-core decode: slice partial sums, outlier lists per (slice, tile, row)
+  size_t o_mfp = 0, o_mfo = 0, o_mfe = 0;
+  int mf_npw = 0, mf_Kz = 0, mf_S = 0, mf_tiles = 0;
+  if (h.mask != CL_MASK_BITMAP && max_M >= 2) {
+    mf_npw = mf_passes(h.dense, h.mask, h.K, h.N);
+    mf_Kz = mf_npw * mf_pass_k(h.dense, h.mask);
+    mf_tiles = (int)ceil_div(h.N, kMfRows);
+    mf_S = (int)ceil_div(h.K, mf_Kz);
+    o_mfp = take((size_t)mf_tiles * mf_S * 32 * kMfRows * 4);
+    if (h.nnz > 0) {
+      o_mfo = take(((size_t)mf_S * mf_tiles * kMfRows + 1) * 4);
+      o_mfe = take((size_t)h.nnz * 4);
+    }
+  }
   // decode low-rank prologue: k-major copy of L, partial sums, arrival counters
   size_t o_lk = 0, o_ls = 0, o_lp = 0, o_lc = 0;
   const int lr_mode = lowrank_mode(h);
@@ -120,6 +134,13 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
     L->pf_t16 = o_pft ? reinterpret_cast<uint16_t*>(d + o_pft) : nullptr;
     L->pf_rp = rp;
     L->pf_Kl = Kx;
+    L->mf_npw = mf_npw;
+    L->mf_Kz = mf_Kz;
+    L->mf_S = mf_S;
+    L->mf_tiles = mf_tiles;
+    L->mf_part = o_mfp ? reinterpret_cast<float*>(d + o_mfp) : nullptr;
+    L->mf_ooff = o_mfo ? reinterpret_cast<int32_t*>(d + o_mfo) : nullptr;
+    L->mf_oent = o_mfe ? reinterpret_cast<uint32_t*>(d + o_mfe) : nullptr;
     L->ws_bytes = off - align256(base);
   }
   return off;
@@ -202,6 +223,29 @@ static void build_prefill_host(const cl_blob_header& h, const uint8_t* b, int Np
     for (int j = 0; j < r; ++j)
       for (int k = 0; k < h.K; ++k) out.l16[(size_t)j * Kl + k] = to16(factor(Lf, Ls, j, k, h.K));
   }
+}
+
+// Outlier lists of the matrix-core decode: the CSR entries regrouped by
+// (K slice z, 128-row tile, row in tile) -- list index (z * tiles + tile) * 128
+// + row -- each list in ascending column order, entry = column - z * Kz (low 16
+// bits) | fp16 value << 16.
+static void build_mfma_outliers(const cl_blob_header& h, const uint8_t* b, int S, int tiles, int Kz,
+                                std::vector<int32_t>& off, std::vector<uint32_t>& ent) {
+  const int32_t* rp = reinterpret_cast<const int32_t*>(b + h.off[CL_SEC_ROWPTR]);
+  const int32_t* col = reinterpret_cast<const int32_t*>(b + h.off[CL_SEC_COL]);
+  const uint16_t* val = reinterpret_cast<const uint16_t*>(b + h.off[CL_SEC_VAL]);
+  off.assign((size_t)S * tiles * kMfRows + 1, 0);
+  auto list = [&](int n, int c) { return ((size_t)(c / Kz) * tiles + n / kMfRows) * kMfRows + n % kMfRows; };
+  for (int n = 0; n < h.N; ++n)
+    for (int p = rp[n]; p < rp[n + 1]; ++p) ++off[list(n, col[p]) + 1];
+  for (size_t i = 1; i < off.size(); ++i) off[i] += off[i - 1];
+  std::vector<int32_t> fill(off.begin(), off.end() - 1);
+  ent.assign((size_t)h.nnz, 0);
+  for (int n = 0; n < h.N; ++n)
+    for (int p = rp[n]; p < rp[n + 1]; ++p) {
+      const int c = col[p];
+      ent[fill[list(n, c)]++] = (uint32_t)(c % Kz) | ((uint32_t)val[p] << 16);
+    }
 }
 
 // The decode prologue's copy of L from the blob's L^T: k-major, two consecutive
@@ -317,6 +361,10 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
   PrefillHost pf;
   if (h->mask != CL_MASK_BITMAP)
     build_prefill_host(*h, static_cast<const uint8_t*>(blob), L->Npad, L->pf_nd, L->pf_rp, L->pf_Kl, pf);
+  std::vector<int32_t> mfo;
+  std::vector<uint32_t> mfe;
+  if (L->mf_ooff)
+    build_mfma_outliers(*h, static_cast<const uint8_t*>(blob), L->mf_S, L->mf_tiles, L->mf_Kz, mfo, mfe);
   std::vector<uint8_t> lrk;
   std::vector<uint16_t> lrs;
   if (L->lr_mode >= 0)
@@ -336,6 +384,10 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
     e = hipMemcpyAsync(L->pf_r16, pf.r16.data(), pf.r16.size() * 2, hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !pf.l16.empty())
     e = hipMemcpyAsync(L->pf_l16, pf.l16.data(), pf.l16.size() * 2, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !mfo.empty())
+    e = hipMemcpyAsync(L->mf_ooff, mfo.data(), mfo.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !mfe.empty())
+    e = hipMemcpyAsync(L->mf_oent, mfe.data(), mfe.size() * 4, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     delete L;
@@ -352,8 +404,12 @@ static cl_status forward_impl(Layer* L, int32_t M, const void* x, float* y, void
   if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 16)
     return fail(CL_EINVAL, "x and y must be 16-byte aligned");
   if (path == CL_PATH_AUTO) path = M <= kMaxDecodeM ? CL_PATH_DECODE : CL_PATH_PREFILL;
-  if (path == CL_PATH_DECODE && M > kMaxDecodeM) return fail(CL_EINVAL, "the decode path takes M <= %d", kMaxDecodeM);
-  if (path != CL_PATH_DECODE && path != CL_PATH_PREFILL) return fail(CL_EINVAL, "unknown path %d", path);
+  if (path != CL_PATH_DECODE && path != CL_PATH_PREFILL && path != CL_PATH_DECODE_VALU && path != CL_PATH_DECODE_MFMA)
+    return fail(CL_EINVAL, "unknown path %d", path);
+  const bool decode = path != CL_PATH_PREFILL;
+  if (decode && M > kMaxDecodeM) return fail(CL_EINVAL, "the decode path takes M <= %d", kMaxDecodeM);
+  if (path == CL_PATH_DECODE_MFMA && L->mf_S == 0)
+    return fail(CL_EUNSUPPORTED, "the matrix-core decode needs a layer without the bitmap mask, created with max_M >= 2");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const void* xa = x;
   hipError_t e = hipSuccess;
@@ -361,8 +417,9 @@ static cl_status forward_impl(Layer* L, int32_t M, const void* x, float* y, void
     e = launch_prep_x(*L, M, x, s);
     xa = L->xprep;
   }
-  if (path == CL_PATH_DECODE) {
-    if (e == hipSuccess) e = launch_decode(*L, M, xa, y, s, ++L->lr_epoch);
+  if (decode) {
+    const int variant = path == CL_PATH_DECODE_VALU ? 1 : path == CL_PATH_DECODE_MFMA ? 2 : 0;
+    if (e == hipSuccess) e = launch_decode(*L, M, xa, y, s, ++L->lr_epoch, variant);
   } else {
     if (e == hipSuccess) e = launch_prefill(*L, M, xa, y, s);
   }

@@ -62,7 +62,16 @@ typedef enum { CL_DENSE_LUT3 = 0, CL_DENSE_LUT4 = 1, CL_DENSE_INT4 = 2, CL_DENSE
 typedef enum { CL_MASK_NONE = 0, CL_MASK_2_4 = 1, CL_MASK_BITMAP = 2 } cl_mask_kind;
 typedef enum { CL_LR_NONE = 0, CL_LR_FP16 = 1, CL_LR_BF16 = 2, CL_LR_INT4 = 3 } cl_lr_kind;
 typedef enum { CL_ACT_F16 = 0, CL_ACT_BF16 = 1 } cl_act_dtype;
-typedef enum { CL_PATH_AUTO = 0, CL_PATH_DECODE = 1, CL_PATH_PREFILL = 2 } cl_path;
+/* Forward paths: AUTO picks by M (decode for M <= 32, else prefill); DECODE
+ * picks the faster decode kernel for M; DECODE_VALU forces the vector-ALU
+ * decode kernels, DECODE_MFMA the matrix-core decode kernel. */
+typedef enum {
+  CL_PATH_AUTO = 0,
+  CL_PATH_DECODE = 1,
+  CL_PATH_PREFILL = 2,
+  CL_PATH_DECODE_VALU = 3,
+  CL_PATH_DECODE_MFMA = 4
+} cl_path;
 
 /*
  * Logical (unpacked) description of one layer.  All pointers are host
@@ -184,8 +193,10 @@ cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes, int32_t m
  * cl_forward -- y = x' W_hat^T for M rows of activations.
  *   x_dev  device, [M, K] fp16 or bf16 (the layer's x_dtype), 16-byte aligned.
  *   y_dev  device, [M, N] fp32, overwritten, 16-byte aligned.
- *   1 <= M <= max_M.  M <= 32 runs the decode kernels (VALU, bandwidth
- *   bound at small M); larger M runs the prefill kernels (bf16 MFMA).
+ *   1 <= M <= max_M.  M <= 32 runs the decode kernels (the vector-ALU
+ *   streaming kernel at small M, the matrix-core decode kernel with weights
+ *   dequantised in registers at larger M); larger M runs the prefill kernels
+ *   (MFMA on dequantised LDS tiles).
  * One forward at a time per handle (the workspace inside dev_buf is shared).
  * Deterministic: the same inputs give bitwise identical y.
  * Errors: CL_EINVAL (M out of range, NULL or misaligned pointers),
@@ -194,7 +205,8 @@ cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes, int32_t m
 cl_status cl_forward(void* handle, int32_t M, const void* x_dev, float* y_dev, void* stream);
 
 /* cl_forward with an explicit path (cl_path); CL_PATH_AUTO behaves as cl_forward.
- * CL_PATH_DECODE requires M <= 32. */
+ * The decode paths require M <= 32; CL_PATH_DECODE_MFMA also a layer without
+ * the bitmap mask, created with max_M >= 2 (else CL_EUNSUPPORTED). */
 cl_status cl_forward_path(void* handle, int32_t M, const void* x_dev, float* y_dev,
                           void* stream, int32_t path);
 

@@ -1,0 +1,167 @@
+"""The matrix-core decode kernel (batch 2..32, weights dequantised in registers)
+against the CPU oracle, through the C ABI (needs an MI355X).
+
+Every format but the bitmap, with and without outliers and rank terms, fp16 and
+bf16 activations, at batch sizes across the 8 / 16 / 32 staging variants, on
+shapes with a partial 128-row tile and a partial K slice; the golden dyadic
+cases exactly; bitwise determinism across the split-K reduction; and the same
+cases through the vector-ALU decode kernels (forced), which the automatic
+choice no longer takes at these batch sizes.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import compressed_linear_amd as cla
+import oracle
+from golden_cases import golden_names, load_golden
+from gpu_util import check_bound, gpu_forward, gpu_layer, to_device_x, torch_cuda
+from synth.layers import LogicalLayer, bf16_bits_from_f32, draw_csr_skewed, make_layer, make_x
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# (cfg, K, N): partial 128-row tiles and K not a multiple of the slice
+SHAPES = {1: (2410, 200), 2: (3000, 330), 3: (2300, 130), 5: (2900, 190)}
+MS = (1, 2, 5, 8, 9, 16, 17, 32)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_mfma_decode_configs(cfg):
+    K, N = SHAPES[cfg]
+    layer = make_layer(cfg, 0, K=K, N=N)
+    mod = gpu_layer(layer, max_M=32)
+    for M in MS:
+        x = make_x(cfg, 0, M, K=K)
+        say("mfma decode", layer.name, "M", M)
+        y = gpu_forward(layer, x, path="decode_mfma", mod=mod)
+        check_bound(y, layer, x, what=f"mfma {layer.name} M={M}")
+    mod.close()
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_valu_decode_forced(cfg):
+    K, N = SHAPES[cfg]
+    layer = make_layer(cfg, 0, K=K, N=N)
+    mod = gpu_layer(layer, max_M=32)
+    for M in (5, 16, 32):
+        x = make_x(cfg, 0, M, K=K)
+        say("valu decode", layer.name, "M", M)
+        y = gpu_forward(layer, x, path="decode_valu", mod=mod)
+        check_bound(y, layer, x, what=f"valu {layer.name} M={M}")
+    mod.close()
+
+
+@pytest.mark.parametrize("name", golden_names())
+def test_mfma_golden_exact(name):
+    layer, x, y_exp, _ = load_golden(name)
+    if layer.mask == "bitmap":
+        pytest.skip("the bitmap format has no matrix-core decode kernel")
+    say("mfma golden", name)
+    mod = gpu_layer(layer, max_M=max(2, x.shape[0]))
+    y = gpu_forward(layer, x, path="decode_mfma", mod=mod)
+    mod.close()
+    assert np.array_equal(y, y_exp), (y, y_exp)
+
+
+def test_mfma_plain_integer_formats():
+    r = np.random.default_rng(15)
+    K, N = 1900, 150
+    for dense, lo, hi in (("int4", -8, 8), ("int8", -127, 128)):
+        q = r.integers(lo, hi, size=(N, K)).astype(np.int8)
+        s = r.uniform(0.001, 0.01, N).astype(np.float16)
+        lay = LogicalLayer(K=K, N=N, dense=dense, qvals=q, row_scale=s)
+        mod = gpu_layer(lay, max_M=32)
+        for M in (2, 13, 32):
+            x = r.normal(0, 1, (M, K)).astype(np.float16)
+            say("mfma plain", dense, "M", M)
+            check_bound(gpu_forward(lay, x, path="decode_mfma", mod=mod), lay, x, what=f"{dense} M={M}")
+        mod.close()
+        layb = lay.with_(x_dtype="bf16")
+        xb = bf16_bits_from_f32(r.normal(0, 1, (6, K)))
+        modb = gpu_layer(layb, max_M=32)
+        check_bound(gpu_forward(layb, xb, path="decode_mfma", mod=modb), layb, xb, what=dense + " bf16")
+        modb.close()
+    lay4 = make_layer(2, 0, K=K, N=N).with_(x_dtype="bf16")
+    xb = bf16_bits_from_f32(r.normal(0, 1, (7, K)))
+    check_bound(gpu_forward(lay4, xb, path="decode_mfma"), lay4, xb, what="lut4 bf16")
+
+
+def test_mfma_lowrank_factor_types():
+    from test_gpu_parity import _with_lowrank
+    for kind, xdt, rank, group in (("fp16", "f16", 70, 128), ("bf16", "bf16", 256, 128), ("int4", "f16", 128, 128),
+                                   ("int4", "bf16", 64, 33), ("fp16", "bf16", 32, 128)):
+        base = make_layer(2, 0, K=1300, N=150).with_(x_dtype=xdt)
+        lay = _with_lowrank(base, kind, rank, group, seed=rank)
+        r = np.random.default_rng(rank)
+        mod = gpu_layer(lay, max_M=32)
+        for M in (3, 16, 32):
+            xf = r.normal(0, 1, (M, 1300))
+            x = bf16_bits_from_f32(xf) if xdt == "bf16" else xf.astype(np.float16)
+            say("mfma lowrank", kind, xdt, rank, group, "M", M)
+            check_bound(gpu_forward(lay, x, path="decode_mfma", mod=mod), lay, x,
+                        what=f"lowrank {kind} {xdt} r{rank} M={M}")
+        mod.close()
+
+
+def test_mfma_outlier_stress_and_tiny_shapes():
+    r = np.random.default_rng(22)
+    K, N = 2100, 257
+    rp, col, val = draw_csr_skewed(r, r, N, K, density=0.01)
+    base = make_layer(2, 0, K=K, N=N)
+    lay = base.with_(csr_row_ptr=rp, csr_col=col, csr_val=val)
+    x = make_x(2, 0, 12, K=K)
+    say("mfma skewed csr")
+    check_bound(gpu_forward(lay, x, path="decode_mfma"), lay, x, what="skewed csr")
+    # a row holding every column as an outlier
+    rp2 = np.zeros(N + 1, np.int32); rp2[6:] = K
+    lay2 = base.with_(csr_row_ptr=rp2, csr_col=np.arange(K, dtype=np.int32),
+                      csr_val=r.normal(0, 0.2, K).astype(np.float16))
+    check_bound(gpu_forward(lay2, x, path="decode_mfma"), lay2, x, what="full row csr")
+    # one row, two columns; odd K (restaged activations)
+    tiny = make_layer(1, 0, K=2, N=1)
+    xt = make_x(1, 0, 2, K=2)
+    check_bound(gpu_forward(tiny, xt, path="decode_mfma"), tiny, xt, what="1x2")
+    odd = make_layer(5, 0, K=333, N=65)
+    xo = make_x(5, 0, 7, K=333)
+    check_bound(gpu_forward(odd, xo, path="decode_mfma"), odd, xo, what="odd K")
+    # clamp (int8, no mask)
+    q = r.integers(-127, 128, size=(70, 640)).astype(np.int8)
+    clamp = LogicalLayer(K=640, N=70, dense="int8", qvals=q, row_scale=np.full(70, 0.01, np.float16),
+                         act_clamp=np.float16(1.5))
+    xc = (r.normal(0, 2, (9, 640))).astype(np.float16)
+    check_bound(gpu_forward(clamp, xc, path="decode_mfma"), clamp, xc, what="clamp")
+
+
+def test_mfma_deterministic_split_k():
+    torch = torch_cuda()
+    layer = make_layer(5, 0, K=6000, N=300)
+    x = make_x(5, 0, 24, K=6000)
+    mod = gpu_layer(layer, max_M=32)
+    xd = to_device_x(x, layer.x_dtype)
+    y1 = mod.forward(xd, path="decode_mfma").cpu().numpy()
+    y2 = mod.forward(xd, path="decode_mfma").cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    check_bound(y1.astype(np.float64), layer, x, what="split-K")
+    mod.close()
+
+
+def test_mfma_path_errors():
+    torch = torch_cuda()
+    layer = make_layer(1, 0, K=100, N=64)
+    mod = gpu_layer(layer, max_M=1)   # created for batch 1: no matrix-core decode workspace
+    x = to_device_x(make_x(1, 0, 1, K=100), "f16")
+    with pytest.raises(cla.ClError):
+        mod.forward(x, path="decode_mfma")
+    mod.close()
+    bm = make_layer(4, 0, K=256, N=64)
+    modb = gpu_layer(bm, max_M=4)
+    xb = to_device_x(make_x(4, 0, 2, K=256), "f16")
+    with pytest.raises(cla.ClError):
+        modb.forward(xb, path="decode_mfma")
+    modb.close()
