@@ -1,6 +1,7 @@
 // decode.hip -- dispatch of the batch 1..32 forward: the row-wise kernel for
-// small M, the matrix-core decode kernel for larger batches, the tile kernel
-// for the bitmap format (and wherever the others do not apply).
+// M <= 3 (M = 1 with bf16 activations) when its staged activations fit in LDS, the matrix-core decode kernel
+// for larger batches and the row-wise kernel's misfits, the tile kernel for the
+// bitmap format (and for layers created for batch 1 only).
 #include "decode_impl.h"
 #include "decode_mfma.h"
 #include "decode_rows.h"
@@ -72,7 +73,10 @@ static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float
 
 hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, uint32_t epoch,
                          int variant) {
-  if (L.mf_S > 0 && (variant == 2 || (variant == 0 && M >= kMfMinM))) return launch_decode_mfma(L, M, x, y, stream);
+  // bf16 activations cost the row-wise kernel two multiply-adds per weight pair
+  // and activation row (no mixed fp16 x bf16 dot product), so it keeps only batch 1
+  const bool mf_auto = M >= kMfMinM || (M >= 2 && L.h.x_dtype == CL_ACT_BF16);
+  if (L.mf_S > 0 && (variant == 2 || (variant == 0 && mf_auto))) return launch_decode_mfma(L, M, x, y, stream);
 
   const cl_blob_header& h = L.h;
   DecodeArgs a = {};
@@ -172,6 +176,8 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
         break;
     }
   }
+  // batches the row-wise kernel cannot stage: the matrix-core kernel where it applies
+  if (variant == 0 && L.mf_S > 0) return launch_decode_mfma(L, M, x, y, stream);
   if (h.lr != CL_LR_NONE) {
     const hipError_t e = launch_lowrank_prologue(L, M, x, stream);
     if (e != hipSuccess) return e;

@@ -136,12 +136,18 @@ __device__ __forceinline__ void lut4_word_single(const uint32_t* lds, uint32_t w
   out[3] = lds_pair16(lds, addr_from_byte<3>(ev, lanebase), addr_from_byte<3>(od, lanebase));
 }
 
-template <int KIND>
+// MT = activation rows staged.  LUT formats use lane-interleaved single-entry
+// tables: one lookup per weight, but conflict-free.  (Per-row pair tables, one
+// lookup per two weights, measured slower here: the 32 rows of a wavefront
+// look up different tables, and their bank conflicts cost more than the
+// lookups they save.)
+template <int KIND, int MT>
 struct MfCfg {
   static constexpr int span = KindTraits<KIND>::span, pairs = KindTraits<KIND>::pairs;
   static constexpr int passk = 2 * kMfCph * span;  // k per pass
   static constexpr int ents = KIND == K_LUT3 ? 8 : KIND == K_LUT4 ? 16 : 0;  // table entries per row
-  // static LDS at address 0: four stacked lane-interleaved table sets, or the 2:4 selectors
+  // static LDS at address 0: four stacked lane-interleaved single-entry table
+  // sets, or the 2:4 selectors
   static constexpr int tab_bytes = ents ? 4 * ents * 256 : KIND == K_INT4_24 ? 128 : 16;
 };
 
@@ -154,8 +160,10 @@ __host__ __device__ inline int mf_trow(int rp) { return ((4 * rp + 255) / 256) *
 // MT = activation rows staged (M <= MT).
 template <int KIND, bool BF16, int MT>
 __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
-  using C = MfCfg<KIND>;
+  using C = MfCfg<KIND, MT>;
   constexpr int SPAN = C::span, P = C::pairs, PASSK = C::passk, NMF = P / 4;  // MFMAs per chunk
+  // outputs v of a lane whose activation row m(v) = 8 (v / 4) + 4 half + v mod 4 is below MT
+  constexpr int NV = MT >= 32 ? 16 : MT / 2;
   constexpr int XR = MT * kMfKzMax / 8 / 256;  // 16-byte activation slots per thread
   constexpr bool LUT = C::ents > 0;
   __shared__ __attribute__((aligned(16))) uint32_t stab[C::tab_bytes / 4];  // at LDS address 0
@@ -238,20 +246,24 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
     for (int i = 0; i < kMfOe; ++i) oent[i] = bload32(re, oe0 + i < oe1 ? (uint32_t)(oe0 + i) * 4u : kNoLoad, 0);
   }
 
-  // ---- LDS: activation slice, tables ----
+  // ---- LDS: activation slice (rows M..MT-1 zero) plus a zero row MT, tables ----
 #pragma unroll
   for (int i = 0; i < XR; ++i) {
     const int s = i * 256 + tid, m = s / slots_row, c = s - m * slots_row;
     if (m < MT && s < MT * slots_row)
       *reinterpret_cast<uint4*>(sb + m * xrow + c * 16) = xs[i];
   }
+  for (int c = tid; c < slots_row; c += 256) *reinterpret_cast<uint4*>(sb + MT * xrow + c * 16) = make_uint4(0, 0, 0, 0);
   const uint32_t lanebase = (uint32_t)lane * 4u, ebias = (uint32_t)(wave * C::ents);
+  auto lut_val = [&](uint32_t h) -> uint32_t {
+    return BF16 ? mf_to16<true>((float)__builtin_bit_cast(_Float16, (uint16_t)h)) : h;
+  };
   if constexpr (LUT) {
     const uint32_t lw[8] = {tv0.x, tv0.y, tv0.z, tv0.w, tv1.x, tv1.y, tv1.z, tv1.w};
 #pragma unroll
     for (int e = 0; e < C::ents; ++e) {
       const uint32_t h = (lw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      stab[(ebias + e) * 64 + lane] = BF16 ? mf_to16<true>((float)__builtin_bit_cast(_Float16, (uint16_t)h)) : h;
+      stab[(ebias + e) * 64 + lane] = lut_val(h);
     }
   } else if constexpr (KIND == K_INT4_24) {
     if (tid < 16) {
@@ -272,8 +284,8 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   const uint32_t mk0 = vconst(KIND == K_LUT3 ? 0x07070707u : 0x0F0F0F0Fu);
   const uint32_t mk1 = vconst(KIND == K_LUT3 ? 0x00070000u : 0x03030303u);
   const uint32_t mk2 = vconst(0x0C0C0C0Cu);
-  const bool mok = mrow < a.M;
-  const uint8_t* xr = sb + mrow * xrow + half * kMfCph * SPAN * 2;
+  const int mrow_s = mrow < MT ? mrow : MT;  // rows past MT read the zero row
+  const uint8_t* xr = sb + mrow_s * xrow + half * kMfCph * SPAN * 2;
   auto comp_pass = [&](const uint4 (&w)[kMfCph], const uint2 (&mw)[kMfCph], int p) {
     if (p >= a.npw) return;
 #pragma unroll
@@ -299,7 +311,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
       const uint8_t* xq = xr + (p * PASSK + q * SPAN) * 2;
 #pragma unroll
       for (int j = 0; j < NMF; ++j) {
-        const uint4 xa = mok ? *reinterpret_cast<const uint4*>(xq + 16 * j) : make_uint4(0, 0, 0, 0);
+        const uint4 xa = *reinterpret_cast<const uint4*>(xq + 16 * j);
         acc = mf_mfma<BF16>(xa, make_uint4(wp[4 * j], wp[4 * j + 1], wp[4 * j + 2], wp[4 * j + 3]), acc);
       }
     }
@@ -327,30 +339,31 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] *= sc;
   }
-  // ---- outliers of this row inside the slice, activations from the staged slice ----
+  // ---- outliers of this row inside the slice, activations from the staged
+  // slice (rows M..MT-1 are zero there, so no batch test is needed) ----
   if (has_csr) {
     const brsrc_t re = make_rsrc(a.oent, (uint32_t)a.nnz * 4u);
+    uint32_t moff[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) moff[v] = (uint32_t)((8 * (v >> 2) + 4 * half + (v & 3)) * xrow);
     for (int e = oe0; e < oe1; ++e) {
       const int i = e - oe0;
-      uint32_t en = 0;
+      uint32_t en = oent[0];
 #pragma unroll
-      for (int u = 0; u < kMfOe; ++u)
+      for (int u = 1; u < kMfOe; ++u)
         if (i == u) en = oent[u];
       if (i >= kMfOe) en = bload32(re, (uint32_t)e * 4u, 0);  // lists longer than the prefetch
-      const int kk = (int)(en & 0xFFFFu);
+      const uint32_t kk2 = (en & 0xFFFFu) * 2u;
       const float val = (float)__builtin_bit_cast(_Float16, (uint16_t)(en >> 16));
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = 8 * (v >> 2) + 4 * half + (v & 3);
-        if (m < a.M) acc[v] = __builtin_fmaf(val, mf_act<BF16>(lds_u16(sdyn, (uint32_t)(m * xrow + kk * 2))), acc[v]);
-      }
+      for (int v = 0; v < NV; ++v) acc[v] = __builtin_fmaf(val, mf_act<BF16>(lds_u16(sdyn, moff[v] + kk2)), acc[v]);
     }
   }
   // ---- rank term (slice 0): [t_hi | t_lo] x [R^T | R^T] on the matrix cores ----
   if (a.r16 != nullptr && z == 0) {
     const int rp2 = 2 * a.rp, trow = mf_trow(a.rp);
     __syncthreads();  // every wave is done with the activation slice
-    for (int i = tid; i < MT * a.rp; i += 256) {
+    for (int i = tid; i < (MT + 1) * a.rp; i += 256) {  // row MT: zeros
       const int m = i / a.rp, j = i - m * a.rp;
       const float tv = (m < a.M && j < a.rank) ? a.t[(size_t)m * a.rank + j] : 0.f;
       const uint32_t hi = mf_to16<BF16>(tv);
@@ -363,8 +376,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
     const brsrc_t rr = make_rsrc(a.r16, (uint32_t)a.Npad * (uint32_t)rp2 * 2u);
     for (int s = 0; s < rp2 / 16; ++s) {
       const uint4 wv = bload128(rr, ((uint32_t)n * (uint32_t)rp2 + (uint32_t)(16 * s + 8 * half)) * 2u, 0);
-      const uint4 ta = mok ? *reinterpret_cast<const uint4*>(sb + mrow * trow + (16 * s + 8 * half) * 2)
-                           : make_uint4(0, 0, 0, 0);
+      const uint4 ta = *reinterpret_cast<const uint4*>(sb + mrow_s * trow + (16 * s + 8 * half) * 2);
       acc = mf_mfma<BF16>(ta, wv, acc);
     }
   }
@@ -429,8 +441,8 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
 
 template <int KIND, bool BF16, int MT>
 static hipError_t launch_mfma_t(const MfArgs& a, hipStream_t st) {
-  const int lds_x = MT * mf_xrow(a.Kz);
-  const int lds_t = a.r16 ? MT * mf_trow(a.rp) : 0;
+  const int lds_x = (MT + 1) * mf_xrow(a.Kz);
+  const int lds_t = a.r16 ? (MT + 1) * mf_trow(a.rp) : 0;
   const int lds = lds_x > lds_t ? lds_x : lds_t;
   hipLaunchKernelGGL((decode_mfma_kernel<KIND, BF16, MT>), dim3(a.tiles * a.S), dim3(256), lds, st, a);
   return hipGetLastError();
@@ -438,7 +450,7 @@ static hipError_t launch_mfma_t(const MfArgs& a, hipStream_t st) {
 
 template <int KIND>
 hipError_t launch_mfma_kind(const MfArgs& a, bool bf16, hipStream_t st) {
-  if (a.Kz > kMfKzMax || a.Kz % MfCfg<KIND>::passk || a.M > 32 || a.M < 1 || a.Kz >= 65536)
+  if (a.Kz > kMfKzMax || a.Kz % MfCfg<KIND, 32>::passk || a.M > 32 || a.M < 1 || a.Kz >= 65536)
     return hipErrorInvalidValue;
   if (a.M <= 8) return bf16 ? launch_mfma_t<KIND, true, 8>(a, st) : launch_mfma_t<KIND, false, 8>(a, st);
   if (a.M <= 16) return bf16 ? launch_mfma_t<KIND, true, 16>(a, st) : launch_mfma_t<KIND, false, 16>(a, st);
