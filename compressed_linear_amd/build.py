@@ -27,7 +27,7 @@ SOURCES = ["pack.cpp", "runtime.hip", "decode.hip", "aux.hip", "prefill.hip",
            "decode_rows_lut3.hip", "decode_rows_lut4.hip", "decode_rows_int4.hip", "decode_rows_int4_24.hip",
            "decode_rows_int8.hip",
            "decode_mfma_lut3.hip", "decode_mfma_lut4.hip", "decode_mfma_int4.hip", "decode_mfma_int4_24.hip",
-           "decode_mfma_int8.hip",
+           "decode_mfma_int8.hip", "decode_mfma_int8_bm.hip",
            "prefill_lut3.hip", "prefill_lut4.hip", "prefill_int.hip", "prefill_lr.hip"]
 
 COMMON = [

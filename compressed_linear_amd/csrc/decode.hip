@@ -26,6 +26,7 @@ extern template hipError_t launch_mfma_kind<K_LUT4>(const MfArgs&, bool, hipStre
 extern template hipError_t launch_mfma_kind<K_INT4>(const MfArgs&, bool, hipStream_t);
 extern template hipError_t launch_mfma_kind<K_INT4_24>(const MfArgs&, bool, hipStream_t);
 extern template hipError_t launch_mfma_kind<K_INT8>(const MfArgs&, bool, hipStream_t);
+extern template hipError_t launch_mfma_kind<K_INT8_BM>(const MfArgs&, bool, hipStream_t);
 
 // Smallest batch that the automatic choice sends to the matrix-core decode kernel.
 constexpr int kMfMinM = 4;
@@ -54,6 +55,8 @@ static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float
   a.ooff = h.nnz > 0 ? L.mf_ooff : nullptr;
   a.oent = L.mf_oent;
   a.nnz = (int)h.nnz;
+  a.nzs = L.mf_nzs;
+  a.dense_bytes = (uint32_t)h.len[CL_SEC_DENSE];
   a.r16 = h.lr != CL_LR_NONE ? L.pf_r16 : nullptr;
   a.t = L.t;
   a.rank = h.rank;
@@ -67,7 +70,8 @@ static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float
     case CL_DENSE_LUT4: return launch_mfma_kind<K_LUT4>(a, bf16, stream);
     case CL_DENSE_INT4:
       return h.mask == CL_MASK_2_4 ? launch_mfma_kind<K_INT4_24>(a, bf16, stream) : launch_mfma_kind<K_INT4>(a, bf16, stream);
-    default: return launch_mfma_kind<K_INT8>(a, bf16, stream);
+    default:
+      return h.mask == CL_MASK_BITMAP ? launch_mfma_kind<K_INT8_BM>(a, bf16, stream) : launch_mfma_kind<K_INT8>(a, bf16, stream);
   }
 }
 

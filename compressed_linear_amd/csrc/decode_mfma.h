@@ -58,6 +58,8 @@ struct MfArgs {
   const void* x;
   int ldx, M, K, N, Npad, chunks;
   int tiles, S, Kz, npw;        // 128-row tiles, K slices, columns per slice, passes per slice
+  const int32_t* nzs;           // bitmap: byte offset of the first kept value of every (row, slice) [Npad][S]
+  uint32_t dense_bytes;         // bytes of the dense section (bitmap: the kept values)
   const int32_t* ooff;          // outlier offsets per (slice, tile, row): [S * tiles * 128 + 1]
   const uint32_t* oent;         // entries: k in slice (low 16 bits) | fp16 value << 16
   int nnz;                      // entries in oent
@@ -141,14 +143,25 @@ __device__ __forceinline__ void lut4_word_single(const uint32_t* lds, uint32_t w
 // lookup per two weights, measured slower here: the 32 rows of a wavefront
 // look up different tables, and their bank conflicts cost more than the
 // lookups they save.)
+//
+// The bitmap format takes one 128-k chunk per lane half and pass: its kept
+// values sit at data-dependent offsets, so each lane stages the window holding
+// its chunk's kept bytes (at most 144 bytes from a 16-byte aligned start) in a
+// slot of its own in LDS, and expands it by the chunk's keep bits with the
+// nibble selector table (the tile kernel's expansion).
+constexpr int kMfBmSlot = 37;  // dwords per lane slot (odd: lanes fall in distinct banks)
 template <int KIND, int MT>
 struct MfCfg {
   static constexpr int span = KindTraits<KIND>::span, pairs = KindTraits<KIND>::pairs;
-  static constexpr int passk = 2 * kMfCph * span;  // k per pass
+  static constexpr int cph = KIND == K_INT8_BM ? 1 : kMfCph;  // chunks per lane half per pass
+  static constexpr int passk = 2 * cph * span;                // k per pass
   static constexpr int ents = KIND == K_LUT3 ? 8 : KIND == K_LUT4 ? 16 : 0;  // table entries per row
   // static LDS at address 0: four stacked lane-interleaved single-entry table
-  // sets, or the 2:4 selectors
-  static constexpr int tab_bytes = ents ? 4 * ents * 256 : KIND == K_INT4_24 ? 128 : 16;
+  // sets, the 2:4 selectors, or the bitmap's nibble selectors and lane slots
+  static constexpr int tab_bytes = ents ? 4 * ents * 256
+                                   : KIND == K_INT4_24 ? 128
+                                   : KIND == K_INT8_BM ? (kBmSelDwords + 256 * kMfBmSlot) * 4
+                                                       : 16;
 };
 
 // LDS bytes per staged activation row: the slice padded so that the row
@@ -162,6 +175,8 @@ template <int KIND, bool BF16, int MT>
 __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   using C = MfCfg<KIND, MT>;
   constexpr int SPAN = C::span, P = C::pairs, PASSK = C::passk, NMF = P / 4;  // MFMAs per chunk
+  constexpr int CPH = C::cph;
+  constexpr bool BM = KIND == K_INT8_BM;
   // outputs v of a lane whose activation row m(v) = 8 (v / 4) + 4 half + v mod 4 is below MT
   constexpr int NV = MT >= 32 ? 16 : MT / 2;
   constexpr int XR = MT * kMfKzMax / 8 / 256;  // 16-byte activation slots per thread
@@ -216,10 +231,10 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   const int cbase = k0 / SPAN;  // first chunk of the slice (Kz is a whole number of passes)
   const brsrc_t rd = make_rsrc(a.dense, (uint32_t)a.Npad * (uint32_t)a.chunks * 16u);
   const brsrc_t rm = make_rsrc(a.meta, KIND == K_INT4_24 ? (uint32_t)a.Npad * (uint32_t)a.chunks * 8u : 0u);
-  auto load_pass = [&](uint4 (&w)[kMfCph], uint2 (&mw)[kMfCph], int p) {
+  auto load_pass = [&](uint4 (&w)[CPH], uint2 (&mw)[CPH], int p) {
 #pragma unroll
-    for (int q = 0; q < kMfCph; ++q) {
-      const int c = cbase + p * 2 * kMfCph + half * kMfCph + q;
+    for (int q = 0; q < CPH; ++q) {
+      const int c = cbase + p * 2 * CPH + half * CPH + q;
       const bool ok = p < a.npw && c < a.chunks;
       const uint32_t idx = (uint32_t)n * (uint32_t)a.chunks + (uint32_t)c;
       w[q] = bload128(rd, ok ? idx * 16u : kNoLoad, 0);
@@ -229,11 +244,26 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
         mw[q] = make_uint2(0, 0);
     }
   };
-  uint4 WA[kMfCph], WB[kMfCph], WC[kMfCph];
-  uint2 MA[kMfCph], MB[kMfCph], MC[kMfCph];
-  load_pass(WA, MA, 0);
-  load_pass(WB, MB, 1);
-  load_pass(WC, MC, 2);
+  uint4 WA[CPH], WB[CPH], WC[CPH];
+  uint2 MA[CPH], MB[CPH], MC[CPH];
+  // bitmap: the keep bits of every pass of the slice and the slice's first kept byte
+  constexpr int NPB = kMfKzMax / (BM ? PASSK : kMfKzMax);
+  uint4 bmeta[NPB];
+  uint32_t nz0 = 0;
+  if constexpr (BM) {
+#pragma unroll
+    for (int p = 0; p < NPB; ++p) {
+      const int c = cbase + 2 * p + half;
+      const bool ok = p < a.npw && c < a.chunks;
+      bmeta[p] = bload128(make_rsrc(a.meta, (uint32_t)a.Npad * (uint32_t)a.chunks * 16u),
+                          ok ? ((uint32_t)n * (uint32_t)a.chunks + (uint32_t)c) * 16u : kNoLoad, 0);
+    }
+    nz0 = bload32(make_rsrc(a.nzs, (uint32_t)a.Npad * (uint32_t)a.S * 4u), ((uint32_t)n * (uint32_t)a.S + (uint32_t)z) * 4u, 0);
+  } else {
+    load_pass(WA, MA, 0);
+    load_pass(WB, MB, 1);
+    load_pass(WC, MC, 2);
+  }
   // keep the issue order (the outlier entries below wait for their offsets:
   // issued before the code stream they would hold it back by one latency)
   __builtin_amdgcn_sched_barrier(0);
@@ -271,6 +301,8 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
       stab[2 * tid] = e.x;
       stab[2 * tid + 1] = e.y;
     }
+  } else if constexpr (BM) {
+    if (tid < 16) stab[tid] = bitmap_sel_entry((uint32_t)tid);
   }
   __syncthreads();
 
@@ -285,11 +317,82 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   const uint32_t mk1 = vconst(KIND == K_LUT3 ? 0x00070000u : 0x03030303u);
   const uint32_t mk2 = vconst(0x0C0C0C0Cu);
   const int mrow_s = mrow < MT ? mrow : MT;  // rows past MT read the zero row
-  const uint8_t* xr = sb + mrow_s * xrow + half * kMfCph * SPAN * 2;
-  auto comp_pass = [&](const uint4 (&w)[kMfCph], const uint2 (&mw)[kMfCph], int p) {
+  const uint8_t* xr = sb + mrow_s * xrow + half * CPH * SPAN * 2;
+  if constexpr (BM) {
+    // kept-byte windows: lane half h's chunk of pass p starts after the slice's
+    // earlier kept values and, for h = 1, after its partner's (lane l - 32) chunk
+    uint32_t start[NPB], cnt[NPB];
+    {
+      uint32_t run = nz0;
+#pragma unroll
+      for (int p = 0; p < NPB; ++p) {
+        cnt[p] = __builtin_popcount(bmeta[p].x) + __builtin_popcount(bmeta[p].y) + __builtin_popcount(bmeta[p].z) +
+                 __builtin_popcount(bmeta[p].w);
+        const uint32_t pc = (uint32_t)__shfl_xor((int)cnt[p], 32, 64);
+        start[p] = run + (half ? pc : 0u);
+        run += cnt[p] + pc;
+      }
+    }
+    const brsrc_t rk = make_rsrc(a.dense, a.dense_bytes);  // kept values; a window past the end reads zero
+    auto load_kept = [&](uint4 (&kw)[9], int p) {
+      const uint32_t b0 = start[p < NPB ? p : 0] & ~15u, end = start[p < NPB ? p : 0] + cnt[p < NPB ? p : 0];
+#pragma unroll
+      for (int i = 0; i < 9; ++i) kw[i] = bload128(rk, p < a.npw && b0 + 16u * i < end ? b0 + 16u * i : kNoLoad, 0);
+    };
+    uint4 KA[9], KB[9];
+    load_kept(KA, 0);
+    load_kept(KB, 1);
+    const uint32_t slot = (uint32_t)(kBmSelDwords + tid * kMfBmSlot) * 4u;
+    auto comp_bm = [&](const uint4 (&kw)[9], int p) {
+      if (p >= a.npw) return;
+      uint32_t* sl = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(stab) + slot);
+#pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        sl[4 * i] = kw[i].x;
+        sl[4 * i + 1] = kw[i].y;
+        sl[4 * i + 2] = kw[i].z;
+        sl[4 * i + 3] = kw[i].w;
+      }
+      uint32_t off = slot + (start[p] & 15u);
+      const uint32_t mw4[4] = {bmeta[p].x, bmeta[p].y, bmeta[p].z, bmeta[p].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // 32 k of the chunk
+        uint32_t wp[16];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const uint32_t nib = (mw4[i] >> (4 * t)) & 0xFu;
+          const uint32_t lo = lds_u32(stab, off & ~3u), hi = lds_u32(stab, (off & ~3u) + 4u);
+          const uint32_t win = __builtin_amdgcn_alignbyte(hi, lo, off & 3u);
+          int8x4_signed(perm(0u, win, lds_u32(stab, nib * 4u)), &wp[2 * t]);
+          off += __builtin_popcount(nib);
+        }
+        if constexpr (BF16) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const half2_t hv = as_h2(wp[j]);
+            wp[j] = mf_to16<true>((float)hv.x) | (mf_to16<true>((float)hv.y) << 16);
+          }
+        }
+        const uint8_t* xq = xr + (p * PASSK + 32 * i) * 2;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 xa = *reinterpret_cast<const uint4*>(xq + 16 * j);
+          acc = mf_mfma<BF16>(xa, make_uint4(wp[4 * j], wp[4 * j + 1], wp[4 * j + 2], wp[4 * j + 3]), acc);
+        }
+      }
+    };
+#pragma unroll
+    for (int p = 0; p < NPB; p += 2) {
+      comp_bm(KA, p);
+      load_kept(KA, p + 2);
+      comp_bm(KB, p + 1);
+      load_kept(KB, p + 3);
+    }
+  } else {
+  auto comp_pass = [&](const uint4 (&w)[CPH], const uint2 (&mw)[CPH], int p) {
     if (p >= a.npw) return;
 #pragma unroll
-    for (int q = 0; q < kMfCph; ++q) {
+    for (int q = 0; q < CPH; ++q) {
       uint32_t wp[P];
       const uint32_t ww[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
       if constexpr (KIND == K_LUT3) {
@@ -332,6 +435,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
     load_pass(WC, MC, p + 5);
   }
 
+  }
   // lane l holds row rt for activation rows m(v) = 8 (v / 4) + 4 half + v mod 4
   // ---- integer formats: the row scale multiplies the dense part only ----
   if constexpr (!LUT) {

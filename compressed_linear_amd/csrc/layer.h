@@ -63,11 +63,12 @@ struct Layer {
                                  // published epoch [65]; counters zero between forwards
   uint32_t lr_epoch = 0;         // forwards issued (the decode kernel's prologue publishes it)
 
-  // matrix-core decode (batch 2..32, all formats but the bitmap; absent when max_M == 1)
+  // matrix-core decode (batch 2..32; absent when max_M == 1)
   int mf_npw = 0, mf_Kz = 0, mf_S = 0, mf_tiles = 0;
   float* mf_part = nullptr;      // slice partial sums [tiles][S][32][128]
   int32_t* mf_ooff = nullptr;    // outlier offsets per (slice, tile, row in tile): [S * tiles * 128 + 1]
   uint32_t* mf_oent = nullptr;   // entries: k in slice | fp16 value << 16
+  int32_t* mf_nzs = nullptr;     // bitmap: first kept byte of every (row, slice) [Npad][S]
   size_t ws_bytes = 0;
 };
 

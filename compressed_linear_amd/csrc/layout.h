@@ -80,7 +80,10 @@ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 constexpr int kMfRows = 128;    // weight rows per workgroup (four wavefronts of 32)
 constexpr int kMfCph = 4;       // chunks per lane half per pass (two halves read one 128-byte line of a row)
 constexpr int kMfKzMax = 1024;  // largest K slice (bounds the activation staging in LDS)
-inline int mf_pass_k(int dense, int mask) { return 2 * kMfCph * kind_info(dense, mask).span; }
+// (the bitmap format: one chunk per lane half and pass)
+inline int mf_pass_k(int dense, int mask) {
+  return 2 * (dense == 3 && mask == 2 ? 1 : kMfCph) * kind_info(dense, mask).span;
+}
 // Passes per K slice: about 1024 columns (768 for the 4-bit LUT, whose tables
 // take more LDS), fewer when the layer would give under two workgroups per CU
 // of a 256-CU device.  Independent of M, so that the outlier lists built at

@@ -38,9 +38,9 @@ static hipError_t prefill_by_decode(const Layer& L, int M, const void* x, float*
     const void* xb = static_cast<const uint16_t*>(x) + (size_t)m0 * ldx;
     Layer Lb = L;
     if (x == L.xprep) Lb.xprep = const_cast<uint16_t*>(static_cast<const uint16_t*>(xb));
-    // the bitmap format always takes the tile kernel, whose prologue is a kernel
-    // of its own (no epoch is published)
-    const hipError_t e = launch_decode(Lb, mb, xb, y + (size_t)m0 * L.h.N, stream, 0u, 1);
+    // the bitmap format takes the matrix-core decode kernel (or, for a layer
+    // without its workspace, the tile kernel); neither publishes an epoch
+    const hipError_t e = launch_decode(Lb, mb, xb, y + (size_t)m0 * L.h.N, stream, 0u, 0);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

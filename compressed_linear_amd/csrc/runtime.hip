@@ -67,7 +67,8 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
   const int Kx = (int)round_up(h.K, 8);
   if (h.has_clamp || (h.K & 7)) o_xp = take((size_t)max_M * Kx * 2);
   // matrix-core prefill (all formats but the bitmap): outlier lists per
-  // (128-row tile, K step), R^T twice and L^T in the MFMA input type, t_hi | t_lo
+  // (128-row tile, K step), R^T twice and L^T in the MFMA input type, t_hi | t_lo;
+  // R^T twice also for a bitmap layer that the matrix-core decode may run (max_M >= 2)
   size_t o_pfp = 0, o_pfe = 0, o_pfr = 0, o_pfl = 0, o_pft = 0;
   int pf_nd = 0;
   const int rp = (int)round_up(h.rank, 8);
@@ -84,11 +85,13 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
       o_pfl = take((size_t)h.rank * Kx * 2);
       o_pft = take((size_t)max_M * 2 * rp * 2);
     }
+  } else if (has_lr && max_M >= 2) {
+    o_pfr = take((size_t)Npad * 2 * rp * 2);
   }
   // matrix-core decode: slice partial sums, outlier lists per (slice, tile, row)
-  size_t o_mfp = 0, o_mfo = 0, o_mfe = 0;
+  size_t o_mfp = 0, o_mfo = 0, o_mfe = 0, o_mfz = 0;
   int mf_npw = 0, mf_Kz = 0, mf_S = 0, mf_tiles = 0;
-  if (h.mask != CL_MASK_BITMAP && max_M >= 2) {
+  if (max_M >= 2) {
     mf_npw = mf_passes(h.dense, h.mask, h.K, h.N);
     mf_Kz = mf_npw * mf_pass_k(h.dense, h.mask);
     mf_tiles = (int)ceil_div(h.N, kMfRows);
@@ -98,6 +101,7 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
       o_mfo = take(((size_t)mf_S * mf_tiles * kMfRows + 1) * 4);
       o_mfe = take((size_t)h.nnz * 4);
     }
+    if (h.mask == CL_MASK_BITMAP) o_mfz = take((size_t)Npad * mf_S * 4);
   }
   // decode low-rank prologue: k-major copy of L, partial sums, arrival counters
   size_t o_lk = 0, o_ls = 0, o_lp = 0, o_lc = 0;
@@ -141,6 +145,7 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
     L->mf_part = o_mfp ? reinterpret_cast<float*>(d + o_mfp) : nullptr;
     L->mf_ooff = o_mfo ? reinterpret_cast<int32_t*>(d + o_mfo) : nullptr;
     L->mf_oent = o_mfe ? reinterpret_cast<uint32_t*>(d + o_mfe) : nullptr;
+    L->mf_nzs = o_mfz ? reinterpret_cast<int32_t*>(d + o_mfz) : nullptr;
     L->ws_bytes = off - align256(base);
   }
   return off;
@@ -166,11 +171,12 @@ struct PrefillHost {
   std::vector<uint32_t> cent;
   std::vector<uint16_t> r16, l16;
 };
+// r16_only: just R^T twice (a bitmap layer: no LDS-tile prefill data).
 static void build_prefill_host(const cl_blob_header& h, const uint8_t* b, int Npad, int nd, int rp, int Kl,
-                               PrefillHost& out) {
+                               PrefillHost& out, bool r16_only) {
   const bool bf = h.x_dtype == CL_ACT_BF16;
   auto to16 = [&](float f) { return bf ? f2bf(f) : f2h(f); };
-  if (h.nnz > 0) {
+  if (h.nnz > 0 && !r16_only) {
     const int bk = pf_step_k(h.dense, h.mask), nt = (int)ceil_div(Npad, kPfTileN);
     const int32_t* rp_ = reinterpret_cast<const int32_t*>(b + h.off[CL_SEC_ROWPTR]);
     const int32_t* col = reinterpret_cast<const int32_t*>(b + h.off[CL_SEC_COL]);
@@ -219,6 +225,7 @@ static void build_prefill_host(const cl_blob_header& h, const uint8_t* b, int Np
         out.r16[(size_t)n * 2 * rp + j] = v;
         out.r16[(size_t)n * 2 * rp + rp + j] = v;
       }
+    if (r16_only) return;
     out.l16.assign((size_t)r * Kl, 0);
     for (int j = 0; j < r; ++j)
       for (int k = 0; k < h.K; ++k) out.l16[(size_t)j * Kl + k] = to16(factor(Lf, Ls, j, k, h.K));
@@ -359,10 +366,30 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
     }
   }
   PrefillHost pf;
-  if (h->mask != CL_MASK_BITMAP)
-    build_prefill_host(*h, static_cast<const uint8_t*>(blob), L->Npad, L->pf_nd, L->pf_rp, L->pf_Kl, pf);
+  if (h->mask != CL_MASK_BITMAP || L->pf_r16)
+    build_prefill_host(*h, static_cast<const uint8_t*>(blob), L->Npad, L->pf_nd, L->pf_rp, L->pf_Kl, pf,
+                       h->mask == CL_MASK_BITMAP);
   std::vector<int32_t> mfo;
   std::vector<uint32_t> mfe;
+  // bitmap, matrix-core decode: first kept byte of every (row, K slice)
+  std::vector<int32_t> mfz;
+  if (L->mf_nzs) {
+    const uint8_t* b = static_cast<const uint8_t*>(blob);
+    const int32_t* off = reinterpret_cast<const int32_t*>(b + h->off[CL_SEC_NZOFF]);
+    const uint32_t* meta = reinterpret_cast<const uint32_t*>(b + h->off[CL_SEC_META]);
+    const int cps = L->mf_Kz / h->span;  // chunks per slice
+    mfz.assign((size_t)L->Npad * L->mf_S, 0);
+    for (int n = 0; n < h->N; ++n) {
+      long long cnt = off[n];
+      for (int zz = 0; zz < L->mf_S; ++zz) {
+        mfz[(size_t)n * L->mf_S + zz] = (int32_t)cnt;
+        for (int c = zz * cps; c < (zz + 1) * cps && c < h->chunks; ++c) {
+          const uint32_t* w = meta + ((size_t)n * h->chunks + c) * 4;
+          cnt += __builtin_popcount(w[0]) + __builtin_popcount(w[1]) + __builtin_popcount(w[2]) + __builtin_popcount(w[3]);
+        }
+      }
+    }
+  }
   if (L->mf_ooff)
     build_mfma_outliers(*h, static_cast<const uint8_t*>(blob), L->mf_S, L->mf_tiles, L->mf_Kz, mfo, mfe);
   std::vector<uint8_t> lrk;
@@ -384,6 +411,8 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
     e = hipMemcpyAsync(L->pf_r16, pf.r16.data(), pf.r16.size() * 2, hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !pf.l16.empty())
     e = hipMemcpyAsync(L->pf_l16, pf.l16.data(), pf.l16.size() * 2, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !mfz.empty())
+    e = hipMemcpyAsync(L->mf_nzs, mfz.data(), mfz.size() * 4, hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !mfo.empty())
     e = hipMemcpyAsync(L->mf_ooff, mfo.data(), mfo.size() * 4, hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !mfe.empty())
@@ -409,7 +438,7 @@ static cl_status forward_impl(Layer* L, int32_t M, const void* x, float* y, void
   const bool decode = path != CL_PATH_PREFILL;
   if (decode && M > kMaxDecodeM) return fail(CL_EINVAL, "the decode path takes M <= %d", kMaxDecodeM);
   if (path == CL_PATH_DECODE_MFMA && L->mf_S == 0)
-    return fail(CL_EUNSUPPORTED, "the matrix-core decode needs a layer without the bitmap mask, created with max_M >= 2");
+    return fail(CL_EUNSUPPORTED, "the matrix-core decode needs a layer created with max_M >= 2");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const void* xa = x;
   hipError_t e = hipSuccess;

@@ -1,8 +1,8 @@
 """The matrix-core decode kernel (batch 2..32, weights dequantised in registers)
 against the CPU oracle, through the C ABI (needs an MI355X).
 
-Every format but the bitmap, with and without outliers and rank terms, fp16 and
-bf16 activations, at batch sizes across the 8 / 16 / 32 staging variants, on
+Every format (the bitmap through its per-lane kept-byte windows), with and
+without outliers and rank terms, fp16 and bf16 activations, at batch sizes across the 8 / 16 / 32 staging variants, on
 shapes with a partial 128-row tile and a partial K slice; the golden dyadic
 cases exactly; bitwise determinism across the split-K reduction; and the same
 cases through the vector-ALU decode kernels (forced), which the automatic
@@ -27,14 +27,14 @@ def say(*a):
 
 
 # (cfg, K, N): partial 128-row tiles and K not a multiple of the slice
-SHAPES = {1: (2410, 200), 2: (3000, 330), 3: (2300, 130), 5: (2900, 190)}
+SHAPES = {1: (2410, 200), 2: (3000, 330), 3: (2300, 130), 4: (2560, 170), 5: (2900, 190)}
 MS = (1, 2, 5, 8, 9, 16, 17, 32)
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_mfma_decode_configs(cfg):
     K, N = SHAPES[cfg]
-    layer = make_layer(cfg, 0, K=K, N=N)
+    layer = make_layer(cfg, 0, K=K, N=N, M_for_clamp=16)
     mod = gpu_layer(layer, max_M=32)
     for M in MS:
         x = make_x(cfg, 0, M, K=K)
@@ -60,8 +60,6 @@ def test_valu_decode_forced(cfg):
 @pytest.mark.parametrize("name", golden_names())
 def test_mfma_golden_exact(name):
     layer, x, y_exp, _ = load_golden(name)
-    if layer.mask == "bitmap":
-        pytest.skip("the bitmap format has no matrix-core decode kernel")
     say("mfma golden", name)
     mod = gpu_layer(layer, max_M=max(2, x.shape[0]))
     y = gpu_forward(layer, x, path="decode_mfma", mod=mod)
@@ -159,9 +157,32 @@ def test_mfma_path_errors():
     with pytest.raises(cla.ClError):
         mod.forward(x, path="decode_mfma")
     mod.close()
-    bm = make_layer(4, 0, K=256, N=64)
-    modb = gpu_layer(bm, max_M=4)
-    xb = to_device_x(make_x(4, 0, 2, K=256), "f16")
-    with pytest.raises(cla.ClError):
-        modb.forward(xb, path="decode_mfma")
-    modb.close()
+
+
+def test_mfma_bitmap_layers():
+    # unstructured masks of other densities (a chunk with no kept value, one
+    # with all 128), a row with no kept value, bitmap rows with outliers and a
+    # rank term, bf16 activations
+    r = np.random.default_rng(41)
+    K, N = 1536, 140
+    keep = (r.random((N, K)) < 0.3).astype(np.uint8)
+    keep[3, :] = 0
+    keep[5, 128:256] = 1
+    keep[7, 256:384] = 0
+    q = r.integers(-127, 128, size=(N, K)).astype(np.int8)
+    s = r.uniform(0.001, 0.01, N).astype(np.float16)
+    lay = LogicalLayer(K=K, N=N, dense="int8", mask="bitmap", qvals=q, keep=keep, row_scale=s)
+    rp, col, val = draw_csr_skewed(r, r, N, K, density=0.005)
+    lay_csr = lay.with_(csr_row_ptr=rp, csr_col=col, csr_val=val)
+    from test_gpu_parity import _with_lowrank
+    lay_lr = _with_lowrank(lay, "int4", 128, 128, seed=9)
+    for L_, what in ((lay, "bitmap 30%"), (lay_csr, "bitmap + csr"), (lay_lr, "bitmap + int4 rank")):
+        mod = gpu_layer(L_, max_M=32)
+        for M in (1, 6, 16, 32):
+            x = r.normal(0, 1, (M, K)).astype(np.float16)
+            say("mfma", what, "M", M)
+            check_bound(gpu_forward(L_, x, path="decode_mfma", mod=mod), L_, x, what=f"{what} M={M}")
+        mod.close()
+    layb = lay.with_(x_dtype="bf16")
+    xb = bf16_bits_from_f32(r.normal(0, 1, (12, K)))
+    check_bound(gpu_forward(layb, xb, path="decode_mfma"), layb, xb, what="bitmap bf16")
