@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "batch-1 µs/layer & effective HBM GB/s (% of peak) for compressed GEMV"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0   # dense fp16 / bf16 matrix-core peak
 ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_lut4_llama7b_b1_traffic.txt")
 KERNEL_SOURCES = ["compressed_linear_amd/csrc/decode_rows.h", "compressed_linear_amd/csrc/unpack.h",
@@ -71,6 +72,39 @@ def read_traffic(bytes_per_launch_alg: float):
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def roofline(cfg: int, M: int, path: str, built, set_bytes: int, us_per_launch: float) -> dict:
+    """Roofline entry for the launches of one layer (mean over the layers of a step).
+
+    Decode (M <= 32) is priced on algorithmic HBM bytes (packed weights + x + y)
+    against the 8 TB/s peak; prefill on algorithmic flops (2*M*K*N for the
+    weight product, 2*M*r*(K+N) for a rank term) against the dense fp16/bf16
+    matrix-core peak.  The counter-based HBM traffic figure is committed for the
+    default workload only (LLaMA-7B set, batch 1), whose step is one decode
+    kernel per layer; elsewhere it is null.
+    """
+    n = len(built)
+    if M > 32:
+        flops = sum(2.0 * M * l.K * l.N + (2.0 * M * l.rank * (l.K + l.N) if l.rank else 0.0) for l, _, _ in built) / n
+        achieved = flops / (us_per_launch * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": f"prefill (weight tiles dequantised into LDS, 16-bit matrix cores), M {M}",
+                "flops_per_launch": int(flops), "us_per_launch": round(us_per_launch, 3)}
+    bytes_per_launch = set_bytes / n
+    achieved = bytes_per_launch / us_per_launch / 1e3
+    default = cfg == 2 and M == 1 and path == "auto"
+    if default:
+        kernel = "decode_rows_kernel (LUT4 + CSR, batch 1)"
+    elif M == 1 or path == "decode_valu":
+        kernel = f"vector-ALU decode, batch {M} (all launches of a layer)"
+    else:
+        kernel = f"decode, batch {M}, path {path} (all launches of a layer)"
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic(bytes_per_launch) if default else None,
+            "kernel": kernel, "bytes_per_launch": int(bytes_per_launch), "us_per_launch": round(us_per_launch, 3)}
 
 
 def layer_bytes(acct: dict, K: int, N: int, M: int) -> int:
@@ -232,16 +266,7 @@ def main():
                               "bytes": b})
             log(f"  {per_layer[-1]}")
 
-    # roofline of the decode kernel: algorithmic bytes per launch over the mean launch duration
-    bytes_per_launch = set_bytes / n_launch
-    us_per_launch = ms_per_step * 1e3 / n_launch
-    achieved = bytes_per_launch / us_per_launch / 1e3
-    traffic = read_traffic(bytes_per_launch)
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "decode_rows_kernel (LUT4 + CSR, batch 1)", "bytes_per_launch": int(bytes_per_launch),
-            "us_per_launch": round(us_per_launch, 3)}
-
+    roof = roofline(cfg, M, a.path, built, set_bytes, ms_per_step * 1e3 / n_launch)
     cpu = None
     if not a.no_cpu_baseline:
         log("timing the CPU oracle baseline")
