@@ -31,9 +31,26 @@ extern template hipError_t launch_mfma_kind<K_INT8_BM>(const MfArgs&, bool, hipS
 // Smallest batch that the automatic choice sends to the matrix-core decode kernel.
 constexpr int kMfMinM = 4;
 
+// x: the caller's activations, or L.xprep when they are clamped / restaged
+// already.  The matrix-core kernel reads them raw when K is a multiple of 8 (16-byte
+// aligned rows) and the low-rank prologue, if any, runs inside the same launch:
+// both then apply the clamp while staging.  Otherwise a prep kernel runs first.
 static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float* y, hipStream_t stream) {
   const cl_blob_header& h = L.h;
-  if (h.lr != CL_LR_NONE) {
+  const bool has_lr = h.lr != CL_LR_NONE;
+  const bool fused_lr = has_lr && L.lr_mode >= 0;
+  const bool raw = L.xprep != nullptr && x != L.xprep;
+  bool clamp_in_kernel = false;
+  if (raw) {
+    if (h.K % 8 == 0 && (!has_lr || fused_lr)) {
+      clamp_in_kernel = h.has_clamp != 0;
+    } else {
+      const hipError_t e = launch_prep_x(L, M, x, stream);
+      if (e != hipSuccess) return e;
+      x = L.xprep;
+    }
+  }
+  if (has_lr && !fused_lr) {
     const hipError_t e = launch_lowrank_prologue(L, M, x, stream);
     if (e != hipSuccess) return e;
   }
@@ -64,6 +81,19 @@ static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float
   a.part = L.mf_part;
   a.counters = L.counters;
   a.y = y;
+  a.clamp = clamp_in_kernel ? 1 : 0;
+  a.cval = (float)__builtin_bit_cast(_Float16, h.act_clamp);
+  if (fused_lr) {
+    a.lrp = lowrank_split_args(L, M, x);
+    a.lr_ntj = L.lr_rpad / 64;
+    a.lrp.ntiles = a.lr_ntj * (int)ceil_div(M, kMfLrTile);
+    a.lrp.flag = L.lr_cnt + 65;
+    a.lrp.epoch = ++L.lr_epoch;
+    a.lrp.clamp = a.clamp;
+    a.lrp.cval = a.cval;
+    a.lr_wgs = L.lr_S * a.lrp.ntiles;
+    a.lr_mode = L.lr_mode;
+  }
   const bool bf16 = h.x_dtype == CL_ACT_BF16;
   switch (h.dense) {
     case CL_DENSE_LUT3: return launch_mfma_kind<K_LUT3>(a, bf16, stream);
@@ -75,12 +105,18 @@ static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float
   }
 }
 
-hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, uint32_t epoch,
-                         int variant) {
+hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, int variant) {
   // bf16 activations cost the row-wise kernel two multiply-adds per weight pair
   // and activation row (no mixed fp16 x bf16 dot product), so it keeps only batch 1
   const bool mf_auto = M >= kMfMinM || (M >= 2 && L.h.x_dtype == CL_ACT_BF16);
   if (L.mf_S > 0 && (variant == 2 || (variant == 0 && mf_auto))) return launch_decode_mfma(L, M, x, y, stream);
+  // the batch 1..3 kernels read clamped / restaged activations
+  const void* x_raw = x;
+  if (L.xprep != nullptr && x != L.xprep) {
+    const hipError_t e = launch_prep_x(L, M, x, stream);
+    if (e != hipSuccess) return e;
+    x = L.xprep;
+  }
 
   const cl_blob_header& h = L.h;
   DecodeArgs a = {};
@@ -149,6 +185,7 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
       if (L.lr_mode >= 0) {
         // the prologue runs as this launch's first workgroups
         r.lrp = lowrank_split_args(L, M, x);
+        const uint32_t epoch = ++L.lr_epoch;
         r.lrp.flag = L.lr_cnt + 65;
         r.lrp.epoch = epoch;
         r.lr_ntj = L.lr_rpad / 64;
@@ -181,7 +218,7 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
     }
   }
   // batches the row-wise kernel cannot stage: the matrix-core kernel where it applies
-  if (variant == 0 && L.mf_S > 0) return launch_decode_mfma(L, M, x, y, stream);
+  if (variant == 0 && L.mf_S > 0) return launch_decode_mfma(L, M, x_raw, y, stream);
   if (h.lr != CL_LR_NONE) {
     const hipError_t e = launch_lowrank_prologue(L, M, x, stream);
     if (e != hipSuccess) return e;

@@ -29,10 +29,14 @@
 // built when the layer is created; the two lanes of a row add them for their
 // activation rows in fp32 from the staged slice.  The rank-r correction ("SLiM"
 // page, review highlights: y += (x' L) R) is added by the slice-0 workgroups as
-// extra MFMA steps over [t_hi | t_lo] x [R^T | R^T], t = x' L computed
-// beforehand in fp32 and split into two 16-bit parts.  The slices' partial sums
-// meet through device-scope stores, and the last workgroup of a tile adds them
-// in slice order (deterministic, no float atomics).
+// extra MFMA steps over [t_hi | t_lo] x [R^T | R^T], t = x' L in fp32 split
+// into two 16-bit parts.  t comes from the launch's first workgroups (the split
+// prologue block of the batch-1 kernel, publishing the forward's epoch) or from
+// a kernel before it; the workgroups of the last K slice, dispatched last, add
+// the rank term and wait for the epoch first.  The slices' partial sums meet
+// through device-scope stores, and the last workgroup of a tile adds them in
+// slice order (deterministic, no float atomics).  With an activation clamp the
+// activations are clamped while they are staged.
 //
 // Weights enter the matrix cores as 16-bit values of the activation type: fp16
 // LUT values exactly for fp16 activations, rounded to nearest-even bf16 for
@@ -41,6 +45,7 @@
 #include <hip/hip_runtime.h>
 
 #include "layer.h"
+#include "lowrank.h"
 #include "unpack.h"
 
 namespace cl {
@@ -69,7 +74,16 @@ struct MfArgs {
   float* part;                  // slice partials [tiles][S][32][128]
   uint32_t* counters;           // arrivals per tile, zero between forwards
   float* y;
+  int clamp;                    // clamp the activations to [-cval, cval] while staging them
+  float cval;
+  // low-rank prologue in this launch: workgroups [0, lr_wgs) run the split
+  // prologue block (activation tiles of 4 rows, lr_mode 0 or 1) and publish
+  // lrp.epoch in *lrp.flag; lr_wgs = 0: t was computed by an earlier kernel
+  LrSplitArgs lrp;
+  int lr_wgs, lr_ntj, lr_mode;
 };
+
+constexpr int kMfLrTile = 4;  // activation rows per tile of the prologue in this launch
 
 template <bool BF16>
 __device__ __forceinline__ mf_f32x16 mf_mfma(uint4 a, uint4 b, mf_f32x16 c) {
@@ -186,7 +200,15 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile = (int)blockIdx.x % a.tiles, z = (int)blockIdx.x / a.tiles;
+  if (a.lr_wgs > 0 && (int)blockIdx.x < a.lr_wgs) {  // a prologue workgroup
+    const int b = blockIdx.x, S = a.lrp.S, s = b % S, tj = (b / S) % a.lr_ntj, tm = b / (S * a.lr_ntj);
+    uint8_t* smem = reinterpret_cast<uint8_t*>(sdyn);
+    if (a.lr_mode == 0) lr_split_block<0, kMfLrTile, BF16>(a.lrp, s, tj, tm, a.lr_ntj, smem);
+    else lr_split_block<1, kMfLrTile, BF16>(a.lrp, s, tj, tm, a.lr_ntj, smem);
+    return;
+  }
+  const int bid = (int)blockIdx.x - a.lr_wgs;
+  const int tile = bid % a.tiles, z = bid / a.tiles;
   const int rt = wave * 32 + (lane & 31);  // row in tile
   const int n = tile * kMfRows + rt;       // weight row of this lane (>= Npad: reads zeros)
   const int k0 = z * a.Kz;
@@ -277,6 +299,10 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   }
 
   // ---- LDS: activation slice (rows M..MT-1 zero) plus a zero row MT, tables ----
+  if (a.clamp) {
+#pragma unroll
+    for (int i = 0; i < XR; ++i) xs[i] = clamp_act8<BF16>(xs[i], a.cval);
+  }
 #pragma unroll
   for (int i = 0; i < XR; ++i) {
     const int s = i * 256 + tid, m = s / slots_row, c = s - m * slots_row;
@@ -463,13 +489,14 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
       for (int v = 0; v < NV; ++v) acc[v] = __builtin_fmaf(val, mf_act<BF16>(lds_u16(sdyn, moff[v] + kk2)), acc[v]);
     }
   }
-  // ---- rank term (slice 0): [t_hi | t_lo] x [R^T | R^T] on the matrix cores ----
-  if (a.r16 != nullptr && z == 0) {
+  // ---- rank term (last slice): [t_hi | t_lo] x [R^T | R^T] on the matrix cores ----
+  if (a.r16 != nullptr && z == a.S - 1) {
     const int rp2 = 2 * a.rp, trow = mf_trow(a.rp);
-    __syncthreads();  // every wave is done with the activation slice
+    if (a.lr_wgs > 0 && wave == 0) wait_lowrank(a.lrp.flag, a.lrp.epoch, lane);
+    __syncthreads();  // t is published; every wave is done with the activation slice
     for (int i = tid; i < (MT + 1) * a.rp; i += 256) {  // row MT: zeros
       const int m = i / a.rp, j = i - m * a.rp;
-      const float tv = (m < a.M && j < a.rank) ? a.t[(size_t)m * a.rank + j] : 0.f;
+      const float tv = (m < a.M && j < a.rank) ? load_dev(a.t + (size_t)m * a.rank + j) : 0.f;
       const uint32_t hi = mf_to16<BF16>(tv);
       const float hf = BF16 ? __uint_as_float(hi << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)hi);
       const uint32_t lo = mf_to16<BF16>(tv - hf);
@@ -547,8 +574,10 @@ template <int KIND, bool BF16, int MT>
 static hipError_t launch_mfma_t(const MfArgs& a, hipStream_t st) {
   const int lds_x = (MT + 1) * mf_xrow(a.Kz);
   const int lds_t = a.r16 ? (MT + 1) * mf_trow(a.rp) : 0;
-  const int lds = lds_x > lds_t ? lds_x : lds_t;
-  hipLaunchKernelGGL((decode_mfma_kernel<KIND, BF16, MT>), dim3(a.tiles * a.S), dim3(256), lds, st, a);
+  const int lds_l = a.lr_wgs > 0 ? lr_scratch_bytes(a.lr_mode, kMfLrTile) : 0;  // prologue workgroups
+  int lds = lds_x > lds_t ? lds_x : lds_t;
+  lds = lds > lds_l ? lds : lds_l;
+  hipLaunchKernelGGL((decode_mfma_kernel<KIND, BF16, MT>), dim3(a.lr_wgs + a.tiles * a.S), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 

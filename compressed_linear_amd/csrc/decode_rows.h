@@ -69,18 +69,6 @@ struct RowArgs {
   uint32_t lr_epoch;
 };
 
-// Bounded wait of a wavefront for the published t (each poll sleeps a few
-// hundred cycles; the bound, far above any producer's run time, only keeps a
-// wavefront from waiting forever should a producer never publish).
-__device__ __forceinline__ void wait_lowrank(const uint32_t* flag, uint32_t epoch, int lane) {
-  if (lane == 0) {
-    uint32_t it = 0;
-    while (__hip_atomic_load(const_cast<uint32_t*>(flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch &&
-           ++it < (1u << 20))
-      __builtin_amdgcn_s_sleep(4);
-  }
-}
-
 // LDS bytes per chunk of staged activations: the chunk's 2 * span bytes padded
 // so that the stride in dwords is 4 * (odd number) and lanes 0..7 of a 128-bit
 // read hit 8 distinct groups of four banks.

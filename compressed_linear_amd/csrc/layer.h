@@ -61,7 +61,7 @@ struct Layer {
   float* lr_part = nullptr;      // partial sums [tiles][S][256]
   uint32_t* lr_cnt = nullptr;    // [128]: arrivals per output tile [0, 64), completed tiles [64],
                                  // published epoch [65]; counters zero between forwards
-  uint32_t lr_epoch = 0;         // forwards issued (the decode kernel's prologue publishes it)
+  mutable uint32_t lr_epoch = 0; // decode launches with a prologue inside (each publishes the next value)
 
   // matrix-core decode (batch 2..32; absent when max_M == 1)
   int mf_npw = 0, mf_Kz = 0, mf_S = 0, mf_tiles = 0;
@@ -78,11 +78,12 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L /* may 
 // Kernel launchers (kernels.hip).  All asynchronous on `stream`.
 hipError_t launch_prep_x(const Layer& L, int M, const void* x, hipStream_t stream);
 hipError_t launch_lowrank_prologue(const Layer& L, int M, const void* x, hipStream_t stream);
-// decode forward (M <= kMaxDecodeM), including the low-rank prologue: inside the
-// batch-1..4 kernel when it applies (publishing `epoch`), else as its own kernel
+// decode forward (M <= kMaxDecodeM), including the activation clamp / restaging
+// (x: the caller's activations, or L.xprep when done already) and the low-rank
+// prologue: inside the decode launch when it applies (publishing ++lr_epoch),
+// else as kernels of their own.
 // variant: 0 the faster kernel for M, 1 the vector-ALU kernels, 2 the matrix-core kernel
-hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, uint32_t epoch,
-                         int variant);
+hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, int variant);
 hipError_t launch_prefill(const Layer& L, int M, const void* x, float* y, hipStream_t stream);
 hipError_t launch_debug(const Layer& L, uint16_t* D16, uint16_t* S16, float* L32, float* R32, hipStream_t stream);
 

@@ -37,7 +37,46 @@ struct LrSplitArgs {
   uint32_t* flag;
   uint32_t epoch;
   int ntiles;
+  // clamp x to [-cval, cval] while staging it (activations not clamped beforehand)
+  int clamp;
+  float cval;
 };
+
+// Activation editor of "Compressing Large Language Models by Joint
+// Sparsification and Quantization" (Approach: one clamp value per layer),
+// applied to eight staged 16-bit activations.  +-c is exact in the activation
+// type (checked by the packer), so the clamped value is the input or +-c
+// exactly, as when the activations are clamped by a kernel of their own.
+template <bool BF16>
+__device__ __forceinline__ uint4 clamp_act8(uint4 v, float c) {
+  uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = fminf(fmaxf(__uint_as_float(u[i] << 16), -c), c);
+      const float hi = fminf(fmaxf(__uint_as_float(u[i] & 0xFFFF0000u), -c), c);
+      u[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+    }
+  } else {
+    const half2_t hc = {(_Float16)c, (_Float16)c}, lc = {(_Float16)-c, (_Float16)-c};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      u[i] = as_u32(__builtin_elementwise_min(__builtin_elementwise_max(as_h2(u[i]), lc), hc));
+  }
+  return make_uint4(u[0], u[1], u[2], u[3]);
+}
+
+// Bounded wait for the published t (each poll sleeps a few hundred cycles; the
+// bound, far above any producer's run time, only keeps a wavefront from
+// waiting forever should a producer never publish).  Lane 0 polls.
+__device__ __forceinline__ void wait_lowrank(const uint32_t* flag, uint32_t epoch, int lane) {
+  if (lane == 0) {
+    uint32_t it = 0;
+    while (__hip_atomic_load(const_cast<uint32_t*>(flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch &&
+           ++it < (1u << 20))
+      __builtin_amdgcn_s_sleep(4);
+  }
+}
 
 template <bool BF16>
 __device__ __forceinline__ float dot2_act(uint32_t a, uint32_t b, float c) {
@@ -119,6 +158,7 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
       }
     }
   }
+  if (a.clamp) xv = clamp_act8<BF16>(xv, a.cval);
   if (tid < MT * 64) *reinterpret_cast<uint4*>(&xs[tid >> 6][8 * (tid & 63)]) = xv;
   __syncthreads();
 

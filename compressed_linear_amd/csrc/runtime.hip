@@ -440,16 +440,16 @@ static cl_status forward_impl(Layer* L, int32_t M, const void* x, float* y, void
   if (path == CL_PATH_DECODE_MFMA && L->mf_S == 0)
     return fail(CL_EUNSUPPORTED, "the matrix-core decode needs a layer created with max_M >= 2");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const void* xa = x;
   hipError_t e = hipSuccess;
-  if (L->xprep) {
-    e = launch_prep_x(*L, M, x, s);
-    xa = L->xprep;
-  }
-  if (decode) {
+  if (decode) {  // the decode dispatch clamps / restages x itself (in its kernels where it can)
     const int variant = path == CL_PATH_DECODE_VALU ? 1 : path == CL_PATH_DECODE_MFMA ? 2 : 0;
-    if (e == hipSuccess) e = launch_decode(*L, M, xa, y, s, ++L->lr_epoch, variant);
+    e = launch_decode(*L, M, x, y, s, variant);
   } else {
+    const void* xa = x;
+    if (L->xprep) {
+      e = launch_prep_x(*L, M, x, s);
+      xa = L->xprep;
+    }
     if (e == hipSuccess) e = launch_prefill(*L, M, xa, y, s);
   }
   if (e != hipSuccess) return fail(CL_EHIP, "launch failed: %s", hipGetErrorString(e));

@@ -198,6 +198,9 @@ cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes, int32_t m
  *   dequantised in registers at larger M); larger M runs the prefill kernels
  *   (MFMA on dequantised LDS tiles).
  * One forward at a time per handle (the workspace inside dev_buf is shared).
+ * A layer with a low-rank part passes each decode launch a new sequence number
+ * (its workgroups publish and wait for it), so a forward recorded into a HIP
+ * graph must not be replayed for such a layer.
  * Deterministic: the same inputs give bitwise identical y.
  * Errors: CL_EINVAL (M out of range, NULL or misaligned pointers),
  * CL_EHIP (launch failure).
@@ -205,8 +208,8 @@ cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes, int32_t m
 cl_status cl_forward(void* handle, int32_t M, const void* x_dev, float* y_dev, void* stream);
 
 /* cl_forward with an explicit path (cl_path); CL_PATH_AUTO behaves as cl_forward.
- * The decode paths require M <= 32; CL_PATH_DECODE_MFMA also a layer without
- * the bitmap mask, created with max_M >= 2 (else CL_EUNSUPPORTED). */
+ * The decode paths require M <= 32; CL_PATH_DECODE_MFMA also a layer created
+ * with max_M >= 2 (else CL_EUNSUPPORTED). */
 cl_status cl_forward_path(void* handle, int32_t M, const void* x_dev, float* y_dev,
                           void* stream, int32_t path);
 
