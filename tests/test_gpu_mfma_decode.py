@@ -186,3 +186,44 @@ def test_mfma_bitmap_layers():
     layb = lay.with_(x_dtype="bf16")
     xb = bf16_bits_from_f32(r.normal(0, 1, (12, K)))
     check_bound(gpu_forward(layb, xb, path="decode_mfma"), layb, xb, what="bitmap bf16")
+
+
+def test_mfma_clamp_and_prologue_in_launch():
+    # the activation clamp applied while staging (K a multiple of 8) and by the
+    # prep kernel (odd K), with and without a rank term whose prologue runs in
+    # the same launch (it stages, and clamps, the activations too); repeated
+    # forwards with new activations on one layer (a stale t would show), and a
+    # bitmap prefill whose 32-row blocks each publish their own epoch
+    from test_gpu_parity import _with_lowrank
+    r = np.random.default_rng(77)
+    cases = []
+    for K, xdt, kind in ((1536, "f16", "int4"), (1000, "bf16", "bf16"), (1001, "f16", "fp16"), (1003, "bf16", "int4")):
+        N = 150
+        q = r.integers(-127, 128, size=(N, K)).astype(np.int8)
+        base = LogicalLayer(K=K, N=N, dense="int8", qvals=q, row_scale=r.uniform(0.001, 0.01, N).astype(np.float16),
+                            act_clamp=np.float16(1.5), x_dtype=xdt)
+        cases.append((f"int8 clamp K{K} {xdt}", base))
+        cases.append((f"int8 clamp + {kind} rank K{K} {xdt}", _with_lowrank(base, kind, 96, 128, seed=K)))
+    lut = make_layer(2, 0, K=1003, N=130).with_(act_clamp=np.float16(2.0))
+    cases.append(("lut4 clamp K1003", lut))
+    for what, lay in cases:
+        mod = gpu_layer(lay, max_M=32)
+        for M in (4, 16, 16, 32):
+            xf = r.normal(0, 1, (M, lay.K)) * np.where(r.random(lay.K) < 0.02, 30.0, 1.0)
+            x = bf16_bits_from_f32(xf) if lay.x_dtype == "bf16" else xf.astype(np.float16)
+            say("mfma", what, "M", M)
+            check_bound(gpu_forward(lay, x, path="decode_mfma", mod=mod), lay, x, what=f"{what} M={M}")
+        mod.close()
+    # bitmap + clamp + int4 rank through the prefill (blocks of 32 rows)
+    K, N = 1536, 140
+    keep = (r.random((N, K)) < 0.5).astype(np.uint8)
+    q = r.integers(-127, 128, size=(N, K)).astype(np.int8)
+    bm = LogicalLayer(K=K, N=N, dense="int8", mask="bitmap", qvals=q, keep=keep,
+                      row_scale=r.uniform(0.001, 0.01, N).astype(np.float16), act_clamp=np.float16(1.5))
+    bm_lr = _with_lowrank(bm, "int4", 128, 128, seed=5)
+    mod = gpu_layer(bm_lr, max_M=100)
+    for M in (100, 16, 70):
+        x = (r.normal(0, 1, (M, K)) * np.where(r.random(K) < 0.01, 30.0, 1.0)).astype(np.float16)
+        say("bitmap clamp rank M", M)
+        check_bound(gpu_forward(bm_lr, x, mod=mod), bm_lr, x, what=f"bitmap clamp rank M={M}")
+    mod.close()
