@@ -74,6 +74,9 @@ inline int pf_step_k(int dense, int mask) {
   return 64;
 }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+// Weight rows per prefill tile: the 3-bit LUT format runs the wide kernel
+// (256-row tiles, outlier entries with an 8-bit row), the others 128.
+inline int pf_tile_rows(int dense) { return dense == 0 ? 256 : kPfTileN; }
 
 // Matrix-core decode (batch 2..32): 128-row tiles, split along K into slices
 // of whole passes (a pass is eight chunks of every row of the tile).

@@ -14,6 +14,7 @@ extern template hipError_t launch_prefill_kind<K_INT4>(const PfArgs&, bool, hipS
 extern template hipError_t launch_prefill_kind<K_INT4_24>(const PfArgs&, bool, hipStream_t);
 extern template hipError_t launch_prefill_kind<K_INT8>(const PfArgs&, bool, hipStream_t);
 extern template hipError_t launch_prefill_kind<K_DENSE16>(const PfArgs&, bool, hipStream_t);
+hipError_t launch_prefill_wide(const PfArgs& a, bool bf16, hipStream_t stream);  // the 3-bit LUT format
 
 // t_hi | t_lo of t = the sum of the prologue's K-split partials, added in a
 // fixed order: [M][2 rp], t_hi = t rounded to the MFMA type, t_lo = the rest.
@@ -113,6 +114,7 @@ hipError_t launch_prefill(const Layer& L, int M, const void* x, float* y, hipStr
     constexpr int KIND = decltype(kind_tag)::value;
     a.nsteps = a.nsteps_dense + (has_lr ? (int)ceil_div(2 * rp, PfCfg<KIND>::bk) : 0);
     a.steps_per_split = a.nsteps;
+    if constexpr (KIND == K_LUT3) return launch_prefill_wide(a, bf16, stream);
     return launch_prefill_kind<KIND>(a, bf16, stream);
   };
   switch (h.dense) {

@@ -77,7 +77,7 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
     const int cps = pf_step_k(h.dense, h.mask) / kind_info(h.dense, h.mask).span;
     pf_nd = (int)ceil_div(h.chunks, cps);
     if (h.nnz > 0) {
-      o_pfp = take((size_t)ceil_div(Npad, kPfTileN) * (pf_nd + 1) * 4);
+      o_pfp = take((size_t)ceil_div(Npad, pf_tile_rows(h.dense)) * (pf_nd + 1) * 4);
       o_pfe = take((size_t)h.nnz * 4);
     }
     if (has_lr) {
@@ -177,14 +177,15 @@ static void build_prefill_host(const cl_blob_header& h, const uint8_t* b, int Np
   const bool bf = h.x_dtype == CL_ACT_BF16;
   auto to16 = [&](float f) { return bf ? f2bf(f) : f2h(f); };
   if (h.nnz > 0 && !r16_only) {
-    const int bk = pf_step_k(h.dense, h.mask), nt = (int)ceil_div(Npad, kPfTileN);
+    const int bk = pf_step_k(h.dense, h.mask), tr = pf_tile_rows(h.dense), nt = (int)ceil_div(Npad, tr);
+    const int rbits = tr == 256 ? 8 : 7;  // entry: row in tile | k in step << rbits | fp16 value << 16
     const int32_t* rp_ = reinterpret_cast<const int32_t*>(b + h.off[CL_SEC_ROWPTR]);
     const int32_t* col = reinterpret_cast<const int32_t*>(b + h.off[CL_SEC_COL]);
     const uint16_t* val = reinterpret_cast<const uint16_t*>(b + h.off[CL_SEC_VAL]);
     out.cptr.assign((size_t)nt * (nd + 1), 0);
     std::vector<int32_t> cnt((size_t)nt * nd, 0);
     for (int n = 0; n < h.N; ++n)
-      for (int p = rp_[n]; p < rp_[n + 1]; ++p) ++cnt[(size_t)(n / kPfTileN) * nd + col[p] / bk];
+      for (int p = rp_[n]; p < rp_[n + 1]; ++p) ++cnt[(size_t)(n / tr) * nd + col[p] / bk];
     int32_t acc = 0;
     for (int t = 0; t < nt; ++t) {
       for (int s = 0; s < nd; ++s) {
@@ -200,8 +201,8 @@ static void build_prefill_host(const cl_blob_header& h, const uint8_t* b, int Np
     for (int n = 0; n < h.N; ++n)
       for (int p = rp_[n]; p < rp_[n + 1]; ++p) {
         const int s = col[p] / bk;
-        out.cent[fill[(size_t)(n / kPfTileN) * nd + s]++] =
-            (uint32_t)(n % kPfTileN) | ((uint32_t)(col[p] - s * bk) << 7) | ((uint32_t)val[p] << 16);
+        out.cent[fill[(size_t)(n / tr) * nd + s]++] =
+            (uint32_t)(n % tr) | ((uint32_t)(col[p] - s * bk) << rbits) | ((uint32_t)val[p] << 16);
       }
   }
   if (h.lr != CL_LR_NONE && h.rank > 0) {
