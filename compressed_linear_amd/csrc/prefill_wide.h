@@ -136,24 +136,29 @@ __global__ void __launch_bounds__(512, 1) prefill_wide_kernel(PfArgs a) {
 
   const brsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.ldx * 2u);
   const brsrc_t rd = make_rsrc(a.dense, (uint32_t)a.Npad * (uint32_t)a.chunks * 16u);
-  const brsrc_t rc = make_rsrc(a.cent, has_csr ? (uint32_t)s_cptr[nd] * 4u : 0u);
+  // (the size read back from LDS is uniform; readfirstlane keeps the descriptor
+  // in scalar registers, without a waterfall loop around every load through it)
+  const brsrc_t rc = make_rsrc(a.cent, has_csr ? (uint32_t)__builtin_amdgcn_readfirstlane(s_cptr[nd]) * 4u : 0u);
   const uint32_t wrow = (uint32_t)n * (uint32_t)a.chunks;
   // activation units of this thread (u = tid + 512 i of the 128 x 10 units of a
   // step): element offset of the unit at step 0, k in step, LDS byte offset.
   // Threads past the 1280 units store zeros into the unused 11th unit of a
   // weight-tile row instead, so the staging has no branch.
+  // xend: the unit is loaded at steps s < xend (inside the dense steps and below ldx)
   uint32_t xoff[kPwAU], xlds[kPwAU];
-  int xk[kPwAU];
-  bool xin[kPwAU];
+  int xend[kPwAU];
 #pragma unroll
   for (int i = 0; i < kPwAU; ++i) {
     const int u = tid + 512 * i;
-    xin[i] = u < kPwBM * 10;
-    const int row = xin[i] ? u / 10 : 0, kk = xin[i] ? u - row * 10 : 0;
-    xk[i] = 8 * kk;
-    xoff[i] = (uint32_t)(m0 + row) * (uint32_t)a.ldx + (uint32_t)(8 * kk);
-    xlds[i] = xin[i] ? (uint32_t)(row * kPwRS + kk * 16) : (uint32_t)(kPwTA + (u - kPwBM * 10) * kPwRS + 160);
+    const bool in = u < kPwBM * 10;
+    const int row = in ? u / 10 : 0, kk = in ? u - row * 10 : 0;
+    const int e = (a.ldx - 8 * kk + kPwBK - 1) / kPwBK;
+    xend[i] = in ? (e < nd ? e : nd) : 0;
+    xoff[i] = ((uint32_t)(m0 + row) * (uint32_t)a.ldx + (uint32_t)(8 * kk)) * 2u;
+    xlds[i] = in ? (uint32_t)(row * kPwRS + kk * 16) : (uint32_t)(kPwTA + (u - kPwBM * 10) * kPwRS + 160);
   }
+  // the code chunk 2 s + shalf exists for steps s < cend
+  const int cend = (a.chunks - shalf + 1) / 2 < nd ? (a.chunks - shalf + 1) / 2 : nd;
 
   struct Stage {
     uint4 xa[kPwAU];
@@ -166,12 +171,9 @@ __global__ void __launch_bounds__(512, 1) prefill_wide_kernel(PfArgs a) {
   // the stage it consumes while the younger stages stay in flight.
   auto load_step = [&](Stage& st, int s, bool valid) {
 #pragma unroll
-    for (int i = 0; i < kPwAU; ++i) {
-      const bool ok = valid && xin[i] && s * kPwBK + xk[i] < a.ldx;
-      st.xa[i] = bload128(rx, ok ? (xoff[i] + (uint32_t)(s * kPwBK)) * 2u : kNoLoad, 0);
-    }
-    const int c = 2 * s + shalf;
-    st.wb = bload128(rd, valid && c < a.chunks ? (wrow + (uint32_t)c) * 16u : kNoLoad, 0);
+    for (int i = 0; i < kPwAU; ++i)
+      st.xa[i] = bload128(rx, s < xend[i] ? xoff[i] + (uint32_t)(s * kPwBK * 2) : kNoLoad, 0);
+    st.wb = bload128(rd, s < cend ? (wrow + (uint32_t)(2 * s + shalf)) * 16u : kNoLoad, 0);
     const int sc = valid ? s : 0;
     const int e0 = has_csr ? s_cptr[sc] : 0, cnt = has_csr ? s_cptr[sc + 1] - e0 : 0;
     st.ce_ok = has_csr && valid && tid < cnt;

@@ -53,20 +53,26 @@ def test_prefill_plain_integer_formats():
         check_bound(gpu_forward(layb, xb, path="prefill"), layb, xb, what=dense + " bf16")
 
 
-def test_prefill_outlier_stress():
+@pytest.mark.parametrize("cfg", [2, 1])
+def test_prefill_outlier_stress(cfg):
+    # cfg 2: the 128 x 128 kernel (4-bit LUT); cfg 1: the wide 3-bit LUT kernel.
+    # Full rows make per-(tile, K step) lists far longer than one entry per thread.
     r = np.random.default_rng(23)
     K, N = 900, 300
     rp, col, val = draw_csr_skewed(r, r, N, K, density=0.01)
-    base = make_layer(2, 0, K=K, N=N)
+    base = make_layer(cfg, 0, K=K, N=N)
     lay = base.with_(csr_row_ptr=rp, csr_col=col, csr_val=val)
-    x = make_x(2, 0, 70, K=K)
-    say("prefill skewed csr")
+    x = make_x(cfg, 0, 70, K=K)
+    say("prefill skewed csr", cfg)
     check_bound(gpu_forward(lay, x, path="prefill"), lay, x, what="skewed csr")
     # rows holding every column as an outlier
     rp2 = np.zeros(N + 1, np.int32); rp2[6:] = K; rp2[200:] = 2 * K
     cols = np.concatenate([np.arange(K), np.arange(K)]).astype(np.int32)
     lay2 = base.with_(csr_row_ptr=rp2, csr_col=cols, csr_val=r.normal(0, 0.2, 2 * K).astype(np.float16))
     check_bound(gpu_forward(lay2, x, path="prefill"), lay2, x, what="full rows csr")
+    xb = bf16_bits_from_f32(r.normal(0, 1, (130, K)))
+    lay3 = lay2.with_(x_dtype="bf16")
+    check_bound(gpu_forward(lay3, xb, path="prefill"), lay3, xb, what="full rows csr bf16")
 
 
 def test_prefill_rank_and_clamp():
