@@ -68,7 +68,7 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
   if (h.has_clamp || (h.K & 7)) o_xp = take((size_t)max_M * Kx * 2);
   // matrix-core prefill (all formats but the bitmap): outlier lists per
   // (128-row tile, K step), R^T twice and L^T in the MFMA input type, t_hi | t_lo;
-  // R^T twice also for a bitmap layer that the matrix-core decode may run (max_M >= 2)
+  // R^T twice also for a bitmap layer (its decode runs on the matrix-core kernel)
   size_t o_pfp = 0, o_pfe = 0, o_pfr = 0, o_pfl = 0, o_pft = 0;
   int pf_nd = 0;
   const int rp = (int)round_up(h.rank, 8);
@@ -85,13 +85,14 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
       o_pfl = take((size_t)h.rank * Kx * 2);
       o_pft = take((size_t)max_M * 2 * rp * 2);
     }
-  } else if (has_lr && max_M >= 2) {
+  } else if (has_lr) {
     o_pfr = take((size_t)Npad * 2 * rp * 2);
   }
   // matrix-core decode: slice partial sums, outlier lists per (slice, tile, row)
   size_t o_mfp = 0, o_mfo = 0, o_mfe = 0, o_mfz = 0;
   int mf_npw = 0, mf_Kz = 0, mf_S = 0, mf_tiles = 0;
-  if (max_M >= 2) {
+  // (bitmap layers at any max_M: the kernel is their decode path at every batch)
+  if (max_M >= 2 || h.mask == CL_MASK_BITMAP) {
     mf_npw = mf_passes(h.dense, h.mask, h.K, h.N);
     mf_Kz = mf_npw * mf_pass_k(h.dense, h.mask);
     mf_tiles = (int)ceil_div(h.N, kMfRows);
@@ -439,7 +440,7 @@ static cl_status forward_impl(Layer* L, int32_t M, const void* x, float* y, void
   const bool decode = path != CL_PATH_PREFILL;
   if (decode && M > kMaxDecodeM) return fail(CL_EINVAL, "the decode path takes M <= %d", kMaxDecodeM);
   if (path == CL_PATH_DECODE_MFMA && L->mf_S == 0)
-    return fail(CL_EUNSUPPORTED, "the matrix-core decode needs a layer created with max_M >= 2");
+    return fail(CL_EUNSUPPORTED, "the matrix-core decode needs a bitmap layer or one created with max_M >= 2");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (decode) {  // the decode dispatch clamps / restages x itself (in its kernels where it can)

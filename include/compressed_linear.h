@@ -208,8 +208,8 @@ cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes, int32_t m
 cl_status cl_forward(void* handle, int32_t M, const void* x_dev, float* y_dev, void* stream);
 
 /* cl_forward with an explicit path (cl_path); CL_PATH_AUTO behaves as cl_forward.
- * The decode paths require M <= 32; CL_PATH_DECODE_MFMA also a layer created
- * with max_M >= 2 (else CL_EUNSUPPORTED). */
+ * The decode paths require M <= 32; CL_PATH_DECODE_MFMA also a bitmap layer or
+ * one created with max_M >= 2 (else CL_EUNSUPPORTED). */
 cl_status cl_forward_path(void* handle, int32_t M, const void* x_dev, float* y_dev,
                           void* stream, int32_t path);
 

@@ -44,7 +44,7 @@ def test_mfma_decode_configs(cfg):
     mod.close()
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_valu_decode_forced(cfg):
     K, N = SHAPES[cfg]
     layer = make_layer(cfg, 0, K=K, N=N)
@@ -146,6 +146,19 @@ def test_mfma_deterministic_split_k():
     y2 = mod.forward(xd, path="decode_mfma").cpu().numpy()
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
     check_bound(y1.astype(np.float64), layer, x, what="split-K")
+    mod.close()
+
+
+def test_bitmap_layer_for_batch_1():
+    # a bitmap layer created for batch 1 still decodes on the matrix-core kernel
+    K, N = SHAPES[4]
+    layer = make_layer(4, 0, K=K, N=N, M_for_clamp=1)
+    mod = gpu_layer(layer, max_M=1)
+    x = make_x(4, 0, 1, K=K)
+    say("bitmap max_M 1")
+    check_bound(gpu_forward(layer, x, mod=mod), layer, x, what="bitmap max_M=1 auto")
+    check_bound(gpu_forward(layer, x, path="decode_mfma", mod=mod), layer, x, what="bitmap max_M=1 mfma")
+    check_bound(gpu_forward(layer, x, path="decode_valu", mod=mod), layer, x, what="bitmap max_M=1 tile kernel")
     mod.close()
 
 
