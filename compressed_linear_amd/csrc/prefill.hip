@@ -8,7 +8,6 @@
 
 namespace cl {
 
-extern template hipError_t launch_prefill_kind<K_LUT3>(const PfArgs&, bool, hipStream_t);
 extern template hipError_t launch_prefill_kind<K_LUT4>(const PfArgs&, bool, hipStream_t);
 extern template hipError_t launch_prefill_kind<K_INT4>(const PfArgs&, bool, hipStream_t);
 extern template hipError_t launch_prefill_kind<K_INT4_24>(const PfArgs&, bool, hipStream_t);
@@ -115,7 +114,7 @@ hipError_t launch_prefill(const Layer& L, int M, const void* x, float* y, hipStr
     a.nsteps = a.nsteps_dense + (has_lr ? (int)ceil_div(2 * rp, PfCfg<KIND>::bk) : 0);
     a.steps_per_split = a.nsteps;
     if constexpr (KIND == K_LUT3) return launch_prefill_wide(a, bf16, stream);
-    return launch_prefill_kind<KIND>(a, bf16, stream);
+    else return launch_prefill_kind<KIND>(a, bf16, stream);
   };
   switch (h.dense) {
     case CL_DENSE_LUT3: return run(std::integral_constant<int, K_LUT3>{});

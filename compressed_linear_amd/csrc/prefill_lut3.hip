@@ -1,10 +1,7 @@
-// prefill_lut3.hip -- matrix-core prefill kernels for one weight format.
-#include "prefill_impl.h"
+// prefill_lut3.hip -- matrix-core prefill for the 3-bit LUT format.
 #include "prefill_wide.h"
 
 namespace cl {
-template hipError_t launch_prefill_kind<K_LUT3>(const PfArgs&, bool, hipStream_t);
-
 // The wide kernel (256 weight rows x 128 activation rows per workgroup).
 hipError_t launch_prefill_wide(const PfArgs& a, bool bf16, hipStream_t st) {
   if (a.cptr && a.nsteps_dense > kPfMaxSteps) return hipErrorInvalidValue;
