@@ -19,10 +19,12 @@
 // lane half 0 and span*(c0 + 4 + q) + 8j..+7 on half 1; the activation operand
 // is read from LDS at the same k, so the sum is unchanged.
 //
-// The LUT tables are lane-interleaved single-entry tables (entry e of lane l
+// 4-bit LUT tables are lane-interleaved single-entry tables (entry e of lane l
 // at byte e*256 + 4l), one stacked set per wavefront, holding the values in the
-// MFMA input type: every lookup is conflict-free.  The activation slice
-// x'[0..M)[k0, k0+Kz) is staged once per workgroup in LDS.
+// MFMA input type: every lookup is conflict-free.  3-bit LUT values stay in
+// registers as byte tables and the codes are turned into values with byte
+// permutes (no lookups).  The activation slice x'[0..M)[k0, k0+Kz) is staged
+// once per workgroup in LDS.
 //
 // Outliers ("SqueezeLLM: Dense-and-Sparse Quantization", Approach: W = D + S)
 // of the tile's rows inside the K slice come as per-(tile, slice, row) lists
@@ -123,23 +125,6 @@ __device__ __forceinline__ uint32_t lds_pair16(const uint32_t* lds, uint32_t a_l
   return as_u32(r);
 }
 
-// 3-bit LUT word through lane-interleaved single-entry tables (entry e of lane
-// l at e*256 + 4l, value in the low half): the ten codes of the word
-// (byte j bits 2..4 = code 2j, bits 5..7 = code 2j+1 for j < 4; the fifth pair
-// gathered by lut3_p4x4 into byte 2) become five pairs.  `b` = entry bias in
-// every byte (the wavefront's table set).
-__device__ __forceinline__ void lut3_word_single(const uint32_t* lds, uint32_t w, uint32_t lanebase, uint32_t out[5],
-                                                 uint32_t b, uint32_t m7, uint32_t m7b2) {
-  const uint32_t ev = ((w >> 2) & m7) | b, od = ((w >> 5) & m7) | b;
-  const uint32_t p4 = lut3_p4x4(w);
-  const uint32_t e4 = ((p4 >> 2) & m7b2) | b, o4 = ((p4 >> 5) & m7b2) | b;
-  out[0] = lds_pair16(lds, addr_from_byte<0>(ev, lanebase), addr_from_byte<0>(od, lanebase));
-  out[1] = lds_pair16(lds, addr_from_byte<1>(ev, lanebase), addr_from_byte<1>(od, lanebase));
-  out[2] = lds_pair16(lds, addr_from_byte<2>(ev, lanebase), addr_from_byte<2>(od, lanebase));
-  out[3] = lds_pair16(lds, addr_from_byte<3>(ev, lanebase), addr_from_byte<3>(od, lanebase));
-  out[4] = lds_pair16(lds, addr_from_byte<2>(e4, lanebase), addr_from_byte<2>(o4, lanebase));
-}
-
 // 4-bit LUT word (device byte order: the pair (c_2b, c_2b+1) rotated left by
 // two bits in byte b) through lane-interleaved single-entry tables: four pairs.
 __device__ __forceinline__ void lut4_word_single(const uint32_t* lds, uint32_t w, uint32_t lanebase, uint32_t out[4],
@@ -152,8 +137,11 @@ __device__ __forceinline__ void lut4_word_single(const uint32_t* lds, uint32_t w
   out[3] = lds_pair16(lds, addr_from_byte<3>(ev, lanebase), addr_from_byte<3>(od, lanebase));
 }
 
-// MT = activation rows staged.  LUT formats use lane-interleaved single-entry
-// tables: one lookup per weight, but conflict-free.  (Per-row pair tables, one
+// MT = activation rows staged.  The 4-bit LUT uses lane-interleaved
+// single-entry tables: one lookup per weight, but conflict-free.  (3-bit LUT
+// single-entry lookups, with an address permute per value and a permute per
+// pair, cost more vector issue than byte permutes over the values held in
+// registers, and they were replaced by those.  Per-row pair tables, one
 // lookup per two weights, measured slower here: the 32 rows of a wavefront
 // look up different tables, and their bank conflicts cost more than the
 // lookups they save.)
@@ -169,7 +157,7 @@ struct MfCfg {
   static constexpr int span = KindTraits<KIND>::span, pairs = KindTraits<KIND>::pairs;
   static constexpr int cph = KIND == K_INT8_BM ? 1 : kMfCph;  // chunks per lane half per pass
   static constexpr int passk = 2 * cph * span;                // k per pass
-  static constexpr int ents = KIND == K_LUT3 ? 8 : KIND == K_LUT4 ? 16 : 0;  // table entries per row
+  static constexpr int ents = KIND == K_LUT4 ? 16 : 0;  // LDS table entries per row (LUT3: values in registers)
   // static LDS at address 0: four stacked lane-interleaved single-entry table
   // sets, the 2:4 selectors, or the bitmap's nibble selectors and lane slots
   static constexpr int tab_bytes = ents ? 4 * ents * 256
@@ -194,7 +182,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   // outputs v of a lane whose activation row m(v) = 8 (v / 4) + 4 half + v mod 4 is below MT
   constexpr int NV = MT >= 32 ? 16 : MT / 2;
   constexpr int XR = MT * kMfKzMax / 8 / 256;  // 16-byte activation slots per thread
-  constexpr bool LUT = C::ents > 0;
+  constexpr bool LUT = KIND == K_LUT3 || KIND == K_LUT4;
   __shared__ __attribute__((aligned(16))) uint32_t stab[C::tab_bytes / 4];  // at LDS address 0
   extern __shared__ __attribute__((aligned(16))) uint32_t sdyn[];          // activation slice, then t
 
@@ -314,7 +302,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   auto lut_val = [&](uint32_t h) -> uint32_t {
     return BF16 ? mf_to16<true>((float)__builtin_bit_cast(_Float16, (uint16_t)h)) : h;
   };
-  if constexpr (LUT) {
+  if constexpr (KIND == K_LUT4) {
     const uint32_t lw[8] = {tv0.x, tv0.y, tv0.z, tv0.w, tv1.x, tv1.y, tv1.z, tv1.w};
 #pragma unroll
     for (int e = 0; e < C::ents; ++e) {
@@ -339,9 +327,14 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   const int mrow = lane & 31;  // activation row of this lane's A operand
   // mask constants in VGPRs and the table-set bias in every byte
   const uint32_t bias4 = ebias * 0x01010101u;
-  const uint32_t mk0 = vconst(KIND == K_LUT3 ? 0x07070707u : 0x0F0F0F0Fu);
-  const uint32_t mk1 = vconst(KIND == K_LUT3 ? 0x00070000u : 0x03030303u);
-  const uint32_t mk2 = vconst(0x0C0C0C0Cu);
+  Lut3Bytes T3 = {0, 0, 0, 0};  // LUT3: the row's values as byte tables in registers
+  if constexpr (KIND == K_LUT3) T3 = lut3_bytes<BF16>(tv0);
+  uint32_t mk0 = 0, mk1 = 0, mk2 = 0;
+  if constexpr (KIND == K_LUT4) {
+    mk0 = vconst(0x0F0F0F0Fu);
+    mk1 = vconst(0x03030303u);
+    mk2 = vconst(0x0C0C0C0Cu);
+  }
   const int mrow_s = mrow < MT ? mrow : MT;  // rows past MT read the zero row
   const uint8_t* xr = sb + mrow_s * xrow + half * CPH * SPAN * 2;
   if constexpr (BM) {
@@ -423,7 +416,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
       const uint32_t ww[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
       if constexpr (KIND == K_LUT3) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lut3_word_single(stab, ww[i], lanebase, &wp[5 * i], bias4, mk0, mk1);
+        for (int i = 0; i < 4; ++i) lut3_word_perm(ww[i], T3, &wp[5 * i]);
       } else if constexpr (KIND == K_LUT4) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) lut4_word_single(stab, ww[i], lanebase, &wp[4 * i], bias4, mk0, mk1, mk2);

@@ -46,32 +46,6 @@ constexpr int kPwLds = kPwBuf + 2 * kPwStage;
 constexpr int kPwAU = 3;                             // activation units per thread per step (1280 units)
 static_assert(kPwLds <= 160 * 1024, "LDS budget");
 
-// The 8 values of a row in the MFMA type, as byte tables for v_perm: low bytes
-// of values 0..3 / 4..7 and high bytes of values 0..3 / 4..7.
-struct PwTab {
-  uint32_t l0, l1, h0, h1;
-};
-
-// Ten 3-bit codes of a device word (byte j < 4: bits 2..4 code 2j, bits 5..7
-// code 2j + 1; the fifth pair from the low two bits of bytes 0..2) into five
-// pairs of values: each byte of a selector word picks one value's low (or
-// high) byte from the row's tables.
-__device__ __forceinline__ void pw_lut3_word(uint32_t w, const PwTab& T, uint32_t out[5]) {
-  const uint32_t ev = (w >> 2) & 0x07070707u, od = (w >> 5) & 0x07070707u;
-  const uint32_t loE = perm(T.l1, T.l0, ev), hiE = perm(T.h1, T.h0, ev);
-  const uint32_t loO = perm(T.l1, T.l0, od), hiO = perm(T.h1, T.h0, od);
-  const uint32_t e01 = perm(hiE, loE, 0x05010400u), e23 = perm(hiE, loE, 0x07030602u);
-  const uint32_t o01 = perm(hiO, loO, 0x05010400u), o23 = perm(hiO, loO, 0x07030602u);
-  out[0] = perm(o01, e01, 0x05040100u);
-  out[1] = perm(o01, e01, 0x07060302u);
-  out[2] = perm(o23, e23, 0x05040100u);
-  out[3] = perm(o23, e23, 0x07060302u);
-  const uint32_t p = lut3_p4x4(w) >> 18;  // code 8 in bits 0..2, code 9 in bits 3..5
-  const uint32_t s = (p & 7u) | ((p & 0x38u) << 5);
-  const uint32_t lo = perm(T.l1, T.l0, s), hi = perm(T.h1, T.h0, s);
-  out[4] = perm(hi, lo, 0x05010400u);
-}
-
 // One outlier entry (row | k << 8 | fp16 value << 16) into the weight tile at
 // byte offset btile, packed atomic add on the dword holding it.
 template <bool BF16>
@@ -117,21 +91,8 @@ __global__ void __launch_bounds__(512, 1) prefill_wide_kernel(PfArgs a) {
   // rows of one half, so its 16-byte LDS stores hit distinct bank groups), and
   // the row's values as byte tables
   const int srow = (tid & 63) + 64 * (tid >> 7), shalf = (tid >> 6) & 1, n = n0 + srow;
-  PwTab T;
-  {
-    const uint4 lv = n < a.Npad ? reinterpret_cast<const uint4*>(a.table)[n] : make_uint4(0, 0, 0, 0);
-    const uint32_t lw[4] = {lv.x, lv.y, lv.z, lv.w};
-    uint32_t v16[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t h = (lw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      v16[e] = BF16 ? to16<true>((float)__builtin_bit_cast(_Float16, (uint16_t)h)) : h;
-    }
-    T.l0 = (v16[0] & 0xFF) | (v16[1] & 0xFF) << 8 | (v16[2] & 0xFF) << 16 | (v16[3] & 0xFF) << 24;
-    T.l1 = (v16[4] & 0xFF) | (v16[5] & 0xFF) << 8 | (v16[6] & 0xFF) << 16 | (v16[7] & 0xFF) << 24;
-    T.h0 = (v16[0] >> 8) | (v16[1] >> 8) << 8 | (v16[2] >> 8) << 16 | (v16[3] >> 8) << 24;
-    T.h1 = (v16[4] >> 8) | (v16[5] >> 8) << 8 | (v16[6] >> 8) << 16 | (v16[7] >> 8) << 24;
-  }
+  const Lut3Bytes T =
+      lut3_bytes<BF16>(n < a.Npad ? reinterpret_cast<const uint4*>(a.table)[n] : make_uint4(0, 0, 0, 0));
   __syncthreads();
 
   const brsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.ldx * 2u);
@@ -186,7 +147,7 @@ __global__ void __launch_bounds__(512, 1) prefill_wide_kernel(PfArgs a) {
     uint32_t wp[20];
     const uint32_t ww[4] = {st.wb.x, st.wb.y, st.wb.z, st.wb.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pw_lut3_word(ww[i], T, &wp[5 * i]);
+    for (int i = 0; i < 4; ++i) lut3_word_perm(ww[i], T, &wp[5 * i]);
     uint8_t* brow = bo + kPwTA + srow * kPwRS + shalf * 80;
 #pragma unroll
     for (int j = 0; j < 5; ++j)

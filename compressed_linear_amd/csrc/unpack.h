@@ -117,6 +117,52 @@ __device__ __forceinline__ void lut3_word(const uint32_t* lds, uint32_t w, uint3
   out[4] = lds_u32(lds, addr_from_byte<2>(p4, lanebase));
 }
 
+// 3-bit LUT dequantisation without table lookups: the 8 values of a row in the
+// MFMA input type, as byte tables for v_perm (low bytes of values 0..3 / 4..7,
+// high bytes of values 0..3 / 4..7), held in registers.
+struct Lut3Bytes {
+  uint32_t l0, l1, h0, h1;
+};
+
+// The row's 8 fp16 LUT values (one 16-byte load) as byte tables, rounded to
+// nearest-even bf16 first when the MFMAs run in bf16.
+template <bool BF16>
+__device__ __forceinline__ Lut3Bytes lut3_bytes(uint4 lv) {
+  const uint32_t lw[4] = {lv.x, lv.y, lv.z, lv.w};
+  uint32_t v16[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t h = (lw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    v16[e] = BF16 ? (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(float)__builtin_bit_cast(_Float16, (uint16_t)h)) : h;
+  }
+  Lut3Bytes T;
+  T.l0 = (v16[0] & 0xFF) | (v16[1] & 0xFF) << 8 | (v16[2] & 0xFF) << 16 | (v16[3] & 0xFF) << 24;
+  T.l1 = (v16[4] & 0xFF) | (v16[5] & 0xFF) << 8 | (v16[6] & 0xFF) << 16 | (v16[7] & 0xFF) << 24;
+  T.h0 = (v16[0] >> 8) | (v16[1] >> 8) << 8 | (v16[2] >> 8) << 16 | (v16[3] >> 8) << 24;
+  T.h1 = (v16[4] >> 8) | (v16[5] >> 8) << 8 | (v16[6] >> 8) << 16 | (v16[7] >> 8) << 24;
+  return T;
+}
+
+// Ten 3-bit codes of a device word (byte j < 4: bits 2..4 code 2j, bits 5..7
+// code 2j + 1; the fifth pair from the low two bits of bytes 0..2) into five
+// pairs of values: each byte of a selector word picks one value's low (or
+// high) byte from the row's tables (about 2.4 vector instructions per weight).
+__device__ __forceinline__ void lut3_word_perm(uint32_t w, const Lut3Bytes& T, uint32_t out[5]) {
+  const uint32_t ev = (w >> 2) & 0x07070707u, od = (w >> 5) & 0x07070707u;
+  const uint32_t loE = perm(T.l1, T.l0, ev), hiE = perm(T.h1, T.h0, ev);
+  const uint32_t loO = perm(T.l1, T.l0, od), hiO = perm(T.h1, T.h0, od);
+  const uint32_t e01 = perm(hiE, loE, 0x05010400u), e23 = perm(hiE, loE, 0x07030602u);
+  const uint32_t o01 = perm(hiO, loO, 0x05010400u), o23 = perm(hiO, loO, 0x07030602u);
+  out[0] = perm(o01, e01, 0x05040100u);
+  out[1] = perm(o01, e01, 0x07060302u);
+  out[2] = perm(o23, e23, 0x05040100u);
+  out[3] = perm(o23, e23, 0x07060302u);
+  const uint32_t p = lut3_p4x4(w) >> 18;  // code 8 in bits 0..2, code 9 in bits 3..5
+  const uint32_t s = (p & 7u) | ((p & 0x38u) << 5);
+  const uint32_t lo = perm(T.l1, T.l0, s), hi = perm(T.h1, T.h0, s);
+  out[4] = perm(hi, lo, 0x05010400u);
+}
+
 // Row table (entry e of the row at rowbase + 4*e, rowbase a multiple of 256):
 // the byte 4 * p goes straight into address byte 0.
 __device__ __forceinline__ void lut3_word_row(const uint32_t* lds, uint32_t w, uint32_t rowbase, uint32_t out[5]) {
