@@ -2,6 +2,7 @@
 from .compressed_linear_oracle import (  # noqa: F401
     TOL_REL,
     activations,
+    round_to_act,
     dense_plane,
     sparse_plane,
     lowrank_factors,

@@ -9,6 +9,8 @@ holds none of the forward's arithmetic.
 What it computes is a plain definition, written out in fp64:
 
     x'      = clamp(x, -c, c) if the layer carries a clamp c, else x
+    x'[:,k] = rnd(x'[:,k] * f_k) on the scaled channels k, if any, where
+              f_k = 1/alpha_k and rnd rounds to the activation type
     W_hat   = D + S + (L_hat R_hat)^T                       [N, K]
     y       = x' W_hat^T                                     [M, N]
     bound   = 1e-3 * |x'| |W_hat|^T                          (elementwise)
@@ -36,12 +38,21 @@ Sources, by page (title, then section):
   * "Compressing Large Language Models by Joint Sparsification and
     Quantization" -- Approach: unstructured sparsity combined with
     quantization; activation outliers clamped with one per-layer strength.
+  * SLiM page, rebuttal section "Output Error Minimization in SLiM-Quant":
+    the weights of about 1 % of the input channels (the most salient) are
+    scaled up by a factor alpha and the matching activations are scaled
+    down by the same factor while the layer runs.
 
 Readings where the pages are silent (each one also listed with the design
 notes): W_hat is [N, K] with rows = output channels, so "per row" LUTs and
 scales belong to an output channel; D and S add (an outlier position keeps
 its dense code as well); the clamp is symmetric, |x'| <= c; the int4 AbsMax
-groups run along each factor's contraction axis; the output is fp32.
+groups run along each factor's contraction axis; the output is fp32.  For
+the channel scaling: the stored weights already carry alpha, the layer
+stores the activation factor f = 1/alpha per scaled channel in fp16, the
+clamp (when both are present) comes first, and a scaled activation is an
+activation again, so x * f is rounded once, to nearest-even, to the
+activation type (fp16 or bf16).
 
 Parity status: every function below is pinned by CPU tests (hand-derived
 closed forms, invariants, library-routine cross-checks, brute force); see
@@ -70,6 +81,24 @@ def _act_to_f64(x, x_dtype: str) -> np.ndarray:
     return np.asarray(x, dtype=np.float16).astype(np.float64)
 
 
+# significand bits (with the leading one) and smallest normal exponent
+_ACT_FORMATS = {"f16": (11, -14), "bf16": (8, -126)}
+
+
+def round_to_act(v, x_dtype: str) -> np.ndarray:
+    """Round fp64 values to the nearest value of the activation type, ties to
+    even, from the definition of a binary floating-point format with p
+    significand bits: the spacing of the values near v is 2^(e - p + 1), with
+    e the exponent of v (not below the smallest normal one, which gives the
+    subnormals).  Values are assumed inside the type's finite range."""
+    p, emin = _ACT_FORMATS[x_dtype]
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)                  # v = m 2^e, 0.5 <= |m| < 1: exponent e - 1
+    e = np.maximum(e - 1, emin)
+    spacing = np.ldexp(1.0, e - (p - 1))
+    return np.rint(v / spacing) * spacing  # exact: a power-of-two rescale, then rint (ties to even)
+
+
 # ---------------------------------------------------------------------------
 # step 1: activation clamp
 # ---------------------------------------------------------------------------
@@ -80,6 +109,8 @@ def activations(layer, x) -> np.ndarray:
     JSQ page, Approach: an activation editor clamps activation outliers with
     a per-layer strength.  Reading: one value c per layer, applied
     symmetrically, x' = min(max(x, -c), c); no clamp when the layer has none.
+    Then the channel scaling of SLiM's output-error variant, if the layer
+    has scaled channels (see the module docstring for its reading).
     """
     xf = _act_to_f64(x, layer.x_dtype)
     if xf.ndim == 1:
@@ -88,6 +119,16 @@ def activations(layer, x) -> np.ndarray:
     if c is not None:
         cf = float(np.float16(c))
         xf = np.minimum(np.maximum(xf, -cf), cf)
+    ch = getattr(layer, "xscale_ch", None)
+    if ch is not None and len(ch):
+        # SLiM page, "Output Error Minimization in SLiM-Quant": the activations
+        # of the scaled channels are divided by alpha, i.e. multiplied by the
+        # stored factor 1/alpha; the product is an activation of the layer's
+        # input type again.
+        f = np.asarray(layer.xscale, dtype=np.float16).astype(np.float64)
+        cols = np.asarray(ch, dtype=np.int64)
+        xf = xf.copy()
+        xf[:, cols] = round_to_act(xf[:, cols] * f[None, :], layer.x_dtype)
     return xf
 
 

@@ -10,6 +10,7 @@ with one stream per quantity, so each array is reproducible on its own:
     1 LUT centroids / scales      5 low-rank L
     2 mask                        6 low-rank R
     3 CSR positions               7 activations (key also holds M)
+                                  8 per-channel activation factors
 
 Rounding to fp16 uses numpy's round-to-nearest-even cast; bf16 values are
 drawn in fp64, cast to fp32 and rounded to bf16 (nearest, ties to even).
@@ -29,7 +30,7 @@ import numpy as np
 ROOT_SEED = 2026
 
 # Stream ids of the seed sequence.
-S_CODES, S_LUT, S_MASK, S_CSR_POS, S_CSR_VAL, S_L, S_R, S_X = range(8)
+S_CODES, S_LUT, S_MASK, S_CSR_POS, S_CSR_VAL, S_L, S_R, S_X, S_XSCALE = range(9)
 
 # The six ways to keep 2 of 4 consecutive weights.
 PAIRS_2_4 = np.array([(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)], dtype=np.int64)
@@ -71,6 +72,10 @@ class LogicalLayer:
               int4: L, R int8 codes in -8..7; L_scale fp16 [ceil(K/g), r],
                     R_scale fp16 [ceil(r/g), N]
       act_clamp  fp16 scalar (np.float16) or None
+      xscale_ch  int32 [n] strictly increasing input channels whose activations
+                 are scaled (SLiM's output-error variant), or None
+      xscale     fp16 [n] the factor each of those activations is multiplied by
+                 (1/alpha, in (0, 1]), or None
       x_dtype    'f16' | 'bf16'
     """
 
@@ -94,6 +99,8 @@ class LogicalLayer:
     L_scale: Optional[np.ndarray] = None
     R_scale: Optional[np.ndarray] = None
     act_clamp: Optional[np.float16] = None
+    xscale_ch: Optional[np.ndarray] = None
+    xscale: Optional[np.ndarray] = None
     x_dtype: str = "f16"
     name: str = ""
     meta: dict = field(default_factory=dict)
@@ -161,6 +168,16 @@ def draw_csr_skewed(rng_pos, rng_val, N, K, density=0.0045, hot_frac=0.01, hot_s
     np.cumsum(np.bincount(rows, minlength=N), out=row_ptr[1:])
     vals = rng_val.normal(0.0, sigma, size=pos.size).astype(np.float16)
     return row_ptr.astype(np.int32), cols, vals
+
+
+def draw_act_scale(rng, K, frac=0.01, alpha_max=4.0):
+    """About `frac` of the K input channels, uniform at random, each with a
+    factor alpha drawn uniformly from [1, alpha_max]; returns the sorted
+    channels (int32) and the activation factors fp16(1/alpha)."""
+    n = int(round(frac * K))
+    ch = np.sort(rng.choice(K, size=n, replace=False)).astype(np.int32)
+    alpha = rng.uniform(1.0, alpha_max, size=n)
+    return ch, (1.0 / alpha).astype(np.float16)
 
 
 def draw_mask_2_4(rng_mask, N, K):
@@ -325,6 +342,13 @@ def make_layer(cfg: int, layer, K: Optional[int] = None, N: Optional[int] = None
                             act_clamp=c, x_dtype="f16", name=tag, meta={"clamp_M": M_for_clamp})
 
     raise ValueError(f"unknown config {cfg}")
+
+
+def with_act_scale(layer: LogicalLayer, seed: int = 0, frac: float = 0.01) -> LogicalLayer:
+    """`layer` with about `frac` of its input channels scaled (seeded by `seed`
+    and the layer's shape), the recipe of SLiM's output-error variant."""
+    ch, f = draw_act_scale(_rng(layer.K, layer.N, S_XSCALE, seed), layer.K, frac)
+    return layer.with_(xscale_ch=ch, xscale=f)
 
 
 def empty_csr(N: int):

@@ -33,6 +33,10 @@ def load_golden(name):
         kw["csr_val"] = np.array(g["csr_val"], dtype=np.float16)
     if "act_clamp" in g:
         kw["act_clamp"] = np.float16(g["act_clamp"])
+    if "xscale_ch" in g:
+        kw["xscale_ch"] = np.array(g["xscale_ch"], dtype=np.int32)
+        kw["xscale"] = np.array(g["xscale"], dtype=np.float16)
+        assert np.array_equal(kw["xscale"].astype(np.float64), np.array(g["xscale"])), "factor not exact in fp16"
     lr = g.get("lr", "none")
     kw["lr"] = lr
     if lr != "none":

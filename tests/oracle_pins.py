@@ -150,6 +150,74 @@ def pin_clamp_identity_rows(O):
     assert np.array_equal(O.forward(layer.with_(act_clamp=None), x), x.astype(np.float64))
 
 
+def pin_round_to_act_library(O):
+    # Nearest-even rounding to the activation type against library casts:
+    # numpy's float64 -> float16 and torch's float32 -> bfloat16.  Random values
+    # over a wide exponent range (fp16 subnormals included) and exact midpoints
+    # between neighbouring values of each type (the ties).
+    import torch
+    r = _rng(41)
+    v = r.normal(0, 1, 4000) * np.exp2(r.integers(-26, 12, 4000))
+    h = r.integers(1, 0x7BFE, 3000).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    for vals in (v, (lo + hi) / 2, -(lo + hi) / 2):
+        assert np.array_equal(O.round_to_act(vals, "f16"), vals.astype(np.float16).astype(np.float64))
+    hb = r.integers(0x0081, 0x7F7E, 3000).astype(np.uint32) << 16
+    lob = hb.view(np.float32).astype(np.float64)
+    hib = (hb + (1 << 16)).view(np.float32).astype(np.float64)
+    v32 = (r.normal(0, 1, 4000) * np.exp2(r.integers(-60, 60, 4000))).astype(np.float32).astype(np.float64)
+    for vals in (v32, (lob + hib) / 2, -(lob + hib) / 2):
+        ref = torch.tensor(vals, dtype=torch.float64).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+        assert np.array_equal(O.round_to_act(vals, "bf16"), ref)
+
+
+def _int8_lr_layer(seed, K=24, N=5, rank=3):
+    r = _rng(seed)
+    q = r.integers(-31, 32, size=(N, K)).astype(np.int8)
+    s = np.exp2(-r.integers(3, 7, size=N)).astype(np.float16)
+    rp, col, val = draw_csr(r, r, N, K, density=0.2)
+    L = (r.integers(-16, 17, size=(K, rank)) / 64).astype(np.float16)
+    R = (r.integers(-16, 17, size=(rank, N)) / 64).astype(np.float16)
+    return LogicalLayer(K=K, N=N, dense="int8", qvals=q, row_scale=s, csr_row_ptr=rp, csr_col=col,
+                        csr_val=val, lr="fp16", rank=rank, L=L, R=R)
+
+
+def pin_act_scale_identity(O):
+    # factors of exactly 1 change nothing
+    layer = _int8_lr_layer(51)
+    x = _x16(52, 3, layer.K)
+    ch = np.array([0, 5, 23], np.int32)
+    scaled = layer.with_(xscale_ch=ch, xscale=np.ones(3, np.float16))
+    assert np.array_equal(O.forward(scaled, x), O.forward(layer, x))
+
+
+def pin_act_scale_equivalence(O):
+    # SLiM's output-error variant keeps the product unchanged: weights of
+    # input channel k times alpha_k, activations of channel k times 1/alpha_k.
+    # With alpha a power of two every scaled value is exact, so the layer whose
+    # column k of D and S and row k of L carry alpha_k, run with the factors
+    # 1/alpha_k, must give the unscaled layer's output.
+    ch = np.array([1, 7, 8, 20], np.int32)
+    alpha = np.array([2.0, 4.0, 4.0, 2.0])
+    for x_dtype in ("f16", "bf16"):
+        layer = _int8_lr_layer(53).with_(x_dtype=x_dtype)
+        r = _rng(54)
+        xf = r.choice([-1.0, 1.0], size=(4, layer.K)) * r.uniform(0.5, 4.0, size=(4, layer.K))
+        x = xf.astype(np.float16) if x_dtype == "f16" else bf16_bits_from_f32(xf.astype(np.float32))
+        q = layer.qvals.astype(np.int64)
+        q[:, ch] *= alpha.astype(np.int64)[None, :]          # |q| <= 31, so 4q still fits int8
+        val = layer.csr_val.astype(np.float64)
+        L = layer.L.astype(np.float64)
+        for j, k in enumerate(ch):
+            val[layer.csr_col == k] *= alpha[j]
+            L[k] *= alpha[j]
+        scaled = layer.with_(qvals=q.astype(np.int8), csr_val=val.astype(np.float16), L=L.astype(np.float16),
+                             xscale_ch=ch, xscale=(1.0 / alpha).astype(np.float16))
+        assert np.isin(layer.csr_col, ch).any()
+        _close(O.forward(scaled, x), O.forward(layer, x))
+
+
 # ---------------------------------------------------------------------------
 # library routines on another route
 # ---------------------------------------------------------------------------
@@ -352,6 +420,9 @@ ALL_PINS = [
     pin_mask_2_4_keeps_two,
     pin_linearity,
     pin_clamp_identity_rows,
+    pin_round_to_act_library,
+    pin_act_scale_identity,
+    pin_act_scale_equivalence,
     pin_library_route,
     pin_lowrank_groups_ragged,
     pin_lut4_equals_int4,

@@ -135,11 +135,99 @@ def _mut_debug_planes_truncate(O):
     O.debug_planes = debug_planes
 
 
+def _scaled_activations(O, order="clamp_first", rnd=None, factor=lambda f: f, shift=0):
+    """activations() with the channel scaling rebuilt with one planted change."""
+    rnd = rnd or O.round_to_act
+
+    def activations(layer, x):
+        xf = O._act_to_f64(x, layer.x_dtype)
+        if xf.ndim == 1:
+            xf = xf[None, :]
+        c = layer.act_clamp
+        ch = layer.xscale_ch
+        if ch is not None and len(ch) and order == "scale_first":
+            f = factor(np.asarray(layer.xscale, np.float16).astype(np.float64))
+            cols = (np.asarray(ch, np.int64) + shift) % layer.K
+            xf = xf.copy()
+            xf[:, cols] = rnd(xf[:, cols] * f[None, :], layer.x_dtype)
+        if c is not None:
+            xf = np.minimum(np.maximum(xf, -float(c)), float(c))
+        if ch is not None and len(ch) and order == "clamp_first":
+            f = factor(np.asarray(layer.xscale, np.float16).astype(np.float64))
+            cols = (np.asarray(ch, np.int64) + shift) % layer.K
+            xf = xf.copy()
+            xf[:, cols] = rnd(xf[:, cols] * f[None, :], layer.x_dtype)
+        return xf
+    return activations
+
+
+def _mut_xscale_ignored(O):
+    orig = O.activations
+    O.activations = lambda layer, x: orig(layer.with_(xscale_ch=None, xscale=None), x)
+
+
+def _mut_xscale_times_alpha(O):
+    O.activations = _scaled_activations(O, factor=lambda f: 1.0 / f)
+
+
+def _mut_xscale_channel_shift(O):
+    O.activations = _scaled_activations(O, shift=1)
+
+
+def _mut_xscale_before_clamp(O):
+    O.activations = _scaled_activations(O, order="scale_first")
+
+
+def _mut_xscale_unrounded(O):
+    O.activations = _scaled_activations(O, rnd=lambda v, dt: v)
+
+
+def _mut_xscale_round_to_f16_always(O):
+    O.activations = _scaled_activations(O, rnd=lambda v, dt: O.round_to_act(v, "f16"))
+
+
+def _mut_round_truncate(O):
+    orig = O.round_to_act
+
+    def round_to_act(v, x_dtype):
+        v = np.asarray(v, np.float64)
+        r = orig(v, x_dtype)
+        # toward zero: step back where nearest rounding went away from zero
+        p, emin = O._ACT_FORMATS[x_dtype]
+        _, e = np.frexp(v)
+        sp = np.ldexp(1.0, np.maximum(e - 1, emin) - (p - 1))
+        return np.where(np.abs(r) > np.abs(v), r - np.sign(v) * sp, r)
+    O.round_to_act = round_to_act
+
+
+def _mut_round_half_away(O):
+    def round_to_act(v, x_dtype):
+        p, emin = O._ACT_FORMATS[x_dtype]
+        v = np.asarray(v, np.float64)
+        _, e = np.frexp(v)
+        sp = np.ldexp(1.0, np.maximum(e - 1, emin) - (p - 1))
+        return np.sign(v) * np.floor(np.abs(v) / sp + 0.5) * sp
+    O.round_to_act = round_to_act
+
+
+def _mut_round_no_subnormals(O):
+    def round_to_act(v, x_dtype):
+        p, _ = O._ACT_FORMATS[x_dtype]
+        v = np.asarray(v, np.float64)
+        _, e = np.frexp(v)
+        sp = np.ldexp(1.0, e - 1 - (p - 1))
+        return np.rint(v / sp) * sp
+    O.round_to_act = round_to_act
+
+
 MUTANTS = [
     _mut_mask_ignored, _mut_scale_per_column, _mut_lut_off_by_one, _mut_sparse_dropped,
     _mut_sparse_sign, _mut_sparse_col_shift, _mut_lowrank_dropped, _mut_lowrank_group_axis,
     _mut_lowrank_R_transposed_use, _mut_clamp_missing, _mut_clamp_one_sided, _mut_bf16_shift,
     _mut_forward_transposed, _mut_debug_planes_truncate,
+    _mut_xscale_ignored, _mut_xscale_times_alpha, _mut_xscale_channel_shift, _mut_xscale_before_clamp,
+    _mut_xscale_unrounded, _mut_xscale_round_to_f16_always, _mut_round_truncate, _mut_round_half_away,
+    _mut_round_no_subnormals,
 ]
 
 
