@@ -29,7 +29,7 @@ LR = {"none": 0, "fp16": 1, "bf16": 2, "int4": 3}
 ACT = {"f16": 0, "bf16": 1}
 PATH = {"auto": 0, "decode": 1, "prefill": 2, "decode_valu": 3, "decode_mfma": 4}
 STATUS = {0: "CL_OK", -1: "CL_EINVAL", -2: "CL_EUNSUPPORTED", -3: "CL_ENOMEM", -4: "CL_EHIP", -5: "CL_ESIZE"}
-SECTIONS = ["dense", "table", "meta", "nzoff", "rowptr", "col", "val", "L", "R", "Lscale", "Rscale"]
+SECTIONS = ["dense", "table", "meta", "nzoff", "rowptr", "col", "val", "L", "R", "Lscale", "Rscale", "xscale"]
 SEC_COUNT = 16
 
 
@@ -50,12 +50,13 @@ class cl_layer_desc(ctypes.Structure):
         ("L", ctypes.c_void_p), ("R", ctypes.c_void_p), ("L_scale", ctypes.c_void_p), ("R_scale", ctypes.c_void_p),
         ("has_clamp", ctypes.c_int32), ("act_clamp", ctypes.c_uint16), ("reserved0", ctypes.c_uint16),
         ("x_dtype", ctypes.c_int32),
+        ("n_xscale", ctypes.c_int32), ("xscale_ch", ctypes.c_void_p), ("xscale", ctypes.c_void_p),
     ]
 
 
 class cl_bytes(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in
-                ("codes", "lut_or_scale", "mask_meta", "csr", "lowrank", "total", "device_padding")]
+                ("codes", "lut_or_scale", "mask_meta", "csr", "lowrank", "act_scale", "total", "device_padding")]
 
 
 class cl_blob_header(ctypes.Structure):
@@ -67,7 +68,7 @@ class cl_blob_header(ctypes.Structure):
         ("n_tiles", ctypes.c_int32), ("chunks", ctypes.c_int32), ("span", ctypes.c_int32),
         ("meta_chunk_bytes", ctypes.c_int32), ("nnz", ctypes.c_int64), ("total_bytes", ctypes.c_uint64),
         ("off", ctypes.c_uint64 * SEC_COUNT), ("len", ctypes.c_uint64 * SEC_COUNT),
-        ("acct", cl_bytes), ("reserved", ctypes.c_uint8 * 64),
+        ("acct", cl_bytes), ("n_xscale", ctypes.c_int32), ("reserved", ctypes.c_uint8 * 60),
     ]
 
 
@@ -166,6 +167,11 @@ def _desc(layer, keep: list) -> cl_layer_desc:
     d.has_clamp = 0 if c is None else 1
     d.act_clamp = 0 if c is None else int(np.array(c, dtype=np.float16).view(np.uint16))
     d.x_dtype = ACT[getattr(layer, "x_dtype", "f16")]
+    ch = getattr(layer, "xscale_ch", None)
+    if ch is not None and len(ch):
+        d.n_xscale = int(len(ch))
+        d.xscale_ch = _ptr(ch, np.int32, keep)
+        d.xscale = _u16(layer.xscale, keep)
     return d
 
 

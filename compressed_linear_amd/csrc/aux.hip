@@ -8,13 +8,25 @@
 namespace cl {
 
 // ---------------------------------------------------------------------------
-// x' = clamp(x, -c, c), copied to a row stride Kx (even) with a zero tail.
-// Activation editor of "Compressing Large Language Models by Joint
-// Sparsification and Quantization", Approach: one clamp value per layer.
+// x' = clamp(x, -c, c), then x'[k] * f[k] on the scaled channels, copied to a
+// row stride Kx (a multiple of 8) with a zero tail.
+// Clamp: activation editor of "Compressing Large Language Models by Joint
+// Sparsification and Quantization", Approach (one clamp value per layer).
+// Scaling: "SLiM" page, rebuttal section "Output Error Minimization in
+// SLiM-Quant" (the activations of the salient channels divided by alpha; the
+// layer stores f = 1/alpha per channel, 1 elsewhere).  x * f is exact in fp32
+// (at most 11 + 11 significant bits, f a normal fp16 <= 1) and is rounded once,
+// to nearest-even, to the activation type.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN stays a quiet NaN
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
 template <bool BF16>
 __global__ void prep_x_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ xp, int M, int K, int Kx,
-                              int has_clamp, float c) {
+                              int has_clamp, float c, const uint16_t* __restrict__ xs) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t total = (size_t)M * Kx;
   if (i >= total) return;
@@ -22,10 +34,11 @@ __global__ void prep_x_kernel(const uint16_t* __restrict__ x, uint16_t* __restri
   uint16_t v = 0;
   if (k < K) {
     v = x[(size_t)m * K + k];
-    if (has_clamp) {
+    if (has_clamp || xs) {
       float f = BF16 ? __uint_as_float((uint32_t)v << 16) : (float)__builtin_bit_cast(_Float16, v);
-      f = fminf(fmaxf(f, -c), c);  // +-c is exact in the activation type (checked by the packer)
-      v = BF16 ? (uint16_t)(__float_as_uint(f) >> 16) : __builtin_bit_cast(uint16_t, (_Float16)f);
+      if (has_clamp) f = fminf(fmaxf(f, -c), c);  // +-c is exact in the activation type (checked by the packer)
+      if (xs) f *= (float)__builtin_bit_cast(_Float16, xs[k]);
+      v = BF16 ? f32_to_bf16_rne(f) : __builtin_bit_cast(uint16_t, (_Float16)f);
     }
   }
   xp[i] = v;
@@ -37,10 +50,10 @@ hipError_t launch_prep_x(const Layer& L, int M, const void* x, hipStream_t strea
   const float c = (float)__builtin_bit_cast(_Float16, L.h.act_clamp);
   if (L.h.x_dtype == CL_ACT_BF16)
     hipLaunchKernelGGL(prep_x_kernel<true>, dim3(blocks), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(x), L.xprep, M, L.h.K, L.Kx, L.h.has_clamp, c);
+                       static_cast<const uint16_t*>(x), L.xprep, M, L.h.K, L.Kx, L.h.has_clamp, c, L.xscale);
   else
     hipLaunchKernelGGL(prep_x_kernel<false>, dim3(blocks), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(x), L.xprep, M, L.h.K, L.Kx, L.h.has_clamp, c);
+                       static_cast<const uint16_t*>(x), L.xprep, M, L.h.K, L.Kx, L.h.has_clamp, c, L.xscale);
   return hipGetLastError();
 }
 

@@ -33,8 +33,9 @@ constexpr int kMfMinM = 4;
 
 // x: the caller's activations, or L.xprep when they are clamped / restaged
 // already.  The matrix-core kernel reads them raw when K is a multiple of 8 (16-byte
-// aligned rows) and the low-rank prologue, if any, runs inside the same launch:
-// both then apply the clamp while staging.  Otherwise a prep kernel runs first.
+// aligned rows), the layer scales no channels and the low-rank prologue, if any,
+// runs inside the same launch: both then apply the clamp while staging.
+// Otherwise a prep kernel runs first.
 static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float* y, hipStream_t stream) {
   const cl_blob_header& h = L.h;
   const bool has_lr = h.lr != CL_LR_NONE;
@@ -42,7 +43,7 @@ static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float
   const bool raw = L.xprep != nullptr && x != L.xprep;
   bool clamp_in_kernel = false;
   if (raw) {
-    if (h.K % 8 == 0 && (!has_lr || fused_lr)) {
+    if (h.K % 8 == 0 && (!has_lr || fused_lr) && L.xscale == nullptr) {
       clamp_in_kernel = h.has_clamp != 0;
     } else {
       const hipError_t e = launch_prep_x(L, M, x, stream);

@@ -38,7 +38,8 @@ struct Layer {
   uint32_t* counters = nullptr;  // [n_tiles + 1], zero between forwards
   float* part = nullptr;         // [n_tiles][split][kMaxDecodeM][64]
   float* t = nullptr;            // [max_M][rank]
-  uint16_t* xprep = nullptr;     // [max_M][Kx]  clamped / padded activations
+  uint16_t* xprep = nullptr;     // [max_M][Kx]  clamped / scaled / padded activations
+  const uint16_t* xscale = nullptr;  // [K] fp16 per-channel activation factors (1 where unscaled), or null
   int Kx = 0;                    // row stride of xprep (even)
 
   // matrix-core prefill (built at create)

@@ -52,6 +52,8 @@ cl_status check_blob(const void* blob, const cl_blob_header** out) {
     if (h->len[s] && (h->off[s] % 256 || h->off[s] + h->len[s] > h->total_bytes))
       return fail(CL_EINVAL, "blob section %d lies outside the blob", s);
   }
+  if (h->n_xscale < 0 || h->n_xscale > h->K || (h->n_xscale > 0) != (h->len[CL_SEC_XSCALE] == (uint64_t)h->K * 2))
+    return fail(CL_EINVAL, "blob header has an inconsistent activation-scale section");
   if (out) *out = h;
   return CL_OK;
 }
@@ -150,6 +152,19 @@ cl_status validate(const cl_layer_desc* d) {
     if (e != 0 && (m & 7u)) return fail(CL_EUNSUPPORTED, "the clamp value is not representable in bf16");
     if (e == 0 && m && (m >> __builtin_ctz(m)) > 0xFF) return fail(CL_EUNSUPPORTED, "the clamp value is not representable in bf16");
   }
+  if (d->n_xscale < 0 || d->n_xscale > d->K) return fail(CL_EINVAL, "n_xscale must be in [0, K]");
+  if (d->n_xscale > 0) {
+    if (!d->xscale_ch || !d->xscale) return fail(CL_EINVAL, "activation scaling arrays are NULL");
+    for (int32_t i = 0; i < d->n_xscale; ++i) {
+      const int32_t c = d->xscale_ch[i];
+      if (c < 0 || c >= d->K) return fail(CL_EINVAL, "scaled channel %d out of range", c);
+      if (i > 0 && c <= d->xscale_ch[i - 1]) return fail(CL_EINVAL, "scaled channels are not strictly increasing");
+      // a normal fp16 in [2^-14, 1]: x * f is then exact in fp32 and cannot overflow
+      if (d->xscale[i] < 0x0400u || d->xscale[i] > 0x3C00u)
+        return fail(CL_EINVAL, "activation factor 0x%04x of channel %d is not a normal value in [2^-14, 1]",
+                    d->xscale[i], c);
+    }
+  }
   return CL_OK;
 }
 
@@ -229,6 +244,10 @@ void make_plan(const cl_layer_desc* d, Plan& p) {
       p.acct.lowrank = 2 * (p.K * r + r * p.N);
     }
   }
+  if (d->n_xscale > 0) {
+    len[CL_SEC_XSCALE] = p.K * 2;
+    p.acct.act_scale = 6 * (uint64_t)d->n_xscale;
+  }
   uint64_t off = round_up(sizeof(cl_blob_header), 256);
   uint64_t dev_total = 0;
   for (int s = 0; s < CL_SEC_COUNT; ++s) {
@@ -239,7 +258,7 @@ void make_plan(const cl_layer_desc* d, Plan& p) {
     dev_total += len[s];
   }
   p.total = off;
-  p.acct.total = p.acct.codes + p.acct.lut_or_scale + p.acct.mask_meta + p.acct.csr + p.acct.lowrank;
+  p.acct.total = p.acct.codes + p.acct.lut_or_scale + p.acct.mask_meta + p.acct.csr + p.acct.lowrank + p.acct.act_scale;
   // every device byte of the packed sections that the canonical count does not include
   p.acct.device_padding = dev_total > p.acct.total ? dev_total - p.acct.total : 0;
 }
@@ -364,6 +383,11 @@ void pack_dense(const cl_layer_desc* d, const Plan& p, uint8_t* blob) {
 
 void pack_rest(const cl_layer_desc* d, const Plan& p, uint8_t* blob) {
   const int64_t K = p.K, N = p.N;
+  if (d->n_xscale > 0) {  // dense per-channel factors, fp16 1 where unscaled
+    uint16_t* xs = reinterpret_cast<uint16_t*>(blob + p.off[CL_SEC_XSCALE]);
+    for (int64_t k = 0; k < K; ++k) xs[k] = 0x3C00u;
+    for (int32_t i = 0; i < d->n_xscale; ++i) xs[d->xscale_ch[i]] = d->xscale[i];
+  }
   uint16_t* tab = reinterpret_cast<uint16_t*>(blob + p.off[CL_SEC_TABLE]);
   if (p.tab_entries)
     memcpy(tab, d->lut, N * p.tab_entries * 2);
@@ -458,6 +482,7 @@ extern "C" cl_status cl_pack(const cl_layer_desc* d, void* blob, size_t* blob_by
     h->len[s] = p.len[s];
   }
   h->acct = p.acct;
+  h->n_xscale = d->n_xscale;
   pack_dense(d, p, b);
   pack_rest(d, p, b);
   *blob_bytes = p.total;

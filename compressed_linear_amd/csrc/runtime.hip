@@ -62,10 +62,11 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
   if (h.mask == CL_MASK_BITMAP) o_nzs = take((size_t)Npad * 4 * split * 4);
   // t = x' L: [max_M][rank] for decode; prefill keeps up to 8 K-split partials [8][max_M][rank rounded to 8]
   if (h.lr != CL_LR_NONE && h.rank > 0) o_t = take((size_t)8 * max_M * round_up(h.rank, 8) * 4);
-  // activations are restaged (clamped, row stride a multiple of 8 for aligned
-  // 128-bit loads) when the layer clamps them or K is not a multiple of 8
+  // activations are restaged (clamped and / or channel-scaled, row stride a
+  // multiple of 8 for aligned 128-bit loads) when the layer clamps or scales
+  // them or K is not a multiple of 8
   const int Kx = (int)round_up(h.K, 8);
-  if (h.has_clamp || (h.K & 7)) o_xp = take((size_t)max_M * Kx * 2);
+  if (h.has_clamp || h.n_xscale > 0 || (h.K & 7)) o_xp = take((size_t)max_M * Kx * 2);
   // matrix-core prefill (all formats but the bitmap): outlier lists per
   // (128-row tile, K step), R^T twice and L^T in the MFMA input type, t_hi | t_lo;
   // R^T twice also for a bitmap layer (its decode runs on the matrix-core kernel)
@@ -335,6 +336,7 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
   uint8_t* d = L->dev;
   L->dense = sec<uint8_t>(d, *h, CL_SEC_DENSE);
   L->table = sec<uint8_t>(d, *h, CL_SEC_TABLE);
+  L->xscale = h->n_xscale > 0 ? sec<uint16_t>(d, *h, CL_SEC_XSCALE) : nullptr;
   L->meta = sec<uint8_t>(d, *h, CL_SEC_META);
   L->nzoff = sec<int32_t>(d, *h, CL_SEC_NZOFF);
   L->rowptr = sec<int32_t>(d, *h, CL_SEC_ROWPTR);

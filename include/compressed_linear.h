@@ -97,6 +97,18 @@ typedef enum {
  *                         axis per output column), fp16 bits.
  *   has_clamp, act_clamp: x' = min(max(x, -c), c) with c = act_clamp (fp16 bits, c >= 0).
  *   x_dtype             : element type of x in cl_forward (fp16 or bf16).
+ *   n_xscale, xscale_ch, xscale: per-channel activation scaling of SLiM's
+ *                         output-error variant ("SLiM" page, rebuttal section "Output
+ *                         Error Minimization in SLiM-Quant": the weights of a few
+ *                         salient input channels carry a factor alpha, their
+ *                         activations are divided by it while the layer runs).
+ *                         The weights given above already include alpha.  xscale_ch
+ *                         [n_xscale] int32, strictly increasing, < K; xscale
+ *                         [n_xscale] fp16 bits of the activation factor f = 1/alpha,
+ *                         a normal value in [2^-14, 1].  After the clamp,
+ *                         x'[m, k] = x'[m, k] * f rounded once (nearest, ties to even)
+ *                         to the activation type.  n_xscale = 0: no scaling (the two
+ *                         pointers may be NULL).
  */
 typedef struct {
   int32_t K, N;
@@ -122,6 +134,9 @@ typedef struct {
   uint16_t act_clamp;
   uint16_t reserved0;
   int32_t x_dtype;          /* cl_act_dtype */
+  int32_t n_xscale;
+  const int32_t* xscale_ch;
+  const uint16_t* xscale;
 } cl_layer_desc;
 
 /*
@@ -135,12 +150,13 @@ typedef struct {
  *                bitmap words plus (N+1)*4 bytes of nonzero offsets.
  *   csr          6*nnz + 4*(N+1)
  *   lowrank      factor bytes (2 per value; int4: 1/2 per value) plus scales
+ *   act_scale    6 per scaled input channel (int32 channel, fp16 factor)
  *   total        the sum of the above
  *   device_padding  extra bytes of the device layout (row and tile padding),
  *                   not part of `total`.
  */
 typedef struct {
-  uint64_t codes, lut_or_scale, mask_meta, csr, lowrank, total;
+  uint64_t codes, lut_or_scale, mask_meta, csr, lowrank, act_scale, total;
   uint64_t device_padding;
 } cl_bytes;
 
@@ -191,7 +207,9 @@ cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes, int32_t m
 
 /*
  * cl_forward -- y = x' W_hat^T for M rows of activations.
- *   x_dev  device, [M, K] fp16 or bf16 (the layer's x_dtype), 16-byte aligned.
+ *   x_dev  device, [M, K] fp16 or bf16 (the layer's x_dtype), 16-byte aligned;
+ *          read only (the clamp and the channel scaling, if the layer has them,
+ *          go to a copy in the workspace or are applied while staging).
  *   y_dev  device, [M, N] fp32, overwritten, 16-byte aligned.
  *   1 <= M <= max_M.  M <= 32 runs the decode kernels (the vector-ALU
  *   streaming kernel at small M, the matrix-core decode kernel with weights
@@ -238,7 +256,7 @@ const char* cl_last_error(void);
  * packer.
  */
 #define CL_BLOB_MAGIC 0x31424C43u /* "CLB1" */
-#define CL_BLOB_VERSION 1u
+#define CL_BLOB_VERSION 2u
 enum {
   CL_SEC_DENSE = 0,   /* dense stream, row-major 16-byte chunks (bitmap: kept values) */
   CL_SEC_TABLE,       /* LUT [Npad * 2^b] fp16 or row scales [Npad] fp16 */
@@ -251,6 +269,7 @@ enum {
   CL_SEC_R,           /* low-rank R, transposed: [Npad][rank] */
   CL_SEC_LSCALE,      /* int4 L scales, [rank][ceil(K/group)] */
   CL_SEC_RSCALE,      /* int4 R scales, [Npad][ceil(rank/group)] */
+  CL_SEC_XSCALE,      /* activation factors fp16 [K], 1 on the unscaled channels */
   CL_SEC_COUNT = 16
 };
 typedef struct {
@@ -266,7 +285,8 @@ typedef struct {
   uint64_t off[CL_SEC_COUNT];
   uint64_t len[CL_SEC_COUNT];
   cl_bytes acct;
-  uint8_t reserved[64];
+  int32_t n_xscale;      /* scaled input channels */
+  uint8_t reserved[60];
 } cl_blob_header;
 
 #ifdef __cplusplus

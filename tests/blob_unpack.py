@@ -112,4 +112,11 @@ def unpack(blob):
         else:
             out["L"] = _sec(blob, h, "L", np.uint16).reshape(r, K).T
             out["R"] = _sec(blob, h, "R", np.uint16).reshape(Npad, r)[:N].T
+    if h["n_xscale"]:
+        # dense fp16 factor per input channel, 1 (0x3C00) where unscaled
+        xs = _sec(blob, h, "xscale", np.uint16)
+        assert xs.size == K
+        ch = np.flatnonzero(xs != 0x3C00).astype(np.int32)
+        out["xscale_dense"] = xs.view(np.float16)
+        out["xscale_ch"], out["xscale"] = ch, xs[ch].view(np.float16)
     return h, out

@@ -33,6 +33,16 @@ def _roundtrip(layer):
         else:
             b = lambda a: np.asarray(a).view(np.uint16)
             assert np.array_equal(u["L"], b(layer.L)) and np.array_equal(u["R"], b(layer.R))
+    ch = layer.xscale_ch
+    assert h["n_xscale"] == (0 if ch is None else len(ch))
+    if ch is not None and len(ch):
+        dense = np.ones(layer.K, np.float16)
+        dense[ch] = layer.xscale
+        assert np.array_equal(u["xscale_dense"].view(np.uint16), dense.view(np.uint16))
+        assert acct["act_scale"] == 6 * len(ch)
+    else:
+        assert acct["act_scale"] == 0 and "xscale" not in h["sections"]
+    assert acct["total"] == sum(acct[f] for f in ("codes", "lut_or_scale", "mask_meta", "csr", "lowrank", "act_scale"))
     return blob, acct
 
 
@@ -45,6 +55,15 @@ def test_roundtrip_golden(name):
 @pytest.mark.parametrize("cfg,K,N", [(1, 1000, 130), (2, 999 + 1, 70), (3, 512, 100), (4, 640, 66), (5, 1210, 129)])
 def test_roundtrip_configs(cfg, K, N):
     _roundtrip(make_layer(cfg, 0, K=K, N=N))
+
+
+@pytest.mark.parametrize("cfg,K,N", [(2, 1000, 70), (4, 640, 66), (5, 1210, 129)])
+def test_roundtrip_act_scale(cfg, K, N):
+    from synth.layers import with_act_scale
+    lay = with_act_scale(make_layer(cfg, 0, K=K, N=N), frac=0.05)
+    _, acct = _roundtrip(lay)
+    _, acct0 = cla.pack(lay.with_(xscale_ch=None, xscale=None))
+    assert acct["total"] == acct0["total"] + 6 * len(lay.xscale_ch)
 
 
 def test_roundtrip_int4_plain_and_int8_plain():
@@ -125,6 +144,13 @@ def test_validation_errors():
     _bad(lay3.with_(qvals=q), -1)                                   # int4 value out of range
     _bad(base.with_(K=0, codes=base.codes[:, :0]), -1)
     _bad(base.with_(act_clamp=np.float16(-1.0)), -1)
+    f = np.full(3, 0.5, np.float16)
+    _bad(base.with_(xscale_ch=np.array([1, 1, 4], np.int32), xscale=f), -1)      # repeated channel
+    _bad(base.with_(xscale_ch=np.array([4, 1, 7], np.int32), xscale=f), -1)      # not increasing
+    _bad(base.with_(xscale_ch=np.array([1, 4, 50], np.int32), xscale=f), -1)     # channel out of range
+    for bad in (0.0, -0.5, 2.0, 2.0 ** -15, np.inf):                               # factor not normal in [2^-14, 1]
+        _bad(base.with_(xscale_ch=np.array([1, 4, 7], np.int32), xscale=np.array([0.5, bad, 0.5], np.float16)), -1)
+    cla.pack(base.with_(xscale_ch=np.array([1, 4, 49], np.int32), xscale=np.array([1.0, 2.0 ** -14, 0.75], np.float16)))
 
 
 def test_size_query_and_small_buffer():
