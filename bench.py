@@ -156,12 +156,14 @@ def to_dev_x(x, x_dtype, dev):
     return torch.from_numpy(np.ascontiguousarray(x.astype(np.float16))).to(dev)
 
 
-def build_layers(cfg: int, M: int):
-    from synth.layers import CONFIGS, make_layer, make_x
+def build_layers(cfg: int, M: int, act_scale: float = 0.0):
+    from synth.layers import CONFIGS, make_layer, make_x, with_act_scale
     import compressed_linear_amd as cla
     out, xs = [], []
     for li, (name, K, N) in enumerate(CONFIGS[cfg]["layers"]):
         layer = make_layer(cfg, li, M_for_clamp=M)
+        if act_scale > 0:
+            layer = with_act_scale(layer, seed=li, frac=act_scale)
         blob, acct = cla.pack(layer)
         out.append((layer, acct, blob))
         xs.append(make_x(cfg, li, M))
@@ -176,6 +178,8 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--M", type=int, default=1)
     ap.add_argument("--path", default="auto")
+    ap.add_argument("--act-scale", type=float, default=0.0,
+                    help="scale this fraction of each layer's input channels (SLiM's output-error variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-layer", action="store_true", help="also time each layer alone")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -207,7 +211,7 @@ def main():
     cfg, M = a.config, a.M
 
     log(f"building config {cfg} M={M}")
-    built, xs_np = build_layers(cfg, M)
+    built, xs_np = build_layers(cfg, M, a.act_scale)
     set_bytes = sum(layer_bytes(acct, l.K, l.N, M) for l, acct, _ in built)
     weight_bytes = sum(int(acct["total"]) for _, acct, _ in built)
     R = max(2, -(-ROTATE_BYTES // weight_bytes))
@@ -290,7 +294,8 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded; LLaMA layer shapes, random codes/LUTs/outliers)",
-        "config": {"workload": f"{CONFIGS[cfg]['desc']}: {layers_desc}", "batch": M,
+        "config": {"workload": f"{CONFIGS[cfg]['desc']}: {layers_desc}"
+                   + (f", {a.act_scale:.1%} of input channels scaled" if a.act_scale > 0 else ""), "batch": M,
                    "layers_per_step": n_launch, "rotating_copies": R,
                    "algorithmic_bytes_per_step": int(set_bytes)},
         "roofline": roof,

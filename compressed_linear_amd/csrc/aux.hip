@@ -18,12 +18,6 @@ namespace cl {
 // (at most 11 + 11 significant bits, f a normal fp16 <= 1) and is rounded once,
 // to nearest-even, to the activation type.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN stays a quiet NaN
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
 template <bool BF16>
 __global__ void prep_x_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ xp, int M, int K, int Kx,
                               int has_clamp, float c, const uint16_t* __restrict__ xs) {
@@ -38,7 +32,7 @@ __global__ void prep_x_kernel(const uint16_t* __restrict__ x, uint16_t* __restri
       float f = BF16 ? __uint_as_float((uint32_t)v << 16) : (float)__builtin_bit_cast(_Float16, v);
       if (has_clamp) f = fminf(fmaxf(f, -c), c);  // +-c is exact in the activation type (checked by the packer)
       if (xs) f *= (float)__builtin_bit_cast(_Float16, xs[k]);
-      v = BF16 ? f32_to_bf16_rne(f) : __builtin_bit_cast(uint16_t, (_Float16)f);
+      v = BF16 ? (uint16_t)f32_to_bf16_rne(f) : __builtin_bit_cast(uint16_t, (_Float16)f);
     }
   }
   xp[i] = v;
@@ -134,7 +128,7 @@ __global__ void __launch_bounds__(256) lr_prologue_kernel(LrArgs a) {
 template <int MODE, int MT, bool BF16>
 __global__ void __launch_bounds__(256) lr_split_kernel(LrSplitArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[LrScratch<MODE, MT>::bytes];
-  lr_split_block<MODE, MT, BF16>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.y, smem);
+  lr_split_block<MODE, MT, BF16, false>(a, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.y, smem);
 }
 
 template <int MODE, int MT>

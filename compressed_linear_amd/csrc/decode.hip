@@ -31,20 +31,27 @@ extern template hipError_t launch_mfma_kind<K_INT8_BM>(const MfArgs&, bool, hipS
 // Smallest batch that the automatic choice sends to the matrix-core decode kernel.
 constexpr int kMfMinM = 4;
 
-// x: the caller's activations, or L.xprep when they are clamped / restaged
-// already.  The matrix-core kernel reads them raw when K is a multiple of 8 (16-byte
-// aligned rows), the layer scales no channels and the low-rank prologue, if any,
-// runs inside the same launch: both then apply the clamp while staging.
-// Otherwise a prep kernel runs first.
+// Whether the decode kernels can read the caller's activations raw and edit
+// them (the clamp, the per-channel factors) while staging them: rows of
+// 16-byte aligned loads (K a multiple of 8) and no low-rank prologue kernel of
+// its own (that kernel reads edited activations).
+static bool edit_in_kernel(const Layer& L) {
+  return L.h.K % 8 == 0 && (L.h.lr == CL_LR_NONE || L.lr_mode >= 0);
+}
+
+// x: the caller's activations, or L.xprep when they are edited / restaged
+// already.  The matrix-core kernel reads them raw where edit_in_kernel allows
+// (the low-rank prologue, if any, then runs inside the same launch and edits
+// them the same way); otherwise a prep kernel runs first.
 static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float* y, hipStream_t stream) {
   const cl_blob_header& h = L.h;
   const bool has_lr = h.lr != CL_LR_NONE;
   const bool fused_lr = has_lr && L.lr_mode >= 0;
   const bool raw = L.xprep != nullptr && x != L.xprep;
-  bool clamp_in_kernel = false;
+  bool edit = false;
   if (raw) {
-    if (h.K % 8 == 0 && (!has_lr || fused_lr) && L.xscale == nullptr) {
-      clamp_in_kernel = h.has_clamp != 0;
+    if (edit_in_kernel(L)) {
+      edit = true;
     } else {
       const hipError_t e = launch_prep_x(L, M, x, stream);
       if (e != hipSuccess) return e;
@@ -82,8 +89,9 @@ static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float
   a.part = L.mf_part;
   a.counters = L.counters;
   a.y = y;
-  a.clamp = clamp_in_kernel ? 1 : 0;
+  a.clamp = edit && h.has_clamp ? 1 : 0;
   a.cval = (float)__builtin_bit_cast(_Float16, h.act_clamp);
+  a.xscale = edit ? L.xscale : nullptr;
   if (fused_lr) {
     a.lrp = lowrank_split_args(L, M, x);
     a.lr_ntj = L.lr_rpad / 64;
@@ -92,6 +100,7 @@ static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float
     a.lrp.epoch = ++L.lr_epoch;
     a.lrp.clamp = a.clamp;
     a.lrp.cval = a.cval;
+    a.lrp.xscale = a.xscale;
     a.lr_wgs = L.lr_S * a.lrp.ntiles;
     a.lr_mode = L.lr_mode;
   }
@@ -111,15 +120,94 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
   // and activation row (no mixed fp16 x bf16 dot product), so it keeps only batch 1
   const bool mf_auto = M >= kMfMinM || (M >= 2 && L.h.x_dtype == CL_ACT_BF16);
   if (L.mf_S > 0 && (variant == 2 || (variant == 0 && mf_auto))) return launch_decode_mfma(L, M, x, y, stream);
-  // the batch 1..3 kernels read clamped / restaged activations
-  const void* x_raw = x;
-  if (L.xprep != nullptr && x != L.xprep) {
+
+  const cl_blob_header& h = L.h;
+  const bool bf16 = h.x_dtype == CL_ACT_BF16;
+  const bool raw = L.xprep != nullptr && x != L.xprep;
+  // M <= 4: row-wise kernel (bandwidth bound) when its staged activations fit
+  // in LDS; the bitmap format always uses the tile kernel (its kept values are
+  // consumed per row at a varying rate).  The row-wise kernel edits raw
+  // activations while staging them where edit_in_kernel allows and its first
+  // staging round holds the whole activation block; the tile kernel reads
+  // edited / restaged ones.
+  RowArgs r = {};
+  bool rows = false, rows_edit = false;
+  if (M <= 4 && h.mask != CL_MASK_BITMAP) {
+    r.dense = reinterpret_cast<const uint4*>(L.dense);
+    r.meta = L.meta;
+    r.table = reinterpret_cast<const uint16_t*>(L.table);
+    r.rowptr = h.nnz > 0 ? L.rowptr : nullptr;
+    r.col = L.col;
+    r.val = L.val;
+    r.R = L.R;
+    r.Rscale = L.Rscale;
+    r.t = L.t;
+    r.y = y;
+    r.K = h.K;
+    r.N = h.N;
+    r.M = M;
+    r.chunks = h.chunks;
+    r.rank = h.lr != CL_LR_NONE ? h.rank : 0;
+    r.group = h.group > 0 ? h.group : 1;
+    r.lr_kind = h.lr;
+    r.Npad = L.Npad;
+    r.nnz = (int)h.nnz;
+    bool one_round = false;
+    switch (h.dense) {
+      case CL_DENSE_LUT3: rows = rows_fit<K_LUT3>(r, &one_round); break;
+      case CL_DENSE_LUT4: rows = rows_fit<K_LUT4>(r, &one_round); break;
+      case CL_DENSE_INT4:
+        rows = h.mask == CL_MASK_2_4 ? rows_fit<K_INT4_24>(r, &one_round) : rows_fit<K_INT4>(r, &one_round);
+        break;
+      default: rows = rows_fit<K_INT8>(r, &one_round); break;
+    }
+    rows_edit = rows && raw && one_round && edit_in_kernel(L);
+  }
+  // batches the row-wise kernel cannot stage: the matrix-core kernel where it applies
+  if (!rows && variant == 0 && L.mf_S > 0) return launch_decode_mfma(L, M, x, y, stream);
+  if (raw && !rows_edit) {
     const hipError_t e = launch_prep_x(L, M, x, stream);
     if (e != hipSuccess) return e;
     x = L.xprep;
   }
+  const int ldx = (x == L.xprep) ? L.Kx : h.K;
 
-  const cl_blob_header& h = L.h;
+  if (rows) {
+    r.x = x;
+    r.ldx = ldx;
+    r.clamp = rows_edit && h.has_clamp ? 1 : 0;
+    r.cval = (float)__builtin_bit_cast(_Float16, h.act_clamp);
+    r.xscale = rows_edit ? L.xscale : nullptr;
+    if (h.lr != CL_LR_NONE) {
+      if (L.lr_mode >= 0) {
+        // the prologue runs as this launch's first workgroups
+        r.lrp = lowrank_split_args(L, M, x);
+        r.lrp.clamp = r.clamp;
+        r.lrp.cval = r.cval;
+        r.lrp.xscale = r.xscale;
+        const uint32_t epoch = ++L.lr_epoch;
+        r.lrp.flag = L.lr_cnt + 65;
+        r.lrp.epoch = epoch;
+        r.lr_ntj = L.lr_rpad / 64;
+        r.lr_wgs = L.lr_S * r.lr_ntj * (int)ceil_div(M, lowrank_tile_m(M));
+        r.lr_mode = L.lr_mode;
+        r.lr_flag = r.lrp.flag;
+        r.lr_epoch = epoch;
+      } else {
+        const hipError_t e = launch_lowrank_prologue(L, M, x, stream);
+        if (e != hipSuccess) return e;
+      }
+    }
+    switch (h.dense) {
+      case CL_DENSE_LUT3: return launch_rows_kind<K_LUT3>(r, L.Npad, bf16, stream);
+      case CL_DENSE_LUT4: return launch_rows_kind<K_LUT4>(r, L.Npad, bf16, stream);
+      case CL_DENSE_INT4:
+        return h.mask == CL_MASK_2_4 ? launch_rows_kind<K_INT4_24>(r, L.Npad, bf16, stream)
+                                     : launch_rows_kind<K_INT4>(r, L.Npad, bf16, stream);
+      default: return launch_rows_kind<K_INT8>(r, L.Npad, bf16, stream);
+    }
+  }
+
   DecodeArgs a = {};
   a.dense = reinterpret_cast<const uint4*>(L.dense);
   a.meta = L.meta;
@@ -138,7 +226,7 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
   a.K = h.K;
   a.N = h.N;
   a.M = M;
-  a.ldx = (x == L.xprep) ? L.Kx : h.K;
+  a.ldx = ldx;
   a.chunks = h.chunks;
   a.span = h.span;
   a.split = L.split;
@@ -148,78 +236,6 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
   a.group = h.group > 0 ? h.group : 1;
   a.lr_kind = h.lr;
   a.Npad = L.Npad;
-  const bool bf16 = h.x_dtype == CL_ACT_BF16;
-  // M <= 4: row-wise kernel (bandwidth bound) when its staged activations fit
-  // in LDS; the bitmap format always uses the tile kernel (its kept values are
-  // consumed per row at a varying rate)
-  if (M <= 4 && h.mask != CL_MASK_BITMAP) {
-    RowArgs r = {};
-    r.dense = a.dense;
-    r.meta = a.meta;
-    r.table = a.table;
-    r.rowptr = a.rowptr;
-    r.col = a.col;
-    r.val = a.val;
-    r.R = a.R;
-    r.Rscale = a.Rscale;
-    r.t = a.t;
-    r.x = x;
-    r.y = y;
-    r.K = a.K;
-    r.N = a.N;
-    r.M = M;
-    r.ldx = a.ldx;
-    r.chunks = a.chunks;
-    r.rank = h.lr != CL_LR_NONE ? a.rank : 0;
-    r.group = a.group;
-    r.lr_kind = a.lr_kind;
-    r.Npad = L.Npad;
-    r.nnz = (int)h.nnz;
-    bool fits = false;
-    switch (h.dense) {
-      case CL_DENSE_LUT3: fits = rows_fit<K_LUT3>(r); break;
-      case CL_DENSE_LUT4: fits = rows_fit<K_LUT4>(r); break;
-      case CL_DENSE_INT4: fits = h.mask == CL_MASK_2_4 ? rows_fit<K_INT4_24>(r) : rows_fit<K_INT4>(r); break;
-      default: fits = rows_fit<K_INT8>(r); break;
-    }
-    if (fits && h.lr != CL_LR_NONE) {
-      if (L.lr_mode >= 0) {
-        // the prologue runs as this launch's first workgroups
-        r.lrp = lowrank_split_args(L, M, x);
-        const uint32_t epoch = ++L.lr_epoch;
-        r.lrp.flag = L.lr_cnt + 65;
-        r.lrp.epoch = epoch;
-        r.lr_ntj = L.lr_rpad / 64;
-        r.lr_wgs = L.lr_S * r.lr_ntj * (int)ceil_div(M, lowrank_tile_m(M));
-        r.lr_mode = L.lr_mode;
-        r.lr_flag = r.lrp.flag;
-        r.lr_epoch = epoch;
-      } else {
-        const hipError_t e = launch_lowrank_prologue(L, M, x, stream);
-        if (e != hipSuccess) return e;
-      }
-    }
-    if (fits) switch (h.dense) {
-      case CL_DENSE_LUT3:
-        if (rows_fit<K_LUT3>(r)) return launch_rows_kind<K_LUT3>(r, L.Npad, bf16, stream);
-        break;
-      case CL_DENSE_LUT4:
-        if (rows_fit<K_LUT4>(r)) return launch_rows_kind<K_LUT4>(r, L.Npad, bf16, stream);
-        break;
-      case CL_DENSE_INT4:
-        if (h.mask == CL_MASK_2_4) {
-          if (rows_fit<K_INT4_24>(r)) return launch_rows_kind<K_INT4_24>(r, L.Npad, bf16, stream);
-        } else if (rows_fit<K_INT4>(r)) {
-          return launch_rows_kind<K_INT4>(r, L.Npad, bf16, stream);
-        }
-        break;
-      default:
-        if (rows_fit<K_INT8>(r)) return launch_rows_kind<K_INT8>(r, L.Npad, bf16, stream);
-        break;
-    }
-  }
-  // batches the row-wise kernel cannot stage: the matrix-core kernel where it applies
-  if (variant == 0 && L.mf_S > 0) return launch_decode_mfma(L, M, x_raw, y, stream);
   if (h.lr != CL_LR_NONE) {
     const hipError_t e = launch_lowrank_prologue(L, M, x, stream);
     if (e != hipSuccess) return e;

@@ -37,8 +37,8 @@
 // a kernel before it; the workgroups of the last K slice, dispatched last, add
 // the rank term and wait for the epoch first.  The slices' partial sums meet
 // through device-scope stores, and the last workgroup of a tile adds them in
-// slice order (deterministic, no float atomics).  With an activation clamp the
-// activations are clamped while they are staged.
+// slice order (deterministic, no float atomics).  With an activation clamp or
+// per-channel activation factors the activations are edited while they are staged.
 //
 // Weights enter the matrix cores as 16-bit values of the activation type: fp16
 // LUT values exactly for fp16 activations, rounded to nearest-even bf16 for
@@ -78,6 +78,7 @@ struct MfArgs {
   float* y;
   int clamp;                    // clamp the activations to [-cval, cval] while staging them
   float cval;
+  const uint16_t* xscale;       // then multiply them by these per-channel factors ([K] fp16; NULL: none)
   // low-rank prologue in this launch: workgroups [0, lr_wgs) run the split
   // prologue block (activation tiles of 4 rows, lr_mode 0 or 1) and publish
   // lrp.epoch in *lrp.flag; lr_wgs = 0: t was computed by an earlier kernel
@@ -191,8 +192,8 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   if (a.lr_wgs > 0 && (int)blockIdx.x < a.lr_wgs) {  // a prologue workgroup
     const int b = blockIdx.x, S = a.lrp.S, s = b % S, tj = (b / S) % a.lr_ntj, tm = b / (S * a.lr_ntj);
     uint8_t* smem = reinterpret_cast<uint8_t*>(sdyn);
-    if (a.lr_mode == 0) lr_split_block<0, kMfLrTile, BF16>(a.lrp, s, tj, tm, a.lr_ntj, smem);
-    else lr_split_block<1, kMfLrTile, BF16>(a.lrp, s, tj, tm, a.lr_ntj, smem);
+    if (a.lr_mode == 0) lr_split_block<0, kMfLrTile, BF16, true>(a.lrp, s, tj, tm, a.lr_ntj, smem);
+    else lr_split_block<1, kMfLrTile, BF16, true>(a.lrp, s, tj, tm, a.lr_ntj, smem);
     return;
   }
   const int bid = (int)blockIdx.x - a.lr_wgs;
@@ -234,6 +235,22 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
     const int s = i * 256 + tid, m = s / slots_row, c = s - m * slots_row, k = k0 + 8 * c;
     const bool ok = m < a.M && k < a.ldx;
     xs[i] = bload128(rx, ok ? ((uint32_t)m * (uint32_t)a.ldx + (uint32_t)k) * 2u : kNoLoad, 0);
+  }
+  if (a.xscale) {
+    // clamped and scaled before the code stream is issued (one exposed load
+    // latency), so that the factors hold no registers while it is in flight
+    const brsrc_t rf = make_rsrc(a.xscale, (uint32_t)a.ldx * 2u);
+    uint4 xf[XR];
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const int s = i * 256 + tid, m = s / slots_row, c = s - m * slots_row, k = k0 + 8 * c;
+      xf[i] = bload128(rf, m < a.M && k < a.ldx ? (uint32_t)k * 2u : kNoLoad, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      if (a.clamp) xs[i] = clamp_act8<BF16>(xs[i], a.cval);
+      xs[i] = scale_act8<BF16>(xs[i], xf[i]);
+    }
   }
 
   __builtin_amdgcn_sched_barrier(0);
@@ -287,7 +304,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   }
 
   // ---- LDS: activation slice (rows M..MT-1 zero) plus a zero row MT, tables ----
-  if (a.clamp) {
+  if (a.clamp && !a.xscale) {
 #pragma unroll
     for (int i = 0; i < XR; ++i) xs[i] = clamp_act8<BF16>(xs[i], a.cval);
   }

@@ -20,7 +20,12 @@
 // The activations are staged once per workgroup in LDS (chunk c of row m at
 // c * XS bytes, XS the chunk's activation bytes padded so that eight lanes'
 // 16-byte reads fall in distinct banks), which keeps them out of the registers
-// and lets the outlier gather read LDS instead of memory.  The row tables are
+// and lets the outlier gather read LDS instead of memory.  At batch 1 the
+// kernel also takes raw activations of a layer that clamps them ("Compressing
+// Large Language Models by Joint Sparsification and Quantization", Approach)
+// or scales some channels ("SLiM" page, rebuttal section "Output Error
+// Minimization in SLiM-Quant") and edits them on their way to LDS, which saves
+// a prep kernel's launch.  The row tables are
 // the kernel's only static LDS array, at address 0, so the table addresses
 // built from the packed bytes are absolute.
 //
@@ -67,6 +72,11 @@ struct RowArgs {
   int lr_wgs, lr_ntj, lr_mode;
   const uint32_t* lr_flag;
   uint32_t lr_epoch;
+  // raw activations (ldx = K): clamp them to [-cval, cval] and multiply them by
+  // the per-channel factors xscale ([K] fp16; NULL: none) while staging them
+  int clamp;
+  float cval;
+  const uint16_t* xscale;
 };
 
 // LDS bytes per chunk of staged activations: the chunk's 2 * span bytes padded
@@ -123,7 +133,7 @@ __device__ __forceinline__ uint4 lds_u128(const uint32_t* lds, uint32_t byte_add
 // XR = activation slots staged per thread, LR = the layer has a low-rank part
 // (a template parameter so that layers without one carry no conditional loads,
 // which would make the compiler's load counting conservative).
-template <int KIND, int MB, bool BF16, int R, int NB, int XR, bool LR>
+template <int KIND, int MB, bool BF16, int R, int NB, int XR, bool LR, bool EDIT>
 __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   constexpr int SPAN = KindTraits<KIND>::span, P = KindTraits<KIND>::pairs, XD = SPAN / 8;  // 16-byte x slots per chunk
   constexpr int XS = RowX<KIND>::stride, XSL = RowX<KIND>::slots;
@@ -136,8 +146,8 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
     if ((int)blockIdx.x < a.lr_wgs) {  // a prologue workgroup; MB is its activation tile
       const int b = blockIdx.x, S = a.lrp.S, s = b % S, tj = (b / S) % a.lr_ntj, tm = b / (S * a.lr_ntj);
       uint8_t* smem = reinterpret_cast<uint8_t*>(sdyn);
-      if (a.lr_mode == 0) lr_split_block<0, MB, BF16>(a.lrp, s, tj, tm, a.lr_ntj, smem);
-      else lr_split_block<1, MB, BF16>(a.lrp, s, tj, tm, a.lr_ntj, smem);
+      if (a.lr_mode == 0) lr_split_block<0, MB, BF16, EDIT>(a.lrp, s, tj, tm, a.lr_ntj, smem);
+      else lr_split_block<1, MB, BF16, EDIT>(a.lrp, s, tj, tm, a.lr_ntj, smem);
       return;
     }
   }
@@ -192,16 +202,27 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   const int SM = a.npass * 64 * XSL;  // slots per activation row
   const int xslots = MB * SM;
   const brsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.ldx * 2u);
-  auto x_src = [&](int s) -> uint32_t {
+  // byte offset of slot s in x (kNoLoad for a zero slot); fac: of its factors instead
+  auto x_src = [&](int s, bool fac = false) -> uint32_t {
     int m = 0;
     if constexpr (MB > 1) m = (s >= SM) + (MB > 2 ? (s >= 2 * SM) + (s >= 3 * SM) : 0);
     const int rem = s - m * SM, c = rem / XSL, d = rem - c * XSL, k = c * SPAN + 8 * d;
     const bool ok = s < xslots && d < XD && m < a.M && k < a.ldx;  // ldx: a multiple of 8, zero past K
-    return ok ? ((uint32_t)m * (uint32_t)a.ldx + (uint32_t)k) * 2u : kNoLoad;
+    return ok ? (fac ? (uint32_t)k * 2u : ((uint32_t)m * (uint32_t)a.ldx + (uint32_t)k) * 2u) : kNoLoad;
   };
   uint4 xs[XR];
 #pragma unroll
   for (int i = 0; i < XR; ++i) xs[i] = bload128(rx, x_src(i * 256 + tid), 0);
+  // EDIT: raw activations; their per-channel factors load beside them and both
+  // are consumed where the activations go to LDS, after the code stream is
+  // issued (measured faster than editing them before it, which exposes one
+  // load latency, and than a prep kernel of its own)
+  uint4 xf[EDIT ? XR : 1];
+  if constexpr (EDIT) {
+    const brsrc_t rf = make_rsrc(a.xscale, a.xscale ? (uint32_t)a.ldx * 2u : 0u);
+#pragma unroll
+    for (int i = 0; i < XR; ++i) xf[i] = a.xscale ? bload128(rf, x_src(i * 256 + tid, true), 0) : make_uint4(0, 0, 0, 0);
+  }
 
   // ---- the code stream: blocks of NB passes, two in flight ----
   const int nblk = (a.npass + NB - 1) / NB;
@@ -264,13 +285,21 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   }
 
   // ---- LDS: activations, t, tables ----
+  if constexpr (EDIT) {
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      if (a.clamp) xs[i] = clamp_act8<BF16>(xs[i], a.cval);
+      if (a.xscale) xs[i] = scale_act8<BF16>(xs[i], xf[i]);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < XR; ++i) {
     const int s = i * 256 + tid;
     if (s < xslots) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(sdyn) + a.lds_x + s * 16) = xs[i];
   }
   // activation blocks larger than one round of XR slots per thread: further
-  // rounds, loaded after the code stream is in flight (their wait covers it)
+  // rounds, loaded after the code stream is in flight (their wait covers it);
+  // never with edits (the host sends such blocks through the prep kernel)
   for (int base = XR * 256; base < xslots; base += XR * 256) {
 #pragma unroll
     for (int i = 0; i < XR; ++i) xs[i] = bload128(rx, x_src(base + i * 256 + tid), 0);
@@ -420,16 +449,28 @@ inline int rows_lds_layout(RowArgs& a) {
 
 // Passes per block: one when a row takes at most two passes (both blocks then
 // hold real chunks), else two.
-template <int KIND, int MB, bool BF16, int R, int XR>
-static void launch_rows_xr(const RowArgs& a, int grid, int lds, hipStream_t st) {
+template <int KIND, int MB, bool BF16, int R, int XR, bool EDIT>
+static void launch_rows_xe(const RowArgs& a, int grid, int lds, hipStream_t st) {
   const bool lr = a.lr_kind != CL_LR_NONE;
   if (a.npass <= 2) {
-    if (lr) hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 1, XR, true>), dim3(grid), dim3(256), lds, st, a);
-    else hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 1, XR, false>), dim3(grid), dim3(256), lds, st, a);
+    if (lr) hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 1, XR, true, EDIT>), dim3(grid), dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 1, XR, false, EDIT>), dim3(grid), dim3(256), lds, st, a);
   } else {
-    if (lr) hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, XR, true>), dim3(grid), dim3(256), lds, st, a);
-    else hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, XR, false>), dim3(grid), dim3(256), lds, st, a);
+    if (lr) hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, XR, true, EDIT>), dim3(grid), dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((decode_rows_kernel<KIND, MB, BF16, R, 2, XR, false, EDIT>), dim3(grid), dim3(256), lds, st, a);
   }
+}
+
+// Kernels that edit raw activations (clamp, per-channel factors) while staging
+// them exist for one activation row only (the batch-1 forward, where a prep
+// kernel of their own would cost a launch of its own); other batches read
+// edited activations.
+template <int KIND, int MB, bool BF16, int R, int XR>
+static void launch_rows_xr(const RowArgs& a, int grid, int lds, hipStream_t st) {
+  if constexpr (MB == 1) {
+    if (a.clamp || a.xscale) return launch_rows_xe<KIND, MB, BF16, R, XR, true>(a, grid, lds, st);
+  }
+  launch_rows_xe<KIND, MB, BF16, R, XR, false>(a, grid, lds, st);
 }
 
 // One activation row: the first staging round is sized to the activation block
@@ -441,6 +482,8 @@ static hipError_t launch_rows_t(RowArgs a, int Npad, hipStream_t st) {
     return hipErrorInvalidConfiguration;
   const int grid = (Npad + 4 * R - 1) / (4 * R) + a.lr_wgs;  // prologue workgroups first
   const int per_thread = (MB * a.npass * 64 * RowX<KIND>::slots + 255) / 256;
+  // raw activations are edited in the first staging round only, at batch 1
+  if ((a.clamp || a.xscale) && (MB != 1 || per_thread > row_x_rounds<MB>())) return hipErrorInvalidValue;
   if constexpr (MB == 1) {
     if (per_thread <= 2)
       launch_rows_xr<KIND, MB, BF16, R, 2>(a, grid, lds, st);
@@ -454,11 +497,17 @@ static hipError_t launch_rows_t(RowArgs a, int Npad, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Whether the row-wise kernel takes this shape (its staged activations fit in LDS).
+// Whether the row-wise kernel takes this shape (its staged activations fit in
+// LDS) and, in *one_round, whether it can edit raw activations: one activation
+// row whose first staging round holds the whole block.
 template <int KIND>
-bool rows_fit(RowArgs a) {
+bool rows_fit(RowArgs a, bool* one_round = nullptr) {
   const int mb = a.M <= 1 ? 1 : a.M <= 2 ? 2 : 4;
   const int lds = mb == 1 ? rows_lds_layout<KIND, 1>(a) : mb == 2 ? rows_lds_layout<KIND, 2>(a) : rows_lds_layout<KIND, 4>(a);
+  if (one_round) {  // edits: batch 1 only
+    const int per_thread = (a.npass * 64 * RowX<KIND>::slots + 255) / 256;
+    *one_round = mb == 1 && per_thread <= row_x_rounds<1>();
+  }
   return lds <= kRowsMaxLds && a.rank <= 256;
 }
 

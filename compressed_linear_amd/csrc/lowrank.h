@@ -37,9 +37,11 @@ struct LrSplitArgs {
   uint32_t* flag;
   uint32_t epoch;
   int ntiles;
-  // clamp x to [-cval, cval] while staging it (activations not clamped beforehand)
+  // clamp x to [-cval, cval] and multiply it by the per-channel factors
+  // xscale ([K] fp16, NULL: none) while staging it (raw activations only)
   int clamp;
   float cval;
+  const uint16_t* xscale;
 };
 
 // Activation editor of "Compressing Large Language Models by Joint
@@ -62,6 +64,38 @@ __device__ __forceinline__ uint4 clamp_act8(uint4 v, float c) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       u[i] = as_u32(__builtin_elementwise_min(__builtin_elementwise_max(as_h2(u[i]), lc), hc));
+  }
+  return make_uint4(u[0], u[1], u[2], u[3]);
+}
+
+// fp32 -> bf16, nearest with ties to even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Per-channel activation factors of SLiM's output-error variant ("SLiM" page,
+// rebuttal section "Output Error Minimization in SLiM-Quant": the activations
+// of the salient channels are divided by alpha; the layer stores f = 1/alpha,
+// 1 elsewhere), applied to eight staged 16-bit activations with their eight
+// fp16 factors.  The product is rounded once to the activation type, nearest
+// with ties to even: an fp16 multiply does exactly that; for bf16 the product
+// of a bf16 and an fp16 value is exact in fp32 (8 + 11 significant bits) and
+// is rounded from there.
+template <bool BF16>
+__device__ __forceinline__ uint4 scale_act8(uint4 v, uint4 f) {
+  uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t g[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (BF16) {
+      const float lo = __uint_as_float(u[i] << 16) * (float)__builtin_bit_cast(_Float16, (uint16_t)(g[i] & 0xFFFFu));
+      const float hi = __uint_as_float(u[i] & 0xFFFF0000u) * (float)__builtin_bit_cast(_Float16, (uint16_t)(g[i] >> 16));
+      u[i] = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    } else {
+      u[i] = as_u32(as_h2(u[i]) * as_h2(g[i]));
+    }
   }
   return make_uint4(u[0], u[1], u[2], u[3]);
 }
@@ -107,7 +141,9 @@ inline int lr_scratch_bytes(int mode, int mt) {
 
 // One workgroup (256 threads) of the split prologue: K slice s, column tile tj
 // of ntj, activation tile tm; `smem` is LrScratch<MODE, MT>::bytes of LDS.
-template <int MODE, int MT, bool BF16>
+// EDIT: the activations may be raw (a.clamp, a.xscale apply); else they are
+// edited already.
+template <int MODE, int MT, bool BF16, bool EDIT>
 __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int tj, int tm, int ntj, uint8_t* smem) {
   using SC = LrScratch<MODE, MT>;
   constexpr int NL = MODE == 0 ? 16 : 4;        // 16-byte loads per thread
@@ -132,6 +168,11 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
     const int m = tid >> 6, k = k0 + 8 * (tid & 63);
     const bool ok = m0 + m < a.M && k < a.ldx;
     xv = bload128(rx, ok ? ((uint32_t)(m0 + m) * (uint32_t)a.ldx + (uint32_t)k) * 2u : kNoLoad, 0);
+  }
+  uint4 xf = make_uint4(0, 0, 0, 0);
+  if (EDIT && a.xscale && tid < MT * 64) {
+    const int k = k0 + 8 * (tid & 63);
+    xf = bload128(make_rsrc(a.xscale, (uint32_t)a.ldx * 2u), k < a.ldx ? (uint32_t)k * 2u : kNoLoad, 0);
   }
   // the slice of L
   const brsrc_t rl = make_rsrc(a.lk, MODE == 0 ? (uint32_t)a.Kl * (uint32_t)a.rpad * 2u : (uint32_t)a.Kl / 2u * (uint32_t)a.rpad);
@@ -158,7 +199,10 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
       }
     }
   }
-  if (a.clamp) xv = clamp_act8<BF16>(xv, a.cval);
+  if constexpr (EDIT) {
+    if (a.clamp) xv = clamp_act8<BF16>(xv, a.cval);
+    if (a.xscale) xv = scale_act8<BF16>(xv, xf);
+  }
   if (tid < MT * 64) *reinterpret_cast<uint4*>(&xs[tid >> 6][8 * (tid & 63)]) = xv;
   __syncthreads();
 

@@ -25,12 +25,12 @@ def say(*a):
 SMALL = {1: (1210, 200), 2: (1000, 150), 3: (768, 130), 4: (1280, 140), 5: (1450, 190)}
 
 
-def _identity_layer(K, x_dtype, clamp, seed):
+def _identity_layer(K, x_dtype, clamp, seed, scaled=True):
     # int8 q = I, scale 1: y[m, n] = x''[m, n] for n < K
     q = np.eye(K, dtype=np.int8)
     lay = LogicalLayer(K=K, N=K, dense="int8", qvals=q, row_scale=np.ones(K, np.float16), x_dtype=x_dtype,
                        act_clamp=None if clamp is None else np.float16(clamp))
-    return with_act_scale(lay, seed=seed, frac=0.3)
+    return with_act_scale(lay, seed=seed, frac=0.3) if scaled else lay
 
 
 def _x_rounding(M, K, x_dtype, seed):
@@ -43,20 +43,23 @@ def _x_rounding(M, K, x_dtype, seed):
     return bf16_bits_from_f32(v.astype(np.float32))
 
 
+# K = 264: the row-wise kernel (batch 1) and the matrix-core decode kernel edit
+# raw activations while staging them; K = 262 (rows not 16-byte aligned) and
+# the batch-3 row-wise kernel read them from the prep kernel; so does prefill
 @pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("clamp", [None, 6.0])
-@pytest.mark.parametrize("path,M", [("decode", 1), ("decode_valu", 3), ("decode_mfma", 8), ("prefill", 40)])
-def test_scaled_activations_bit_exact(x_dtype, clamp, path, M):
-    K = 264
-    layer = _identity_layer(K, x_dtype, clamp, seed=1)
+@pytest.mark.parametrize("clamp,scaled", [(None, True), (6.0, True), (6.0, False)])
+@pytest.mark.parametrize("path,M,K", [("decode", 1, 264), ("decode", 1, 262), ("decode_valu", 3, 264),
+                                      ("decode_mfma", 8, 264), ("decode_mfma", 2, 262), ("prefill", 40, 264)])
+def test_scaled_activations_bit_exact(x_dtype, clamp, scaled, path, M, K):
+    layer = _identity_layer(K, x_dtype, clamp, seed=1, scaled=scaled)
     x = _x_rounding(M, K, x_dtype, seed=2)
-    say("identity", x_dtype, clamp, path, M)
+    say("identity", x_dtype, clamp, scaled, path, M, K)
     y = gpu_forward(layer, x, path=path, mod=None)
     xpp = oracle.activations(layer, x)
     assert np.array_equal(y, xpp), f"{int((y != xpp).sum())} activations differ"
-    # the scaling changed many of them, and some by a rounding
-    raw = oracle.activations(layer.with_(xscale_ch=None, xscale=None), x)
-    assert (xpp != raw).sum() > M * len(layer.xscale_ch) // 2
+    if scaled:  # the scaling changed many of them, and some by a rounding
+        raw = oracle.activations(layer.with_(xscale_ch=None, xscale=None), x)
+        assert (xpp != raw).sum() > M * len(layer.xscale_ch) // 2
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
@@ -70,6 +73,20 @@ def test_scaled_forward_all_paths(cfg):
         say("scaled", layer.name, path, "M", M)
         y = gpu_forward(layer, x, path=path)
         check_bound(y, layer, x, what=f"{layer.name} {path} M={M}")
+
+
+@pytest.mark.parametrize("cfg,K,N", [(1, 1216, 200), (5, 1456, 190), (3, 768, 130), (1, 16400, 70)])
+def test_scaled_batch1_in_kernel_and_long_rows(cfg, K, N):
+    # K a multiple of 8: batch 1 edits in the row-wise kernel (with the fused
+    # low-rank prologue for workload 5 and 3); K = 16400 takes more than one
+    # staging round, so its activations come from the prep kernel
+    li = 1 if cfg == 3 else 0
+    layer = with_act_scale(make_layer(cfg, li, K=K, N=N), seed=11, frac=0.02)
+    for M in (1, 2):
+        x = make_x(cfg, li, M, K=K)
+        say("scaled batch", layer.name, "M", M)
+        y = gpu_forward(layer, x, path="decode")
+        check_bound(y, layer, x, what=f"{layer.name} M={M}")
 
 
 def test_scaled_layer_full_size_sampled_rows():
