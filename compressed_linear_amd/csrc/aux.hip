@@ -18,36 +18,43 @@ namespace cl {
 // (at most 11 + 11 significant bits, f a normal fp16 <= 1) and is rounded once,
 // to nearest-even, to the activation type.
 // ---------------------------------------------------------------------------
+// One thread per eight consecutive channels of one row (grid: K groups x M rows);
+// rows of 16-byte loads when K is a multiple of 8, element loads otherwise.
 template <bool BF16>
-__global__ void prep_x_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ xp, int M, int K, int Kx,
-                              int has_clamp, float c, const uint16_t* __restrict__ xs) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t total = (size_t)M * Kx;
-  if (i >= total) return;
-  const int m = (int)(i / Kx), k = (int)(i % Kx);
-  uint16_t v = 0;
-  if (k < K) {
-    v = x[(size_t)m * K + k];
-    if (has_clamp || xs) {
-      float f = BF16 ? __uint_as_float((uint32_t)v << 16) : (float)__builtin_bit_cast(_Float16, v);
-      if (has_clamp) f = fminf(fmaxf(f, -c), c);  // +-c is exact in the activation type (checked by the packer)
-      if (xs) f *= (float)__builtin_bit_cast(_Float16, xs[k]);
-      v = BF16 ? (uint16_t)f32_to_bf16_rne(f) : __builtin_bit_cast(uint16_t, (_Float16)f);
+__global__ void __launch_bounds__(256) prep_x_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ xp, int K,
+                                                     int Kx, int has_clamp, float c, const uint16_t* __restrict__ xs) {
+  const int m = blockIdx.y, k = ((int)blockIdx.x * 256 + (int)threadIdx.x) * 8;
+  if (k >= Kx) return;
+  const uint16_t* xr = x + (size_t)m * K;
+  uint4 v, f = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+  if ((K & 7) == 0) {  // Kx == K: k + 8 <= K, 16-byte aligned rows
+    v = *reinterpret_cast<const uint4*>(xr + k);
+    if (xs) f = *reinterpret_cast<const uint4*>(xs + k);
+  } else {
+    uint32_t e[4], g[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k0 = k + 2 * j, k1 = k0 + 1;
+      e[j] = (k0 < K ? (uint32_t)xr[k0] : 0u) | ((k1 < K ? (uint32_t)xr[k1] : 0u) << 16);
+      g[j] = (xs && k0 < K ? (uint32_t)xs[k0] : 0x3C00u) | ((xs && k1 < K ? (uint32_t)xs[k1] : 0x3C00u) << 16);
     }
+    v = make_uint4(e[0], e[1], e[2], e[3]);
+    f = make_uint4(g[0], g[1], g[2], g[3]);
   }
-  xp[i] = v;
+  if (has_clamp) v = clamp_act8<BF16>(v, c);  // +-c is exact in the activation type (checked by the packer)
+  if (xs) v = scale_act8<BF16>(v, f);
+  *reinterpret_cast<uint4*>(xp + (size_t)m * Kx + k) = v;
 }
 
 hipError_t launch_prep_x(const Layer& L, int M, const void* x, hipStream_t stream) {
-  const size_t total = (size_t)M * L.Kx;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
+  const dim3 grid((unsigned)ceil_div(L.Kx / 8, 256), (unsigned)M);
   const float c = (float)__builtin_bit_cast(_Float16, L.h.act_clamp);
   if (L.h.x_dtype == CL_ACT_BF16)
-    hipLaunchKernelGGL(prep_x_kernel<true>, dim3(blocks), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(x), L.xprep, M, L.h.K, L.Kx, L.h.has_clamp, c, L.xscale);
+    hipLaunchKernelGGL(prep_x_kernel<true>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), L.xprep, L.h.K, L.Kx, L.h.has_clamp, c, L.xscale);
   else
-    hipLaunchKernelGGL(prep_x_kernel<false>, dim3(blocks), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(x), L.xprep, M, L.h.K, L.Kx, L.h.has_clamp, c, L.xscale);
+    hipLaunchKernelGGL(prep_x_kernel<false>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x), L.xprep, L.h.K, L.Kx, L.h.has_clamp, c, L.xscale);
   return hipGetLastError();
 }
 

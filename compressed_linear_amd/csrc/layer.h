@@ -44,6 +44,8 @@ struct Layer {
 
   // matrix-core prefill (built at create)
   int pf_nd = 0;                 // K steps over the packed weights
+  uint8_t* pf_dense8 = nullptr;  // bitmap layers created for prefill: dense INT8 chunk stream (zero where dropped)
+  int pf_chunks8 = 0;            // its 16-byte chunks per row
   int32_t* pf_cptr = nullptr;    // outliers per (128-row tile, step): offsets [n_tiles128][pf_nd + 1]
   uint32_t* pf_cent = nullptr;   // entries: row in tile | k in step << 7 | fp16 value << 16
   uint16_t* pf_r16 = nullptr;    // [Npad][2 rp]: R^T twice, in the MFMA input type

@@ -30,7 +30,8 @@ __global__ void __launch_bounds__(256) pf_tsplit_kernel(const float* t, size_t t
   t16[i] = (uint16_t)(v < rp ? hi : to16<BF16>(s - hif));
 }
 
-// The bitmap format has no matrix-core loader: row blocks of 32 through the decode kernels.
+// A bitmap layer created for decode batches only (no dense int8 copy): row
+// blocks of 32 through the decode kernels.
 static hipError_t prefill_by_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream) {
   const int ldx = (x == L.xprep) ? L.Kx : L.h.K;
   for (int m0 = 0; m0 < M; m0 += kMaxDecodeM) {
@@ -50,7 +51,10 @@ static hipError_t prefill_by_decode(const Layer& L, int M, const void* x, float*
 
 hipError_t launch_prefill(const Layer& L, int M, const void* x, float* y, hipStream_t stream) {
   const cl_blob_header& h = L.h;
-  if (h.mask == CL_MASK_BITMAP) return prefill_by_decode(L, M, x, y, stream);
+  // the bitmap format: the INT8 tile loader over its dense int8 copy when the
+  // layer was created for prefill batches, else the matrix-core decode in blocks
+  const bool dense8 = L.pf_dense8 != nullptr;
+  if (h.mask == CL_MASK_BITMAP && !dense8) return prefill_by_decode(L, M, x, y, stream);
   const bool bf16 = h.x_dtype == CL_ACT_BF16;
   PfArgs a = {};
   a.x = static_cast<const uint16_t*>(x);
@@ -98,10 +102,10 @@ hipError_t launch_prefill(const Layer& L, int M, const void* x, float* y, hipStr
   }
   a.N = h.N;
   a.Npad = L.Npad;
-  a.dense = reinterpret_cast<const uint4*>(L.dense);
-  a.meta = L.meta;
+  a.dense = reinterpret_cast<const uint4*>(dense8 ? L.pf_dense8 : L.dense);
+  a.meta = dense8 ? nullptr : L.meta;
   a.table = reinterpret_cast<const uint16_t*>(L.table);
-  a.chunks = h.chunks;
+  a.chunks = dense8 ? L.pf_chunks8 : h.chunks;
   a.cptr = L.pf_cptr;
   a.cent = L.pf_cent;
   a.y = y;

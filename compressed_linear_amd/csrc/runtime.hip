@@ -67,16 +67,26 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
   // them or K is not a multiple of 8
   const int Kx = (int)round_up(h.K, 8);
   if (h.has_clamp || h.n_xscale > 0 || (h.K & 7)) o_xp = take((size_t)max_M * Kx * 2);
-  // matrix-core prefill (all formats but the bitmap): outlier lists per
-  // (128-row tile, K step), R^T twice and L^T in the MFMA input type, t_hi | t_lo;
-  // R^T twice also for a bitmap layer (its decode runs on the matrix-core kernel)
-  size_t o_pfp = 0, o_pfe = 0, o_pfr = 0, o_pfl = 0, o_pft = 0;
-  int pf_nd = 0;
+  // matrix-core prefill: outlier lists per (128-row tile, K step), R^T twice
+  // and L^T in the MFMA input type, t_hi | t_lo.  A bitmap layer created for
+  // batches above the decode range runs the INT8 tile loader on a dense int8
+  // copy of its weights (zero where dropped); otherwise it keeps only R^T twice
+  // (its decode runs on the matrix-core kernel)
+  size_t o_pfp = 0, o_pfe = 0, o_pfr = 0, o_pfl = 0, o_pft = 0, o_pfd = 0;
+  int pf_nd = 0, pf_chunks8 = 0;
   const int rp = (int)round_up(h.rank, 8);
   const bool has_lr = h.lr != CL_LR_NONE && h.rank > 0;
-  if (h.mask != CL_MASK_BITMAP) {
-    const int cps = pf_step_k(h.dense, h.mask) / kind_info(h.dense, h.mask).span;
-    pf_nd = (int)ceil_div(h.chunks, cps);
+  const bool bm_prefill = h.mask == CL_MASK_BITMAP && max_M > kMaxDecodeM;
+  if (h.mask != CL_MASK_BITMAP || bm_prefill) {
+    const int pmask = bm_prefill ? CL_MASK_NONE : h.mask;
+    const int span = kind_info(h.dense, pmask).span;
+    const int chunks = bm_prefill ? (int)ceil_div(h.K, span) : h.chunks;
+    const int cps = pf_step_k(h.dense, pmask) / span;
+    pf_nd = (int)ceil_div(chunks, cps);
+    if (bm_prefill) {
+      pf_chunks8 = chunks;
+      o_pfd = take((size_t)Npad * chunks * 16);
+    }
     if (h.nnz > 0) {
       o_pfp = take((size_t)ceil_div(Npad, pf_tile_rows(h.dense)) * (pf_nd + 1) * 4);
       o_pfe = take((size_t)h.nnz * 4);
@@ -133,6 +143,8 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
     L->xprep = o_xp ? reinterpret_cast<uint16_t*>(d + o_xp) : nullptr;
     L->Kx = Kx;
     L->pf_nd = pf_nd;
+    L->pf_dense8 = o_pfd ? d + o_pfd : nullptr;
+    L->pf_chunks8 = pf_chunks8;
     L->pf_cptr = o_pfp ? reinterpret_cast<int32_t*>(d + o_pfp) : nullptr;
     L->pf_cent = o_pfe ? reinterpret_cast<uint32_t*>(d + o_pfe) : nullptr;
     L->pf_r16 = o_pfr ? reinterpret_cast<uint16_t*>(d + o_pfr) : nullptr;
@@ -370,9 +382,29 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
     }
   }
   PrefillHost pf;
-  if (h->mask != CL_MASK_BITMAP || L->pf_r16)
+  const bool bm_pf = L->pf_dense8 != nullptr;
+  if (h->mask != CL_MASK_BITMAP || bm_pf || L->pf_r16)
     build_prefill_host(*h, static_cast<const uint8_t*>(blob), L->Npad, L->pf_nd, L->pf_rp, L->pf_Kl, pf,
-                       h->mask == CL_MASK_BITMAP);
+                       h->mask == CL_MASK_BITMAP && !bm_pf);
+  // bitmap layer for prefill: the dense INT8 chunk stream (u = q + 128, 16 k per
+  // chunk, rows of pf_chunks8 chunks; 128 = zero for dropped weights and padding)
+  std::vector<uint8_t> d8;
+  if (bm_pf) {
+    d8.assign((size_t)L->Npad * L->pf_chunks8 * 16, 128u);
+    const uint8_t* b = static_cast<const uint8_t*>(blob);
+    const int32_t* off = reinterpret_cast<const int32_t*>(b + h->off[CL_SEC_NZOFF]);
+    const uint32_t* meta = reinterpret_cast<const uint32_t*>(b + h->off[CL_SEC_META]);
+    const int8_t* kept = reinterpret_cast<const int8_t*>(b + h->off[CL_SEC_DENSE]);
+    for (int n = 0; n < h->N; ++n) {
+      long long p = off[n];
+      uint8_t* row = d8.data() + (size_t)n * L->pf_chunks8 * 16;
+      for (int c = 0; c < h->chunks; ++c) {
+        const uint32_t* w = meta + ((size_t)n * h->chunks + c) * 4;
+        for (int t = 0; t < 128; ++t)
+          if ((w[t >> 5] >> (t & 31)) & 1u) row[128 * c + t] = (uint8_t)(kept[p++] + 128);
+      }
+    }
+  }
   std::vector<int32_t> mfo;
   std::vector<uint32_t> mfe;
   // bitmap, matrix-core decode: first kept byte of every (row, K slice)
@@ -407,6 +439,7 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
   if (e == hipSuccess) e = hipMemsetAsync(L->counters, 0, (size_t)(h->n_tiles + ceil_div(max_M, 32) + 8) * 4, s);
   if (e == hipSuccess && !nzs.empty())
     e = hipMemcpyAsync(L->nzstart, nzs.data(), nzs.size() * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !d8.empty()) e = hipMemcpyAsync(L->pf_dense8, d8.data(), d8.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !pf.cptr.empty())
     e = hipMemcpyAsync(L->pf_cptr, pf.cptr.data(), pf.cptr.size() * 4, hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !pf.cent.empty())

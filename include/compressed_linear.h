@@ -184,8 +184,10 @@ cl_status cl_pack(const cl_layer_desc* desc, void* blob, size_t* blob_bytes, cl_
  * workspace (split-K partial sums, counters, the low-rank intermediate
  * x' L_hat, restaged activations) and the data the matrix-core path derives
  * at create (outlier lists per 128-row tile and K step, the low-rank factors
- * in the 16-bit MFMA input type).  Returns 0 if the blob is malformed or
- * max_M < 1.
+ * in the 16-bit MFMA input type; for a bitmap layer with max_M > 32, a dense
+ * int8 copy of its weights, N*K bytes rounded up, zero where dropped, that the
+ * prefill's matrix-core tile loader reads).  Returns 0 if the blob is
+ * malformed or max_M < 1.
  */
 size_t cl_device_bytes(const void* blob, int32_t max_M);
 

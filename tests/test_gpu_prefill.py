@@ -1,8 +1,8 @@
 """The matrix-core prefill kernel against the CPU oracle, through the C ABI
 (needs an MI355X).
 
-Every format but the bitmap (whose prefill runs through the decode kernels),
-with outliers and rank terms of every factor type, fp16 and bf16 activations,
+Every format (the bitmap through a dense int8 copy built when the layer is
+created for prefill batches, or through the decode kernels otherwise), with outliers and rank terms of every factor type, fp16 and bf16 activations,
 on shapes with partial 128-row tiles in both M and N and a partial last K step;
 skewed outliers and rows holding every column as an outlier (long per-(tile,
 step) lists); a clamped layer; bitwise determinism.
@@ -104,3 +104,43 @@ def test_prefill_deterministic():
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
     check_bound(y1.astype(np.float64), layer, x, what="determinism")
     mod.close()
+
+
+@pytest.mark.parametrize("lr", ["none", "int4", "fp16"])
+def test_prefill_bitmap_dense_copy(lr):
+    # INT8 50 % bitmap + clamp (workload 4's format) on a layer created for
+    # prefill batches: the INT8 tile loader over the dense int8 copy; ragged K
+    # (not a multiple of the 128-k bitmap chunk or the 64-k step), partial tiles,
+    # full-row outliers and a rank term
+    from synth.layers import absmax_int4_groups
+    r = np.random.default_rng(41)
+    K, N = 1000, 290
+    base = make_layer(4, 0, K=K, N=N, M_for_clamp=64)
+    rp, col, val = draw_csr_skewed(r, r, N, K, density=0.01)
+    lay = base.with_(csr_row_ptr=rp, csr_col=col, csr_val=val)
+    if lr == "int4":
+        Lq, Ls = absmax_int4_groups(r.normal(0, 0.01, (K, 32)), 128)
+        Rq, Rs = absmax_int4_groups(r.normal(0, 0.01, (32, N)), 128)
+        lay = lay.with_(lr="int4", rank=32, group=128, L=Lq, R=Rq, L_scale=Ls, R_scale=Rs)
+    elif lr == "fp16":
+        lay = lay.with_(lr="fp16", rank=24, L=r.normal(0, 0.01, (K, 24)).astype(np.float16),
+                        R=r.normal(0, 0.01, (24, N)).astype(np.float16))
+    mod = gpu_layer(lay, max_M=300)
+    for M in (33, 129, 300):
+        x = make_x(4, 0, M, K=K)
+        say("bitmap prefill", lr, "M", M)
+        check_bound(gpu_forward(lay, x, path="prefill", mod=mod), lay, x, what=f"bitmap prefill {lr} M={M}")
+        # the same layer's batch-1..32 decode still runs the matrix-core decode kernel
+    x = make_x(4, 0, 16, K=K)
+    check_bound(gpu_forward(lay, x, path="auto", mod=mod), lay, x, what="bitmap decode, prefill-sized layer")
+    mod.close()
+
+
+def test_prefill_bitmap_golden_exact():
+    # the hand-derived INT8 bitmap + clamp case through the dense-copy prefill: exact
+    from golden_cases import load_golden
+    layer, x, y_exp, _ = load_golden("int8_bitmap_clamp_2x8")
+    mod = gpu_layer(layer, max_M=64)
+    y = gpu_forward(layer, x, path="prefill", mod=mod)
+    mod.close()
+    assert np.array_equal(y, y_exp), (y, y_exp)
