@@ -1,0 +1,121 @@
+"""CPU oracle of the data-free LUT packer -- TEST INFRASTRUCTURE.
+
+Only the test suite may import or run this module.  The HIP library never
+calls it and it never calls the HIP library; they share no code.
+
+What it computes, from fp16 weights W [N, K] (rows = output channels):
+
+  1. Outliers.  The n_out weights of largest magnitude leave the dense part
+     for a full-precision CSR matrix; among equal magnitudes the one with the
+     smaller row-major index goes first.
+  2. Per-row k-means.  The remaining weights of each row are clustered into
+     2^b centroids by Lloyd's iterations in one dimension, starting from 2^b
+     points spread evenly over [min, max] of the row:
+         c_j = min + (max - min) (2j + 1) / 2^(b+1)
+     A weight belongs to the nearest centroid (the lower one on a tie, i.e.
+     to cluster j when it equals the midpoint of c_j and c_(j+1)); a centroid
+     becomes the mean of its weights, and keeps its value when it has none.
+     Iterations stop when no centroid changes, or after max_iter.
+  3. Codes.  The LUT is the centroids rounded to fp16 (nearest, ties to even);
+     every dense weight takes the code of its nearest LUT value (lower code on
+     a tie).  An outlier's position takes the code nearest to 0 and its CSR
+     value is fp16(w - lut[that code]), so that D + S reproduces it.
+
+Sources, by page (title, then section):
+  * "SqueezeLLM: Dense-and-Sparse Quantization" -- Approach: non-uniform LUT
+    quantization whose centroids come from k-means over each output channel's
+    weights, with outliers (and sensitive weights) kept apart in a
+    full-precision CSR matrix, 0.45 % in total.  Measured-effects table: the
+    sensitivity-agnostic clustering (plain k-means) is one of the ablations.
+    The Fisher weighting itself needs gradients and data and is not here.
+
+Readings where the page is silent (each one also listed with the design
+notes): outliers by magnitude over the whole layer; the evenly spaced
+initialisation, the tie rules and the stopping rule above; an outlier's dense
+code.  Arithmetic: weights are fp16, so every sum of them is an exact integer
+multiple of 2^-24; the sums are kept as such integers (exact in any order, for
+|w| < 8192 and K <= 65536), a centroid is that sum over the count in fp64 (one
+rounding), boundaries are (c_j + c_(j+1)) / 2 in fp64, and every comparison is
+exact.  The fp64 -> fp16 rounding follows the format's definition.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+FIX = float(1 << 24)  # fp16 values are integer multiples of 2^-24
+
+
+def round_to_f16(v) -> np.ndarray:
+    """Nearest fp16 value (ties to even) of fp64 values inside the fp16 range,
+    from the definition: spacing 2^(e - 10), e the exponent (>= -14)."""
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    e = np.maximum(e - 1, -14)
+    sp = np.ldexp(1.0, e - 10)
+    return np.rint(v / sp) * sp
+
+
+def select_outliers(W, n_out: int) -> np.ndarray:
+    """Boolean mask [N, K] of the n_out largest |w|, ties to the lower row-major index."""
+    a = np.abs(np.asarray(W, dtype=np.float16).astype(np.float64)).ravel()
+    order = np.lexsort((np.arange(a.size), -a))  # by -|w|, then by index
+    mask = np.zeros(a.size, dtype=bool)
+    mask[order[:n_out]] = True
+    return mask.reshape(np.asarray(W).shape)
+
+
+def kmeans_row(v16, k: int, max_iter: int):
+    """Lloyd's iterations on one row's dense weights (fp16 array); returns the fp64 centroids."""
+    v = np.asarray(v16, dtype=np.float16).astype(np.float64)
+    if v.size == 0:
+        return np.zeros(k)
+    q = np.rint(v * FIX).astype(np.int64)          # exact integers
+    mn, mx = v.min(), v.max()
+    c = mn + ((mx - mn) * (2 * np.arange(k) + 1)) / (2 * k)
+    for _ in range(max_iter):
+        b = (c[:-1] + c[1:]) * 0.5                 # boundaries
+        idx = np.searchsorted(b, v, side="left")   # number of boundaries < v
+        sums = np.zeros(k, dtype=np.int64)
+        np.add.at(sums, idx, q)
+        cnt = np.bincount(idx, minlength=k)
+        new = c.copy()
+        nz = cnt > 0
+        new[nz] = (sums[nz].astype(np.float64) / cnt[nz]) / FIX
+        if np.array_equal(new, c):
+            break
+        c = new
+    return c
+
+
+def nearest_code(v, lut16) -> np.ndarray:
+    """Code of the nearest LUT value (lower code on a tie); lut16 sorted ascending."""
+    l = np.asarray(lut16, dtype=np.float16).astype(np.float64)
+    b = (l[:-1] + l[1:]) * 0.5
+    return np.searchsorted(b, np.asarray(v, dtype=np.float64), side="left").astype(np.uint8)
+
+
+def fit_lut(W, bits: int, n_out: int, max_iter: int):
+    """codes uint8 [N, K], lut fp16 [N, 2^b], CSR (row_ptr int32 [N+1], col int32, val fp16)."""
+    W16 = np.asarray(W, dtype=np.float16)
+    N, K = W16.shape
+    k = 1 << bits
+    out = select_outliers(W16, n_out)
+    codes = np.zeros((N, K), dtype=np.uint8)
+    lut = np.zeros((N, k), dtype=np.float16)
+    rows, cols, vals = [], [], []
+    for n in range(N):
+        dense = ~out[n]
+        c = kmeans_row(W16[n, dense], k, max_iter)
+        l16 = round_to_f16(c).astype(np.float16)
+        lut[n] = l16
+        w = W16[n].astype(np.float64)
+        codes[n] = nearest_code(np.where(dense, w, 0.0), l16)
+        oc = np.flatnonzero(out[n])
+        for j in oc:
+            rows.append(n)
+            cols.append(j)
+            vals.append(round_to_f16(w[j] - float(l16[codes[n, j]])))
+    row_ptr = np.zeros(N + 1, dtype=np.int32)
+    np.cumsum(np.bincount(np.asarray(rows, dtype=np.int64), minlength=N), out=row_ptr[1:])
+    return (codes, lut, row_ptr, np.asarray(cols, dtype=np.int32),
+            np.asarray(vals, dtype=np.float64).astype(np.float16))

@@ -1,0 +1,147 @@
+"""Pins of the packer oracle (oracle/fit_oracle.py) against facts that do not
+come from it: hand-derived examples, brute force, the fixed-point property of
+Lloyd's iterations, scikit-learn's k-means and numpy's fp16 cast.  Each pin
+takes the oracle module as an argument so that the mutation tests can run
+them against broken copies."""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _rng(s):
+    return np.random.default_rng(s)
+
+
+def pin_worked_example(F):
+    # SqueezeLLM page, Approach (per-channel centroids; outliers to CSR).
+    # Row 0: 0..7 and 100.  100 is the one outlier; the dense values start from
+    # c_j = 7 (2j + 1) / 16 = 0.4375, 1.3125, ..., 6.5625 with midpoints
+    # 0.875, 1.75, ..., 6.125, so value j joins cluster j and c_j = j: LUT 0..7,
+    # codes = values, the outlier takes the code nearest to 0 (code 0, value 0)
+    # and its CSR value is 100 - 0 = 100.
+    # Row 1: -4, -4, 0, 4, 4 x2: k = 8 from [-4, 4]: c_j = -4 + 8 (2j+1) / 16 =
+    # -3.5, -2.5, ..., 3.5; -4 -> 0, 0 sits on the midpoint of c_3 = -0.5 and
+    # c_4 = 0.5 -> cluster 3 (lower); 4 -> 7.  Means: c_0 = -4, c_3 = 0, c_7 = 4,
+    # the others keep their values; next round: same assignment, stop.
+    W = np.array([[0, 1, 2, 3, 4, 5, 6, 7, 100],
+                  [-4, -4, 0, 4, 4, 4, 4, 4, 4]], np.float16)
+    codes, lut, rp, col, val = F.fit_lut(W, 3, 1, 50)
+    assert np.array_equal(lut[0].astype(np.float64), np.arange(8.0)), lut[0]
+    assert np.array_equal(codes[0], [0, 1, 2, 3, 4, 5, 6, 7, 0])
+    assert list(rp) == [0, 1, 1] and list(col) == [8] and float(val[0]) == 100.0
+    assert np.array_equal(lut[1].astype(np.float64), [-4, -2.5, -1.5, 0, 0.5, 1.5, 2.5, 4])
+    assert np.array_equal(codes[1], [0, 0, 3, 7, 7, 7, 7, 7, 7])
+
+
+def pin_round_f16_library(F):
+    r = _rng(61)
+    v = r.normal(0, 1, 5000) * np.exp2(r.integers(-26, 14, 5000))
+    h = r.integers(1, 0x7BFE, 3000).astype(np.uint16)
+    mid = (h.view(np.float16).astype(np.float64) + (h + 1).view(np.float16).astype(np.float64)) / 2
+    for x in (v, mid, -mid):
+        assert np.array_equal(F.round_to_f16(x), x.astype(np.float16).astype(np.float64))
+
+
+def pin_outliers_brute(F):
+    r = _rng(62)
+    W = r.normal(0, 1, (7, 13)).astype(np.float16)
+    W[2, 3] = W[5, 1] = W[0, 12] = np.float16(-9.0)   # equal magnitudes: row-major order decides
+    W[4, 4] = np.float16(9.0)
+    for n_out in (0, 1, 3, 4, 5, 20, 91):
+        m = F.select_outliers(W, n_out)
+        flat = [(-abs(float(W.flat[i])), i) for i in range(W.size)]
+        want = {i for _, i in sorted(flat)[:n_out]}
+        assert set(np.flatnonzero(m.ravel())) == want, n_out
+    m = F.select_outliers(W, 3)
+    assert set(np.flatnonzero(m.ravel())) == {12, 3 + 13 * 2, 4 + 13 * 4}  # the three |w| = 9 of lowest index
+
+
+def _assign(v, c):
+    d = np.abs(v[:, None] - c[None, :])
+    return np.argmin(d, axis=1)  # first (lower) index on a tie
+
+
+def pin_kmeans_fixed_point(F):
+    r = _rng(63)
+    for k in (8, 16):
+        for K in (5, 40, 333):
+            v = (r.normal(0, 0.02, K) * (1 + 20 * (r.random(K) < 0.01))).astype(np.float16)
+            v[: K // 5] = v[K // 5: 2 * (K // 5)]             # duplicates
+            c = F.kmeans_row(v, k, 500)
+            x = v.astype(np.float64)
+            lab = _assign(x, c)
+            for j in range(k):
+                if (lab == j).any():
+                    assert abs(c[j] - x[lab == j].mean()) <= 1e-12 * max(1e-300, abs(c[j])) + 1e-18, (k, K, j)
+            # nearest-centroid assignment is what the boundaries give
+            b = (c[:-1] + c[1:]) * 0.5
+            assert np.array_equal(np.searchsorted(b, x, side="left"), lab)
+
+
+def pin_kmeans_sklearn(F):
+    from sklearn.cluster import KMeans
+    r = _rng(64)
+    checked = 0
+    for t in range(12):
+        k = 8
+        v = r.normal(0, 0.02, 400).astype(np.float16)
+        x = v.astype(np.float64)
+        init = x.min() + ((x.max() - x.min()) * (2 * np.arange(k) + 1)) / (2 * k)
+        c = F.kmeans_row(v, k, 300)
+        km = KMeans(n_clusters=k, init=init.reshape(-1, 1), n_init=1, max_iter=300, tol=0.0,
+                    algorithm="lloyd").fit(x.reshape(-1, 1))
+        lab = _assign(x, c)
+        if len(set(lab)) < k:
+            continue  # an empty cluster: scikit-learn relocates it, the page's reading keeps it
+        assert np.allclose(np.sort(km.cluster_centers_.ravel()), c, rtol=0, atol=1e-12)
+        checked += 1
+    assert checked >= 6
+
+
+def pin_sse_monotone(F):
+    r = _rng(65)
+    v = r.standard_t(3, 700).astype(np.float16) * np.float16(0.01)
+    x = v.astype(np.float64)
+    prev = np.inf
+    for it in range(1, 15):
+        c = F.kmeans_row(v, 16, it)
+        sse = float(((x - c[_assign(x, c)]) ** 2).sum())
+        assert sse <= prev * (1 + 1e-12)
+        prev = sse
+
+
+def pin_codes_and_residual(F):
+    r = _rng(66)
+    W = (r.normal(0, 0.02, (9, 150)) * (1 + 40 * (r.random((9, 150)) < 0.005))).astype(np.float16)
+    for bits in (3, 4):
+        codes, lut, rp, col, val = F.fit_lut(W, bits, 14, 60)
+        out = np.zeros(W.shape, bool)
+        for n in range(9):
+            out[n, col[rp[n]:rp[n + 1]]] = True
+        assert out.sum() == 14
+        assert np.all(np.diff(lut.astype(np.float64), axis=1) >= 0)
+        w = W.astype(np.float64)
+        l = lut.astype(np.float64)
+        for n in range(9):
+            tgt = np.where(out[n], 0.0, w[n])
+            assert np.array_equal(codes[n], np.argmin(np.abs(tgt[:, None] - l[n][None, :]), axis=1))
+            for p in range(rp[n], rp[n + 1]):
+                j = col[p]
+                exact = w[n, j] - l[n, codes[n, j]]
+                assert float(val[p]) == float(np.float16(exact))
+        # outliers are the largest magnitudes
+        assert np.abs(w[out]).min() >= np.abs(w[~out]).max()
+
+
+ALL_PINS = [pin_worked_example, pin_round_f16_library, pin_outliers_brute, pin_kmeans_fixed_point,
+            pin_kmeans_sklearn, pin_sse_monotone, pin_codes_and_residual]
+
+
+def failing_pins(F):
+    bad = []
+    for p in ALL_PINS:
+        try:
+            p(F)
+        except Exception as e:  # noqa: BLE001
+            bad.append((p.__name__, repr(e)[:200]))
+    return bad

@@ -1,0 +1,127 @@
+"""The packer oracle against its pins, and planted mistakes in copies of it (no GPU)."""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+import fit_pins
+
+FIT_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "fit_oracle.py")
+
+
+def fresh():
+    spec = importlib.util.spec_from_file_location("fit_mutant", FIT_FILE)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+@pytest.mark.parametrize("pin", fit_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_fit_pin(pin):
+    pin(fresh())
+
+
+def _mut_outliers_signed(F):
+    def select_outliers(W, n_out):
+        a = np.asarray(W, np.float16).astype(np.float64).ravel()
+        order = np.lexsort((np.arange(a.size), -a))
+        m = np.zeros(a.size, bool)
+        m[order[:n_out]] = True
+        return m.reshape(np.asarray(W).shape)
+    F.select_outliers = select_outliers
+
+
+def _mut_outlier_ties_high(F):
+    def select_outliers(W, n_out):
+        a = np.abs(np.asarray(W, np.float16).astype(np.float64)).ravel()
+        order = np.lexsort((-np.arange(a.size), -a))
+        m = np.zeros(a.size, bool)
+        m[order[:n_out]] = True
+        return m.reshape(np.asarray(W).shape)
+    F.select_outliers = select_outliers
+
+
+def _kmeans_variant(F, init="even", side="left", empty="keep", one_pass=False):
+    def kmeans_row(v16, k, max_iter):
+        v = np.asarray(v16, np.float16).astype(np.float64)
+        if v.size == 0:
+            return np.zeros(k)
+        mn, mx = v.min(), v.max()
+        c = mn + (mx - mn) * np.arange(k) / (k - 1) if init == "ends" else mn + ((mx - mn) * (2 * np.arange(k) + 1)) / (2 * k)
+        for _ in range(1 if one_pass else max_iter):
+            b = (c[:-1] + c[1:]) * 0.5
+            idx = np.searchsorted(b, v, side=side)
+            sums = np.zeros(k)
+            np.add.at(sums, idx, v)
+            cnt = np.bincount(idx, minlength=k)
+            new = c.copy() if empty == "keep" else np.zeros(k)
+            nz = cnt > 0
+            new[nz] = sums[nz] / cnt[nz]
+            if np.array_equal(new, c):
+                break
+            c = new
+        return c
+    F.kmeans_row = kmeans_row
+
+
+def _mut_init_ends(F):
+    _kmeans_variant(F, init="ends")
+
+
+def _mut_ties_upper(F):
+    _kmeans_variant(F, side="right")
+
+
+def _mut_empty_to_zero(F):
+    _kmeans_variant(F, empty="zero")
+
+
+def _mut_one_iteration(F):
+    _kmeans_variant(F, one_pass=True)
+
+
+def _mut_lut_truncated(F):
+    orig = F.round_to_f16
+
+    def round_to_f16(v):
+        v = np.asarray(v, np.float64)
+        r = orig(v)
+        _, e = np.frexp(v)
+        sp = np.ldexp(1.0, np.maximum(e - 1, -14) - 10)
+        return np.where(np.abs(r) > np.abs(v), r - np.sign(v) * sp, r)
+    F.round_to_f16 = round_to_f16
+
+
+def _mut_code_ties_upper(F):
+    def nearest_code(v, lut16):
+        l = np.asarray(lut16, np.float16).astype(np.float64)
+        b = (l[:-1] + l[1:]) * 0.5
+        return np.searchsorted(b, np.asarray(v, np.float64), side="right").astype(np.uint8)
+    F.nearest_code = nearest_code
+
+
+def _mut_outlier_code_nearest_w(F):
+    orig_fit = F.fit_lut
+
+    def fit_lut(W, bits, n_out, max_iter):
+        codes, lut, rp, col, val = orig_fit(W, bits, n_out, max_iter)
+        W16 = np.asarray(W, np.float16)
+        for n in range(W16.shape[0]):
+            for p in range(rp[n], rp[n + 1]):
+                j = col[p]
+                codes[n, j] = F.nearest_code(np.array([float(W16[n, j])]), lut[n])[0]
+                val[p] = np.float16(float(W16[n, j]) - float(lut[n, codes[n, j]]))
+        return codes, lut, rp, col, val
+    F.fit_lut = fit_lut
+
+
+MUTANTS = [_mut_outliers_signed, _mut_outlier_ties_high, _mut_init_ends, _mut_ties_upper, _mut_empty_to_zero,
+           _mut_one_iteration, _mut_lut_truncated, _mut_code_ties_upper, _mut_outlier_code_nearest_w]
+
+
+@pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__[5:])
+def test_fit_pins_catch_mutant(mutate):
+    F = fresh()
+    mutate(F)
+    assert fit_pins.failing_pins(F), f"no pin caught {mutate.__name__}"
