@@ -170,6 +170,62 @@ def build_layers(cfg: int, M: int, act_scale: float = 0.0):
     return out, xs
 
 
+def bench_fit(a, dev):
+    """--fit: the data-free LUT packer (cl_fit_lut) on one LLaMA-7B projection."""
+    import torch
+    import compressed_linear_amd as cla
+    N, K, bits, frac, iters = 11008, 4096, 4, 0.0045, 30
+    r = np.random.default_rng(2026)
+    w = r.normal(0, 0.02, (N, K))
+    w = np.where(r.random((N, K)) < 0.003, r.normal(0, 0.3, (N, K)), w).astype(np.float16)
+    n_out = int(round(frac * N * K))
+    Wd = torch.from_numpy(w.view(np.int16)).view(torch.float16).to(dev)
+    for _ in range(max(1, a.warmup // 10)):
+        cla.fit_lut(Wd, bits, n_out, iters)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(3, a.steps // 40)
+    stats = {}
+    e0.record(stream)
+    for _ in range(reps):
+        cla.fit_lut(Wd, bits, n_out, iters, stats)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    # ALU bound: one element-iteration = the weight's 2^b - 1 boundary compares in fp64 (and its
+    # cluster sum), against MI355X's fp64 vector rate of 39.3 T operations/s (78.6 TFLOP/s counting
+    # an FMA as two), i.e. 39.3e12 / (2^b - 1) element-iterations per second
+    elem_iters = stats["total_iters"] * (K - n_out / N)
+    peak_ei = 39.3e12 / ((1 << bits) - 1)
+    # algorithmic bytes: the weights read once, codes and LUTs written, the CSR part written
+    alg = N * K * 2 + N * K + N * (1 << bits) * 2 + (N + 1) * 4 + n_out * 6
+    cpu = None
+    if not a.no_cpu_baseline:
+        from oracle import fit_oracle as F
+        rows = 64
+        t0 = time.perf_counter()
+        F.fit_lut(w[:rows], bits, int(round(frac * rows * K)), iters)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(rows * K / dt / 1e6, 3), "unit": "M weights/s", "cores": 1, "kind": "oracle",
+               "sample": f"the packer oracle on the first {rows} rows ({rows * K} weights), numpy, one process"}
+    out = {
+        "metric": "data-free LUT packing throughput (cl_fit_lut)",
+        "value": round(N * K / ms / 1e6, 3), "unit": "G weights/s", "n_gpus": 1, "steps": reps,
+        "warmup": max(1, a.warmup // 10), "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp16 in, f64 sums", "data": "synthetic (seeded)",
+        "config": {"workload": f"LLaMA-7B gate projection {K}->{N}, {bits}-bit LUT, {frac:.2%} outliers, "
+                               f"{iters} Lloyd iterations at most"},
+        "roofline": {"bound": "alu", "achieved": round(elem_iters / ms / 1e6, 2), "peak": round(peak_ei / 1e9, 2),
+                     "unit": "G element-iterations/s", "frac": round(elem_iters / ms * 1e3 / peak_ei, 4),
+                     "traffic": None, "kernel": "cl_fit_lut (all kernels of one call)",
+                     "lloyd_iterations_per_row": round(stats["total_iters"] / N, 2),
+                     "hbm_GBps_on_algorithmic_bytes": round(alg / ms / 1e6, 1), "bytes_per_call": alg},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +238,7 @@ def main():
                     help="scale this fraction of each layer's input channels (SLiM's output-error variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-layer", action="store_true", help="also time each layer alone")
+    ap.add_argument("--fit", action="store_true", help="time the data-free LUT packer instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for the byte counters)")
     a = ap.parse_args()
@@ -208,6 +265,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}), flush=True)
         return
+    if a.fit:
+        return bench_fit(a, dev)
     cfg, M = a.config, a.M
 
     log(f"building config {cfg} M={M}")

@@ -14,13 +14,13 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["ClError", "lib", "pack", "blob_header", "CompressedLinear", "LIB_PATH", "EXPORTED_SYMBOLS"]
+__all__ = ["ClError", "lib", "pack", "blob_header", "CompressedLinear", "fit_lut", "LIB_PATH", "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcompressed_linear.so")
 
 EXPORTED_SYMBOLS = [
     "cl_pack", "cl_device_bytes", "cl_create", "cl_forward", "cl_forward_path",
-    "cl_debug_dequant", "cl_destroy", "cl_last_error",
+    "cl_debug_dequant", "cl_destroy", "cl_last_error", "cl_fit_lut_work_bytes", "cl_fit_lut",
 ]
 
 DENSE = {"lut3": 0, "lut4": 1, "int4": 2, "int8": 3}
@@ -107,6 +107,11 @@ def lib():
         L.cl_destroy.restype = ctypes.c_int
         L.cl_last_error.argtypes = []
         L.cl_last_error.restype = ctypes.c_char_p
+        L.cl_fit_lut_work_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        L.cl_fit_lut_work_bytes.restype = ctypes.c_size_t
+        L.cl_fit_lut.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                 ctypes.c_int32] + [ctypes.c_void_p] * 7 + [ctypes.POINTER(ctypes.c_int64)]
+        L.cl_fit_lut.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -282,3 +287,30 @@ class CompressedLinear:
             self.close()
         except Exception:  # noqa: BLE001 -- interpreter shutdown
             pass
+
+
+def fit_lut(W, bits: int, n_out: int, max_iter: int = 50, stats: Optional[dict] = None):
+    """Data-free LUT packing on the GPU (cl_fit_lut): W is a torch fp16 [N, K]
+    tensor on a ROCm device.  Returns device tensors (codes uint8 [N, K], lut
+    fp16 [N, 2^bits], row_ptr int32 [N+1], col int32 [n_out], val fp16 [n_out]);
+    `stats`, if given, receives the Lloyd iterations run (summed over rows)."""
+    import torch
+    if W.dtype != torch.float16 or W.dim() != 2 or not W.is_cuda:
+        raise ValueError("W must be a 2-D float16 tensor on a ROCm device")
+    W = W.contiguous()
+    N, K = W.shape
+    dev = W.device
+    codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    lut = torch.empty((N, 1 << bits), dtype=torch.float16, device=dev)
+    row_ptr = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    col = torch.empty(max(n_out, 1), dtype=torch.int32, device=dev)
+    val = torch.empty(max(n_out, 1), dtype=torch.float16, device=dev)
+    work = torch.empty(max(int(lib().cl_fit_lut_work_bytes(N, K)), 8), dtype=torch.uint8, device=dev)
+    iters = ctypes.c_int64(0)
+    st = lib().cl_fit_lut(W.data_ptr(), N, K, bits, n_out, max_iter, codes.data_ptr(), lut.data_ptr(),
+                          row_ptr.data_ptr(), col.data_ptr(), val.data_ptr(), work.data_ptr(),
+                          torch.cuda.current_stream(dev).cuda_stream, ctypes.byref(iters))
+    _check(st, "cl_fit_lut")
+    if stats is not None:
+        stats["total_iters"] = int(iters.value)
+    return codes, lut, row_ptr, col[:n_out], val[:n_out]

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcompressed_linear.so")
 ARCH = os.environ.get("CL_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["pack.cpp", "runtime.hip", "decode.hip", "aux.hip", "prefill.hip",
+SOURCES = ["pack.cpp", "runtime.hip", "decode.hip", "aux.hip", "prefill.hip", "fit.hip",
            "decode_lut3.hip", "decode_lut4.hip", "decode_int4.hip", "decode_int4_24.hip",
            "decode_int8.hip", "decode_int8_bm.hip",
            "decode_rows_lut3.hip", "decode_rows_lut4.hip", "decode_rows_int4.hip", "decode_rows_int4_24.hip",

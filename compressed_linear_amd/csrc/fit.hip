@@ -1,0 +1,455 @@
+// fit.hip -- data-free LUT packing of an fp16 weight matrix on the GPU.
+//
+// "SqueezeLLM: Dense-and-Sparse Quantization", Approach: each output channel
+// (row) gets a non-uniform LUT whose values are k-means centroids of its
+// weights, and the outliers leave the dense part for a full-precision CSR
+// matrix (0.45 % of the weights in the page's runs).  The sensitivity weighting
+// (Fisher information) needs gradients and data; this is the page's
+// sensitivity-agnostic variant (its measured-effects table), from weights alone:
+//
+//   1. outliers: the n_out weights of largest magnitude, ties to the lower
+//      row-major index -- a two-pass radix select over the 15-bit magnitude
+//      (high 8 bits, then low 7), per-row counts of the threshold value and a
+//      scan that hands each row its share of the ties;
+//   2. per row (one workgroup): Lloyd's iterations in one dimension over the
+//      row's dense weights from 2^b evenly spaced starting points; a weight
+//      joins the nearest centroid (the lower one on a tie), a centroid becomes
+//      the mean of its weights (kept when it has none), until no centroid moves
+//      or max_iter rounds;
+//   3. LUT = centroids rounded to fp16; every dense weight takes its nearest LUT
+//      value's code (lower on a tie); an outlier's position takes the code
+//      nearest to 0 and its CSR value is fp16(w - lut[code]).
+//
+// All arithmetic that decides a result is exact or rounded once in a fixed
+// order: fp16 weights are integer multiples of 2^-24, so the cluster sums are
+// kept as 64-bit integers (exact in any order for |w| < 8192, K <= 30720), a
+// centroid is sum / count in fp64, boundaries are (c_j + c_j+1) / 2 in fp64.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+#include "layout.h"
+
+namespace cl {
+
+namespace {
+
+constexpr int kFitThreads = 256;
+constexpr int kFitMaxK = 30720;  // the row and its outlier bits fit 64 KiB of LDS
+
+// Work buffer layout (bytes), for N rows.
+struct FitWork {
+  static constexpr size_t hist1 = 0;          // u32 [256]: magnitude >> 7
+  static constexpr size_t hist2 = 1024;       // u32 [128]: magnitude & 127 within the selected bucket
+  static constexpr size_t scal = 1536;        // i64 [8]: bucket, need, T, r, bad flag
+  static constexpr size_t rows = 1600;        // per row: gt u32 [N], eq u32 [N], eqbase i64 [N]
+  __host__ __device__ static size_t gt(int) { return rows; }
+  __host__ __device__ static size_t eq(int N) { return rows + (size_t)N * 4; }
+  __host__ __device__ static size_t eqbase(int N) { return (rows + (size_t)N * 8 + 7) & ~(size_t)7; }
+  __host__ __device__ static size_t bytes(int N) { return eqbase(N) + (size_t)N * 8; }
+};
+enum { S_BUCKET = 0, S_NEED, S_T, S_R, S_BAD, S_ITERS };
+
+__device__ __forceinline__ uint32_t mag(uint16_t h) { return h & 0x7FFFu; }
+
+// fp16 bits -> the weight as an integer multiple of 2^-24 (exact).
+__device__ __forceinline__ long long f16_fixed(uint16_t h) {
+  const uint32_t e = (h >> 10) & 31u, m = h & 0x3FFu;
+  const long long q = e ? (long long)(m | 0x400u) << (e - 1) : (long long)m;
+  return (h & 0x8000u) ? -q : q;
+}
+
+// fp64 -> fp16 bits, nearest with ties to even, for values inside the fp16
+// range (the centroids and outlier residuals of weights below 8192).
+__device__ __forceinline__ uint16_t f64_to_f16_rne(double d) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(d);
+  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+  const unsigned long long a = u & 0x7FFFFFFFFFFFFFFFull;
+  if (a == 0) return (uint16_t)sign;
+  const int e = (int)(a >> 52) - 1023;
+  const unsigned long long m = (a & 0xFFFFFFFFFFFFFull) | 0x10000000000000ull;  // 53-bit significand
+  if (e >= 16) return (uint16_t)(sign | 0x7C00u);
+  // keep the bits of weight >= 2^-24 (subnormal) or the top 11 (normal)
+  const int shift = e >= -14 ? 42 : 28 - e;
+  if (shift > 63) return (uint16_t)sign;
+  unsigned long long q = m >> shift;
+  const unsigned long long rem = m & ((1ull << shift) - 1), half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1))) ++q;
+  if (e >= -14) {
+    int ee = e;
+    if (q == 2048) { q = 1024; ++ee; }
+    if (ee >= 16) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | ((uint32_t)(ee + 15) << 10) | ((uint32_t)q & 0x3FFu));
+  }
+  return (uint16_t)(sign | (uint32_t)q);  // q == 1024 is the smallest normal
+}
+
+__device__ __forceinline__ double f16_to_f64(uint16_t h) { return (double)(float)__builtin_bit_cast(_Float16, h); }
+
+// ---- 1. radix select of the outlier threshold ----
+__global__ void __launch_bounds__(256) fit_hist_kernel(const uint16_t* __restrict__ W, long long total, int pass,
+                                                      uint8_t* __restrict__ work) {
+  __shared__ uint32_t h[256];
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  long long* sc = reinterpret_cast<long long*>(work + FitWork::scal);
+  const uint32_t bucket = pass ? (uint32_t)sc[S_BUCKET] : 0u;
+  uint32_t bad = 0;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
+    const uint32_t u = mag(W[i]);
+    if (pass == 0) {
+      bad |= u >= 0x7000u;  // |w| >= 8192, inf or NaN
+      atomicAdd(&h[u >> 7], 1u);
+    } else if ((u >> 7) == bucket) {
+      atomicAdd(&h[u & 127u], 1u);
+    }
+  }
+  if (bad) atomicOr(reinterpret_cast<unsigned long long*>(&sc[S_BAD]), 1ull);
+  __syncthreads();
+  uint32_t* g = reinterpret_cast<uint32_t*>(work + (pass ? FitWork::hist2 : FitWork::hist1));
+  if ((int)threadIdx.x < (pass ? 128 : 256) && h[threadIdx.x]) atomicAdd(&g[threadIdx.x], h[threadIdx.x]);
+}
+
+// One thread: walk the histogram from the largest magnitude down until n_out is reached.
+__global__ void fit_select_kernel(long long n_out, int pass, uint8_t* __restrict__ work) {
+  long long* sc = reinterpret_cast<long long*>(work + FitWork::scal);
+  const uint32_t* g = reinterpret_cast<const uint32_t*>(work + (pass ? FitWork::hist2 : FitWork::hist1));
+  const int nb = pass ? 128 : 256;
+  long long need = pass ? sc[S_NEED] : n_out;
+  if (need <= 0) {  // no outliers: a threshold above every magnitude
+    sc[S_BUCKET] = 256;
+    sc[S_NEED] = 0;
+    sc[S_T] = 0x8000;
+    sc[S_R] = 0;
+    return;
+  }
+  int b = nb - 1;
+  for (; b > 0; --b) {
+    if ((long long)g[b] >= need) break;
+    need -= g[b];
+  }
+  if (pass == 0) {
+    sc[S_BUCKET] = b;
+    sc[S_NEED] = need;
+  } else {
+    sc[S_T] = (sc[S_BUCKET] << 7) | b;
+    sc[S_R] = need;  // weights of magnitude T that become outliers, lowest indices first
+  }
+}
+
+// ---- per-row counts above / at the threshold ----
+__global__ void __launch_bounds__(256) fit_rowstat_kernel(const uint16_t* __restrict__ W, int K, uint8_t* __restrict__ work,
+                                                          int N) {
+  const long long* sc = reinterpret_cast<const long long*>(work + FitWork::scal);
+  const uint32_t T = (uint32_t)sc[S_T];
+  const uint16_t* row = W + (size_t)blockIdx.x * K;
+  uint32_t gt = 0, eq = 0;
+  for (int k = threadIdx.x; k < K; k += 256) {
+    const uint32_t u = mag(row[k]);
+    gt += u > T;
+    eq += u == T;
+  }
+  __shared__ uint32_t sg[256], se[256];
+  sg[threadIdx.x] = gt;
+  se[threadIdx.x] = eq;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) {
+      sg[threadIdx.x] += sg[threadIdx.x + s];
+      se[threadIdx.x] += se[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    reinterpret_cast<uint32_t*>(work + FitWork::gt(N))[blockIdx.x] = sg[0];
+    reinterpret_cast<uint32_t*>(work + FitWork::eq(N))[blockIdx.x] = se[0];
+  }
+}
+
+// One workgroup: eqbase = exclusive scan of the rows' threshold counts, each
+// row's outlier count, row_ptr = exclusive scan of those (row_ptr[N] = n_out).
+__global__ void __launch_bounds__(1024) fit_scan_kernel(int N, uint8_t* __restrict__ work, int32_t* __restrict__ row_ptr) {
+  const long long* sc = reinterpret_cast<const long long*>(work + FitWork::scal);
+  const long long r = sc[S_R];
+  const uint32_t* gt = reinterpret_cast<const uint32_t*>(work + FitWork::gt(N));
+  const uint32_t* eq = reinterpret_cast<const uint32_t*>(work + FitWork::eq(N));
+  long long* eqbase = reinterpret_cast<long long*>(work + FitWork::eqbase(N));
+  __shared__ long long se[1024], so[1024];
+  long long carry_e = 0, carry_o = 0;
+  for (int base = 0; base < N; base += 1024) {
+    const int n = base + (int)threadIdx.x;
+    const long long e = n < N ? (long long)eq[n] : 0;
+    se[threadIdx.x] = e;
+    __syncthreads();
+    for (int s = 1; s < 1024; s <<= 1) {  // inclusive scan
+      const long long v = (int)threadIdx.x >= s ? se[threadIdx.x - s] : 0;
+      __syncthreads();
+      se[threadIdx.x] += v;
+      __syncthreads();
+    }
+    const long long ebase = carry_e + se[threadIdx.x] - e;
+    long long take = r - ebase;
+    take = take < 0 ? 0 : (take > e ? e : take);
+    const long long o = n < N ? (long long)gt[n] + take : 0;
+    if (n < N) eqbase[n] = ebase;
+    so[threadIdx.x] = o;
+    __syncthreads();
+    for (int s = 1; s < 1024; s <<= 1) {
+      const long long v = (int)threadIdx.x >= s ? so[threadIdx.x - s] : 0;
+      __syncthreads();
+      so[threadIdx.x] += v;
+      __syncthreads();
+    }
+    if (n < N) row_ptr[n] = (int32_t)(carry_o + so[threadIdx.x] - o);
+    const long long te = se[1023], to = so[1023];
+    __syncthreads();
+    carry_e += te;
+    carry_o += to;
+  }
+  if (threadIdx.x == 0) row_ptr[N] = (int32_t)carry_o;
+}
+
+// Exclusive prefix of a per-thread flag over the workgroup in thread order,
+// plus the workgroup's total.  `tmp`: 4 ints of LDS.
+__device__ __forceinline__ int wg_prefix(bool f, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long bal = __ballot(f);
+  const int below = __popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) tmp[wave] = __popcll(bal);
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    before += w < wave ? tmp[w] : 0;
+    tot += tmp[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return before + below;
+}
+
+// ---- 2 and 3: one workgroup per row ----
+template <int NC>
+__global__ void __launch_bounds__(kFitThreads) fit_rows_kernel(const uint16_t* __restrict__ W, int N, int K, int max_iter,
+                                                               int n_out,
+                                                               const uint8_t* __restrict__ work,
+                                                               const int32_t* __restrict__ row_ptr,
+                                                               uint8_t* __restrict__ codes, uint16_t* __restrict__ lut,
+                                                               int32_t* __restrict__ col, uint16_t* __restrict__ val) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+  uint16_t* v16 = reinterpret_cast<uint16_t*>(dyn);                       // the row, [K]
+  uint32_t* outb = reinterpret_cast<uint32_t*>(dyn + ((size_t)K * 2 + 15) / 16 * 16);  // outlier bits, [K/32]
+  __shared__ double cen[NC];
+  __shared__ float bnd32[NC];
+  __shared__ unsigned long long wsum[4][NC];
+  __shared__ uint32_t wcnt[4][NC];
+  __shared__ int tmp[4];
+  __shared__ int s_changed;
+  __shared__ uint32_t s_mn, s_mx;
+  __shared__ int s_any;
+
+  const int n = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long long* sc = reinterpret_cast<const long long*>(work + FitWork::scal);
+  const uint32_t T = (uint32_t)sc[S_T];
+  const long long r = sc[S_R];
+  const long long eqbase = reinterpret_cast<const long long*>(work + FitWork::eqbase(N))[n];
+  const uint16_t* row = W + (size_t)n * K;
+  for (int k = tid; k < K; k += kFitThreads) v16[k] = row[k];
+  for (int i = tid; i < (K + 31) / 32; i += kFitThreads) outb[i] = 0;
+  if (tid == 0) {
+    s_mn = 0xFFFFFFFFu;
+    s_mx = 0;
+    s_any = 0;
+  }
+  __syncthreads();
+
+  // outliers in index order: tiles of 256 consecutive weights, thread t on weight 256 i + t
+  const int base_out = row_ptr[n];
+  int eq_run = 0, out_run = 0;
+  for (int k0 = 0; k0 < K; k0 += kFitThreads) {
+    const int k = k0 + tid;
+    const uint32_t u = k < K ? mag(v16[k]) : 0u;
+    const bool eq = k < K && u == T;
+    int eq_tot;
+    const int eq_rank = eq_run + wg_prefix(eq, tmp, &eq_tot);
+    const bool out = k < K && (u > T || (eq && eqbase + eq_rank < r));
+    int out_tot;
+    const int out_rank = out_run + wg_prefix(out, tmp, &out_tot);
+    if (out) {
+      atomicOr(&outb[k >> 5], 1u << (k & 31));
+      if (base_out + out_rank < n_out) col[base_out + out_rank] = k;  // always, by the counts; bounds kept anyway
+    }
+    eq_run += eq_tot;
+    out_run += out_tot;
+  }
+  __syncthreads();
+
+  // range of the dense weights: order-preserving keys of fp16 values (-0 taken as +0)
+  auto key = [](uint16_t h) -> uint32_t {
+    h = h == 0x8000u ? (uint16_t)0 : h;
+    return (h & 0x8000u) ? (uint32_t)(~h & 0xFFFFu) : (uint32_t)(h | 0x8000u);
+  };
+  auto unkey = [](uint32_t kk) -> uint16_t { return (kk & 0x8000u) ? (uint16_t)(kk & 0x7FFFu) : (uint16_t)(~kk & 0xFFFFu); };
+  uint32_t mn = 0xFFFFFFFFu, mx = 0;
+  bool any = false;
+  for (int k = tid; k < K; k += kFitThreads) {
+    if ((outb[k >> 5] >> (k & 31)) & 1u) continue;
+    const uint32_t kk = key(v16[k]);
+    mn = kk < mn ? kk : mn;
+    mx = kk > mx ? kk : mx;
+    any = true;
+  }
+  if (any) {
+    atomicMin(&s_mn, mn);
+    atomicMax(&s_mx, mx);
+    atomicOr(&s_any, 1);
+  }
+  __syncthreads();
+
+  if (tid < NC) {
+    if (s_any) {
+      const double dmn = f16_to_f64(unkey(s_mn)), dmx = f16_to_f64(unkey(s_mx));
+      cen[tid] = dmn + ((dmx - dmn) * (double)(2 * tid + 1)) / (double)(2 * NC);
+    } else {
+      cen[tid] = 0.0;
+    }
+  }
+  __syncthreads();
+
+  int done = 0;
+  for (int it = 0; it < max_iter && s_any; ++it) {
+    ++done;
+    // v > b holds exactly when v > RD32(b) for an fp32 v (no fp32 lies strictly
+    // between RD32(b) and b), so the assignment compares in fp32
+    if (tid < NC - 1) bnd32[tid] = __double2float_rd((cen[tid] + cen[tid + 1]) * 0.5);
+    if (tid < 4 * NC) {
+      (&wsum[0][0])[tid] = 0;
+      (&wcnt[0][0])[tid] = 0;
+    }
+    if (tid == 0) s_changed = 0;
+    __syncthreads();
+    float b[NC - 1];
+#pragma unroll
+    for (int j = 0; j < NC - 1; ++j) b[j] = bnd32[j];
+    for (int k = tid; k < K; k += kFitThreads) {
+      if ((outb[k >> 5] >> (k & 31)) & 1u) continue;
+      const uint16_t h = v16[k];
+      const float v = (float)__builtin_bit_cast(_Float16, h);
+      int idx = 0;
+#pragma unroll
+      for (int j = 0; j < NC - 1; ++j) idx += v > b[j];
+      // per-wavefront cluster sums: exact integers, so their order is free
+      atomicAdd(&wsum[wave][idx], (unsigned long long)f16_fixed(h));
+      atomicAdd(&wcnt[wave][idx], 1u);
+    }
+    __syncthreads();
+    if (tid < NC) {
+      const long long s = (long long)(wsum[0][tid] + wsum[1][tid] + wsum[2][tid] + wsum[3][tid]);
+      const int c = (int)(wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid]);
+      if (c > 0) {
+        const double nc = ((double)s / (double)c) * (1.0 / 16777216.0);
+        if (nc != cen[tid]) {
+          cen[tid] = nc;
+          s_changed = 1;
+        }
+      }
+    }
+    __syncthreads();
+    if (!s_changed) break;
+  }
+
+  if (tid == 0 && done)
+    atomicAdd(reinterpret_cast<unsigned long long*>(const_cast<uint8_t*>(work) + FitWork::scal + S_ITERS * 8),
+              (unsigned long long)done);
+  // LUT and codes
+  __shared__ uint16_t l16[NC];
+  __shared__ double lb[NC];
+  if (tid < NC) {
+    l16[tid] = f64_to_f16_rne(cen[tid]);
+    lut[(size_t)n * NC + tid] = l16[tid];
+  }
+  __syncthreads();
+  if (tid < NC - 1) lb[tid] = (f16_to_f64(l16[tid]) + f16_to_f64(l16[tid + 1])) * 0.5;
+  __syncthreads();
+  double b[NC - 1];
+#pragma unroll
+  for (int j = 0; j < NC - 1; ++j) b[j] = lb[j];
+  uint8_t* crow = codes + (size_t)n * K;
+  for (int k = tid; k < K; k += kFitThreads) {
+    const bool out = (outb[k >> 5] >> (k & 31)) & 1u;
+    const double v = out ? 0.0 : f16_to_f64(v16[k]);
+    int idx = 0;
+#pragma unroll
+    for (int j = 0; j < NC - 1; ++j) idx += b[j] < v;
+    crow[k] = (uint8_t)idx;
+  }
+  // outlier values, in the same index order as their columns
+  int idx0 = 0;
+  {
+    double t = 0.0;
+#pragma unroll
+    for (int j = 0; j < NC - 1; ++j) idx0 += b[j] < t;
+  }
+  out_run = 0;
+  for (int k0 = 0; k0 < K; k0 += kFitThreads) {
+    const int k = k0 + tid;
+    const bool out = k < K && ((outb[k >> 5] >> (k & 31)) & 1u);
+    int out_tot;
+    const int out_rank = out_run + wg_prefix(out, tmp, &out_tot);
+    if (out && base_out + out_rank < n_out)
+      val[base_out + out_rank] = f64_to_f16_rne(f16_to_f64(v16[k]) - f16_to_f64(l16[idx0]));
+    out_run += out_tot;
+  }
+}
+
+}  // namespace
+
+}  // namespace cl
+
+using namespace cl;
+
+extern "C" size_t cl_fit_lut_work_bytes(int32_t N, int32_t K) {
+  if (N < 1 || K < 1) return 0;
+  return FitWork::bytes(N);
+}
+
+extern "C" cl_status cl_fit_lut(const uint16_t* W, int32_t N, int32_t K, int32_t bits, int64_t n_out, int32_t max_iter,
+                                uint8_t* codes, uint16_t* lut, int32_t* row_ptr, int32_t* col, uint16_t* val,
+                                void* work, void* stream, int64_t* total_iters) {
+  clear_error();
+  if (N < 1 || K < 1) return fail(CL_EINVAL, "N and K must be >= 1");
+  if (K > kFitMaxK || N > (1 << 24)) return fail(CL_ESIZE, "the fitter takes K <= %d and N <= 2^24", kFitMaxK);
+  if (bits != 3 && bits != 4) return fail(CL_EINVAL, "bits must be 3 or 4");
+  if (max_iter < 1) return fail(CL_EINVAL, "max_iter must be >= 1");
+  const long long total = (long long)N * K;
+  if (n_out < 0 || n_out > total || n_out > 0x7FFFFFFFLL) return fail(CL_EINVAL, "n_out out of range");
+  if (!W || !codes || !lut || !row_ptr || !work || (n_out > 0 && (!col || !val)))
+    return fail(CL_EINVAL, "a required pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(work) % 8) return fail(CL_EINVAL, "work must be 8-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* wk = static_cast<uint8_t*>(work);
+  hipError_t e = hipMemsetAsync(wk, 0, FitWork::rows, s);  // histograms and scalars
+  const int hb = (int)(total / 256 / 8 + 1 > 2048 ? 2048 : total / 256 / 8 + 1);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(fit_hist_kernel, dim3(hb), dim3(256), 0, s, W, total, 0, wk);
+    hipLaunchKernelGGL(fit_select_kernel, dim3(1), dim3(1), 0, s, (long long)n_out, 0, wk);
+    hipLaunchKernelGGL(fit_hist_kernel, dim3(hb), dim3(256), 0, s, W, total, 1, wk);
+    hipLaunchKernelGGL(fit_select_kernel, dim3(1), dim3(1), 0, s, (long long)n_out, 1, wk);
+    hipLaunchKernelGGL(fit_rowstat_kernel, dim3(N), dim3(256), 0, s, W, K, wk, N);
+    hipLaunchKernelGGL(fit_scan_kernel, dim3(1), dim3(1024), 0, s, N, wk, row_ptr);
+    const size_t lds = ((size_t)K * 2 + 15) / 16 * 16 + ((size_t)K + 31) / 32 * 4;
+    if (bits == 3)
+      hipLaunchKernelGGL(fit_rows_kernel<8>, dim3(N), dim3(kFitThreads), lds, s, W, N, K, max_iter, (int)n_out, wk, row_ptr, codes,
+                         lut, col, val);
+    else
+      hipLaunchKernelGGL(fit_rows_kernel<16>, dim3(N), dim3(kFitThreads), lds, s, W, N, K, max_iter, (int)n_out, wk, row_ptr, codes,
+                         lut, col, val);
+    e = hipGetLastError();
+  }
+  long long sc[8] = {};
+  if (e == hipSuccess) e = hipMemcpyAsync(sc, wk + FitWork::scal, sizeof(sc), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(CL_EHIP, "fit failed: %s", hipGetErrorString(e));
+  if (sc[S_BAD]) return fail(CL_EINVAL, "a weight is not finite or its magnitude is 8192 or more (outputs are not valid)");
+  if (total_iters) *total_iters = sc[S_ITERS];
+  return CL_OK;
+}

@@ -253,6 +253,47 @@ cl_status cl_destroy(void* handle);
 const char* cl_last_error(void);
 
 /*
+ * cl_fit_lut_work_bytes -- device scratch (bytes) that cl_fit_lut needs for an
+ * N x K matrix; 0 if N or K < 1.
+ */
+size_t cl_fit_lut_work_bytes(int32_t N, int32_t K);
+
+/*
+ * cl_fit_lut -- data-free LUT packing of an fp16 weight matrix on the GPU, the
+ * step before cl_pack ("SqueezeLLM: Dense-and-Sparse Quantization", Approach:
+ * per-output-channel non-uniform LUTs from k-means, outliers to a
+ * full-precision CSR matrix; the sensitivity-agnostic variant of its
+ * measured-effects table, from weights alone).
+ *   W         device, [N, K] fp16 weights, row = output channel; finite,
+ *             |w| < 8192.
+ *   bits      3 or 4 (LUTs of 8 or 16 values).
+ *   n_out     weights moved to the CSR part: the n_out of largest magnitude,
+ *             ties to the lower row-major index (0 <= n_out <= N*K, < 2^31).
+ *   max_iter  Lloyd iterations per row at most (>= 1); a row stops when no
+ *             centroid moves.  Row n starts from 2^b points spread evenly over
+ *             [min, max] of its dense weights: c_j = min + (max-min)(2j+1)/2^(b+1);
+ *             a weight joins the nearest centroid (the lower on a tie); a
+ *             centroid becomes the mean of its weights (kept when it has none).
+ *   outputs (device, caller-owned): codes [N*K] uint8 (nearest LUT value, the
+ *             lower code on a tie; an outlier's position takes the code nearest
+ *             to 0); lut [N * 2^b] fp16 (the centroids rounded to nearest-even);
+ *             row_ptr [N+1] int32, col [n_out] int32 (ascending in each row),
+ *             val [n_out] fp16 = fp16(w - lut[code]) -- exactly the logical
+ *             arrays cl_pack takes for a LUT layer with CSR outliers.
+ *   work      device, cl_fit_lut_work_bytes(N, K) bytes, 8-byte aligned.
+ *   stream    hipStream_t; the call synchronizes it before returning.
+ *   total_iters  host, optional (NULL): the Lloyd iterations run, summed over rows.
+ * Deterministic: cluster sums are exact integers (weights are multiples of
+ * 2^-24), every other decision exact or rounded once in a fixed order.
+ * Errors: CL_EINVAL (sizes, bits, n_out, max_iter, NULL pointers, or a weight
+ * that is not finite or has |w| >= 8192: outputs then undefined), CL_ESIZE
+ * (K > 30720 or N > 2^24), CL_EHIP.
+ */
+cl_status cl_fit_lut(const uint16_t* W, int32_t N, int32_t K, int32_t bits, int64_t n_out, int32_t max_iter,
+                     uint8_t* codes, uint16_t* lut, int32_t* row_ptr, int32_t* col, uint16_t* val,
+                     void* work, void* stream, int64_t* total_iters);
+
+/*
  * Header at the start of every packed blob (little endian).  Exposed so that
  * tools can inspect a blob; the section layouts are documented with the
  * packer.

@@ -1,0 +1,134 @@
+"""The data-free LUT packer (cl_fit_lut) against its CPU oracle, through the C
+ABI (needs an MI355X).
+
+Bit for bit: codes, LUTs, CSR row pointers, columns and values, at sizes the
+oracle runs in seconds (ragged K, ties at the outlier threshold, rows that are
+all outliers, no outliers, one iteration).  At a LLaMA layer's full size: the
+outlier set's defining properties over the whole matrix and the k-means,
+LUT and codes of sampled rows against the oracle.  End to end: the fitted
+layer packed and run through the forward matches the oracle's forward of it.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import compressed_linear_amd as cla
+from oracle import fit_oracle as F
+from gpu_util import check_bound, gpu_forward, torch_cuda
+from synth.layers import LogicalLayer
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _weights(seed, N, K, tail=0.003):
+    r = np.random.default_rng(seed)
+    w = r.normal(0, 0.02, (N, K))
+    big = r.random((N, K)) < tail
+    w = np.where(big, r.normal(0, 0.3, (N, K)), w)
+    return w.astype(np.float16)
+
+
+def _gpu_fit(W, bits, n_out, iters):
+    torch = torch_cuda()
+    Wd = torch.from_numpy(W.view(np.int16)).view(torch.float16).cuda()
+    codes, lut, rp, col, val = cla.fit_lut(Wd, bits, n_out, iters)
+    torch.cuda.synchronize()
+    return (codes.cpu().numpy(), lut.cpu().numpy(), rp.cpu().numpy(), col.cpu().numpy(), val.cpu().numpy())
+
+
+def _same(g, o, what):
+    names = ["codes", "lut", "row_ptr", "col", "val"]
+    for nm, a, b in zip(names, g, o):
+        a = np.asarray(a)
+        b = np.asarray(b)
+        if a.dtype == np.float16:
+            a, b = a.view(np.uint16), b.view(np.uint16)
+        assert a.shape == b.shape and np.array_equal(a, b), f"{what}: {nm} differs at {np.argwhere(a != b)[:5]}"
+
+
+@pytest.mark.parametrize("N,K,bits,frac,iters", [(130, 1000, 3, 0.0045, 50), (70, 777, 4, 0.01, 50),
+                                                 (33, 37, 3, 0.05, 50), (5, 1, 4, 0.0, 50), (40, 300, 4, 0.0045, 1),
+                                                 (300, 4096, 4, 0.0045, 30)])
+def test_fit_bit_exact(N, K, bits, frac, iters):
+    W = _weights(N * 7 + K, N, K)
+    n_out = int(round(frac * N * K))
+    say("fit", N, K, bits, n_out, iters)
+    _same(_gpu_fit(W, bits, n_out, iters), F.fit_lut(W, bits, n_out, iters), f"{N}x{K} b{bits}")
+
+
+def test_fit_ties_and_degenerate_rows():
+    r = np.random.default_rng(3)
+    # few distinct magnitudes: many ties at the threshold, split across rows
+    W = r.choice(np.array([-0.5, -0.25, 0.0, 0.125, 0.25, 0.5], np.float16), size=(60, 260))
+    W[7] = np.float16(0.0)            # a row of zeros (and -0)
+    W[8, ::2] = np.float16(-0.0)
+    W[9] = np.float16(0.5)            # a row that becomes all outliers
+    for n_out in (0, 1, 260 + 17, 3000, 60 * 260):
+        say("ties", n_out)
+        _same(_gpu_fit(W, 3, n_out, 40), F.fit_lut(W, 3, n_out, 40), f"ties n_out={n_out}")
+
+
+def test_fit_rejects_bad_input():
+    torch = torch_cuda()
+    W = _weights(5, 8, 64)
+    W[3, 3] = np.float16(9000.0)
+    with pytest.raises(cla.ClError):
+        _gpu_fit(W, 3, 4, 10)
+    Wd = torch.zeros((4, 40000), dtype=torch.float16, device="cuda")
+    with pytest.raises(cla.ClError):
+        cla.fit_lut(Wd, 3, 1, 10)
+    with pytest.raises(cla.ClError):
+        cla.fit_lut(torch.zeros((4, 64), dtype=torch.float16, device="cuda"), 5, 1, 10)
+
+
+def test_fit_full_size_properties_and_sampled_rows():
+    # LLaMA-7B gate projection shape, 0.45 % outliers, 4-bit
+    N, K, bits = 11008, 4096, 4
+    W = _weights(11, N, K)
+    n_out = int(round(0.0045 * N * K))
+    say("fit full size", N, K, n_out)
+    codes, lut, rp, col, val = _gpu_fit(W, bits, n_out, 30)
+    assert rp[0] == 0 and rp[-1] == n_out and np.all(np.diff(rp) >= 0)
+    out = np.zeros((N, K), bool)
+    rows = np.repeat(np.arange(N), np.diff(rp))
+    out[rows, col] = True
+    assert out.sum() == n_out
+    for n in np.random.default_rng(1).choice(N, 40, replace=False):
+        assert np.all(np.diff(col[rp[n]:rp[n + 1]]) > 0)
+    a = np.abs(W.astype(np.float64))
+    thr = a[out].min()
+    assert thr >= a[~out].max()
+    # ties at the threshold: the outliers among them have the lowest indices
+    tie = np.flatnonzero((a == thr).ravel())
+    chosen = out.ravel()[tie]
+    assert np.all(chosen[:chosen.sum()]) and not np.any(chosen[chosen.sum():])
+    # sampled rows: k-means, LUT, codes and outlier values against the oracle
+    for n in np.random.default_rng(2).choice(N, 24, replace=False):
+        dense = ~out[n]
+        c = F.kmeans_row(W[n, dense], 1 << bits, 30)
+        l16 = F.round_to_f16(c).astype(np.float16)
+        assert np.array_equal(lut[n].view(np.uint16), l16.view(np.uint16)), n
+        w = W[n].astype(np.float64)
+        assert np.array_equal(codes[n], F.nearest_code(np.where(dense, w, 0.0), l16)), n
+        c0 = F.nearest_code(np.array([0.0]), l16)[0]
+        want = F.round_to_f16(w[col[rp[n]:rp[n + 1]]] - float(l16[c0])).astype(np.float16)
+        assert np.array_equal(val[rp[n]:rp[n + 1]].view(np.uint16), want.view(np.uint16)), n
+
+
+def test_fit_then_forward():
+    # the fitted arrays are a LUT layer with CSR outliers: pack, create, forward
+    N, K = 300, 1024
+    W = _weights(21, N, K)
+    codes, lut, rp, col, val = _gpu_fit(W, 4, int(0.0045 * N * K), 40)
+    layer = LogicalLayer(K=K, N=N, dense="lut4", codes=codes, lut=lut, csr_row_ptr=rp, csr_col=col, csr_val=val)
+    x = np.random.default_rng(4).normal(0, 1, (3, K)).astype(np.float16)
+    y = gpu_forward(layer, x)
+    check_bound(y, layer, x, what="fitted layer")
+    # and the fitted layer approximates the original weights
+    y_w = x.astype(np.float64) @ W.astype(np.float64).T
+    assert np.linalg.norm(y - y_w) < 0.2 * np.linalg.norm(y_w)
