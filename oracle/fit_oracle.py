@@ -119,3 +119,83 @@ def fit_lut(W, bits: int, n_out: int, max_iter: int):
     np.cumsum(np.bincount(np.asarray(rows, dtype=np.int64), minlength=N), out=row_ptr[1:])
     return (codes, lut, row_ptr, np.asarray(cols, dtype=np.int32),
             np.asarray(vals, dtype=np.float64).astype(np.float16))
+
+
+# ---------------------------------------------------------------------------
+# Integer formats: magnitude masks and the SLiM-Quant clip search
+# ---------------------------------------------------------------------------
+#
+# "SLiM: One-shot Quantization and Sparsity with Low-rank Approximation for LLM
+# Weight Compression" -- review highlights: symmetric weight quantization that
+# clips the weights before rounding to the nearest integer, the clipping
+# threshold found by a grid search (the page's probabilistic formulation has
+# lost its equations).  Rebuttal "Unstructured vs. 2:4 Sparsity": 2:4 and
+# unstructured masks.  "Compressing Large Language Models by Joint
+# Sparsification and Quantization", Approach: unstructured sparsity with
+# quantization.  Pruning metrics that need activations (Wanda, SAR) are out;
+# the data-free mask keeps the largest magnitudes.
+#
+# Readings: per output channel (row) a scale s = fp16(i * max|w| / (qmax * G))
+# for the grid point i in 1..G (the clipping threshold i/G of the row's largest
+# kept magnitude; the division in fp64, then rounded to fp16), codes
+# q = clamp(rint(w / s), -qmax, qmax) with qmax = 2^(b-1) - 1, and the grid point
+# with the smallest squared error sum (w - s q)^2 over the kept weights wins
+# (the lower i on a tie); the errors are exact integers in units of 2^-48.
+# Masks: 2:4 keeps the two largest |w| of each group of four consecutive
+# weights, "half" keeps the floor(K/2) largest of each row; ties to the lower
+# index.  Dropped weights get q = 0.
+
+def magnitude_mask(W, kind: str) -> np.ndarray:
+    """keep uint8 [N, K] of the data-free mask ('2:4' or 'half')."""
+    a = np.abs(np.asarray(W, dtype=np.float16).astype(np.float64))
+    N, K = a.shape
+    keep = np.zeros((N, K), dtype=np.uint8)
+    if kind == "2:4":
+        for n in range(N):
+            for g in range(K // 4):
+                grp = a[n, 4 * g:4 * g + 4]
+                order = sorted(range(4), key=lambda t: (-grp[t], t))
+                keep[n, 4 * g + order[0]] = keep[n, 4 * g + order[1]] = 1
+    elif kind == "half":
+        for n in range(N):
+            order = np.lexsort((np.arange(K), -a[n]))
+            keep[n, order[:K // 2]] = 1
+    else:
+        keep[:] = 1
+    return keep
+
+
+def clip_search_row(w16, kept, bits: int, grid: int):
+    """(scale fp16, q int8 [K]) of one row by the grid search above."""
+    qmax = (1 << (bits - 1)) - 1
+    w = np.asarray(w16, dtype=np.float16).astype(np.float64)
+    k = np.asarray(kept, dtype=bool)
+    q = np.zeros(w.size, dtype=np.int64)
+    m = float(np.abs(w[k]).max()) if k.any() else 0.0
+    wi = [int(v) for v in np.rint(w[k] * FIX).astype(np.int64)]
+    best = None
+    for i in range(1, grid + 1):
+        s = float(round_to_f16((i * m) / (qmax * grid)))
+        if s == 0.0:
+            continue
+        qi = np.clip(np.rint(w[k] / s), -qmax, qmax).astype(np.int64)
+        si = int(round(s * FIX))
+        err = sum((a - si * int(b)) ** 2 for a, b in zip(wi, qi))
+        if best is None or err < best[0]:
+            best = (err, s, qi)
+    if best is None:
+        return np.float16(0.0), q.astype(np.int8)
+    q[k] = best[2]
+    return np.float16(best[1]), q.astype(np.int8)
+
+
+def fit_int(W, bits: int, mask: str, grid: int):
+    """qvals int8 [N, K], row_scale fp16 [N], keep uint8 [N, K] (all ones without a mask)."""
+    W16 = np.asarray(W, dtype=np.float16)
+    keep = magnitude_mask(W16, mask)
+    N, K = W16.shape
+    q = np.zeros((N, K), dtype=np.int8)
+    s = np.zeros(N, dtype=np.float16)
+    for n in range(N):
+        s[n], q[n] = clip_search_row(W16[n], keep[n], bits, grid)
+    return q, s, keep

@@ -133,8 +133,84 @@ def pin_codes_and_residual(F):
         assert np.abs(w[out]).min() >= np.abs(w[~out]).max()
 
 
+# ---------------------------------------------------------------------------
+# integer formats: masks and the clip search
+# ---------------------------------------------------------------------------
+
+def pin_int_worked_example(F):
+    # SLiM page, highlights (symmetric quantization, clipping, grid search).
+    # w = [1, -2, 3, 0.5, 0.25, -7, 6, 0], qmax = 7, G = 4: m = 7, s_i = i/4.
+    #   s = 1:    q = [1,-2,3,0,0,-7,6,0] (0.5 rounds to even 0); err = 0.5^2 + 0.25^2 = 0.3125
+    #   s = 0.75: q = [1,-3,4,1,0,-7,7,0]; err = 4 * 0.0625 + 1.75^2 + 0.75^2 = 3.875
+    #   s = 0.5:  q = [2,-4,6,1,0,-7,7,0]; err = 0.0625 + 3.5^2 + 2.5^2 = 18.5625
+    #   s = 0.25: larger still.  Best: s = 1.
+    w = np.array([[1, -2, 3, 0.5, 0.25, -7, 6, 0]], np.float16)
+    q, s, keep = F.fit_int(w, 4, "none", 4)
+    assert float(s[0]) == 1.0 and list(q[0]) == [1, -2, 3, 0, 0, -7, 6, 0]
+    # 2:4 keeps (-2, 3) and (-7, 6): all on the grid at s = 1, error 0
+    q, s, keep = F.fit_int(w, 4, "2:4", 4)
+    assert list(keep[0]) == [0, 1, 1, 0, 0, 1, 1, 0] and float(s[0]) == 1.0
+    assert list(q[0]) == [0, -2, 3, 0, 0, -7, 6, 0]
+
+
+def _beaten(a, i, idx):
+    return sum(1 for u in idx if a[u] > a[i] or (a[u] == a[i] and u < i))
+
+
+def pin_masks_brute(F):
+    r = _rng(71)
+    W = r.choice(np.array([-1.0, -0.5, 0.5, 1.0, 2.0, 0.0], np.float16), size=(6, 24))  # many ties
+    a = np.abs(W.astype(np.float64))
+    k24 = F.magnitude_mask(W, "2:4")
+    kh = F.magnitude_mask(W, "half")
+    for n in range(6):
+        for t in range(24):
+            g = list(range(4 * (t // 4), 4 * (t // 4) + 4))
+            assert k24[n, t] == (1 if _beaten(a[n], t, g) < 2 else 0)
+            assert kh[n, t] == (1 if _beaten(a[n], t, range(24)) < 12 else 0)
+    assert np.all(k24.reshape(6, 6, 4).sum(axis=2) == 2) and np.all(kh.sum(axis=1) == 12)
+
+
+def pin_clip_search_fractions(F):
+    # exact errors with Fractions, an independent route to the same argmin
+    from fractions import Fraction
+    r = _rng(72)
+    for bits, G in ((4, 12), (8, 6)):
+        qmax = (1 << (bits - 1)) - 1
+        for t in range(6):
+            w = (r.normal(0, 0.02, 40) * (1 + 8 * (r.random(40) < 0.05))).astype(np.float16)
+            kept = r.random(40) < 0.7
+            s, q = F.clip_search_row(w, kept, bits, G)
+            m = max(abs(Fraction(float(v))) for v in w[kept])
+            best = None
+            for i in range(1, G + 1):
+                si = float(np.float16(float(Fraction(i) * m / (qmax * G))))
+                if si == 0:
+                    continue
+                qi = [max(-qmax, min(qmax, int(np.rint(float(v) / si)))) for v in w[kept]]
+                err = sum((Fraction(float(v)) - Fraction(si) * b) ** 2 for v, b in zip(w[kept], qi))
+                if best is None or err < best[0]:
+                    best = (err, si, qi)
+            assert float(s) == best[1]
+            assert list(q[kept]) == best[2] and not q[~kept].any()
+
+
+def pin_clip_never_worse_than_absmax(F):
+    r = _rng(73)
+    W = (r.standard_t(3, (5, 64)) * 0.01).astype(np.float16)
+    q, s, keep = F.fit_int(W, 4, "none", 20)
+    w = W.astype(np.float64)
+    for n in range(5):
+        err = ((w[n] - float(s[n]) * q[n]) ** 2).sum()
+        s1 = float(np.float16(np.abs(w[n]).max() / 7))
+        q1 = np.clip(np.rint(w[n] / s1), -7, 7)
+        assert err <= ((w[n] - s1 * q1) ** 2).sum() * (1 + 1e-12)
+        assert np.abs(q[n]).max() <= 7
+
+
 ALL_PINS = [pin_worked_example, pin_round_f16_library, pin_outliers_brute, pin_kmeans_fixed_point,
-            pin_kmeans_sklearn, pin_sse_monotone, pin_codes_and_residual]
+            pin_kmeans_sklearn, pin_sse_monotone, pin_codes_and_residual, pin_int_worked_example,
+            pin_masks_brute, pin_clip_search_fractions, pin_clip_never_worse_than_absmax]
 
 
 def failing_pins(F):

@@ -125,3 +125,70 @@ def test_fit_pins_catch_mutant(mutate):
     F = fresh()
     mutate(F)
     assert fit_pins.failing_pins(F), f"no pin caught {mutate.__name__}"
+
+
+def _mut_mask_ties_high(F):
+    orig = F.magnitude_mask
+
+    def magnitude_mask(W, kind):
+        W = np.asarray(W, np.float16)
+        return orig(W[:, ::-1], kind)[:, ::-1] if kind != "2:4" else \
+            orig(W.reshape(W.shape[0], -1, 4)[:, :, ::-1].reshape(W.shape), kind).reshape(W.shape[0], -1, 4)[:, :, ::-1].reshape(W.shape)
+    F.magnitude_mask = magnitude_mask
+
+
+def _mut_mask_signed(F):
+    orig = F.magnitude_mask
+
+    def magnitude_mask(W, kind):
+        W = np.asarray(W, np.float16)
+        shifted = (W.astype(np.float64) + 100.0).astype(np.float16)  # ranks by signed value
+        return orig(shifted, kind)
+    F.magnitude_mask = magnitude_mask
+
+
+def _clip_variant(F, qmax_plus=0, err_all=False, worst=False, trunc=False):
+    def clip_search_row(w16, kept, bits, grid):
+        qmax = (1 << (bits - 1)) - 1 + qmax_plus
+        w = np.asarray(w16, np.float16).astype(np.float64)
+        k = np.asarray(kept, bool)
+        q = np.zeros(w.size, np.int64)
+        m = float(np.abs(w[k]).max()) if k.any() else 0.0
+        best = None
+        for i in range(1, grid + 1):
+            s = float(F.round_to_f16((i * m) / ((qmax - qmax_plus) * grid)))
+            if s == 0.0:
+                continue
+            rnd = np.trunc if trunc else np.rint
+            qi = np.clip(rnd(w[k] / s), -qmax, qmax).astype(np.int64)
+            err = ((w[k] - s * qi) ** 2).sum() + (((w[~k]) ** 2).sum() if err_all else 0.0)
+            better = best is None or (err > best[0] if worst else err < best[0])
+            if better:
+                best = (err, s, qi)
+        if best is None:
+            return np.float16(0.0), q.astype(np.int8)
+        q[k] = best[2]
+        return np.float16(best[1]), q.astype(np.int8)
+    F.clip_search_row = clip_search_row
+
+
+def _mut_qmax_asymmetric(F):
+    _clip_variant(F, qmax_plus=1)
+
+
+def _mut_worst_scale(F):
+    _clip_variant(F, worst=True)
+
+
+def _mut_truncating_codes(F):
+    _clip_variant(F, trunc=True)
+
+
+INT_MUTANTS = [_mut_mask_ties_high, _mut_mask_signed, _mut_qmax_asymmetric, _mut_worst_scale, _mut_truncating_codes]
+
+
+@pytest.mark.parametrize("mutate", INT_MUTANTS, ids=lambda f: f.__name__[5:])
+def test_fit_pins_catch_int_mutant(mutate):
+    F = fresh()
+    mutate(F)
+    assert fit_pins.failing_pins(F), f"no pin caught {mutate.__name__}"
