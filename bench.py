@@ -170,10 +170,59 @@ def build_layers(cfg: int, M: int, act_scale: float = 0.0):
     return out, xs
 
 
+def bench_fit_int(a, dev):
+    """--fit int: the data-free int4 2:4 packer (cl_fit_int) on the 4096 -> 11008 projection."""
+    import torch
+    import compressed_linear_amd as cla
+    N, K, grid = 11008, 4096, 100
+    r = np.random.default_rng(2027)
+    w = r.normal(0, 0.02, (N, K))
+    w = np.where(r.random((N, K)) < 0.002, r.normal(0, 0.3, (N, K)), w).astype(np.float16)
+    Wd = torch.from_numpy(w.view(np.int16)).view(torch.float16).to(dev)
+    cla.fit_int(Wd, 4, "2:4", grid)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(3, a.steps // 40)
+    e0.record(stream)
+    for _ in range(reps):
+        cla.fit_int(Wd, 4, "2:4", grid)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    # ALU bound: one element-candidate (a kept weight under one scale candidate) = an fp64
+    # division (about 8 operations), rint, the clamp, an integer multiply-subtract and a
+    # 128-bit square-accumulate: about 20 operations at 39.3 T operations/s
+    ec = N * (K // 2) * grid
+    peak = 39.3e12 / 20
+    cpu = None
+    if not a.no_cpu_baseline:
+        from oracle import fit_oracle as F
+        t0 = time.perf_counter()
+        F.fit_int(w[:2], 4, "2:4", grid)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(2 * K / dt / 1e6, 4), "unit": "M weights/s", "cores": 1, "kind": "oracle",
+               "sample": f"the packer oracle on the first 2 rows ({2 * K} weights), Python integers, one process"}
+    out = {
+        "metric": "data-free int4 2:4 packing throughput (cl_fit_int)",
+        "value": round(N * K / ms / 1e6, 3), "unit": "G weights/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16 in, f64 division, 128-bit integer errors", "data": "synthetic (seeded)",
+        "config": {"workload": f"up projection {K}->{N}, int4, magnitude 2:4, clip grid of {grid}"},
+        "roofline": {"bound": "alu", "achieved": round(ec / ms / 1e6, 2), "peak": round(peak / 1e9, 2),
+                     "unit": "G element-candidates/s", "frac": round(ec / ms * 1e3 / peak, 4), "traffic": None,
+                     "kernel": "fit_int_kernel<7>"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_fit(a, dev):
     """--fit: the data-free LUT packer (cl_fit_lut) on one LLaMA-7B projection."""
     import torch
     import compressed_linear_amd as cla
+    if a.fit == "int":
+        return bench_fit_int(a, dev)
     N, K, bits, frac, iters = 11008, 4096, 4, 0.0045, 30
     r = np.random.default_rng(2026)
     w = r.normal(0, 0.02, (N, K))
@@ -238,7 +287,8 @@ def main():
                     help="scale this fraction of each layer's input channels (SLiM's output-error variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-layer", action="store_true", help="also time each layer alone")
-    ap.add_argument("--fit", action="store_true", help="time the data-free LUT packer instead of the forward")
+    ap.add_argument("--fit", nargs="?", const="lut", choices=["lut", "int"],
+                    help="time a data-free packer (LUT k-means, or the int4 2:4 clip search) instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for the byte counters)")
     a = ap.parse_args()

@@ -14,13 +14,15 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["ClError", "lib", "pack", "blob_header", "CompressedLinear", "fit_lut", "LIB_PATH", "EXPORTED_SYMBOLS"]
+__all__ = ["ClError", "lib", "pack", "blob_header", "CompressedLinear", "fit_lut", "fit_int", "LIB_PATH",
+           "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcompressed_linear.so")
 
 EXPORTED_SYMBOLS = [
     "cl_pack", "cl_device_bytes", "cl_create", "cl_forward", "cl_forward_path",
     "cl_debug_dequant", "cl_destroy", "cl_last_error", "cl_fit_lut_work_bytes", "cl_fit_lut",
+    "cl_fit_int",
 ]
 
 DENSE = {"lut3": 0, "lut4": 1, "int4": 2, "int8": 3}
@@ -112,6 +114,8 @@ def lib():
         L.cl_fit_lut.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                  ctypes.c_int32] + [ctypes.c_void_p] * 7 + [ctypes.POINTER(ctypes.c_int64)]
         L.cl_fit_lut.restype = ctypes.c_int
+        L.cl_fit_int.argtypes = [ctypes.c_void_p] + [ctypes.c_int32] * 5 + [ctypes.c_void_p] * 5
+        L.cl_fit_int.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -314,3 +318,25 @@ def fit_lut(W, bits: int, n_out: int, max_iter: int = 50, stats: Optional[dict] 
     if stats is not None:
         stats["total_iters"] = int(iters.value)
     return codes, lut, row_ptr, col[:n_out], val[:n_out]
+
+
+def fit_int(W, bits: int, mask: str = "none", grid: int = 100):
+    """Data-free integer packing on the GPU (cl_fit_int): W is a torch fp16 [N, K]
+    tensor on a ROCm device; mask 'none', '2:4' (bits 4) or 'bitmap' (bits 8, half
+    of each row).  Returns device tensors (qvals int8 [N, K], row_scale fp16 [N],
+    keep uint8 [N, K] or None)."""
+    import torch
+    if W.dtype != torch.float16 or W.dim() != 2 or not W.is_cuda:
+        raise ValueError("W must be a 2-D float16 tensor on a ROCm device")
+    W = W.contiguous()
+    N, K = W.shape
+    dev = W.device
+    q = torch.empty((N, K), dtype=torch.int8, device=dev)
+    s = torch.empty(N, dtype=torch.float16, device=dev)
+    keep = None if mask == "none" else torch.empty((N, K), dtype=torch.uint8, device=dev)
+    work = torch.empty(8, dtype=torch.uint8, device=dev)
+    st = lib().cl_fit_int(W.data_ptr(), N, K, bits, MASK[mask], grid, q.data_ptr(), s.data_ptr(),
+                          None if keep is None else keep.data_ptr(), work.data_ptr(),
+                          torch.cuda.current_stream(dev).cuda_stream)
+    _check(st, "cl_fit_int")
+    return q, s, keep

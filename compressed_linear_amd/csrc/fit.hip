@@ -22,7 +22,7 @@
 //
 // All arithmetic that decides a result is exact or rounded once in a fixed
 // order: fp16 weights are integer multiples of 2^-24, so the cluster sums are
-// kept as 64-bit integers (exact in any order for |w| < 8192, K <= 30720), a
+// kept as 64-bit integers (exact in any order for |w| < 8192, K <= 28672), a
 // centroid is sum / count in fp64, boundaries are (c_j + c_j+1) / 2 in fp64.
 #include <hip/hip_runtime.h>
 
@@ -34,7 +34,7 @@ namespace cl {
 namespace {
 
 constexpr int kFitThreads = 256;
-constexpr int kFitMaxK = 30720;  // the row and its outlier bits fit 64 KiB of LDS
+constexpr int kFitMaxK = 28672;  // the row and its mask bits, with the static LDS, fit 64 KiB
 
 // Work buffer layout (bytes), for N rows.
 struct FitWork {
@@ -401,6 +401,180 @@ __global__ void __launch_bounds__(kFitThreads) fit_rows_kernel(const uint16_t* _
   }
 }
 
+// ---- integer formats: data-free mask and SLiM-Quant clip search, one workgroup per row ----
+//
+// "SLiM" page, review highlights: symmetric quantization that clips the weights
+// before rounding to nearest, the clipping threshold found by a grid search (the
+// page's probabilistic formulation has lost its equations; read here as the
+// plain squared error of the row's kept weights).  Rebuttal "Unstructured vs.
+// 2:4 Sparsity" and "Compressing Large Language Models by Joint Sparsification
+// and Quantization", Approach: 2:4 and unstructured masks; without activations
+// the mask keeps the largest magnitudes (ties to the lower index).
+//   scale candidates s_i = fp16((i * max|w|) / (qmax * G)), i = 1..G (fp64 division,
+//   then nearest-even fp16); codes q = clamp(rint(w / s_i), -qmax, qmax); the
+//   error sum of (w - s_i q)^2 over the kept weights is an exact 128-bit integer
+//   in units of 2^-48; the smallest wins, the lower i on a tie.
+typedef unsigned __int128 u128;
+
+template <int QMAX>
+__global__ void __launch_bounds__(kFitThreads) fit_int_kernel(const uint16_t* __restrict__ W, int K, int mask, int grid,
+                                                              int8_t* __restrict__ qvals, uint16_t* __restrict__ row_scale,
+                                                              uint8_t* __restrict__ keep_out, unsigned long long* __restrict__ bad) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+  uint16_t* v16 = reinterpret_cast<uint16_t*>(dyn);
+  uint32_t* keepb = reinterpret_cast<uint32_t*>(dyn + ((size_t)K * 2 + 15) / 16 * 16);
+  __shared__ uint32_t hist[256];
+  __shared__ u128 red[4];
+  __shared__ int tmp[4];
+  __shared__ uint32_t s_T, s_mag;
+  __shared__ int s_r, s_bucket;
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* row = W + (size_t)n * K;
+  uint32_t nonfinite = 0;
+  for (int k = tid; k < K; k += kFitThreads) {
+    v16[k] = row[k];
+    nonfinite |= (row[k] & 0x7C00u) == 0x7C00u;
+  }
+  for (int i = tid; i < (K + 31) / 32; i += kFitThreads) keepb[i] = 0;
+  if (nonfinite) atomicOr(bad, 1ull);
+  if (tid == 0) s_mag = 0;
+  __syncthreads();
+
+  // ---- mask ----
+  if (mask == CL_MASK_2_4) {
+    for (int g = tid; g < K / 4; g += kFitThreads) {
+      uint32_t a[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[t] = mag(v16[4 * g + t]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        int beaten = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) beaten += (a[u] > a[t]) || (a[u] == a[t] && u < t);
+        if (beaten < 2) atomicOr(&keepb[(4 * g + t) >> 5], 1u << ((4 * g + t) & 31));
+      }
+    }
+  } else if (mask == CL_MASK_BITMAP) {
+    // the floor(K/2) largest magnitudes: radix select (high 8 bits, low 7), ties by index
+    const int want = K / 2;
+    for (int pass = 0; pass < 2; ++pass) {
+      hist[tid] = 0;
+      __syncthreads();
+      for (int k = tid; k < K; k += kFitThreads) {
+        const uint32_t u = mag(v16[k]);
+        if (pass == 0) atomicAdd(&hist[u >> 7], 1u);
+        else if ((int)(u >> 7) == s_bucket) atomicAdd(&hist[u & 127u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int need = pass == 0 ? want : s_r, b = pass == 0 ? 255 : 127;
+        if (need <= 0) {
+          s_bucket = 256;
+          s_T = 0x8000u;
+          s_r = 0;
+        } else {
+          for (; b > 0; --b) {
+            if ((int)hist[b] >= need) break;
+            need -= (int)hist[b];
+          }
+          if (pass == 0) {
+            s_bucket = b;
+            s_r = need;
+          } else {
+            s_T = ((uint32_t)s_bucket << 7) | (uint32_t)b;
+            s_r = need;
+          }
+        }
+      }
+      __syncthreads();
+      if (s_bucket == 256) break;
+    }
+    const uint32_t T = s_T;
+    const int r = s_r;
+    int eq_run = 0;
+    for (int k0 = 0; k0 < K; k0 += kFitThreads) {
+      const int k = k0 + tid;
+      const uint32_t u = k < K ? mag(v16[k]) : 0u;
+      const bool eq = k < K && u == T;
+      int tot;
+      const int rank = eq_run + wg_prefix(eq, tmp, &tot);
+      if (k < K && (u > T || (eq && rank < r))) atomicOr(&keepb[k >> 5], 1u << (k & 31));
+      eq_run += tot;
+    }
+  } else {
+    for (int i = tid; i < K / 32; i += kFitThreads) keepb[i] = 0xFFFFFFFFu;
+    if (tid == 0 && (K & 31)) keepb[K / 32] = (1u << (K & 31)) - 1u;
+  }
+  __syncthreads();
+  auto kept = [&](int k) -> bool { return (keepb[k >> 5] >> (k & 31)) & 1u; };
+  uint32_t mx = 0;
+  for (int k = tid; k < K; k += kFitThreads)
+    if (kept(k)) mx = max(mx, mag(v16[k]));
+  if (mx) atomicMax(&s_mag, mx);
+  __syncthreads();
+  const double m = f16_to_f64((uint16_t)s_mag);
+
+  // ---- clip search ----
+  u128 best = ~(u128)0;
+  int best_i = 0;
+  uint16_t best_s = 0;
+  for (int i = 1; i <= grid; ++i) {
+    const uint16_t s16 = f64_to_f16_rne(((double)i * m) / (double)(QMAX * grid));
+    if ((s16 & 0x7FFFu) == 0) continue;  // uniform: every thread skips
+    const double sd = f16_to_f64(s16);
+    const long long S = f16_fixed(s16);
+    u128 acc = 0;
+    for (int k = tid; k < K; k += kFitThreads) {
+      if (!kept(k)) continue;
+      const uint16_t h = v16[k];
+      double qd = rint(f16_to_f64(h) / sd);
+      qd = qd > QMAX ? QMAX : (qd < -QMAX ? -QMAX : qd);
+      const long long d = f16_fixed(h) - S * (long long)qd;
+      const unsigned long long ad = (unsigned long long)(d < 0 ? -d : d);
+      acc += (u128)ad * ad;
+    }
+    // 128-bit sum over the wavefront (two 64-bit halves and the carry), then the four wavefronts
+    unsigned long long lo = (unsigned long long)acc, hi = (unsigned long long)(acc >> 64);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long lo2 = __shfl_xor(lo, o, 64), hi2 = __shfl_xor(hi, o, 64);
+      const unsigned long long sl = lo + lo2;
+      hi = hi + hi2 + (sl < lo ? 1ull : 0ull);
+      lo = sl;
+    }
+    if ((tid & 63) == 0) red[tid >> 6] = ((u128)hi << 64) | lo;
+    __syncthreads();
+    if (tid == 0) {
+      const u128 tot = red[0] + red[1] + red[2] + red[3];
+      if (tot < best) {
+        best = tot;
+        best_i = i;
+        best_s = s16;
+      }
+    }
+    __syncthreads();
+  }
+  __shared__ uint16_t s_best;
+  if (tid == 0) {
+    s_best = best_i ? best_s : (uint16_t)0;
+    row_scale[n] = s_best;
+  }
+  __syncthreads();
+  const uint16_t s16 = s_best;
+  const double sd = f16_to_f64(s16);
+  int8_t* qrow = qvals + (size_t)n * K;
+  uint8_t* krow = keep_out ? keep_out + (size_t)n * K : nullptr;
+  for (int k = tid; k < K; k += kFitThreads) {
+    int q = 0;
+    if (kept(k) && (s16 & 0x7FFFu)) {
+      double qd = rint(f16_to_f64(v16[k]) / sd);
+      q = (int)(qd > QMAX ? QMAX : (qd < -QMAX ? -QMAX : qd));
+    }
+    qrow[k] = (int8_t)q;
+    if (krow) krow[k] = kept(k) ? 1 : 0;
+  }
+}
+
 }  // namespace
 
 }  // namespace cl
@@ -451,5 +625,38 @@ extern "C" cl_status cl_fit_lut(const uint16_t* W, int32_t N, int32_t K, int32_t
   if (e != hipSuccess) return fail(CL_EHIP, "fit failed: %s", hipGetErrorString(e));
   if (sc[S_BAD]) return fail(CL_EINVAL, "a weight is not finite or its magnitude is 8192 or more (outputs are not valid)");
   if (total_iters) *total_iters = sc[S_ITERS];
+  return CL_OK;
+}
+
+extern "C" cl_status cl_fit_int(const uint16_t* W, int32_t N, int32_t K, int32_t bits, int32_t mask, int32_t grid,
+                                int8_t* qvals, uint16_t* row_scale, uint8_t* keep, void* work, void* stream) {
+  clear_error();
+  if (N < 1 || K < 1) return fail(CL_EINVAL, "N and K must be >= 1");
+  if (K > kFitMaxK || N > (1 << 24)) return fail(CL_ESIZE, "the fitter takes K <= %d and N <= 2^24", kFitMaxK);
+  if (bits != 4 && bits != 8) return fail(CL_EINVAL, "bits must be 4 or 8");
+  if (mask != CL_MASK_NONE && mask != CL_MASK_2_4 && mask != CL_MASK_BITMAP) return fail(CL_EINVAL, "unknown mask %d", mask);
+  if (mask == CL_MASK_2_4 && (bits != 4 || K % 4)) return fail(CL_EUNSUPPORTED, "2:4 needs bits = 4 and K % 4 == 0");
+  if (mask == CL_MASK_BITMAP && bits != 8) return fail(CL_EUNSUPPORTED, "the unstructured mask needs bits = 8");
+  if (grid < 1 || grid > 4096) return fail(CL_EINVAL, "grid must be in [1, 4096]");
+  if (!W || !qvals || !row_scale || !work || (mask != CL_MASK_NONE && !keep))
+    return fail(CL_EINVAL, "a required pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(work) % 8) return fail(CL_EINVAL, "work must be 8-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned long long* bad = static_cast<unsigned long long*>(work);
+  hipError_t e = hipMemsetAsync(bad, 0, 8, s);
+  const size_t lds = ((size_t)K * 2 + 15) / 16 * 16 + ((size_t)K + 31) / 32 * 4;
+  if (e == hipSuccess) {
+    if (bits == 4)
+      hipLaunchKernelGGL(fit_int_kernel<7>, dim3(N), dim3(kFitThreads), lds, s, W, K, mask, grid, qvals, row_scale, keep, bad);
+    else
+      hipLaunchKernelGGL(fit_int_kernel<127>, dim3(N), dim3(kFitThreads), lds, s, W, K, mask, grid, qvals, row_scale, keep,
+                         bad);
+    e = hipGetLastError();
+  }
+  unsigned long long flag = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&flag, bad, 8, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(CL_EHIP, "fit failed: %s", hipGetErrorString(e));
+  if (flag) return fail(CL_EINVAL, "a weight is not finite (outputs are not valid)");
   return CL_OK;
 }

@@ -287,11 +287,45 @@ size_t cl_fit_lut_work_bytes(int32_t N, int32_t K);
  * 2^-24), every other decision exact or rounded once in a fixed order.
  * Errors: CL_EINVAL (sizes, bits, n_out, max_iter, NULL pointers, or a weight
  * that is not finite or has |w| >= 8192: outputs then undefined), CL_ESIZE
- * (K > 30720 or N > 2^24), CL_EHIP.
+ * (K > 28672 or N > 2^24), CL_EHIP.
  */
 cl_status cl_fit_lut(const uint16_t* W, int32_t N, int32_t K, int32_t bits, int64_t n_out, int32_t max_iter,
                      uint8_t* codes, uint16_t* lut, int32_t* row_ptr, int32_t* col, uint16_t* val,
                      void* work, void* stream, int64_t* total_iters);
+
+/*
+ * cl_fit_int -- data-free packing of an fp16 weight matrix into the integer
+ * formats on the GPU, the step before cl_pack ("SLiM" page, review highlights:
+ * symmetric quantization that clips the weights before rounding to nearest,
+ * the clipping threshold found by a grid search -- its probabilistic
+ * formulation has no equations on the page, read as the plain squared error;
+ * rebuttal "Unstructured vs. 2:4 Sparsity" and "Compressing Large Language
+ * Models by Joint Sparsification and Quantization", Approach: 2:4 and
+ * unstructured masks, here by magnitude since activation-aware metrics need data).
+ *   W          device, [N, K] fp16 weights (finite), row = output channel.
+ *   bits       4 (codes -7..7) or 8 (-127..127): qmax = 2^(bits-1) - 1.
+ *   mask       CL_MASK_NONE; CL_MASK_2_4 (bits 4, K % 4 == 0): the two largest
+ *              |w| of each group of four consecutive weights; CL_MASK_BITMAP
+ *              (bits 8): the floor(K/2) largest |w| of each row.  Ties go to
+ *              the lower index.
+ *   grid       G in [1, 4096]: per row, the scale candidates
+ *              s_i = fp16((i * max|w_kept|) / (qmax * G)), i = 1..G (fp64 division,
+ *              nearest-even fp16); codes q = clamp(rint(w / s_i), -qmax, qmax);
+ *              the candidate with the smallest sum of (w - s_i q)^2 over the kept
+ *              weights (exact: a 128-bit integer in units of 2^-48) wins, the lower
+ *              i on a tie.  A row with nothing kept or no positive candidate gets
+ *              scale 0 and codes 0.
+ *   outputs (device, caller-owned): qvals [N*K] int8 (0 where dropped),
+ *              row_scale [N] fp16, keep [N*K] uint8 0/1 (may be NULL without a
+ *              mask) -- the logical arrays cl_pack takes for the integer formats.
+ *   work       device, 8 bytes, 8-byte aligned.
+ *   stream     hipStream_t; the call synchronizes it before returning.
+ * Errors: CL_EINVAL (sizes, bits, grid, NULL pointers, a weight that is not
+ * finite: outputs then undefined), CL_EUNSUPPORTED (a mask with the other bit
+ * width, 2:4 with K % 4 != 0), CL_ESIZE (K > 28672 or N > 2^24), CL_EHIP.
+ */
+cl_status cl_fit_int(const uint16_t* W, int32_t N, int32_t K, int32_t bits, int32_t mask, int32_t grid,
+                     int8_t* qvals, uint16_t* row_scale, uint8_t* keep, void* work, void* stream);
 
 /*
  * Header at the start of every packed blob (little endian).  Exposed so that

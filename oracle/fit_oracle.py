@@ -34,7 +34,7 @@ notes): outliers by magnitude over the whole layer; the evenly spaced
 initialisation, the tie rules and the stopping rule above; an outlier's dense
 code.  Arithmetic: weights are fp16, so every sum of them is an exact integer
 multiple of 2^-24; the sums are kept as such integers (exact in any order, for
-|w| < 8192 and K <= 30720), a centroid is that sum over the count in fp64 (one
+|w| < 8192 and K <= 28672), a centroid is that sum over the count in fp64 (one
 rounding), boundaries are (c_j + c_(j+1)) / 2 in fp64, and every comparison is
 exact.  The fp64 -> fp16 rounding follows the format's definition.
 """

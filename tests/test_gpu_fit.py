@@ -132,3 +132,75 @@ def test_fit_then_forward():
     # and the fitted layer approximates the original weights
     y_w = x.astype(np.float64) @ W.astype(np.float64).T
     assert np.linalg.norm(y - y_w) < 0.2 * np.linalg.norm(y_w)
+
+
+# ---------------------------------------------------------------------------
+# integer formats (cl_fit_int)
+# ---------------------------------------------------------------------------
+
+OMASK = {"none": "none", "2:4": "2:4", "bitmap": "half"}
+
+
+def _gpu_fit_int(W, bits, mask, grid):
+    torch = torch_cuda()
+    Wd = torch.from_numpy(W.view(np.int16)).view(torch.float16).cuda()
+    q, s, keep = cla.fit_int(Wd, bits, mask, grid)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy(), None if keep is None else keep.cpu().numpy()
+
+
+@pytest.mark.parametrize("N,K,bits,mask,grid", [(40, 256, 4, "2:4", 20), (30, 333, 8, "bitmap", 12),
+                                                (25, 100, 4, "none", 50), (9, 1, 8, "bitmap", 5),
+                                                (12, 1000, 8, "none", 3), (16, 64, 4, "2:4", 1)])
+def test_fit_int_bit_exact(N, K, bits, mask, grid):
+    W = _weights(N * 3 + K, N, K, tail=0.02)
+    say("fit int", N, K, bits, mask, grid)
+    q, s, keep = _gpu_fit_int(W, bits, mask, grid)
+    oq, os_, ok = F.fit_int(W, bits, OMASK[mask], grid)
+    assert np.array_equal(s.view(np.uint16), os_.view(np.uint16)), np.argwhere(s.view(np.uint16) != os_.view(np.uint16))[:5]
+    assert np.array_equal(q, oq)
+    if keep is not None:
+        assert np.array_equal(keep, ok)
+
+
+def test_fit_int_ties_and_degenerate_rows():
+    r = np.random.default_rng(8)
+    W = r.choice(np.array([-0.5, -0.25, 0.0, 0.125, 0.25, 0.5], np.float16), size=(20, 96))
+    W[3] = np.float16(0.0)
+    W[4, ::3] = np.float16(-0.0)
+    for bits, mask in ((4, "2:4"), (8, "bitmap"), (4, "none")):
+        say("fit int ties", bits, mask)
+        q, s, keep = _gpu_fit_int(W, bits, mask, 16)
+        oq, os_, ok = F.fit_int(W, bits, OMASK[mask], 16)
+        assert np.array_equal(s.view(np.uint16), os_.view(np.uint16)) and np.array_equal(q, oq)
+        if keep is not None:
+            assert np.array_equal(keep, ok)
+
+
+def test_fit_int_full_size_properties_and_sampled_rows():
+    # SLiM-style INT4 2:4 at the up projection's shape (4096 -> 11008)
+    N, K = 11008, 4096
+    W = _weights(13, N, K, tail=0.002)
+    say("fit int full size")
+    q, s, keep = _gpu_fit_int(W, 4, "2:4", 100)
+    assert np.all(keep.reshape(N, K // 4, 4).sum(axis=2) == 2)
+    assert np.abs(q).max() <= 7 and not q[keep == 0].any()
+    for n in np.random.default_rng(3).choice(N, 3, replace=False):
+        ok = F.magnitude_mask(W[n:n + 1], "2:4")[0]
+        assert np.array_equal(keep[n], ok)
+        os_, oq = F.clip_search_row(W[n], ok.astype(bool), 4, 100)
+        assert s[n].view(np.uint16) == np.float16(os_).view(np.uint16) and np.array_equal(q[n], oq), n
+
+
+def test_fit_int_then_forward():
+    N, K = 260, 1024
+    W = _weights(31, N, K)
+    q, s, keep = _gpu_fit_int(W, 4, "2:4", 60)
+    layer = LogicalLayer(K=K, N=N, dense="int4", mask="2:4", qvals=q, row_scale=s, keep=keep)
+    x = np.random.default_rng(5).normal(0, 1, (4, K)).astype(np.float16)
+    y = gpu_forward(layer, x)
+    check_bound(y, layer, x, what="fitted int4 2:4 layer")
+    q8, s8, k8 = _gpu_fit_int(W, 8, "bitmap", 60)
+    layer8 = LogicalLayer(K=K, N=N, dense="int8", mask="bitmap", qvals=q8, row_scale=s8, keep=k8)
+    y8 = gpu_forward(layer8, x)
+    check_bound(y8, layer8, x, what="fitted int8 bitmap layer")
