@@ -199,3 +199,36 @@ def fit_int(W, bits: int, mask: str, grid: int):
     for n in range(N):
         s[n], q[n] = clip_search_row(W16[n], keep[n], bits, grid)
     return q, s, keep
+
+
+# ---------------------------------------------------------------------------
+# AbsMax group quantization of the low-rank factors
+# ---------------------------------------------------------------------------
+#
+# "SLiM" page, review highlights: the low-rank adapters are quantized with an
+# AbsMax group scheme, group size 128.  Readings: 4-bit codes, groups of `group`
+# consecutive entries along the first axis of the factor as stored logically
+# (L [K, r]: along K for each rank column; R [r, N]: along r for each output
+# column), scale = fp16(max|v| / 7) (fp64 division, nearest-even fp16),
+# q = clamp(rint(v / scale), -8, 7) in fp64; an all-zero group gets scale 0, q 0.
+
+def absmax_groups(F16, group: int, dtype: str = "f16"):
+    """q int8 [R, C], scale fp16 [ceil(R / group), C] of a factor given as fp16
+    values or bf16 bit patterns."""
+    if dtype == "bf16":
+        u = np.asarray(F16, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        v = u.view(np.float32).astype(np.float64)
+    else:
+        v = np.asarray(F16, dtype=np.float16).astype(np.float64)
+    R, C = v.shape
+    ng = -(-R // group)
+    q = np.zeros((R, C), dtype=np.int8)
+    sc = np.zeros((ng, C), dtype=np.float16)
+    for g in range(ng):
+        blk = v[g * group:(g + 1) * group]
+        s = round_to_f16(np.abs(blk).max(axis=0) / 7.0)
+        sc[g] = s.astype(np.float16)
+        for c in range(C):
+            if s[c] > 0:
+                q[g * group:(g + 1) * group, c] = np.clip(np.rint(blk[:, c] / s[c]), -8, 7).astype(np.int8)
+    return q, sc

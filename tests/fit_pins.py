@@ -208,9 +208,49 @@ def pin_clip_never_worse_than_absmax(F):
         assert np.abs(q[n]).max() <= 7
 
 
+# ---------------------------------------------------------------------------
+# AbsMax group quantization of factors
+# ---------------------------------------------------------------------------
+
+def pin_absmax_worked_example(F):
+    # SLiM page, highlights (AbsMax groups).  Column 0, group 4: [0.875, -1.75, 0.375, 0]:
+    # max = 1.75, scale = 1.75 / 7 = 0.25 (exact); v / s = [3.5, -7, 1.5, 0] -> rint (ties to
+    # even) [4, -7, 2, 0].  Ragged second group [0.4375]: scale 0.0625, q = 7.
+    # Column 1 is all zero: scale 0, q 0.
+    v = np.array([[0.875, 0], [-1.75, 0], [0.375, 0], [0, 0], [0.4375, 0]], np.float16)
+    q, sc = F.absmax_groups(v, 4)
+    assert float(sc[0, 0]) == 0.25 and float(sc[0, 1]) == 0.0 and float(sc[1, 0]) == 0.0625
+    assert list(q[:, 0]) == [4, -7, 2, 0, 7] and not q[:, 1].any()
+
+
+def pin_absmax_properties(F):
+    r = _rng(74)
+    for dtype in ("f16", "bf16"):
+        for R, C, g in ((300, 5, 128), (37, 3, 8), (10, 4, 1)):
+            x = r.normal(0, 0.01, (R, C))
+            if dtype == "bf16":
+                v = (np.ascontiguousarray(x.astype(np.float32)).view(np.uint32) + 0x8000 >> 16).astype(np.uint16)
+                vf = (v.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            else:
+                v = x.astype(np.float16)
+                vf = v.astype(np.float64)
+            q, sc = F.absmax_groups(v, g, dtype)
+            assert sc.shape == (-(-R // g), C) and np.abs(q).max() <= 7
+            s_full = np.repeat(sc.astype(np.float64), g, axis=0)[:R]
+            # every value is within half a step of its code, and each group's
+            # largest magnitude maps to +-7
+            assert np.all(np.abs(vf - s_full * q) <= s_full / 2 + 1e-300)
+            for gi in range(sc.shape[0]):
+                blk = np.abs(vf[gi * g:(gi + 1) * g])
+                for c in range(C):
+                    j = int(np.argmax(blk[:, c]))
+                    assert abs(int(q[gi * g + j, c])) == 7
+
+
 ALL_PINS = [pin_worked_example, pin_round_f16_library, pin_outliers_brute, pin_kmeans_fixed_point,
             pin_kmeans_sklearn, pin_sse_monotone, pin_codes_and_residual, pin_int_worked_example,
-            pin_masks_brute, pin_clip_search_fractions, pin_clip_never_worse_than_absmax]
+            pin_masks_brute, pin_clip_search_fractions, pin_clip_never_worse_than_absmax,
+            pin_absmax_worked_example, pin_absmax_properties]
 
 
 def failing_pins(F):

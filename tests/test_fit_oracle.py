@@ -192,3 +192,29 @@ def test_fit_pins_catch_int_mutant(mutate):
     F = fresh()
     mutate(F)
     assert fit_pins.failing_pins(F), f"no pin caught {mutate.__name__}"
+
+
+def _mut_absmax_axis(F):
+    orig = F.absmax_groups
+
+    def absmax_groups(F16, group, dtype="f16"):
+        q, sc = orig(np.asarray(F16).T, group, dtype)
+        ng = -(-np.asarray(F16).shape[0] // group)
+        return q.T, np.resize(sc.T, (ng, np.asarray(F16).shape[1])).astype(np.float16)
+    F.absmax_groups = absmax_groups
+
+
+def _mut_absmax_div8(F):
+    src = F.absmax_groups
+
+    def absmax_groups(F16, group, dtype="f16"):
+        q, sc = src(F16, group, dtype)
+        return np.clip(np.rint(q * 7 / 8), -8, 7).astype(np.int8), (sc.astype(np.float64) * 8 / 7).astype(np.float16)
+    F.absmax_groups = absmax_groups
+
+
+@pytest.mark.parametrize("mutate", [_mut_absmax_axis, _mut_absmax_div8], ids=lambda f: f.__name__[5:])
+def test_fit_pins_catch_absmax_mutant(mutate):
+    F = fresh()
+    mutate(F)
+    assert fit_pins.failing_pins(F), f"no pin caught {mutate.__name__}"
