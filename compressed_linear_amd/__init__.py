@@ -14,7 +14,7 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["ClError", "lib", "pack", "blob_header", "CompressedLinear", "fit_lut", "fit_int", "LIB_PATH",
+__all__ = ["ClError", "lib", "pack", "blob_header", "CompressedLinear", "fit_lut", "fit_int", "quant_absmax", "LIB_PATH",
            "EXPORTED_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcompressed_linear.so")
@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcompress
 EXPORTED_SYMBOLS = [
     "cl_pack", "cl_device_bytes", "cl_create", "cl_forward", "cl_forward_path",
     "cl_debug_dequant", "cl_destroy", "cl_last_error", "cl_fit_lut_work_bytes", "cl_fit_lut",
-    "cl_fit_int",
+    "cl_fit_int", "cl_quant_absmax",
 ]
 
 DENSE = {"lut3": 0, "lut4": 1, "int4": 2, "int8": 3}
@@ -116,6 +116,8 @@ def lib():
         L.cl_fit_lut.restype = ctypes.c_int
         L.cl_fit_int.argtypes = [ctypes.c_void_p] + [ctypes.c_int32] * 5 + [ctypes.c_void_p] * 5
         L.cl_fit_int.restype = ctypes.c_int
+        L.cl_quant_absmax.argtypes = [ctypes.c_void_p] + [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3
+        L.cl_quant_absmax.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -340,3 +342,20 @@ def fit_int(W, bits: int, mask: str = "none", grid: int = 100):
                           torch.cuda.current_stream(dev).cuda_stream)
     _check(st, "cl_fit_int")
     return q, s, keep
+
+
+def quant_absmax(F, group: int = 128):
+    """AbsMax int4 groups of a factor on the GPU (cl_quant_absmax): F is a torch
+    fp16 or bf16 [R, C] tensor on a ROCm device, grouped along R.  Returns device
+    tensors (q int8 [R, C], scale fp16 [ceil(R / group), C])."""
+    import torch
+    if F.dtype not in (torch.float16, torch.bfloat16) or F.dim() != 2 or not F.is_cuda:
+        raise ValueError("F must be a 2-D float16 / bfloat16 tensor on a ROCm device")
+    F = F.contiguous()
+    R, C = F.shape
+    q = torch.empty((R, C), dtype=torch.int8, device=F.device)
+    sc = torch.empty((-(-R // group), C), dtype=torch.float16, device=F.device)
+    st = lib().cl_quant_absmax(F.data_ptr(), R, C, group, 1 if F.dtype == torch.bfloat16 else 0, q.data_ptr(),
+                               sc.data_ptr(), torch.cuda.current_stream(F.device).cuda_stream)
+    _check(st, "cl_quant_absmax")
+    return q, sc

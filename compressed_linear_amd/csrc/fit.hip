@@ -575,6 +575,36 @@ __global__ void __launch_bounds__(kFitThreads) fit_int_kernel(const uint16_t* __
   }
 }
 
+// ---- AbsMax int4 groups of a low-rank factor, one thread per (group, column) ----
+// "SLiM" page, review highlights: the adapters are quantized with an AbsMax group
+// scheme, group size 128.  F is [R, C] (L [K, r]: groups along K; R [r, N]:
+// groups along r); scale = fp16(max|v| / 7) (fp64 division, nearest-even fp16),
+// q = clamp(rint(v / scale), -8, 7) in fp64; an all-zero group: scale 0, q 0.
+template <bool BF16>
+__global__ void __launch_bounds__(256) fit_absmax_kernel(const uint16_t* __restrict__ F, int R, int C, int group,
+                                                         int8_t* __restrict__ q, uint16_t* __restrict__ scale) {
+  const int cb = (C + 255) / 256, g = (int)(blockIdx.x / cb), c = (int)(blockIdx.x % cb) * 256 + (int)threadIdx.x;
+  if (c >= C) return;
+  const int r0 = g * group, r1 = min(R, r0 + group);
+  auto val = [&](int r) -> double {
+    const uint16_t h = F[(size_t)r * C + c];
+    return BF16 ? (double)__uint_as_float((uint32_t)h << 16) : f16_to_f64(h);
+  };
+  double m = 0.0;
+  for (int r = r0; r < r1; ++r) m = fmax(m, fabs(val(r)));
+  const uint16_t s16 = f64_to_f16_rne(m / 7.0);
+  scale[(size_t)g * C + c] = s16;
+  const double sd = f16_to_f64(s16);
+  for (int r = r0; r < r1; ++r) {
+    double qd = 0.0;
+    if (sd > 0.0) {
+      qd = rint(val(r) / sd);
+      qd = qd > 7.0 ? 7.0 : (qd < -8.0 ? -8.0 : qd);
+    }
+    q[(size_t)r * C + c] = (int8_t)qd;
+  }
+}
+
 }  // namespace
 
 }  // namespace cl
@@ -658,5 +688,24 @@ extern "C" cl_status cl_fit_int(const uint16_t* W, int32_t N, int32_t K, int32_t
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(CL_EHIP, "fit failed: %s", hipGetErrorString(e));
   if (flag) return fail(CL_EINVAL, "a weight is not finite (outputs are not valid)");
+  return CL_OK;
+}
+
+extern "C" cl_status cl_quant_absmax(const uint16_t* F, int32_t R, int32_t C, int32_t group, int32_t bf16, int8_t* q,
+                                     uint16_t* scale, void* stream) {
+  clear_error();
+  if (R < 1 || C < 1 || group < 1) return fail(CL_EINVAL, "R, C and group must be >= 1");
+  if ((long long)R * C > (1ll << 40)) return fail(CL_ESIZE, "the factor is too large");
+  if (!F || !q || !scale) return fail(CL_EINVAL, "a required pointer is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const long long blocks = ceil_div(C, 256) * ceil_div(R, group);
+  if (blocks > 0x7FFFFFFFLL) return fail(CL_ESIZE, "the factor is too large");
+  const dim3 grid((unsigned)blocks);
+  if (bf16)
+    hipLaunchKernelGGL(fit_absmax_kernel<true>, grid, dim3(256), 0, s, F, R, C, group, q, scale);
+  else
+    hipLaunchKernelGGL(fit_absmax_kernel<false>, grid, dim3(256), 0, s, F, R, C, group, q, scale);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CL_EHIP, "launch failed: %s", hipGetErrorString(e));
   return CL_OK;
 }

@@ -328,6 +328,24 @@ cl_status cl_fit_int(const uint16_t* W, int32_t N, int32_t K, int32_t bits, int3
                      int8_t* qvals, uint16_t* row_scale, uint8_t* keep, void* work, void* stream);
 
 /*
+ * cl_quant_absmax -- AbsMax int4 group quantization of a low-rank factor on the
+ * GPU ("SLiM" page, review highlights: the adapters are quantized with an AbsMax
+ * group scheme, group size 128), the step before cl_pack for CL_LR_INT4.
+ *   F       device, [R, C] fp16 values (bf16 = 0) or bf16 bit patterns (bf16 = 1),
+ *           finite; L is passed as [K, r], R as [r, N].
+ *   group   groups of `group` consecutive entries along the first axis, per column
+ *           (the last one ragged).
+ *   q       device, [R, C] int8 codes: clamp(rint(v / scale), -8, 7) in fp64.
+ *   scale   device, [ceil(R / group), C] fp16: fp16(max|v| / 7) of the group (fp64
+ *           division, nearest-even); 0 for an all-zero group (its codes 0) --
+ *           the L_scale / R_scale layouts cl_pack takes.
+ *   stream  hipStream_t; asynchronous.
+ * Errors: CL_EINVAL (sizes, NULL pointers), CL_ESIZE, CL_EHIP.
+ */
+cl_status cl_quant_absmax(const uint16_t* F, int32_t R, int32_t C, int32_t group, int32_t bf16, int8_t* q,
+                          uint16_t* scale, void* stream);
+
+/*
  * Header at the start of every packed blob (little endian).  Exposed so that
  * tools can inspect a blob; the section layouts are documented with the
  * packer.

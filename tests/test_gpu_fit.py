@@ -16,7 +16,7 @@ import pytest
 import compressed_linear_amd as cla
 from oracle import fit_oracle as F
 from gpu_util import check_bound, gpu_forward, torch_cuda
-from synth.layers import LogicalLayer
+from synth.layers import LogicalLayer, bf16_bits_from_f32, make_layer, make_x
 
 pytestmark = pytest.mark.gpu
 
@@ -204,3 +204,44 @@ def test_fit_int_then_forward():
     layer8 = LogicalLayer(K=K, N=N, dense="int8", mask="bitmap", qvals=q8, row_scale=s8, keep=k8)
     y8 = gpu_forward(layer8, x)
     check_bound(y8, layer8, x, what="fitted int8 bitmap layer")
+
+
+# ---------------------------------------------------------------------------
+# AbsMax int4 groups of the low-rank factors (cl_quant_absmax)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("R,C,g", [(4096, 128, 128), (1000, 70, 128), (37, 5, 8), (9, 300, 1), (11008, 64, 128)])
+def test_quant_absmax_bit_exact(dtype, R, C, g):
+    torch = torch_cuda()
+    r = np.random.default_rng(R + C + g)
+    x = r.normal(0, 0.01, (R, C))
+    x[: min(g, R), 0] = 0.0  # an all-zero group
+    if dtype == "bf16":
+        bits = bf16_bits_from_f32(x.astype(np.float32))
+        Fd = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        host = bits
+    else:
+        host = x.astype(np.float16)
+        Fd = torch.from_numpy(host).cuda()
+    say("absmax", dtype, R, C, g)
+    q, sc = cla.quant_absmax(Fd, g)
+    torch.cuda.synchronize()
+    oq, osc = F.absmax_groups(host, g, dtype)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16), osc.view(np.uint16))
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
+def test_quant_absmax_then_forward():
+    # rank-64 factors quantized on the GPU feed an int4 low-rank layer
+    torch = torch_cuda()
+    r = np.random.default_rng(9)
+    base = make_layer(3, 1, K=768, N=130)
+    Lf = r.normal(0, 0.01, (768, 64)).astype(np.float16)
+    Rf = r.normal(0, 0.01, (64, 130)).astype(np.float16)
+    Lq, Ls = cla.quant_absmax(torch.from_numpy(Lf).cuda(), 128)
+    Rq, Rs = cla.quant_absmax(torch.from_numpy(Rf).cuda(), 128)
+    layer = base.with_(lr="int4", rank=64, group=128, L=Lq.cpu().numpy(), R=Rq.cpu().numpy(),
+                       L_scale=Ls.cpu().numpy(), R_scale=Rs.cpu().numpy())
+    x = make_x(3, 1, 8, K=768)
+    check_bound(gpu_forward(layer, x), layer, x, what="int4 factors quantized on the GPU")
