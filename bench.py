@@ -283,6 +283,8 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--M", type=int, default=1)
     ap.add_argument("--path", default="auto")
+    ap.add_argument("--graph", action="store_true",
+                    help="record one pass over the rotating copies into a HIP graph and time its replays")
     ap.add_argument("--act-scale", type=float, default=0.0,
                     help="scale this fraction of each layer's input channels (SLiM's output-error variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -346,11 +348,39 @@ def main():
         step(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(a.steps):
-        step(a.warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    if a.graph:
+        # one pass over the rotating copies recorded into a HIP graph, replayed
+        gs = torch.cuda.Stream(device=dev)
+        gsp = gs.cuda_stream
+
+        def steps_on(handle):
+            for i in range(R):
+                for h, xp, yp in ptrs[i]:
+                    st = fwd(h, M, xp, yp, handle, path)
+                    if st != 0:
+                        raise cla.ClError(st, "cl_forward", cla.lib().cl_last_error().decode())
+        with torch.cuda.stream(gs):
+            steps_on(gsp)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            steps_on(gsp)
+        torch.cuda.synchronize()
+        reps = max(1, -(-a.steps // R))
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        a.steps = reps * R
+    else:
+        e0.record(stream)
+        for i in range(a.steps):
+            step(a.warmup + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
     ms_per_step = ms / a.steps
     n_launch = len(built)
@@ -404,6 +434,8 @@ def main():
         "dtype": dtype,
         "data": "synthetic (seeded; LLaMA layer shapes, random codes/LUTs/outliers)",
         "config": {"workload": f"{CONFIGS[cfg]['desc']}: {layers_desc}"
+                   + (" (HIP graph replay)" if a.graph else "")
+                   + ""
                    + (f", {a.act_scale:.1%} of input channels scaled" if a.act_scale > 0 else ""), "batch": M,
                    "layers_per_step": n_launch, "rotating_copies": R,
                    "algorithmic_bytes_per_step": int(set_bytes)},

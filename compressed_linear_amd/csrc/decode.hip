@@ -31,6 +31,16 @@ extern template hipError_t launch_mfma_kind<K_INT8_BM>(const MfArgs&, bool, hipS
 // Smallest batch that the automatic choice sends to the matrix-core decode kernel.
 constexpr int kMfMinM = 4;
 
+// The epoch a launch with the low-rank prologue inside publishes: a new nonzero
+// value per direct call; 0 while the stream is being recorded into a graph (the
+// launch then derives its generation on the device, so replays stay valid).
+static uint32_t next_epoch(const Layer& L, hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) == hipSuccess && st != hipStreamCaptureStatusNone) return 0u;
+  if (++L.lr_epoch == 0) ++L.lr_epoch;
+  return L.lr_epoch;
+}
+
 // Whether the decode kernels can read the caller's activations raw and edit
 // them (the clamp, the per-channel factors) while staging them: rows of
 // 16-byte aligned loads (K a multiple of 8) and no low-rank prologue kernel of
@@ -97,7 +107,7 @@ static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float
     a.lr_ntj = L.lr_rpad / 64;
     a.lrp.ntiles = a.lr_ntj * (int)ceil_div(M, kMfLrTile);
     a.lrp.flag = L.lr_cnt + 65;
-    a.lrp.epoch = ++L.lr_epoch;
+    a.lrp.epoch = next_epoch(L, stream);
     a.lrp.clamp = a.clamp;
     a.lrp.cval = a.cval;
     a.lrp.xscale = a.xscale;
@@ -185,14 +195,13 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
         r.lrp.clamp = r.clamp;
         r.lrp.cval = r.cval;
         r.lrp.xscale = r.xscale;
-        const uint32_t epoch = ++L.lr_epoch;
         r.lrp.flag = L.lr_cnt + 65;
-        r.lrp.epoch = epoch;
+        r.lrp.epoch = next_epoch(L, stream);
         r.lr_ntj = L.lr_rpad / 64;
         r.lr_wgs = L.lr_S * r.lr_ntj * (int)ceil_div(M, lowrank_tile_m(M));
         r.lr_mode = L.lr_mode;
         r.lr_flag = r.lrp.flag;
-        r.lr_epoch = epoch;
+        r.lr_epoch = r.lrp.epoch;
       } else {
         const hipError_t e = launch_lowrank_prologue(L, M, x, stream);
         if (e != hipSuccess) return e;

@@ -33,9 +33,9 @@
 // page, review highlights: y += (x' L) R) is added by the slice-0 workgroups as
 // extra MFMA steps over [t_hi | t_lo] x [R^T | R^T], t = x' L in fp32 split
 // into two 16-bit parts.  t comes from the launch's first workgroups (the split
-// prologue block of the batch-1 kernel, publishing the forward's epoch) or from
-// a kernel before it; the workgroups of the last K slice, dispatched last, add
-// the rank term and wait for the epoch first.  The slices' partial sums meet
+// prologue block of the batch-1 kernel, publishing the launch's generation) or
+// from a kernel before it; the workgroups of the last K slice, dispatched last,
+// add the rank term and wait for that generation first.  The slices' partial sums meet
 // through device-scope stores, and the last workgroup of a tile adds them in
 // slice order (deterministic, no float atomics).  With an activation clamp or
 // per-channel activation factors the activations are edited while they are staged.
@@ -81,7 +81,9 @@ struct MfArgs {
   const uint16_t* xscale;       // then multiply them by these per-channel factors ([K] fp16; NULL: none)
   // low-rank prologue in this launch: workgroups [0, lr_wgs) run the split
   // prologue block (activation tiles of 4 rows, lr_mode 0 or 1) and publish
-  // lrp.epoch in *lrp.flag; lr_wgs = 0: t was computed by an earlier kernel
+  // lrp.epoch (or, for epoch 0, the launch's generation), which the last
+  // slice's workgroups wait for (and, in a recorded launch, count themselves
+  // done after); lr_wgs = 0: t was computed by an earlier kernel
   LrSplitArgs lrp;
   int lr_wgs, lr_ntj, lr_mode;
 };
@@ -502,7 +504,8 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   // ---- rank term (last slice): [t_hi | t_lo] x [R^T | R^T] on the matrix cores ----
   if (a.r16 != nullptr && z == a.S - 1) {
     const int rp2 = 2 * a.rp, trow = mf_trow(a.rp);
-    if (a.lr_wgs > 0 && wave == 0) wait_lowrank(a.lrp.flag, a.lrp.epoch, lane);
+    const uint32_t target = a.lr_wgs > 0 ? lr_target(a.lrp.flag, a.lrp.epoch) : 0u;
+    if (a.lr_wgs > 0 && wave == 0) wait_lowrank(lr_word(a.lrp.flag, a.lrp.epoch), target, lane);
     __syncthreads();  // t is published; every wave is done with the activation slice
     for (int i = tid; i < (MT + 1) * a.rp; i += 256) {  // row MT: zeros
       const int m = i / a.rp, j = i - m * a.rp;
@@ -513,7 +516,8 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
       *reinterpret_cast<uint16_t*>(sb + m * trow + j * 2) = (uint16_t)hi;
       *reinterpret_cast<uint16_t*>(sb + m * trow + (a.rp + j) * 2) = (uint16_t)lo;
     }
-    __syncthreads();
+    __syncthreads();  // the workgroup's reads of t are done (their values are in LDS)
+    if (a.lr_wgs > 0 && a.lrp.epoch == 0 && tid == 0) lr_reader_done(a.lrp.flag, target, a.tiles, tile);
     const brsrc_t rr = make_rsrc(a.r16, (uint32_t)a.Npad * (uint32_t)rp2 * 2u);
     for (int s = 0; s < rp2 / 16; ++s) {
       const uint4 wv = bload128(rr, ((uint32_t)n * (uint32_t)rp2 + (uint32_t)(16 * s + 8 * half)) * 2u, 0);

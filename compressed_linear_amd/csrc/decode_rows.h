@@ -66,11 +66,13 @@ struct RowArgs {
   int lds_x;  // byte offset of the staged activations in the dynamic LDS
   // Low-rank prologue in the same launch: workgroups [0, lr_wgs) compute t
   // (lr_mode 0 or 1, blocks S x lr_ntj x activation tiles) and publish
-  // lr_epoch in *lr_flag; the row workgroups wait for it before reading t.
+  // lr_epoch, or for lr_epoch 0 (a launch recorded into a graph) the launch's
+  // generation (lr_target); the row workgroups wait for it before reading t
+  // and, in a recorded launch, count themselves done afterwards.
   // lr_wgs = 0: t was computed by an earlier kernel (lr_flag NULL).
   LrSplitArgs lrp;
   int lr_wgs, lr_ntj, lr_mode;
-  const uint32_t* lr_flag;
+  uint32_t* lr_flag;
   uint32_t lr_epoch;
   // raw activations (ldx = K): clamp them to [-cval, cval] and multiply them by
   // the per-channel factors xscale ([K] fp16; NULL: none) while staging them
@@ -407,7 +409,8 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   if constexpr (LR) {
     // t is ready once the prologue (earlier kernel, or this launch's first
     // workgroups) has published it; read through the coherent path
-    if (a.lr_flag != nullptr) wait_lowrank(a.lr_flag, a.lr_epoch, lane);
+    const uint32_t target = a.lr_flag != nullptr ? lr_target(a.lr_flag, a.lr_epoch) : 0u;
+    if (a.lr_flag != nullptr) wait_lowrank(lr_word(a.lr_flag, a.lr_epoch), target, lane);
     float tv[MB][4];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
@@ -422,6 +425,10 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int m = 0; m < MB; ++m) acc[r][m] = __builtin_fmaf(tv[m][i], rv[r][i], acc[r][m]);
+    if (a.lr_flag != nullptr && a.lr_epoch == 0) {  // recorded launch: the workgroup's reads of t are done
+      __syncthreads();
+      if (tid == 0) lr_reader_done(a.lr_flag, target, (int)gridDim.x - a.lr_wgs, (int)blockIdx.x - a.lr_wgs);
+    }
   }
   // ---- reduce over the lanes and store ----
 #pragma unroll

@@ -62,9 +62,11 @@ struct Layer {
   uint8_t* lr_lk = nullptr;      // L, k-major in k pairs: 16-bit [Kl/2][rpad][2]; int4 bytes [Kl/2][rpad] (k even low nibble)
   uint16_t* lr_ls = nullptr;     // int4: scales k-major [ceil(Kl/group)][rpad]
   float* lr_part = nullptr;      // partial sums [tiles][S][256]
-  uint32_t* lr_cnt = nullptr;    // [128]: arrivals per output tile [0, 64), completed tiles [64],
-                                 // published epoch [65]; counters zero between forwards
-  mutable uint32_t lr_epoch = 0; // decode launches with a prologue inside (each publishes the next value)
+  mutable uint32_t lr_epoch = 0; // epochs of direct calls with the prologue inside (never 0)
+  uint32_t* lr_cnt = nullptr;    // [kLrCntWords]: arrivals per output tile [0, 64), completed tiles [64],
+                                 // published epoch [65], published generation [66], finished
+                                 // generation [67], finished reader slots [68], reader slots at
+                                 // 128 + 32 j (j < 32); counters zero between forwards
 
   // matrix-core decode (batch 2..32; absent when max_M == 1)
   int mf_npw = 0, mf_Kz = 0, mf_S = 0, mf_tiles = 0;
@@ -83,8 +85,8 @@ hipError_t launch_prep_x(const Layer& L, int M, const void* x, hipStream_t strea
 hipError_t launch_lowrank_prologue(const Layer& L, int M, const void* x, hipStream_t stream);
 // decode forward (M <= kMaxDecodeM), including the activation clamp / restaging
 // (x: the caller's activations, or L.xprep when done already) and the low-rank
-// prologue: inside the decode launch when it applies (publishing ++lr_epoch),
-// else as kernels of their own.
+// prologue: inside the decode launch when it applies (publishing the launch's
+// generation, derived on the device), else as kernels of their own.
 // variant: 0 the faster kernel for M, 1 the vector-ALU kernels, 2 the matrix-core kernel
 hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, int variant);
 hipError_t launch_prefill(const Layer& L, int M, const void* x, float* y, hipStream_t stream);

@@ -82,6 +82,7 @@ inline int pf_tile_rows(int dense) { return dense == 0 ? 256 : kPfTileN; }
 // of whole passes (a pass is eight chunks of every row of the tile).
 constexpr int kMfRows = 128;    // weight rows per workgroup (four wavefronts of 32)
 constexpr int kMfCph = 4;       // chunks per lane half per pass (two halves read one 128-byte line of a row)
+constexpr int kLrCntWords = 128 + 32 * 32;  // low-rank prologue counters and generation words (u32)
 constexpr int kMfKzMax = 1024;  // largest K slice (bounds the activation staging in LDS)
 // (the bitmap format: one chunk per lane half and pass)
 inline int mf_pass_k(int dense, int mask) {

@@ -31,8 +31,9 @@ struct LrSplitArgs {
   uint32_t* cnt;      // arrivals per (tj, tm) tile
   float* t;
   // inside the decode kernel only (NULL otherwise): the workgroup that
-  // completes the last tile publishes `epoch` in *flag once every t value of
-  // this forward is in memory; `done` counts completed tiles
+  // completes the last tile publishes the launch's epoch (or, for epoch 0, its
+  // generation; see lr_target) once every t value of the forward is in memory;
+  // `done` counts completed tiles
   uint32_t* done;
   uint32_t* flag;
   uint32_t epoch;
@@ -100,13 +101,50 @@ __device__ __forceinline__ uint4 scale_act8(uint4 v, uint4 f) {
   return make_uint4(u[0], u[1], u[2], u[3]);
 }
 
+// Publication of t by a prologue inside a decode launch.  Words of the
+// counters from `flag` (word 65) on: [0] the epoch published by the last
+// launch called directly (the host passes a new epoch each call), [1] the
+// generation published by the last launch recorded into a graph, [2] gen, the
+// generation of the last recorded launch whose readers of t have all finished,
+// [3] the count of finished reader slots; from word 128 on, kLrSlots slot
+// counters of finished readers, one per 128-byte line (atomics on one line
+// serialize).  A recorded launch gets epoch 0 and derives its generation,
+// gen + 1, on the device, so that a replay needs no new argument: gen only
+// moves when the launch's last reader is done, so every workgroup of the
+// launch reads the same value.  The two kinds keep separate words, so direct
+// calls and replays can interleave.
+constexpr int kLrSlots = 32;
+__device__ __forceinline__ uint32_t lr_target(const uint32_t* flag, uint32_t epoch) {
+  return epoch ? epoch
+               : __hip_atomic_load(const_cast<uint32_t*>(flag) + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+}
+__device__ __forceinline__ uint32_t* lr_word(const uint32_t* flag, uint32_t epoch) {
+  return const_cast<uint32_t*>(flag) + (epoch ? 0 : 1);
+}
+
+// Recorded launches: one call per reader of t (reader `idx` of `readers`) after
+// its last read of t; the last one of the launch moves gen on.
+__device__ __forceinline__ void lr_reader_done(uint32_t* flag, uint32_t generation, int readers, int idx) {
+  const int j = idx % kLrSlots;
+  const int share = readers / kLrSlots + (j < readers % kLrSlots ? 1 : 0);
+  const int used = readers < kLrSlots ? readers : kLrSlots;
+  uint32_t* slot = flag - 65 + 128 + 32 * j;
+  if (__hip_atomic_fetch_add(slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(share - 1)) {
+    __hip_atomic_store(slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__hip_atomic_fetch_add(flag + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(used - 1)) {
+      __hip_atomic_store(flag + 3, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(flag + 2, generation, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Bounded wait for the published t (each poll sleeps a few hundred cycles; the
 // bound, far above any producer's run time, only keeps a wavefront from
-// waiting forever should a producer never publish).  Lane 0 polls.
-__device__ __forceinline__ void wait_lowrank(const uint32_t* flag, uint32_t epoch, int lane) {
+// waiting forever should a producer never publish).  Lane 0 polls `word`.
+__device__ __forceinline__ void wait_lowrank(const uint32_t* word, uint32_t target, int lane) {
   if (lane == 0) {
     uint32_t it = 0;
-    while (__hip_atomic_load(const_cast<uint32_t*>(flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch &&
+    while (__hip_atomic_load(const_cast<uint32_t*>(word), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != target &&
            ++it < (1u << 20))
       __builtin_amdgcn_s_sleep(4);
   }
@@ -303,7 +341,7 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
     return;
   }
   // inside the decode kernel: t through the coherent path, then count the
-  // tile; the last tile publishes this forward's epoch
+  // tile; the last tile publishes this launch's epoch or generation
   if (store) store_dev(a.t + (size_t)(m0 + m) * a.rank + j, tv);
   wait_stores();
   __syncthreads();
@@ -311,7 +349,7 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
     const uint32_t old = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (uint32_t)(a.ntiles - 1)) {
       __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next forward
-      __hip_atomic_store(a.flag, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(lr_word(a.flag, a.epoch), lr_target(a.flag, a.epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

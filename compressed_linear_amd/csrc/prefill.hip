@@ -40,10 +40,10 @@ static hipError_t prefill_by_decode(const Layer& L, int M, const void* x, float*
     Layer Lb = L;
     if (x == L.xprep) Lb.xprep = const_cast<uint16_t*>(static_cast<const uint16_t*>(xb));
     // the bitmap format takes the matrix-core decode kernel (or, for a layer
-    // without its workspace, the tile kernel); a block with a low-rank prologue
-    // inside publishes the next epoch of the layer's count
+    // without its workspace, the tile kernel); each block with a low-rank
+    // prologue inside publishes an epoch (or generation) of its own
     const hipError_t e = launch_decode(Lb, mb, xb, y + (size_t)m0 * L.h.N, stream, 0);
-    L.lr_epoch = Lb.lr_epoch;
+    L.lr_epoch = Lb.lr_epoch;  // the copy took the next epochs
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

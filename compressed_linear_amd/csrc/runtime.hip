@@ -125,7 +125,7 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
     if (lr_mode == 1) o_ls = take((size_t)ceil_div(Kl, h.group) * lr_rpad * 2);
     const int mt = (int)ceil_div(max_M < kMaxDecodeM ? max_M : kMaxDecodeM, 4);
     o_lp = take((size_t)(lr_rpad / 64) * mt * lr_S * 256 * 4);
-    o_lc = take(128 * 4);
+    o_lc = take(kLrCntWords * 4);
   }
   if (L) {
     uint8_t* d = L->dev;
@@ -435,7 +435,7 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
   hipError_t e = hipMemcpyAsync(d, blob, h->total_bytes, hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !lrk.empty()) e = hipMemcpyAsync(L->lr_lk, lrk.data(), lrk.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !lrs.empty()) e = hipMemcpyAsync(L->lr_ls, lrs.data(), lrs.size() * 2, hipMemcpyHostToDevice, s);
-  if (e == hipSuccess && L->lr_cnt) e = hipMemsetAsync(L->lr_cnt, 0, 128 * 4, s);
+  if (e == hipSuccess && L->lr_cnt) e = hipMemsetAsync(L->lr_cnt, 0, kLrCntWords * 4, s);
   if (e == hipSuccess) e = hipMemsetAsync(L->counters, 0, (size_t)(h->n_tiles + ceil_div(max_M, 32) + 8) * 4, s);
   if (e == hipSuccess && !nzs.empty())
     e = hipMemcpyAsync(L->nzstart, nzs.data(), nzs.size() * 4, hipMemcpyHostToDevice, s);

@@ -218,9 +218,10 @@ cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes, int32_t m
  *   dequantised in registers at larger M); larger M runs the prefill kernels
  *   (MFMA on dequantised LDS tiles).
  * One forward at a time per handle (the workspace inside dev_buf is shared).
- * A layer with a low-rank part passes each decode launch a new sequence number
- * (its workgroups publish and wait for it), so a forward recorded into a HIP
- * graph must not be replayed for such a layer.
+ * A forward may be recorded into a HIP graph and replayed: the kernels keep
+ * their own state on the device (counters return to zero, and a launch that
+ * computes x' L_hat inside derives its generation from device memory), so no
+ * argument changes between replays.
  * Deterministic: the same inputs give bitwise identical y.
  * Errors: CL_EINVAL (M out of range, NULL or misaligned pointers),
  * CL_EHIP (launch failure).
