@@ -245,3 +245,14 @@ def test_quant_absmax_then_forward():
                        L_scale=Ls.cpu().numpy(), R_scale=Rs.cpu().numpy())
     x = make_x(3, 1, 8, K=768)
     check_bound(gpu_forward(layer, x), layer, x, what="int4 factors quantized on the GPU")
+
+
+def test_fit_longest_rows():
+    # K = 28672 (LLaMA-70B down projection's rows): the largest row the packers take
+    N, K = 24, 28672
+    W = _weights(17, N, K)
+    say("fit long rows")
+    _same(_gpu_fit(W, 3, int(0.0045 * N * K), 12), F.fit_lut(W, 3, int(0.0045 * N * K), 12), "K=28672 lut3")
+    q, s, keep = _gpu_fit_int(W[:6], 8, "bitmap", 4)
+    oq, os_, ok = F.fit_int(W[:6], 8, "half", 4)
+    assert np.array_equal(s.view(np.uint16), os_.view(np.uint16)) and np.array_equal(q, oq) and np.array_equal(keep, ok)
