@@ -240,3 +240,18 @@ def test_mfma_clamp_and_prologue_in_launch():
         say("bitmap clamp rank M", M)
         check_bound(gpu_forward(bm_lr, x, mod=mod), bm_lr, x, what=f"bitmap clamp rank M={M}")
     mod.close()
+
+
+@pytest.mark.parametrize("K", [1456, 8200])
+def test_bf16_batch1_fp16_staging_and_fallback(K):
+    # bf16 activations that fp16 holds exactly run the fp16 dot products; one
+    # value outside fp16 (huge, or a tiny one with bits below fp16's resolution)
+    # sends the whole row to the bf16 path: both within the bound
+    layer = make_layer(5, 0, K=K, N=190)
+    x = make_x(5, 0, 1, K=K)
+    say("bf16 batch 1", K)
+    check_bound(gpu_forward(layer, x, path="decode"), layer, x, what="exact in fp16")
+    for bad in (np.float32(3.0e5), np.float32(1.2345e-7), np.float32(-7.0e-38)):
+        xb = x.copy()
+        xb[0, K // 3] = bf16_bits_from_f32(np.array([bad], np.float32))[0]
+        check_bound(gpu_forward(layer, xb, path="decode"), layer, xb, what=f"fallback {bad}")
