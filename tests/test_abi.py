@@ -58,3 +58,24 @@ def test_host_errors_without_gpu():
     junk = np.zeros(4096, np.uint8)
     assert L.cl_create(junk.ctypes.data, None, 0, 1, None, ctypes.byref(h)) == -1
     assert b"magic" in L.cl_last_error()
+
+
+def test_packer_entry_points_validate_on_the_host():
+    # argument errors come back before any device work (no GPU needed)
+    L = cla.lib()
+    fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    assert L.cl_fit_lut_work_bytes(0, 5) == 0 and L.cl_fit_lut_work_bytes(4, 4) > 0
+    assert L.cl_fit_lut(fake, 4, 64, 5, 1, 10, fake, fake, fake, fake, fake, fake, None, None) == -1  # bits
+    assert b"bits" in L.cl_last_error()
+    assert L.cl_fit_lut(fake, 4, 40000, 3, 1, 10, fake, fake, fake, fake, fake, fake, None, None) == -5  # K too big
+    assert L.cl_fit_lut(fake, 4, 64, 3, 10 ** 6, 10, fake, fake, fake, fake, fake, fake, None, None) == -1  # n_out
+    assert L.cl_fit_lut(fake, 4, 64, 4, 1, 0, fake, fake, fake, fake, fake, fake, None, None) == -1  # max_iter
+    assert L.cl_fit_lut(None, 4, 64, 4, 1, 5, fake, fake, fake, fake, fake, fake, None, None) == -1  # NULL W
+    assert L.cl_fit_int(fake, 4, 64, 8, 1, 10, fake, fake, fake, fake, None) == -2  # 2:4 needs int4
+    assert L.cl_fit_int(fake, 4, 62, 4, 1, 10, fake, fake, fake, fake, None) == -2  # 2:4 needs K % 4 == 0
+    assert L.cl_fit_int(fake, 4, 64, 4, 2, 10, fake, fake, fake, fake, None) == -2  # unstructured needs int8
+    assert L.cl_fit_int(fake, 4, 64, 5, 0, 10, fake, fake, fake, fake, None) == -1  # bits
+    assert L.cl_fit_int(fake, 4, 64, 4, 0, 0, fake, fake, fake, fake, None) == -1  # grid
+    assert L.cl_fit_int(fake, 4, 64, 4, 1, 10, fake, fake, None, fake, None) == -1  # keep required with a mask
+    assert L.cl_quant_absmax(fake, 16, 8, 0, 0, fake, fake, None) == -1  # group
+    assert L.cl_quant_absmax(None, 16, 8, 4, 0, fake, fake, None) == -1  # NULL factor
