@@ -412,6 +412,71 @@ def pin_bound(O):
     assert abs(B[0, 1] - 7.125e-3) < 1e-15
 
 
+def pin_forward_and_bound(O):
+    """forward_and_bound, the checker of every GPU parity test, against hand values and the pinned pair."""
+    # lut4_lr_bf16_2x4: W_hat = D + (L R)^T with (L R)^T rows [2, 0.5, 1, 0.125] and [-1, 3, -0.5, 0.75]:
+    # W_hat row 0 = [-2+2, 1.75+0.5, 0+1, -1+0.125] = [0, 2.25, 1, -0.875],
+    # row 1 = [-1/16-1, 2/16+3, -3/16-0.5, -15/16+0.75] = [-1.0625, 3.125, -0.6875, -0.1875];
+    # |x| = [1, 2, 0.5, 4]: bound row 0 = 1e-3 (0 + 4.5 + 0.5 + 3.5) = 8.5e-3,
+    # row 1 = 1e-3 (1.0625 + 6.25 + 0.34375 + 0.75) = 8.40625e-3
+    layer, x, y_exp, _ = load_golden("lut4_lr_bf16_2x4")
+    y, B = O.forward_and_bound(layer, x)
+    assert np.array_equal(y, y_exp), f"{y} != {y_exp}"
+    assert abs(B[0, 0] - 8.5e-3) < 1e-15 and abs(B[0, 1] - 8.40625e-3) < 1e-15, B
+    # lut3_csr_2x10: the hand bound of pin_bound
+    layer, x, y_exp, _ = load_golden("lut3_csr_2x10")
+    y, B = O.forward_and_bound(layer, x)
+    assert np.array_equal(y, y_exp)
+    assert abs(B[0, 0] - 10.5e-3) < 1e-15 and abs(B[0, 1] - 7.125e-3) < 1e-15, B
+    # every worked example: the hand-derived outputs
+    for name in golden_names():
+        layer, x, y_exp, _ = load_golden(name)
+        y, B = O.forward_and_bound(layer, x)
+        assert np.array_equal(y, y_exp), name
+        assert (B >= 0).all(), name
+    # random layers of every format, both activation types, with clamps and rank terms: the same
+    # numbers as the separately pinned forward and bound, bit for bit, on a row subset too
+    r = _rng(123)
+    for seed, (dense, mask, lr, xd) in enumerate([("lut3", "none", "fp16", "f16"), ("lut4", "none", "bf16", "bf16"),
+                                                  ("int4", "2:4", "int4", "f16"), ("int8", "bitmap", "none", "bf16"),
+                                                  ("int4", "none", "none", "f16"), ("int8", "none", "fp16", "f16")]):
+        N, K, rk = 7, 24, 3
+        kw = dict(K=K, N=N, dense=dense, mask=mask, x_dtype=xd)
+        if dense.startswith("lut"):
+            codes, lut = draw_lut_codes(r, r, N, K, int(dense[3]))
+            kw.update(codes=codes, lut=lut)
+        else:
+            lo = -8 if dense == "int4" else -127
+            kw.update(qvals=r.integers(lo, -lo, size=(N, K)).astype(np.int8),
+                      row_scale=(r.random(N) * 0.05 + 0.01).astype(np.float16))
+            if mask == "2:4":
+                kw["keep"] = draw_mask_2_4(r, N, K)
+            elif mask == "bitmap":
+                kw["keep"] = draw_mask_half(r, N, K)
+        rp, col, val = draw_csr(r, r, N, K, density=0.1)
+        kw.update(csr_row_ptr=rp, csr_col=col, csr_val=val)
+        if lr == "int4":
+            kw.update(lr="int4", rank=rk, group=8, L=r.integers(-8, 8, size=(K, rk)).astype(np.int8),
+                      R=r.integers(-8, 8, size=(rk, N)).astype(np.int8),
+                      L_scale=(r.random((3, rk)) * 0.1).astype(np.float16),
+                      R_scale=(r.random((1, N)) * 0.1).astype(np.float16))
+        elif lr == "bf16":
+            kw.update(lr="bf16", rank=rk, L=bf16_bits_from_f32(r.normal(0, 0.1, (K, rk)).astype(np.float32)),
+                      R=bf16_bits_from_f32(r.normal(0, 0.1, (rk, N)).astype(np.float32)))
+        elif lr == "fp16":
+            kw.update(lr="fp16", rank=rk, L=r.normal(0, 0.1, (K, rk)).astype(np.float16),
+                      R=r.normal(0, 0.1, (rk, N)).astype(np.float16))
+        if seed % 2:
+            kw["act_clamp"] = np.float16(1.5)
+        layer = LogicalLayer(**kw)
+        xf = r.normal(0, 1, (3, K)).astype(np.float32)
+        x = bf16_bits_from_f32(xf) if xd == "bf16" else xf.astype(np.float16)
+        for rows in (None, [6, 0, 3]):
+            y, B = O.forward_and_bound(layer, x, rows)
+            assert np.array_equal(y, O.forward(layer, x, rows)), (dense, mask, lr, xd, rows)
+            assert np.array_equal(B, O.bound(layer, x, rows)), (dense, mask, lr, xd, rows)
+
+
 ALL_PINS = [
     pin_golden,
     pin_bf16_decode,
@@ -431,6 +496,7 @@ ALL_PINS = [
     pin_debug_planes,
     pin_row_subset,
     pin_bound,
+    pin_forward_and_bound,
 ]
 
 

@@ -220,6 +220,26 @@ def _mut_round_no_subnormals(O):
     O.round_to_act = round_to_act
 
 
+def _mut_fab_bound_signed(O):
+    # forward_and_bound's tolerance taken on W_hat instead of |W_hat|
+    def forward_and_bound(layer, x, rows=None):
+        xp = O.activations(layer, x)
+        W = O.reconstruct(layer, rows)
+        return xp @ W.T, O.TOL_REL * np.abs(np.abs(xp) @ W.T)
+    O.forward_and_bound = forward_and_bound
+
+
+def _mut_fab_no_rank_term(O):
+    # forward_and_bound's y built from D + S only
+    def forward_and_bound(layer, x, rows=None):
+        xp = O.activations(layer, x)
+        idx = O._rows(layer, rows)
+        W = O.reconstruct(layer, rows)
+        Wds = O.dense_plane(layer, idx) + O.sparse_plane(layer, idx)
+        return xp @ Wds.T, O.TOL_REL * (np.abs(xp) @ np.abs(W).T)
+    O.forward_and_bound = forward_and_bound
+
+
 MUTANTS = [
     _mut_mask_ignored, _mut_scale_per_column, _mut_lut_off_by_one, _mut_sparse_dropped,
     _mut_sparse_sign, _mut_sparse_col_shift, _mut_lowrank_dropped, _mut_lowrank_group_axis,
@@ -227,7 +247,7 @@ MUTANTS = [
     _mut_forward_transposed, _mut_debug_planes_truncate,
     _mut_xscale_ignored, _mut_xscale_times_alpha, _mut_xscale_channel_shift, _mut_xscale_before_clamp,
     _mut_xscale_unrounded, _mut_xscale_round_to_f16_always, _mut_round_truncate, _mut_round_half_away,
-    _mut_round_no_subnormals,
+    _mut_round_no_subnormals, _mut_fab_bound_signed, _mut_fab_no_rank_term,
 ]
 
 
