@@ -78,7 +78,9 @@ struct Layer {
 };
 
 // Workspace layout and size for a blob header (used by cl_device_bytes and cl_create).
-size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L /* may be NULL */, size_t base);
+// *largest (optional) receives the size of the largest single workspace buffer.
+size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L /* may be NULL */, size_t base,
+                        size_t* largest = nullptr);
 
 // Kernel launchers (kernels.hip).  All asynchronous on `stream`.
 hipError_t launch_prep_x(const Layer& L, int M, const void* x, hipStream_t stream);

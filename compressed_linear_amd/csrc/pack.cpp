@@ -38,22 +38,110 @@ cl_status fail(cl_status st, const char* fmt, ...) {
 
 void clear_error() { g_err.clear(); }
 
+// Largest section or device buffer: the kernels address every buffer through
+// a hardware-checked 32-bit byte range whose top half is the "no load" offset.
+constexpr uint64_t kMaxBufferBytes = (uint64_t)1 << 31;
+
+// Section lengths a header implies (the bitmap's DENSE length depends on its
+// kept counts and is checked against NZOFF instead; returned as 0 here).
+static void expected_lengths(const cl_blob_header* h, uint64_t len[CL_SEC_COUNT]) {
+  const KindInfo ki = kind_info(h->dense, h->mask);
+  const uint64_t N = (uint64_t)h->N, K = (uint64_t)h->K, Npad = (uint64_t)h->n_tiles * kTileRows;
+  const uint64_t C = (uint64_t)h->chunks, r = (uint64_t)h->rank, g = h->group > 0 ? (uint64_t)h->group : 1;
+  for (int s = 0; s < CL_SEC_COUNT; ++s) len[s] = 0;
+  const bool bitmap = h->mask == CL_MASK_BITMAP;
+  if (!bitmap) len[CL_SEC_DENSE] = Npad * C * kChunkBytes;
+  if (ki.meta_chunk_bytes) len[CL_SEC_META] = Npad * C * (uint64_t)ki.meta_chunk_bytes;
+  if (bitmap) len[CL_SEC_NZOFF] = (N + 1) * 4;
+  len[CL_SEC_TABLE] = ki.table_entries ? Npad * (uint64_t)ki.table_entries * 2 : Npad * 2;
+  if (h->nnz > 0) {
+    len[CL_SEC_ROWPTR] = (N + 1) * 4;
+    len[CL_SEC_COL] = (uint64_t)h->nnz * 4;
+    len[CL_SEC_VAL] = (uint64_t)h->nnz * 2;
+  }
+  if (h->lr != CL_LR_NONE) {
+    if (h->lr == CL_LR_INT4) {
+      len[CL_SEC_L] = r * ((K + 1) / 2);
+      len[CL_SEC_R] = Npad * ((r + 1) / 2);
+      len[CL_SEC_LSCALE] = (uint64_t)ceil_div((int64_t)K, (int64_t)g) * r * 2;
+      len[CL_SEC_RSCALE] = (uint64_t)ceil_div((int64_t)r, (int64_t)g) * Npad * 2;
+    } else {
+      len[CL_SEC_L] = K * r * 2;
+      len[CL_SEC_R] = r * Npad * 2;
+    }
+  }
+  if (h->n_xscale > 0) len[CL_SEC_XSCALE] = K * 2;
+}
+
+// A blob is trusted by cl_create and the kernels only after this check: the
+// header fields agree with each other, every section has the length the
+// header implies and lies inside total_bytes (overflow-safe), no section
+// reaches 2 GiB, and the contents the host and the kernels index with are in
+// range -- CSR row pointers and columns, the bitmap's row offsets against its
+// keep bits, zero keep bits on the padding rows.  The blob must hold
+// total_bytes bytes (a blob from cl_pack does).
 cl_status check_blob(const void* blob, const cl_blob_header** out) {
   if (!blob) return fail(CL_EINVAL, "blob is NULL");
   if (reinterpret_cast<uintptr_t>(blob) % 8) return fail(CL_EINVAL, "blob is not 8-byte aligned");
   const cl_blob_header* h = static_cast<const cl_blob_header*>(blob);
   if (h->magic != CL_BLOB_MAGIC || h->version != CL_BLOB_VERSION)
     return fail(CL_EINVAL, "not a compressed-linear blob (magic/version)");
-  if (h->K < 1 || h->N < 1 || h->n_tiles != (int32_t)ceil_div(h->N, kTileRows))
+  if (h->K < 1 || h->N < 1 || h->K > (1 << 24) || h->N > (1 << 24) || h->n_tiles != (int32_t)ceil_div(h->N, kTileRows))
     return fail(CL_EINVAL, "blob header has inconsistent dimensions");
-  KindInfo ki = kind_info(h->dense, h->mask);
-  if (ki.span == 0 || ki.span != h->span) return fail(CL_EINVAL, "blob header has an unknown format");
+  const KindInfo ki = kind_info(h->dense, h->mask);
+  if (ki.span == 0 || ki.span != h->span || h->chunks != (int32_t)ceil_div(h->K, ki.span) ||
+      h->meta_chunk_bytes != ki.meta_chunk_bytes)
+    return fail(CL_EINVAL, "blob header has an unknown or inconsistent format");
+  if (h->lr < CL_LR_NONE || h->lr > CL_LR_INT4 || (h->lr == CL_LR_NONE) != (h->rank == 0) || h->rank < 0 ||
+      h->rank > 4096 || (h->lr == CL_LR_INT4 ? h->group < 1 : h->group != 0))
+    return fail(CL_EINVAL, "blob header has an inconsistent low-rank part");
+  if ((h->x_dtype != CL_ACT_F16 && h->x_dtype != CL_ACT_BF16) || (h->has_clamp != 0 && h->has_clamp != 1))
+    return fail(CL_EINVAL, "blob header has an unknown activation type or clamp flag");
+  if (h->nnz < 0 || h->nnz > 0x7FFFFFFFLL) return fail(CL_EINVAL, "blob header has nnz out of range");
+  if (h->n_xscale < 0 || h->n_xscale > h->K) return fail(CL_EINVAL, "blob header has an inconsistent activation-scale section");
+  if (h->total_bytes < sizeof(cl_blob_header)) return fail(CL_EINVAL, "blob header has total_bytes below the header");
+  uint64_t want[CL_SEC_COUNT];
+  expected_lengths(h, want);
   for (int s = 0; s < CL_SEC_COUNT; ++s) {
-    if (h->len[s] && (h->off[s] % 256 || h->off[s] + h->len[s] > h->total_bytes))
+    const uint64_t len = h->len[s], off = h->off[s];
+    if (len >= kMaxBufferBytes) return fail(CL_ESIZE, "blob section %d holds 2 GiB or more", s);
+    if (len && (off % 256 || off < sizeof(cl_blob_header) || len > h->total_bytes || off > h->total_bytes - len))
       return fail(CL_EINVAL, "blob section %d lies outside the blob", s);
+    const bool dense_bm = s == CL_SEC_DENSE && h->mask == CL_MASK_BITMAP;
+    if (!dense_bm && len != want[s])
+      return fail(CL_EINVAL, "blob section %d has %llu bytes, the header implies %llu", s, (unsigned long long)len,
+                  (unsigned long long)want[s]);
   }
-  if (h->n_xscale < 0 || h->n_xscale > h->K || (h->n_xscale > 0) != (h->len[CL_SEC_XSCALE] == (uint64_t)h->K * 2))
-    return fail(CL_EINVAL, "blob header has an inconsistent activation-scale section");
+  const uint8_t* b = static_cast<const uint8_t*>(blob);
+  if (h->nnz > 0) {
+    const int32_t* rp = reinterpret_cast<const int32_t*>(b + h->off[CL_SEC_ROWPTR]);
+    const int32_t* col = reinterpret_cast<const int32_t*>(b + h->off[CL_SEC_COL]);
+    if (rp[0] != 0 || (int64_t)rp[h->N] != h->nnz) return fail(CL_EINVAL, "blob CSR row pointers do not run from 0 to nnz");
+    for (int64_t n = 0; n < h->N; ++n) {
+      if (rp[n + 1] < rp[n]) return fail(CL_EINVAL, "blob CSR row pointers decrease at row %lld", (long long)n);
+      for (int64_t p = rp[n]; p < rp[n + 1]; ++p)
+        if (col[p] < 0 || col[p] >= h->K || (p > rp[n] && col[p] <= col[p - 1]))
+          return fail(CL_EINVAL, "blob CSR columns of row %lld are out of range or not increasing", (long long)n);
+    }
+  }
+  if (h->mask == CL_MASK_BITMAP) {
+    const int32_t* off = reinterpret_cast<const int32_t*>(b + h->off[CL_SEC_NZOFF]);
+    const uint32_t* meta = reinterpret_cast<const uint32_t*>(b + h->off[CL_SEC_META]);
+    const int64_t C = h->chunks, Npad = (int64_t)h->n_tiles * kTileRows;
+    if (off[0] != 0) return fail(CL_EINVAL, "blob bitmap offsets do not start at 0");
+    for (int64_t n = 0; n < Npad; ++n) {
+      int64_t kept = 0;
+      for (int64_t i = 0; i < C * 4; ++i) kept += __builtin_popcount(meta[n * C * 4 + i]);
+      if (n >= h->N) {
+        if (kept) return fail(CL_EINVAL, "blob bitmap keeps weights on padding row %lld", (long long)n);
+        continue;
+      }
+      if (off[n] % 16 || (int64_t)off[n + 1] - (int64_t)off[n] < kept)
+        return fail(CL_EINVAL, "blob bitmap offsets of row %lld do not hold its kept values", (long long)n);
+    }
+    if ((uint64_t)off[h->N] + 64 > h->len[CL_SEC_DENSE])
+      return fail(CL_EINVAL, "blob bitmap values run past their section");
+  }
   if (out) *out = h;
   return CL_OK;
 }
@@ -88,6 +176,27 @@ cl_status validate(const cl_layer_desc* d) {
     return fail(CL_EUNSUPPORTED, "the 2:4 mask is built for INT4 values");
   if (d->mask == CL_MASK_2_4 && d->K % 4) return fail(CL_EUNSUPPORTED, "2:4 needs K %% 4 == 0 (K=%d)", d->K);
   const int64_t K = d->K, N = d->N;
+  {  // sizes first (from the dimensions alone, before any array is read): no section may reach 2 GiB
+    cl_blob_header hd = {};
+    hd.K = d->K;
+    hd.N = d->N;
+    hd.dense = d->dense;
+    hd.mask = d->mask;
+    hd.n_tiles = (int32_t)ceil_div(N, kTileRows);
+    hd.chunks = (int32_t)ceil_div(K, kind_info(d->dense, d->mask).span);
+    hd.lr = d->rank > 0 ? d->lr : CL_LR_NONE;
+    hd.rank = d->lr != CL_LR_NONE && d->rank > 0 ? d->rank : 0;
+    hd.group = d->group > 0 ? d->group : 1;
+    hd.nnz = d->nnz > 0 ? d->nnz : 0;
+    hd.n_xscale = d->n_xscale > 0 ? 1 : 0;
+    uint64_t len[CL_SEC_COUNT];
+    expected_lengths(&hd, len);
+    // (the bitmap's kept values are counted, and checked, once the mask is read)
+    for (int sct = 0; sct < CL_SEC_COUNT; ++sct)
+      if (len[sct] >= kMaxBufferBytes)
+        return fail(CL_ESIZE, "section %d of the device layout would hold %llu bytes (at most 2^31 - 1)", sct,
+                    (unsigned long long)len[sct]);
+  }
   if (lut) {
     if (!d->codes || !d->lut) return fail(CL_EINVAL, "LUT formats need codes and lut");
     const int nb = d->dense == CL_DENSE_LUT3 ? 8 : 16;
@@ -181,7 +290,7 @@ void make_plan(const cl_layer_desc* d, Plan& p) {
   p.nnz = d->nnz;
   const bool has_lr = d->lr != CL_LR_NONE && d->rank > 0;
   p.rank = has_lr ? d->rank : 0;
-  p.group = d->lr == CL_LR_INT4 ? d->group : 0;
+  p.group = has_lr && d->lr == CL_LR_INT4 ? d->group : 0;
 
   uint64_t len[CL_SEC_COUNT] = {};
   const bool bitmap = d->mask == CL_MASK_BITMAP;
@@ -445,6 +554,10 @@ extern "C" cl_status cl_pack(const cl_layer_desc* d, void* blob, size_t* blob_by
   if (st != CL_OK) return st;
   Plan p;
   make_plan(d, p);
+  for (int sct = 0; sct < CL_SEC_COUNT; ++sct)
+    if (p.len[sct] >= kMaxBufferBytes)
+      return fail(CL_ESIZE, "section %d of the device layout would hold %llu bytes (at most 2^31 - 1)", sct,
+                  (unsigned long long)p.len[sct]);
   if (acct) *acct = p.acct;
   if (!blob) {
     *blob_bytes = p.total;

@@ -1,7 +1,6 @@
 // runtime.hip -- the C ABI: upload, forward dispatch, debug dequantisation.
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -11,22 +10,11 @@
 
 namespace cl {
 
-static int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return (v && *v) ? atoi(v) : dflt;
-}
-
-// Split-K workgroups per tile: enough workgroups for about two per CU, each
-// wave still streaming at least a few chunks.  CL_SPLIT overrides (tuning).
+// Split-K workgroups per tile of the tile kernel: enough workgroups for about
+// two per CU, each wave still streaming at least a few chunks.
 static int choose_split(const cl_blob_header& h, int num_cus) {
-  const int forced = env_int("CL_SPLIT", 0);
-  int s;
-  if (forced > 0) {
-    s = forced;
-  } else {
-    const int target = 2 * num_cus;
-    s = (int)((target + h.n_tiles / 2) / h.n_tiles);
-  }
+  const int target = 2 * num_cus;
+  int s = (int)((target + h.n_tiles / 2) / h.n_tiles);
   const int max_by_chunks = h.chunks / (4 * 2) > 0 ? h.chunks / (4 * 2) : 1;
   if (s > max_by_chunks) s = max_by_chunks;
   if (s > 64) s = 64;
@@ -46,13 +34,14 @@ static int lowrank_mode(const cl_blob_header& h) {
   return lbf == xbf ? 0 : -1;
 }
 
-size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t base) {
+size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t base, size_t* largest) {
   const int split = L ? L->split : 64;  // size query: the largest split
   const int Npad = h.n_tiles * 64;
-  size_t off = align256(base);
+  size_t off = align256(base), big = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off = align256(off + bytes);
+    if (bytes > big) big = bytes;
     return o;
   };
   const int mblocks = (int)ceil_div(max_M, 32);
@@ -162,7 +151,18 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
     L->mf_nzs = o_mfz ? reinterpret_cast<int32_t*>(d + o_mfz) : nullptr;
     L->ws_bytes = off - align256(base);
   }
+  if (largest) *largest = big;
   return off;
+}
+
+// The kernels address every device buffer through a 32-bit byte range whose
+// top half is the "no load" offset, so no buffer may reach 2 GiB: a workspace
+// buffer, or the activations of max_M rows.
+static bool buffers_fit(const cl_blob_header& h, int32_t max_M) {
+  size_t largest = 0;
+  workspace_layout(h, max_M, nullptr, h.total_bytes, &largest);
+  const size_t xbytes = (size_t)max_M * (size_t)round_up(h.K, 8) * 2;
+  return largest < ((size_t)1 << 31) && xbytes < ((size_t)1 << 31);
 }
 
 // Host fp16 / bf16 helpers for the prefill's converted copies (round to nearest even).
@@ -313,6 +313,10 @@ using namespace cl;
 extern "C" size_t cl_device_bytes(const void* blob, int32_t max_M) {
   const cl_blob_header* h;
   if (max_M < 1 || check_blob(blob, &h) != CL_OK) return 0;
+  if (!buffers_fit(*h, max_M)) {
+    fail(CL_ESIZE, "a workspace buffer or the activations of max_M rows would reach 2 GiB");
+    return 0;
+  }
   return workspace_layout(*h, max_M, nullptr, h->total_bytes);
 }
 
@@ -325,6 +329,7 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
   cl_status st = check_blob(blob, &h);
   if (st != CL_OK) return st;
   if (max_M < 1) return fail(CL_EINVAL, "max_M must be >= 1");
+  if (!buffers_fit(*h, max_M)) return fail(CL_ESIZE, "a workspace buffer or the activations of max_M rows would reach 2 GiB");
   if (!dev_buf || reinterpret_cast<uintptr_t>(dev_buf) % 256) return fail(CL_EINVAL, "dev_buf must be 256-byte aligned");
   if (h->lr != CL_LR_NONE && h->rank > 256) return fail(CL_EUNSUPPORTED, "ranks above 256 are not built");
   Layer* L = new (std::nothrow) Layer();

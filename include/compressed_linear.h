@@ -171,8 +171,11 @@ typedef struct {
  * (shapes, code or value ranges, a 2:4 group without exactly two kept, CSR
  * pointers not nondecreasing, columns out of range, unsorted or repeated),
  * CL_EUNSUPPORTED for combinations not built (a mask on a LUT format, a
- * 2:4 mask with K % 4 != 0), CL_ESIZE for dimensions above 2^24 or
- * nnz above 2^31 - 1, CL_ENOMEM if *blob_bytes is too small.
+ * 2:4 mask with K % 4 != 0), CL_ESIZE for dimensions above 2^24,
+ * nnz above 2^31 - 1, or a section of the device layout of 2^31 bytes or
+ * more (checked from the dimensions before any array is read; the kernels
+ * address each buffer through a 32-bit range), CL_ENOMEM if *blob_bytes is
+ * too small.
  * The blob is self-describing (it starts with a cl_blob_header) and may be
  * saved and reloaded byte for byte.
  */
@@ -187,7 +190,16 @@ cl_status cl_pack(const cl_layer_desc* desc, void* blob, size_t* blob_bytes, cl_
  * in the 16-bit MFMA input type; for a bitmap layer with max_M > 32, a dense
  * int8 copy of its weights, N*K bytes rounded up, zero where dropped, that the
  * prefill's matrix-core tile loader reads).  Returns 0 if the blob is
- * malformed or max_M < 1.
+ * malformed (the reason in cl_last_error), max_M < 1, or a workspace buffer or
+ * the activations of max_M rows would take 2^31 bytes or more.
+ *
+ * Blob checks (here and in cl_create), on the host: the header fields agree
+ * with each other; every section has the length the header implies and lies
+ * inside total_bytes (overflow-safe); the CSR row pointers run from 0 to nnz
+ * without decreasing and each row's columns increase strictly below K; the
+ * bitmap's row offsets are multiples of 16 that hold each row's kept values
+ * inside its section, and padding rows keep nothing.  The blob buffer must
+ * hold total_bytes bytes (a blob written by cl_pack does).
  */
 size_t cl_device_bytes(const void* blob, int32_t max_M);
 
@@ -201,8 +213,9 @@ size_t cl_device_bytes(const void* blob, int32_t max_M);
  *   stream    hipStream_t for the upload, the workspace clear and the
  *             derived tables (built on the host from the blob, then copied).
  *   handle    out: opaque handle (host memory owned by the library).
- * Errors: CL_EINVAL (malformed blob, NULL or misaligned pointers),
- * CL_ENOMEM (dev_bytes too small), CL_EHIP (copy failed).
+ * Errors: CL_EINVAL (malformed blob, see cl_device_bytes; NULL or misaligned
+ * pointers), CL_ESIZE (a workspace buffer or the activations of max_M rows
+ * at 2^31 bytes or more), CL_ENOMEM (dev_bytes too small), CL_EHIP (copy failed).
  */
 cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes, int32_t max_M,
                     void* stream, void** handle);

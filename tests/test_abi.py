@@ -79,3 +79,94 @@ def test_packer_entry_points_validate_on_the_host():
     assert L.cl_fit_int(fake, 4, 64, 4, 1, 10, fake, fake, None, fake, None) == -1  # keep required with a mask
     assert L.cl_quant_absmax(fake, 16, 8, 0, 0, fake, fake, None) == -1  # group
     assert L.cl_quant_absmax(None, 16, 8, 4, 0, fake, fake, None) == -1  # NULL factor
+
+
+def _blob_of(layer):
+    blob, _ = cla.pack(layer)
+    return blob.copy()
+
+
+def _section(blob, name, dtype):
+    off, ln = cla.blob_header(blob)["sections"][name]
+    return blob[off:off + ln].view(dtype)
+
+
+def _device_bytes(blob, max_M=1):
+    L = cla.lib()
+    n = L.cl_device_bytes(blob.ctypes.data, max_M)
+    return n, L.cl_last_error().decode()
+
+
+def _set_header(blob, field, value, index=None):
+    h = cla.cl_blob_header.from_buffer(blob)
+    if index is None:
+        setattr(h, field, value)
+    else:
+        getattr(h, field)[index] = value
+    return blob
+
+
+def test_corrupt_blobs_are_rejected_on_the_host():
+    # cl_create and the kernels trust a blob only after check_blob; cl_device_bytes runs the
+    # same check without a GPU and returns 0 (with the reason in cl_last_error) for a bad blob
+    from synth.layers import make_layer
+    good = _blob_of(make_layer(1, 0, K=200, N=70))
+    assert _device_bytes(good)[0] > 0
+    nnz = int(cla.blob_header(good)["nnz"])
+    assert nnz > 3
+
+    def bad(mutate, word):
+        b = good.copy()
+        mutate(b)
+        n, msg = _device_bytes(b)
+        assert n == 0 and word in msg, msg
+
+    bad(lambda b: _section(b, "rowptr", np.int32).__setitem__(5, 10 ** 6), "CSR")  # decreasing after row 5
+    bad(lambda b: _section(b, "rowptr", np.int32).__setitem__(-1, nnz - 1), "CSR")  # does not end at nnz
+    bad(lambda b: _section(b, "col", np.int32).__setitem__(0, 200), "CSR")  # column == K
+    bad(lambda b: _section(b, "col", np.int32).__setitem__(0, -1), "CSR")
+    rp = _section(good, "rowptr", np.int32)
+    row = int(np.argmax(np.diff(rp) >= 2))
+    bad(lambda b: _section(b, "col", np.int32).__setitem__(rp[row] + 1, _section(b, "col", np.int32)[rp[row]]),
+        "increasing")  # a repeated column
+    # section bounds: an offset that would wrap, a length that disagrees with the header
+    s_col = cla.SECTIONS.index("col")
+    bad(lambda b: _set_header(b, "off", (1 << 64) - 256, s_col), "outside")
+    bad(lambda b: _set_header(b, "len", 4 * nnz - 4, s_col), "implies")
+    bad(lambda b: _set_header(b, "total_bytes", 1024), "outside")
+    # header fields that disagree with each other
+    bad(lambda b: _set_header(b, "chunks", 3), "format")
+    bad(lambda b: _set_header(b, "rank", 8), "low-rank")
+    bad(lambda b: _set_header(b, "nnz", -1), "nnz")
+    # bitmap: a row's offsets too short for its kept values, keep bits on a padding row
+    gb = _blob_of(make_layer(4, 0, K=256, N=70, M_for_clamp=2))
+    assert _device_bytes(gb)[0] > 0
+    b = gb.copy()
+    nzo = _section(b, "nzoff", np.int32)
+    nzo[1] = nzo[0]
+    n, msg = _device_bytes(b)
+    assert n == 0 and "bitmap" in msg, msg
+    b = gb.copy()
+    meta = _section(b, "meta", np.uint32).reshape(128, -1)  # Npad = 128 rows of keep bits
+    meta[100, 0] = 1
+    n, msg = _device_bytes(b)
+    assert n == 0 and "padding" in msg, msg
+
+
+def test_buffers_of_2_gib_are_refused():
+    # the kernels address every buffer through a 32-bit range: no section or workspace
+    # buffer may reach 2 GiB (CL_ESIZE), checked before any array is read
+    L = cla.lib()
+    d = cla.cl_layer_desc()
+    d.K, d.N = 1 << 24, 1 << 13
+    d.dense = 0
+    d.codes = 256  # never dereferenced: the size check comes first
+    d.lut = 256
+    size = ctypes.c_size_t(0)
+    assert L.cl_pack(ctypes.byref(d), None, ctypes.byref(size), None) == -5
+    assert b"2^31" in L.cl_last_error()
+    from synth.layers import make_layer
+    blob = _blob_of(make_layer(1, 0, K=4096, N=64))
+    assert L.cl_device_bytes(blob.ctypes.data, 1) > 0
+    assert L.cl_device_bytes(blob.ctypes.data, 1 << 18) == 0  # activations of 2^18 rows: 2 GiB
+    assert b"2 GiB" in L.cl_last_error()
