@@ -101,12 +101,16 @@ __device__ __forceinline__ uint32_t to16(float f) {
   if constexpr (BF16) return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
-// fp16 pair -> pair of the MFMA type
+
+// q * s of an integer format in the MFMA type, rounded once to nearest-even:
+// an fp16 multiply rounds the exact product; for bf16 the product is exact in
+// fp32 (at most 8 + 11 significant bits) and is rounded from there (rounding
+// it to fp16 first would round twice).
 template <bool BF16>
-__device__ __forceinline__ uint32_t pair_to16(uint32_t h) {
-  if constexpr (!BF16) return h;
-  const half2_t v = as_h2(h);
-  return to16<true>((float)v.x) | (to16<true>((float)v.y) << 16);
+__device__ __forceinline__ uint32_t scale_pair16(uint32_t qpair, half2_t rscale) {
+  if constexpr (!BF16) return as_u32(as_h2(qpair) * rscale);
+  const half2_t q = as_h2(qpair);
+  return to16<true>((float)q.x * (float)rscale.x) | (to16<true>((float)q.y * (float)rscale.y) << 16);
 }
 
 __device__ __forceinline__ uint4 pf_lds128(const uint32_t* lds, uint32_t byte_addr) {
@@ -288,7 +292,7 @@ __global__ void __launch_bounds__(2 * kPfThreads, 1) prefill_kernel(PfArgs a) {
           chunk_pairs<KIND, false>(smem, st.wb[q], make_uint4(st.wm[q].x, st.wm[q].y, 0, 0), lanebase, 0u, wp, ebias);
           if constexpr (!LUT) {  // LUT tables already hold the MFMA type
 #pragma unroll
-            for (int j = 0; j < KindTraits<KIND>::pairs; ++j) wp[j] = pair_to16<BF16>(as_u32(as_h2(wp[j]) * rscale));
+            for (int j = 0; j < KindTraits<KIND>::pairs; ++j) wp[j] = scale_pair16<BF16>(wp[j], rscale);
           }
 #pragma unroll
           for (int j = 0; j < KindTraits<KIND>::pairs / 4; ++j)
