@@ -15,15 +15,18 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["ClError", "lib", "pack", "blob_header", "CompressedLinear", "fit_lut", "fit_int", "quant_absmax", "LIB_PATH",
-           "EXPORTED_SYMBOLS"]
+           "EXPORTED_SYMBOLS", "PROBE_SYMBOLS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcompressed_linear.so")
 
 EXPORTED_SYMBOLS = [
     "cl_pack", "cl_device_bytes", "cl_create", "cl_forward", "cl_forward_path",
     "cl_debug_dequant", "cl_destroy", "cl_last_error", "cl_fit_lut_work_bytes", "cl_fit_lut",
-    "cl_fit_int", "cl_quant_absmax",
+    "cl_fit_int", "cl_quant_absmax", "cl_set_wait_limit",
 ]
+
+# measurement aids of the benchmark (include/cl_probe.h), exported by the same library
+PROBE_SYMBOLS = ["cl_probe_read", "cl_probe_read_sink_words", "cl_probe_empty"]
 
 DENSE = {"lut3": 0, "lut4": 1, "int4": 2, "int8": 3}
 MASK = {"none": 0, "2:4": 1, "bitmap": 2}
@@ -118,6 +121,14 @@ def lib():
         L.cl_fit_int.restype = ctypes.c_int
         L.cl_quant_absmax.argtypes = [ctypes.c_void_p] + [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3
         L.cl_quant_absmax.restype = ctypes.c_int
+        L.cl_set_wait_limit.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int32]
+        L.cl_set_wait_limit.restype = ctypes.c_int
+        L.cl_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+        L.cl_probe_read.restype = ctypes.c_int
+        L.cl_probe_read_sink_words.argtypes = [ctypes.c_size_t]
+        L.cl_probe_read_sink_words.restype = ctypes.c_size_t
+        L.cl_probe_empty.argtypes = [ctypes.c_void_p]
+        L.cl_probe_empty.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -282,6 +293,11 @@ class CompressedLinear:
                                     torch.cuda.current_stream(self.device).cuda_stream)
         _check(st, "cl_debug_dequant")
         return D16, S16, L32, R32
+
+    def set_wait_limit(self, max_polls: int = 1 << 20, withhold: bool = False):
+        """Test support (cl_set_wait_limit): the bound of the in-launch wait for
+        x' L, and a switch that withholds its publication."""
+        _check(lib().cl_set_wait_limit(self._h, int(max_polls), 1 if withhold else 0), "cl_set_wait_limit")
 
     def close(self):
         if getattr(self, "_h", None):

@@ -111,8 +111,11 @@ static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float
     a.lrp.clamp = a.clamp;
     a.lrp.cval = a.cval;
     a.lrp.xscale = a.xscale;
+    a.lrp.withhold = L.wait_withhold;
     a.lr_wgs = L.lr_S * a.lrp.ntiles;
     a.lr_mode = L.lr_mode;
+    a.lr_max_polls = L.wait_polls;
+    a.lr_err = L.wait_err_dev;
   }
   const bool bf16 = h.x_dtype == CL_ACT_BF16;
   switch (h.dense) {
@@ -200,8 +203,11 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
         r.lr_ntj = L.lr_rpad / 64;
         r.lr_wgs = L.lr_S * r.lr_ntj * (int)ceil_div(M, lowrank_tile_m(M));
         r.lr_mode = L.lr_mode;
+        r.lrp.withhold = L.wait_withhold;
         r.lr_flag = r.lrp.flag;
         r.lr_epoch = r.lrp.epoch;
+        r.lr_max_polls = L.wait_polls;
+        r.lr_err = L.wait_err_dev;
       } else {
         const hipError_t e = launch_lowrank_prologue(L, M, x, stream);
         if (e != hipSuccess) return e;

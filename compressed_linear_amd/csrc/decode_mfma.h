@@ -86,6 +86,8 @@ struct MfArgs {
   // done after); lr_wgs = 0: t was computed by an earlier kernel
   LrSplitArgs lrp;
   int lr_wgs, lr_ntj, lr_mode;
+  uint32_t lr_max_polls;  // bound of the wait for t
+  uint32_t* lr_err;       // set when a wait gives up (host memory)
 };
 
 constexpr int kMfLrTile = 4;  // activation rows per tile of the prologue in this launch
@@ -167,6 +169,7 @@ struct MfCfg {
                                    : KIND == K_INT4_24 ? 128
                                    : KIND == K_INT8_BM ? (kBmSelDwords + 256 * kMfBmSlot) * 4
                                                        : 16;
+  static constexpr int ok_word = tab_bytes / 4;  // after the tables: whether t was published
 };
 
 // LDS bytes per staged activation row: the slice padded so that the row
@@ -186,7 +189,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   constexpr int NV = MT >= 32 ? 16 : MT / 2;
   constexpr int XR = MT * kMfKzMax / 8 / 256;  // 16-byte activation slots per thread
   constexpr bool LUT = KIND == K_LUT3 || KIND == K_LUT4;
-  __shared__ __attribute__((aligned(16))) uint32_t stab[C::tab_bytes / 4];  // at LDS address 0
+  __shared__ __attribute__((aligned(16))) uint32_t stab[C::tab_bytes / 4 + 4];  // at LDS address 0
   extern __shared__ __attribute__((aligned(16))) uint32_t sdyn[];          // activation slice, then t
 
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
@@ -505,11 +508,16 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   if (a.r16 != nullptr && z == a.S - 1) {
     const int rp2 = 2 * a.rp, trow = mf_trow(a.rp);
     const uint32_t target = a.lr_wgs > 0 ? lr_target(a.lrp.flag, a.lrp.epoch) : 0u;
-    if (a.lr_wgs > 0 && wave == 0) wait_lowrank(lr_word(a.lrp.flag, a.lrp.epoch), target, lane);
-    __syncthreads();  // t is published; every wave is done with the activation slice
+    if (wave == 0) {
+      const bool ok = a.lr_wgs == 0 ||
+                      wait_lowrank(lr_word(a.lrp.flag, a.lrp.epoch), target, lane, a.lr_max_polls, a.lr_err);
+      if (lane == 0) stab[C::ok_word] = ok ? 1u : 0u;
+    }
+    __syncthreads();  // t is published (or the wait gave up); every wave is done with the activation slice
+    const bool t_ok = stab[C::ok_word] != 0u;
     for (int i = tid; i < (MT + 1) * a.rp; i += 256) {  // row MT: zeros
       const int m = i / a.rp, j = i - m * a.rp;
-      const float tv = (m < a.M && j < a.rank) ? load_dev(a.t + (size_t)m * a.rank + j) : 0.f;
+      const float tv = (m < a.M && j < a.rank) ? (t_ok ? load_dev(a.t + (size_t)m * a.rank + j) : __builtin_nanf("")) : 0.f;
       const uint32_t hi = mf_to16<BF16>(tv);
       const float hf = BF16 ? __uint_as_float(hi << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)hi);
       const uint32_t lo = mf_to16<BF16>(tv - hf);

@@ -74,6 +74,8 @@ struct RowArgs {
   int lr_wgs, lr_ntj, lr_mode;
   uint32_t* lr_flag;
   uint32_t lr_epoch;
+  uint32_t lr_max_polls;  // bound of the wait for t
+  uint32_t* lr_err;       // set when a wait gives up (host memory)
   // raw activations (ldx = K): clamp them to [-cval, cval] and multiply them by
   // the per-channel factors xscale ([K] fp16; NULL: none) while staging them
   int clamp;
@@ -410,14 +412,15 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
     // t is ready once the prologue (earlier kernel, or this launch's first
     // workgroups) has published it; read through the coherent path
     const uint32_t target = a.lr_flag != nullptr ? lr_target(a.lr_flag, a.lr_epoch) : 0u;
-    if (a.lr_flag != nullptr) wait_lowrank(lr_word(a.lr_flag, a.lr_epoch), target, lane);
+    const bool t_ok =
+        a.lr_flag == nullptr || wait_lowrank(lr_word(a.lr_flag, a.lr_epoch), target, lane, a.lr_max_polls, a.lr_err);
     float tv[MB][4];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = lane + 64 * i;
-        tv[m][i] = (j < a.rank && m < a.M) ? load_dev(a.t + (size_t)m * a.rank + j) : 0.f;
+        tv[m][i] = (j < a.rank && m < a.M) ? (t_ok ? load_dev(a.t + (size_t)m * a.rank + j) : __builtin_nanf("")) : 0.f;
       }
 #pragma unroll
     for (int r = 0; r < R; ++r)

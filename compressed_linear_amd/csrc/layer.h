@@ -10,6 +10,7 @@ namespace cl {
 
 constexpr int kMaxDecodeM = 32;
 constexpr int kLrSlice = 512;  // K rows per workgroup of the decode low-rank prologue
+constexpr uint32_t kLrMaxPolls = 1u << 20;  // default bound of the in-launch wait for t (polls)
 
 struct Layer {
   cl_blob_header h;          // copy of the blob header
@@ -75,6 +76,15 @@ struct Layer {
   uint32_t* mf_oent = nullptr;   // entries: k in slice | fp16 value << 16
   int32_t* mf_nzs = nullptr;     // bitmap: first kept byte of every (row, slice) [Npad][S]
   size_t ws_bytes = 0;
+
+  // waits for t inside a launch: poll bound, the error word a wait that gives
+  // up sets (pinned host memory, so the next forward reads it without a sync;
+  // wait_err_dev is its device address), and the test switch that withholds
+  // the publication of t
+  uint32_t wait_polls = 0;
+  int wait_withhold = 0;
+  volatile uint32_t* wait_err_host = nullptr;
+  uint32_t* wait_err_dev = nullptr;
 };
 
 // Workspace layout and size for a blob header (used by cl_device_bytes and cl_create).

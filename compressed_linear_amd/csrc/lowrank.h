@@ -38,6 +38,7 @@ struct LrSplitArgs {
   uint32_t* flag;
   uint32_t epoch;
   int ntiles;
+  int withhold;       // test support: compute t but never publish it (every reader's wait then gives up)
   // clamp x to [-cval, cval] and multiply it by the per-channel factors
   // xscale ([K] fp16, NULL: none) while staging it (raw activations only)
   int clamp;
@@ -138,16 +139,29 @@ __device__ __forceinline__ void lr_reader_done(uint32_t* flag, uint32_t generati
   }
 }
 
-// Bounded wait for the published t (each poll sleeps a few hundred cycles; the
-// bound, far above any producer's run time, only keeps a wavefront from
-// waiting forever should a producer never publish).  Lane 0 polls `word`.
-__device__ __forceinline__ void wait_lowrank(const uint32_t* word, uint32_t target, int lane) {
+// Bounded wait for the published t.  Lane 0 polls `word` (each poll sleeps a
+// few hundred cycles) at most max_polls times after the first look; the
+// default bound, far above any producer's run time, only keeps a wavefront
+// from waiting forever should a producer never publish (its progress rests on
+// the producers being dispatched before the readers, the launch's first
+// workgroups).  A wait that gives up records it in the layer's error word
+// (host memory, read by the next forward) and returns false for the whole
+// wavefront: the caller then writes NaN instead of using a stale t.
+__device__ __forceinline__ bool wait_lowrank(const uint32_t* word, uint32_t target, int lane, uint32_t max_polls,
+                                             uint32_t* err) {
+  int ok = 1;
   if (lane == 0) {
     uint32_t it = 0;
-    while (__hip_atomic_load(const_cast<uint32_t*>(word), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != target &&
-           ++it < (1u << 20))
+    while (__hip_atomic_load(const_cast<uint32_t*>(word), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != target) {
+      if (it++ >= max_polls) {
+        ok = 0;
+        break;
+      }
       __builtin_amdgcn_s_sleep(4);
+    }
+    if (!ok) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
+  return __shfl(ok, 0, 64) != 0;
 }
 
 template <bool BF16>
@@ -198,6 +212,10 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = s * kLrSlice, j0 = tj * 64, m0 = tm * MT;
   const int jg = tid % LG, pr = tid / LG;
+  // the value this launch publishes, read before any work: the generation
+  // cannot move while the launch's readers wait for it, and a publish that
+  // comes late (after a reader gave up) then cannot run ahead of a later launch
+  const uint32_t publish = a.flag != nullptr ? lr_target(a.flag, a.epoch) : 0u;
 
   // activations of the slice (zero past K and past M)
   const brsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.ldx * 2u);
@@ -349,7 +367,7 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
     const uint32_t old = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (uint32_t)(a.ntiles - 1)) {
       __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next forward
-      __hip_atomic_store(lr_word(a.flag, a.epoch), lr_target(a.flag, a.epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!a.withhold) __hip_atomic_store(lr_word(a.flag, a.epoch), publish, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

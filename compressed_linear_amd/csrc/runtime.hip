@@ -301,6 +301,12 @@ static void build_lowrank_host(const cl_blob_header& h, const uint8_t* b, int mo
     for (int q = 0; q < gk; ++q) ls[(size_t)q * rpad + j] = Ls[(size_t)j * gk + q];
 }
 
+static void destroy_layer(Layer* L) {
+  if (!L) return;
+  if (L->wait_err_host) (void)hipHostFree(const_cast<uint32_t*>(L->wait_err_host));
+  delete L;
+}
+
 template <class T>
 static T* sec(uint8_t* dev, const cl_blob_header& h, int s) {
   return h.len[s] ? reinterpret_cast<T*>(dev + h.off[s]) : nullptr;
@@ -339,14 +345,29 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
   L->max_M = max_M;
   L->Npad = h->n_tiles * 64;
   int dev = 0;
-  hipGetDevice(&dev);
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   int cus = 256;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
   L->num_cus = cus;
   L->split = choose_split(*h, cus);
+  L->wait_polls = kLrMaxPolls;
+  {  // the error word of the waits for t, in pinned host memory mapped for the device
+    void* hp = nullptr;
+    void* dp = nullptr;
+    hipError_t he = hipHostMalloc(&hp, 64, hipHostMallocMapped);
+    if (he == hipSuccess) he = hipHostGetDevicePointer(&dp, hp, 0);
+    if (he != hipSuccess) {
+      if (hp) (void)hipHostFree(hp);
+      delete L;
+      return fail(CL_EHIP, "pinned error word: %s", hipGetErrorString(he));
+    }
+    L->wait_err_host = static_cast<volatile uint32_t*>(hp);
+    L->wait_err_host[0] = 0;
+    L->wait_err_dev = static_cast<uint32_t*>(dp);
+  }
   const size_t need = workspace_layout(*h, max_M, L, h->total_bytes);
   if (dev_bytes < need) {
-    delete L;
+    destroy_layer(L);
     return fail(CL_ENOMEM, "dev_buf needs %zu bytes, got %zu", need, dev_bytes);
   }
   L->dev_bytes = dev_bytes;
@@ -461,7 +482,7 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
     e = hipMemcpyAsync(L->mf_oent, mfe.data(), mfe.size() * 4, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
-    delete L;
+    destroy_layer(L);
     return fail(CL_EHIP, "upload failed: %s", hipGetErrorString(e));
   }
   *handle = L;
@@ -481,6 +502,11 @@ static cl_status forward_impl(Layer* L, int32_t M, const void* x, float* y, void
   if (decode && M > kMaxDecodeM) return fail(CL_EINVAL, "the decode path takes M <= %d", kMaxDecodeM);
   if (path == CL_PATH_DECODE_MFMA && L->mf_S == 0)
     return fail(CL_EUNSUPPORTED, "the matrix-core decode needs a bitmap layer or one created with max_M >= 2");
+  if (L->wait_err_host && L->wait_err_host[0]) {  // set by a wait for t that gave up in an earlier forward
+    L->wait_err_host[0] = 0;
+    return fail(CL_EHIP, "an earlier forward on this layer gave up waiting for x' L inside its launch; "
+                         "its outputs hold NaN (reported once; this call did nothing)");
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (decode) {  // the decode dispatch clamps / restages x itself (in its kernels where it can)
@@ -522,6 +548,15 @@ extern "C" cl_status cl_debug_dequant(void* handle, uint16_t* D16, uint16_t* S16
 
 extern "C" cl_status cl_destroy(void* handle) {
   clear_error();
-  delete static_cast<Layer*>(handle);
+  destroy_layer(static_cast<Layer*>(handle));
+  return CL_OK;
+}
+
+extern "C" cl_status cl_set_wait_limit(void* handle, uint32_t max_polls, int32_t withhold) {
+  clear_error();
+  Layer* L = static_cast<Layer*>(handle);
+  if (!L) return fail(CL_EINVAL, "handle is NULL");
+  L->wait_polls = max_polls;
+  L->wait_withhold = withhold ? 1 : 0;
   return CL_OK;
 }

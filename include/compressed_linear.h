@@ -236,8 +236,12 @@ cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes, int32_t m
  * computes x' L_hat inside derives its generation from device memory), so no
  * argument changes between replays.
  * Deterministic: the same inputs give bitwise identical y.
+ * The layer's own low-rank prologue runs inside the decode launch where it
+ * can: its waits for x' L_hat are bounded, and one that gives up (see
+ * cl_set_wait_limit) leaves NaN in the outputs it could not finish.
  * Errors: CL_EINVAL (M out of range, NULL or misaligned pointers),
- * CL_EHIP (launch failure).
+ * CL_EHIP (launch failure; or an earlier forward's wait gave up -- reported
+ * once, and this call then launches nothing).
  */
 cl_status cl_forward(void* handle, int32_t M, const void* x_dev, float* y_dev, void* stream);
 
@@ -260,8 +264,28 @@ cl_status cl_forward_path(void* handle, int32_t M, const void* x_dev, float* y_d
 cl_status cl_debug_dequant(void* handle, uint16_t* D16, uint16_t* S16, float* L32, float* R32,
                            void* stream);
 
-/* cl_destroy -- free the host handle.  The caller frees dev_buf afterwards. */
+/* cl_destroy -- free the host handle (and its pinned error word).  The caller
+ * frees dev_buf afterwards. */
 cl_status cl_destroy(void* handle);
+
+/*
+ * cl_set_wait_limit -- test support for the failure path of the low-rank
+ * prologue inside a decode launch ("SLiM" page, review highlights: y gets the
+ * term (x' L_hat) R_hat).  A batch-1..32 forward of a layer with a low-rank
+ * part computes t = x' L_hat in the launch's first workgroups and publishes
+ * it; the workgroups that add the rank term wait for it, polling a bounded
+ * number of times.
+ *   handle     from cl_create.
+ *   max_polls  bound of that wait, in polls of a few hundred cycles after the
+ *              first look (cl_create sets 2^20, far above any producer's time).
+ *   withhold   nonzero: the prologue computes t but does not publish it, so
+ *              every wait runs to its bound and every kernel still ends.
+ * A wait that gives up writes NaN to the outputs that needed t and sets the
+ * layer's error word (pinned host memory); the next cl_forward on the handle
+ * then returns CL_EHIP, once, without launching anything.
+ * Errors: CL_EINVAL (NULL handle).
+ */
+cl_status cl_set_wait_limit(void* handle, uint32_t max_polls, int32_t withhold);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* cl_last_error(void);

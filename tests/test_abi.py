@@ -12,17 +12,19 @@ import compressed_linear_amd as cla
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "compressed_linear.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "cl_probe.h")
 
 
-def header_functions():
-    src = open(HEADER).read()
+def header_functions(path=HEADER):
+    src = open(path).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(cl_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(cl_[a-z_0-9]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
-    names = header_functions()
-    assert set(names) == set(cla.EXPORTED_SYMBOLS)
+    assert set(header_functions()) == set(cla.EXPORTED_SYMBOLS)
+    assert set(header_functions(PROBE_HEADER)) == set(cla.PROBE_SYMBOLS)
+    names = header_functions() + header_functions(PROBE_HEADER)
     L = cla.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -52,6 +54,7 @@ def test_host_errors_without_gpu():
     assert b"handle" in L.cl_last_error()
     assert L.cl_debug_dequant(None, None, None, None, None, None) == -1
     assert L.cl_destroy(None) == 0
+    assert L.cl_set_wait_limit(None, 0, 1) == -1
     assert L.cl_device_bytes(None, 1) == 0
     h = ctypes.c_void_p()
     assert L.cl_create(None, None, 0, 1, None, ctypes.byref(h)) == -1
