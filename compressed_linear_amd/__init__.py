@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcompress
 EXPORTED_SYMBOLS = [
     "cl_pack", "cl_device_bytes", "cl_create", "cl_forward", "cl_forward_path",
     "cl_debug_dequant", "cl_destroy", "cl_last_error", "cl_fit_lut_work_bytes", "cl_fit_lut",
-    "cl_fit_int", "cl_quant_absmax", "cl_set_wait_limit",
+    "cl_fit_int", "cl_quant_absmax", "cl_set_wait_limit", "cl_fit_lut_noalloc",
 ]
 
 # measurement aids of the benchmark (include/cl_probe.h), exported by the same library
@@ -121,6 +121,10 @@ def lib():
         L.cl_fit_int.restype = ctypes.c_int
         L.cl_quant_absmax.argtypes = [ctypes.c_void_p] + [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3
         L.cl_quant_absmax.restype = ctypes.c_int
+        L.cl_fit_lut_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 6 + \
+            [ctypes.POINTER(ctypes.c_int64)]
+        L.cl_fit_lut_noalloc.restype = ctypes.c_int
         L.cl_set_wait_limit.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int32]
         L.cl_set_wait_limit.restype = ctypes.c_int
         L.cl_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]

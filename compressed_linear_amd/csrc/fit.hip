@@ -26,6 +26,8 @@
 // centroid is sum / count in fp64, boundaries are (c_j + c_j+1) / 2 in fp64.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "internal.h"
 #include "layout.h"
 
@@ -611,6 +613,93 @@ __global__ void __launch_bounds__(256) fit_absmax_kernel(const uint16_t* __restr
 
 using namespace cl;
 
+namespace cl {
+namespace {
+
+__global__ void fit_zero_kernel(unsigned long long* __restrict__ p, int n8) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n8) p[i] = 0ull;
+}
+
+cl_status fit_lut_check(const uint16_t* W, int32_t N, int32_t K, int32_t bits, int64_t n_out, int32_t max_iter,
+                        uint8_t* codes, uint16_t* lut, int32_t* row_ptr, int32_t* col, uint16_t* val) {
+  if (N < 1 || K < 1) return fail(CL_EINVAL, "N and K must be >= 1");
+  if (K > kFitMaxK || N > (1 << 24)) return fail(CL_ESIZE, "the fitter takes K <= %d and N <= 2^24", kFitMaxK);
+  if (bits != 3 && bits != 4) return fail(CL_EINVAL, "bits must be 3 or 4");
+  if (max_iter < 1) return fail(CL_EINVAL, "max_iter must be >= 1");
+  const long long total = (long long)N * K;
+  if (n_out < 0 || n_out > total || n_out > 0x7FFFFFFFLL) return fail(CL_EINVAL, "n_out out of range");
+  if (!W || !codes || !lut || !row_ptr || (n_out > 0 && (!col || !val))) return fail(CL_EINVAL, "a required pointer is NULL");
+  return CL_OK;
+}
+
+// The fit of a checked call, with its scratch at `wk` (FitWork::bytes(N) bytes,
+// 8-byte aligned): histograms and scalars are cleared by a kernel (no memset
+// node), the kernels run, and the call waits for the scalars it reports.
+cl_status fit_lut_run(const uint16_t* W, int32_t N, int32_t K, int32_t bits, int64_t n_out, int32_t max_iter,
+                      uint8_t* codes, uint16_t* lut, int32_t* row_ptr, int32_t* col, uint16_t* val, uint8_t* wk,
+                      hipStream_t s, int64_t* total_iters) {
+  const long long total = (long long)N * K;
+  const int hb = (int)(total / 256 / 8 + 1 > 2048 ? 2048 : total / 256 / 8 + 1);
+  static_assert(FitWork::rows % 8 == 0, "the cleared head is whole words");
+  hipLaunchKernelGGL(fit_zero_kernel, dim3((unsigned)ceil_div(FitWork::rows / 8, 256)), dim3(256), 0, s,
+                     reinterpret_cast<unsigned long long*>(wk), (int)(FitWork::rows / 8));  // histograms and scalars
+  hipLaunchKernelGGL(fit_hist_kernel, dim3(hb), dim3(256), 0, s, W, total, 0, wk);
+  hipLaunchKernelGGL(fit_select_kernel, dim3(1), dim3(1), 0, s, (long long)n_out, 0, wk);
+  hipLaunchKernelGGL(fit_hist_kernel, dim3(hb), dim3(256), 0, s, W, total, 1, wk);
+  hipLaunchKernelGGL(fit_select_kernel, dim3(1), dim3(1), 0, s, (long long)n_out, 1, wk);
+  hipLaunchKernelGGL(fit_rowstat_kernel, dim3(N), dim3(256), 0, s, W, K, wk, N);
+  hipLaunchKernelGGL(fit_scan_kernel, dim3(1), dim3(1024), 0, s, N, wk, row_ptr);
+  const size_t lds = ((size_t)K * 2 + 15) / 16 * 16 + ((size_t)K + 31) / 32 * 4;
+  if (bits == 3)
+    hipLaunchKernelGGL(fit_rows_kernel<8>, dim3(N), dim3(kFitThreads), lds, s, W, N, K, max_iter, (int)n_out, wk, row_ptr,
+                       codes, lut, col, val);
+  else
+    hipLaunchKernelGGL(fit_rows_kernel<16>, dim3(N), dim3(kFitThreads), lds, s, W, N, K, max_iter, (int)n_out, wk, row_ptr,
+                       codes, lut, col, val);
+  hipError_t e = hipGetLastError();
+  long long sc[8] = {};
+  if (e == hipSuccess) e = hipMemcpyAsync(sc, wk + FitWork::scal, sizeof(sc), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(CL_EHIP, "fit failed: %s", hipGetErrorString(e));
+  if (sc[S_BAD]) return fail(CL_EINVAL, "a weight is not finite or its magnitude is 8192 or more (outputs are not valid)");
+  if (total_iters) *total_iters = sc[S_ITERS];
+  return CL_OK;
+}
+
+// Scratch of the fitter variant that allocates nothing: one array per device,
+// held until the process ends; its device address is looked up once per
+// device (the name is only a host-side stand-in) and kept.  Calls on one
+// device share it.
+constexpr size_t kFitScratchBytes = (size_t)2 << 20;
+// rows it serves: FitWork::bytes(N) = 1600 + 16 N <= 2 MiB
+constexpr int kFitNoallocMaxRows = (int)((kFitScratchBytes - FitWork::rows) / 16);
+static_assert(FitWork::rows % 8 == 0 && FitWork::rows + 16 * (size_t)kFitNoallocMaxRows <= kFitScratchBytes,
+              "the scratch holds the work of kFitNoallocMaxRows rows");
+__device__ __align__(256) uint8_t scratch[kFitScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+cl_status scratch_of_current_device(uint8_t** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CL_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(CL_EUNSUPPORTED, "device %d beyond the %d this library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (es != hipSuccess || !p) return fail(CL_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(es));
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return CL_OK;
+}
+
+}  // namespace
+}  // namespace cl
+
 extern "C" size_t cl_fit_lut_work_bytes(int32_t N, int32_t K) {
   if (N < 1 || K < 1) return 0;
   return FitWork::bytes(N);
@@ -620,42 +709,28 @@ extern "C" cl_status cl_fit_lut(const uint16_t* W, int32_t N, int32_t K, int32_t
                                 uint8_t* codes, uint16_t* lut, int32_t* row_ptr, int32_t* col, uint16_t* val,
                                 void* work, void* stream, int64_t* total_iters) {
   clear_error();
-  if (N < 1 || K < 1) return fail(CL_EINVAL, "N and K must be >= 1");
-  if (K > kFitMaxK || N > (1 << 24)) return fail(CL_ESIZE, "the fitter takes K <= %d and N <= 2^24", kFitMaxK);
-  if (bits != 3 && bits != 4) return fail(CL_EINVAL, "bits must be 3 or 4");
-  if (max_iter < 1) return fail(CL_EINVAL, "max_iter must be >= 1");
-  const long long total = (long long)N * K;
-  if (n_out < 0 || n_out > total || n_out > 0x7FFFFFFFLL) return fail(CL_EINVAL, "n_out out of range");
-  if (!W || !codes || !lut || !row_ptr || !work || (n_out > 0 && (!col || !val)))
-    return fail(CL_EINVAL, "a required pointer is NULL");
+  cl_status st = fit_lut_check(W, N, K, bits, n_out, max_iter, codes, lut, row_ptr, col, val);
+  if (st != CL_OK) return st;
+  if (!work) return fail(CL_EINVAL, "a required pointer is NULL");
   if (reinterpret_cast<uintptr_t>(work) % 8) return fail(CL_EINVAL, "work must be 8-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* wk = static_cast<uint8_t*>(work);
-  hipError_t e = hipMemsetAsync(wk, 0, FitWork::rows, s);  // histograms and scalars
-  const int hb = (int)(total / 256 / 8 + 1 > 2048 ? 2048 : total / 256 / 8 + 1);
-  if (e == hipSuccess) {
-    hipLaunchKernelGGL(fit_hist_kernel, dim3(hb), dim3(256), 0, s, W, total, 0, wk);
-    hipLaunchKernelGGL(fit_select_kernel, dim3(1), dim3(1), 0, s, (long long)n_out, 0, wk);
-    hipLaunchKernelGGL(fit_hist_kernel, dim3(hb), dim3(256), 0, s, W, total, 1, wk);
-    hipLaunchKernelGGL(fit_select_kernel, dim3(1), dim3(1), 0, s, (long long)n_out, 1, wk);
-    hipLaunchKernelGGL(fit_rowstat_kernel, dim3(N), dim3(256), 0, s, W, K, wk, N);
-    hipLaunchKernelGGL(fit_scan_kernel, dim3(1), dim3(1024), 0, s, N, wk, row_ptr);
-    const size_t lds = ((size_t)K * 2 + 15) / 16 * 16 + ((size_t)K + 31) / 32 * 4;
-    if (bits == 3)
-      hipLaunchKernelGGL(fit_rows_kernel<8>, dim3(N), dim3(kFitThreads), lds, s, W, N, K, max_iter, (int)n_out, wk, row_ptr, codes,
-                         lut, col, val);
-    else
-      hipLaunchKernelGGL(fit_rows_kernel<16>, dim3(N), dim3(kFitThreads), lds, s, W, N, K, max_iter, (int)n_out, wk, row_ptr, codes,
-                         lut, col, val);
-    e = hipGetLastError();
-  }
-  long long sc[8] = {};
-  if (e == hipSuccess) e = hipMemcpyAsync(sc, wk + FitWork::scal, sizeof(sc), hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e != hipSuccess) return fail(CL_EHIP, "fit failed: %s", hipGetErrorString(e));
-  if (sc[S_BAD]) return fail(CL_EINVAL, "a weight is not finite or its magnitude is 8192 or more (outputs are not valid)");
-  if (total_iters) *total_iters = sc[S_ITERS];
-  return CL_OK;
+  return fit_lut_run(W, N, K, bits, n_out, max_iter, codes, lut, row_ptr, col, val, static_cast<uint8_t*>(work),
+                     static_cast<hipStream_t>(stream), total_iters);
+}
+
+extern "C" cl_status cl_fit_lut_noalloc(const uint16_t* W, int32_t N, int32_t K, int32_t bits, int64_t n_out,
+                                        int32_t max_iter, uint8_t* codes, uint16_t* lut, int32_t* row_ptr, int32_t* col,
+                                        uint16_t* val, void* stream, int64_t* total_iters) {
+  clear_error();
+  cl_status st = fit_lut_check(W, N, K, bits, n_out, max_iter, codes, lut, row_ptr, col, val);
+  if (st != CL_OK) return st;
+  if (N > kFitNoallocMaxRows || FitWork::bytes(N) > kFitScratchBytes)
+    return fail(CL_ESIZE, "the fitter without a work buffer takes N <= %d rows (its scratch is %zu bytes)",
+                kFitNoallocMaxRows, kFitScratchBytes);
+  uint8_t* wk = nullptr;
+  st = scratch_of_current_device(&wk);
+  if (st != CL_OK) return st;
+  return fit_lut_run(W, N, K, bits, n_out, max_iter, codes, lut, row_ptr, col, val, wk, static_cast<hipStream_t>(stream),
+                     total_iters);
 }
 
 extern "C" cl_status cl_fit_int(const uint16_t* W, int32_t N, int32_t K, int32_t bits, int32_t mask, int32_t grid,

@@ -332,6 +332,26 @@ cl_status cl_fit_lut(const uint16_t* W, int32_t N, int32_t K, int32_t bits, int6
                      void* work, void* stream, int64_t* total_iters);
 
 /*
+ * cl_fit_lut_noalloc -- cl_fit_lut for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same kernels and outputs, with the work buffer
+ * replaced by a scratch array of 2 MiB that the library holds on every device
+ * it runs on until the process ends (static device memory; this call
+ * allocates nothing and calls no allocating routine).
+ *   Arguments as cl_fit_lut, without `work`; N <= 130972 rows (the scratch
+ *   holds 1600 + 16 N bytes).
+ * Calls on one device share that scratch: calls that overlap on one device
+ * (other streams, other threads) race and give undefined outputs; calls in
+ * sequence are independent (each clears what must start at zero).  Like
+ * cl_fit_lut it waits for its stream before returning.
+ * Errors: those of cl_fit_lut; CL_ESIZE also for N above 130972;
+ * CL_EUNSUPPORTED for a device index of 64 or more.
+ */
+cl_status cl_fit_lut_noalloc(const uint16_t* W, int32_t N, int32_t K, int32_t bits, int64_t n_out, int32_t max_iter,
+                             uint8_t* codes, uint16_t* lut, int32_t* row_ptr, int32_t* col, uint16_t* val,
+                             void* stream, int64_t* total_iters);
+
+/*
  * cl_fit_int -- data-free packing of an fp16 weight matrix into the integer
  * formats on the GPU, the step before cl_pack ("SLiM" page, review highlights:
  * symmetric quantization that clips the weights before rounding to nearest,

@@ -80,6 +80,10 @@ def test_packer_entry_points_validate_on_the_host():
     assert L.cl_fit_int(fake, 4, 64, 5, 0, 10, fake, fake, fake, fake, None) == -1  # bits
     assert L.cl_fit_int(fake, 4, 64, 4, 0, 0, fake, fake, fake, fake, None) == -1  # grid
     assert L.cl_fit_int(fake, 4, 64, 4, 1, 10, fake, fake, None, fake, None) == -1  # keep required with a mask
+    # the fitter without a work buffer: rows beyond its static scratch, before any device work
+    assert L.cl_fit_lut_noalloc(fake, 200000, 64, 4, 1, 10, fake, fake, fake, fake, fake, None, None) == -5
+    assert b"N <= 130972" in L.cl_last_error()
+    assert L.cl_fit_lut_noalloc(fake, 4, 64, 5, 1, 10, fake, fake, fake, fake, fake, None, None) == -1  # bits
     assert L.cl_quant_absmax(fake, 16, 8, 0, 0, fake, fake, None) == -1  # group
     assert L.cl_quant_absmax(None, 16, 8, 4, 0, fake, fake, None) == -1  # NULL factor
 
