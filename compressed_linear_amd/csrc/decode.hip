@@ -162,17 +162,18 @@ hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStre
     r.chunks = h.chunks;
     r.rank = h.lr != CL_LR_NONE ? h.rank : 0;
     r.group = h.group > 0 ? h.group : 1;
+    r.group_mul = (uint32_t)((65536 + r.group - 1) / r.group);
     r.lr_kind = h.lr;
     r.Npad = L.Npad;
     r.nnz = (int)h.nnz;
     bool one_round = false;
     switch (h.dense) {
-      case CL_DENSE_LUT3: rows = rows_fit<K_LUT3>(r, &one_round); break;
-      case CL_DENSE_LUT4: rows = rows_fit<K_LUT4>(r, &one_round); break;
+      case CL_DENSE_LUT3: rows = rows_fit<K_LUT3>(r, bf16, &one_round); break;
+      case CL_DENSE_LUT4: rows = rows_fit<K_LUT4>(r, bf16, &one_round); break;
       case CL_DENSE_INT4:
-        rows = h.mask == CL_MASK_2_4 ? rows_fit<K_INT4_24>(r, &one_round) : rows_fit<K_INT4>(r, &one_round);
+        rows = h.mask == CL_MASK_2_4 ? rows_fit<K_INT4_24>(r, bf16, &one_round) : rows_fit<K_INT4>(r, bf16, &one_round);
         break;
-      default: rows = rows_fit<K_INT8>(r, &one_round); break;
+      default: rows = rows_fit<K_INT8>(r, bf16, &one_round); break;
     }
     rows_edit = rows && raw && one_round && edit_in_kernel(L);
   }

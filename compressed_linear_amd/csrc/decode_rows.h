@@ -59,6 +59,7 @@ struct RowArgs {
   const void* x;
   float* y;
   int K, N, M, ldx, chunks, rank, group, lr_kind;
+  uint32_t group_mul;  // ceil(2^16 / group): (j * group_mul) >> 16 == j / group for every rank index j < 256
   int Npad;   // rows with storage (a multiple of 64)
   int nnz;    // outliers in the layer
   int npass;  // ceil(chunks / 64)
@@ -105,6 +106,10 @@ constexpr int row_tab_bytes() {
 // issued before the code stream, further rounds after it).
 template <int MB>
 constexpr int row_x_rounds() { return MB <= 2 ? 8 : 12; }
+// Slots per thread that one staging round of one activation row may hold: the
+// round that edits raw activations, or converts bf16 ones (all of the row).
+template <bool BF16>
+constexpr int row_x_slots1() { return BF16 ? 16 : 8; }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -129,6 +134,52 @@ __device__ __forceinline__ float mac2r(uint32_t w, uint32_t xv, float acc) {
   }
 }
 
+// bf16 activations of a batch-1 row staged as fp16 (the multiply-adds then run
+// as fp16 dot products, one instruction per weight pair, instead of two mixed
+// fp16 x bf16 multiply-adds and conversions): every value is multiplied by the
+// same power of two 2^(112 - b), chosen from the row's largest exponent e_max
+// so that the largest magnitude lands in [2^14, 2^15) (b = max(e_max - 29, 0)),
+// and the row's sum is multiplied back by 2^(b - 112) before the rank term.
+// A bf16 value (8 significant bits) whose scaled exponent stays in fp16's
+// normal range is exact; so is a bf16 subnormal when b = 0.  Values more than
+// 2^29 below the row's largest are replaced by a value within 2^-14 of them in
+// scaled units (less than 2^-28 of the row's largest magnitude).
+typedef unsigned short xh_u16x2 __attribute__((ext_vector_type(2)));
+// packed 16-bit maxima of 2|bf16| (the bits shifted left by one drop the sign;
+// a form of its own, so that the compiler does not keep the conversion's
+// masked values alive from here to the conversion)
+__device__ __forceinline__ uint32_t xh_absmax2(uint32_t m, uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const xh_u16x2 one = {1, 1};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    m = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(xh_u16x2, m),
+                                                               (xh_u16x2)(__builtin_bit_cast(xh_u16x2, w[i]) << one)));
+  return m;
+}
+// maximum over the wavefront: rotations inside rows of 16 lanes, then the four rows
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x124, 0xF, 0xF, false));  // row_ror 4
+  m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x128, 0xF, 0xF, false));  // row_ror 8
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)m, 32), (uint32_t)__builtin_amdgcn_readlane((int)m, 48)));
+}
+// |bf16| bits minus b << 7 in each half (saturating at 0) is the fp16 exponent
+// and the top 7 significand bits, three places to the right; the sign is kept.
+__device__ __forceinline__ uint4 xh_convert(uint4 v, uint32_t sub2) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const xh_u16x2 d = __builtin_elementwise_sub_sat(__builtin_bit_cast(xh_u16x2, w[i] & 0x7FFF7FFFu),
+                                                     __builtin_bit_cast(xh_u16x2, sub2));
+    const xh_u16x2 three = {3, 3};
+    w[i] = (w[i] & 0x80008000u) | __builtin_bit_cast(uint32_t, (xh_u16x2)(d << three));
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 __device__ __forceinline__ uint4 lds_u128(const uint32_t* lds, uint32_t byte_addr) {
   return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(lds) + byte_addr);
 }
@@ -142,8 +193,13 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   constexpr int SPAN = KindTraits<KIND>::span, P = KindTraits<KIND>::pairs, XD = SPAN / 8;  // 16-byte x slots per chunk
   constexpr int XS = RowX<KIND>::stride, XSL = RowX<KIND>::slots;
   constexpr bool LUT = KIND == K_LUT3 || KIND == K_LUT4;
+  // bf16 activations of one row: staged as fp16 with a row scale (one staging
+  // round holds the whole row; the host checks it)
+  constexpr bool XH = BF16 && MB == 1;
+  constexpr bool XB = BF16 && !XH;  // bf16 values in LDS (multiply-adds in fp32)
   constexpr uint32_t RTB = (uint32_t)row_table_bytes<KIND>();  // bytes of one row table
-  __shared__ __attribute__((aligned(16))) uint32_t stab[row_tab_bytes<KIND, R>() / 4];  // at LDS address 0
+  constexpr int XMAXW = row_tab_bytes<KIND, R>() / 4;          // after the tables: the waves' row maxima
+  __shared__ __attribute__((aligned(16))) uint32_t stab[row_tab_bytes<KIND, R>() / 4 + 4];  // at LDS address 0
   extern __shared__ __attribute__((aligned(16))) uint32_t sdyn[];                      // t, then the activations
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   if constexpr (LR) {
@@ -277,9 +333,10 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
         const int j = lane + 64 * i;
         const uint32_t n = (uint32_t)(row0 + r);
         const bool ok = j < a.rank;  // rows past Npad are out of range
+        const uint32_t jg = ((uint32_t)j * a.group_mul) >> 16;  // j / group (int4 scales)
         // int4: R^T codes [Npad][ceil(r/2)], scales [Npad][ceil(r/g)]; else R^T [Npad][r] 16-bit
         const uint32_t byte = bload8(rR, ok && lr4 ? n * (uint32_t)((a.rank + 1) >> 1) + (uint32_t)(j >> 1) : kNoLoad, 0);
-        const uint32_t sc = bload16(rRs, ok && lr4 ? (n * (uint32_t)gr + (uint32_t)(j / a.group)) * 2u : kNoLoad, 0);
+        const uint32_t sc = bload16(rRs, ok && lr4 ? (n * (uint32_t)gr + jg) * 2u : kNoLoad, 0);
         const uint32_t u = bload16(rR, ok && !lr4 ? (n * (uint32_t)a.rank + (uint32_t)j) * 2u : kNoLoad, 0);
         const int qv = (int)((byte >> (4 * (j & 1))) & 0xFu) - 8;
         const float v4 = ok ? (float)qv * (float)__builtin_bit_cast(_Float16, (uint16_t)sc) : 0.f;
@@ -296,6 +353,22 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
       if (a.xscale) xs[i] = scale_act8<BF16>(xs[i], xf[i]);
     }
   }
+  float xunscale = 1.f;  // XH: 2^(b - 112), the inverse of the staging scale
+  bool xfinite = true;
+  if constexpr (XH) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < XR; ++i) mx = xh_absmax2(mx, xs[i]);  // slots past the row read zero
+    mx = wave_max_u32(max(mx & 0xFFFFu, mx >> 16) >> 1);
+    if (lane == 0) stab[XMAXW + wave] = mx;
+    __syncthreads();
+    const uint32_t M16 = max(max(stab[XMAXW], stab[XMAXW + 1]), max(stab[XMAXW + 2], stab[XMAXW + 3]));
+    xfinite = M16 < 0x7F80u;  // an infinite or NaN activation makes every output of the row NaN
+    const uint32_t emax = M16 >> 7, b = emax > 29u ? emax - 29u : 0u;
+    xunscale = __uint_as_float((b + 15u) << 23);
+#pragma unroll
+    for (int i = 0; i < XR; ++i) xs[i] = xh_convert(xs[i], (b << 7) * 0x00010001u);
+  }
 #pragma unroll
   for (int i = 0; i < XR; ++i) {
     const int s = i * 256 + tid;
@@ -303,8 +376,9 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   }
   // activation blocks larger than one round of XR slots per thread: further
   // rounds, loaded after the code stream is in flight (their wait covers it);
-  // never with edits (the host sends such blocks through the prep kernel)
-  for (int base = XR * 256; base < xslots; base += XR * 256) {
+  // never with edits (the host sends such blocks through the prep kernel),
+  // never with bf16 activations at batch 1 (one round holds the row)
+  for (int base = XR * 256; !XH && base < xslots; base += XR * 256) {
 #pragma unroll
     for (int i = 0; i < XR; ++i) xs[i] = bload128(rx, x_src(base + i * 256 + tid), 0);
 #pragma unroll
@@ -363,7 +437,7 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
 #pragma unroll
           for (int m = 0; m < MB; ++m)
 #pragma unroll
-            for (int j = 0; j < P; ++j) acc[r][m] = mac2r<BF16>(wp[j], xv[m][j], acc[r][m]);
+            for (int j = 0; j < P; ++j) acc[r][m] = mac2r<XB>(wp[j], xv[m][j], acc[r][m]);
         }
       }
     }
@@ -392,7 +466,7 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
   // ---- outliers: activations gathered from LDS ----
   auto x_lds = [&](int m, int k) -> float {
     const int c = k / SPAN, o = k - c * SPAN;
-    return act_f32<BF16>(lds_u16(sdyn, (uint32_t)(a.lds_x + m * a.xrow + c * XS + 2 * o)));
+    return act_f32<XB>(lds_u16(sdyn, (uint32_t)(a.lds_x + m * a.xrow + c * XS + 2 * o)));
   };
   if (has_csr) {
 #pragma unroll
@@ -406,6 +480,10 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
         for (int m = 0; m < MB; ++m) acc[r][m] = __builtin_fmaf(v, x_lds(m, cc), acc[r][m]);
       }
     }
+  }
+  if constexpr (XH) {  // back from the staging scale (exact: a power of two), before the rank term
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r][0] = xfinite ? acc[r][0] * xunscale : __builtin_nanf("");
   }
   // ---- rank terms: t (LDS) times R^T ----
   if constexpr (LR) {
@@ -492,15 +570,21 @@ static hipError_t launch_rows_t(RowArgs a, int Npad, hipStream_t st) {
     return hipErrorInvalidConfiguration;
   const int grid = (Npad + 4 * R - 1) / (4 * R) + a.lr_wgs;  // prologue workgroups first
   const int per_thread = (MB * a.npass * 64 * RowX<KIND>::slots + 255) / 256;
-  // raw activations are edited in the first staging round only, at batch 1
-  if ((a.clamp || a.xscale) && (MB != 1 || per_thread > row_x_rounds<MB>())) return hipErrorInvalidValue;
+  // raw activations are edited in the first staging round only, at batch 1;
+  // bf16 activations at batch 1 are staged in one round (converted to fp16 there)
+  if ((a.clamp || a.xscale) && (MB != 1 || per_thread > row_x_slots1<BF16>())) return hipErrorInvalidValue;
+  if (BF16 && MB == 1 && per_thread > row_x_slots1<BF16>()) return hipErrorInvalidValue;
   if constexpr (MB == 1) {
     if (per_thread <= 2)
       launch_rows_xr<KIND, MB, BF16, R, 2>(a, grid, lds, st);
     else if (per_thread <= 4)
       launch_rows_xr<KIND, MB, BF16, R, 4>(a, grid, lds, st);
-    else
+    else if (per_thread <= 6)
+      launch_rows_xr<KIND, MB, BF16, R, 6>(a, grid, lds, st);
+    else if (!BF16 || per_thread <= 8)
       launch_rows_xr<KIND, MB, BF16, R, row_x_rounds<MB>()>(a, grid, lds, st);
+    else
+      launch_rows_xr<KIND, MB, BF16, R, BF16 ? 16 : row_x_rounds<MB>()>(a, grid, lds, st);
   } else {
     launch_rows_xr<KIND, MB, BF16, R, row_x_rounds<MB>()>(a, grid, lds, st);
   }
@@ -511,13 +595,15 @@ static hipError_t launch_rows_t(RowArgs a, int Npad, hipStream_t st) {
 // LDS) and, in *one_round, whether it can edit raw activations: one activation
 // row whose first staging round holds the whole block.
 template <int KIND>
-bool rows_fit(RowArgs a, bool* one_round = nullptr) {
+bool rows_fit(RowArgs a, bool bf16, bool* one_round = nullptr) {
   const int mb = a.M <= 1 ? 1 : a.M <= 2 ? 2 : 4;
   const int lds = mb == 1 ? rows_lds_layout<KIND, 1>(a) : mb == 2 ? rows_lds_layout<KIND, 2>(a) : rows_lds_layout<KIND, 4>(a);
+  const int per_thread1 = (a.npass * 64 * RowX<KIND>::slots + 255) / 256;
   if (one_round) {  // edits: batch 1 only
-    const int per_thread = (a.npass * 64 * RowX<KIND>::slots + 255) / 256;
-    *one_round = mb == 1 && per_thread <= row_x_rounds<1>();
+    *one_round = mb == 1 && per_thread1 <= (bf16 ? row_x_slots1<true>() : row_x_slots1<false>());
   }
+  // bf16 at batch 1: the whole row in one staging round
+  if (bf16 && mb == 1 && per_thread1 > row_x_slots1<true>()) return false;
   return lds <= kRowsMaxLds && a.rank <= 256;
 }
 

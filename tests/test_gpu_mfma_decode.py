@@ -242,16 +242,47 @@ def test_mfma_clamp_and_prologue_in_launch():
     mod.close()
 
 
-@pytest.mark.parametrize("K", [1456, 8200])
-def test_bf16_batch1_fp16_staging_and_fallback(K):
-    # bf16 activations that fp16 holds exactly run the fp16 dot products; one
-    # value outside fp16 (huge, or a tiny one with bits below fp16's resolution)
-    # sends the whole row to the bf16 path: both within the bound
+@pytest.mark.parametrize("K", [1456, 8200, 28672])
+def test_bf16_batch1_rows_staged_as_fp16(K):
+    # bf16 activations at batch 1 are staged as fp16 times a power of two fixed
+    # by the row's largest magnitude: rows of any range stay within the bound
     layer = make_layer(5, 0, K=K, N=190)
     x = make_x(5, 0, 1, K=K)
     say("bf16 batch 1", K)
-    check_bound(gpu_forward(layer, x, path="decode"), layer, x, what="exact in fp16")
-    for bad in (np.float32(3.0e5), np.float32(1.2345e-7), np.float32(-7.0e-38)):
+    check_bound(gpu_forward(layer, x, path="decode"), layer, x, what="N(0, 1) row")
+    for big in (np.float32(3.0e5), np.float32(1.0e30), np.float32(-3.0e38), np.float32(1.2345e-7),
+                np.float32(-7.0e-38)):
         xb = x.copy()
-        xb[0, K // 3] = bf16_bits_from_f32(np.array([bad], np.float32))[0]
-        check_bound(gpu_forward(layer, xb, path="decode"), layer, xb, what=f"fallback {bad}")
+        xb[0, K // 3] = bf16_bits_from_f32(np.array([big], np.float32))[0]
+        check_bound(gpu_forward(layer, xb, path="decode"), layer, xb, what=f"one value {big}")
+    r = np.random.default_rng(K)
+    for lo, hi in ((-60, 60), (-130, -100), (-8, 120)):  # whole rows over wide ranges of exponents
+        v = r.choice([-1.0, 1.0], K) * r.uniform(1, 2, K) * np.exp2(r.integers(lo, hi, K))
+        xw = bf16_bits_from_f32(v.astype(np.float32))[None, :]
+        check_bound(gpu_forward(layer, xw, path="decode"), layer, xw, what=f"exponents {lo}..{hi}")
+    xz = np.zeros((1, K), np.uint16)  # zero row: the outputs are the rank term of a zero t, i.e. zero
+    assert np.array_equal(gpu_forward(layer, xz, path="decode"), np.zeros((1, layer.N)))
+    xn = x.copy()
+    xn[0, 7] = 0x7F80  # +inf: every output of the row is NaN
+    assert np.isnan(gpu_forward(layer, xn, path="decode")).all()
+
+
+def test_bf16_batch1_staging_exact_within_range():
+    # identity layer (int8 q = I, scale 1), bf16 activations: y[n] = x'[n] exactly for
+    # every value within 2^29 of the row's largest magnitude; values further below
+    # are off by less than 2^-28 of that magnitude
+    K = 1200
+    layer = LogicalLayer(K=K, N=K, dense="int8", qvals=np.eye(K, dtype=np.int8), row_scale=np.ones(K, np.float16),
+                         x_dtype="bf16")
+    r = np.random.default_rng(7)
+    v = r.choice([-1.0, 1.0], K) * r.uniform(1, 2, K) * np.exp2(r.integers(-20, 9, K))
+    v[3] = 2.0 ** 8 * 1.5  # the row's largest magnitude sits in [2^8, 2^9)
+    v[10:20] = r.uniform(1, 2, 10) * np.exp2(r.integers(-60, -25, 10))  # more than 2^29 below it
+    x = bf16_bits_from_f32(v.astype(np.float32))[None, :]
+    say("bf16 staging exactness")
+    y = gpu_forward(layer, x, path="decode")
+    xf = oracle.activations(layer, x)
+    far = np.zeros(K, bool)
+    far[10:20] = True
+    assert np.array_equal(y[0, ~far], xf[0, ~far])
+    assert (np.abs(y[0, far] - xf[0, far]) < 2.0 ** -28 * 2.0 ** 9).all()
