@@ -48,7 +48,7 @@ TRAFFIC_FILES = {(5, 1): os.path.join(ROOT, "profiles", "decode_lut3_lr_llama70b
                  (2, 1): os.path.join(ROOT, "profiles", "decode_lut4_llama7b_b1_traffic.txt")}
 KERNEL_SOURCES = ["compressed_linear_amd/csrc/decode_rows.h", "compressed_linear_amd/csrc/unpack.h",
                   "compressed_linear_amd/csrc/decode.hip", "compressed_linear_amd/csrc/layout.h",
-                  "compressed_linear_amd/csrc/lowrank.h"]
+                  "compressed_linear_amd/csrc/lowrank.h", "compressed_linear_amd/csrc/decode_stream.h"]
 
 
 def log(*a):
@@ -88,6 +88,14 @@ def read_traffic(cfg: int, M: int):
         return None
 
 
+def batch1_kernel(l) -> str:
+    """The kernel a batch-1 forward of layer l runs on the auto path: the
+    streaming kernel for long rows (K >= 16384, or a rank term and K >= 2N, the
+    library's rule in decode.hip), the row-wise kernel otherwise."""
+    lr = bool(l.rank)
+    return "decode_stream_kernel" if (l.K >= 16384 or (lr and l.K >= 2 * l.N)) else "decode_rows_kernel"
+
+
 def roofline(cfg: int, M: int, path: str, built, set_bytes: int, us_per_launch: float, graph: bool) -> dict:
     """Roofline entry for the launches of one layer (mean over the layers of a step).
 
@@ -110,7 +118,8 @@ def roofline(cfg: int, M: int, path: str, built, set_bytes: int, us_per_launch: 
     achieved = bytes_per_launch / us_per_launch / 1e3
     if M == 1 and path == "auto":
         kind = built[0][0].dense.upper()
-        kernel = f"decode_rows_kernel ({kind}, batch 1; one launch per layer, rank prologue inside)"
+        names = sorted({batch1_kernel(l) for l, _, _ in built})
+        kernel = f"{' + '.join(names)} ({kind}, batch 1; one launch per layer, rank prologue inside)"
     elif path == "decode_valu":
         kernel = f"vector-ALU decode, batch {M} (all launches of a layer)"
     else:

@@ -32,7 +32,7 @@ DENSE = {"lut3": 0, "lut4": 1, "int4": 2, "int8": 3}
 MASK = {"none": 0, "2:4": 1, "bitmap": 2}
 LR = {"none": 0, "fp16": 1, "bf16": 2, "int4": 3}
 ACT = {"f16": 0, "bf16": 1}
-PATH = {"auto": 0, "decode": 1, "prefill": 2, "decode_valu": 3, "decode_mfma": 4}
+PATH = {"auto": 0, "decode": 1, "prefill": 2, "decode_valu": 3, "decode_mfma": 4, "decode_stream": 5}
 STATUS = {0: "CL_OK", -1: "CL_EINVAL", -2: "CL_EUNSUPPORTED", -3: "CL_ENOMEM", -4: "CL_EHIP", -5: "CL_ESIZE"}
 SECTIONS = ["dense", "table", "meta", "nzoff", "rowptr", "col", "val", "L", "R", "Lscale", "Rscale", "xscale"]
 SEC_COUNT = 16

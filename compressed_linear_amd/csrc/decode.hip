@@ -5,6 +5,9 @@
 #include "decode_impl.h"
 #include "decode_mfma.h"
 #include "decode_rows.h"
+#include "decode_stream.h"
+
+#include <algorithm>
 
 namespace cl {
 
@@ -20,6 +23,12 @@ extern template hipError_t launch_rows_kind<K_LUT4>(const RowArgs&, int, bool, h
 extern template hipError_t launch_rows_kind<K_INT4>(const RowArgs&, int, bool, hipStream_t);
 extern template hipError_t launch_rows_kind<K_INT4_24>(const RowArgs&, int, bool, hipStream_t);
 extern template hipError_t launch_rows_kind<K_INT8>(const RowArgs&, int, bool, hipStream_t);
+
+extern template hipError_t launch_stream_kind<K_LUT3>(const StreamArgs&, int, int, int, bool, hipStream_t);
+extern template hipError_t launch_stream_kind<K_LUT4>(const StreamArgs&, int, int, int, bool, hipStream_t);
+extern template hipError_t launch_stream_kind<K_INT4>(const StreamArgs&, int, int, int, bool, hipStream_t);
+extern template hipError_t launch_stream_kind<K_INT4_24>(const StreamArgs&, int, int, int, bool, hipStream_t);
+extern template hipError_t launch_stream_kind<K_INT8>(const StreamArgs&, int, int, int, bool, hipStream_t);
 
 extern template hipError_t launch_mfma_kind<K_LUT3>(const MfArgs&, bool, hipStream_t);
 extern template hipError_t launch_mfma_kind<K_LUT4>(const MfArgs&, bool, hipStream_t);
@@ -128,7 +137,212 @@ static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float
   }
 }
 
+// ---------------------------------------------------------------------------
+// Batch 1 on the streaming kernel: the plan (rows per workgroup, wavefronts per
+// workgroup, LDS layout) is made at create so that every workgroup is resident
+// at once, two per CU (one when its LDS does not allow two), each wavefront
+// walking a few row pairs.
+// ---------------------------------------------------------------------------
+static size_t a16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+template <int KIND>
+static StreamPlanH plan_stream_k(const cl_blob_header& h, const int32_t* rp, int C, int lr_mode) {
+  StreamPlanH p;
+  constexpr bool LUT = KIND == K_LUT3 || KIND == K_LUT4;
+  constexpr int RTB = row_table_bytes<KIND>();
+  constexpr int TABW = LUT ? kStMaxWaves * 2 * RTB / 4 : (KIND == K_INT4_24 ? 64 : 4);
+  constexpr int TB = KIND == K_LUT4 ? 32 : KIND == K_LUT3 ? 16 : 2;
+  const int N = h.N;
+  if (h.K > 65535 || C < 1) return p;  // outlier columns are packed in 16 bits
+  const bool lr = h.lr != CL_LR_NONE && h.rank > 0, lr4 = h.lr == CL_LR_INT4;
+  if (lr && h.rank > 256) return p;
+  const int rrb = lr ? (lr4 ? (h.rank + 1) / 2 : 2 * h.rank) : 0;
+  const int rscb = lr4 ? 2 * (int)ceil_div(h.rank, h.group) : 0;
+  if (lr && (rrb % 2 || rscb % 2)) return p;  // rank rows are staged with 16-byte loads from 8-row boundaries
+  const int npass = (int)ceil_div(h.chunks, 64);
+  const size_t xbytes = (size_t)npass * 64 * RowX<KIND>::stride;
+  const size_t static_lds = (size_t)(TABW + kStMaxWaves) * 4;
+  const size_t lr_lds = (lr && lr_mode >= 0) ? (size_t)lr_scratch_bytes(lr_mode, 1) : 0;
+  const long long P = ceil_div(N, 2);
+  for (int k = 2; k >= 1; --k) {
+    long long q = ceil_div(P, 8LL * k * C);
+    if (q < 1) q = 1;
+    int wpg = (int)ceil_div(ceil_div(P, q), (long long)k * C);
+    wpg = wpg < 4 ? 4 : wpg > kStMaxWaves ? kStMaxWaves : wpg;
+    while (stream_slots_per_thread<KIND>(npass, wpg * 64) > 12 && wpg < kStMaxWaves) ++wpg;
+    if (stream_slots_per_thread<KIND>(npass, wpg * 64) > 12) return p;
+    auto rows_of = [&](long long qq) { return (int)(2 * qq * wpg); };
+    while (q > 1 && (rows_of(q) > kStMaxRows || (long long)rows_of(q) * rrb > kStRankBytes ||
+                     (long long)rows_of(q) * rscb > (long long)wpg * 64 * 16))
+      --q;
+    const int RW = rows_of(q);
+    if (RW > kStMaxRows || (long long)RW * rrb > kStRankBytes || (long long)RW * rscb > (long long)wpg * 64 * 16) return p;
+    const int nwg = (int)ceil_div(N, RW);
+    // outliers of the busiest wavefront
+    long long most = 0;
+    if (rp) {
+      for (int w = 0; w < nwg; ++w) {
+        const int r0 = w * RW, rw = N - r0 < RW ? N - r0 : RW, ngr = (rw + 1) / 2;
+        const int nq = (ngr + wpg - 1) / wpg;
+        for (int v = 0; v < wpg; ++v) {
+          const int a0 = 2 * nq * v, a1 = 2 * nq * (v + 1) < rw ? 2 * nq * (v + 1) : rw;
+          if (a0 < a1) most = std::max<long long>(most, (long long)rp[r0 + a1] - rp[r0 + a0]);
+        }
+      }
+    }
+    int cap = (int)ceil_div(most > 0 ? most : 1, 64) * 64;
+    if (cap > 64 * kStOutLoads) cap = 64 * kStOutLoads;  // entries past it are read from memory
+    StreamPlanH t;
+    size_t off = a16(xbytes);
+    t.lds_meta = (int)off;
+    off += a16((size_t)RW * TB);
+    t.lds_rp = (int)off;
+    off += a16((size_t)(RW + 1) * 4);
+    t.lds_rank = (int)off;
+    off += a16((size_t)RW * rrb);
+    t.lds_rsc = (int)off;
+    off += a16((size_t)RW * rscb);
+    t.lds_out = (int)off;
+    off += (size_t)wpg * cap * 4;
+    const size_t dyn = off > lr_lds ? off : lr_lds;
+    if ((size_t)k * (dyn + static_lds) > 160 * 1024) continue;
+    t.ok = 1;
+    t.wpg = wpg;
+    t.rows_per_wg = RW;
+    t.nwg = nwg;
+    t.npass = npass;
+    t.lds = (int)dyn;
+    t.out_cap = cap;
+    t.rank_row_bytes = rrb;
+    t.rsc_row_bytes = rscb;
+    return t;
+  }
+  return p;
+}
+
+// Which batch-1 layers take the streaming kernel.  Measured on one MI355X (us
+// per layer, streaming / row-wise): LLaMA-70B LUT3 + bf16 rank 64: 8192 ->
+// 10240 20.6 / 17.9, 8192 -> 28672 37.1 / 37.1, 28672 -> 8192 31.0 / 39.1;
+// INT4 2:4 + int4 rank 128: 4096 -> 11008 16.1 / 16.4, 11008 -> 4096 12.1 /
+// 15.3; LUT3 4096 -> 4096 6.7 / 5.2; LLaMA-7B LUT4 layers 1.2-1.3x slower
+// streamed (with few rows per wavefront pair the row-wise kernel keeps more
+// wavefronts resident).  The streaming kernel wins on long rows: K of 16384 or
+// more, or a rank term with K at least twice N.
+static bool stream_wins(const cl_blob_header& h) {
+  const bool lr = h.lr != CL_LR_NONE && h.rank > 0;
+  return h.K >= 16384 || (lr && h.K >= 2 * h.N);
+}
+
+StreamPlanH plan_stream(const cl_blob_header& h, const int32_t* rowptr, int num_cus, int lr_mode) {
+  const int32_t* rp = h.nnz > 0 ? rowptr : nullptr;
+  StreamPlanH p;
+  switch (h.dense) {
+    case CL_DENSE_LUT3: p = plan_stream_k<K_LUT3>(h, rp, num_cus, lr_mode); break;
+    case CL_DENSE_LUT4: p = plan_stream_k<K_LUT4>(h, rp, num_cus, lr_mode); break;
+    case CL_DENSE_INT4:
+      p = h.mask == CL_MASK_2_4 ? plan_stream_k<K_INT4_24>(h, rp, num_cus, lr_mode)
+                                : plan_stream_k<K_INT4>(h, rp, num_cus, lr_mode);
+      break;
+    default:
+      if (h.mask == CL_MASK_BITMAP) return StreamPlanH();
+      p = plan_stream_k<K_INT8>(h, rp, num_cus, lr_mode);
+  }
+  p.pick = p.ok && stream_wins(h);
+  return p;
+}
+
+static hipError_t launch_decode_stream(const Layer& L, const void* x, float* y, hipStream_t stream) {
+  const cl_blob_header& h = L.h;
+  const bool bf16 = h.x_dtype == CL_ACT_BF16;
+  const bool raw = L.xprep != nullptr && x != L.xprep;
+  bool edit = false;
+  if (raw) {
+    if (edit_in_kernel(L)) {
+      edit = true;
+    } else {
+      const hipError_t e = launch_prep_x(L, 1, x, stream);
+      if (e != hipSuccess) return e;
+      x = L.xprep;
+    }
+  }
+  StreamArgs s = {};
+  RowArgs& r = s.r;
+  r.dense = reinterpret_cast<const uint4*>(L.dense);
+  r.meta = L.meta;
+  r.table = reinterpret_cast<const uint16_t*>(L.table);
+  r.rowptr = h.nnz > 0 ? L.rowptr : nullptr;
+  r.col = L.col;
+  r.val = L.val;
+  r.R = L.R;
+  r.Rscale = L.Rscale;
+  r.t = L.t;
+  r.x = x;
+  r.ldx = (x == L.xprep) ? L.Kx : h.K;
+  r.y = y;
+  r.K = h.K;
+  r.N = h.N;
+  r.M = 1;
+  r.chunks = h.chunks;
+  r.rank = h.lr != CL_LR_NONE ? h.rank : 0;
+  r.group = h.group > 0 ? h.group : 1;
+  r.group_mul = (uint32_t)((65536 + r.group - 1) / r.group);
+  r.lr_kind = h.lr;
+  r.Npad = L.Npad;
+  r.nnz = (int)h.nnz;
+  r.clamp = edit && h.has_clamp ? 1 : 0;
+  r.cval = (float)__builtin_bit_cast(_Float16, h.act_clamp);
+  r.xscale = edit ? L.xscale : nullptr;
+  int lr_lds = 0;
+  if (h.lr != CL_LR_NONE) {
+    if (L.lr_mode >= 0) {  // the prologue runs as this launch's first workgroups
+      r.lrp = lowrank_split_args(L, 1, x);
+      r.lrp.clamp = r.clamp;
+      r.lrp.cval = r.cval;
+      r.lrp.xscale = r.xscale;
+      r.lrp.flag = L.lr_cnt + 65;
+      r.lrp.epoch = next_epoch(L, stream);
+      r.lrp.withhold = L.wait_withhold;
+      r.lr_ntj = L.lr_rpad / 64;
+      r.lr_wgs = L.lr_S * r.lr_ntj;
+      r.lr_mode = L.lr_mode;
+      r.lr_flag = r.lrp.flag;
+      r.lr_epoch = r.lrp.epoch;
+      r.lr_max_polls = L.wait_polls;
+      r.lr_err = L.wait_err_dev;
+      lr_lds = lr_scratch_bytes(L.lr_mode, 1);
+    } else {
+      const hipError_t e = launch_lowrank_prologue(L, 1, x, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  const StreamPlanH& p = L.st;
+  s.rows_per_wg = p.rows_per_wg;
+  s.npass = p.npass;
+  s.lds_meta = p.lds_meta;
+  s.lds_rp = p.lds_rp;
+  s.lds_rank = p.lds_rank;
+  s.lds_rsc = p.lds_rsc;
+  s.lds_out = p.lds_out;
+  s.rank_row_bytes = p.rank_row_bytes;
+  s.rsc_row_bytes = p.rsc_row_bytes;
+  s.out_cap = p.out_cap;
+  s.row_waves = p.nwg * p.wpg;
+  const int lds = p.lds > lr_lds ? p.lds : lr_lds;
+  const int grid = r.lr_wgs + p.nwg, threads = p.wpg * 64;
+  switch (h.dense) {
+    case CL_DENSE_LUT3: return launch_stream_kind<K_LUT3>(s, grid, threads, lds, bf16, stream);
+    case CL_DENSE_LUT4: return launch_stream_kind<K_LUT4>(s, grid, threads, lds, bf16, stream);
+    case CL_DENSE_INT4:
+      return h.mask == CL_MASK_2_4 ? launch_stream_kind<K_INT4_24>(s, grid, threads, lds, bf16, stream)
+                                   : launch_stream_kind<K_INT4>(s, grid, threads, lds, bf16, stream);
+    default: return launch_stream_kind<K_INT8>(s, grid, threads, lds, bf16, stream);
+  }
+}
+
 hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, int variant) {
+  // batch 1: the streaming kernel where it is the faster one for the layer's shape
+  if (M == 1 && L.st.ok && (variant == 3 || (variant == 0 && L.st.pick))) return launch_decode_stream(L, x, y, stream);
+
   // bf16 activations cost the row-wise kernel two multiply-adds per weight pair
   // and activation row (no mixed fp16 x bf16 dot product), so it keeps only batch 1
   const bool mf_auto = M >= kMfMinM || (M >= 2 && L.h.x_dtype == CL_ACT_BF16);

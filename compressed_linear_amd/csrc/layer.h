@@ -12,6 +12,16 @@ constexpr int kMaxDecodeM = 32;
 constexpr int kLrSlice = 512;  // K rows per workgroup of the decode low-rank prologue
 constexpr uint32_t kLrMaxPolls = 1u << 20;  // default bound of the in-launch wait for t (polls)
 
+// Launch plan of the batch-1 streaming kernel, made at create (ok = 0: the
+// row-wise kernel serves batch 1).  LDS offsets are bytes into the dynamic LDS.
+struct StreamPlanH {
+  int ok = 0;    // the layer fits the kernel's plan
+  int pick = 0;  // and the kernel is the faster batch-1 choice for its shape
+  int wpg = 0, rows_per_wg = 0, nwg = 0, npass = 0, lds = 0, out_cap = 0;
+  int lds_meta = 0, lds_rp = 0, lds_rank = 0, lds_rsc = 0, lds_out = 0;
+  int rank_row_bytes = 0, rsc_row_bytes = 0;
+};
+
 struct Layer {
   cl_blob_header h;          // copy of the blob header
   uint8_t* dev = nullptr;    // dev_buf (caller owned)
@@ -81,6 +91,7 @@ struct Layer {
   // up sets (pinned host memory, so the next forward reads it without a sync;
   // wait_err_dev is its device address), and the test switch that withholds
   // the publication of t
+  StreamPlanH st;                // batch-1 streaming kernel
   uint32_t wait_polls = 0;
   int wait_withhold = 0;
   volatile uint32_t* wait_err_host = nullptr;
@@ -99,9 +110,13 @@ hipError_t launch_lowrank_prologue(const Layer& L, int M, const void* x, hipStre
 // (x: the caller's activations, or L.xprep when done already) and the low-rank
 // prologue: inside the decode launch when it applies (publishing the launch's
 // generation, derived on the device), else as kernels of their own.
-// variant: 0 the faster kernel for M, 1 the vector-ALU kernels, 2 the matrix-core kernel
+// variant: 0 the faster kernel for M, 1 the vector-ALU kernels (row-wise at M = 1),
+// 2 the matrix-core kernel, 3 the batch-1 streaming kernel (M = 1, st.ok)
 hipError_t launch_decode(const Layer& L, int M, const void* x, float* y, hipStream_t stream, int variant);
 hipError_t launch_prefill(const Layer& L, int M, const void* x, float* y, hipStream_t stream);
+// Plan of the batch-1 streaming kernel from the blob header and its CSR row
+// pointers (NULL without outliers), for a device of num_cus CUs.
+StreamPlanH plan_stream(const cl_blob_header& h, const int32_t* rowptr, int num_cus, int lr_mode);
 hipError_t launch_debug(const Layer& L, uint16_t* D16, uint16_t* S16, float* L32, float* R32, hipStream_t stream);
 
 }  // namespace cl

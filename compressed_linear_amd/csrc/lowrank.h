@@ -191,8 +191,9 @@ inline int lr_scratch_bytes(int mode, int mt) {
                    : (mt == 1 ? LrScratch<1, 1>::bytes : mt == 2 ? LrScratch<1, 2>::bytes : LrScratch<1, 4>::bytes);
 }
 
-// One workgroup (256 threads) of the split prologue: K slice s, column tile tj
-// of ntj, activation tile tm; `smem` is LrScratch<MODE, MT>::bytes of LDS.
+// One workgroup (256 threads, or more: the threads past 256 compute nothing
+// that is kept) of the split prologue: K slice s, column tile tj of ntj,
+// activation tile tm; `smem` is LrScratch<MODE, MT>::bytes of LDS.
 // EDIT: the activations may be raw (a.clamp, a.xscale apply); else they are
 // edited already.
 template <int MODE, int MT, bool BF16, bool EDIT>
@@ -244,7 +245,7 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
   if constexpr (MODE == 1) {
     const int ng = (k0 + kLrSlice - 1) / a.group - g0 + 1;
     const brsrc_t rs = make_rsrc(a.ls, (uint32_t)((a.Kl + a.group - 1) / a.group) * (uint32_t)a.rpad * 2u);
-    for (int i = tid; i < ng * 8; i += 256) {
+    for (int i = tid; i < ng * 8; i += (int)blockDim.x) {
       const int row = i >> 3, part = i & 7;
       const uint4 v = bload128(rs, ((uint32_t)(g0 + row) * (uint32_t)a.rpad + (uint32_t)(j0 + 8 * part)) * 2u, 0);
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
@@ -310,7 +311,7 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
       v += __shfl_xor(v, 32, 64);
       acc[m][j] = v;
     }
-  if (lane < 16) {
+  if (lane < 16 && tid < 256) {  // a wider workgroup's threads past 256 only keep the barriers
     const int grp = MODE == 0 ? wave : wave * 4 + (lane >> 2);
 #pragma unroll
     for (int m = 0; m < MT; ++m)

@@ -407,6 +407,10 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
       }
     }
   }
+  // batch 1: the streaming kernel's plan (its outlier capacity from the row pointers)
+  L->st = plan_stream(*h, h->nnz > 0 ? reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(blob) + h->off[CL_SEC_ROWPTR])
+                                     : nullptr,
+                      L->num_cus, L->lr_mode);
   PrefillHost pf;
   const bool bm_pf = L->pf_dense8 != nullptr;
   if (h->mask != CL_MASK_BITMAP || bm_pf || L->pf_r16)
@@ -496,12 +500,15 @@ static cl_status forward_impl(Layer* L, int32_t M, const void* x, float* y, void
   if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 16)
     return fail(CL_EINVAL, "x and y must be 16-byte aligned");
   if (path == CL_PATH_AUTO) path = M <= kMaxDecodeM ? CL_PATH_DECODE : CL_PATH_PREFILL;
-  if (path != CL_PATH_DECODE && path != CL_PATH_PREFILL && path != CL_PATH_DECODE_VALU && path != CL_PATH_DECODE_MFMA)
+  if (path != CL_PATH_DECODE && path != CL_PATH_PREFILL && path != CL_PATH_DECODE_VALU &&
+      path != CL_PATH_DECODE_MFMA && path != CL_PATH_DECODE_STREAM)
     return fail(CL_EINVAL, "unknown path %d", path);
   const bool decode = path != CL_PATH_PREFILL;
   if (decode && M > kMaxDecodeM) return fail(CL_EINVAL, "the decode path takes M <= %d", kMaxDecodeM);
   if (path == CL_PATH_DECODE_MFMA && L->mf_S == 0)
     return fail(CL_EUNSUPPORTED, "the matrix-core decode needs a bitmap layer or one created with max_M >= 2");
+  if (path == CL_PATH_DECODE_STREAM && (M != 1 || !L->st.ok))
+    return fail(CL_EUNSUPPORTED, "the streaming decode takes M = 1 and a layer that fits its LDS plan");
   if (L->wait_err_host && L->wait_err_host[0]) {  // set by a wait for t that gave up in an earlier forward
     L->wait_err_host[0] = 0;
     return fail(CL_EHIP, "an earlier forward on this layer gave up waiting for x' L inside its launch; "
@@ -510,7 +517,8 @@ static cl_status forward_impl(Layer* L, int32_t M, const void* x, float* y, void
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (decode) {  // the decode dispatch clamps / restages x itself (in its kernels where it can)
-    const int variant = path == CL_PATH_DECODE_VALU ? 1 : path == CL_PATH_DECODE_MFMA ? 2 : 0;
+    const int variant = path == CL_PATH_DECODE_VALU ? 1 : path == CL_PATH_DECODE_MFMA ? 2
+                      : path == CL_PATH_DECODE_STREAM ? 3 : 0;
     e = launch_decode(*L, M, x, y, s, variant);
   } else {
     const void* xa = x;

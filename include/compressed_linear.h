@@ -63,14 +63,17 @@ typedef enum { CL_MASK_NONE = 0, CL_MASK_2_4 = 1, CL_MASK_BITMAP = 2 } cl_mask_k
 typedef enum { CL_LR_NONE = 0, CL_LR_FP16 = 1, CL_LR_BF16 = 2, CL_LR_INT4 = 3 } cl_lr_kind;
 typedef enum { CL_ACT_F16 = 0, CL_ACT_BF16 = 1 } cl_act_dtype;
 /* Forward paths: AUTO picks by M (decode for M <= 32, else prefill); DECODE
- * picks the faster decode kernel for M; DECODE_VALU forces the vector-ALU
- * decode kernels, DECODE_MFMA the matrix-core decode kernel. */
+ * picks the faster decode kernel for M and the layer's shape; DECODE_VALU
+ * forces the vector-ALU decode kernels (at M = 1 the row-wise one),
+ * DECODE_MFMA the matrix-core decode kernel, DECODE_STREAM the batch-1
+ * streaming kernel. */
 typedef enum {
   CL_PATH_AUTO = 0,
   CL_PATH_DECODE = 1,
   CL_PATH_PREFILL = 2,
   CL_PATH_DECODE_VALU = 3,
-  CL_PATH_DECODE_MFMA = 4
+  CL_PATH_DECODE_MFMA = 4,
+  CL_PATH_DECODE_STREAM = 5
 } cl_path;
 
 /*
@@ -247,7 +250,8 @@ cl_status cl_forward(void* handle, int32_t M, const void* x_dev, float* y_dev, v
 
 /* cl_forward with an explicit path (cl_path); CL_PATH_AUTO behaves as cl_forward.
  * The decode paths require M <= 32; CL_PATH_DECODE_MFMA also a bitmap layer or
- * one created with max_M >= 2 (else CL_EUNSUPPORTED). */
+ * one created with max_M >= 2, CL_PATH_DECODE_STREAM M = 1 and a layer whose
+ * shape fits the streaming kernel's LDS plan (else CL_EUNSUPPORTED). */
 cl_status cl_forward_path(void* handle, int32_t M, const void* x_dev, float* y_dev,
                           void* stream, int32_t path);
 

@@ -11,7 +11,7 @@ other rounding, for a layer without a low-rank part.
 
 Expected values, from the oracle's planes D and S (fp64) and the readings of
 each route (every rounding nearest-even):
-  decode kernels (row-wise, tile, matrix-core): the weight enters the product
+  decode kernels (streaming, row-wise, tile, matrix-core): the weight enters the product
       as fp16 LUT value, or (matrix-core kernel, bf16 activations) that value
       rounded to bf16; integer codes exactly, the row scale applied to the
       fp32 sum (q * s is exact in fp32); the outlier is added in fp32:
@@ -67,7 +67,8 @@ def expected(layer, ks, route):
 
 
 ROUTES = {  # route -> (path, activation rows per launch)
-    "rows1": ("decode", 1),        # batch-1 row kernel (raw activations edited in it when the layer clamps)
+    "stream": ("decode_stream", 1),  # batch-1 streaming kernel (raw activations edited in it when the layer clamps)
+    "rows1": ("decode_valu", 1),   # row kernel, one activation row
     "rows4": ("decode_valu", 4),   # row kernel, four activation rows
     "tile": ("decode_valu", 32),   # tile kernel
     "mfma": ("decode_mfma", 32),   # matrix-core decode
@@ -128,7 +129,7 @@ def small_layer(fmt, x_dtype, K, N=200, seed=0):
 def _routes_for(layer):
     rs = ["tile", "mfma", "prefill"]
     if layer.mask != "bitmap":  # the bitmap decodes on the tile and matrix-core kernels only
-        rs = ["rows1", "rows4"] + rs
+        rs = ["stream", "rows1", "rows4"] + rs
     return rs
 
 
@@ -148,7 +149,7 @@ def test_every_route_bit_exact_small(fmt, x_dtype, K):
     try:
         for route in _routes_for(layer):
             ks = np.arange(K)
-            if route == "rows1":  # one launch per k: a sample
+            if route in ("stream", "rows1"):  # one launch per k: a sample
                 ks = np.unique(np.r_[0, 1, 39, 40, 63, 64, K - 2, K - 1, np.random.default_rng(K).integers(0, K, 24)])
             say(layer.name, route, len(ks))
             check_route(mod, layer, ks, route, layer.name)
@@ -180,7 +181,8 @@ def test_every_route_bit_exact_full_size_sampled(cfg, name):
     mod = gpu_layer(layer, max_M=len(ks))
     try:
         for route in _routes_for(layer):
-            kk = {"rows1": _spread(ks, 8), "rows4": _spread(ks, 16), "tile": _spread(ks, 32)}.get(route, ks)
+            kk = {"stream": _spread(ks, 8), "rows1": _spread(ks, 8), "rows4": _spread(ks, 16),
+                  "tile": _spread(ks, 32)}.get(route, ks)
             say(layer.name, route, len(kk))
             check_route(mod, layer, kk, route, layer.name)
     finally:
