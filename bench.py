@@ -88,12 +88,11 @@ def read_traffic(cfg: int, M: int):
         return None
 
 
-def batch1_kernel(l) -> str:
+def batch1_kernel(l, acct) -> str:
     """The kernel a batch-1 forward of layer l runs on the auto path: the
-    streaming kernel for long rows (K >= 16384, or a rank term and K >= 2N, the
-    library's rule in decode.hip), the row-wise kernel otherwise."""
-    lr = bool(l.rank)
-    return "decode_stream_kernel" if (l.K >= 16384 or (lr and l.K >= 2 * l.N)) else "decode_rows_kernel"
+    streaming kernel for layers of 28 MiB of code chunks or more (the library's
+    rule in decode.hip), the row-wise kernel otherwise."""
+    return "decode_stream_kernel" if acct["codes"] >= (28 << 20) else "decode_rows_kernel"
 
 
 def roofline(cfg: int, M: int, path: str, built, set_bytes: int, us_per_launch: float, graph: bool) -> dict:
@@ -118,7 +117,7 @@ def roofline(cfg: int, M: int, path: str, built, set_bytes: int, us_per_launch: 
     achieved = bytes_per_launch / us_per_launch / 1e3
     if M == 1 and path == "auto":
         kind = built[0][0].dense.upper()
-        names = sorted({batch1_kernel(l) for l, _, _ in built})
+        names = sorted({batch1_kernel(l, acct) for l, acct, _ in built})
         kernel = f"{' + '.join(names)} ({kind}, batch 1; one launch per layer, rank prologue inside)"
     elif path == "decode_valu":
         kernel = f"vector-ALU decode, batch {M} (all launches of a layer)"

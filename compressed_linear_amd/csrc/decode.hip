@@ -140,60 +140,56 @@ static hipError_t launch_decode_mfma(const Layer& L, int M, const void* x, float
 // ---------------------------------------------------------------------------
 // Batch 1 on the streaming kernel: the plan (rows per workgroup, wavefronts per
 // workgroup, LDS layout) is made at create so that every workgroup is resident
-// at once, two per CU (one when its LDS does not allow two), each wavefront
-// walking a few row pairs.
+// at once: one workgroup of 16 wavefronts per CU, or two of 8 when the LDS of
+// one does not allow 16.
 // ---------------------------------------------------------------------------
 static size_t a16(size_t v) { return (v + 15) & ~(size_t)15; }
 
 template <int KIND>
-static StreamPlanH plan_stream_k(const cl_blob_header& h, const int32_t* rp, int C, int lr_mode) {
+static StreamPlanH plan_stream_k(const cl_blob_header& h, const int32_t* rp, int num_cus, int lr_mode) {
   StreamPlanH p;
   constexpr bool LUT = KIND == K_LUT3 || KIND == K_LUT4;
   constexpr int RTB = row_table_bytes<KIND>();
-  constexpr int TABW = LUT ? kStMaxWaves * 2 * RTB / 4 : (KIND == K_INT4_24 ? 64 : 4);
   constexpr int TB = KIND == K_LUT4 ? 32 : KIND == K_LUT3 ? 16 : 2;
-  const int N = h.N;
-  if (h.K > 65535 || C < 1) return p;  // outlier columns are packed in 16 bits
+  const int N = h.N, C = (int)h.chunks;
+  // outlier columns are packed in 16 bits; a pass meets at most one row boundary
+  if (h.K > 65535 || C < 64) return p;
   const bool lr = h.lr != CL_LR_NONE && h.rank > 0, lr4 = h.lr == CL_LR_INT4;
   if (lr && h.rank > 256) return p;
   const int rrb = lr ? (lr4 ? (h.rank + 1) / 2 : 2 * h.rank) : 0;
   const int rscb = lr4 ? 2 * (int)ceil_div(h.rank, h.group) : 0;
-  if (lr && (rrb % 2 || rscb % 2)) return p;  // rank rows are staged with 16-byte loads from 8-row boundaries
-  const int npass = (int)ceil_div(h.chunks, 64);
-  const size_t xbytes = (size_t)npass * 64 * RowX<KIND>::stride;
-  const size_t static_lds = (size_t)(TABW + kStMaxWaves) * 4;
-  const size_t lr_lds = (lr && lr_mode >= 0) ? (size_t)lr_scratch_bytes(lr_mode, 1) : 0;
-  const long long P = ceil_div(N, 2);
-  for (int k = 2; k >= 1; --k) {
-    long long q = ceil_div(P, 8LL * k * C);
-    if (q < 1) q = 1;
-    int wpg = (int)ceil_div(ceil_div(P, q), (long long)k * C);
-    wpg = wpg < 4 ? 4 : wpg > kStMaxWaves ? kStMaxWaves : wpg;
-    while (stream_slots_per_thread<KIND>(npass, wpg * 64) > 12 && wpg < kStMaxWaves) ++wpg;
-    if (stream_slots_per_thread<KIND>(npass, wpg * 64) > 12) return p;
-    auto rows_of = [&](long long qq) { return (int)(2 * qq * wpg); };
-    while (q > 1 && (rows_of(q) > kStMaxRows || (long long)rows_of(q) * rrb > kStRankBytes ||
-                     (long long)rows_of(q) * rscb > (long long)wpg * 64 * 16))
-      --q;
-    const int RW = rows_of(q);
-    if (RW > kStMaxRows || (long long)RW * rrb > kStRankBytes || (long long)RW * rscb > (long long)wpg * 64 * 16) return p;
+  if (lr && (rrb % 2 || rscb % 2)) return p;
+  // rank rows and scales are staged with 16-byte loads: rows per workgroup a multiple of m
+  int m = 1;
+  while ((m * rrb) % 16 || (m * rscb) % 16) m *= 2;
+  for (int wpg = kStMaxWaves; wpg >= 8; wpg /= 2) {
+    const int threads = wpg * 64, k = kStMaxWaves / wpg;  // workgroups per CU
+    if (stream_slots_per_thread<KIND>(C, threads) > 12) continue;
+    // the prologue workgroups (the launch's first) hold their CUs while they
+    // run: the row workgroups take the others, so that none waits for a CU
+    const int lr_wgs = (lr && lr_mode >= 0) ? stream_lr_slices((int)ceil_div(h.K, kLrSlice), threads) *
+                                                  (int)ceil_div(h.rank, 64) : 0;
+    const size_t lr_lds = lr_wgs ? (size_t)lr_scratch_bytes(lr_mode, 1, threads == 1024 ? 1024 : 256) : 0;
+    const long long slots = (long long)num_cus * k - lr_wgs;
+    if (slots < (long long)num_cus * k / 2) continue;
+    const int RW = (int)(ceil_div(ceil_div(N, slots), m) * m);
+    if (RW + 1 > threads) continue;                       // one row (pointer) per thread
+    if (LUT && RW * RTB > stream_tab_bytes<KIND>()) continue;  // row tables in the static array
+    if ((long long)RW * rrb > 2LL * 16 * threads || (long long)RW * rscb > 16LL * threads) continue;
     const int nwg = (int)ceil_div(N, RW);
-    // outliers of the busiest wavefront
-    long long most = 0;
-    if (rp) {
+    long long most = 0;  // outliers of the busiest workgroup
+    if (rp)
       for (int w = 0; w < nwg; ++w) {
-        const int r0 = w * RW, rw = N - r0 < RW ? N - r0 : RW, ngr = (rw + 1) / 2;
-        const int nq = (ngr + wpg - 1) / wpg;
-        for (int v = 0; v < wpg; ++v) {
-          const int a0 = 2 * nq * v, a1 = 2 * nq * (v + 1) < rw ? 2 * nq * (v + 1) : rw;
-          if (a0 < a1) most = std::max<long long>(most, (long long)rp[r0 + a1] - rp[r0 + a0]);
-        }
+        const int r0 = w * RW, r1 = r0 + RW < N ? r0 + RW : N;
+        most = std::max<long long>(most, (long long)rp[r1] - rp[r0]);
       }
-    }
-    int cap = (int)ceil_div(most > 0 ? most : 1, 64) * 64;
-    if (cap > 64 * kStOutLoads) cap = 64 * kStOutLoads;  // entries past it are read from memory
+    const int cap = (int)std::min<long long>(most, (long long)kStOutLoads * threads);
     StreamPlanH t;
-    size_t off = a16(xbytes);
+    size_t off = 0;
+    t.lds_x = (int)off;
+    off += a16((size_t)C * RowX<KIND>::stride);
+    t.lds_max = (int)off;
+    off += (size_t)kStMaxWaves * 4;
     t.lds_meta = (int)off;
     off += a16((size_t)RW * TB);
     t.lds_rp = (int)off;
@@ -202,15 +198,20 @@ static StreamPlanH plan_stream_k(const cl_blob_header& h, const int32_t* rp, int
     off += a16((size_t)RW * rrb);
     t.lds_rsc = (int)off;
     off += a16((size_t)RW * rscb);
+    t.lds_part0 = (int)off;
+    off += (size_t)RW * 256;
+    t.lds_part1 = (int)off;
+    off += (size_t)wpg * 256;
     t.lds_out = (int)off;
-    off += (size_t)wpg * cap * 4;
+    off += a16((size_t)cap * 4);  // columns and values, 16 bits each
+    t.lds_t = (int)off;
+    off += lr ? (size_t)h.rank * 4 : 0;
     const size_t dyn = off > lr_lds ? off : lr_lds;
-    if ((size_t)k * (dyn + static_lds) > 160 * 1024) continue;
+    if ((size_t)k * (dyn + stream_tab_bytes<KIND>()) > 160 * 1024) continue;
     t.ok = 1;
     t.wpg = wpg;
     t.rows_per_wg = RW;
     t.nwg = nwg;
-    t.npass = npass;
     t.lds = (int)dyn;
     t.out_cap = cap;
     t.rank_row_bytes = rrb;
@@ -220,17 +221,18 @@ static StreamPlanH plan_stream_k(const cl_blob_header& h, const int32_t* rp, int
   return p;
 }
 
-// Which batch-1 layers take the streaming kernel.  Measured on one MI355X (us
-// per layer, streaming / row-wise): LLaMA-70B LUT3 + bf16 rank 64: 8192 ->
-// 10240 20.6 / 17.9, 8192 -> 28672 37.1 / 37.1, 28672 -> 8192 31.0 / 39.1;
-// INT4 2:4 + int4 rank 128: 4096 -> 11008 16.1 / 16.4, 11008 -> 4096 12.1 /
-// 15.3; LUT3 4096 -> 4096 6.7 / 5.2; LLaMA-7B LUT4 layers 1.2-1.3x slower
-// streamed (with few rows per wavefront pair the row-wise kernel keeps more
-// wavefronts resident).  The streaming kernel wins on long rows: K of 16384 or
-// more, or a rank term with K at least twice N.
+// Which batch-1 layers take the streaming kernel.  Its launch costs a fixed
+// few microseconds (dispatch of full-CU workgroups, staging the activations and
+// row tables once per CU) and then streams at close to the memory rate; the
+// row-wise kernel starts at once but streams slower.  Measured on one MI355X
+// (us per layer, streaming / row-wise): LLaMA-70B LUT3 + bf16 rank 64 8192 ->
+// 10240 (32 MiB of codes) 17.1 / 18.7, 8192 -> 28672 30.7 / 36.6, 28672 ->
+// 8192 30.9 / 37.0; LLaMA-7B LUT4 4096 -> 12288 (24 MiB) 12.9 / 9.8, 4096 ->
+// 11008 12.1 / 9.8; INT4 2:4 + int4 rank 128 4096 -> 11008 16.3 / 16.0;
+// LUT3 4096 -> 4096 7.6 / 4.9.  The streaming kernel takes layers of 28 MiB
+// of codes or more.
 static bool stream_wins(const cl_blob_header& h) {
-  const bool lr = h.lr != CL_LR_NONE && h.rank > 0;
-  return h.K >= 16384 || (lr && h.K >= 2 * h.N);
+  return (unsigned long long)h.N * h.chunks * 16ull >= (28ull << 20);
 }
 
 StreamPlanH plan_stream(const cl_blob_header& h, const int32_t* rowptr, int num_cus, int lr_mode) {
@@ -302,14 +304,15 @@ static hipError_t launch_decode_stream(const Layer& L, const void* x, float* y, 
       r.lrp.flag = L.lr_cnt + 65;
       r.lrp.epoch = next_epoch(L, stream);
       r.lrp.withhold = L.wait_withhold;
+      r.lrp.S = stream_lr_slices(L.lr_S, L.st.wpg * 64);  // blocks over longer K slices
       r.lr_ntj = L.lr_rpad / 64;
-      r.lr_wgs = L.lr_S * r.lr_ntj;
+      r.lr_wgs = r.lrp.S * r.lr_ntj;
       r.lr_mode = L.lr_mode;
       r.lr_flag = r.lrp.flag;
       r.lr_epoch = r.lrp.epoch;
       r.lr_max_polls = L.wait_polls;
       r.lr_err = L.wait_err_dev;
-      lr_lds = lr_scratch_bytes(L.lr_mode, 1);
+      lr_lds = lr_scratch_bytes(L.lr_mode, 1, L.st.wpg * 64 == 1024 ? 1024 : 256);
     } else {
       const hipError_t e = launch_lowrank_prologue(L, 1, x, stream);
       if (e != hipSuccess) return e;
@@ -317,16 +320,20 @@ static hipError_t launch_decode_stream(const Layer& L, const void* x, float* y, 
   }
   const StreamPlanH& p = L.st;
   s.rows_per_wg = p.rows_per_wg;
-  s.npass = p.npass;
+  s.lds_x = p.lds_x;
+  s.lds_max = p.lds_max;
   s.lds_meta = p.lds_meta;
   s.lds_rp = p.lds_rp;
   s.lds_rank = p.lds_rank;
   s.lds_rsc = p.lds_rsc;
+  s.lds_part0 = p.lds_part0;
+  s.lds_part1 = p.lds_part1;
   s.lds_out = p.lds_out;
+  s.lds_t = p.lds_t;
   s.rank_row_bytes = p.rank_row_bytes;
   s.rsc_row_bytes = p.rsc_row_bytes;
   s.out_cap = p.out_cap;
-  s.row_waves = p.nwg * p.wpg;
+  s.lr_readers = p.nwg;
   const int lds = p.lds > lr_lds ? p.lds : lr_lds;
   const int grid = r.lr_wgs + p.nwg, threads = p.wpg * 64;
   switch (h.dense) {

@@ -269,9 +269,9 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
       const int c = cbase + p * 2 * CPH + half * CPH + q;
       const bool ok = p < a.npw && c < a.chunks;
       const uint32_t idx = (uint32_t)n * (uint32_t)a.chunks + (uint32_t)c;
-      w[q] = bload128(rd, ok ? idx * 16u : kNoLoad, 0);
+      w[q] = bload128_nt(rd, ok ? idx * 16u : kNoLoad, 0);
       if constexpr (KIND == K_INT4_24)
-        mw[q] = bload64(rm, ok ? idx * 8u : kNoLoad, 0);
+        mw[q] = bload64_nt(rm, ok ? idx * 8u : kNoLoad, 0);
       else
         mw[q] = make_uint2(0, 0);
     }

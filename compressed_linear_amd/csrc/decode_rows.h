@@ -296,9 +296,9 @@ __global__ void __launch_bounds__(256) decode_rows_kernel(RowArgs a) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const uint32_t idx = (uint32_t)(row0 + r) * (uint32_t)a.chunks + (uint32_t)c;  // rows past Npad: out of range
-        w[q][r] = bload128(rd, okc ? idx * 16u : kNoLoad, 0);
+        w[q][r] = bload128_nt(rd, okc ? idx * 16u : kNoLoad, 0);
         if constexpr (KIND == K_INT4_24)
-          mw[q][r] = bload64(rm, okc ? idx * 8u : kNoLoad, 0);
+          mw[q][r] = bload64_nt(rm, okc ? idx * 8u : kNoLoad, 0);
         else
           mw[q][r] = make_uint2(0, 0);
       }

@@ -1,25 +1,30 @@
-// decode_stream.h -- batch-1 forward streamed by resident wavefronts.
+// decode_stream.h -- batch-1 forward: every wavefront streams an equal share of
+// its workgroup's code chunks.
 //
-// The row-wise kernel gives each wavefront two rows: every wavefront issues
-// its loads, waits, then multiplies, so the memory latency and the vector work
-// of the resident wavefronts follow each other instead of overlapping, and the
-// per-workgroup work (staging the activations) is spread over only eight rows.
-// Here a workgroup of 4..8 wavefronts owns a contiguous range of rows sized so
-// that all workgroups are resident at once (two per CU), and each wavefront
-// walks its own rows two at a time ("groups") with the code stream pipelined
-// across group boundaries: while one group is multiplied, the codes of the
-// next ones are in flight.
+// A workgroup of up to 16 wavefronts owns a contiguous block of rows, sized so
+// that every workgroup of the launch is resident at once.  The rows' code
+// chunks are contiguous in memory (row-major, `chunks` per row), so the
+// workgroup's chunks form one flat range; each wavefront takes an equal slice
+// of it (whole passes of 64 chunks, at least one row's worth), whatever the
+// row boundaries, and walks it one chunk per lane per pass.  No lane idles at
+// the end of a row (K = 8192 in 40-weight chunks is 205 chunks: four 64-lane
+// passes per row would leave 20% of the lanes without work), the code loads
+// need no per-load address work, and the loads of the next passes are in
+// flight while one pass is multiplied.
 //
-// Everything a group needs besides its codes is staged in LDS once per
-// workgroup before the walk (the activations, converted to fp16 with a row
-// scale when they are bf16; the LUT values or row scales, row pointers and
-// rank-factor rows of the workgroup's rows) or once per wavefront (the
-// outliers of its rows, packed as column | fp16 value << 16), so the loads
-// inside the walk are the code blocks alone and the compiler's load counting
-// stays exact.  Dequantisation, the balanced outlier spread over the lanes
-// ("SqueezeLLM: Dense-and-Sparse Quantization", Approach and measured-effects
-// table) and the rank-r term ("SLiM" page, review highlights) are those of the
-// row-wise kernel; t = x' L_hat comes from the launch's first workgroups.
+// A row has at least 64 chunks, so a pass meets at most one row boundary, at a
+// lane that is the same for the whole wavefront: the lanes before it are in
+// row n, the lanes from it on in row n + 1.  At that pass each lane's partial
+// sum of row n goes to LDS; a row split between two slices gets one such
+// vector from each.  After the walk, each row's partial vectors, its outliers
+// (the balanced spread over the lanes of "SqueezeLLM: Dense-and-Sparse
+// Quantization", Approach and measured-effects table) and its rank-r term
+// ("SLiM" page, review highlights) are summed by one wavefront reduction.
+// Everything besides the codes (activations, converted to fp16 with a row
+// scale when they are bf16; LUT tables or row scales; row pointers; outliers;
+// rank-factor rows) is staged in LDS once per workgroup before the walk, so
+// the loads inside it are the code chunks alone and the compiler's load
+// counting stays exact.  t = x' L_hat comes from the launch's first workgroups.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -27,75 +32,100 @@
 
 namespace cl {
 
-constexpr int kStMaxWaves = 8;    // wavefronts per workgroup (4..8)
-constexpr int kStOutLoads = 8;    // outlier entries a lane loads for its wavefront
-constexpr int kStMaxRows = 128;   // rows per workgroup (metadata staged one vector per thread)
-constexpr int kStRankBytes = 8192;  // rank-factor bytes staged per workgroup (two vectors per thread)
+constexpr int kStMaxWaves = 16;  // wavefronts per workgroup
+constexpr int kStOutLoads = 6;   // outlier entries a thread stages
+#ifndef CL_ST_NB
+#define CL_ST_NB 4
+#endif
+#ifndef CL_ST_NBUF
+#define CL_ST_NBUF 2
+#endif
+constexpr int kStNB = CL_ST_NB;      // passes per block of the code stream
+constexpr int kStNBUF = CL_ST_NBUF;  // blocks in flight
 
 struct StreamArgs {
   RowArgs r;            // pointers, sizes, activation edits, the in-launch prologue
-  int rows_per_wg;      // RW: rows of each workgroup (a multiple of 8)
-  int npass;            // passes of 64 chunks per row
-  int lds_meta;         // LDS byte offsets: per-row LUT values / scales,
-  int lds_rp;           //   row pointers (RW + 1),
-  int lds_rank;         //   rank-factor rows (RW x rank_row_bytes),
-  int lds_rsc;          //   int4 rank-factor scales (RW x rsc_row_bytes),
-  int lds_out;          //   outliers, out_cap entries per wavefront
+  int rows_per_wg;      // rows of each workgroup (the last may have fewer)
+  int lds_x;            // dynamic LDS byte offsets: activations,
+  int lds_max;          //   per-wavefront maxima (bf16 rows),
+  int lds_meta;         //   per-row LUT values / scales,
+  int lds_rp;           //   row pointers (rows + 1),
+  int lds_rank;         //   rank-factor rows (rows x rank_row_bytes),
+  int lds_rsc;          //   int4 rank-factor scales (rows x rsc_row_bytes),
+  int lds_part0;        //   per-lane partial sums: one vector per row,
+  int lds_part1;        //   one per wavefront (its first row, when its slice starts inside it),
+  int lds_out;          //   outliers: out_cap 16-bit columns, then out_cap fp16 values,
+  int lds_t;            //   t = x' L_hat (rank floats)
   int rank_row_bytes;   // bytes of one R^T row (16-bit: 2 rank, int4: ceil(rank / 2))
   int rsc_row_bytes;    // bytes of one row of int4 R^T scales
-  int out_cap;          // outlier entries staged per wavefront (<= 64 * kStOutLoads)
-  int row_waves;        // wavefronts of the row workgroups (readers of t in a recorded launch)
+  int out_cap;          // outlier entries staged per workgroup (<= threads * kStOutLoads)
+  int lr_readers;       // readers of t in a recorded launch (one per row workgroup)
 };
 
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  // rows of 16 lanes: quad swaps, then rotations by 4 and 8; then the four rows in a fixed order
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (a + b) + (c + d);
+// Static LDS of the tables, the kernel's one static array (at LDS address 0, so
+// that lookups at offsets built by v_perm need no base added): LUT row tables
+// of up to 128 (LUT3, 256 bytes each) or 64 (LUT4, 1 KiB each) rows, or the
+// 2:4 selector table.
+template <int KIND>
+constexpr int stream_tab_bytes() {
+  return KIND == K_LUT3 ? 128 * 256 : KIND == K_LUT4 ? 64 * 1024 : KIND == K_INT4_24 ? 256 : 16;
 }
 
-// NB = passes per block of the code stream (two blocks in flight), XR =
-// activation slots staged per thread (one round), LR = low-rank part, EDIT =
-// raw activations edited (clamp, per-channel factors) while staged.
-template <int KIND, bool BF16, int NB, int XR, bool LR, bool EDIT>
-__global__ void __launch_bounds__(512) decode_stream_kernel(StreamArgs sa) {
+// Chunks of one wavefront's slice: the workgroup's F chunks over wpg
+// wavefronts, rounded up to whole passes, and at least one row (so that a row
+// spans at most two slices).
+__host__ __device__ inline int stream_slice(int F, int C, int wpg) {
+  const int even = ((F + wpg - 1) / wpg + 63) & ~63, row = (C + 63) & ~63;
+  return even > row ? even : row;
+}
+
+// Prologue blocks of a streaming launch: a workgroup of 16 wavefronts works on
+// a K slice four times as long as the 256-thread block's.
+inline int stream_lr_slices(int lr_S, int threads) { return threads == 1024 ? (lr_S + 3) / 4 : lr_S; }
+
+// XR = activation slots staged per thread, LR = low-rank part, EDIT = raw
+// activations edited (clamp, per-channel factors) while staged.
+template <int KIND, bool BF16, int XR, bool LR, bool EDIT>
+__global__ void __launch_bounds__(1024) decode_stream_kernel(StreamArgs sa) {
   const RowArgs& a = sa.r;
-  constexpr int R = 2;
+  constexpr int NB = KIND == K_INT4_24 ? 2 : kStNB;  // 2:4 chunks dequantise to 32 pairs: fewer blocks in registers
   constexpr int SPAN = KindTraits<KIND>::span, P = KindTraits<KIND>::pairs, XD = SPAN / 8;
   constexpr int XS = RowX<KIND>::stride, XSL = RowX<KIND>::slots;
   constexpr bool LUT = KIND == K_LUT3 || KIND == K_LUT4;
   constexpr uint32_t RTB = (uint32_t)row_table_bytes<KIND>();
-  constexpr uint32_t TB = KIND == K_LUT4 ? 32u : KIND == K_LUT3 ? 16u : 2u;  // metadata bytes per row
-  constexpr int TABW = LUT ? kStMaxWaves * R * (int)RTB / 4 : (KIND == K_INT4_24 ? 64 : 4);
-  __shared__ __attribute__((aligned(16))) uint32_t stab[TABW + kStMaxWaves];  // tables at LDS address 0, then row maxima
+  constexpr int TB = KIND == K_LUT4 ? 32 : KIND == K_LUT3 ? 16 : 2;  // metadata bytes per row
+  __shared__ __attribute__((aligned(16))) uint32_t stab[stream_tab_bytes<KIND>() / 4];  // at LDS address 0
   extern __shared__ __attribute__((aligned(16))) uint32_t sdyn[];
   uint8_t* sb = reinterpret_cast<uint8_t*>(sdyn);
   const int tid = threadIdx.x, nthr = blockDim.x, wpg = nthr >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   if constexpr (LR) {
-    if ((int)blockIdx.x < a.lr_wgs) {  // a prologue workgroup (threads past 256 only keep the barriers)
+    if ((int)blockIdx.x < a.lr_wgs) {  // a prologue workgroup
       const int b = blockIdx.x, S = a.lrp.S, s = b % S, tj = (b / S) % a.lr_ntj, tm = b / (S * a.lr_ntj);
-      if (a.lr_mode == 0) lr_split_block<0, 1, BF16, EDIT>(a.lrp, s, tj, tm, a.lr_ntj, sb);
-      else lr_split_block<1, 1, BF16, EDIT>(a.lrp, s, tj, tm, a.lr_ntj, sb);
+      if (nthr == 1024) {
+        if (a.lr_mode == 0) lr_split_block<0, 1, BF16, EDIT, 1024>(a.lrp, s, tj, tm, a.lr_ntj, sb);
+        else lr_split_block<1, 1, BF16, EDIT, 1024>(a.lrp, s, tj, tm, a.lr_ntj, sb);
+      } else {
+        if (a.lr_mode == 0) lr_split_block<0, 1, BF16, EDIT>(a.lrp, s, tj, tm, a.lr_ntj, sb);
+        else lr_split_block<1, 1, BF16, EDIT>(a.lrp, s, tj, tm, a.lr_ntj, sb);
+      }
       return;
     }
   }
   const int wg = (int)blockIdx.x - (LR ? a.lr_wgs : 0);
-  const int r0 = wg * sa.rows_per_wg;                       // first row of the workgroup
-  const int rw = min(sa.rows_per_wg, a.N - r0);             // its rows (>= 1)
-  const int ngr = (rw + R - 1) / R;                         // its groups
-  const int nq = (ngr + wpg - 1) / wpg;                     // groups per wavefront
-  const int q0 = wave * nq, nqw = max(0, min(q0 + nq, ngr) - q0);  // this wavefront's groups [q0, q0 + nqw)
+  const int r0 = wg * sa.rows_per_wg;            // first row of the workgroup
+  const int rw = min(sa.rows_per_wg, a.N - r0);  // its rows (>= 1)
+  const int C = a.chunks, F = rw * C;            // chunks per row, of the workgroup
+  const int Lw = stream_slice(F, C, wpg);
+  const int f0 = wave * Lw, f1 = min(F, f0 + Lw);  // this wavefront's slice [f0, f1)
+  const int np = f0 < f1 ? (f1 - f0 + 63) >> 6 : 0;
   const bool has_csr = a.rowptr != nullptr;
+  // the workgroup's outliers [E0, E1): scalar loads, waited for with the activations
+  const int E0 = has_csr ? a.rowptr[r0] : 0, E1 = has_csr ? a.rowptr[r0 + rw] : 0;
 
-  // ---- activations: one staging round (XR slots per thread) ----
-  const int SM = sa.npass * 64 * XSL;  // slots of the row
+  // ---- activations and LUT values / scales, staged before the walk and
+  // waited for before anything else is asked for ----
+  const int SM = C * XSL;  // activation slots of the row
   const brsrc_t rx = make_rsrc(a.x, (uint32_t)a.ldx * 2u);
   auto x_src = [&](int s) -> uint32_t {  // byte offset of slot s in x (and in the factors), or kNoLoad
     int k, d = 0;
@@ -116,13 +146,87 @@ __global__ void __launch_bounds__(512) decode_stream_kernel(StreamArgs sa) {
   if constexpr (EDIT) {
     const brsrc_t rf = make_rsrc(a.xscale, a.xscale ? (uint32_t)a.ldx * 2u : 0u);
 #pragma unroll
-    for (int i = 0; i < XR; ++i) xf[i] = a.xscale ? bload128(rf, x_src(i * nthr + tid), 0) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < XR; ++i) xf[i] = bload128(rf, a.xscale ? x_src(i * nthr + tid) : kNoLoad, 0);
+  }
+  uint4 mv[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+  {
+    const brsrc_t rtab = make_rsrc(a.table, (uint32_t)a.Npad * (uint32_t)TB);
+    const uint32_t o = tid < rw ? (uint32_t)(r0 + tid) * (uint32_t)TB : kNoLoad;
+    if constexpr (TB == 2) {
+      mv[0].x = bload16(rtab, o, 0);
+    } else {
+      mv[0] = bload128(rtab, o, 0);
+      if constexpr (TB == 32) mv[1] = bload128(rtab, tid < rw ? o + 16u : kNoLoad, 0);
+    }
   }
 
-  // ---- metadata of the workgroup's rows (one or two vectors per thread) ----
-  const brsrc_t rtab = make_rsrc(a.table, (uint32_t)a.Npad * TB);
-  const uint32_t mbytes = (uint32_t)rw * TB;
-  const uint4 mv = bload128(rtab, (uint32_t)(16 * tid) < mbytes ? (uint32_t)r0 * TB + 16u * (uint32_t)tid : kNoLoad, 0);
+  // ---- LDS before the walk: activations (bf16: as fp16 with the row scale), LUT values / scales ----
+  if constexpr (EDIT) {
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      if (a.clamp) xs[i] = clamp_act8<BF16>(xs[i], a.cval);
+      if (a.xscale) xs[i] = scale_act8<BF16>(xs[i], xf[i]);
+    }
+  }
+  float xunscale = 1.f;
+  bool xfinite = true;
+  if constexpr (BF16) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < XR; ++i) mx = xh_absmax2(mx, xs[i]);
+    mx = wave_max_u32(max(mx & 0xFFFFu, mx >> 16) >> 1);
+    uint32_t* smax = reinterpret_cast<uint32_t*>(sb + sa.lds_max);
+    if (lane == 0) smax[wave] = mx;
+    __syncthreads();
+    uint32_t M16 = 0;
+    for (int w = 0; w < wpg; ++w) M16 = max(M16, smax[w]);
+    xfinite = M16 < 0x7F80u;
+    const uint32_t emax = M16 >> 7, b = emax > 29u ? emax - 29u : 0u;
+    xunscale = __uint_as_float((b + 15u) << 23);
+#pragma unroll
+    for (int i = 0; i < XR; ++i) xs[i] = xh_convert(xs[i], (b << 7) * 0x00010001u);
+  }
+#pragma unroll
+  for (int i = 0; i < XR; ++i) {
+    const int s = i * nthr + tid;
+    if (s < SM) *reinterpret_cast<uint4*>(sb + sa.lds_x + s * 16) = xs[i];
+  }
+  if (tid < rw) {
+    if constexpr (TB == 2) {
+      *reinterpret_cast<uint16_t*>(sb + sa.lds_meta + 2 * tid) = (uint16_t)mv[0].x;
+    } else {
+      *reinterpret_cast<uint4*>(sb + sa.lds_meta + TB * tid) = mv[0];
+      if constexpr (TB == 32) *reinterpret_cast<uint4*>(sb + sa.lds_meta + TB * tid + 16) = mv[1];
+    }
+  }
+  if constexpr (KIND == K_INT4_24) {
+    if (tid < 16) {
+      const uint2 e = seltab_2_4_entry((uint32_t)tid);
+      stab[2 * tid] = e.x;
+      stab[2 * tid + 1] = e.y;
+    }
+  }
+  __syncthreads();
+  // LUT row tables from the staged values (LUT3: 64 pair entries; LUT4: 256)
+  if constexpr (KIND == K_LUT3) {
+    for (int i = tid; i < rw * 64; i += nthr) {
+      const int q = i >> 6, e = i & 63;
+      const uint16_t* lt = reinterpret_cast<const uint16_t*>(sb + sa.lds_meta + 16 * q);
+      stab[i] = (uint32_t)lt[e & 7] | ((uint32_t)lt[e >> 3] << 16);
+    }
+  } else if constexpr (KIND == K_LUT4) {
+    for (int i = tid; i < rw * 256; i += nthr) {
+      const int q = i >> 8, e = i & 255;
+      const uint16_t* lt = reinterpret_cast<const uint16_t*>(sb + sa.lds_meta + 32 * q);
+      stab[i] = (uint32_t)lt[e & 15] | ((uint32_t)lt[e >> 4] << 16);
+    }
+  }
+  if constexpr (LUT) __syncthreads();
+
+  // ---- the loads of the walk, issued once the activations are staged (a
+  // CU holds a bounded number of requests in flight: issued earlier, behind
+  // the whole launch's code stream, they would hold up the staging) ----
+  asm volatile("" ::: "memory");
   const brsrc_t rrp = make_rsrc(a.rowptr, has_csr ? (uint32_t)(a.N + 1) * 4u : 0u);
   const uint32_t rpv = bload32(rrp, tid <= rw ? (uint32_t)(r0 + tid) * 4u : kNoLoad, 0);
   uint4 kv[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
@@ -141,70 +245,139 @@ __global__ void __launch_bounds__(512) decode_stream_kernel(StreamArgs sa) {
     ksv = bload128(rRs, lr4 && (uint32_t)(16 * tid) < sbytes ? (uint32_t)r0 * (uint32_t)sa.rsc_row_bytes + 16u * (uint32_t)tid
                                                               : kNoLoad, 0);
   }
-
-  // ---- the code stream: blocks of NB passes of this wavefront's groups, two in flight ----
-  const int nblk = (sa.npass + NB - 1) / NB, TBK = nqw * nblk;
-  const brsrc_t rd = make_rsrc(a.dense, (uint32_t)a.Npad * (uint32_t)a.chunks * 16u);
-  const brsrc_t rm = make_rsrc(a.meta, KIND == K_INT4_24 ? (uint32_t)a.Npad * (uint32_t)a.chunks * 8u : 0u);
-  int lq = 0, lbb = 0;  // group and block of the next load
-  auto load_blk = [&](uint4 (&w)[NB][R], uint2 (&mw)[NB][R], int j) {
-    const int n0 = r0 + R * (q0 + lq);
+  const int nblk = (np + NB - 1) / NB;
+  const brsrc_t rd = make_rsrc(a.dense, (uint32_t)a.Npad * (uint32_t)C * 16u);
+  const brsrc_t rm = make_rsrc(a.meta, KIND == K_INT4_24 ? (uint32_t)a.Npad * (uint32_t)C * 8u : 0u);
+  const uint32_t gchunk = (uint32_t)r0 * (uint32_t)C + (uint32_t)f0 + (uint32_t)lane;  // this lane's first chunk
+  auto load_blk = [&](uint4 (&w)[NB], uint2 (&mw)[NB], int j) {
+    // a block past the slice loads nothing; passes past the slice inside the
+    // last block read chunks of the next slice (or zero past the buffer) and are masked
+    const uint32_t c0 = gchunk + (uint32_t)(j * NB * 64);
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-      const int c = (lbb * NB + q) * 64 + lane;
-      const bool okc = j < TBK && c < a.chunks;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint32_t idx = (uint32_t)(n0 + r) * (uint32_t)a.chunks + (uint32_t)c;
-        w[q][r] = bload128(rd, okc ? idx * 16u : kNoLoad, 0);
-        if constexpr (KIND == K_INT4_24)
-          mw[q][r] = bload64(rm, okc ? idx * 8u : kNoLoad, 0);
-        else
-          mw[q][r] = make_uint2(0, 0);
-      }
-    }
-    if (++lbb == nblk) {
-      lbb = 0;
-      ++lq;
+      w[q] = bload128_nt(rd, j < nblk ? (c0 + 64u * q) * 16u : kNoLoad, 0);
+      if constexpr (KIND == K_INT4_24)
+        mw[q] = bload64_nt(rm, j < nblk ? (c0 + 64u * q) * 8u : kNoLoad, 0);
+      else
+        mw[q] = make_uint2(0, 0);
     }
   };
-  uint4 WA[NB][R], WB[NB][R];
-  uint2 MA[NB][R], MB_[NB][R];
-  load_blk(WA, MA, 0);
-  load_blk(WB, MB_, 1);
-
-  // ---- LDS: activations (bf16: as fp16 with the row scale), metadata, selector table ----
-  if constexpr (EDIT) {
+  constexpr int NBUF = kStNBUF;
+  uint4 W[NBUF][NB];
+  uint2 MW[NBUF][NB];
 #pragma unroll
-    for (int i = 0; i < XR; ++i) {
-      if (a.clamp) xs[i] = clamp_act8<BF16>(xs[i], a.cval);
-      if (a.xscale) xs[i] = scale_act8<BF16>(xs[i], xf[i]);
+  for (int b = 0; b < NBUF; ++b) load_blk(W[b], MW[b], b);
+  // the workgroup's outliers (entries past out_cap are read from memory in
+  // the finalisation).  Every load of the kernel is issued on every path (an
+  // unused one reads nothing): the compiler's count of loads in flight then
+  // stays exact, and no wait asks for more than the data it needs.
+  uint32_t oc[kStOutLoads], ov[kStOutLoads];
+  {
+    const brsrc_t rcol = make_rsrc(a.col, has_csr ? (uint32_t)a.nnz * 4u : 0u);
+    const brsrc_t rval = make_rsrc(a.val, has_csr ? (uint32_t)a.nnz * 2u : 0u);
+#pragma unroll
+    for (int i = 0; i < kStOutLoads; ++i) {
+      const int j = tid + nthr * i, e = E0 + j;
+      const bool ok = has_csr && e < E1 && j < sa.out_cap;
+      oc[i] = bload32(rcol, ok ? (uint32_t)e * 4u : kNoLoad, 0);
+      ov[i] = bload16(rval, ok ? (uint32_t)e * 2u : kNoLoad, 0);
     }
   }
-  float xunscale = 1.f;
-  bool xfinite = true;
-  if constexpr (BF16) {
-    uint32_t mx = 0;
+
+  // ---- the walk: one chunk per lane per pass ----
+  // The next row boundary B (a flat chunk index of the workgroup) and the row
+  // n that ends there are wave-uniform; a lane's chunk f = f0 + 64 p + lane is
+  // chunk f - (B - C) of row n when f < B, chunk f - B of row n + 1 otherwise.
+  int n = f0 / C, B = (n + 1) * C;
+  const int lxs = lane * XS;
+  float acc = 0.f;
+  auto deposit = [&](int row, float v) {  // this slice's partial sums of `row`
+    const int off = row * C >= f0 ? sa.lds_part0 + row * 256 : sa.lds_part1 + wave * 256;
+    *reinterpret_cast<float*>(sb + off + 4 * lane) = v;
+  };
+  auto pass = [&](const uint4& w, const uint2& mw, int p) {
+    const int Pp = f0 + 64 * p;
+    const int sB = B - Pp, sE = f1 - Pp;  // first lane of row n + 1 / past the slice
+    const bool slow = sB < 64 || sE < 64;  // wave-uniform
+    int xo = lxs + (Pp + C - B) * XS + sa.lds_x;
+    uint32_t rb = (uint32_t)n * RTB;
+    const bool nl = lane >= sB && lane < sE;  // in row n + 1
+    if (slow) {
+      if (nl) {
+        xo -= C * XS;
+        rb += RTB;
+      }
+      if (lane >= sE) xo = sa.lds_x;  // past the slice: any staged activation (the sum is masked)
+    }
+    uint32_t xv[P];
 #pragma unroll
-    for (int i = 0; i < XR; ++i) mx = xh_absmax2(mx, xs[i]);
-    mx = wave_max_u32(max(mx & 0xFFFFu, mx >> 16) >> 1);
-    if (lane == 0) stab[TABW + wave] = mx;
-    __syncthreads();
-    uint32_t M16 = 0;
-    for (int w = 0; w < wpg; ++w) M16 = max(M16, stab[TABW + w]);
-    xfinite = M16 < 0x7F80u;
-    const uint32_t emax = M16 >> 7, b = emax > 29u ? emax - 29u : 0u;
-    xunscale = __uint_as_float((b + 15u) << 23);
+    for (int d = 0; d < XD; ++d) {
+      const uint4 v = lds_u128(sdyn, (uint32_t)(xo + 16 * d));
+      xv[4 * d] = v.x;
+      xv[4 * d + 1] = v.y;
+      xv[4 * d + 2] = v.z;
+      xv[4 * d + 3] = v.w;
+    }
+    uint32_t wp[P];
+    chunk_pairs<KIND, true>(stab, w, make_uint4(mw.x, mw.y, 0, 0), rb, 0u, wp);
+    float t = slow ? 0.f : acc;
 #pragma unroll
-    for (int i = 0; i < XR; ++i) xs[i] = xh_convert(xs[i], (b << 7) * 0x00010001u);
+    for (int jj = 0; jj < P; ++jj) t = mac2r<false>(wp[jj], xv[jj], t);
+    if (!slow) {
+      acc = t;
+    } else {
+      if (lane >= sE) t = 0.f;
+      if (sB < sE) {  // row n ends inside this pass
+        deposit(n, nl ? acc : acc + t);
+        acc = nl ? t : 0.f;
+        ++n;
+        B += C;
+      } else {
+        acc += t;
+      }
+    }
+  };
+  // A block with no row boundary and no slice end in it (the usual case) runs
+  // as one straight stretch of code, so that the compiler can overlap one
+  // pass's table lookups with the previous pass's multiply-adds.
+  auto fast_pass = [&](const uint4& w, const uint2& mw, int p) {
+    const int Pp = f0 + 64 * p;
+    const uint32_t xo = (uint32_t)(lxs + (Pp + C - B) * XS + sa.lds_x);
+    uint32_t xv[P];
+#pragma unroll
+    for (int d = 0; d < XD; ++d) {
+      const uint4 v = lds_u128(sdyn, xo + 16u * d);
+      xv[4 * d] = v.x;
+      xv[4 * d + 1] = v.y;
+      xv[4 * d + 2] = v.z;
+      xv[4 * d + 3] = v.w;
+    }
+    uint32_t wp[P];
+    chunk_pairs<KIND, true>(stab, w, make_uint4(mw.x, mw.y, 0, 0), (uint32_t)n * RTB, 0u, wp);
+#pragma unroll
+    for (int jj = 0; jj < P; ++jj) acc = mac2r<false>(wp[jj], xv[jj], acc);
+  };
+  auto comp_blk = [&](const uint4 (&w)[NB], const uint2 (&mw)[NB], int j) {
+    const int P0 = f0 + 64 * NB * j;  // the block's first chunk
+    if (B - P0 >= 64 * NB && f1 - P0 >= 64 * NB) {
+#pragma unroll
+      for (int q = 0; q < NB; ++q) fast_pass(w[q], mw[q], j * NB + q);
+    } else {
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+        if (j * NB + q < np) pass(w[q], mw[q], j * NB + q);
+    }
+  };
+  // first round of blocks; then the data the finalisation needs goes to LDS
+  // (loaded before the code stream, so it has arrived with the first blocks)
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b) {
+    comp_blk(W[b], MW[b], b);
+    load_blk(W[b], MW[b], b + NBUF);
   }
-#pragma unroll
-  for (int i = 0; i < XR; ++i) {
-    const int s = i * nthr + tid;
-    if (s < SM) *reinterpret_cast<uint4*>(sb + s * 16) = xs[i];
-  }
-  if ((uint32_t)(16 * tid) < mbytes) *reinterpret_cast<uint4*>(sb + sa.lds_meta + 16 * tid) = mv;
-  if (tid <= rw) *reinterpret_cast<uint32_t*>(sb + sa.lds_rp + 4 * tid) = has_csr ? rpv : 0u;
+  // (the staged values are stored as loaded: an operation on them here would
+  // let the compiler move it, and its wait, up to the loads, behind the code stream)
+  if (tid <= rw) *reinterpret_cast<uint32_t*>(sb + sa.lds_rp + 4 * tid) = rpv;
   if constexpr (LR) {
     const uint32_t kb = (uint32_t)rw * (uint32_t)sa.rank_row_bytes;
 #pragma unroll
@@ -215,228 +388,145 @@ __global__ void __launch_bounds__(512) decode_stream_kernel(StreamArgs sa) {
     if (lr4 && (uint32_t)(16 * tid) < (uint32_t)rw * (uint32_t)sa.rsc_row_bytes)
       *reinterpret_cast<uint4*>(sb + sa.lds_rsc + 16 * tid) = ksv;
   }
-  if constexpr (KIND == K_INT4_24) {
-    if (tid < 16) {
-      const uint2 e = seltab_2_4_entry((uint32_t)tid);
-      stab[2 * tid] = e.x;
-      stab[2 * tid + 1] = e.y;
-    }
-  }
-  __syncthreads();
-
-  // ---- this wavefront's outliers, packed into its LDS region ----
-  const int rwa = R * q0, rwb = min(rw, R * (q0 + nqw));  // its rows, relative to r0
-  int E0w = 0;
-  if (has_csr && nqw > 0) {
-    E0w = (int)*reinterpret_cast<const uint32_t*>(sb + sa.lds_rp + 4 * rwa);
-    const int E1w = (int)*reinterpret_cast<const uint32_t*>(sb + sa.lds_rp + 4 * rwb);
-    const brsrc_t rcol = make_rsrc(a.col, (uint32_t)a.nnz * 4u), rval = make_rsrc(a.val, (uint32_t)a.nnz * 2u);
-    uint32_t oc[kStOutLoads], ov[kStOutLoads];
+  if (has_csr) {
+    uint16_t* ocol = reinterpret_cast<uint16_t*>(sb + sa.lds_out);
+    uint16_t* oval = ocol + sa.out_cap;
 #pragma unroll
     for (int i = 0; i < kStOutLoads; ++i) {
-      const int e = E0w + lane + 64 * i;
-      const bool ok = e < E1w && lane + 64 * i < sa.out_cap;
-      oc[i] = bload32(rcol, ok ? (uint32_t)e * 4u : kNoLoad, 0);
-      ov[i] = bload16(rval, ok ? (uint32_t)e * 2u : kNoLoad, 0);
-    }
-    uint32_t* ob = reinterpret_cast<uint32_t*>(sb + sa.lds_out) + wave * sa.out_cap;
-#pragma unroll
-    for (int i = 0; i < kStOutLoads; ++i)
-      if (lane + 64 * i < sa.out_cap) ob[lane + 64 * i] = (oc[i] & 0xFFFFu) | (ov[i] << 16);
-  }
-
-  // ---- per group: tables, multiply, outliers, rank term, reduction ----
-  const uint32_t tabbase = (uint32_t)wave * R * RTB;
-  auto setup = [&](int q) {  // tables of group q (rows r0 + R (q0 + q) ...)
-    if constexpr (LUT) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int rl = R * (q0 + q) + r;  // row relative to r0 (rows past rw read their zero metadata)
-        if constexpr (KIND == K_LUT3) {
-          const uint4 lv = *reinterpret_cast<const uint4*>(sb + sa.lds_meta + 16 * rl);
-          const uint32_t lw[4] = {lv.x, lv.y, lv.z, lv.w};
-          const int ca = lane & 7, cb = lane >> 3;
-          const uint32_t va = (lw[ca >> 1] >> (16 * (ca & 1))) & 0xFFFFu;
-          const uint32_t vb = (lw[cb >> 1] >> (16 * (cb & 1))) & 0xFFFFu;
-          stab[(tabbase >> 2) + r * 64 + lane] = va | (vb << 16);
-        } else {
-          const uint32_t* lw = reinterpret_cast<const uint32_t*>(sb + sa.lds_meta + 32 * rl);
-          const uint2 lo = *reinterpret_cast<const uint2*>(lw + 2 * (lane & 3));
-          const uint32_t hi = ((lw[(lane >> 2) >> 1] >> (16 * ((lane >> 2) & 1))) & 0xFFFFu) << 16;
-          *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(stab) + tabbase + r * RTB + 16 * lane) =
-              make_uint4((lo.x & 0xFFFFu) | hi, (lo.x >> 16) | hi, (lo.y & 0xFFFFu) | hi, (lo.y >> 16) | hi);
-        }
+      const int j = tid + nthr * i;
+      if (j < sa.out_cap) {
+        ocol[j] = (uint16_t)oc[i];
+        oval[j] = (uint16_t)ov[i];
       }
     }
-  };
-  // t = x' L_hat: waited for and read once per wavefront, at its first group's end
-  float tv[4] = {0.f, 0.f, 0.f, 0.f};
-  bool t_read = false;
-  const uint32_t target = (LR && a.lr_flag != nullptr) ? lr_target(a.lr_flag, a.lr_epoch) : 0u;
-  auto read_t = [&]() {
-    if constexpr (LR) {
+  }
+  for (int j0 = NBUF; j0 < nblk; j0 += NBUF) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      comp_blk(W[b], MW[b], j0 + b);
+      load_blk(W[b], MW[b], j0 + b + NBUF);
+    }
+  }
+  if (np > 0) deposit(n, acc);  // the slice's last row
+
+  // ---- t = x' L_hat: the first wavefront waits for it and copies it to LDS ----
+  float* st = reinterpret_cast<float*>(sb + sa.lds_t);
+  if constexpr (LR) {
+    if (wave == 0) {
+      const uint32_t target = a.lr_flag != nullptr ? lr_target(a.lr_flag, a.lr_epoch) : 0u;
       const bool t_ok =
           a.lr_flag == nullptr || wait_lowrank(lr_word(a.lr_flag, a.lr_epoch), target, lane, a.lr_max_polls, a.lr_err);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = lane + 64 * i;
-        tv[i] = j < a.rank ? (t_ok ? load_dev(a.t + j) : __builtin_nanf("")) : 0.f;
+        if (j < a.rank) st[j] = t_ok ? load_dev(a.t + j) : __builtin_nanf("");
       }
-      if (a.lr_flag != nullptr && a.lr_epoch == 0) {  // recorded launch: this wavefront's reads of t are done
+      if (a.lr_flag != nullptr && a.lr_epoch == 0) {  // recorded launch: this workgroup's reads of t are done
         __builtin_amdgcn_s_waitcnt(0);
-        if (lane == 0) lr_reader_done(a.lr_flag, target, sa.row_waves, wg * wpg + wave);
+        if (lane == 0) lr_reader_done(a.lr_flag, target, sa.lr_readers, wg);
       }
-      t_read = true;
     }
-  };
+  }
+  __syncthreads();
+
+  // ---- per row (eight threads each): partial sums, outliers, rank term ----
   auto x_lds = [&](int k) -> float {
     const int c = k / SPAN, o = k - c * SPAN;
-    return act_f32<false>(lds_u16(sdyn, (uint32_t)(c * XS + 2 * o)));  // fp16 (bf16 rows were converted)
+    return act_f32<false>(lds_u16(sdyn, (uint32_t)(sa.lds_x + c * XS + 2 * o)));  // fp16 (bf16 rows were converted)
   };
-  const uint32_t* ob = reinterpret_cast<const uint32_t*>(sb + sa.lds_out) + wave * sa.out_cap;
-  auto finalize = [&](int q, const float (&acc)[R]) {
-    if constexpr (LR) {
-      if (!t_read) read_t();
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int rl = R * (q0 + q) + r, n = r0 + rl;
-      float v = acc[r];
-      if constexpr (!LUT) v *= (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb + sa.lds_meta + 2 * rl));
-      if (has_csr && rl < rw) {
-        const int e0 = (int)*reinterpret_cast<const uint32_t*>(sb + sa.lds_rp + 4 * rl);
-        const int e1 = (int)*reinterpret_cast<const uint32_t*>(sb + sa.lds_rp + 4 * rl + 4);
-        for (int e = e0 + lane; e < e1; e += 64) {
-          const int ix = e - E0w;
-          uint32_t en;
-          if (ix < sa.out_cap) en = ob[ix];
-          else en = ((uint32_t)a.col[e] & 0xFFFFu) | ((uint32_t)a.val[e] << 16);  // past the staged entries
-          v = __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(en >> 16)), x_lds((int)(en & 0xFFFFu)), v);
+  const uint16_t* ocol = reinterpret_cast<const uint16_t*>(sb + sa.lds_out);
+  const uint16_t* oval = ocol + sa.out_cap;
+  const int u = tid & 7;
+  for (int rb0 = 0; rb0 < rw; rb0 += nthr >> 3) {
+    const int rl = rb0 + (tid >> 3);
+    float v = 0.f;
+    if (rl < rw) {
+      const float4 pa = *reinterpret_cast<const float4*>(sb + sa.lds_part0 + rl * 256 + 32 * u);
+      const float4 pb = *reinterpret_cast<const float4*>(sb + sa.lds_part0 + rl * 256 + 32 * u + 16);
+      v = ((pa.x + pa.y) + (pa.z + pa.w)) + ((pb.x + pb.y) + (pb.z + pb.w));
+      const int w1 = rl * C / Lw + 1;  // the slice that may start inside the row
+      if (w1 * Lw < (rl + 1) * C) {
+        const float4 qa = *reinterpret_cast<const float4*>(sb + sa.lds_part1 + w1 * 256 + 32 * u);
+        const float4 qb = *reinterpret_cast<const float4*>(sb + sa.lds_part1 + w1 * 256 + 32 * u + 16);
+        v += ((qa.x + qa.y) + (qa.z + qa.w)) + ((qb.x + qb.y) + (qb.z + qb.w));
+      }
+      if constexpr (!LUT)
+        v *= (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(sb + sa.lds_meta + 2 * rl));
+      if (has_csr) {
+        const int e0 = (int)*reinterpret_cast<const uint32_t*>(sb + sa.lds_rp + 4 * rl) - E0;
+        const int e1 = (int)*reinterpret_cast<const uint32_t*>(sb + sa.lds_rp + 4 * rl + 4) - E0;
+        for (int e = e0 + u; e < e1; e += 8) {
+          uint32_t c, vb;
+          if (e < sa.out_cap) {
+            c = ocol[e];
+            vb = oval[e];
+          } else {  // past the staged entries
+            c = (uint32_t)a.col[E0 + e];
+            vb = a.val[E0 + e];
+          }
+          v = __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)vb), x_lds((int)c), v);
         }
       }
       if constexpr (BF16) v = xfinite ? v * xunscale : __builtin_nanf("");
       if constexpr (LR) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {  // branch-free: rank indices past the rank read index 0 and add 0
-          const int j0 = lane + 64 * i;
-          const bool okj = j0 < a.rank;
-          const int j = okj ? j0 : 0;
+        const uint8_t* rrow = sb + sa.lds_rank + rl * sa.rank_row_bytes;
+        for (int j = u; j < a.rank; j += 8) {
           float rvv;
           if (lr4) {
-            const uint32_t byte = sb[sa.lds_rank + rl * sa.rank_row_bytes + (j >> 1)];
+            const uint32_t byte = rrow[j >> 1];
             const uint32_t jg = ((uint32_t)j * a.group_mul) >> 16;
             const uint16_t sc = *reinterpret_cast<const uint16_t*>(sb + sa.lds_rsc + rl * sa.rsc_row_bytes + 2 * jg);
             rvv = (float)((int)((byte >> (4 * (j & 1))) & 0xFu) - 8) * (float)__builtin_bit_cast(_Float16, sc);
           } else {
-            const uint32_t u = *reinterpret_cast<const uint16_t*>(sb + sa.lds_rank + rl * sa.rank_row_bytes + 2 * j);
-            rvv = a.lr_kind == CL_LR_BF16 ? __uint_as_float(u << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)u);
+            const uint32_t uu = *reinterpret_cast<const uint16_t*>(rrow + 2 * j);
+            rvv = a.lr_kind == CL_LR_BF16 ? __uint_as_float(uu << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)uu);
           }
-          v = __builtin_fmaf(okj ? tv[i] : 0.f, okj ? rvv : 0.f, v);
-        }
-      }
-      v = wave_sum_dpp(v);
-      if (lane == 0 && rl < rw) a.y[n] = v;
-    }
-  };
-
-  float acc[R] = {0.f, 0.f};
-  int cq = 0, cbb = 0;  // group and block being multiplied
-  auto comp_blk = [&](const uint4 (&w)[NB][R], const uint2 (&mw)[NB][R], int j) {
-    if (j >= TBK) return;
-    if (cbb == 0) {
-      if (j > 0) {
-        finalize(cq - 1, acc);
-        acc[0] = acc[1] = 0.f;
-      }
-      setup(cq);
-    }
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int p = cbb * NB + q;
-      if (p < sa.npass) {
-        const int c = p * 64 + lane;
-        uint32_t xv[P];
-#pragma unroll
-        for (int d = 0; d < XD; ++d) {
-          const uint4 v = lds_u128(sdyn, (uint32_t)(c * XS + 16 * d));
-          xv[4 * d] = v.x;
-          xv[4 * d + 1] = v.y;
-          xv[4 * d + 2] = v.z;
-          xv[4 * d + 3] = v.w;
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          uint32_t wp[P];
-          chunk_pairs<KIND, true>(stab, w[q][r], make_uint4(mw[q][r].x, mw[q][r].y, 0, 0), tabbase + (uint32_t)r * RTB,
-                                  0u, wp);
-#pragma unroll
-          for (int jj = 0; jj < P; ++jj) acc[r] = mac2r<false>(wp[jj], xv[jj], acc[r]);
+          v = __builtin_fmaf(st[j], rvv, v);
         }
       }
     }
-    if (++cbb == nblk) {
-      cbb = 0;
-      ++cq;
-    }
-  };
-  comp_blk(WA, MA, 0);
-  load_blk(WA, MA, 2);
-  comp_blk(WB, MB_, 1);
-  load_blk(WB, MB_, 3);
-  for (int j = 2; j < TBK; j += 2) {
-    comp_blk(WA, MA, j);
-    load_blk(WA, MA, j + 2);
-    comp_blk(WB, MB_, j + 1);
-    load_blk(WB, MB_, j + 3);
-  }
-  if (nqw > 0) finalize(nqw - 1, acc);
-  if constexpr (LR) {
-    // a recorded launch counts every row wavefront as a reader of t, this one too if it had no group
-    if (!t_read && a.lr_flag != nullptr && a.lr_epoch == 0 && lane == 0)
-      lr_reader_done(a.lr_flag, target, sa.row_waves, wg * wpg + wave);
+    // the eight threads of the row: quad swaps, then the mirrored quad of each half row
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    if (u == 0 && rl < rw) a.y[r0 + rl] = v;
   }
 }
 
-template <int KIND, bool BF16, int NB, int XR, bool LR>
+template <int KIND, bool BF16, int XR, bool LR>
 static void launch_stream_e(const StreamArgs& s, int grid, int threads, int lds, hipStream_t st) {
   if (s.r.clamp || s.r.xscale)
-    hipLaunchKernelGGL((decode_stream_kernel<KIND, BF16, NB, XR, LR, true>), dim3(grid), dim3(threads), lds, st, s);
+    hipLaunchKernelGGL((decode_stream_kernel<KIND, BF16, XR, LR, true>), dim3(grid), dim3(threads), lds, st, s);
   else
-    hipLaunchKernelGGL((decode_stream_kernel<KIND, BF16, NB, XR, LR, false>), dim3(grid), dim3(threads), lds, st, s);
+    hipLaunchKernelGGL((decode_stream_kernel<KIND, BF16, XR, LR, false>), dim3(grid), dim3(threads), lds, st, s);
 }
 
-template <int KIND, bool BF16, int NB, int XR>
+template <int KIND, bool BF16, int XR>
 static void launch_stream_l(const StreamArgs& s, int grid, int threads, int lds, hipStream_t st) {
-  if (s.r.lr_kind != CL_LR_NONE) launch_stream_e<KIND, BF16, NB, XR, true>(s, grid, threads, lds, st);
-  else launch_stream_e<KIND, BF16, NB, XR, false>(s, grid, threads, lds, st);
+  if (s.r.lr_kind != CL_LR_NONE) launch_stream_e<KIND, BF16, XR, true>(s, grid, threads, lds, st);
+  else launch_stream_e<KIND, BF16, XR, false>(s, grid, threads, lds, st);
 }
 
-// Slots per thread the staging needs, and the instantiated round sizes.
+// Staging slots per thread of one activation row (the host rejects plans above 12).
+template <int KIND>
+inline int stream_slots_per_thread(int chunks, int threads) {
+  return (chunks * RowX<KIND>::slots + threads - 1) / threads;
+}
+
 template <int KIND, bool BF16>
 static hipError_t launch_stream_t(const StreamArgs& s, int grid, int threads, int lds, hipStream_t st) {
-  const int slots = s.npass * 64 * RowX<KIND>::slots, per = (slots + threads - 1) / threads;
-  if (s.npass <= 2) {
-    if (per <= 4) launch_stream_l<KIND, BF16, 1, 4>(s, grid, threads, lds, st);
-    else if (per <= 8) launch_stream_l<KIND, BF16, 1, 8>(s, grid, threads, lds, st);
-    else return hipErrorInvalidConfiguration;
-  } else {
-    if (per <= 4) launch_stream_l<KIND, BF16, 2, 4>(s, grid, threads, lds, st);
-    else if (per <= 8) launch_stream_l<KIND, BF16, 2, 8>(s, grid, threads, lds, st);
-    else if (per <= 12) launch_stream_l<KIND, BF16, 2, 12>(s, grid, threads, lds, st);
-    else return hipErrorInvalidConfiguration;
-  }
+  const int per = stream_slots_per_thread<KIND>(s.r.chunks, threads);
+  if (per <= 2) launch_stream_l<KIND, BF16, 2>(s, grid, threads, lds, st);
+  else if (per <= 4) launch_stream_l<KIND, BF16, 4>(s, grid, threads, lds, st);
+  else if (per <= 8) launch_stream_l<KIND, BF16, 8>(s, grid, threads, lds, st);
+  else if (per <= 12) launch_stream_l<KIND, BF16, 12>(s, grid, threads, lds, st);
+  else return hipErrorInvalidConfiguration;
   return hipGetLastError();
 }
 
 template <int KIND>
 hipError_t launch_stream_kind(const StreamArgs& s, int grid, int threads, int lds, bool bf16, hipStream_t st) {
   return bf16 ? launch_stream_t<KIND, true>(s, grid, threads, lds, st) : launch_stream_t<KIND, false>(s, grid, threads, lds, st);
-}
-
-// Staging slots per thread at `threads` threads (the host rejects plans above 12).
-template <int KIND>
-inline int stream_slots_per_thread(int npass, int threads) {
-  return (npass * 64 * RowX<KIND>::slots + threads - 1) / threads;
 }
 
 }  // namespace cl

@@ -174,44 +174,50 @@ __device__ __forceinline__ float dot2_act(uint32_t a, uint32_t b, float c) {
   }
 }
 
-template <int MODE, int MT>
+// NT = threads of a prologue block: its K slice is kLrSlice * NT / 256 rows.
+template <int MODE, int MT, int NT = 256>
 struct LrScratch {
-  static constexpr int NG = MODE == 0 ? 4 : 16;   // reduction groups left after the shuffles
-  static constexpr int NSC = kLrSlice / 16 + 1;   // int4 scale rows a slice can touch (group >= 16)
-  static constexpr int xs = 0;                                   // uint16 [MT][kLrSlice]
-  static constexpr int sc = xs + MT * kLrSlice * 2;              // float [NSC][64] (int4)
+  static constexpr int SL = kLrSlice * NT / 256;  // K rows of the slice
+  static constexpr int NG = MODE == 0 ? NT / 64 : NT / 16;  // reduction groups left after the shuffles
+  static constexpr int NSC = SL / 16 + 1;         // int4 scale rows a slice can touch (group >= 16)
+  static constexpr int xs = 0;                                   // uint16 [MT][SL]
+  static constexpr int sc = xs + MT * SL * 2;                    // float [NSC][64] (int4)
   static constexpr int red = sc + (MODE == 1 ? NSC * 64 * 4 : 16);  // float [NG][MT * 64]
   static constexpr int last = red + NG * MT * 64 * 4;            // int
   static constexpr int bytes = last + 16;
 };
 
 // LDS the block code needs (host side: sizes the decode kernel's dynamic LDS).
-inline int lr_scratch_bytes(int mode, int mt) {
+inline int lr_scratch_bytes(int mode, int mt, int nt = 256) {
+  if (nt == 1024) return mode == 0 ? LrScratch<0, 1, 1024>::bytes : LrScratch<1, 1, 1024>::bytes;
   return mode == 0 ? (mt == 1 ? LrScratch<0, 1>::bytes : mt == 2 ? LrScratch<0, 2>::bytes : LrScratch<0, 4>::bytes)
                    : (mt == 1 ? LrScratch<1, 1>::bytes : mt == 2 ? LrScratch<1, 2>::bytes : LrScratch<1, 4>::bytes);
 }
 
-// One workgroup (256 threads, or more: the threads past 256 compute nothing
-// that is kept) of the split prologue: K slice s, column tile tj of ntj,
-// activation tile tm; `smem` is LrScratch<MODE, MT>::bytes of LDS.
-// EDIT: the activations may be raw (a.clamp, a.xscale apply); else they are
-// edited already.
-template <int MODE, int MT, bool BF16, bool EDIT>
+// One workgroup of the split prologue (NT working threads; a wider
+// workgroup's threads past NT compute nothing that is kept): K slice s of
+// LrScratch<MODE, MT, NT>::SL rows, column tile tj of ntj, activation tile tm;
+// `smem` is LrScratch<MODE, MT, NT>::bytes of LDS.  EDIT: the activations may
+// be raw (a.clamp, a.xscale apply); else they are edited already.
+template <int MODE, int MT, bool BF16, bool EDIT, int NT = 256>
 __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int tj, int tm, int ntj, uint8_t* smem) {
-  using SC = LrScratch<MODE, MT>;
+  using SC = LrScratch<MODE, MT, NT>;
+  constexpr int SL = SC::SL;
   constexpr int NL = MODE == 0 ? 16 : 4;        // 16-byte loads per thread
   constexpr int JL = MODE == 0 ? 4 : 16;        // columns per thread
   constexpr int LG = 64 / JL;                   // threads per K pair row of the tile
-  constexpr int PR = 256 / LG;                  // K pair rows in flight per workgroup
+  constexpr int PR = NT / LG;                   // K pair rows in flight per workgroup
   constexpr int NG = SC::NG;
-  typedef uint16_t xrow_t[kLrSlice];
+  constexpr int XT = SL / 8;                    // threads staging one activation row of the slice
+  static_assert(2 * PR * NL == SL, "the loads cover the slice");
+  typedef uint16_t xrow_t[SL];
   typedef float redrow_t[MT * 64];
   xrow_t* xs = reinterpret_cast<xrow_t*>(smem + SC::xs);
   float* sc = reinterpret_cast<float*>(smem + SC::sc);
   redrow_t* red = reinterpret_cast<redrow_t*>(smem + SC::red);
   int& s_last = *reinterpret_cast<int*>(smem + SC::last);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int k0 = s * kLrSlice, j0 = tj * 64, m0 = tm * MT;
+  const int k0 = s * SL, j0 = tj * 64, m0 = tm * MT;
   const int jg = tid % LG, pr = tid / LG;
   // the value this launch publishes, read before any work: the generation
   // cannot move while the launch's readers wait for it, and a publish that
@@ -221,29 +227,30 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
   // activations of the slice (zero past K and past M)
   const brsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * (uint32_t)a.ldx * 2u);
   uint4 xv = make_uint4(0, 0, 0, 0);
-  if (tid < MT * 64) {
-    const int m = tid >> 6, k = k0 + 8 * (tid & 63);
+  if (tid < MT * XT) {
+    const int m = tid / XT, k = k0 + 8 * (tid % XT);
     const bool ok = m0 + m < a.M && k < a.ldx;
     xv = bload128(rx, ok ? ((uint32_t)(m0 + m) * (uint32_t)a.ldx + (uint32_t)k) * 2u : kNoLoad, 0);
   }
   uint4 xf = make_uint4(0, 0, 0, 0);
-  if (EDIT && a.xscale && tid < MT * 64) {
-    const int k = k0 + 8 * (tid & 63);
+  if (EDIT && a.xscale && tid < MT * XT) {
+    const int k = k0 + 8 * (tid % XT);
     xf = bload128(make_rsrc(a.xscale, (uint32_t)a.ldx * 2u), k < a.ldx ? (uint32_t)k * 2u : kNoLoad, 0);
   }
   // the slice of L
   const brsrc_t rl = make_rsrc(a.lk, MODE == 0 ? (uint32_t)a.Kl * (uint32_t)a.rpad * 2u : (uint32_t)a.Kl / 2u * (uint32_t)a.rpad);
   uint4 w[NL];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
+  for (int i = 0; i < NL; ++i) {  // a wider workgroup's threads past NT load nothing
     const uint32_t p = (uint32_t)(k0 / 2 + pr + PR * i);
-    w[i] = bload128(rl, MODE == 0 ? (p * (uint32_t)a.rpad + (uint32_t)(j0 + JL * jg)) * 4u
-                                  : p * (uint32_t)a.rpad + (uint32_t)(j0 + JL * jg), 0);
+    w[i] = bload128(rl, tid >= NT ? kNoLoad
+                        : MODE == 0 ? (p * (uint32_t)a.rpad + (uint32_t)(j0 + JL * jg)) * 4u
+                                    : p * (uint32_t)a.rpad + (uint32_t)(j0 + JL * jg), 0);
   }
   // int4 scale rows of the slice, as fp32
   const int g0 = MODE == 1 ? k0 / a.group : 0;
   if constexpr (MODE == 1) {
-    const int ng = (k0 + kLrSlice - 1) / a.group - g0 + 1;
+    const int ng = (k0 + SL - 1) / a.group - g0 + 1;
     const brsrc_t rs = make_rsrc(a.ls, (uint32_t)((a.Kl + a.group - 1) / a.group) * (uint32_t)a.rpad * 2u);
     for (int i = tid; i < ng * 8; i += (int)blockDim.x) {
       const int row = i >> 3, part = i & 7;
@@ -260,7 +267,7 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
     if (a.clamp) xv = clamp_act8<BF16>(xv, a.cval);
     if (a.xscale) xv = scale_act8<BF16>(xv, xf);
   }
-  if (tid < MT * 64) *reinterpret_cast<uint4*>(&xs[tid >> 6][8 * (tid & 63)]) = xv;
+  if (tid < MT * XT) *reinterpret_cast<uint4*>(&xs[tid / XT][8 * (tid % XT)]) = xv;
   __syncthreads();
 
   float acc[MT][JL];
@@ -311,7 +318,7 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
       v += __shfl_xor(v, 32, 64);
       acc[m][j] = v;
     }
-  if (lane < 16 && tid < 256) {  // a wider workgroup's threads past 256 only keep the barriers
+  if (lane < 16 && tid < NT) {  // a wider workgroup's threads past NT only keep the barriers
     const int grp = MODE == 0 ? wave : wave * 4 + (lane >> 2);
 #pragma unroll
     for (int m = 0; m < MT; ++m)

@@ -31,6 +31,8 @@ CASES = [
     (2, 0, 1000, 150, 1, "auto"),        # no rank term
     (4, 0, 1280, 140, 16, "auto"),       # bitmap + clamp (split-K counters)
     (5, 0, 1456, 190, 40, "prefill"),    # prefill with the rank prologue
+    (5, 0, 2600, 700, 1, "decode_stream"),  # batch-1 streaming kernel with the prologue inside
+    (3, 1, 4160, 600, 1, "decode_stream"),
 ]
 
 

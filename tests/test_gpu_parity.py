@@ -142,6 +142,59 @@ def test_rows_large_activation_block(case):
         check_bound(gpu_forward(layer, x, path="decode"), layer, x, what=f"big lds {layer.name} M={M}")
 
 
+# The batch-1 streaming kernel (rows of at least 64 chunks): every workload's
+# formats with their rank terms, rows split between wavefronts and a short
+# last workgroup (N off the rows per workgroup), activation edits, and a
+# workgroup whose outliers overflow its staged entries (read from memory)
+STREAM_CASES = [
+    # (cfg, K, N, variant)
+    (5, 2600, 2600, "base"),       # LUT3 + CSR + bf16 rank 64, bf16 activations
+    (3, 4160, 1300, "base"),       # INT4 2:4 + int4 rank 128
+    (1, 4096, 700, "base"),        # LUT3 + CSR
+    (2, 2088, 3000, "act_scale"),  # LUT4 + CSR, per-channel factors edited while staged
+    (2, 2088, 2600, "full_rows"),  # four rows with every column an outlier in one workgroup
+    (2, 2600, 1500, "fp16_r70"),   # fp16 rank 70
+    (2, 2600, 900, "bf16_r256"),   # bf16 rank 256, bf16 activations
+    (2, 2600, 600, "int4_r64_g33"),  # int4 rank 64, odd groups
+]
+
+
+@pytest.mark.parametrize("case", STREAM_CASES, ids=lambda c: f"cfg{c[0]}-K{c[1]}-N{c[2]}-{c[3]}")
+def test_stream_kernel(case):
+    from synth.layers import with_act_scale
+    cfg, K, N, variant = case
+    layer = make_layer(cfg, 0, K=K, N=N, M_for_clamp=1)
+    r = np.random.default_rng(K + N)
+    if variant == "act_scale":
+        layer = with_act_scale(layer, seed=4)
+    elif variant == "full_rows":
+        rp = np.zeros(N + 1, np.int64)
+        counts = np.zeros(N, np.int64)
+        counts[11:15] = K  # rows 11..14: the second workgroup of 11 rows
+        rp[1:] = np.cumsum(counts)
+        col = np.tile(np.arange(K), 4).astype(np.int32)
+        layer = layer.with_(csr_row_ptr=rp.astype(np.int32), csr_col=col,
+                            csr_val=r.normal(0, 0.05, len(col)).astype(np.float16))
+    elif variant == "fp16_r70":
+        layer = _with_lowrank(layer, "fp16", 70, seed=1)
+    elif variant == "bf16_r256":
+        layer = _with_lowrank(layer.with_(x_dtype="bf16"), "bf16", 256, seed=2)
+    elif variant == "int4_r64_g33":
+        layer = _with_lowrank(layer, "int4", 64, group=33, seed=3)
+    xf = r.normal(0, 1, (1, K))
+    x = bf16_bits_from_f32(xf) if layer.x_dtype == "bf16" else xf.astype(np.float16)
+    say("stream", case)
+    mod = gpu_layer(layer, max_M=2)
+    try:
+        ys = gpu_forward(layer, x, path="decode_stream", mod=mod)
+        check_bound(ys, layer, x, what=f"stream {case}")
+        yr = gpu_forward(layer, x, path="decode_valu", mod=mod)  # the row-wise kernel on the same layer
+        y_ref, B = oracle.forward_and_bound(layer, x)
+        assert (np.abs(ys - yr) <= 2 * B).all()
+    finally:
+        mod.close()
+
+
 def test_deterministic():
     torch = torch_cuda()
     layer = make_layer(5, 0, K=1450, N=190)

@@ -126,10 +126,16 @@ def small_layer(fmt, x_dtype, K, N=200, seed=0):
     return LogicalLayer(**kw)
 
 
+SPAN = {"lut3": 40, "lut4": 32, "int4": 32, "int8": 16}  # weights per 16-byte code chunk
+
+
 def _routes_for(layer):
     rs = ["tile", "mfma", "prefill"]
     if layer.mask != "bitmap":  # the bitmap decodes on the tile and matrix-core kernels only
-        rs = ["stream", "rows1", "rows4"] + rs
+        rs = ["rows1", "rows4"] + rs
+        span = 64 if layer.mask == "2:4" else SPAN[layer.dense]
+        if -(-layer.K // span) >= 64:  # the streaming kernel takes rows of at least 64 chunks
+            rs = ["stream"] + rs
     return rs
 
 
@@ -153,6 +159,29 @@ def test_every_route_bit_exact_small(fmt, x_dtype, K):
                 ks = np.unique(np.r_[0, 1, 39, 40, 63, 64, K - 2, K - 1, np.random.default_rng(K).integers(0, K, 24)])
             say(layer.name, route, len(ks))
             check_route(mod, layer, ks, route, layer.name)
+    finally:
+        mod.close()
+
+
+# The streaming kernel: rows of 65-66 chunks with a ragged last chunk, 2600
+# rows (11 per workgroup: slices of 128 chunks cross two or three row
+# boundaries and split rows between wavefronts; the last workgroup is short).
+STREAM_K = {"lut3": 2568, "lut4": 2088, "int4": 2088, "int4_24": 4168, "int8": 1048}
+
+
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("fmt", [f for f in FORMATS if f != "int8_bm"])
+def test_stream_route_bit_exact(fmt, x_dtype):
+    from gpu_util import gpu_layer
+    K = STREAM_K[fmt]
+    layer = small_layer(fmt, x_dtype, K, N=2600)
+    mod = gpu_layer(layer, max_M=8)
+    try:
+        span = 64 if fmt == "int4_24" else SPAN[fmt[:4]]
+        ks = np.unique(np.r_[0, 1, span - 1, span, 63 * span, 64 * span - 1, K - 2, K - 1,
+                             np.random.default_rng(K).integers(0, K, 12)])
+        say(layer.name, "stream", len(ks))
+        check_route(mod, layer, ks, "stream", layer.name)
     finally:
         mod.close()
 

@@ -24,16 +24,18 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# (workload, M, path): the batch-1 row kernel with bf16 and with int4 factors,
-# the row kernel at batch 2 (fp16), the matrix-core decode kernel at batch 4 and 8
-CASES = [(5, 1, "auto"), (3, 1, "auto"), (3, 2, "auto"), (5, 4, "auto"), (3, 8, "decode_mfma")]
+# (workload, M, path, K): the batch-1 row kernel with bf16 and with int4
+# factors, the row kernel at batch 2 (fp16), the matrix-core decode kernel at
+# batch 4 and 8, the batch-1 streaming kernel with bf16 and with int4 factors
+CASES = [(5, 1, "decode_valu", 1280), (3, 1, "decode_valu", 1280), (3, 2, "auto", 1280), (5, 4, "auto", 1280),
+         (3, 8, "decode_mfma", 1280), (5, 1, "decode_stream", 2600), (3, 1, "decode_stream", 4160)]
 
 
-@pytest.mark.parametrize("cfg,M,path", CASES)
-def test_wait_give_up_is_reported(cfg, M, path):
+@pytest.mark.parametrize("cfg,M,path,K", CASES)
+def test_wait_give_up_is_reported(cfg, M, path, K):
     torch = torch_cuda()
-    layer = make_layer(cfg, 0, K=1280, N=200)
-    x = make_x(cfg, 0, M, K=1280)
+    layer = make_layer(cfg, 0, K=K, N=200)
+    x = make_x(cfg, 0, M, K=K)
     say("wait give-up", cfg, M, path)
     mod = gpu_layer(layer, max_M=max(M, 8))
     try:
