@@ -250,14 +250,15 @@ __global__ void __launch_bounds__(1024) decode_stream_kernel(StreamArgs sa) {
   const brsrc_t rm = make_rsrc(a.meta, KIND == K_INT4_24 ? (uint32_t)a.Npad * (uint32_t)C * 8u : 0u);
   const uint32_t gchunk = (uint32_t)r0 * (uint32_t)C + (uint32_t)f0 + (uint32_t)lane;  // this lane's first chunk
   auto load_blk = [&](uint4 (&w)[NB], uint2 (&mw)[NB], int j) {
-    // a block past the slice loads nothing; passes past the slice inside the
-    // last block read chunks of the next slice (or zero past the buffer) and are masked
+    // a pass past the slice loads nothing; lanes past the slice's end inside
+    // its last pass read chunks of the next slice (or zero past the buffer) and are masked
     const uint32_t c0 = gchunk + (uint32_t)(j * NB * 64);
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
-      w[q] = bload128_nt(rd, j < nblk ? (c0 + 64u * q) * 16u : kNoLoad, 0);
+      const bool live = j * NB + q < np;
+      w[q] = bload128_nt(rd, live ? (c0 + 64u * q) * 16u : kNoLoad, 0);
       if constexpr (KIND == K_INT4_24)
-        mw[q] = bload64_nt(rm, j < nblk ? (c0 + 64u * q) * 8u : kNoLoad, 0);
+        mw[q] = bload64_nt(rm, live ? (c0 + 64u * q) * 8u : kNoLoad, 0);
       else
         mw[q] = make_uint2(0, 0);
     }
