@@ -1,4 +1,4 @@
-"""CPU oracle of the data-free LUT packer -- TEST INFRASTRUCTURE.
+"""CPU oracle of the data-free packers -- TEST INFRASTRUCTURE.
 
 Only the test suite may import or run this module.  The HIP library never
 calls it and it never calls the HIP library; they share no code.
@@ -21,7 +21,16 @@ What it computes, from fp16 weights W [N, K] (rows = output channels):
      a tie).  An outlier's position takes the code nearest to 0 and its CSR
      value is fp16(w - lut[that code]), so that D + S reproduces it.
 
+Naive-LoRA (naive_lora below): the rank-r factors whose product is the
+truncated SVD of the residual E = W - W_hat, the approximation of least
+Frobenius error (Eckart-Young).
+
 Sources, by page (title, then section):
+  * "SLiM: One-shot Quantization and Sparsity with Low-rank Approximation for
+    LLM Weight Compression" -- review highlights, SLiM-LoRA bullet: Naive-LoRA
+    minimises the plain error norm between the original and the compressed
+    weight matrix (the saliency-weighted SLiM-LoRA needs calibration data and
+    is not here).
   * "SqueezeLLM: Dense-and-Sparse Quantization" -- Approach: non-uniform LUT
     quantization whose centroids come from k-means over each output channel's
     weights, with outliers (and sensitive weights) kept apart in a
@@ -232,3 +241,27 @@ def absmax_groups(F16, group: int, dtype: str = "f16"):
             if s[c] > 0:
                 q[g * group:(g + 1) * group, c] = np.clip(np.rint(blk[:, c] / s[c]), -8, 7).astype(np.int8)
     return q, sc
+
+
+def naive_lora(E, rank: int):
+    """Naive-LoRA factors of the residual E [N, K] = W - W_hat (rows = output
+    channels), SLiM page, review highlights, SLiM-LoRA bullet: with the SVD
+    E = U diag(s) V^T (s descending), (L R)^T = U_r diag(s_r) V_r^T, the
+    rank-r approximation of least Frobenius (and spectral) error.  The split
+    of diag(s_r) between the factors is not given by the page; this reading
+    gives each factor its square root:
+        L = V_r diag(sqrt(s_r))   [K, rank]      R = diag(sqrt(s_r)) U_r^T   [rank, N]
+    so that L^T L = R R^T = diag(s_r).  Ranks past min(N, K) get zero columns.
+    Returns L, R (float64) and s_r."""
+    E = np.asarray(E, dtype=np.float64)
+    N, K = E.shape
+    U, s, Vt = np.linalg.svd(E, full_matrices=False)
+    r = min(rank, s.size)
+    sq = np.sqrt(s[:r])
+    L = np.zeros((K, rank))
+    R = np.zeros((rank, N))
+    L[:, :r] = Vt[:r].T * sq
+    R[:r] = (U[:, :r] * sq).T
+    sv = np.zeros(rank)
+    sv[:r] = s[:r]
+    return L, R, sv

@@ -247,10 +247,55 @@ def pin_absmax_properties(F):
                     assert abs(int(q[gi * g + j, c])) == 7
 
 
+def pin_lora_worked_examples(F):
+    # SLiM page, review highlights, SLiM-LoRA bullet (Naive-LoRA: least error norm).
+    # diag(3, 1, 2): the best rank-2 approximation keeps 3 and 2 and drops 1.
+    E = np.diag([3.0, 1.0, 2.0])
+    L, R, s = F.naive_lora(E, 2)
+    assert np.allclose((L @ R).T, np.diag([3.0, 0.0, 2.0]), atol=1e-12), (L @ R).T
+    assert np.allclose(s, [3.0, 2.0])
+    # a rank-1 matrix a b^T: one factor pair reproduces it, sigma = |a| |b| = 5 * 13
+    a, b = np.array([3.0, 4.0]), np.array([5.0, 0.0, 12.0])
+    L, R, s = F.naive_lora(np.outer(a, b), 1)
+    assert np.allclose((L @ R).T, np.outer(a, b), atol=1e-12) and abs(s[0] - 65.0) < 1e-12
+    # the square-root split: L^T L = R R^T = diag(s)
+    assert np.allclose(L.T @ L, np.diag(s)) and np.allclose(R @ R.T, np.diag(s))
+    # rank past min(N, K): exact, zero columns beyond
+    L, R, s = F.naive_lora(np.outer(a, b), 4)
+    assert np.allclose((L @ R).T, np.outer(a, b), atol=1e-12) and np.all(L[:, 2:] == 0) and np.all(s[2:] == 0)
+
+
+def pin_lora_eckart_young(F):
+    # the error of the truncation is the root-sum-square of the dropped singular
+    # values, here from the eigenvalues of E^T E (another routine); no rank-r
+    # matrix does better than it (random rank-r candidates, and the best one
+    # perturbed); the factors' product does not depend on SVD sign choices
+    # (E and -E, E and E^T give the negated / transposed products)
+    r = _rng(77)
+    for N, K, rank in ((40, 25, 5), (17, 60, 3), (30, 30, 29)):
+        E = r.normal(0, 1, (N, K)) * np.exp(-np.arange(K) / 9.0)
+        L, R, s = F.naive_lora(E, rank)
+        A = (L @ R).T
+        lam = np.sort(np.linalg.eigvalsh(E.T @ E))[::-1]
+        err = np.linalg.norm(E - A)
+        assert abs(err - np.sqrt(max(lam[rank:].sum(), 0.0))) <= 1e-9 * np.linalg.norm(E), (err, lam[rank:].sum())
+        assert np.allclose(s ** 2, lam[:rank], rtol=1e-9, atol=1e-9 * lam[0])
+        for _ in range(5):
+            B = r.normal(0, 1, (N, rank)) @ r.normal(0, 1, (rank, K))
+            B *= np.vdot(B, E) / np.vdot(B, B)  # the best multiple of a random rank-r matrix
+            assert np.linalg.norm(E - B) >= err
+            P = ((L + 1e-3 * r.normal(0, 1, L.shape)) @ (R + 1e-3 * r.normal(0, 1, R.shape))).T  # rank r still
+            assert np.linalg.norm(E - P) >= err - 1e-12
+        L2, R2, _ = F.naive_lora(-E, rank)
+        assert np.allclose((L2 @ R2).T, -A, atol=1e-9)
+        L3, R3, _ = F.naive_lora(E.T, rank)
+        assert np.allclose(L3 @ R3, A, atol=1e-9)
+
+
 ALL_PINS = [pin_worked_example, pin_round_f16_library, pin_outliers_brute, pin_kmeans_fixed_point,
             pin_kmeans_sklearn, pin_sse_monotone, pin_codes_and_residual, pin_int_worked_example,
             pin_masks_brute, pin_clip_search_fractions, pin_clip_never_worse_than_absmax,
-            pin_absmax_worked_example, pin_absmax_properties]
+            pin_absmax_worked_example, pin_absmax_properties, pin_lora_worked_examples, pin_lora_eckart_young]
 
 
 def failing_pins(F):

@@ -218,3 +218,51 @@ def test_fit_pins_catch_absmax_mutant(mutate):
     F = fresh()
     mutate(F)
     assert fit_pins.failing_pins(F), f"no pin caught {mutate.__name__}"
+
+
+# Naive-LoRA: planted mistakes the pins must catch
+def _mut_lora_smallest(F):
+    def naive_lora(E, rank):
+        E = np.asarray(E, dtype=np.float64)
+        U, s, Vt = np.linalg.svd(E, full_matrices=False)
+        idx = np.argsort(s)[:rank]  # the smallest singular values instead of the largest
+        sq = np.sqrt(s[idx])
+        return Vt[idx].T * sq, (U[:, idx] * sq).T, s[idx]
+    F.naive_lora = naive_lora
+
+
+def _mut_lora_unsplit(F):
+    def naive_lora(E, rank):
+        E = np.asarray(E, dtype=np.float64)
+        U, s, Vt = np.linalg.svd(E, full_matrices=False)
+        r = min(rank, s.size)
+        L = np.zeros((E.shape[1], rank)); R = np.zeros((rank, E.shape[0])); sv = np.zeros(rank)
+        L[:, :r] = Vt[:r].T * s[:r]  # all of s in L
+        R[:r] = U[:, :r].T
+        sv[:r] = s[:r]
+        return L, R, sv
+    F.naive_lora = naive_lora
+
+
+def _mut_lora_transposed(F):
+    def naive_lora(E, rank):
+        E = np.asarray(E, dtype=np.float64)
+        U, s, Vt = np.linalg.svd(E, full_matrices=False)
+        r = min(rank, s.size)
+        sq = np.sqrt(s[:r])
+        L = np.zeros((E.shape[1], rank)); R = np.zeros((rank, E.shape[0])); sv = np.zeros(rank)
+        L[:, :r] = (U[:, :r] * sq)[:E.shape[1]] if E.shape[0] >= E.shape[1] else np.pad(U[:, :r] * sq, ((0, E.shape[1] - E.shape[0]), (0, 0)))
+        R[:r] = (Vt[:r].T * sq).T[:, :E.shape[0]] if E.shape[1] >= E.shape[0] else np.pad((Vt[:r].T * sq).T, ((0, 0), (0, E.shape[0] - E.shape[1])))
+        sv[:r] = s[:r]
+        return L, R, sv
+    F.naive_lora = naive_lora
+
+
+LORA_MUTANTS = [_mut_lora_smallest, _mut_lora_unsplit, _mut_lora_transposed]
+
+
+@pytest.mark.parametrize("mutate", LORA_MUTANTS, ids=lambda f: f.__name__[5:])
+def test_lora_mutant_caught(mutate):
+    F = fresh()
+    mutate(F)
+    assert fit_pins.failing_pins(F), "no pin caught the planted mistake"
