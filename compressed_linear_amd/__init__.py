@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcompress
 EXPORTED_SYMBOLS = [
     "cl_pack", "cl_device_bytes", "cl_create", "cl_forward", "cl_forward_path",
     "cl_debug_dequant", "cl_destroy", "cl_last_error", "cl_fit_lut_work_bytes", "cl_fit_lut",
-    "cl_fit_int", "cl_quant_absmax", "cl_set_wait_limit", "cl_fit_lut_noalloc",
+    "cl_fit_int", "cl_quant_absmax", "cl_set_wait_limit", "cl_fit_lut_noalloc", "cl_fit_lowrank",
 ]
 
 # measurement aids of the benchmark (include/cl_probe.h), exported by the same library
@@ -121,6 +121,9 @@ def lib():
         L.cl_fit_int.restype = ctypes.c_int
         L.cl_quant_absmax.argtypes = [ctypes.c_void_p] + [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3
         L.cl_quant_absmax.restype = ctypes.c_int
+        L.cl_fit_lowrank.argtypes = ([ctypes.c_void_p] + [ctypes.c_int32] * 5 + [ctypes.c_uint64] +
+                                     [ctypes.c_void_p] * 4)
+        L.cl_fit_lowrank.restype = ctypes.c_int
         L.cl_fit_lut_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 6 + \
             [ctypes.POINTER(ctypes.c_int64)]
@@ -379,3 +382,23 @@ def quant_absmax(F, group: int = 128):
                                sc.data_ptr(), torch.cuda.current_stream(F.device).cuda_stream)
     _check(st, "cl_quant_absmax")
     return q, sc
+
+
+def fit_lowrank(E, rank: int, oversample: int = 16, iters: int = 8, seed: int = 0):
+    """Naive-LoRA factors of the residual E = W - W_hat (cl_fit_lowrank): E is a
+    torch float32 [N, K] tensor on a ROCm device.  Returns device tensors
+    (L fp32 [K, rank], R fp32 [rank, N]) and the singular-value estimates (a
+    host numpy array), with (L R)^T close to E's rank-`rank` truncated SVD."""
+    import numpy as np
+    import torch
+    if E.dtype != torch.float32 or E.dim() != 2 or not E.is_cuda:
+        raise ValueError("E must be a 2-D float32 tensor on a ROCm device")
+    E = E.contiguous()
+    N, K = E.shape
+    L = torch.empty((K, rank), dtype=torch.float32, device=E.device)
+    R = torch.empty((rank, N), dtype=torch.float32, device=E.device)
+    sv = np.zeros(rank, dtype=np.float32)
+    st = lib().cl_fit_lowrank(E.data_ptr(), N, K, rank, oversample, iters, seed, L.data_ptr(), R.data_ptr(),
+                              sv.ctypes.data, torch.cuda.current_stream(E.device).cuda_stream)
+    _check(st, "cl_fit_lowrank")
+    return L, R, sv

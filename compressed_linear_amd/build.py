@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcompressed_linear.so")
 ARCH = os.environ.get("CL_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["pack.cpp", "runtime.hip", "decode.hip", "aux.hip", "prefill.hip", "fit.hip", "probe.hip",
+SOURCES = ["pack.cpp", "runtime.hip", "decode.hip", "aux.hip", "prefill.hip", "fit.hip", "fit_lowrank.cpp", "probe.hip",
            "decode_lut3.hip", "decode_lut4.hip", "decode_int4.hip", "decode_int4_24.hip",
            "decode_int8.hip", "decode_int8_bm.hip",
            "decode_rows_lut3.hip", "decode_rows_lut4.hip", "decode_rows_int4.hip", "decode_rows_int4_24.hip",
@@ -31,6 +31,8 @@ SOURCES = ["pack.cpp", "runtime.hip", "decode.hip", "aux.hip", "prefill.hip", "f
            "decode_mfma_lut3.hip", "decode_mfma_lut4.hip", "decode_mfma_int4.hip", "decode_mfma_int4_24.hip",
            "decode_mfma_int8.hip", "decode_mfma_int8_bm.hip",
            "prefill_lut3.hip", "prefill_lut4.hip", "prefill_int.hip", "prefill_lr.hip"]
+
+LIBS = ["-lrocblas"]  # the Naive-LoRA fitter's products with the residual
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
@@ -69,7 +71,7 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs + LIBS
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

@@ -408,6 +408,32 @@ cl_status cl_quant_absmax(const uint16_t* F, int32_t R, int32_t C, int32_t group
                           uint16_t* scale, void* stream);
 
 /*
+ * cl_fit_lowrank -- Naive-LoRA ("SLiM" page, review highlights, SLiM-LoRA
+ * bullet: the low-rank part that minimises the plain error norm between the
+ * original and the compressed weight matrix): factors L, R of rank `rank`
+ * such that (L R)^T approximates the truncated SVD of the residual
+ * E = W - W_hat, found by randomized subspace iteration (rocBLAS products on
+ * the GPU, m x m eigenproblems on the host; m = min(rank + oversample, N, K)).
+ * The singular values are split evenly: L = V_r diag(sqrt(s)), R = diag(sqrt(s))
+ * U_r^T.  The factors are fp32; cast them (or quantize with cl_quant_absmax)
+ * for cl_pack.
+ *   E           device, [N, K] fp32 row-major (rows = output channels), finite.
+ *   rank        1..512; ranks past min(N, K) get zero factors.
+ *   oversample  extra columns of the search subspace (>= 0; 16 is a good start).
+ *   iters       power iterations, 0..100 (each one: two products with E).
+ *   seed        of the Gaussian start matrix (the result depends on it only
+ *               through rounding once the iteration has converged).
+ *   L           device, [K, rank] fp32 row-major; R device, [rank, N] fp32.
+ *   sigma       host, [rank] fp32 singular-value estimates (descending), or NULL.
+ *   stream      hipStream_t; the call returns when the factors are written.
+ * Allocates its work matrices (about 4 (N + K) m + 8 m^2 bytes).
+ * Errors: CL_EINVAL (sizes, NULL pointers), CL_ESIZE (2^31 elements or bytes
+ * in E or a work matrix), CL_ENOMEM, CL_EHIP.
+ */
+cl_status cl_fit_lowrank(const float* E, int32_t N, int32_t K, int32_t rank, int32_t oversample, int32_t iters,
+                         uint64_t seed, float* L, float* R, float* sigma, void* stream);
+
+/*
  * Header at the start of every packed blob (little endian).  Exposed so that
  * tools can inspect a blob; the section layouts are documented with the
  * packer.

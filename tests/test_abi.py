@@ -177,3 +177,14 @@ def test_buffers_of_2_gib_are_refused():
     assert L.cl_device_bytes(blob.ctypes.data, 1) > 0
     assert L.cl_device_bytes(blob.ctypes.data, 1 << 18) == 0  # activations of 2^18 rows: 2 GiB
     assert b"2 GiB" in L.cl_last_error()
+
+
+def test_fit_lowrank_host_checks():
+    # argument errors are reported before any device work (no GPU needed)
+    L = cla.lib()
+    assert L.cl_fit_lowrank(None, 10, 10, 2, 4, 2, 0, 1, 1, None, None) == -1          # E NULL
+    assert L.cl_fit_lowrank(1, 10, 10, 0, 4, 2, 0, 1, 1, None, None) == -1             # rank 0
+    assert L.cl_fit_lowrank(1, 10, 10, 513, 4, 2, 0, 1, 1, None, None) == -1           # rank above 512
+    assert L.cl_fit_lowrank(1, 10, 10, 2, -1, 2, 0, 1, 1, None, None) == -1            # oversample < 0
+    assert L.cl_fit_lowrank(1, 10, 10, 2, 4, 101, 0, 1, 1, None, None) == -1           # iters > 100
+    assert L.cl_fit_lowrank(1, 1 << 16, 1 << 16, 2, 4, 2, 0, 1, 1, None, None) == -5   # 2^32 elements
