@@ -90,9 +90,11 @@ def read_traffic(cfg: int, M: int):
 
 def batch1_kernel(l, acct) -> str:
     """The kernel a batch-1 forward of layer l runs on the auto path: the
-    streaming kernel for layers of 28 MiB of code chunks or more (the library's
-    rule in decode.hip), the row-wise kernel otherwise."""
-    return "decode_stream_kernel" if acct["codes"] >= (28 << 20) else "decode_rows_kernel"
+    streaming kernel for layers of 28 MiB of code chunks or more, or with a
+    rank term and K < N (the library's rule in decode.hip), the row-wise kernel
+    otherwise."""
+    stream = acct["codes"] >= (28 << 20) or (bool(l.rank) and l.K < l.N)
+    return "decode_stream_kernel" if stream else "decode_rows_kernel"
 
 
 def roofline(cfg: int, M: int, path: str, built, set_bytes: int, us_per_launch: float, graph: bool) -> dict:

@@ -167,7 +167,7 @@ static StreamPlanH plan_stream_k(const cl_blob_header& h, const int32_t* rp, int
     if (stream_slots_per_thread<KIND>(C, threads) > 12) continue;
     // the prologue workgroups (the launch's first) hold their CUs while they
     // run: the row workgroups take the others, so that none waits for a CU
-    const int lr_wgs = (lr && lr_mode >= 0) ? stream_lr_slices((int)ceil_div(h.K, kLrSlice), threads) *
+    const int lr_wgs = (lr && lr_mode >= 0) ? stream_lr_slices((int)ceil_div(h.K, kLrSlice), threads, lr_mode) *
                                                   (int)ceil_div(h.rank, 64) : 0;
     const size_t lr_lds = lr_wgs ? (size_t)lr_scratch_bytes(lr_mode, 1, threads == 1024 ? 1024 : 256) : 0;
     const long long slots = (long long)num_cus * k - lr_wgs;
@@ -224,15 +224,19 @@ static StreamPlanH plan_stream_k(const cl_blob_header& h, const int32_t* rp, int
 // Which batch-1 layers take the streaming kernel.  Its launch costs a fixed
 // few microseconds (dispatch of full-CU workgroups, staging the activations and
 // row tables once per CU) and then streams at close to the memory rate; the
-// row-wise kernel starts at once but streams slower.  Measured on one MI355X
-// (us per layer, streaming / row-wise): LLaMA-70B LUT3 + bf16 rank 64 8192 ->
-// 10240 (32 MiB of codes) 17.1 / 18.7, 8192 -> 28672 30.7 / 36.6, 28672 ->
-// 8192 30.9 / 37.0; LLaMA-7B LUT4 4096 -> 12288 (24 MiB) 12.9 / 9.8, 4096 ->
-// 11008 12.1 / 9.8; INT4 2:4 + int4 rank 128 4096 -> 11008 16.3 / 16.0;
-// LUT3 4096 -> 4096 7.6 / 4.9.  The streaming kernel takes layers of 28 MiB
-// of codes or more.
+// row-wise kernel starts at once but streams slower.  With a rank term, the
+// streaming kernel's prologue hands t to its readers in one trip through memory
+// (tagged partial sums), the row-wise kernel's in several.  Measured on one
+// MI355X (us per layer, streaming / row-wise): LLaMA-70B LUT3 + bf16 rank 64
+// 8192 -> 10240 (32 MiB of codes) 16.1 / 16.6, 8192 -> 28672 29.5 / 37.9,
+// 28672 -> 8192 30.4 / 36.9; INT4 2:4 + int4 rank 128 4096 -> 11008 (11 MiB)
+// 12.6 / 15.3, 11008 -> 4096 15.3 / 14.9; LLaMA-7B LUT4 4096 -> 12288 (24 MiB)
+// 11.6 / 9.2; LUT3 4096 -> 4096 7.6 / 4.9.  The streaming kernel takes layers
+// of 28 MiB of codes or more, and layers with a rank term whose rows are
+// shorter than their count (K < N: the walk outlasts the prologue).
 static bool stream_wins(const cl_blob_header& h) {
-  return (unsigned long long)h.N * h.chunks * 16ull >= (28ull << 20);
+  const bool lr = h.lr != CL_LR_NONE && h.rank > 0;
+  return (unsigned long long)h.N * h.chunks * 16ull >= (28ull << 20) || (lr && h.K < h.N);
 }
 
 StreamPlanH plan_stream(const cl_blob_header& h, const int32_t* rowptr, int num_cus, int lr_mode) {
@@ -304,7 +308,7 @@ static hipError_t launch_decode_stream(const Layer& L, const void* x, float* y, 
       r.lrp.flag = L.lr_cnt + 65;
       r.lrp.epoch = next_epoch(L, stream);
       r.lrp.withhold = L.wait_withhold;
-      r.lrp.S = stream_lr_slices(L.lr_S, L.st.wpg * 64);  // blocks over longer K slices
+      r.lrp.S = stream_lr_slices(L.lr_S, L.st.wpg * 64, L.lr_mode);  // blocks over longer K slices
       r.lr_ntj = L.lr_rpad / 64;
       r.lr_wgs = r.lrp.S * r.lr_ntj;
       r.lr_mode = L.lr_mode;

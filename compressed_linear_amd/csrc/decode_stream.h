@@ -80,8 +80,12 @@ __host__ __device__ inline int stream_slice(int F, int C, int wpg) {
 }
 
 // Prologue blocks of a streaming launch: a workgroup of 16 wavefronts works on
-// a K slice four times as long as the 256-thread block's.
-inline int stream_lr_slices(int lr_S, int threads) { return threads == 1024 ? (lr_S + 3) / 4 : lr_S; }
+// a K slice four (fp16 / bf16 factors) or two (int4) times as long as the
+// 256-thread block's.
+inline int stream_lr_slices(int lr_S, int threads, int lr_mode) {
+  const int f = threads != 1024 ? 1 : lr_mode == 0 ? lr_slice_rows<0, 1024>() / kLrSlice : lr_slice_rows<1, 1024>() / kLrSlice;
+  return (lr_S + f - 1) / f;
+}
 
 // XR = activation slots staged per thread, LR = low-rank part, EDIT = raw
 // activations edited (clamp, per-channel factors) while staged.
@@ -103,11 +107,11 @@ __global__ void __launch_bounds__(1024) decode_stream_kernel(StreamArgs sa) {
     if ((int)blockIdx.x < a.lr_wgs) {  // a prologue workgroup
       const int b = blockIdx.x, S = a.lrp.S, s = b % S, tj = (b / S) % a.lr_ntj, tm = b / (S * a.lr_ntj);
       if (nthr == 1024) {
-        if (a.lr_mode == 0) lr_split_block<0, 1, BF16, EDIT, 1024>(a.lrp, s, tj, tm, a.lr_ntj, sb);
-        else lr_split_block<1, 1, BF16, EDIT, 1024>(a.lrp, s, tj, tm, a.lr_ntj, sb);
+        if (a.lr_mode == 0) lr_split_block<0, 1, BF16, EDIT, 1024, true>(a.lrp, s, tj, tm, a.lr_ntj, sb);
+        else lr_split_block<1, 1, BF16, EDIT, 1024, true>(a.lrp, s, tj, tm, a.lr_ntj, sb);
       } else {
-        if (a.lr_mode == 0) lr_split_block<0, 1, BF16, EDIT>(a.lrp, s, tj, tm, a.lr_ntj, sb);
-        else lr_split_block<1, 1, BF16, EDIT>(a.lrp, s, tj, tm, a.lr_ntj, sb);
+        if (a.lr_mode == 0) lr_split_block<0, 1, BF16, EDIT, 256, true>(a.lrp, s, tj, tm, a.lr_ntj, sb);
+        else lr_split_block<1, 1, BF16, EDIT, 256, true>(a.lrp, s, tj, tm, a.lr_ntj, sb);
       }
       return;
     }
@@ -410,17 +414,23 @@ __global__ void __launch_bounds__(1024) decode_stream_kernel(StreamArgs sa) {
   }
   if (np > 0) deposit(n, acc);  // the slice's last row
 
-  // ---- t = x' L_hat: the first wavefront waits for it and copies it to LDS ----
+  // ---- t = x' L_hat: the first wavefront adds up the prologue's tagged
+  // partial sums (or reads t written by an earlier kernel) into LDS ----
   float* st = reinterpret_cast<float*>(sb + sa.lds_t);
   if constexpr (LR) {
     if (wave == 0) {
       const uint32_t target = a.lr_flag != nullptr ? lr_target(a.lr_flag, a.lr_epoch) : 0u;
-      const bool t_ok =
-          a.lr_flag == nullptr || wait_lowrank(lr_word(a.lr_flag, a.lr_epoch), target, lane, a.lr_max_polls, a.lr_err);
+      float tv[4];
+      if (a.lr_flag != nullptr) {
+        read_t_tagged(a.lrp.part, a.lrp.S, a.rank, lr_tag(a.lr_epoch, target), lane, a.lr_max_polls, a.lr_err, tv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tv[i] = lane + 64 * i < a.rank ? load_dev(a.t + lane + 64 * i) : 0.f;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = lane + 64 * i;
-        if (j < a.rank) st[j] = t_ok ? load_dev(a.t + j) : __builtin_nanf("");
+        if (j < a.rank) st[j] = tv[i];
       }
       if (a.lr_flag != nullptr && a.lr_epoch == 0) {  // recorded launch: this workgroup's reads of t are done
         __builtin_amdgcn_s_waitcnt(0);

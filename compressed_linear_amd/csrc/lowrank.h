@@ -164,6 +164,58 @@ __device__ __forceinline__ bool wait_lowrank(const uint32_t* word, uint32_t targ
   return __shfl(ok, 0, 64) != 0;
 }
 
+// Reader of tagged partial sums: t[j] for j = lane + 64 i < rank (i < 4), the
+// sum over the S slices in slice order of the words of (tile j / 64, slice s),
+// once all of them carry `tag`.  The words are read with device-scope loads
+// (past the CU's own cache, which may hold an earlier launch's words), eight
+// in flight at a time.  Bounded like wait_lowrank: a wait that gives up records
+// it in the layer's error word and gives NaN.
+__device__ __forceinline__ bool read_t_tagged(const float* part, int S, int rank, uint32_t tag, int lane, uint32_t max_polls,
+                                              uint32_t* err, float (&tv)[4]) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const int ntj = (rank + 63) >> 6;
+  const brsrc_t rp = make_rsrc(part, (uint32_t)ntj * (uint32_t)S * 512u);
+  uint32_t it = 0;
+  bool ok = false;
+  for (;;) {
+    bool mine = true;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = lane + 64 * i;
+      float sum = 0.f;
+      const uint32_t col = ((uint32_t)(j >> 6) * (uint32_t)S * 64u + (uint32_t)(j & 63)) * 8u;
+      for (int s0 = 0; s0 < S; s0 += 8) {
+        u32x2 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const bool live = j < rank && s0 + q < S;
+          v[q] = __builtin_amdgcn_raw_buffer_load_b64(rp, live ? col + (uint32_t)(s0 + q) * 512u : kNoLoad, 0, 16);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (j < rank && s0 + q < S) {
+            mine = mine && v[q].y == tag;
+            sum += __uint_as_float(v[q].x);
+          }
+        }
+      }
+      tv[i] = sum;
+    }
+    if (__builtin_amdgcn_read_exec() == __ballot(mine)) {  // every lane's words are this launch's
+      ok = true;
+      break;
+    }
+    if (it++ >= max_polls) break;
+    __builtin_amdgcn_s_sleep(4);
+  }
+  if (!ok) {
+    if (lane == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tv[i] = lane + 64 * i < rank ? __builtin_nanf("") : 0.f;
+  }
+  return ok;
+}
+
 template <bool BF16>
 __device__ __forceinline__ float dot2_act(uint32_t a, uint32_t b, float c) {
   if constexpr (BF16) {
@@ -174,10 +226,19 @@ __device__ __forceinline__ float dot2_act(uint32_t a, uint32_t b, float c) {
   }
 }
 
-// NT = threads of a prologue block: its K slice is kLrSlice * NT / 256 rows.
+// NT = threads of a prologue block.  A thread loads NL 16-byte pieces of the
+// slice: 16 of fp16 / bf16 factors, 4 of int4 ones (2 in a 1024-thread block,
+// whose dequantisation would otherwise outlast the rest of the launch), so the
+// slice has 2 (NT / 16) NL rows (16-bit) or 2 (NT / 4) NL rows (int4).
+template <int MODE, int NT>
+constexpr int lr_loads() { return MODE == 0 ? 16 : NT == 1024 ? 2 : 4; }
+template <int MODE, int NT>
+constexpr int lr_slice_rows() { return 2 * (NT / (MODE == 0 ? 16 : 4)) * lr_loads<MODE, NT>(); }
+static_assert(lr_slice_rows<0, 256>() == kLrSlice && lr_slice_rows<1, 256>() == kLrSlice, "256-thread slices");
+
 template <int MODE, int MT, int NT = 256>
 struct LrScratch {
-  static constexpr int SL = kLrSlice * NT / 256;  // K rows of the slice
+  static constexpr int SL = lr_slice_rows<MODE, NT>();  // K rows of the slice
   static constexpr int NG = MODE == 0 ? NT / 64 : NT / 16;  // reduction groups left after the shuffles
   static constexpr int NSC = SL / 16 + 1;         // int4 scale rows a slice can touch (group >= 16)
   static constexpr int xs = 0;                                   // uint16 [MT][SL]
@@ -199,11 +260,21 @@ inline int lr_scratch_bytes(int mode, int mt, int nt = 256) {
 // LrScratch<MODE, MT, NT>::SL rows, column tile tj of ntj, activation tile tm;
 // `smem` is LrScratch<MODE, MT, NT>::bytes of LDS.  EDIT: the activations may
 // be raw (a.clamp, a.xscale apply); else they are edited already.
-template <int MODE, int MT, bool BF16, bool EDIT, int NT = 256>
+// Tagged partial sums (TAG, one activation row): instead of the arrival
+// count, the last block's sum, the store of t and the published word, each
+// block writes its 64 partial sums as 64-bit words (fp32 value, launch tag)
+// that its readers load, check and add in slice order themselves -- one trip
+// through memory instead of six.  The tag is the launch's epoch, or for a
+// recorded launch its generation with the top bit set.
+__device__ __forceinline__ uint32_t lr_tag(uint32_t epoch, uint32_t target) {
+  return epoch ? epoch : (0x80000000u | target);
+}
+
+template <int MODE, int MT, bool BF16, bool EDIT, int NT = 256, bool TAG = false>
 __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int tj, int tm, int ntj, uint8_t* smem) {
   using SC = LrScratch<MODE, MT, NT>;
   constexpr int SL = SC::SL;
-  constexpr int NL = MODE == 0 ? 16 : 4;        // 16-byte loads per thread
+  constexpr int NL = lr_loads<MODE, NT>();      // 16-byte loads per thread
   constexpr int JL = MODE == 0 ? 4 : 16;        // columns per thread
   constexpr int LG = 64 / JL;                   // threads per K pair row of the tile
   constexpr int PR = NT / LG;                   // K pair rows in flight per workgroup
@@ -331,6 +402,15 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
   if (o < MT * 64) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) v += red[g][o];
+  }
+  if constexpr (TAG) {
+    static_assert(MT == 1, "tagged partial sums of one activation row");
+    if (o < 64) {
+      const uint32_t tag = lr_tag(a.epoch, publish) ^ (a.withhold ? 0x40000000u : 0u);  // withheld: never matches
+      uint64_t* dst = reinterpret_cast<uint64_t*>(a.part) + ((size_t)(tm * ntj + tj) * a.S + s) * 64 + o;
+      __hip_atomic_store(dst, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
   }
   const int m = o >> 6, j = j0 + (o & 63);
   const bool store = o < MT * 64 && m0 + m < a.M && j < a.rank;
