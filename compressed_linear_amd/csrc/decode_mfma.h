@@ -55,6 +55,9 @@ namespace cl {
 typedef __bf16 mf_bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 mf_f16x8 __attribute__((ext_vector_type(8)));
 typedef float mf_f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 mf_bf16x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 mf_f16x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t mf_u32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kMfOe = 8;  // outlier entries per lane loaded with the code stream
 
@@ -99,6 +102,23 @@ __device__ __forceinline__ mf_f32x16 mf_mfma(uint4 a, uint4 b, mf_f32x16 c) {
                                                    0, 0, 0);
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(mf_f16x8, a), __builtin_bit_cast(mf_f16x8, b), c, 0, 0,
                                                 0);
+}
+
+// Sparse-A matrix-core step for 2:4 weights (v_smfmac_f32_32x32x32): the
+// weight operand a holds eight kept values of lane (row l mod 32, half h) --
+// the two kept values of each of four consecutive groups of four k -- and idx
+// (bits 16 ABID ..) their 2-bit positions in the group, in the same order; the
+// activation operand of lane half h' is x at 8h'..8h'+7 of lane half 0's 16 k
+// (b0) and of lane half 1's (b1).  The output is transposed against mf_mfma:
+// lane l holds activation row l mod 32 for weight rows 8 (v / 4) + 4 h + v mod 4.
+template <bool BF16, int ABID>
+__device__ __forceinline__ mf_f32x16 mf_smfmac(uint4 a, uint4 b0, uint4 b1, uint32_t idx, mf_f32x16 c) {
+  const mf_u32x8 b = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  if constexpr (BF16)
+    return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(mf_bf16x8, a), __builtin_bit_cast(mf_bf16x16, b), c,
+                                                     (int)idx, 0, ABID);
+  return __builtin_amdgcn_smfmac_f32_32x32x32_f16(__builtin_bit_cast(mf_f16x8, a), __builtin_bit_cast(mf_f16x16, b), c,
+                                                  (int)idx, 0, ABID);
 }
 
 template <bool BF16>
@@ -185,6 +205,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   constexpr int SPAN = C::span, P = C::pairs, PASSK = C::passk, NMF = P / 4;  // MFMAs per chunk
   constexpr int CPH = C::cph;
   constexpr bool BM = KIND == K_INT8_BM;
+  constexpr bool SP = KIND == K_INT4_24;  // 2:4 on the sparse-A instruction (kept values and positions as stored)
   // outputs v of a lane whose activation row m(v) = 8 (v / 4) + 4 half + v mod 4 is below MT
   constexpr int NV = MT >= 32 ? 16 : MT / 2;
   constexpr int XR = MT * kMfKzMax / 8 / 256;  // 16-byte activation slots per thread
@@ -359,6 +380,7 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   }
   const int mrow_s = mrow < MT ? mrow : MT;  // rows past MT read the zero row
   const uint8_t* xr = sb + mrow_s * xrow + half * CPH * SPAN * 2;
+  const uint8_t* xsp = sb + mrow_s * xrow + half * 16;  // 2:4: lane half h' reads k 8h'..8h'+7 of each 16-k segment
   if constexpr (BM) {
     // kept-byte windows: lane half h's chunk of pass p starts after the slice's
     // earlier kept values and, for h = 1, after its partner's (lane l - 32) chunk
@@ -434,8 +456,33 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
     if (p >= a.npw) return;
 #pragma unroll
     for (int q = 0; q < CPH; ++q) {
-      uint32_t wp[P];
       const uint32_t ww[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+      if constexpr (SP) {
+        // word i of the chunk holds the kept pairs of groups 4i..4i+3 (16 k of
+        // the row) and meta bits 16 (i mod 2).. of word i / 2 their positions:
+        // one sparse step per word, lane half 1 on the chunk four later
+        const uint8_t* x0 = xsp + (p * PASSK + q * SPAN) * 2;
+        const uint8_t* x1 = xsp + (p * PASSK + (CPH + q) * SPAN) * 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t v[4];
+          int4_word(ww[i], v);
+          if constexpr (BF16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const half2_t hv = as_h2(v[j]);
+              v[j] = mf_to16<true>((float)hv.x) | (mf_to16<true>((float)hv.y) << 16);
+            }
+          }
+          const uint4 av = make_uint4(v[0], v[1], v[2], v[3]);
+          const uint4 b0 = *reinterpret_cast<const uint4*>(x0 + 32 * i);
+          const uint4 b1 = *reinterpret_cast<const uint4*>(x1 + 32 * i);
+          const uint32_t idx = i < 2 ? mw[q].x : mw[q].y;
+          acc = (i & 1) ? mf_smfmac<BF16, 1>(av, b0, b1, idx, acc) : mf_smfmac<BF16, 0>(av, b0, b1, idx, acc);
+        }
+        continue;
+      }
+      uint32_t wp[P];
       if constexpr (KIND == K_LUT3) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) lut3_word_perm(ww[i], T3, &wp[5 * i]);
@@ -478,9 +525,14 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
 
   }
   // lane l holds row rt for activation rows m(v) = 8 (v / 4) + 4 half + v mod 4
+  // (2:4: transposed, brought back below, after the outliers)
+  const mf_f32x16 dsum = acc;
   // ---- integer formats: the row scale multiplies the dense part only ----
-  if constexpr (!LUT) {
-    const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)scale16);
+  const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)scale16);
+  if constexpr (SP) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  } else if constexpr (!LUT) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] *= sc;
   }
@@ -503,6 +555,19 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
 #pragma unroll
       for (int v = 0; v < NV; ++v) acc[v] = __builtin_fmaf(val, mf_act<BF16>(lds_u16(sdyn, moff[v] + kk2)), acc[v]);
     }
+  }
+  if constexpr (SP) {
+    // the dense sums to this lane's row through LDS (each wave's own 32 x 33
+    // floats of the activation slice's space, free once every wave is past
+    // the outliers), times the row scale, plus the outliers
+    __syncthreads();
+    float* tr = reinterpret_cast<float*>(sb) + wave * (32 * 33);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tr[(8 * (v >> 2) + 4 * half + (v & 3)) * 33 + (lane & 31)] = dsum[v];
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = __builtin_fmaf(tr[(lane & 31) * 33 + 8 * (v >> 2) + 4 * half + (v & 3)], sc, acc[v]);
+    __syncthreads();  // the space is reused below (t, the last-arrival flag)
   }
   // ---- rank term (last slice): [t_hi | t_lo] x [R^T | R^T] on the matrix cores ----
   if (a.r16 != nullptr && z == a.S - 1) {
@@ -599,6 +664,7 @@ static hipError_t launch_mfma_t(const MfArgs& a, hipStream_t st) {
   const int lds_l = a.lr_wgs > 0 ? lr_scratch_bytes(a.lr_mode, kMfLrTile) : 0;  // prologue workgroups
   int lds = lds_x > lds_t ? lds_x : lds_t;
   lds = lds > lds_l ? lds : lds_l;
+  if constexpr (KIND == K_INT4_24) lds = lds > 4 * 32 * 33 * 4 ? lds : 4 * 32 * 33 * 4;  // the 2:4 transposition
   hipLaunchKernelGGL((decode_mfma_kernel<KIND, BF16, MT>), dim3(a.lr_wgs + a.tiles * a.S), dim3(256), lds, st, a);
   return hipGetLastError();
 }
