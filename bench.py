@@ -45,7 +45,8 @@ ROTATE_BYTES = 1 << 30
 # counter summaries of HBM traffic per workload (committed under profiles/), each
 # valid only for the kernel sources it was taken with
 TRAFFIC_FILES = {(5, 1): os.path.join(ROOT, "profiles", "decode_lut3_lr_llama70b_b1_traffic.txt"),
-                 (2, 1): os.path.join(ROOT, "profiles", "decode_lut4_llama7b_b1_traffic.txt")}
+                 (2, 1): os.path.join(ROOT, "profiles", "decode_lut4_llama7b_b1_traffic.txt"),
+                 (3, 1): os.path.join(ROOT, "profiles", "decode_int4_24_lr128_b1_traffic.txt")}
 KERNEL_SOURCES = ["compressed_linear_amd/csrc/decode_rows.h", "compressed_linear_amd/csrc/unpack.h",
                   "compressed_linear_amd/csrc/decode.hip", "compressed_linear_amd/csrc/layout.h",
                   "compressed_linear_amd/csrc/lowrank.h", "compressed_linear_amd/csrc/decode_stream.h"]

@@ -373,15 +373,11 @@ __global__ void __launch_bounds__(1024) decode_stream_kernel(StreamArgs sa) {
         if (j * NB + q < np) pass(w[q], mw[q], j * NB + q);
     }
   };
-  // first round of blocks; then the data the finalisation needs goes to LDS
-  // (loaded before the code stream, so it has arrived with the first blocks)
-#pragma unroll
-  for (int b = 0; b < NBUF; ++b) {
-    comp_blk(W[b], MW[b], b);
-    load_blk(W[b], MW[b], b + NBUF);
-  }
-  // (the staged values are stored as loaded: an operation on them here would
-  // let the compiler move it, and its wait, up to the loads, behind the code stream)
+  // Row pointers and rank-factor rows go to LDS now: they were asked for
+  // before the code stream, so waiting for them waits for none of it (loads
+  // complete in order), and their registers are free for the walk.  (They
+  // are stored as loaded: an operation on them here would let the compiler
+  // move it, and its wait, up to the loads.)
   if (tid <= rw) *reinterpret_cast<uint32_t*>(sb + sa.lds_rp + 4 * tid) = rpv;
   if constexpr (LR) {
     const uint32_t kb = (uint32_t)rw * (uint32_t)sa.rank_row_bytes;
@@ -392,6 +388,13 @@ __global__ void __launch_bounds__(1024) decode_stream_kernel(StreamArgs sa) {
     }
     if (lr4 && (uint32_t)(16 * tid) < (uint32_t)rw * (uint32_t)sa.rsc_row_bytes)
       *reinterpret_cast<uint4*>(sb + sa.lds_rsc + 16 * tid) = ksv;
+  }
+  // first round of blocks; then the outliers (asked for after the first
+  // blocks of the code stream) go to LDS
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b) {
+    comp_blk(W[b], MW[b], b);
+    load_blk(W[b], MW[b], b + NBUF);
   }
   if (has_csr) {
     uint16_t* ocol = reinterpret_cast<uint16_t*>(sb + sa.lds_out);
