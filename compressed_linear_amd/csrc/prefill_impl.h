@@ -120,6 +120,26 @@ __device__ __forceinline__ void pf_st128(uint32_t* lds, uint32_t byte_addr, uint
   *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(lds) + byte_addr) = v;
 }
 
+typedef __bf16 pf_bf16x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 pf_f16x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t pf_u32x8 __attribute__((ext_vector_type(8)));
+
+// 2:4 weights on the sparse-A instruction (v_smfmac_f32_32x32x32): w holds the
+// eight kept values of lane (weight row l mod 32, half h) -- the kept pairs of
+// four consecutive groups of four k -- and idx (bits 16 ABID ..) their 2-bit
+// positions; the activation operand of lane half h' is x at 8h'..8h'+7 of
+// lane half 0's 16 k (x0) and of lane half 1's (x1).  The output holds weight
+// rows along the lane's registers and activation rows along the lanes.
+template <bool BF16, int ABID>
+__device__ __forceinline__ pf_f32x16 pf_smfmac(uint4 w, uint4 x0, uint4 x1, uint32_t idx, pf_f32x16 c) {
+  const pf_u32x8 b = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  if constexpr (BF16)
+    return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(pf_bf16x8, w), __builtin_bit_cast(pf_bf16x16, b), c,
+                                                     (int)idx, 0, ABID);
+  return __builtin_amdgcn_smfmac_f32_32x32x32_f16(__builtin_bit_cast(pf_f16x8, w), __builtin_bit_cast(pf_f16x16, b), c,
+                                                  (int)idx, 0, ABID);
+}
+
 template <bool BF16>
 __device__ __forceinline__ pf_f32x16 pf_mfma(uint4 a, uint4 b, pf_f32x16 c) {
   if constexpr (BF16)
@@ -146,10 +166,20 @@ __device__ __forceinline__ void pf_add_outlier(uint32_t* smem, uint32_t btile, u
                                           __builtin_bit_cast(pf_f16x2, pk));
 }
 
-template <int KIND, bool BF16>
+// SP: INT4 2:4 without outliers on the sparse-A instruction.  The staging
+// waves write each weight row's step as its 64 kept values in the MFMA type
+// and its 2-bit positions (no zeros), the MFMA waves take half as many steps,
+// and the accumulators hold the output transposed (weight rows along the
+// registers); the rank steps then run with the weights as the first operand.
+template <int KIND, bool BF16, bool SP = false>
 __global__ void __launch_bounds__(2 * kPfThreads, 1) prefill_kernel(PfArgs a) {
   using C = PfCfg<KIND>;
   constexpr int BK = C::bk, TS = C::ts, SPAN = C::span, BUF = C::buf;
+  static_assert(!SP || (KIND == K_INT4_24 && BK == 128), "the sparse tile holds one 128-k step of 2:4 rows");
+  // sparse tile row: 64 kept values (128 bytes), then for each of the two
+  // chunks a position word per MFMA lane half (16 bytes); 144 = 16 * 9 keeps
+  // 16-byte reads of consecutive rows on distinct banks
+  constexpr int TSS = 144;
   constexpr bool CODES = KIND != K_DENSE16;
   constexpr bool LUT = KIND == K_LUT3 || KIND == K_LUT4;
   constexpr int A_OFF = C::tab, B_OFF = C::tab + 128 * TS;  // tile buffer b at + b * BUF
@@ -285,7 +315,25 @@ __global__ void __launch_bounds__(2 * kPfThreads, 1) prefill_kernel(PfArgs a) {
         pf_st128(smem, bo + (uint32_t)(A_OFF + m * TS + kk * 16), st.xa[i]);
       }
       const uint32_t brow = bo + (uint32_t)(B_OFF + nl * TS + half * C::vpt * 2);
-      if constexpr (CODES) {
+      if constexpr (SP) {
+        // this thread's chunk (64 k): word i holds the kept pairs of groups
+        // 4i..4i+3, meta word j the positions of groups 8j..8j+7; position
+        // words regrouped so that MFMA lane half h finds its bits of both of
+        // the chunk's 32-k steps in one word (ABID 0 and 1)
+        const uint32_t srow = bo + (uint32_t)(B_OFF + nl * TSS);
+        const uint32_t ww[4] = {st.wb[0].x, st.wb[0].y, st.wb[0].z, st.wb[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t v[4];
+          int4_word(ww[i], v);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = scale_pair16<BF16>(v[j], rscale);
+          pf_st128(smem, srow + (uint32_t)(half * 64 + 16 * i), make_uint4(v[0], v[1], v[2], v[3]));
+        }
+        const uint32_t m0w = st.wm[0].x, m1w = st.wm[0].y;
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(smem) + srow + 128u + (uint32_t)(half * 8)) =
+            make_uint2((m0w & 0xFFFFu) | (m1w << 16), (m0w >> 16) | (m1w & 0xFFFF0000u));
+      } else if constexpr (CODES) {
 #pragma unroll
         for (int q = 0; q < C::cpt; ++q) {
           uint32_t wp[KindTraits<KIND>::pairs];
@@ -398,18 +446,84 @@ __global__ void __launch_bounds__(2 * kPfThreads, 1) prefill_kernel(PfArgs a) {
       acc[1][1] = pf_mfma<BF16>(a1, b1, acc[1][1]);
     }
   };
+  // SP: acc[j][i] = weight block j x activation block i (transposed output)
+  const uint32_t srow0 = (uint32_t)(B_OFF + (wn_ * 64 + (lane & 31)) * TSS + (lane >> 5) * 16);  // kept values
+  const uint32_t prow0 = (uint32_t)(B_OFF + (wn_ * 64 + (lane & 31)) * TSS + 128 + (lane >> 5) * 4);  // position words
+  const uint32_t xrow0 = (uint32_t)(A_OFF + (wm_ * 64 + (lane & 31)) * TS + (lane >> 5) * 16);  // activations
+  auto smma = [&](int buf, int c) {  // the two 32-k steps of chunk c
+    const uint32_t bo = (uint32_t)(buf * BUF);
+    const uint32_t p0 = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(smem) + bo + prow0 + 8 * c);
+    const uint32_t p1 =
+        *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(smem) + bo + prow0 + 32 * TSS + 8 * c);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = 2 * c + u;
+      const uint4 w0 = pf_lds128(smem, bo + srow0 + q * 32), w1 = pf_lds128(smem, bo + srow0 + 32 * TSS + q * 32);
+      const uint4 x0a = pf_lds128(smem, bo + xrow0 + q * 64), x0b = pf_lds128(smem, bo + xrow0 + q * 64 + 32);
+      const uint4 x1a = pf_lds128(smem, bo + xrow0 + 32 * TS + q * 64),
+                  x1b = pf_lds128(smem, bo + xrow0 + 32 * TS + q * 64 + 32);
+      if (u == 0) {
+        acc[0][0] = pf_smfmac<BF16, 0>(w0, x0a, x0b, p0, acc[0][0]);
+        acc[0][1] = pf_smfmac<BF16, 0>(w0, x1a, x1b, p0, acc[0][1]);
+        acc[1][0] = pf_smfmac<BF16, 0>(w1, x0a, x0b, p1, acc[1][0]);
+        acc[1][1] = pf_smfmac<BF16, 0>(w1, x1a, x1b, p1, acc[1][1]);
+      } else {
+        acc[0][0] = pf_smfmac<BF16, 1>(w0, x0a, x0b, p0, acc[0][0]);
+        acc[0][1] = pf_smfmac<BF16, 1>(w0, x1a, x1b, p0, acc[0][1]);
+        acc[1][0] = pf_smfmac<BF16, 1>(w1, x0a, x0b, p1, acc[1][0]);
+        acc[1][1] = pf_smfmac<BF16, 1>(w1, x1a, x1b, p1, acc[1][1]);
+      }
+    }
+  };
+  auto mma_t = [&](int buf, int ks0, int ks1) {  // dense steps with the weights first (SP's rank steps)
+    const uint32_t bo = (uint32_t)(buf * BUF);
+#pragma unroll
+    for (int ks = ks0; ks < ks1; ++ks) {
+      const uint4 a0 = pf_lds128(smem, bo + arow + ks * 32), a1 = pf_lds128(smem, bo + arow + 32 * TS + ks * 32);
+      const uint4 b0 = pf_lds128(smem, bo + brow0 + ks * 32), b1 = pf_lds128(smem, bo + brow0 + 32 * TS + ks * 32);
+      acc[0][0] = pf_mfma<BF16>(b0, a0, acc[0][0]);
+      acc[0][1] = pf_mfma<BF16>(b0, a1, acc[0][1]);
+      acc[1][0] = pf_mfma<BF16>(b1, a0, acc[1][0]);
+      acc[1][1] = pf_mfma<BF16>(b1, a1, acc[1][1]);
+    }
+  };
+  const int sdm = max(s0, min(s1, a.nsteps_dense));  // the last weight step + 1 (rank steps after it)
   __syncthreads();  // first staged step: tile landed
   __syncthreads();  // its outliers added
   for (int s = s0; s < s1; ++s) {
     const int buf = (s - s0) & 1;
-    mma(buf, 0, (BK / 16) / 2);
-    __syncthreads();
-    mma(buf, (BK / 16) / 2, BK / 16);
+    if constexpr (SP) {
+      if (s < sdm) smma(buf, 0);
+      else mma_t(buf, 0, (BK / 16) / 2);
+      __syncthreads();
+      if (s < sdm) smma(buf, 1);
+      else mma_t(buf, (BK / 16) / 2, BK / 16);
+    } else {
+      mma(buf, 0, (BK / 16) / 2);
+      __syncthreads();
+      mma(buf, (BK / 16) / 2, BK / 16);
+    }
     __syncthreads();
   }
 
   // ---- store: lane l of block (i, j) holds column n = l mod 32, rows 8 (v/4) + 4 (l/32) + v mod 4 ----
   float* yz = a.y + (size_t)blockIdx.z * a.ystride;
+  if constexpr (SP) {
+    // acc[j][i]: lane l holds activation row m = l mod 32 of block i for
+    // weight rows 8 (v/4) + 4 (l/32) + v mod 4 of block j
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int m = m0 + wm_ * 64 + i * 32 + (lane & 31);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int nn = n0 + wn_ * 64 + j * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (m < a.M && nn < a.ncols) yz[(size_t)m * a.ldy + nn] = acc[j][i][v];
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -428,6 +542,12 @@ hipError_t launch_prefill_t(const PfArgs& a, hipStream_t st) {
   if (a.cptr && a.nsteps_dense > kPfMaxSteps) return hipErrorInvalidValue;
   const int z = (int)ceil_div(a.nsteps, a.steps_per_split);
   dim3 grid((unsigned)ceil_div(a.ncols, kPfBN), (unsigned)ceil_div(a.M, kPfBM), (unsigned)z);
+  if constexpr (KIND == K_INT4_24) {
+    if (a.cptr == nullptr) {  // no outliers: the sparse-A instruction takes the stored 2:4 form
+      hipLaunchKernelGGL((prefill_kernel<KIND, BF16, true>), grid, dim3(2 * kPfThreads), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((prefill_kernel<KIND, BF16>), grid, dim3(2 * kPfThreads), 0, st, a);
   return hipGetLastError();
 }

@@ -102,7 +102,7 @@ def check_route(mod, layer, ks, route, what):
     return int(bad.size)
 
 
-def small_layer(fmt, x_dtype, K, N=200, seed=0):
+def small_layer(fmt, x_dtype, K, N=200, seed=0, csr=True):
     r = np.random.default_rng([31, seed, K, N])
     kw = dict(K=K, N=N, x_dtype=x_dtype, name=f"{fmt}/{x_dtype}/{K}x{N}")
     if fmt in ("lut3", "lut4"):
@@ -121,8 +121,9 @@ def small_layer(fmt, x_dtype, K, N=200, seed=0):
             kw.update(mask="bitmap", keep=draw_mask_half(r, N, K))
         if dense == "int8":
             kw["act_clamp"] = np.float16(6.0)  # raw activations edited while staging (1 < 6: unchanged)
-    rp, col, val = draw_csr(r, r, N, K, density=0.01)
-    kw.update(csr_row_ptr=rp, csr_col=col, csr_val=val)
+    if csr:
+        rp, col, val = draw_csr(r, r, N, K, density=0.01)
+        kw.update(csr_row_ptr=rp, csr_col=col, csr_val=val)
     return LogicalLayer(**kw)
 
 
@@ -159,6 +160,25 @@ def test_every_route_bit_exact_small(fmt, x_dtype, K):
                 ks = np.unique(np.r_[0, 1, 39, 40, 63, 64, K - 2, K - 1, np.random.default_rng(K).integers(0, K, 24)])
             say(layer.name, route, len(ks))
             check_route(mod, layer, ks, route, layer.name)
+    finally:
+        mod.close()
+
+
+# INT4 2:4 without outliers (SLiM's form): the prefill runs it on the sparse-A
+# instruction with the stored kept values and positions (no zero expansion);
+# the matrix-core decode does so with or without outliers.  K = 1204: 19
+# chunks (the last 128-k step holds one); K = 260: 5 chunks; N = 200 leaves a
+# partial 128-row tile.
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("K", [1208, 1204, 260])
+def test_2_4_sparse_instruction_bit_exact(x_dtype, K):
+    from gpu_util import gpu_layer
+    layer = small_layer("int4_24", x_dtype, K, seed=1, csr=False)
+    mod = gpu_layer(layer, max_M=K)
+    try:
+        for route in ("mfma", "prefill"):
+            say(layer.name, "no outliers", route)
+            check_route(mod, layer, np.arange(K), route, layer.name + " no outliers")
     finally:
         mod.close()
 
