@@ -194,8 +194,9 @@ static StreamPlanH plan_stream_k(const cl_blob_header& h, const int32_t* rp, int
     off += a16((size_t)RW * TB);
     t.lds_rp = (int)off;
     off += a16((size_t)(RW + 1) * 4);
+    const int rrs = rrb >= 16 && (rrb & (rrb - 1)) == 0 ? rrb + 16 : rrb;  // padded: rows read together on other banks
     t.lds_rank = (int)off;
-    off += a16((size_t)RW * rrb);
+    off += a16((size_t)RW * rrs);
     t.lds_rsc = (int)off;
     off += a16((size_t)RW * rscb);
     t.lds_part0 = (int)off;
@@ -215,6 +216,7 @@ static StreamPlanH plan_stream_k(const cl_blob_header& h, const int32_t* rp, int
     t.lds = (int)dyn;
     t.out_cap = cap;
     t.rank_row_bytes = rrb;
+    t.rank_row_stride = rrs;
     t.rsc_row_bytes = rscb;
     return t;
   }
@@ -335,6 +337,7 @@ static hipError_t launch_decode_stream(const Layer& L, const void* x, float* y, 
   s.lds_out = p.lds_out;
   s.lds_t = p.lds_t;
   s.rank_row_bytes = p.rank_row_bytes;
+  s.rank_row_stride = p.rank_row_stride;
   s.rsc_row_bytes = p.rsc_row_bytes;
   s.out_cap = p.out_cap;
   s.lr_readers = p.nwg;

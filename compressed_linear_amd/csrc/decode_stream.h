@@ -57,6 +57,8 @@ struct StreamArgs {
   int lds_out;          //   outliers: out_cap 16-bit columns, then out_cap fp16 values,
   int lds_t;            //   t = x' L_hat (rank floats)
   int rank_row_bytes;   // bytes of one R^T row (16-bit: 2 rank, int4: ceil(rank / 2))
+  int rank_row_stride;  // its LDS stride: 16 bytes more when a power of two of at least 16
+                        // (rows that a wavefront reads together then fall on different banks)
   int rsc_row_bytes;    // bytes of one row of int4 R^T scales
   int out_cap;          // outlier entries staged per workgroup (<= threads * kStOutLoads)
   int lr_readers;       // readers of t in a recorded launch (one per row workgroup)
@@ -380,11 +382,15 @@ __global__ void __launch_bounds__(1024) decode_stream_kernel(StreamArgs sa) {
   // move it, and its wait, up to the loads.)
   if (tid <= rw) *reinterpret_cast<uint32_t*>(sb + sa.lds_rp + 4 * tid) = rpv;
   if constexpr (LR) {
-    const uint32_t kb = (uint32_t)rw * (uint32_t)sa.rank_row_bytes;
+    const uint32_t rrb = (uint32_t)sa.rank_row_bytes, kb = (uint32_t)rw * rrb;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t o = 16u * (uint32_t)(tid + i * nthr);
-      if (o < kb) *reinterpret_cast<uint4*>(sb + sa.lds_rank + o) = kv[i];
+      // padded rows have a power-of-two length: row and offset by shifts
+      const uint32_t lo = sa.rank_row_stride != sa.rank_row_bytes
+                              ? (o >> __builtin_ctz(rrb)) * (uint32_t)sa.rank_row_stride + (o & (rrb - 1u))
+                              : o;
+      if (o < kb) *reinterpret_cast<uint4*>(sb + sa.lds_rank + lo) = kv[i];
     }
     if (lr4 && (uint32_t)(16 * tid) < (uint32_t)rw * (uint32_t)sa.rsc_row_bytes)
       *reinterpret_cast<uint4*>(sb + sa.lds_rsc + 16 * tid) = ksv;
@@ -462,7 +468,7 @@ __global__ void __launch_bounds__(1024) decode_stream_kernel(StreamArgs sa) {
     return __builtin_fmaf((float)__builtin_bit_cast(_Float16, a.val[E0 + e]), x_lds((int)a.col[E0 + e]), v);
   };
   auto rank_term = [&](int rl, int j, float v) -> float {  // v + R^T[row rl][j] (staged in LDS) * t_j
-    const uint8_t* rrow = sb + sa.lds_rank + rl * sa.rank_row_bytes;
+    const uint8_t* rrow = sb + sa.lds_rank + rl * sa.rank_row_stride;
     float rvv;
     if (lr4) {
       const uint32_t byte = rrow[j >> 1];
@@ -534,8 +540,40 @@ __global__ void __launch_bounds__(1024) decode_stream_kernel(StreamArgs sa) {
         for (; e < e1; e += 8) v = outlier_mem(e, v);
       }
       if constexpr (BF16) v = xfinite ? v * xunscale : __builtin_nanf("");
-      if constexpr (LR)
-        for (int j = u; j < a.rank; j += 8) v = rank_term(rl, j, v);
+      if constexpr (LR) {
+        const int rpt = a.rank >> 3;  // rank terms a thread: a contiguous run of them
+        const uint32_t rrow = (uint32_t)(sa.lds_rank + rl * sa.rank_row_stride);
+        if (!lr4 && (a.rank & 31) == 0) {  // 16-bit factors, four terms at a time
+          for (int j = u * rpt; j < (u + 1) * rpt; j += 4) {
+            const uint2 r4 = lds_u64(sdyn, rrow + 2 * j);
+            const float4 t4 = *reinterpret_cast<const float4*>(st + j);
+            const uint32_t rr[2] = {r4.x, r4.y};
+            float f[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t h = (rr[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
+              f[q] = a.lr_kind == CL_LR_BF16 ? __uint_as_float(h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+            }
+            v = __builtin_fmaf(t4.x, f[0], v);
+            v = __builtin_fmaf(t4.y, f[1], v);
+            v = __builtin_fmaf(t4.z, f[2], v);
+            v = __builtin_fmaf(t4.w, f[3], v);
+          }
+        } else if (lr4 && (a.rank & 63) == 0 && (a.group & 7) == 0) {  // int4 factors, eight terms (one scale) at a time
+          for (int j = u * rpt; j < (u + 1) * rpt; j += 8) {
+            const uint32_t b8 = lds_u32(sdyn, rrow + j / 2);
+            const uint32_t jg = ((uint32_t)j * a.group_mul) >> 16;
+            const float sc = (float)__builtin_bit_cast(
+                _Float16, (uint16_t)lds_u16(sdyn, (uint32_t)(sa.lds_rsc + rl * sa.rsc_row_bytes + 2 * jg)));
+            const float4 t0 = *reinterpret_cast<const float4*>(st + j), t1 = *reinterpret_cast<const float4*>(st + j + 4);
+            const float tq[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v = __builtin_fmaf(tq[q], (float)((int)((b8 >> (4 * q)) & 0xFu) - 8) * sc, v);
+          }
+        } else {
+          for (int j = u; j < a.rank; j += 8) v = rank_term(rl, j, v);
+        }
+      }
     }
     // the eight threads of the row: quad swaps, then the mirrored quad of each half row
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]

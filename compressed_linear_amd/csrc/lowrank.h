@@ -227,11 +227,11 @@ __device__ __forceinline__ float dot2_act(uint32_t a, uint32_t b, float c) {
 }
 
 // NT = threads of a prologue block.  A thread loads NL 16-byte pieces of the
-// slice: 16 of fp16 / bf16 factors, 4 of int4 ones (2 in a 1024-thread block,
+// slice: 16 of fp16 / bf16 factors, 4 of int4 ones (1 in a 1024-thread block,
 // whose dequantisation would otherwise outlast the rest of the launch), so the
 // slice has 2 (NT / 16) NL rows (16-bit) or 2 (NT / 4) NL rows (int4).
 template <int MODE, int NT>
-constexpr int lr_loads() { return MODE == 0 ? 16 : NT == 1024 ? 2 : 4; }
+constexpr int lr_loads() { return MODE == 0 ? 16 : NT == 1024 ? 1 : 4; }
 template <int MODE, int NT>
 constexpr int lr_slice_rows() { return 2 * (NT / (MODE == 0 ? 16 : 4)) * lr_loads<MODE, NT>(); }
 static_assert(lr_slice_rows<0, 256>() == kLrSlice && lr_slice_rows<1, 256>() == kLrSlice, "256-thread slices");
