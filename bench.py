@@ -92,9 +92,9 @@ def read_traffic(cfg: int, M: int):
 def batch1_kernel(l, acct) -> str:
     """The kernel a batch-1 forward of layer l runs on the auto path: the
     streaming kernel for layers of 28 MiB of code chunks or more, or with a
-    rank term and K < N (the library's rule in decode.hip), the row-wise kernel
+    rank term (the library's rule in decode.hip), the row-wise kernel
     otherwise."""
-    stream = acct["codes"] >= (28 << 20) or (bool(l.rank) and l.K < l.N)
+    stream = acct["codes"] >= (28 << 20) or bool(l.rank)
     return "decode_stream_kernel" if stream else "decode_rows_kernel"
 
 

@@ -232,13 +232,12 @@ static StreamPlanH plan_stream_k(const cl_blob_header& h, const int32_t* rp, int
 // MI355X (us per layer, streaming / row-wise): LLaMA-70B LUT3 + bf16 rank 64
 // 8192 -> 10240 (32 MiB of codes) 16.1 / 16.6, 8192 -> 28672 29.5 / 37.9,
 // 28672 -> 8192 30.4 / 36.9; INT4 2:4 + int4 rank 128 4096 -> 11008 (11 MiB)
-// 12.6 / 15.3, 11008 -> 4096 15.3 / 14.9; LLaMA-7B LUT4 4096 -> 12288 (24 MiB)
-// 11.6 / 9.2; LUT3 4096 -> 4096 7.6 / 4.9.  The streaming kernel takes layers
-// of 28 MiB of codes or more, and layers with a rank term whose rows are
-// shorter than their count (K < N: the walk outlasts the prologue).
+// 10.5 / 15.3, 11008 -> 4096 14.2 / 14.9; LLaMA-7B LUT4 4096 -> 12288 (24 MiB)
+// 12.5 / 9.8; LUT3 4096 -> 4096 7.3 / 4.9.  The streaming kernel takes layers
+// of 28 MiB of codes or more, and layers with a rank term.
 static bool stream_wins(const cl_blob_header& h) {
   const bool lr = h.lr != CL_LR_NONE && h.rank > 0;
-  return (unsigned long long)h.N * h.chunks * 16ull >= (28ull << 20) || (lr && h.K < h.N);
+  return (unsigned long long)h.N * h.chunks * 16ull >= (28ull << 20) || lr;
 }
 
 StreamPlanH plan_stream(const cl_blob_header& h, const int32_t* rowptr, int num_cus, int lr_mode) {

@@ -72,7 +72,8 @@ struct Layer {
   int lr_S = 0;                  // K slices of kLrSlice rows
   uint8_t* lr_lk = nullptr;      // L, k-major in k pairs: 16-bit [Kl/2][rpad][2]; int4 bytes [Kl/2][rpad] (k even low nibble)
   uint16_t* lr_ls = nullptr;     // int4: scales k-major [ceil(Kl/group)][rpad]
-  float* lr_part = nullptr;      // partial sums [tiles][S][256]
+  float* lr_part = nullptr;      // partial sums [tiles][S][256] (tagged 64-bit words in the streaming kernel)
+  size_t lr_part_bytes = 0;
   mutable uint32_t lr_epoch = 0; // epochs of direct calls with the prologue inside (never 0)
   uint32_t* lr_cnt = nullptr;    // [kLrCntWords]: arrivals per output tile [0, 64), completed tiles [64],
                                  // published epoch [65], published generation [66], finished

@@ -105,7 +105,7 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
     if (h.mask == CL_MASK_BITMAP) o_mfz = take((size_t)Npad * mf_S * 4);
   }
   // decode low-rank prologue: k-major copy of L, partial sums, arrival counters
-  size_t o_lk = 0, o_ls = 0, o_lp = 0, o_lc = 0;
+  size_t o_lk = 0, o_ls = 0, o_lp = 0, o_lc = 0, lp_bytes = 0;
   const int lr_mode = lowrank_mode(h);
   const int lr_rpad = (int)round_up(h.rank > 0 ? h.rank : 1, 64), lr_S = (int)ceil_div(h.K, kLrSlice);
   if (has_lr && lr_mode >= 0) {
@@ -113,7 +113,8 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
     o_lk = take(lr_mode == 0 ? Kl * lr_rpad * 2 : Kl / 2 * lr_rpad);
     if (lr_mode == 1) o_ls = take((size_t)ceil_div(Kl, h.group) * lr_rpad * 2);
     const int mt = (int)ceil_div(max_M < kMaxDecodeM ? max_M : kMaxDecodeM, 4);
-    o_lp = take((size_t)(lr_rpad / 64) * mt * lr_S * 256 * 4);
+    lp_bytes = (size_t)(lr_rpad / 64) * mt * lr_S * 256 * 4;
+    o_lp = take(lp_bytes);
     o_lc = take(kLrCntWords * 4);
   }
   if (L) {
@@ -124,6 +125,7 @@ size_t workspace_layout(const cl_blob_header& h, int32_t max_M, Layer* L, size_t
     L->lr_lk = o_lk ? d + o_lk : nullptr;
     L->lr_ls = o_ls ? reinterpret_cast<uint16_t*>(d + o_ls) : nullptr;
     L->lr_part = o_lp ? reinterpret_cast<float*>(d + o_lp) : nullptr;
+    L->lr_part_bytes = lp_bytes;
     L->lr_cnt = o_lc ? reinterpret_cast<uint32_t*>(d + o_lc) : nullptr;
     L->counters = reinterpret_cast<uint32_t*>(d + o_cnt);
     L->part = reinterpret_cast<float*>(d + o_part);
@@ -466,6 +468,10 @@ extern "C" cl_status cl_create(const void* blob, void* dev_buf, size_t dev_bytes
   if (e == hipSuccess && !lrk.empty()) e = hipMemcpyAsync(L->lr_lk, lrk.data(), lrk.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !lrs.empty()) e = hipMemcpyAsync(L->lr_ls, lrs.data(), lrs.size() * 2, hipMemcpyHostToDevice, s);
   if (e == hipSuccess && L->lr_cnt) e = hipMemsetAsync(L->lr_cnt, 0, kLrCntWords * 4, s);
+  // the tagged partial sums of t: tag 0 matches no launch (epochs start at 1,
+  // recorded launches carry the top bit), so words that an earlier layer left
+  // in this memory cannot pass for this layer's
+  if (e == hipSuccess && L->lr_part) e = hipMemsetAsync(L->lr_part, 0, L->lr_part_bytes, s);
   if (e == hipSuccess) e = hipMemsetAsync(L->counters, 0, (size_t)(h->n_tiles + ceil_div(max_M, 32) + 8) * 4, s);
   if (e == hipSuccess && !nzs.empty())
     e = hipMemcpyAsync(L->nzstart, nzs.data(), nzs.size() * 4, hipMemcpyHostToDevice, s);

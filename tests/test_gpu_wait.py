@@ -60,3 +60,39 @@ def test_wait_give_up_is_reported(cfg, M, path, K):
         check_bound(y.cpu().numpy().astype(np.float64), layer, x, what="after")
     finally:
         mod.close()
+
+
+# A layer created in memory where an earlier layer of the same shape ran the
+# batch-1 streaming kernel: every new layer's first forward has epoch 1, so
+# tagged partial sums of t left there by the earlier layer carry the tag the
+# new layer's readers wait for, unless cl_create clears them.  Short rows make
+# the readers ask for t before the new launch's prologue has written it, so a
+# stale value shows (a large activation makes the two layers' t differ by far
+# more than the bound).
+@pytest.mark.parametrize("cfg,K", [(5, 8200), (3, 4160)])
+def test_stream_kernel_tags_cleared_at_create(cfg, K):
+    import ctypes
+    from synth.layers import bf16_bits_from_f32
+    torch = torch_cuda()
+    layer = make_layer(cfg, 0, K=K, N=190)
+    blob, _ = cla.pack(layer)
+    L = cla.lib()
+    n = L.cl_device_bytes(blob.ctypes.data, 1)
+    buf = torch.empty(n + 256, dtype=torch.uint8, device="cuda")
+    base = buf.data_ptr() + ((-buf.data_ptr()) % 256)
+    stream = torch.cuda.current_stream().cuda_stream
+    x0 = make_x(cfg, 0, 1, K=K)
+    x1 = x0.copy()
+    big = 3.0e5 if layer.x_dtype == "bf16" else 3.0e4
+    x1[0, K // 3] = bf16_bits_from_f32(np.array([big], np.float32))[0] if layer.x_dtype == "bf16" else np.float16(big)
+    say("tags cleared at create", cfg, K)
+    for trial in range(3):
+        for i, x in enumerate((x0, x1)):
+            h = ctypes.c_void_p()
+            assert L.cl_create(blob.ctypes.data, base, n, 1, stream, ctypes.byref(h)) == 0
+            xd = to_device_x(x, layer.x_dtype)
+            y = torch.empty((1, layer.N), dtype=torch.float32, device="cuda")
+            assert L.cl_forward_path(h, 1, xd.data_ptr(), y.data_ptr(), stream, cla.PATH["decode_stream"]) == 0
+            torch.cuda.synchronize()
+            assert L.cl_destroy(h) == 0
+            check_bound(y.cpu().numpy().astype(np.float64), layer, x, what=f"trial {trial} x{i}")
