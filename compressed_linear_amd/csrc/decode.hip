@@ -167,9 +167,15 @@ static StreamPlanH plan_stream_k(const cl_blob_header& h, const int32_t* rp, int
     if (stream_slots_per_thread<KIND>(C, threads) > 12) continue;
     // the prologue workgroups (the launch's first) hold their CUs while they
     // run: the row workgroups take the others, so that none waits for a CU
-    const int lr_wgs = (lr && lr_mode >= 0) ? stream_lr_slices((int)ceil_div(h.K, kLrSlice), threads, lr_mode) *
-                                                  (int)ceil_div(h.rank, 64) : 0;
-    const size_t lr_lds = lr_wgs ? (size_t)lr_scratch_bytes(lr_mode, 1, threads == 1024 ? 1024 : 256) : 0;
+    // int4 factors in 1024-thread blocks: 512-row slices while that needs at
+    // most 16 blocks, else 2048-row ones (fewer CUs taken from the rows; their
+    // longer dequantisation still ends before the walk).  Measured, SLiM int4
+    // rank 128, us per layer with 512 / 1024 / 2048-row slices: 4096 -> 11008
+    // 10.5 / 10.9 / 13.4, 11008 -> 4096 14.1 / 13.9 / 13.6.
+    const int lr_S = (int)ceil_div(h.K, kLrSlice), ntj = (int)ceil_div(h.rank, 64);
+    const int nl = (lr && lr_mode == 1 && threads == 1024 && stream_lr_slices(lr_S, threads, 1, 1) * ntj > 16) ? 4 : 1;
+    const int lr_wgs = (lr && lr_mode >= 0) ? stream_lr_slices(lr_S, threads, lr_mode, nl) * ntj : 0;
+    const size_t lr_lds = lr_wgs ? (size_t)lr_scratch_bytes(lr_mode, 1, threads == 1024 ? 1024 : 256, nl) : 0;
     const long long slots = (long long)num_cus * k - lr_wgs;
     if (slots < (long long)num_cus * k / 2) continue;
     const int RW = (int)(ceil_div(ceil_div(N, slots), m) * m);
@@ -216,6 +222,7 @@ static StreamPlanH plan_stream_k(const cl_blob_header& h, const int32_t* rp, int
     t.lds = (int)dyn;
     t.out_cap = cap;
     t.rank_row_bytes = rrb;
+    t.lr_nl = nl;
     t.rank_row_stride = rrs;
     t.rsc_row_bytes = rscb;
     return t;
@@ -309,7 +316,7 @@ static hipError_t launch_decode_stream(const Layer& L, const void* x, float* y, 
       r.lrp.flag = L.lr_cnt + 65;
       r.lrp.epoch = next_epoch(L, stream);
       r.lrp.withhold = L.wait_withhold;
-      r.lrp.S = stream_lr_slices(L.lr_S, L.st.wpg * 64, L.lr_mode);  // blocks over longer K slices
+      r.lrp.S = stream_lr_slices(L.lr_S, L.st.wpg * 64, L.lr_mode, L.st.lr_nl);  // blocks over longer K slices
       r.lr_ntj = L.lr_rpad / 64;
       r.lr_wgs = r.lrp.S * r.lr_ntj;
       r.lr_mode = L.lr_mode;
@@ -317,7 +324,7 @@ static hipError_t launch_decode_stream(const Layer& L, const void* x, float* y, 
       r.lr_epoch = r.lrp.epoch;
       r.lr_max_polls = L.wait_polls;
       r.lr_err = L.wait_err_dev;
-      lr_lds = lr_scratch_bytes(L.lr_mode, 1, L.st.wpg * 64 == 1024 ? 1024 : 256);
+      lr_lds = lr_scratch_bytes(L.lr_mode, 1, L.st.wpg * 64 == 1024 ? 1024 : 256, L.st.lr_nl);
     } else {
       const hipError_t e = launch_lowrank_prologue(L, 1, x, stream);
       if (e != hipSuccess) return e;
@@ -340,6 +347,7 @@ static hipError_t launch_decode_stream(const Layer& L, const void* x, float* y, 
   s.rsc_row_bytes = p.rsc_row_bytes;
   s.out_cap = p.out_cap;
   s.lr_readers = p.nwg;
+  s.lr_nl = p.lr_nl;
   const int lds = p.lds > lr_lds ? p.lds : lr_lds;
   const int grid = r.lr_wgs + p.nwg, threads = p.wpg * 64;
   switch (h.dense) {

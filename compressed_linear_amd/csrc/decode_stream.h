@@ -62,6 +62,7 @@ struct StreamArgs {
   int rsc_row_bytes;    // bytes of one row of int4 R^T scales
   int out_cap;          // outlier entries staged per workgroup (<= threads * kStOutLoads)
   int lr_readers;       // readers of t in a recorded launch (one per row workgroup)
+  int lr_nl;            // int4 factors in 1024-thread prologue blocks: 16-byte loads a thread (1 or 4)
 };
 
 // Static LDS of the tables, the kernel's one static array (at LDS address 0, so
@@ -84,8 +85,10 @@ __host__ __device__ inline int stream_slice(int F, int C, int wpg) {
 // Prologue blocks of a streaming launch: a workgroup of 16 wavefronts works on
 // a K slice four (fp16 / bf16 factors) or two (int4) times as long as the
 // 256-thread block's.
-inline int stream_lr_slices(int lr_S, int threads, int lr_mode) {
-  const int f = threads != 1024 ? 1 : lr_mode == 0 ? lr_slice_rows<0, 1024>() / kLrSlice : lr_slice_rows<1, 1024>() / kLrSlice;
+inline int stream_lr_slices(int lr_S, int threads, int lr_mode, int nl = 1) {
+  const int f = threads != 1024 ? 1
+                : lr_mode == 0 ? lr_slice_rows<0, 1024>() / kLrSlice
+                               : (nl == 4 ? lr_slice_rows<1, 1024, 4>() : lr_slice_rows<1, 1024>()) / kLrSlice;
   return (lr_S + f - 1) / f;
 }
 
@@ -110,6 +113,7 @@ __global__ void __launch_bounds__(1024) decode_stream_kernel(StreamArgs sa) {
       const int b = blockIdx.x, S = a.lrp.S, s = b % S, tj = (b / S) % a.lr_ntj, tm = b / (S * a.lr_ntj);
       if (nthr == 1024) {
         if (a.lr_mode == 0) lr_split_block<0, 1, BF16, EDIT, 1024, true>(a.lrp, s, tj, tm, a.lr_ntj, sb);
+        else if (sa.lr_nl == 4) lr_split_block<1, 1, BF16, EDIT, 1024, true, 4>(a.lrp, s, tj, tm, a.lr_ntj, sb);
         else lr_split_block<1, 1, BF16, EDIT, 1024, true>(a.lrp, s, tj, tm, a.lr_ntj, sb);
       } else {
         if (a.lr_mode == 0) lr_split_block<0, 1, BF16, EDIT, 256, true>(a.lrp, s, tj, tm, a.lr_ntj, sb);

@@ -20,6 +20,7 @@ struct StreamPlanH {
   int wpg = 0, rows_per_wg = 0, nwg = 0, lds = 0, out_cap = 0;
   int lds_x = 0, lds_max = 0, lds_meta = 0, lds_rp = 0, lds_rank = 0, lds_rsc = 0, lds_part0 = 0, lds_part1 = 0, lds_out = 0, lds_t = 0;
   int rank_row_bytes = 0, rank_row_stride = 0, rsc_row_bytes = 0;
+  int lr_nl = 1;  // int4 prologue: 16-byte loads a thread of a 1024-thread block
 };
 
 struct Layer {

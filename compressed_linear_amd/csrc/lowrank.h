@@ -227,18 +227,18 @@ __device__ __forceinline__ float dot2_act(uint32_t a, uint32_t b, float c) {
 }
 
 // NT = threads of a prologue block.  A thread loads NL 16-byte pieces of the
-// slice: 16 of fp16 / bf16 factors, 4 of int4 ones (1 in a 1024-thread block,
-// whose dequantisation would otherwise outlast the rest of the launch), so the
-// slice has 2 (NT / 16) NL rows (16-bit) or 2 (NT / 4) NL rows (int4).
-template <int MODE, int NT>
-constexpr int lr_loads() { return MODE == 0 ? 16 : NT == 1024 ? 1 : 4; }
-template <int MODE, int NT>
-constexpr int lr_slice_rows() { return 2 * (NT / (MODE == 0 ? 16 : 4)) * lr_loads<MODE, NT>(); }
+// slice: 16 of fp16 / bf16 factors, 4 of int4 ones (1 or 4 in a 1024-thread
+// block, NLX: the streaming kernel's choice per layer), so the slice has
+// 2 (NT / 16) NL rows (16-bit) or 2 (NT / 4) NL rows (int4).
+template <int MODE, int NT, int NLX = 0>
+constexpr int lr_loads() { return NLX ? NLX : MODE == 0 ? 16 : NT == 1024 ? 1 : 4; }
+template <int MODE, int NT, int NLX = 0>
+constexpr int lr_slice_rows() { return 2 * (NT / (MODE == 0 ? 16 : 4)) * lr_loads<MODE, NT, NLX>(); }
 static_assert(lr_slice_rows<0, 256>() == kLrSlice && lr_slice_rows<1, 256>() == kLrSlice, "256-thread slices");
 
-template <int MODE, int MT, int NT = 256>
+template <int MODE, int MT, int NT = 256, int NLX = 0>
 struct LrScratch {
-  static constexpr int SL = lr_slice_rows<MODE, NT>();  // K rows of the slice
+  static constexpr int SL = lr_slice_rows<MODE, NT, NLX>();  // K rows of the slice
   static constexpr int NG = MODE == 0 ? NT / 64 : NT / 16;  // reduction groups left after the shuffles
   static constexpr int NSC = SL / 16 + 1;         // int4 scale rows a slice can touch (group >= 16)
   static constexpr int xs = 0;                                   // uint16 [MT][SL]
@@ -249,8 +249,8 @@ struct LrScratch {
 };
 
 // LDS the block code needs (host side: sizes the decode kernel's dynamic LDS).
-inline int lr_scratch_bytes(int mode, int mt, int nt = 256) {
-  if (nt == 1024) return mode == 0 ? LrScratch<0, 1, 1024>::bytes : LrScratch<1, 1, 1024>::bytes;
+inline int lr_scratch_bytes(int mode, int mt, int nt = 256, int nl = 1) {
+  if (nt == 1024) return mode == 0 ? LrScratch<0, 1, 1024>::bytes : nl == 4 ? LrScratch<1, 1, 1024, 4>::bytes : LrScratch<1, 1, 1024>::bytes;
   return mode == 0 ? (mt == 1 ? LrScratch<0, 1>::bytes : mt == 2 ? LrScratch<0, 2>::bytes : LrScratch<0, 4>::bytes)
                    : (mt == 1 ? LrScratch<1, 1>::bytes : mt == 2 ? LrScratch<1, 2>::bytes : LrScratch<1, 4>::bytes);
 }
@@ -270,11 +270,11 @@ __device__ __forceinline__ uint32_t lr_tag(uint32_t epoch, uint32_t target) {
   return epoch ? epoch : (0x80000000u | target);
 }
 
-template <int MODE, int MT, bool BF16, bool EDIT, int NT = 256, bool TAG = false>
+template <int MODE, int MT, bool BF16, bool EDIT, int NT = 256, bool TAG = false, int NLX = 0>
 __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int tj, int tm, int ntj, uint8_t* smem) {
-  using SC = LrScratch<MODE, MT, NT>;
+  using SC = LrScratch<MODE, MT, NT, NLX>;
   constexpr int SL = SC::SL;
-  constexpr int NL = lr_loads<MODE, NT>();      // 16-byte loads per thread
+  constexpr int NL = lr_loads<MODE, NT, NLX>();  // 16-byte loads per thread
   constexpr int JL = MODE == 0 ? 4 : 16;        // columns per thread
   constexpr int LG = 64 / JL;                   // threads per K pair row of the tile
   constexpr int PR = NT / LG;                   // K pair rows in flight per workgroup
