@@ -92,6 +92,31 @@ inline int stream_lr_slices(int lr_S, int threads, int lr_mode, int nl = 1) {
   return (lr_S + f - 1) / f;
 }
 
+// 2:4 gather selector (16 entries, one per meta nibble i0 | i1 << 2): the
+// bytes of activations i0 and i1 of a group of four, picked by v_perm from the
+// group's two activation pairs.
+__device__ __forceinline__ uint32_t xsel_2_4_entry(uint32_t nib) {
+  const uint32_t i0 = nib & 3u, i1 = nib >> 2;
+  return (2u * i0) | ((2u * i0 + 1u) << 8) | ((2u * i1) << 16) | ((2u * i1 + 1u) << 24);
+}
+
+// One 2:4 chunk (sixteen groups of four weights, two kept in each): the kept
+// values as fp16 pairs qv[g] = (v0, v1) and the activations at their
+// positions xg[g] = (x[i0], x[i1]), gathered from the chunk's activation pairs
+// xv with the selector of the group's meta nibble (table at LDS address 0).
+// Half the dot products of expanding the weights to four positions with zeros.
+__device__ __forceinline__ void int4_24_gather(const uint32_t* lds, const uint4& w, const uint2& mw, const uint32_t (&xv)[32],
+                                               uint32_t (&qv)[16], uint32_t (&xg)[16]) {
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  const uint32_t mm[2] = {mw.x, mw.y};
+#pragma unroll
+  for (int g = 0; g < 16; ++g) {
+    qv[g] = int4_pair(ww[g / 4], 4 * (g % 4));
+    const uint32_t sel = lds_u32(lds, ((mm[g / 8] >> (4 * (g % 8))) & 0xFu) * 4u);
+    xg[g] = perm(xv[2 * g + 1], xv[2 * g], sel);
+  }
+}
+
 // XR = activation slots staged per thread, LR = low-rank part, EDIT = raw
 // activations edited (clamp, per-channel factors) while staged.
 template <int KIND, bool BF16, int XR, bool LR, bool EDIT>
@@ -210,11 +235,7 @@ __global__ void __launch_bounds__(1024) decode_stream_kernel(StreamArgs sa) {
     }
   }
   if constexpr (KIND == K_INT4_24) {
-    if (tid < 16) {
-      const uint2 e = seltab_2_4_entry((uint32_t)tid);
-      stab[2 * tid] = e.x;
-      stab[2 * tid + 1] = e.y;
-    }
+    if (tid < 16) stab[tid] = xsel_2_4_entry((uint32_t)tid);
   }
   __syncthreads();
   // LUT row tables from the staged values (LUT3: 64 pair entries; LUT4: 256)
@@ -329,11 +350,18 @@ __global__ void __launch_bounds__(1024) decode_stream_kernel(StreamArgs sa) {
       xv[4 * d + 2] = v.z;
       xv[4 * d + 3] = v.w;
     }
-    uint32_t wp[P];
-    chunk_pairs<KIND, true>(stab, w, make_uint4(mw.x, mw.y, 0, 0), rb, 0u, wp);
     float t = slow ? 0.f : acc;
+    if constexpr (KIND == K_INT4_24) {
+      uint32_t qv[16], xg[16];
+      int4_24_gather(stab, w, mw, xv, qv, xg);
 #pragma unroll
-    for (int jj = 0; jj < P; ++jj) t = mac2r<false>(wp[jj], xv[jj], t);
+      for (int jj = 0; jj < 16; ++jj) t = mac2r<false>(qv[jj], xg[jj], t);
+    } else {
+      uint32_t wp[P];
+      chunk_pairs<KIND, true>(stab, w, make_uint4(mw.x, mw.y, 0, 0), rb, 0u, wp);
+#pragma unroll
+      for (int jj = 0; jj < P; ++jj) t = mac2r<false>(wp[jj], xv[jj], t);
+    }
     if (!slow) {
       acc = t;
     } else {
@@ -363,10 +391,17 @@ __global__ void __launch_bounds__(1024) decode_stream_kernel(StreamArgs sa) {
       xv[4 * d + 2] = v.z;
       xv[4 * d + 3] = v.w;
     }
-    uint32_t wp[P];
-    chunk_pairs<KIND, true>(stab, w, make_uint4(mw.x, mw.y, 0, 0), (uint32_t)n * RTB, 0u, wp);
+    if constexpr (KIND == K_INT4_24) {
+      uint32_t qv[16], xg[16];
+      int4_24_gather(stab, w, mw, xv, qv, xg);
 #pragma unroll
-    for (int jj = 0; jj < P; ++jj) acc = mac2r<false>(wp[jj], xv[jj], acc);
+      for (int jj = 0; jj < 16; ++jj) acc = mac2r<false>(qv[jj], xg[jj], acc);
+    } else {
+      uint32_t wp[P];
+      chunk_pairs<KIND, true>(stab, w, make_uint4(mw.x, mw.y, 0, 0), (uint32_t)n * RTB, 0u, wp);
+#pragma unroll
+      for (int jj = 0; jj < P; ++jj) acc = mac2r<false>(wp[jj], xv[jj], acc);
+    }
   };
   auto comp_blk = [&](const uint4 (&w)[NB], const uint2 (&mw)[NB], int j) {
     const int P0 = f0 + 64 * NB * j;  // the block's first chunk
