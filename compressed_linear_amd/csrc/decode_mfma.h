@@ -618,7 +618,9 @@ __global__ void __launch_bounds__(256, 2) decode_mfma_kernel(MfArgs a) {
   }
   wait_stores();
   __syncthreads();  // every wave is past its last read of the staged slice: its first dword holds the flag
-  volatile uint32_t* s_last = sdyn;
+  // LDS-typed: a generic volatile pointer would be a flat access, waited for with every memory operation
+  volatile __attribute__((address_space(3))) uint32_t* s_last =
+      reinterpret_cast<volatile __attribute__((address_space(3))) uint32_t*>(reinterpret_cast<uintptr_t>(sdyn));
   if (tid == 0) {
     const uint32_t old = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *s_last = old == (uint32_t)(a.S - 1) ? 1u : 0u;

@@ -286,7 +286,10 @@ __device__ __forceinline__ void lr_split_block(const LrSplitArgs& a, int s, int 
   xrow_t* xs = reinterpret_cast<xrow_t*>(smem + SC::xs);
   float* sc = reinterpret_cast<float*>(smem + SC::sc);
   redrow_t* red = reinterpret_cast<redrow_t*>(smem + SC::red);
-  int& s_last = *reinterpret_cast<int*>(smem + SC::last);
+  // an LDS-typed reference: smem reaches some callers as a generic pointer,
+  // and a flat access would wait for every outstanding memory operation
+  __attribute__((address_space(3))) int& s_last =
+      *reinterpret_cast<__attribute__((address_space(3))) int*>(reinterpret_cast<uintptr_t>(smem + SC::last));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = s * SL, j0 = tj * 64, m0 = tm * MT;
   const int jg = tid % LG, pr = tid / LG;
