@@ -83,8 +83,8 @@ __host__ __device__ inline int stream_slice(int F, int C, int wpg) {
 }
 
 // Prologue blocks of a streaming launch: a workgroup of 16 wavefronts works on
-// a K slice four (fp16 / bf16 factors) or two (int4) times as long as the
-// 256-thread block's.
+// a K slice four (fp16 / bf16 factors) or one or four (int4, nl) times as long
+// as the 256-thread block's.
 inline int stream_lr_slices(int lr_S, int threads, int lr_mode, int nl = 1) {
   const int f = threads != 1024 ? 1
                 : lr_mode == 0 ? lr_slice_rows<0, 1024>() / kLrSlice
